@@ -1,0 +1,172 @@
+"""Pins for the oracle's backward pass and the densification statistics.
+
+The backward is the exact derivative of the (pinned) forward, so central finite
+differences of the forward pin it.  "Enabling the absolute-gradient strategy in 3D
+Gaussian Splatting" (jsqmd.com) s2 motivates the absolute statistic by per-pixel gradients
+that cancel in the plain sum; the symmetric case below has exactly that property.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from tile_differentiable_rasterizer_amd import scenes
+
+
+def small_scene(seed, n=6, L=3, W=32, H=32):
+    rng = np.random.default_rng(seed)
+    means = np.stack([rng.uniform(-0.3, 0.3, n), rng.uniform(-0.3, 0.3, n), rng.uniform(2.0, 3.0, n)], 1)
+    scales = np.exp(rng.uniform(-3.0, -2.2, (n, 3)))
+    quats = rng.normal(size=(n, 4))
+    opac = 1 / (1 + np.exp(-rng.normal(size=n)))
+    K = (L + 1) ** 2
+    sh = rng.normal(0, 0.3, (n, K, 3))
+    sh[:, 0, :] = rng.uniform(-0.5, 1.0, (n, 3))
+    sc = scenes.Scene(*(a.astype(np.float32) for a in (means, scales, quats, opac, sh)), L)
+    cam = scenes.look_at((0.3, -0.2, -0.4), (0.0, 0.0, 2.5), 40.0, 40.0, W / 2, H / 2, W, H)
+    return sc, cam
+
+
+def test_screen_gradients_match_finite_differences(orc):
+    for seed in (1, 2, 3):
+        sc, cam = small_scene(seed)
+        r = orc.end_to_end(sc, cam)
+        W, H = cam.width, cam.height
+        rng = np.random.default_rng(100 + seed)
+        dL = rng.normal(size=(3, H, W))
+        bg = (0.1, 0.2, 0.3)
+        gs = orc.render_bwd(W, H, bg, r["rec"], r["svals"], r["ranges"], sc.n, dL)
+
+        def loss(rec):
+            out = orc.render_pixels(W, H, bg, rec, r["svals"], r["ranges"])
+            img = out["col"].reshape(H, W, 3).transpose(2, 0, 1)
+            return float(np.sum(img * dL)), out["n"].copy()
+
+        base_n = loss(r["rec"])[1]
+        scale = np.max(np.abs(gs[:, :9])) + 1e-30
+        n_checked = 0
+        for g in range(sc.n):
+            if r["proj"]["n_tiles"][g] == 0:
+                continue
+            for e in range(9):
+                rec_p, rec_m = r["rec"].copy(), r["rec"].copy()
+                h = 1e-6 * max(abs(r["rec"][g, e]), 1e-2)
+                rec_p[g, e] += h
+                rec_m[g, e] -= h
+                lp, np_ = loss(rec_p)
+                lm, nm_ = loss(rec_m)
+                if not (np.array_equal(np_, base_n) and np.array_equal(nm_, base_n)):
+                    continue
+                fd = (lp - lm) / (2 * h)
+                assert gs[g, e] == pytest.approx(fd, rel=1e-5, abs=1e-7 * scale), (seed, g, e)
+                n_checked += 1
+        assert n_checked >= 40
+
+
+def test_parameter_gradients_match_finite_differences(orc):
+    n_checked = 0
+    for seed in (4, 5, 6):
+        sc, cam = small_scene(seed)
+        W, H = cam.width, cam.height
+        r = orc.end_to_end(sc, cam)
+        rng = np.random.default_rng(200 + seed)
+        dL = rng.normal(size=(3, H, W))
+        bg = (0.0, 0.0, 0.0)
+        gs = orc.render_bwd(W, H, bg, r["rec"], r["svals"], r["ranges"], sc.n, dL)
+        g3 = orc.project_bwd(sc, cam, gs)
+        params = [np.asarray(a, np.float32).astype(np.float64).copy()
+                  for a in (sc.means, sc.scales, sc.quats, sc.opacities, sc.sh.reshape(sc.n, -1))]
+        grads = [g3["dmeans"], g3["dscales"], g3["dquats"], g3["dopacity"], g3["dsh"].reshape(sc.n, -1)]
+        _, _, _, h0 = orc.forward_raw(*params, sc.sh_degree, cam, bg)
+        for pi, (par, grd) in enumerate(zip(params, grads)):
+            flat = par.reshape(-1)
+            gflat = grd.reshape(-1)
+            scale = np.max(np.abs(gflat)) + 1e-30
+            for idx in range(flat.size):
+                old = flat[idx]
+                h = 1e-6 * max(abs(old), 1e-2)
+                flat[idx] = old + h
+                ip, _, _, hp = orc.forward_raw(*params, sc.sh_degree, cam, bg)
+                flat[idx] = old - h
+                im, _, _, hm = orc.forward_raw(*params, sc.sh_degree, cam, bg)
+                flat[idx] = old
+                if hp != h0 or hm != h0:
+                    continue
+                fd = (np.sum(ip * dL) - np.sum(im * dL)) / (2 * h)
+                assert gflat[idx] == pytest.approx(fd, rel=1e-5, abs=1e-6 * scale), (seed, pi, idx)
+                n_checked += 1
+    assert n_checked > 300
+
+
+def test_absolute_statistic_survives_cancellation(orc):
+    """One isotropic Gaussian centred on a pixel corner, uniform upstream gradient: the
+    per-pixel mean gradients cancel in the sum, their norms do not."""
+    W = H = 32
+    sig = 3.0
+    rec = np.array([[16.0, 16.0, 1 / sig ** 2, 0.0, 1 / sig ** 2, 0.7, 0.4, 0.5, 0.6]])
+    trect = np.array([[0, 1, 0, 1]], np.int32)
+    k, v = orc.emit_pairs(trect, np.array([4], np.int64), np.array([2.0], np.float32).view(np.uint32), 2)
+    sk, sv = orc.sort_pairs(k, v)
+    rg = orc.tile_ranges(sk, 4)
+    gs = orc.render_bwd(W, H, (0.0, 0.0, 0.0), rec, sv, rg, 1, np.ones((3, H, W)))
+    assert abs(gs[0, 0]) < 1e-12 and abs(gs[0, 1]) < 1e-12
+    assert gs[0, 9] > 0.1
+    # the statistics: accum[:,0] is the norm of the summed gradient, accum[:,1] the sum of norms
+    stat_plain = math.hypot(gs[0, 0], gs[0, 1])
+    assert stat_plain < 1e-12 < gs[0, 9]
+
+
+def test_opacity_gradient_closed_form_at_centre(orc):
+    """dC/do = c * G at a pixel of a single unclamped Gaussian."""
+    W = H = 16
+    sig, o = 2.0, 0.6
+    u, v = 8.5 + 0.3, 8.5 - 0.2
+    c = (0.3, 0.8, 0.5)
+    rec = np.array([[u, v, 1 / sig ** 2, 0.0, 1 / sig ** 2, o, *c]])
+    trect = np.array([[0, 0, 0, 0]], np.int32)
+    k, vv = orc.emit_pairs(trect, np.array([1], np.int64), np.array([2.0], np.float32).view(np.uint32), 1)
+    rg = orc.tile_ranges(k, 1)
+    dL = np.zeros((3, H, W))
+    dL[1, 8, 8] = 1.0
+    gs = orc.render_bwd(W, H, (0.0, 0.0, 0.0), rec, vv, rg, 1, dL)
+    G = math.exp(-(0.3 ** 2 + 0.2 ** 2) / (2 * sig * sig))
+    assert gs[0, 5] == pytest.approx(c[1] * G, rel=1e-12)
+    assert gs[0, 7] == pytest.approx(o * G, rel=1e-12)
+
+
+def test_stats_accumulate_and_count_visible(orc):
+    sc, cam = small_scene(9)
+    r = orc.end_to_end(sc, cam)
+    W, H = cam.width, cam.height
+    dL = np.random.default_rng(1).normal(size=(3, H, W))
+    gs = orc.render_bwd(W, H, (0, 0, 0), r["rec"], r["svals"], r["ranges"], sc.n, dL)
+    g1 = orc.project_bwd(sc, cam, gs)
+    g2 = orc.project_bwd(sc, cam, gs, accum=g1["accum"], denom=g1["denom"])
+    vis = r["proj"]["n_tiles"] > 0
+    assert np.array_equal(g1["denom"], vis.astype(np.int64))
+    assert np.array_equal(g2["denom"], 2 * vis.astype(np.int64))
+    assert np.allclose(g1["accum"][:, 0], np.hypot(gs[:, 0], gs[:, 1]) * vis)
+    assert np.allclose(g1["accum"][:, 1], gs[:, 9] * vis)
+    assert np.allclose(g2["accum"], 2 * g1["accum"])
+
+
+def test_absolute_statistic_is_sum_of_per_pixel_l2_norms(orc):
+    """sum_p ||g_p||_2 by definition: restrict the upstream gradient to one pixel at a
+    time (the mean gradient is linear in it), take the L2 norm, and sum."""
+    sc, cam = small_scene(12, n=4, W=16, H=16)
+    r = orc.end_to_end(sc, cam)
+    W, H = cam.width, cam.height
+    dL = np.random.default_rng(3).normal(size=(3, H, W))
+    full = orc.render_bwd(W, H, (0, 0, 0), r["rec"], r["svals"], r["ranges"], sc.n, dL)
+    acc = np.zeros(sc.n)
+    acc_uv = np.zeros((sc.n, 2))
+    for j in range(H):
+        for i in range(W):
+            one = np.zeros_like(dL)
+            one[:, j, i] = dL[:, j, i]
+            gp = orc.render_bwd(W, H, (0, 0, 0), r["rec"], r["svals"], r["ranges"], sc.n, one)
+            acc += np.hypot(gp[:, 0], gp[:, 1])
+            acc_uv += gp[:, :2]
+    assert np.allclose(full[:, 9], acc, rtol=1e-12, atol=1e-15)
+    assert np.allclose(full[:, :2], acc_uv, rtol=1e-10, atol=1e-13)
+    assert np.any(acc > 0)
