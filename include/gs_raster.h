@@ -1,0 +1,205 @@
+/*
+ * gs_raster.h -- C ABI of the MI355X (gfx950) tile rasteriser for 3D Gaussian splatting.
+ *
+ * The five calls follow the pipeline the pages describe: project every Gaussian to a 2D
+ * Gaussian, assign it to 16x16 tiles, sort each tile's list by depth, composite every
+ * pixel front to back with transmittance, and run the reverse pass that feeds the
+ * densification statistics.
+ *   - "Implementing Better Gaussian Splatting in Julia" (pwwt.cn): s1.1 pipeline, s3.1
+ *     the Gaussian record (position, scale, quaternion rotation, opacity, colour), s3.2
+ *     projection through the Jacobian, s3.3 front-to-back compositing, s4.3 16x16 tiles
+ *     and the influence radius, s5.1/s5.3 preallocated buffers and data resident on GPU.
+ *   - "Better Gaussian Splatting in Julia" (lshu.cn): s3.1 parameter table (mean,
+ *     covariance, SH coefficients by degree, opacity), s3.2 the rasterize pipeline
+ *     (project_gaussians, assign_to_tiles, sort_by_depth!, blend), s7.2 buffers passed in.
+ *   - "Enabling the absolute-gradient strategy in 3D Gaussian Splatting" (jsqmd.com):
+ *     s1-s3 the view-space and absolute gradient accumulators and their visibility mask.
+ *   - "Training 10M Gaussians in 8 GB: Spirula Studio's VRAM efficiency" (mhpq.cn): the
+ *     32-bit index wrap section (64-bit addressing, overflow is an error, never a wrap).
+ *
+ * Conventions
+ *  - Pointers are DEVICE pointers owned by the caller unless marked [host].  The library
+ *    never allocates memory; scratch space comes from one caller workspace sized by
+ *    gs_workspace_bytes().  Arrays are dense, row major, naturally aligned (16 bytes for
+ *    float arrays read as vectors: means/scales/quats/sh/rec).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued on it; only
+ *    gs_bin_tiles synchronises it, once, to read the pair count back.
+ *  - Every call validates its arguments before touching the GPU and returns a gs_status.
+ *  - Calls keep no global state and may run concurrently on different streams with
+ *    different buffers.
+ *  - Numbers: fp32 storage; the projection evaluates the binning-critical geometry
+ *    (camera-space mean, 2D covariance, support, pixel box) in float64 and rounds once.
+ *  - Gaussians with NaN/Inf inputs are culled (every visibility test fails on NaN).
+ */
+#ifndef GS_RASTER_H
+#define GS_RASTER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gs_status;
+enum {
+  GS_OK = 0,
+  GS_ERR_INVALID_ARG = 1, /* null pointer with n > 0, sh_degree not in 0..3, bad camera   */
+  GS_ERR_CAPACITY = 2,    /* pair buffer too small; *n_pairs holds the required count     */
+  GS_ERR_OVERFLOW = 3,    /* n >= 2^32, width/height > 65535, or a count past int64        */
+  GS_ERR_HIP = 4,         /* a HIP launch or runtime call failed                          */
+  GS_ERR_WORKSPACE = 5    /* workspace NULL or smaller than gs_workspace_bytes()          */
+};
+
+#define GS_TILE 16       /* tiles are 16x16 pixels                                          */
+#define GS_REC_FLOATS 12 /* floats per projected render record                            */
+#define GS_GRAD_SCREEN 10 /* floats per Gaussian in the screen-space gradient block        */
+
+/* Pinhole camera, OpenCV frame: x right, y down, z forward.  x_cam = R x_world + t with
+ * R row major.  Pixel (i, j) has its centre at (i + 0.5, j + 0.5).  Gaussians with
+ * z_cam <= near_z are culled.  The camera centre used for view-dependent colour is
+ * -R^T t.  width, height in 1..65535; fx, fy, near_z > 0. */
+typedef struct gs_camera {
+  float R[9];
+  float t[3];
+  float fx, fy, cx, cy;
+  int32_t width, height;
+  float near_z;
+} gs_camera;
+
+/* Output of gs_project, N rows each (device pointers, caller-owned).
+ *  rec[n][12]: u, v (2D mean, pixels); A, B, C (conic = inverse 2D covariance
+ *              [[A, B], [B, C]]); opacity; r, g, b (colour, clamped at 0);
+ *              word 9 = px0 | px1 << 16 and word 10 = py0 | py1 << 16 (the pixel-centre
+ *              bounding box of the support ellipse, clamped to the image, as uint32
+ *              bit patterns); word 11 = 0.  All zero for a culled Gaussian.
+ *  depth[n]:   camera-space z rounded once to fp32 (sort keys use its bit pattern).
+ *  rect[n][4]: tile rectangle tx0, tx1, ty0, ty1 (inclusive); zero when culled.
+ *  n_tiles[n]: (tx1 - tx0 + 1) * (ty1 - ty0 + 1), or 0 when culled.
+ *  clamp[n]:   bit c set when colour channel c was negative before the clamp at 0. */
+typedef struct gs_projected {
+  float* rec;
+  float* depth;
+  uint16_t* rect;
+  uint32_t* n_tiles;
+  uint8_t* clamp;
+} gs_projected;
+
+/* Gradients written by gs_render_bwd (all overwritten, N rows each).
+ *  grad_screen[n][10]: dL/du, dL/dv, dL/dA, dL/dB, dL/dC, dL/dopacity, dL/dr, dL/dg,
+ *                      dL/db, and sum over pixels of ||dL_p/d(u, v)||_2 (the absolute
+ *                      view-space gradient).  B is the off-diagonal conic entry, which
+ *                      enters the exponent as 2 B dx dy.
+ *  dmeans[n][3], dscales[n][3], dquats[n][4] (w, x, y, z), dsh[n][K][3]: gradients with
+ *                      respect to the inputs of gs_project.  The opacity gradient is
+ *                      grad_screen column 5. */
+typedef struct gs_grads {
+  float* grad_screen;
+  float* dmeans;
+  float* dscales;
+  float* dquats;
+  float* dsh;
+} gs_grads;
+
+/*
+ * gs_project -- project N Gaussians ("Implementing Better Gaussian Splatting in Julia"
+ * s3.1-3.2; "Better Gaussian Splatting in Julia" s3.1-3.2).
+ *  means[n][3]      world-space centres
+ *  scales[n][3]     linear standard deviations along the local axes
+ *  quats[n][4]      rotation quaternion (w, x, y, z); normalised inside
+ *  opacities[n]     opacity in (0, 1) (already activated)
+ *  sh[n][K][3]      SH coefficients, K = (sh_degree + 1)^2, real basis with the
+ *                   Condon-Shortley phase; colour = max(0, 0.5 + sum_k Y_k(d) sh_k)
+ *                   with d the unit direction from the camera centre to the mean
+ *  cam [host]       camera
+ * The 2D covariance is J W Sigma W^T J^T (first-order perspective Jacobian J at the
+ * camera-space mean, no low-pass dilation).  A Gaussian is kept when z > near_z,
+ * det > 0, opacity >= 1/255 and its support {q <= 2 ln(255 opacity)} covers at least
+ * one pixel centre; the tile rect is the support's pixel-centre bounding box >> 4.
+ * Errors: INVALID_ARG, OVERFLOW (n >= 2^32), HIP.
+ */
+gs_status gs_project(int64_t n, const float* means, const float* scales, const float* quats,
+                     const float* opacities, const float* sh, int32_t sh_degree,
+                     const gs_camera* cam, gs_projected out, void* stream);
+
+/*
+ * gs_workspace_bytes -- bytes of device workspace that gs_bin_tiles and gs_sort_keys need
+ * for n Gaussians, up to pair_capacity pairs and num_tiles tiles (the largest stage; the
+ * two calls reuse the same workspace).  Returns 0 for invalid arguments.
+ */
+size_t gs_workspace_bytes(int64_t n, int64_t pair_capacity, int32_t num_tiles);
+
+/*
+ * gs_bin_tiles -- duplicate every visible Gaussian once per covered tile ("Better Gaussian
+ * Splatting in Julia" s3.2 assign_to_tiles).  Pairs come out in Gaussian-id order, tiles
+ * row by row inside a Gaussian:
+ *   keys[p] = tile_id << 32 | bits(depth),  tile_id = ty * tiles_x + tx
+ *   vals[p] = Gaussian id
+ * Writes the pair count P to *n_pairs [host] (this is the call's one device->host read and
+ * stream synchronisation).  With keys == NULL only P is computed.  If P > capacity,
+ * returns GS_ERR_CAPACITY with *n_pairs = P and writes no pairs.
+ * Errors: INVALID_ARG, WORKSPACE, CAPACITY, OVERFLOW, HIP.
+ */
+gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint64_t* keys,
+                       uint32_t* vals, int64_t capacity, int64_t* n_pairs, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * gs_sort_keys -- stable LSD radix sort of (keys, vals) over the key's significant bits
+ * (32 + ceil(log2(num_tiles))), 8 bits per pass, digits constant over all keys skipped
+ * ("Better Gaussian Splatting in Julia" s3.2 sort_by_depth!; "Implementing Better
+ * Gaussian Splatting in Julia" s3.3 depth order).  Equal keys keep their input order, so
+ * pairs emitted in id order come out with depth ties broken by Gaussian id.  The result is
+ * left in keys/vals; keys_tmp/vals_tmp are scratch of the same size.  Then writes
+ * tile_ranges[num_tiles][2] = [first, last + 1) of each tile in the sorted order ([0, 0)
+ * for an empty tile).  Keys must have tile_id < num_tiles.
+ * Errors: INVALID_ARG, WORKSPACE, OVERFLOW, HIP.
+ */
+gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, uint64_t* keys, uint32_t* vals,
+                       uint64_t* keys_tmp, uint32_t* vals_tmp, int64_t* tile_ranges,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gs_render_fwd -- composite every pixel front to back over its tile's sorted list
+ * ("Implementing Better Gaussian Splatting in Julia" s3.3 and s5.4, the tile method):
+ *   alpha = min(0.99, opacity * exp(-q/2)), q = A dx^2 + 2 B dx dy + C dy^2,
+ *   (dx, dy) = pixel centre - (u, v); contributions with alpha < 1/255 are skipped;
+ *   C += rgb * alpha * T; T *= 1 - alpha; the pixel stops once T < 1e-4;
+ *   image = C + T * bg.
+ *  image[3][H][W] (planar), final_T[H][W], n_contrib[H][W] = 1 + the tile-list position
+ *  of the last contributor (0 if none), which gs_render_bwd needs.
+ * Errors: INVALID_ARG, HIP.
+ */
+gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_vals,
+                        const int64_t* tile_ranges, const gs_camera* cam, const float bg[3],
+                        float* image, float* final_T, uint32_t* n_contrib, void* stream);
+
+/*
+ * gs_render_bwd -- reverse pass of gs_render_fwd and of gs_project, plus densification
+ * statistics ("Enabling the absolute-gradient strategy in 3D Gaussian Splatting" s1-s3):
+ * given dL/dimage[3][H][W], writes every gradient in `out` (overwritten) and, when
+ * densify_accum / densify_denom are non-NULL, ACCUMULATES for every visible Gaussian
+ * (n_tiles > 0):
+ *   densify_accum[i][0] += || (dL/du, dL/dv) ||_2          (view-space gradient norm)
+ *   densify_accum[i][1] += sum_p || dL_p/d(u, v) ||_2       (absolute gradient)
+ *   densify_denom[i]    += 1
+ * Inputs are those of the matching gs_project / gs_sort_keys / gs_render_fwd calls.
+ * Float atomics make the screen gradients' summation order, and so their last bits,
+ * vary between runs.
+ * Errors: INVALID_ARG, HIP.
+ */
+gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, const float* quats,
+                        const float* opacities, const float* sh, int32_t sh_degree,
+                        const gs_camera* cam, gs_projected proj, const uint32_t* sorted_vals,
+                        const int64_t* tile_ranges, const float bg[3], const float* final_T,
+                        const uint32_t* n_contrib, const float* dL_dimage, gs_grads out,
+                        float* densify_accum, int32_t* densify_denom, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* gs_status_string(gs_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GS_RASTER_H */

@@ -189,8 +189,14 @@ def render_brute(W: int, H: int, bg, rec, order):
     return image, T
 
 
-def render_bwd(W: int, H: int, bg, rec, vals, ranges, n: int, dL_dimg) -> np.ndarray:
-    """grad_screen (n, 10): dL/d(u, v, A, B, C, opacity, r, g, b), sum_p ||dL_p/d(u, v)||."""
+def num_threads() -> int:
+    return int(_load().orc_num_threads())
+
+
+def render_bwd(W: int, H: int, bg, rec, vals, ranges, n: int, dL_dimg, with_abs: bool = False, pix=None):
+    """grad_screen (n, 10): dL/d(u, v, A, B, C, opacity, r, g, b), sum_p ||dL_p/d(u, v)||.
+
+    With ``with_abs`` also returns the per-element sum of |per-pixel terms|."""
     lib = _load()
     rec = np.ascontiguousarray(rec, dtype=np.float64)
     vals = np.ascontiguousarray(vals, dtype=np.uint32)
@@ -198,9 +204,12 @@ def render_bwd(W: int, H: int, bg, rec, vals, ranges, n: int, dL_dimg) -> np.nda
     bg = np.ascontiguousarray(bg, dtype=np.float64)
     dL = np.ascontiguousarray(np.asarray(dL_dimg, dtype=np.float64).reshape(3, H, W))
     gs = np.zeros((n, 10))
+    ga = np.zeros((n, 10)) if with_abs else None
+    pixa = None if pix is None else np.ascontiguousarray(pix, dtype=np.int64)
     lib.orc_render_bwd(C.c_int64(W), C.c_int64(H), _p(bg), _p(rec), _p(vals), _p(ranges),
-                       C.c_int64(n), _p(dL), _p(gs))
-    return gs
+                       C.c_int64(n), _p(dL), _p(gs), _p(ga), C.c_int64(0 if pixa is None else pixa.shape[0]),
+                       _p(pixa))
+    return (gs, ga) if with_abs else gs
 
 
 def project_bwd(scene, cam, grad_screen, accum=None, denom=None) -> dict:

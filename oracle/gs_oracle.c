@@ -27,6 +27,18 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the OpenMP loops use (1 without OpenMP). */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 #define ORC_AMAX ((double)0.99f)              /* alpha clamp                         */
 #define ORC_AMIN ((double)(float)(1.0 / 255.0)) /* skip contributions below this alpha */
@@ -532,16 +544,23 @@ void orc_render_brute(int64_t W, int64_t H, const double bg[3], const double* re
 /* ------------------------------------------------------------------------------------ */
 void orc_render_bwd(int64_t W, int64_t H, const double bg[3], const double* rec,
                     const uint32_t* vals, const int64_t* ranges, int64_t n,
-                    const double* dL_dimg, double* grad_screen) {
+                    const double* dL_dimg, double* grad_screen, double* grad_abs,
+                    int64_t npix, const int64_t* pix) {
+  /* pix (optional): only these pixels (linear j*W + i) contribute; NULL = all W*H. */
+  /* grad_abs (optional): per element, the sum of |per-pixel terms|, so a caller can tell
+   * an ill-conditioned sum (|sum| << sum |terms|) from a wrong one. */
   const int64_t tiles_x = (W + ORC_TILE - 1) / ORC_TILE;
   memset(grad_screen, 0, sizeof(double) * 10 * (size_t)n);
+  if (grad_abs) memset(grad_abs, 0, sizeof(double) * 10 * (size_t)n);
 #pragma omp parallel
   {
     int64_t cap = 1024;
     uint32_t* ids = (uint32_t*)malloc(sizeof(uint32_t) * cap);
     double* st = (double*)malloc(sizeof(double) * 6 * cap);
+    const int64_t count = pix ? npix : W * H;
 #pragma omp for schedule(dynamic, 64)
-    for (int64_t lin = 0; lin < W * H; ++lin) {
+    for (int64_t pi = 0; pi < count; ++pi) {
+      const int64_t lin = pix ? pix[pi] : pi;
       const int64_t i = lin % W, j = lin / W;
       const double px = i + 0.5, py = j + 0.5;
       const uint32_t* list;
@@ -602,6 +621,13 @@ void orc_render_bwd(int64_t W, int64_t H, const double bg[3], const double* rec,
         for (int e = 0; e < 10; ++e) {
 #pragma omp atomic
           out[e] += g[e];
+        }
+        if (grad_abs) {
+          double* oa = grad_abs + 10 * (size_t)id;
+          for (int e = 0; e < 10; ++e) {
+#pragma omp atomic
+            oa[e] += fabs(g[e]);
+          }
         }
       }
     }

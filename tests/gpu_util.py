@@ -1,0 +1,182 @@
+"""Helpers for the GPU parity tests: run each C-ABI stage, bring results to the host, and
+compare them with the float64 oracle under the acceptance rules:
+
+* projection: same visibility, tile rect, pixel box and depth bits; 2D mean within 1e-4 px,
+  conic within 1e-5 relative, colour within 1e-5 (absolute or relative to 1);
+* binning and sorting: bit-exact keys, ids and tile ranges;
+* compositing: every channel and the final transmittance within 1e-4 of some result that a
+  correct evaluation of the thresholds can give (the oracle enumerates the two sides of any
+  decision that float32 rounding could flip), and the same contributor count;
+* gradients: |g - g_ref| <= max(1e-3 |g_ref|, 1e-5, 8 * 2^-24 * S), where S is the sum of
+  the absolute per-pixel terms that make up the element (the oracle reports it).  The
+  last term is float32's own floor for a sum whose terms cancel: each per-pixel term
+  carries a few float32 roundings and the sum adds a few more, so a correct float32
+  result can be off by a small multiple of 2^-24 * S even when |g_ref| << S.  Elements
+  that pass only through that term are counted and reported.
+
+Each oracle stage consumes the previous GPU stage's output lifted exactly to float64, so a
+mismatch names the stage that caused it.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from tile_differentiable_rasterizer_amd import raster
+
+PIX_TOL = 1e-4
+GRAD_REL, GRAD_ABS = 1e-3, 1e-5
+
+
+def say(msg: str):
+    print(msg, flush=True)
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def gpu_stages(scene, cam, bg=(0.0, 0.0, 0.0), keep_unsorted=True):
+    """Run project, bin, sort, render through the C ABI; return host copies."""
+    dev = torch.device("cuda")
+    means, scales, quats, opac, sh = raster.scene_to_device(scene, dev)
+    n = scene.n
+    tiles = cam.tiles_x * cam.tiles_y
+    proj = raster.project(means, scales, quats, opac, sh, scene.sh_degree, cam)
+    ws = torch.empty(max(raster.workspace_bytes(n, 1, tiles), 8), dtype=torch.uint8, device=dev)
+    st, P = raster.bin_tiles(proj, cam, None, None, ws)
+    assert st == raster.GS_OK
+    keys = torch.empty(max(P, 1), dtype=torch.int64, device=dev)
+    vals = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(raster.workspace_bytes(n, P, tiles), dtype=torch.uint8, device=dev)
+    st, P2 = raster.bin_tiles(proj, cam, keys, vals, ws)
+    assert st == raster.GS_OK and P2 == P
+    torch.cuda.synchronize()
+    out = dict(P=P, n=n)
+    if keep_unsorted:
+        out["keys_unsorted"] = to_np(keys[:P]).view(np.uint64).copy()
+        out["vals_unsorted"] = to_np(vals[:P]).view(np.uint32).copy()
+    ktmp = torch.empty_like(keys)
+    vtmp = torch.empty_like(vals)
+    ranges = torch.empty((tiles, 2), dtype=torch.int64, device=dev)
+    raster.sort_keys(P, tiles, keys, vals, ktmp, vtmp, ranges, ws)
+    image = torch.empty((3, cam.height, cam.width), dtype=torch.float32, device=dev)
+    final_T = torch.empty((cam.height, cam.width), dtype=torch.float32, device=dev)
+    n_contrib = torch.empty((cam.height, cam.width), dtype=torch.int32, device=dev)
+    raster.render_fwd(proj, vals, ranges, cam, bg, image, final_T, n_contrib)
+    torch.cuda.synchronize()
+    rec = to_np(proj["rec"])
+    out.update(
+        rec=rec, bbox=rec[:, 9:11].view(np.uint32), depth_bits=to_np(proj["depth"]).view(np.uint32),
+        rect=to_np(proj["rect"]).view(np.uint16).astype(np.int32), n_tiles=to_np(proj["n_tiles"]).view(np.uint32),
+        clamp=to_np(proj["clamp"]), keys=to_np(keys[:P]).view(np.uint64).copy(),
+        vals=to_np(vals[:P]).view(np.uint32).copy(), ranges=to_np(ranges), image=to_np(image),
+        final_T=to_np(final_T), n_contrib=to_np(n_contrib).view(np.uint32),
+        dev=dict(means=means, scales=scales, quats=quats, opac=opac, sh=sh, proj=proj, vals=vals, ranges=ranges,
+                 final_T=final_T, n_contrib=n_contrib, image=image))
+    return out
+
+
+def rec9(g) -> np.ndarray:
+    """The GPU's render records as the oracle's (u, v, A, B, C, o, r, g, b), exact in f64."""
+    return np.ascontiguousarray(g["rec"][:, :9].astype(np.float64))
+
+
+def check_projection(scene, cam, g, label=""):
+    p = oracle.project(scene, cam)
+    flags = p["flags"]
+    vis_o = p["n_tiles"] > 0
+    vis_g = g["n_tiles"] > 0
+    edge = (flags & 2) != 0
+    bad_vis = np.nonzero((vis_o != vis_g) & ~edge)[0]
+    assert bad_vis.size == 0, f"{label}: visibility differs for ids {bad_vis[:10]}"
+    both = vis_o & vis_g & ~edge
+    assert np.array_equal(g["n_tiles"][both], p["n_tiles"][both].astype(np.uint32)), label
+    assert np.array_equal(g["rect"][both], p["trect"][both]), label
+    px = p["pxrect"][both]
+    bx, by = g["bbox"][both, 0], g["bbox"][both, 1]
+    gpx = np.stack([bx & 0xFFFF, bx >> 16, by & 0xFFFF, by >> 16], 1).astype(np.int32)
+    assert np.array_equal(gpx, px), f"{label}: pixel box differs"
+    tie = (flags & 1) != 0
+    vis_d = vis_o & vis_g & ~tie
+    assert np.array_equal(g["depth_bits"][vis_d], p["depth_bits"][vis_d]), f"{label}: depth bits differ"
+    r = g["rec"][both].astype(np.float64)
+    assert np.max(np.abs(r[:, 0:2] - p["uv"][both]), initial=0) <= 1e-4, f"{label}: 2D mean"
+    cn = p["conic"][both]
+    scale = np.abs(cn[:, 0]) + np.abs(cn[:, 2])
+    err = np.abs(r[:, 2:5] - cn) / scale[:, None]
+    assert np.max(err, initial=0) <= 1e-5, f"{label}: conic rel err {np.max(err, initial=0)}"
+    assert np.array_equal(r[:, 5], p["opacity"][both]), f"{label}: opacity"
+    cerr = np.abs(r[:, 6:9] - p["rgb"][both]) / np.maximum(1.0, np.abs(p["rgb"][both]))
+    assert np.max(cerr, initial=0) <= 1e-5, f"{label}: colour err {np.max(cerr, initial=0)}"
+    csure = both & ((flags & 4) == 0)
+    assert np.array_equal(g["clamp"][csure], p["clamp"][csure]), f"{label}: clamp bits"
+    return dict(visible=int(vis_g.sum()), edge=int(edge.sum()), ties=int(tie.sum()))
+
+
+def check_binning(cam, g, label=""):
+    trect = np.ascontiguousarray(g["rect"].astype(np.int32))
+    k, v = oracle.emit_pairs(trect, g["n_tiles"].astype(np.int64), g["depth_bits"], cam.tiles_x)
+    assert k.shape[0] == g["P"], f"{label}: pair count {g['P']} vs {k.shape[0]}"
+    if "keys_unsorted" in g:
+        assert np.array_equal(g["keys_unsorted"], k), f"{label}: emitted keys differ"
+        assert np.array_equal(g["vals_unsorted"], v), f"{label}: emitted ids differ"
+    sk, sv = oracle.sort_pairs(k, v)
+    assert np.array_equal(g["keys"], sk), f"{label}: sorted keys differ"
+    assert np.array_equal(g["vals"], sv), f"{label}: sorted ids differ"
+    rg = oracle.tile_ranges(sk, cam.num_tiles)
+    assert np.array_equal(g["ranges"], rg), f"{label}: tile ranges differ"
+
+
+def compare_pixels(gpu_col, gpu_T, gpu_n, orc, label="", tol=PIX_TOL):
+    """gpu_col (npix, 3), gpu_T (npix,), gpu_n (npix,) against oracle render_pixels output."""
+    nb = orc["nbranch"]
+    br = orc["branches"]  # (npix, 4, 5)
+    ok = np.zeros(gpu_col.shape[0], bool)
+    for m in range(4):
+        valid = nb > m
+        d = np.abs(br[:, m, 0:3] - gpu_col).max(axis=1)
+        dT = np.abs(br[:, m, 3] - gpu_T)
+        same_n = br[:, m, 4] == gpu_n
+        ok |= valid & (d <= tol) & (dT <= tol) & same_n
+    excluded = nb == 0
+    bad = np.nonzero(~ok & ~excluded)[0]
+    if bad.size:
+        i = bad[0]
+        raise AssertionError(
+            f"{label}: {bad.size} pixels differ; first idx {i}: gpu {gpu_col[i]} T {gpu_T[i]} n {gpu_n[i]} "
+            f"oracle {orc['col'][i]} T {orc['T'][i]} n {orc['n'][i]} nbranch {nb[i]}")
+    return dict(pixels=int(gpu_col.shape[0]), ambiguous=int((nb > 1).sum()), excluded=int(excluded.sum()))
+
+
+def check_render_chained(cam, g, bg=(0.0, 0.0, 0.0), pix=None, label=""):
+    W, H = cam.width, cam.height
+    orc = oracle.render_pixels(W, H, bg, rec9(g), g["vals"], g["ranges"], pix)
+    img = g["image"].reshape(3, -1).T
+    T = g["final_T"].reshape(-1)
+    n = g["n_contrib"].reshape(-1).astype(np.int64)
+    if pix is not None:
+        img, T, n = img[pix], T[pix], n[pix]
+    return compare_pixels(img, T, n, orc, label)
+
+
+COND_ULPS = 8.0 * 2.0 ** -24
+
+
+def grad_mismatch(gpu, ref, absum=None, counts=None):
+    """Indices violating the gradient tolerance, and the worst ratio |g - ref| / tol.
+
+    With ``absum`` (per-element sum of |terms|) the float32 conditioning floor joins the
+    tolerance; ``counts`` (a dict) then receives how many elements needed it."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    tol = np.maximum(GRAD_REL * np.abs(ref), GRAD_ABS)
+    if absum is not None:
+        cond = COND_ULPS * np.asarray(absum, np.float64)
+        if counts is not None:
+            err = np.abs(gpu - ref)
+            counts["conditioning_only"] = int(np.sum((err > tol) & (err <= cond)))
+        tol = np.maximum(tol, cond)
+    r = np.abs(gpu - ref) / tol
+    return np.nonzero(r > 1.0), float(np.max(r, initial=0.0))

@@ -1,0 +1,168 @@
+// gs_api.hip -- the extern "C" boundary of libgsraster: argument validation (before any
+// HIP call), the workspace layout, and kernel launches on the caller's stream.  Every
+// buffer belongs to the caller; nothing here allocates.
+#include <math.h>
+#include <string.h>
+
+#include "gs_device.h"
+
+namespace gs {
+hipError_t launch_project(int64_t n, const float* means, const float* scales, const float* quats,
+                          const float* opac, const float* sh, int L, const DevCamera& cam,
+                          const gs_projected& out, hipStream_t s);
+hipError_t launch_project_bwd(int64_t n, const float* means, const float* scales, const float* quats,
+                              const float* sh, int L, const DevCamera& cam, const gs_projected& proj,
+                              const gs_grads& gr, float* accum, int32_t* denom, hipStream_t s);
+size_t bin_workspace_bytes(int64_t n);
+hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, void* ws, hipStream_t s);
+uint64_t* bin_total_ptr(int64_t n, void* ws);
+hipError_t launch_bin_emit(int64_t n, const gs_projected& proj, int tiles_x, const void* ws, uint64_t* keys,
+                           uint32_t* vals, hipStream_t s);
+size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles);
+hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
+                       uint32_t* vals_tmp, int64_t* ranges, void* ws, hipStream_t s);
+hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
+hipError_t launch_render_fwd(const gs_projected& proj, const uint32_t* vals, const int64_t* ranges,
+                             const DevCamera& cam, const float bg[3], float* image, float* final_T,
+                             uint32_t* n_contrib, hipStream_t s);
+hipError_t launch_render_bwd(const gs_projected& proj, const uint32_t* vals, const int64_t* ranges,
+                             const DevCamera& cam, const float bg[3], const float* final_T,
+                             const uint32_t* n_contrib, const float* dL, float* gscreen, hipStream_t s);
+}  // namespace gs
+
+using namespace gs;
+
+namespace {
+
+constexpr int64_t kMaxGaussians = (int64_t)1 << 32;  // ids are uint32
+
+bool camera_ok(const gs_camera* c) {
+  if (!c) return false;
+  if (!(c->fx > 0.0f) || !(c->fy > 0.0f) || !(c->near_z > 0.0f)) return false;
+  if (c->width <= 0 || c->height <= 0) return false;
+  return true;
+}
+
+bool camera_fits(const gs_camera* c) { return c->width <= 65535 && c->height <= 65535; }
+
+DevCamera dev_camera(const gs_camera* c) {
+  DevCamera d;
+  for (int i = 0; i < 9; ++i) d.R[i] = c->R[i];
+  for (int i = 0; i < 3; ++i) d.t[i] = c->t[i];
+  d.fx = c->fx; d.fy = c->fy; d.cx = c->cx; d.cy = c->cy; d.near_z = c->near_z;
+  for (int i = 0; i < 3; ++i) d.campos[i] = -(d.R[i] * d.t[0] + d.R[3 + i] * d.t[1] + d.R[6 + i] * d.t[2]);
+  d.width = c->width; d.height = c->height;
+  d.tiles_x = (c->width + kTile - 1) / kTile;
+  d.tiles_y = (c->height + kTile - 1) / kTile;
+  return d;
+}
+
+bool projected_ok(const gs_projected& p) { return p.rec && p.depth && p.rect && p.n_tiles && p.clamp; }
+
+gs_status hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gs_status_string(gs_status s) {
+  switch (s) {
+    case GS_OK: return "ok";
+    case GS_ERR_INVALID_ARG: return "invalid argument";
+    case GS_ERR_CAPACITY: return "pair buffer too small";
+    case GS_ERR_OVERFLOW: return "size overflow";
+    case GS_ERR_HIP: return "HIP error";
+    case GS_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+size_t gs_workspace_bytes(int64_t n, int64_t pair_capacity, int32_t num_tiles) {
+  if (n < 0 || pair_capacity < 0 || num_tiles < 1) return 0;
+  const size_t a = bin_workspace_bytes(n);
+  const size_t b = sort_workspace_bytes(pair_capacity, num_tiles);
+  return a > b ? a : b;
+}
+
+gs_status gs_project(int64_t n, const float* means, const float* scales, const float* quats,
+                     const float* opacities, const float* sh, int32_t sh_degree, const gs_camera* cam,
+                     gs_projected out, void* stream) {
+  if (n < 0 || sh_degree < 0 || sh_degree > 3 || !camera_ok(cam)) return GS_ERR_INVALID_ARG;
+  if (n >= kMaxGaussians || !camera_fits(cam)) return GS_ERR_OVERFLOW;
+  if (n == 0) return GS_OK;
+  if (!means || !scales || !quats || !opacities || !sh || !projected_ok(out)) return GS_ERR_INVALID_ARG;
+  const DevCamera d = dev_camera(cam);
+  return hip_status(launch_project(n, means, scales, quats, opacities, sh, sh_degree, d, out,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint64_t* keys, uint32_t* vals,
+                       int64_t capacity, int64_t* n_pairs, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (n < 0 || capacity < 0 || !n_pairs || !camera_ok(cam)) return GS_ERR_INVALID_ARG;
+  if (n >= kMaxGaussians || !camera_fits(cam)) return GS_ERR_OVERFLOW;
+  if (n > 0 && !projected_ok(proj)) return GS_ERR_INVALID_ARG;
+  if (keys && !vals) return GS_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < bin_workspace_bytes(n)) return GS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_bin_count(n, proj.n_tiles, workspace, s);
+  if (e != hipSuccess) return GS_ERR_HIP;
+  uint64_t total = 0;
+  if (hipMemcpyAsync(&total, bin_total_ptr(n, workspace), sizeof total, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return GS_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return GS_ERR_HIP;
+  if (total > (uint64_t)INT64_MAX) return GS_ERR_OVERFLOW;
+  *n_pairs = (int64_t)total;
+  if (!keys) return GS_OK;
+  if ((int64_t)total > capacity) return GS_ERR_CAPACITY;
+  const DevCamera d = dev_camera(cam);
+  return hip_status(launch_bin_emit(n, proj, d.tiles_x, workspace, keys, vals, s));
+}
+
+gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
+                       uint32_t* vals_tmp, int64_t* tile_ranges, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (n_pairs < 0 || num_tiles < 1 || !tile_ranges) return GS_ERR_INVALID_ARG;
+  if (n_pairs > 0 && (!keys || !vals || !keys_tmp || !vals_tmp)) return GS_ERR_INVALID_ARG;
+  if (n_pairs >= ((int64_t)1 << 62)) return GS_ERR_OVERFLOW;
+  if (!workspace || workspace_bytes < sort_workspace_bytes(n_pairs, num_tiles)) return GS_ERR_WORKSPACE;
+  return hip_status(launch_sort(n_pairs, num_tiles, keys, vals, keys_tmp, vals_tmp, tile_ranges, workspace,
+                                static_cast<hipStream_t>(stream)));
+}
+
+gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_vals, const int64_t* tile_ranges,
+                        const gs_camera* cam, const float bg[3], float* image, float* final_T,
+                        uint32_t* n_contrib, void* stream) {
+  if (n < 0 || !camera_ok(cam) || !bg || !image || !final_T || !n_contrib || !tile_ranges) return GS_ERR_INVALID_ARG;
+  if (n >= kMaxGaussians || !camera_fits(cam)) return GS_ERR_OVERFLOW;
+  if (n > 0 && (!projected_ok(proj) || !sorted_vals)) return GS_ERR_INVALID_ARG;
+  const DevCamera d = dev_camera(cam);
+  return hip_status(launch_render_fwd(proj, sorted_vals, tile_ranges, d, bg, image, final_T, n_contrib,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, const float* quats,
+                        const float* opacities, const float* sh, int32_t sh_degree, const gs_camera* cam,
+                        gs_projected proj, const uint32_t* sorted_vals, const int64_t* tile_ranges,
+                        const float bg[3], const float* final_T, const uint32_t* n_contrib,
+                        const float* dL_dimage, gs_grads out, float* densify_accum, int32_t* densify_denom,
+                        void* stream) {
+  (void)opacities;
+  if (n < 0 || sh_degree < 0 || sh_degree > 3 || !camera_ok(cam) || !bg || !final_T || !n_contrib ||
+      !dL_dimage || !tile_ranges)
+    return GS_ERR_INVALID_ARG;
+  if (n >= kMaxGaussians || !camera_fits(cam)) return GS_ERR_OVERFLOW;
+  if (n == 0) return GS_OK;
+  if (!means || !scales || !quats || !sh || !projected_ok(proj) || !sorted_vals) return GS_ERR_INVALID_ARG;
+  if (!out.grad_screen || !out.dmeans || !out.dscales || !out.dquats || !out.dsh) return GS_ERR_INVALID_ARG;
+  const DevCamera d = dev_camera(cam);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_fill_u32(out.grad_screen, n * GS_GRAD_SCREEN, 0u, s);
+  if (e == hipSuccess)
+    e = launch_render_bwd(proj, sorted_vals, tile_ranges, d, bg, final_T, n_contrib, dL_dimage, out.grad_screen, s);
+  if (e == hipSuccess)
+    e = launch_project_bwd(n, means, scales, quats, sh, sh_degree, d, proj, out, densify_accum, densify_denom, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,463 @@
+// gs_project.hip -- projection of 3D Gaussians to screen (forward) and the per-Gaussian
+// chain rule back to the 3D parameters (backward), for gfx950.
+//
+// "Implementing Better Gaussian Splatting in Julia" (pwwt.cn) s3.1: a Gaussian is a
+// centre, a scale and a quaternion rotation (the covariance is built from them, so it
+// stays positive semi-definite), an opacity and a colour; s3.2: the centre goes to camera
+// then pixel coordinates and the 3D covariance is projected through the Jacobian of the
+// perspective map.  "Better Gaussian Splatting in Julia" (lshu.cn) s3.1: colour from SH
+// coefficients whose count depends on the degree.  The formulas (EWA 2D covariance, real
+// SH) are the textbook ones; the pages omit them.
+//
+// Memory: SoA inputs read once, coalesced.  SH rows (up to 192 B per Gaussian) are staged
+// through LDS with an odd float4 row stride so each lane then reads its own row without
+// bank conflicts.  The binning-critical geometry (camera-space mean, 2D covariance,
+// support, pixel box) is evaluated in float64 and rounded once; colour is float32.
+#include "gs_device.h"
+#include "gs_sh.h"
+
+namespace gs {
+
+constexpr int kProjBlock = 256;
+
+template <int L>
+struct ShLayout {
+  static constexpr int K = (L + 1) * (L + 1);
+  static constexpr int ROW = 3 * K;  // floats per Gaussian
+  static constexpr bool V4 = (ROW % 4) == 0;
+  // odd stride in the unit the rows are read with (float4 or float): conflict-free
+  static constexpr int STRIDE = V4 ? (((ROW / 4) & 1) ? ROW : ROW + 4) : ((ROW & 1) ? ROW : ROW + 1);
+};
+
+// Coalesced copy of `cnt` SH rows from global memory into LDS rows of STRIDE floats.
+template <int L>
+__device__ __forceinline__ void load_sh_rows(const float* __restrict__ src, int cnt, float* s_sh) {
+  using S = ShLayout<L>;
+  if constexpr (S::V4) {
+    constexpr int R4 = S::ROW / 4;
+    const float4* s4 = reinterpret_cast<const float4*>(src);
+    const int total = cnt * R4;
+    float4 tmp[R4];
+#pragma unroll
+    for (int it = 0; it < R4; ++it) {
+      const int f = it * kProjBlock + (int)threadIdx.x;
+      tmp[it] = f < total ? s4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int it = 0; it < R4; ++it) {
+      const int f = it * kProjBlock + (int)threadIdx.x;
+      if (f < total) {
+        const int g = f / R4, c = f - g * R4;
+        *reinterpret_cast<float4*>(s_sh + g * S::STRIDE + 4 * c) = tmp[it];
+      }
+    }
+  } else {
+    const int total = cnt * S::ROW;
+    for (int it = 0; it < S::ROW; ++it) {
+      const int f = it * kProjBlock + (int)threadIdx.x;
+      if (f < total) {
+        const int g = f / S::ROW, c = f - g * S::ROW;
+        s_sh[g * S::STRIDE + c] = src[f];
+      }
+    }
+  }
+}
+
+// Coalesced copy of `cnt` LDS rows back to global memory.
+template <int L>
+__device__ __forceinline__ void store_sh_rows(float* __restrict__ dst, int cnt, const float* s_sh) {
+  using S = ShLayout<L>;
+  if constexpr (S::V4) {
+    constexpr int R4 = S::ROW / 4;
+    float4* d4 = reinterpret_cast<float4*>(dst);
+    const int total = cnt * R4;
+#pragma unroll
+    for (int it = 0; it < R4; ++it) {
+      const int f = it * kProjBlock + (int)threadIdx.x;
+      if (f < total) {
+        const int g = f / R4, c = f - g * R4;
+        d4[f] = *reinterpret_cast<const float4*>(s_sh + g * S::STRIDE + 4 * c);
+      }
+    }
+  } else {
+    const int total = cnt * S::ROW;
+    for (int it = 0; it < S::ROW; ++it) {
+      const int f = it * kProjBlock + (int)threadIdx.x;
+      if (f < total) {
+        const int g = f / S::ROW, c = f - g * S::ROW;
+        dst[f] = s_sh[g * S::STRIDE + c];
+      }
+    }
+  }
+}
+
+// This lane's SH row from LDS into registers.
+template <int L>
+__device__ __forceinline__ void read_row(const float* s_sh, int tid, float* coef) {
+  using S = ShLayout<L>;
+  const float* row = s_sh + tid * S::STRIDE;
+  if constexpr (S::V4) {
+#pragma unroll
+    for (int c = 0; c < S::ROW / 4; ++c) {
+      const float4 q = reinterpret_cast<const float4*>(row)[c];
+      coef[4 * c] = q.x; coef[4 * c + 1] = q.y; coef[4 * c + 2] = q.z; coef[4 * c + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < S::ROW; ++c) coef[c] = row[c];
+  }
+}
+
+// Geometry shared by the forward and the backward, float64.
+struct Geom {
+  double t[3];      // camera-space mean
+  double qn[4];     // unit quaternion
+  double qlen;      // |q| of the input
+  double Rq[9];     // rotation of qn
+  double M[9];      // Rq diag(s)
+  double S[6];      // Sigma: xx, xy, xz, yy, yz, zz
+};
+
+__device__ __forceinline__ void geom(const DevCamera& cam, double mx, double my, double mz,
+                                     const double s[3], const float4 qf, Geom& g) {
+  const double* W = cam.R;
+  g.t[0] = W[0] * mx + W[1] * my + W[2] * mz + cam.t[0];
+  g.t[1] = W[3] * mx + W[4] * my + W[5] * mz + cam.t[1];
+  g.t[2] = W[6] * mx + W[7] * my + W[8] * mz + cam.t[2];
+  const double qw = qf.x, qx = qf.y, qy = qf.z, qz = qf.w;
+  g.qlen = sqrt(qw * qw + qx * qx + qy * qy + qz * qz);
+  const double il = 1.0 / g.qlen;
+  const double w = qw * il, x = qx * il, y = qy * il, z = qz * il;
+  g.qn[0] = w; g.qn[1] = x; g.qn[2] = y; g.qn[3] = z;
+  double* R = g.Rq;
+  R[0] = 1.0 - 2.0 * (y * y + z * z); R[1] = 2.0 * (x * y - w * z); R[2] = 2.0 * (x * z + w * y);
+  R[3] = 2.0 * (x * y + w * z); R[4] = 1.0 - 2.0 * (x * x + z * z); R[5] = 2.0 * (y * z - w * x);
+  R[6] = 2.0 * (x * z - w * y); R[7] = 2.0 * (y * z + w * x); R[8] = 1.0 - 2.0 * (x * x + y * y);
+#pragma unroll
+  for (int r = 0; r < 3; ++r)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) g.M[3 * r + c] = R[3 * r + c] * s[c];
+  const double* M = g.M;
+  g.S[0] = M[0] * M[0] + M[1] * M[1] + M[2] * M[2];
+  g.S[1] = M[0] * M[3] + M[1] * M[4] + M[2] * M[5];
+  g.S[2] = M[0] * M[6] + M[1] * M[7] + M[2] * M[8];
+  g.S[3] = M[3] * M[3] + M[4] * M[4] + M[5] * M[5];
+  g.S[4] = M[3] * M[6] + M[4] * M[7] + M[5] * M[8];
+  g.S[5] = M[6] * M[6] + M[7] * M[7] + M[8] * M[8];
+}
+
+__device__ __forceinline__ void sym_mul(const double S[6], const double v[3], double out[3]) {
+  out[0] = S[0] * v[0] + S[1] * v[1] + S[2] * v[2];
+  out[1] = S[1] * v[0] + S[3] * v[1] + S[4] * v[2];
+  out[2] = S[2] * v[0] + S[4] * v[1] + S[5] * v[2];
+}
+
+// Rows of T = J W, J the perspective Jacobian at the camera-space mean.
+__device__ __forceinline__ void proj_rows(const DevCamera& cam, const double t[3], double t0[3],
+                                          double t1[3]) {
+  const double iz = 1.0 / t[2];
+  const double j00 = cam.fx * iz, j02 = -cam.fx * t[0] * iz * iz;
+  const double j11 = cam.fy * iz, j12 = -cam.fy * t[1] * iz * iz;
+  const double* W = cam.R;
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    t0[c] = j00 * W[c] + j02 * W[6 + c];
+    t1[c] = j11 * W[3 + c] + j12 * W[6 + c];
+  }
+}
+
+template <int L>
+__global__ __launch_bounds__(kProjBlock) void k_project(
+    int64_t n, const float* __restrict__ means, const float* __restrict__ scales,
+    const float4* __restrict__ quats, const float* __restrict__ opac, const float* __restrict__ sh,
+    const DevCamera cam, float4* __restrict__ rec, float* __restrict__ depth_out,
+    ushort4* __restrict__ rect_out, uint32_t* __restrict__ ntiles_out, uint8_t* __restrict__ clamp_out) {
+  using S = ShLayout<L>;
+  __shared__ float s_sh[kProjBlock * S::STRIDE];
+  const int64_t base = (int64_t)blockIdx.x * kProjBlock;
+  const int cnt = (int)min((int64_t)kProjBlock, n - base);
+  load_sh_rows<L>(sh + base * S::ROW, cnt, s_sh);
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid >= cnt) return;
+  const int64_t i = base + tid;
+
+  const double mx = means[3 * i], my = means[3 * i + 1], mz = means[3 * i + 2];
+  const double sc[3] = {scales[3 * i], scales[3 * i + 1], scales[3 * i + 2]};
+  Geom g;
+  geom(cam, mx, my, mz, sc, quats[i], g);
+  depth_out[i] = (float)g.t[2];
+
+  // view-dependent colour: 0.5 + sum_k Y_k(d) sh_k, clamped at 0
+  float coef[S::ROW];
+  read_row<L>(s_sh, tid, coef);
+  const double vx = mx - cam.campos[0], vy = my - cam.campos[1], vz = mz - cam.campos[2];
+  const double il = 1.0 / sqrt(vx * vx + vy * vy + vz * vz);
+  float Y[S::K];
+  sh_basis<L>((float)(vx * il), (float)(vy * il), (float)(vz * il), Y);
+  float col[3];
+  uint32_t cl = 0;
+#pragma unroll
+  for (int ch = 0; ch < 3; ++ch) {
+    float acc = 0.5f;
+#pragma unroll
+    for (int k = 0; k < S::K; ++k) acc = fmaf(Y[k], coef[3 * k + ch], acc);
+    if (acc < 0.0f) { cl |= 1u << ch; acc = 0.0f; }
+    col[ch] = acc;
+  }
+  clamp_out[i] = (uint8_t)cl;
+
+  float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0, r2 = r0;
+  ushort4 rc = make_ushort4(0, 0, 0, 0);
+  uint32_t nt = 0;
+  if (g.t[2] > cam.near_z) {  // NaN fails
+    double t0[3], t1[3], St0[3], St1[3];
+    proj_rows(cam, g.t, t0, t1);
+    sym_mul(g.S, t0, St0);
+    sym_mul(g.S, t1, St1);
+    const double a = t0[0] * St0[0] + t0[1] * St0[1] + t0[2] * St0[2];
+    const double b = t0[0] * St1[0] + t0[1] * St1[1] + t0[2] * St1[2];
+    const double c = t1[0] * St1[0] + t1[1] * St1[1] + t1[2] * St1[2];
+    const double det = a * c - b * b;
+    const double o = opac[i];
+    if (det > 0.0 && o >= (double)kAlphaMin) {
+      const double iz = 1.0 / g.t[2];
+      const double u = cam.fx * g.t[0] * iz + cam.cx;
+      const double v = cam.fy * g.t[1] * iz + cam.cy;
+      // support: alpha >= 1/255  <=>  q <= tau; the ellipse's half extents
+      const double tau = 2.0 * log(o / (double)kAlphaMin);
+      const double ex = sqrt(tau * a), ey = sqrt(tau * c);
+      double lx = ceil(u - ex - 0.5), hx = floor(u + ex - 0.5);
+      double ly = ceil(v - ey - 0.5), hy = floor(v + ey - 0.5);
+      if (lx < 0.0) lx = 0.0;
+      if (ly < 0.0) ly = 0.0;
+      if (hx > (double)(cam.width - 1)) hx = (double)(cam.width - 1);
+      if (hy > (double)(cam.height - 1)) hy = (double)(cam.height - 1);
+      if (lx <= hx && ly <= hy) {
+        const uint32_t px0 = (uint32_t)lx, px1 = (uint32_t)hx, py0 = (uint32_t)ly, py1 = (uint32_t)hy;
+        const double idet = 1.0 / det;
+        r0 = make_float4((float)u, (float)v, (float)(c * idet), (float)(-b * idet));
+        r1 = make_float4((float)(a * idet), (float)o, col[0], col[1]);
+        r2 = make_float4(col[2], __uint_as_float(px0 | (px1 << 16)), __uint_as_float(py0 | (py1 << 16)), 0.0f);
+        rc = make_ushort4((uint16_t)(px0 >> 4), (uint16_t)(px1 >> 4), (uint16_t)(py0 >> 4), (uint16_t)(py1 >> 4));
+        nt = ((px1 >> 4) - (px0 >> 4) + 1) * ((py1 >> 4) - (py0 >> 4) + 1);
+      }
+    }
+  }
+  rec[3 * i] = r0;
+  rec[3 * i + 1] = r1;
+  rec[3 * i + 2] = r2;
+  rect_out[i] = rc;
+  ntiles_out[i] = nt;
+}
+
+// Backward of the projection for one Gaussian (float64 geometry), plus the densification
+// statistics of "Enabling the absolute-gradient strategy in 3D Gaussian Splatting"
+// (jsqmd.com) s3.1: accumulate the view-space gradient norm and the absolute gradient,
+// and count the views in which the Gaussian was visible.
+template <int L>
+__global__ __launch_bounds__(kProjBlock) void k_project_bwd(
+    int64_t n, const float* __restrict__ means, const float* __restrict__ scales,
+    const float4* __restrict__ quats, const float* __restrict__ sh, const DevCamera cam,
+    const uint32_t* __restrict__ ntiles, const uint8_t* __restrict__ clampb,
+    const float* __restrict__ gscreen, float* __restrict__ dmeans, float* __restrict__ dscales,
+    float4* __restrict__ dquats, float* __restrict__ dsh, float2* __restrict__ accum,
+    int32_t* __restrict__ denom) {
+  using S = ShLayout<L>;
+  __shared__ float s_sh[kProjBlock * S::STRIDE];
+  const int64_t base = (int64_t)blockIdx.x * kProjBlock;
+  const int cnt = (int)min((int64_t)kProjBlock, n - base);
+  load_sh_rows<L>(sh + base * S::ROW, cnt, s_sh);
+  __syncthreads();
+  const int tid = threadIdx.x;
+  if (tid < cnt) {
+    const int64_t i = base + tid;
+    const bool vis = ntiles[i] > 0;
+    float gsv[GS_GRAD_SCREEN];
+#pragma unroll
+    for (int e = 0; e < GS_GRAD_SCREEN; ++e) gsv[e] = gscreen[GS_GRAD_SCREEN * i + e];
+    float coef[S::ROW];
+    read_row<L>(s_sh, tid, coef);
+    float drow[S::ROW];
+    double dmu[3] = {0.0, 0.0, 0.0}, ds[3] = {0.0, 0.0, 0.0}, dq[4] = {0.0, 0.0, 0.0, 0.0};
+    const double mx = means[3 * i], my = means[3 * i + 1], mz = means[3 * i + 2];
+    if (vis) {
+      // colour: rgb = max(raw, 0); the clamp stops the gradient
+      const uint32_t cl = clampb[i];
+      float draw[3];
+#pragma unroll
+      for (int ch = 0; ch < 3; ++ch) draw[ch] = (cl >> ch) & 1u ? 0.0f : gsv[6 + ch];
+      const double vx = mx - cam.campos[0], vy = my - cam.campos[1], vz = mz - cam.campos[2];
+      const double dist = sqrt(vx * vx + vy * vy + vz * vz);
+      const double il = 1.0 / dist;
+      const float dx = (float)(vx * il), dy = (float)(vy * il), dz = (float)(vz * il);
+      float Y[S::K];
+      float dY[S::K][3];
+      sh_basis<L>(dx, dy, dz, Y);
+      sh_basis_grad<L>(dx, dy, dz, dY);
+      float dd[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < S::K; ++k) {
+        float w = 0.f;
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch) {
+          drow[3 * k + ch] = Y[k] * draw[ch];
+          w = fmaf(coef[3 * k + ch], draw[ch], w);
+        }
+        dd[0] = fmaf(w, dY[k][0], dd[0]);
+        dd[1] = fmaf(w, dY[k][1], dd[1]);
+        dd[2] = fmaf(w, dY[k][2], dd[2]);
+      }
+      // d = v/|v|: dd/dmu = (I - d d^T)/|v|
+      const double pr = (double)dd[0] * dx + (double)dd[1] * dy + (double)dd[2] * dz;
+      dmu[0] = ((double)dd[0] - pr * dx) * il;
+      dmu[1] = ((double)dd[1] - pr * dy) * il;
+      dmu[2] = ((double)dd[2] - pr * dz) * il;
+
+      const double sc[3] = {scales[3 * i], scales[3 * i + 1], scales[3 * i + 2]};
+      Geom g;
+      geom(cam, mx, my, mz, sc, quats[i], g);
+      double t0[3], t1[3], St0[3], St1[3];
+      proj_rows(cam, g.t, t0, t1);
+      sym_mul(g.S, t0, St0);
+      sym_mul(g.S, t1, St1);
+      const double a = t0[0] * St0[0] + t0[1] * St0[1] + t0[2] * St0[2];
+      const double b = t0[0] * St1[0] + t0[1] * St1[1] + t0[2] * St1[2];
+      const double c = t1[0] * St1[0] + t1[1] * St1[1] + t1[2] * St1[2];
+      const double det = a * c - b * b, id2 = 1.0 / (det * det);
+      // conic (A, B, C) = (c, -b, a)/det
+      const double gA = gsv[2], gB = gsv[3], gC = gsv[4];
+      const double da = (-c * c * gA + b * c * gB - b * b * gC) * id2;
+      const double db = (2.0 * b * c * gA - (a * c + b * b) * gB + 2.0 * a * b * gC) * id2;
+      const double dc = (-b * b * gA + a * b * gB - a * a * gC) * id2;
+      // a = t0.S t0, b = t0.S t1, c = t1.S t1
+      double dT0[3], dT1[3];
+#pragma unroll
+      for (int e = 0; e < 3; ++e) {
+        dT0[e] = 2.0 * da * St0[e] + db * St1[e];
+        dT1[e] = db * St0[e] + 2.0 * dc * St1[e];
+      }
+      // T = J W  ->  dJ = dT W^T (only the non-zero entries of J matter)
+      const double* W = cam.R;
+      const double dJ00 = dT0[0] * W[0] + dT0[1] * W[1] + dT0[2] * W[2];
+      const double dJ02 = dT0[0] * W[6] + dT0[1] * W[7] + dT0[2] * W[8];
+      const double dJ11 = dT1[0] * W[3] + dT1[1] * W[4] + dT1[2] * W[5];
+      const double dJ12 = dT1[0] * W[6] + dT1[1] * W[7] + dT1[2] * W[8];
+      const double x = g.t[0], y = g.t[1], z = g.t[2], iz = 1.0 / z, iz2 = iz * iz, iz3 = iz2 * iz;
+      const double fx = cam.fx, fy = cam.fy;
+      const double du = gsv[0], dv = gsv[1];
+      double dt[3];
+      dt[0] = -fx * iz2 * dJ02 + du * fx * iz;
+      dt[1] = -fy * iz2 * dJ12 + dv * fy * iz;
+      dt[2] = -fx * iz2 * dJ00 + 2.0 * fx * x * iz3 * dJ02 - fy * iz2 * dJ11 + 2.0 * fy * y * iz3 * dJ12 -
+              du * fx * x * iz2 - dv * fy * y * iz2;
+#pragma unroll
+      for (int e = 0; e < 3; ++e) dmu[e] += W[e] * dt[0] + W[3 + e] * dt[1] + W[6 + e] * dt[2];
+      // dSigma (full matrix) = da t0 t0^T + db t0 t1^T + dc t1 t1^T; Sigma = M M^T
+      double dSs[9];  // dSigma + dSigma^T
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 3; ++cc)
+          dSs[3 * r + cc] = 2.0 * da * t0[r] * t0[cc] + db * (t0[r] * t1[cc] + t1[r] * t0[cc]) +
+                            2.0 * dc * t1[r] * t1[cc];
+      double dR[9];
+#pragma unroll
+      for (int r = 0; r < 3; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 3; ++cc) {
+          const double dM = dSs[3 * r] * g.M[cc] + dSs[3 * r + 1] * g.M[3 + cc] + dSs[3 * r + 2] * g.M[6 + cc];
+          ds[cc] += dM * g.Rq[3 * r + cc];
+          dR[3 * r + cc] = dM * sc[cc];
+        }
+      const double w = g.qn[0], qx = g.qn[1], qy = g.qn[2], qz = g.qn[3];
+      double dqn[4];
+      dqn[0] = 2.0 * (-qz * dR[1] + qy * dR[2] + qz * dR[3] - qx * dR[5] - qy * dR[6] + qx * dR[7]);
+      dqn[1] = 2.0 * (qy * dR[1] + qz * dR[2] + qy * dR[3] - 2.0 * qx * dR[4] - w * dR[5] + qz * dR[6] +
+                      w * dR[7] - 2.0 * qx * dR[8]);
+      dqn[2] = 2.0 * (-2.0 * qy * dR[0] + qx * dR[1] + w * dR[2] + qx * dR[3] + qz * dR[5] - w * dR[6] +
+                      qz * dR[7] - 2.0 * qy * dR[8]);
+      dqn[3] = 2.0 * (-2.0 * qz * dR[0] - w * dR[1] + qx * dR[2] + w * dR[3] - 2.0 * qz * dR[4] + qy * dR[5] +
+                      qx * dR[6] + qy * dR[7]);
+      // qn = q/|q|
+      const double pq = dqn[0] * w + dqn[1] * qx + dqn[2] * qy + dqn[3] * qz;
+      const double iq = 1.0 / g.qlen;
+      dq[0] = (dqn[0] - pq * w) * iq;
+      dq[1] = (dqn[1] - pq * qx) * iq;
+      dq[2] = (dqn[2] - pq * qy) * iq;
+      dq[3] = (dqn[3] - pq * qz) * iq;
+      if (accum) {
+        float2 acc = accum[i];
+        acc.x += (float)sqrt(du * du + dv * dv);
+        acc.y += gsv[9];
+        accum[i] = acc;
+      }
+      if (denom) denom[i] += 1;
+    } else {
+#pragma unroll
+      for (int k = 0; k < S::ROW; ++k) drow[k] = 0.0f;
+    }
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      dmeans[3 * i + e] = (float)dmu[e];
+      dscales[3 * i + e] = (float)ds[e];
+    }
+    dquats[i] = make_float4((float)dq[0], (float)dq[1], (float)dq[2], (float)dq[3]);
+    // this lane's dsh row replaces its own (already read) SH row in LDS
+    float* row = s_sh + tid * S::STRIDE;
+#pragma unroll
+    for (int k = 0; k < S::ROW; ++k) row[k] = drow[k];
+  }
+  __syncthreads();
+  store_sh_rows<L>(dsh + base * S::ROW, cnt, s_sh);
+}
+
+template <int L>
+static hipError_t launch_project_L(int64_t n, const float* means, const float* scales,
+                                   const float* quats, const float* opac, const float* sh,
+                                   const DevCamera& cam, const gs_projected& out, hipStream_t s) {
+  const unsigned blocks = (unsigned)((n + kProjBlock - 1) / kProjBlock);
+  k_project<L><<<blocks, kProjBlock, 0, s>>>(
+      n, means, scales, reinterpret_cast<const float4*>(quats), opac, sh, cam,
+      reinterpret_cast<float4*>(out.rec), out.depth, reinterpret_cast<ushort4*>(out.rect), out.n_tiles,
+      out.clamp);
+  return hipGetLastError();
+}
+
+hipError_t launch_project(int64_t n, const float* means, const float* scales, const float* quats,
+                          const float* opac, const float* sh, int L, const DevCamera& cam,
+                          const gs_projected& out, hipStream_t s) {
+  switch (L) {
+    case 0: return launch_project_L<0>(n, means, scales, quats, opac, sh, cam, out, s);
+    case 1: return launch_project_L<1>(n, means, scales, quats, opac, sh, cam, out, s);
+    case 2: return launch_project_L<2>(n, means, scales, quats, opac, sh, cam, out, s);
+    default: return launch_project_L<3>(n, means, scales, quats, opac, sh, cam, out, s);
+  }
+}
+
+template <int L>
+static hipError_t launch_project_bwd_L(int64_t n, const float* means, const float* scales,
+                                       const float* quats, const float* sh, const DevCamera& cam,
+                                       const gs_projected& proj, const gs_grads& gr, float* accum,
+                                       int32_t* denom, hipStream_t s) {
+  const unsigned blocks = (unsigned)((n + kProjBlock - 1) / kProjBlock);
+  k_project_bwd<L><<<blocks, kProjBlock, 0, s>>>(
+      n, means, scales, reinterpret_cast<const float4*>(quats), sh, cam, proj.n_tiles, proj.clamp,
+      gr.grad_screen, gr.dmeans, gr.dscales, reinterpret_cast<float4*>(gr.dquats), gr.dsh,
+      reinterpret_cast<float2*>(accum), denom);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_bwd(int64_t n, const float* means, const float* scales,
+                              const float* quats, const float* sh, int L, const DevCamera& cam,
+                              const gs_projected& proj, const gs_grads& gr, float* accum,
+                              int32_t* denom, hipStream_t s) {
+  switch (L) {
+    case 0: return launch_project_bwd_L<0>(n, means, scales, quats, sh, cam, proj, gr, accum, denom, s);
+    case 1: return launch_project_bwd_L<1>(n, means, scales, quats, sh, cam, proj, gr, accum, denom, s);
+    case 2: return launch_project_bwd_L<2>(n, means, scales, quats, sh, cam, proj, gr, accum, denom, s);
+    default: return launch_project_bwd_L<3>(n, means, scales, quats, sh, cam, proj, gr, accum, denom, s);
+  }
+}
+
+}  // namespace gs

@@ -1,0 +1,302 @@
+// gs_sort.hip -- stable LSD radix sort of (tile | depth) keys with single-pass
+// ("onesweep") digit passes, and per-tile range extraction, for gfx950.
+//
+// "Better Gaussian Splatting in Julia" (lshu.cn) s3.2 (sort_by_depth!) and
+// "Implementing Better Gaussian Splatting in Julia" (pwwt.cn) s3.3: each tile's list is
+// ordered by the depth of the Gaussian centres.  Sorting the 64-bit key tile << 32 |
+// bits(depth) orders by tile, then depth (positive floats order like their bit patterns);
+// the sort is stable, so pairs emitted in Gaussian-id order keep id order among equal keys.
+//
+// Structure (the decoupled look-back scheme of Merrill & Garland, and the single-pass radix
+// sort of Adinets & Merrill, re-designed for 64-wide wavefronts):
+//   k_sort_hist   one read of the keys: histograms of every 8-bit digit at once
+//   k_sort_plan   exclusive scan of each histogram (global digit bases); marks digits that
+//                 are constant over all keys (those passes are skipped) and assigns the
+//                 ping-pong buffers on the device, so no host round trip is needed
+//   k_onesweep    per pass: each workgroup takes a 4096-key partition by atomic ticket,
+//                 ranks its keys stably (wavefront ballots match equal digits; per-wave
+//                 digit counters in LDS), publishes per-digit counts and resolves its
+//                 global offsets by looking back over earlier partitions' published
+//                 counts, reorders the partition in LDS by digit and writes each digit's
+//                 run contiguously
+//   k_sort_copy   moves the result back to keys/vals after an odd number of passes
+//   k_ranges      [first, last + 1) of every tile from the sorted keys
+#include "gs_device.h"
+
+namespace gs {
+
+constexpr int kSortBlock = 256;
+constexpr int kSortKPT = 16;
+constexpr int kSortPart = kSortBlock * kSortKPT;  // keys per partition
+constexpr int kRadix = 256;
+constexpr int kMaxPasses = 8;
+constexpr uint64_t kFlagAgg = 1ull << 62;    // partition's own count published
+constexpr uint64_t kFlagPre = 2ull << 62;    // inclusive prefix through this partition
+constexpr uint64_t kValMask = (1ull << 62) - 1;
+
+// Workspace layout (bytes from the workspace start).
+struct SortLayout {
+  size_t hist, base, plan, tickets, status, total;
+  int64_t parts;
+};
+
+SortLayout sort_layout(int64_t n_pairs, int passes) {
+  SortLayout l;
+  l.parts = (n_pairs + kSortPart - 1) / kSortPart;
+  l.hist = 0;
+  l.base = l.hist + sizeof(uint64_t) * kMaxPasses * kRadix;
+  l.plan = l.base + sizeof(uint64_t) * kMaxPasses * kRadix;
+  l.tickets = l.plan + 256;
+  l.status = l.tickets + 256;
+  l.total = l.status + sizeof(uint64_t) * (size_t)passes * (size_t)l.parts * kRadix;
+  return l;
+}
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t count, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  const int64_t want = (count + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
+  k_fill_u32<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), count, v);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kSortBlock) void k_sort_hist(const uint64_t* __restrict__ keys, int64_t P,
+                                                          int passes, uint64_t* __restrict__ hist) {
+  __shared__ uint32_t s_h[kMaxPasses * kRadix];
+  for (int i = threadIdx.x; i < passes * kRadix; i += kSortBlock) s_h[i] = 0;
+  __syncthreads();
+  for (int64_t i = (int64_t)blockIdx.x * kSortBlock + threadIdx.x; i < P; i += (int64_t)gridDim.x * kSortBlock) {
+    const uint64_t k = keys[i];
+    for (int p = 0; p < passes; ++p) atomicAdd(&s_h[p * kRadix + ((k >> (8 * p)) & 0xFF)], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < passes * kRadix; i += kSortBlock)
+    if (s_h[i]) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[i]), (unsigned long long)s_h[i]);
+}
+
+// plan[p] = -1 (skip), 0 (keys -> tmp) or 1 (tmp -> keys); plan[kMaxPasses] = buffer
+// holding the result (0 = keys, 1 = tmp).
+__global__ __launch_bounds__(kRadix) void k_sort_plan(const uint64_t* __restrict__ hist, uint64_t* __restrict__ base,
+                                                      int32_t* __restrict__ plan, int passes, uint64_t P) {
+  __shared__ uint64_t s_w[kRadix / kWave];
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  int cur = 0;
+  for (int p = 0; p < passes; ++p) {
+    const uint64_t h = hist[p * kRadix + tid];
+    const uint64_t inc = wave_inclusive_scan(h);
+    if (lane == kWave - 1) s_w[wave] = inc;
+    __syncthreads();
+    uint64_t pre = inc - h;
+    for (int w = 0; w < wave; ++w) pre += s_w[w];
+    base[p * kRadix + tid] = pre;
+    const bool trivial = __syncthreads_or(h == P) != 0;
+    if (tid == 0) plan[p] = trivial ? -1 : cur;
+    if (!trivial) cur ^= 1;
+  }
+  if (tid == 0) plan[kMaxPasses] = cur;
+}
+
+__device__ __forceinline__ uint64_t status_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void status_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kSortBlock) void k_onesweep(
+    uint64_t* __restrict__ k0, uint32_t* __restrict__ v0, uint64_t* __restrict__ k1, uint32_t* __restrict__ v1,
+    int64_t P, int pass, int bits, const int32_t* __restrict__ plan, const uint64_t* __restrict__ dbase,
+    uint64_t* __restrict__ status, uint32_t* __restrict__ tickets) {
+  const int mode = plan[pass];
+  if (mode < 0) return;  // digit constant over all keys: nothing to do
+  const uint64_t* kin = mode ? k1 : k0;
+  const uint32_t* vin = mode ? v1 : v0;
+  uint64_t* kout = mode ? k0 : k1;
+  uint32_t* vout = mode ? v0 : v1;
+  const int shift = 8 * pass;
+  const uint32_t dmask = (1u << bits) - 1u;
+
+  __shared__ uint64_t s_keys[kSortPart];
+  __shared__ uint32_t s_vals[kSortPart];
+  __shared__ uint32_t s_wh[kSortBlock / kWave][kRadix];  // per-wave digit counters, then offsets
+  __shared__ uint32_t s_lbase[kRadix];                   // partition-local digit starts
+  __shared__ uint64_t s_gbase[kRadix];                   // global digit starts for this partition
+  __shared__ uint32_t s_w[kSortBlock / kWave];
+  __shared__ uint32_t s_part;
+
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  if (tid == 0) s_part = atomicAdd(tickets + pass, 1u);
+  for (int i = tid; i < (kSortBlock / kWave) * kRadix; i += kSortBlock) (&s_wh[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t part = s_part;
+  const int64_t base = part * kSortPart;
+
+  // wave-striped: wave w owns keys [w*1024, (w+1)*1024) of the partition, in order
+  uint64_t key[kSortKPT];
+  uint32_t val[kSortKPT];
+  uint32_t rank[kSortKPT];
+#pragma unroll
+  for (int j = 0; j < kSortKPT; ++j) {
+    const int64_t idx = base + wave * (kSortKPT * kWave) + j * kWave + lane;
+    key[j] = idx < P ? kin[idx] : ~0ull;
+    val[j] = idx < P ? vin[idx] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kSortKPT; ++j) {
+    const int64_t idx = base + wave * (kSortKPT * kWave) + j * kWave + lane;
+    const bool valid = idx < P;
+    const uint32_t d = (uint32_t)(key[j] >> shift) & dmask;
+    // lanes holding the same digit: intersect ballots of every digit bit
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t bb = __ballot(bit);
+      m &= bit ? bb : ~bb;
+    }
+    const uint32_t below = (uint32_t)__popcll(m & lanemask_lt());
+    uint32_t prev = 0;
+    if (valid) prev = s_wh[wave][d];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    rank[j] = prev + below;
+    if (valid && below == 0) s_wh[wave][d] = prev + (uint32_t)__popcll(m);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+
+  // thread d owns digit d: wave offsets, publish the partition's count
+  const int d = tid;
+  uint32_t tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSortBlock / kWave; ++w) {
+    const uint32_t c = s_wh[w][d];
+    s_wh[w][d] = tot;
+    tot += c;
+  }
+  uint64_t* my_status = status + part * kRadix + d;
+  status_store(my_status, (part == 0 ? kFlagPre : kFlagAgg) | (uint64_t)tot);
+  // partition-local exclusive scan over digits
+  {
+    const uint32_t inc = wave_inclusive_scan(tot);
+    if (lane == kWave - 1) s_w[wave] = inc;
+    __syncthreads();
+    uint32_t pre = inc - tot;
+    for (int w = 0; w < wave; ++w) pre += s_w[w];
+    s_lbase[d] = pre;
+  }
+  __syncthreads();
+  // reorder the partition by digit in LDS (stable)
+#pragma unroll
+  for (int j = 0; j < kSortKPT; ++j) {
+    const int64_t idx = base + wave * (kSortKPT * kWave) + j * kWave + lane;
+    if (idx < P) {
+      const uint32_t dd = (uint32_t)(key[j] >> shift) & dmask;
+      const uint32_t pos = s_lbase[dd] + s_wh[wave][dd] + rank[j];
+      s_keys[pos] = key[j];
+      s_vals[pos] = val[j];
+    }
+  }
+  // look back over earlier partitions for this digit's global offset
+  uint64_t excl = 0;
+  if (part > 0) {
+    int64_t p = part - 1;
+    while (true) {
+      const uint64_t sv = status_load(status + p * kRadix + d);
+      const uint64_t flag = sv & ~kValMask;
+      if (flag == 0) {
+        __builtin_amdgcn_s_sleep(1);
+        continue;
+      }
+      excl += sv & kValMask;
+      if (flag == kFlagPre) break;
+      --p;
+    }
+    status_store(my_status, kFlagPre | (excl + tot));
+  }
+  s_gbase[d] = dbase[d] + excl;
+  __syncthreads();
+  // write each digit's run contiguously
+  const int nvalid = (int)min((int64_t)kSortPart, P - base);
+  for (int i = tid; i < nvalid; i += kSortBlock) {
+    const uint64_t k = s_keys[i];
+    const uint32_t dd = (uint32_t)(k >> shift) & dmask;
+    const uint64_t g = s_gbase[dd] + (uint64_t)(i - (int)s_lbase[dd]);
+    kout[g] = k;
+    vout[g] = s_vals[i];
+  }
+}
+
+__global__ void k_sort_copy(const int32_t* __restrict__ plan, const uint64_t* __restrict__ k1,
+                            const uint32_t* __restrict__ v1, uint64_t* __restrict__ k0, uint32_t* __restrict__ v0,
+                            int64_t P) {
+  if (plan[kMaxPasses] == 0) return;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < P; i += (int64_t)gridDim.x * blockDim.x) {
+    k0[i] = k1[i];
+    v0[i] = v1[i];
+  }
+}
+
+__global__ void k_ranges(const uint64_t* __restrict__ keys, int64_t P, int64_t num_tiles,
+                         int64_t* __restrict__ ranges) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= P) return;
+  const uint64_t t = keys[i] >> 32;
+  if (t >= (uint64_t)num_tiles) return;
+  if (i == 0 || (keys[i - 1] >> 32) != t) ranges[2 * t] = i;
+  if (i == P - 1 || (keys[i + 1] >> 32) != t) ranges[2 * t + 1] = i + 1;
+}
+
+int sort_significant_bits(int64_t num_tiles) {
+  int tb = 0;
+  while (tb < 32 && ((int64_t)1 << tb) < num_tiles) ++tb;
+  return 32 + tb;
+}
+
+size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles) {
+  const int passes = (sort_significant_bits(num_tiles) + 7) / 8;
+  return sort_layout(n_pairs, passes).total;
+}
+
+hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
+                       uint32_t* vals_tmp, int64_t* ranges, void* ws, hipStream_t s) {
+  hipError_t e = launch_fill_u32(ranges, 4 * num_tiles, 0u, s);
+  if (e != hipSuccess || P == 0) return e;
+  const int sig = sort_significant_bits(num_tiles);
+  const int passes = (sig + 7) / 8;
+  const SortLayout l = sort_layout(P, passes);
+  char* w = static_cast<char*>(ws);
+  uint64_t* hist = reinterpret_cast<uint64_t*>(w + l.hist);
+  uint64_t* dbase = reinterpret_cast<uint64_t*>(w + l.base);
+  int32_t* plan = reinterpret_cast<int32_t*>(w + l.plan);
+  uint32_t* tickets = reinterpret_cast<uint32_t*>(w + l.tickets);
+  uint64_t* status = reinterpret_cast<uint64_t*>(w + l.status);
+  // zero histograms, plan, tickets and every pass's status words (no memset: capture-safe)
+  if ((e = launch_fill_u32(w, (int64_t)(l.total / 4), 0u, s)) != hipSuccess) return e;
+  {
+    const int64_t want = (P + kSortBlock * 16 - 1) / (kSortBlock * 16);
+    const unsigned blocks = (unsigned)(want < 2048 ? (want > 0 ? want : 1) : 2048);
+    k_sort_hist<<<blocks, kSortBlock, 0, s>>>(keys, P, passes, hist);
+  }
+  k_sort_plan<<<1, kRadix, 0, s>>>(hist, dbase, plan, passes, (uint64_t)P);
+  for (int p = 0; p < passes; ++p) {
+    const int bits = sig - 8 * p < 8 ? sig - 8 * p : 8;
+    k_onesweep<<<(unsigned)l.parts, kSortBlock, 0, s>>>(keys, vals, keys_tmp, vals_tmp, P, p, bits, plan,
+                                                      dbase + p * kRadix, status + (size_t)p * l.parts * kRadix,
+                                                      tickets);
+  }
+  {
+    const int64_t want = (P + 255) / 256;
+    const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+    k_sort_copy<<<blocks, 256, 0, s>>>(plan, keys_tmp, vals_tmp, keys, vals, P);
+  }
+  k_ranges<<<(unsigned)((P + 255) / 256), 256, 0, s>>>(keys, P, num_tiles, ranges);
+  return hipGetLastError();
+}
+
+}  // namespace gs

@@ -1,0 +1,246 @@
+"""ctypes binding of libgsraster (the C ABI in include/gs_raster.h).
+
+Argument marshalling only: torch provides device memory and the current stream; every
+step of the computation runs in the HIP kernels behind the C ABI.  Importing this module
+fails loudly when the library has not been built (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsraster.so")
+
+GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_OVERFLOW, GS_ERR_HIP, GS_ERR_WORKSPACE = range(6)
+TILE = 16
+REC_FLOATS = 12
+GRAD_SCREEN = 10
+
+EXPORTS = ("gs_project", "gs_workspace_bytes", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd",
+           "gs_render_bwd", "gs_status_string")
+
+
+class GsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib().gs_status_string(status).decode()} (status {status})")
+
+
+class GsCamera(C.Structure):
+    _fields_ = [("R", C.c_float * 9), ("t", C.c_float * 3), ("fx", C.c_float), ("fy", C.c_float),
+                ("cx", C.c_float), ("cy", C.c_float), ("width", C.c_int32), ("height", C.c_int32),
+                ("near_z", C.c_float)]
+
+
+class GsProjected(C.Structure):
+    _fields_ = [("rec", C.c_void_p), ("depth", C.c_void_p), ("rect", C.c_void_p),
+                ("n_tiles", C.c_void_p), ("clamp", C.c_void_p)]
+
+
+class GsGrads(C.Structure):
+    _fields_ = [("grad_screen", C.c_void_p), ("dmeans", C.c_void_p), ("dscales", C.c_void_p),
+                ("dquats", C.c_void_p), ("dsh", C.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                              "or python -m tile_differentiable_rasterizer_amd._build")
+        L = C.CDLL(_LIB_PATH)
+        vp, i64, i32, sz = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t
+        L.gs_project.argtypes = [i64, vp, vp, vp, vp, vp, i32, C.POINTER(GsCamera), GsProjected, vp]
+        L.gs_workspace_bytes.argtypes = [i64, i64, i32]
+        L.gs_workspace_bytes.restype = sz
+        L.gs_bin_tiles.argtypes = [i64, GsProjected, C.POINTER(GsCamera), vp, vp, i64, C.POINTER(i64), vp, sz, vp]
+        L.gs_sort_keys.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gs_render_fwd.argtypes = [i64, GsProjected, vp, vp, C.POINTER(GsCamera), C.POINTER(C.c_float), vp, vp,
+                                    vp, vp]
+        L.gs_render_bwd.argtypes = [i64, vp, vp, vp, vp, vp, i32, C.POINTER(GsCamera), GsProjected, vp, vp,
+                                    C.POINTER(C.c_float), vp, vp, vp, GsGrads, vp, vp, vp]
+        for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd"):
+            getattr(L, name).restype = i32
+        L.gs_status_string.argtypes = [i32]
+        L.gs_status_string.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != GS_OK:
+        raise GsError(status, where)
+
+
+def camera_struct(cam) -> GsCamera:
+    """gs_camera from an object with R (3x3), t (3), fx, fy, cx, cy, width, height, near."""
+    c = GsCamera()
+    R = np.asarray(cam.R, dtype=np.float32).reshape(9)
+    t = np.asarray(cam.t, dtype=np.float32).reshape(3)
+    for i in range(9):
+        c.R[i] = float(R[i])
+    for i in range(3):
+        c.t[i] = float(t[i])
+    c.fx, c.fy, c.cx, c.cy = float(cam.fx), float(cam.fy), float(cam.cx), float(cam.cy)
+    c.width, c.height = int(cam.width), int(cam.height)
+    c.near_z = float(cam.near)
+    return c
+
+
+def _bg(bg):
+    arr = (C.c_float * 3)(*[float(x) for x in bg])
+    return arr
+
+
+def alloc_projected(n: int, device="cuda") -> dict:
+    return dict(rec=torch.empty((n, REC_FLOATS), dtype=torch.float32, device=device),
+                depth=torch.empty(n, dtype=torch.float32, device=device),
+                rect=torch.empty((n, 4), dtype=torch.int16, device=device),
+                n_tiles=torch.empty(n, dtype=torch.int32, device=device),
+                clamp=torch.empty(n, dtype=torch.uint8, device=device))
+
+
+def projected_struct(p: dict) -> GsProjected:
+    return GsProjected(_ptr(p["rec"]), _ptr(p["depth"]), _ptr(p["rect"]), _ptr(p["n_tiles"]), _ptr(p["clamp"]))
+
+
+def project(means, scales, quats, opacities, sh, sh_degree: int, cam, out: dict | None = None, stream=None) -> dict:
+    """gs_project.  Tensors: float32 CUDA, contiguous.  Returns the gs_projected buffers."""
+    n = means.shape[0]
+    if out is None:
+        out = alloc_projected(n, means.device)
+    camc = camera_struct(cam)
+    _check(lib().gs_project(n, _ptr(means), _ptr(scales), _ptr(quats), _ptr(opacities), _ptr(sh), int(sh_degree),
+                            C.byref(camc), projected_struct(out), _stream(stream)), "gs_project")
+    return out
+
+
+def workspace_bytes(n: int, pair_capacity: int, num_tiles: int) -> int:
+    return int(lib().gs_workspace_bytes(n, pair_capacity, num_tiles))
+
+
+def bin_tiles(proj: dict, cam, keys, vals, workspace, stream=None) -> tuple[int, int]:
+    """gs_bin_tiles.  Returns (status, P); status is GS_OK or GS_ERR_CAPACITY."""
+    n = proj["rec"].shape[0]
+    camc = camera_struct(cam)
+    P = C.c_int64(0)
+    cap = keys.shape[0] if keys is not None else 0
+    st = lib().gs_bin_tiles(n, projected_struct(proj), C.byref(camc), _ptr(keys), _ptr(vals), cap, C.byref(P),
+                            _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
+    if st not in (GS_OK, GS_ERR_CAPACITY):
+        _check(st, "gs_bin_tiles")
+    return st, int(P.value)
+
+
+def sort_keys(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, ranges, workspace, stream=None):
+    _check(lib().gs_sort_keys(n_pairs, num_tiles, _ptr(keys), _ptr(vals), _ptr(keys_tmp), _ptr(vals_tmp),
+                              _ptr(ranges), _ptr(workspace), workspace.numel(), _stream(stream)), "gs_sort_keys")
+
+
+def render_fwd(proj: dict, sorted_vals, ranges, cam, bg, image, final_T, n_contrib, stream=None):
+    camc = camera_struct(cam)
+    _check(lib().gs_render_fwd(proj["rec"].shape[0], projected_struct(proj), _ptr(sorted_vals), _ptr(ranges),
+                               C.byref(camc), _bg(bg), _ptr(image), _ptr(final_T), _ptr(n_contrib),
+                               _stream(stream)), "gs_render_fwd")
+
+
+def alloc_grads(n: int, sh_degree: int, device="cuda") -> dict:
+    K = (sh_degree + 1) ** 2
+    return dict(grad_screen=torch.empty((n, GRAD_SCREEN), dtype=torch.float32, device=device),
+                dmeans=torch.empty((n, 3), dtype=torch.float32, device=device),
+                dscales=torch.empty((n, 3), dtype=torch.float32, device=device),
+                dquats=torch.empty((n, 4), dtype=torch.float32, device=device),
+                dsh=torch.empty((n, K, 3), dtype=torch.float32, device=device))
+
+
+def render_bwd(means, scales, quats, opacities, sh, sh_degree, cam, proj, sorted_vals, ranges, bg, final_T,
+               n_contrib, dL_dimage, grads: dict | None = None, accum=None, denom=None, stream=None) -> dict:
+    n = means.shape[0]
+    if grads is None:
+        grads = alloc_grads(n, sh_degree, means.device)
+    camc = camera_struct(cam)
+    g = GsGrads(_ptr(grads["grad_screen"]), _ptr(grads["dmeans"]), _ptr(grads["dscales"]), _ptr(grads["dquats"]),
+                _ptr(grads["dsh"]))
+    _check(lib().gs_render_bwd(n, _ptr(means), _ptr(scales), _ptr(quats), _ptr(opacities), _ptr(sh),
+                               int(sh_degree), C.byref(camc), projected_struct(proj), _ptr(sorted_vals),
+                               _ptr(ranges), _bg(bg), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), g,
+                               _ptr(accum), _ptr(denom), _stream(stream)), "gs_render_bwd")
+    return grads
+
+
+class Rasterizer:
+    """Holds one scene's buffers and runs the five calls in order.
+
+    Buffers are allocated by torch and reused across frames; the pair buffers grow when
+    gs_bin_tiles reports that they are too small.
+    """
+
+    def __init__(self, means, scales, quats, opacities, sh, sh_degree: int, pair_capacity: int = 0):
+        self.means, self.scales, self.quats, self.opac, self.sh = means, scales, quats, opacities, sh
+        self.sh_degree = int(sh_degree)
+        self.n = int(means.shape[0])
+        self.device = means.device
+        self.proj = alloc_projected(self.n, self.device)
+        self.capacity = 0
+        self.keys = self.vals = self.keys_tmp = self.vals_tmp = None
+        self.workspace = None
+        self._ensure_pairs(max(pair_capacity, 1), 1)
+
+    def _ensure_pairs(self, cap: int, num_tiles: int):
+        if cap > self.capacity:
+            self.capacity = int(cap)
+            d = self.device
+            self.keys = torch.empty(self.capacity, dtype=torch.int64, device=d)
+            self.vals = torch.empty(self.capacity, dtype=torch.int32, device=d)
+            self.keys_tmp = torch.empty(self.capacity, dtype=torch.int64, device=d)
+            self.vals_tmp = torch.empty(self.capacity, dtype=torch.int32, device=d)
+        need = workspace_bytes(self.n, self.capacity, num_tiles)
+        if self.workspace is None or self.workspace.numel() < need:
+            self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+
+    def forward(self, cam, bg=(0.0, 0.0, 0.0), stream=None) -> dict:
+        W, H = int(cam.width), int(cam.height)
+        tiles = ((W + TILE - 1) // TILE) * ((H + TILE - 1) // TILE)
+        self._ensure_pairs(self.capacity, tiles)
+        project(self.means, self.scales, self.quats, self.opac, self.sh, self.sh_degree, cam, self.proj, stream)
+        st, P = bin_tiles(self.proj, cam, self.keys, self.vals, self.workspace, stream)
+        if st == GS_ERR_CAPACITY:
+            self._ensure_pairs(P + P // 4 + 1, tiles)
+            st, P = bin_tiles(self.proj, cam, self.keys, self.vals, self.workspace, stream)
+            _check(st, "gs_bin_tiles")
+        ranges = torch.empty((tiles, 2), dtype=torch.int64, device=self.device)
+        sort_keys(P, tiles, self.keys, self.vals, self.keys_tmp, self.vals_tmp, ranges, self.workspace, stream)
+        image = torch.empty((3, H, W), dtype=torch.float32, device=self.device)
+        final_T = torch.empty((H, W), dtype=torch.float32, device=self.device)
+        n_contrib = torch.empty((H, W), dtype=torch.int32, device=self.device)
+        render_fwd(self.proj, self.vals, ranges, cam, bg, image, final_T, n_contrib, stream)
+        return dict(image=image, final_T=final_T, n_contrib=n_contrib, ranges=ranges, n_pairs=P,
+                    keys=self.keys[:P], vals=self.vals[:P], proj=self.proj, cam=cam, bg=tuple(bg))
+
+    def backward(self, fwd: dict, dL_dimage, accum=None, denom=None, stream=None) -> dict:
+        return render_bwd(self.means, self.scales, self.quats, self.opac, self.sh, self.sh_degree, fwd["cam"],
+                          fwd["proj"], self.vals, fwd["ranges"], fwd["bg"], fwd["final_T"], fwd["n_contrib"],
+                          dL_dimage, None, accum, denom, stream)
+
+
+def scene_to_device(scene, device="cuda"):
+    """Upload a scenes.Scene's arrays once (float32, contiguous)."""
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    return f(scene.means), f(scene.scales), f(scene.quats), f(scene.opacities), f(scene.sh)
