@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to aim for")
+    ap.add_argument("--profile", action="store_true",
+                    help="profiler run: no CPU baseline, plus a 1 GiB device copy that calibrates HBM counters")
     return ap.parse_args()
 
 
@@ -79,6 +81,7 @@ def main():
     tiles = cams[0].num_tiles
     H, W = cams[0].height, cams[0].width
     ranges = [torch.empty((tiles, 2), dtype=torch.int64, device=dev) for _ in cams]
+    orders = [torch.empty(tiles, dtype=torch.int32, device=dev) for _ in cams]
     images = [torch.empty((3, H, W), dtype=torch.float32, device=dev) for _ in cams]
     finalT = [torch.empty((H, W), dtype=torch.float32, device=dev) for _ in cams]
     ncon = [torch.empty((H, W), dtype=torch.int32, device=dev) for _ in cams]
@@ -98,13 +101,14 @@ def main():
         st, P = raster.bin_tiles(rz.proj, cam, rz.keys, rz.vals, rz.workspace)
         assert st == raster.GS_OK
         e[2].record(stream)
-        raster.sort_keys(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, ranges[k], rz.workspace)
+        raster.sort_keys(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, ranges[k], rz.workspace, orders[k])
         e[3].record(stream)
-        raster.render_fwd(rz.proj, rz.vals, ranges[k], cam, (0.0, 0.0, 0.0), images[k], finalT[k], ncon[k])
+        raster.render_fwd(rz.proj, rz.vals, ranges[k], cam, (0.0, 0.0, 0.0), images[k], finalT[k], ncon[k],
+                          orders[k])
         e[4].record(stream)
         if with_bwd:
             raster.render_bwd(means, scales, quats, opac, sh, sc.sh_degree, cam, rz.proj, rz.vals, ranges[k],
-                              (0.0, 0.0, 0.0), finalT[k], ncon[k], dLs[k], grads, accum, denom)
+                              (0.0, 0.0, 0.0), finalT[k], ncon[k], dLs[k], grads, accum, denom, orders[k])
             e[5].record(stream)
         rec.append((e, with_bwd, P))
 
@@ -125,6 +129,14 @@ def main():
                 times["render_bwd"].append(e[4].elapsed_time(e[5]))
         return t1 - t0, times, [p for _, _, p in recs]
 
+    if args.profile:
+        # a plain copy of known size: 1 GiB read + 1 GiB written, for counter calibration
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        args.no_cpu_baseline = True
     log("warm-up")
     run(args.warmup, True)
     log(f"timed: {args.steps} steps x {len(cams)} cameras, forward + backward")

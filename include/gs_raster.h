@@ -152,12 +152,14 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
  * pairs emitted in id order come out with depth ties broken by Gaussian id.  The result is
  * left in keys/vals; keys_tmp/vals_tmp are scratch of the same size.  Then writes
  * tile_ranges[num_tiles][2] = [first, last + 1) of each tile in the sorted order ([0, 0)
- * for an empty tile).  Keys must have tile_id < num_tiles.
+ * for an empty tile) and, when tile_order is non-NULL, tile_order[num_tiles] = every tile
+ * id once, longest lists first (a schedule for the compositing calls; it does not change
+ * their results).  Keys must have tile_id < num_tiles.
  * Errors: INVALID_ARG, WORKSPACE, OVERFLOW, HIP.
  */
 gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, uint64_t* keys, uint32_t* vals,
                        uint64_t* keys_tmp, uint32_t* vals_tmp, int64_t* tile_ranges,
-                       void* workspace, size_t workspace_bytes, void* stream);
+                       int32_t* tile_order, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gs_render_fwd -- composite every pixel front to back over its tile's sorted list
@@ -167,12 +169,14 @@ gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, uint64_t* keys, uint3
  *   C += rgb * alpha * T; T *= 1 - alpha; the pixel stops once T < 1e-4;
  *   image = C + T * bg.
  *  image[3][H][W] (planar), final_T[H][W], n_contrib[H][W] = 1 + the tile-list position
- *  of the last contributor (0 if none), which gs_render_bwd needs.
+ *  of the last contributor (0 if none), which gs_render_bwd needs.  tile_order (nullable)
+ *  is the schedule written by gs_sort_keys; NULL processes tiles in id order.
  * Errors: INVALID_ARG, HIP.
  */
 gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_vals,
-                        const int64_t* tile_ranges, const gs_camera* cam, const float bg[3],
-                        float* image, float* final_T, uint32_t* n_contrib, void* stream);
+                        const int64_t* tile_ranges, const int32_t* tile_order,
+                        const gs_camera* cam, const float bg[3], float* image, float* final_T,
+                        uint32_t* n_contrib, void* stream);
 
 /*
  * gs_render_bwd -- reverse pass of gs_render_fwd and of gs_project, plus densification
@@ -191,9 +195,9 @@ gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_val
 gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, const float* quats,
                         const float* opacities, const float* sh, int32_t sh_degree,
                         const gs_camera* cam, gs_projected proj, const uint32_t* sorted_vals,
-                        const int64_t* tile_ranges, const float bg[3], const float* final_T,
-                        const uint32_t* n_contrib, const float* dL_dimage, gs_grads out,
-                        float* densify_accum, int32_t* densify_denom, void* stream);
+                        const int64_t* tile_ranges, const int32_t* tile_order, const float bg[3],
+                        const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
+                        gs_grads out, float* densify_accum, int32_t* densify_denom, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* gs_status_string(gs_status status);

@@ -60,20 +60,21 @@ def gpu_stages(scene, cam, bg=(0.0, 0.0, 0.0), keep_unsorted=True):
     ktmp = torch.empty_like(keys)
     vtmp = torch.empty_like(vals)
     ranges = torch.empty((tiles, 2), dtype=torch.int64, device=dev)
-    raster.sort_keys(P, tiles, keys, vals, ktmp, vtmp, ranges, ws)
+    order = torch.empty(tiles, dtype=torch.int32, device=dev)
+    raster.sort_keys(P, tiles, keys, vals, ktmp, vtmp, ranges, ws, order)
     image = torch.empty((3, cam.height, cam.width), dtype=torch.float32, device=dev)
     final_T = torch.empty((cam.height, cam.width), dtype=torch.float32, device=dev)
     n_contrib = torch.empty((cam.height, cam.width), dtype=torch.int32, device=dev)
-    raster.render_fwd(proj, vals, ranges, cam, bg, image, final_T, n_contrib)
+    raster.render_fwd(proj, vals, ranges, cam, bg, image, final_T, n_contrib, order)
     torch.cuda.synchronize()
     rec = to_np(proj["rec"])
     out.update(
         rec=rec, bbox=rec[:, 9:11].view(np.uint32), depth_bits=to_np(proj["depth"]).view(np.uint32),
         rect=to_np(proj["rect"]).view(np.uint16).astype(np.int32), n_tiles=to_np(proj["n_tiles"]).view(np.uint32),
         clamp=to_np(proj["clamp"]), keys=to_np(keys[:P]).view(np.uint64).copy(),
-        vals=to_np(vals[:P]).view(np.uint32).copy(), ranges=to_np(ranges), image=to_np(image),
+        vals=to_np(vals[:P]).view(np.uint32).copy(), ranges=to_np(ranges), order=to_np(order), image=to_np(image),
         final_T=to_np(final_T), n_contrib=to_np(n_contrib).view(np.uint32),
-        dev=dict(means=means, scales=scales, quats=quats, opac=opac, sh=sh, proj=proj, vals=vals, ranges=ranges,
+        dev=dict(means=means, scales=scales, quats=quats, opac=opac, sh=sh, proj=proj, vals=vals, ranges=ranges, order=order,
                  final_T=final_T, n_contrib=n_contrib, image=image))
     return out
 
@@ -127,6 +128,12 @@ def check_binning(cam, g, label=""):
     assert np.array_equal(g["vals"], sv), f"{label}: sorted ids differ"
     rg = oracle.tile_ranges(sk, cam.num_tiles)
     assert np.array_equal(g["ranges"], rg), f"{label}: tile ranges differ"
+    # the schedule: a permutation of the tiles with non-increasing list-length buckets
+    order = g["order"]
+    assert np.array_equal(np.sort(order), np.arange(cam.num_tiles)), f"{label}: tile order is not a permutation"
+    lens = (rg[:, 1] - rg[:, 0])[order]
+    lg = np.floor(np.log2(np.maximum(lens, 1)))
+    assert np.all(np.diff(lg) <= 0), f"{label}: tile order is not longest-first"
 
 
 def compare_pixels(gpu_col, gpu_T, gpu_n, orc, label="", tol=PIX_TOL):

@@ -38,7 +38,8 @@ def _run(sc, cam, target, label):
     accum = torch.zeros((n, 2), dtype=torch.float32, device="cuda")
     denom = torch.zeros(n, dtype=torch.int32, device="cuda")
     grads = raster.render_bwd(d["means"], d["scales"], d["quats"], d["opac"], d["sh"], sc.sh_degree, cam, d["proj"],
-                              d["vals"], d["ranges"], bg, d["final_T"], d["n_contrib"], dLd, None, accum, denom)
+                              d["vals"], d["ranges"], bg, d["final_T"], d["n_contrib"], dLd, None, accum, denom,
+                              order=d["order"])
     torch.cuda.synchronize()
     gs = to_np(grads["grad_screen"]).astype(np.float64)
     say(f"{label}: oracle backward")
@@ -94,7 +95,7 @@ def test_backward_1m_720p_and_stats_accumulate():
     acc1 = accum.clone()
     raster.render_bwd(d["means"], d["scales"], d["quats"], d["opac"], d["sh"], sc.sh_degree, cam, d["proj"],
                       d["vals"], d["ranges"], (0.0, 0.0, 0.0), d["final_T"], d["n_contrib"], dLd, grads, accum,
-                      denom)
+                      denom)  # natural tile order: the schedule must not change results
     torch.cuda.synchronize()
     vis = torch.from_numpy((g["n_tiles"] > 0).astype(np.int32)).cuda()
     assert torch.equal(denom, 2 * vis)

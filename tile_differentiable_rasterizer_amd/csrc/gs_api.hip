@@ -20,13 +20,13 @@ hipError_t launch_bin_emit(int64_t n, const gs_projected& proj, int tiles_x, con
                            uint32_t* vals, hipStream_t s);
 size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles);
 hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
-                       uint32_t* vals_tmp, int64_t* ranges, void* ws, hipStream_t s);
+                       uint32_t* vals_tmp, int64_t* ranges, int32_t* order, void* ws, hipStream_t s);
 hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
 hipError_t launch_render_fwd(const gs_projected& proj, const uint32_t* vals, const int64_t* ranges,
-                             const DevCamera& cam, const float bg[3], float* image, float* final_T,
-                             uint32_t* n_contrib, hipStream_t s);
+                             const int32_t* order, const DevCamera& cam, const float bg[3], float* image,
+                             float* final_T, uint32_t* n_contrib, hipStream_t s);
 hipError_t launch_render_bwd(const gs_projected& proj, const uint32_t* vals, const int64_t* ranges,
-                             const DevCamera& cam, const float bg[3], const float* final_T,
+                             const int32_t* order, const DevCamera& cam, const float bg[3], const float* final_T,
                              const uint32_t* n_contrib, const float* dL, float* gscreen, hipStream_t s);
 }  // namespace gs
 
@@ -120,33 +120,33 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
 }
 
 gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
-                       uint32_t* vals_tmp, int64_t* tile_ranges, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       uint32_t* vals_tmp, int64_t* tile_ranges, int32_t* tile_order, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (n_pairs < 0 || num_tiles < 1 || !tile_ranges) return GS_ERR_INVALID_ARG;
   if (n_pairs > 0 && (!keys || !vals || !keys_tmp || !vals_tmp)) return GS_ERR_INVALID_ARG;
   if (n_pairs >= ((int64_t)1 << 62)) return GS_ERR_OVERFLOW;
   if (!workspace || workspace_bytes < sort_workspace_bytes(n_pairs, num_tiles)) return GS_ERR_WORKSPACE;
-  return hip_status(launch_sort(n_pairs, num_tiles, keys, vals, keys_tmp, vals_tmp, tile_ranges, workspace,
-                                static_cast<hipStream_t>(stream)));
+  return hip_status(launch_sort(n_pairs, num_tiles, keys, vals, keys_tmp, vals_tmp, tile_ranges, tile_order,
+                                workspace, static_cast<hipStream_t>(stream)));
 }
 
 gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_vals, const int64_t* tile_ranges,
-                        const gs_camera* cam, const float bg[3], float* image, float* final_T,
-                        uint32_t* n_contrib, void* stream) {
+                        const int32_t* tile_order, const gs_camera* cam, const float bg[3], float* image,
+                        float* final_T, uint32_t* n_contrib, void* stream) {
   if (n < 0 || !camera_ok(cam) || !bg || !image || !final_T || !n_contrib || !tile_ranges) return GS_ERR_INVALID_ARG;
   if (n >= kMaxGaussians || !camera_fits(cam)) return GS_ERR_OVERFLOW;
   if (n > 0 && (!projected_ok(proj) || !sorted_vals)) return GS_ERR_INVALID_ARG;
   const DevCamera d = dev_camera(cam);
-  return hip_status(launch_render_fwd(proj, sorted_vals, tile_ranges, d, bg, image, final_T, n_contrib,
+  return hip_status(launch_render_fwd(proj, sorted_vals, tile_ranges, tile_order, d, bg, image, final_T, n_contrib,
                                       static_cast<hipStream_t>(stream)));
 }
 
 gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, const float* quats,
                         const float* opacities, const float* sh, int32_t sh_degree, const gs_camera* cam,
                         gs_projected proj, const uint32_t* sorted_vals, const int64_t* tile_ranges,
-                        const float bg[3], const float* final_T, const uint32_t* n_contrib,
-                        const float* dL_dimage, gs_grads out, float* densify_accum, int32_t* densify_denom,
-                        void* stream) {
+                        const int32_t* tile_order, const float bg[3], const float* final_T,
+                        const uint32_t* n_contrib, const float* dL_dimage, gs_grads out, float* densify_accum,
+                        int32_t* densify_denom, void* stream) {
   (void)opacities;
   if (n < 0 || sh_degree < 0 || sh_degree > 3 || !camera_ok(cam) || !bg || !final_T || !n_contrib ||
       !dL_dimage || !tile_ranges)
@@ -159,7 +159,8 @@ gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_fill_u32(out.grad_screen, n * GS_GRAD_SCREEN, 0u, s);
   if (e == hipSuccess)
-    e = launch_render_bwd(proj, sorted_vals, tile_ranges, d, bg, final_T, n_contrib, dL_dimage, out.grad_screen, s);
+    e = launch_render_bwd(proj, sorted_vals, tile_ranges, tile_order, d, bg, final_T, n_contrib, dL_dimage,
+                          out.grad_screen, s);
   if (e == hipSuccess)
     e = launch_project_bwd(n, means, scales, quats, sh, sh_degree, d, proj, out, densify_accum, densify_denom, s);
   return hip_status(e);

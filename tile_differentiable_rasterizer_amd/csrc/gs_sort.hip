@@ -252,6 +252,35 @@ __global__ void k_ranges(const uint64_t* __restrict__ keys, int64_t P, int64_t n
   if (i == P - 1 || (keys[i + 1] >> 32) != t) ranges[2 * t + 1] = i + 1;
 }
 
+// tile_order: tile ids by decreasing list length (counting sort over 128 buckets, four per
+// octave; order inside a bucket is arbitrary).  The compositing kernels take tiles in this
+// order so that the longest lists start first.
+__device__ __forceinline__ int length_bucket(int64_t len) {
+  if (len < 4) return (int)len;
+  const int lg = 63 - __clzll((unsigned long long)len);
+  return min(127, 4 * lg + (int)((len >> (lg - 2)) & 3));
+}
+
+__global__ __launch_bounds__(1024) void k_tile_order(const int64_t* __restrict__ ranges, int64_t num_tiles,
+                                                    int32_t* __restrict__ order) {
+  __shared__ uint32_t s_cnt[128];
+  __shared__ uint32_t s_cur[128];
+  if (threadIdx.x < 128) s_cnt[threadIdx.x] = 0;
+  __syncthreads();
+  for (int64_t t = threadIdx.x; t < num_tiles; t += 1024)
+    atomicAdd(&s_cnt[length_bucket(ranges[2 * t + 1] - ranges[2 * t])], 1u);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t acc = 0;
+    for (int b = 127; b >= 0; --b) { s_cur[b] = acc; acc += s_cnt[b]; }
+  }
+  __syncthreads();
+  for (int64_t t = threadIdx.x; t < num_tiles; t += 1024) {
+    const uint32_t pos = atomicAdd(&s_cur[length_bucket(ranges[2 * t + 1] - ranges[2 * t])], 1u);
+    order[pos] = (int32_t)t;
+  }
+}
+
 int sort_significant_bits(int64_t num_tiles) {
   int tb = 0;
   while (tb < 32 && ((int64_t)1 << tb) < num_tiles) ++tb;
@@ -264,9 +293,13 @@ size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles) {
 }
 
 hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
-                       uint32_t* vals_tmp, int64_t* ranges, void* ws, hipStream_t s) {
+                       uint32_t* vals_tmp, int64_t* ranges, int32_t* order, void* ws, hipStream_t s) {
   hipError_t e = launch_fill_u32(ranges, 4 * num_tiles, 0u, s);
-  if (e != hipSuccess || P == 0) return e;
+  if (e != hipSuccess) return e;
+  if (P == 0) {
+    if (order) k_tile_order<<<1, 1024, 0, s>>>(ranges, num_tiles, order);
+    return hipGetLastError();
+  }
   const int sig = sort_significant_bits(num_tiles);
   const int passes = (sig + 7) / 8;
   const SortLayout l = sort_layout(P, passes);
@@ -296,6 +329,7 @@ hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* v
     k_sort_copy<<<blocks, 256, 0, s>>>(plan, keys_tmp, vals_tmp, keys, vals, P);
   }
   k_ranges<<<(unsigned)((P + 255) / 256), 256, 0, s>>>(keys, P, num_tiles, ranges);
+  if (order) k_tile_order<<<1, 1024, 0, s>>>(ranges, num_tiles, order);
   return hipGetLastError();
 }
 

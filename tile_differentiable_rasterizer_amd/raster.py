@@ -60,10 +60,10 @@ def lib():
         L.gs_workspace_bytes.argtypes = [i64, i64, i32]
         L.gs_workspace_bytes.restype = sz
         L.gs_bin_tiles.argtypes = [i64, GsProjected, C.POINTER(GsCamera), vp, vp, i64, C.POINTER(i64), vp, sz, vp]
-        L.gs_sort_keys.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
-        L.gs_render_fwd.argtypes = [i64, GsProjected, vp, vp, C.POINTER(GsCamera), C.POINTER(C.c_float), vp, vp,
-                                    vp, vp]
-        L.gs_render_bwd.argtypes = [i64, vp, vp, vp, vp, vp, i32, C.POINTER(GsCamera), GsProjected, vp, vp,
+        L.gs_sort_keys.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gs_render_fwd.argtypes = [i64, GsProjected, vp, vp, vp, C.POINTER(GsCamera), C.POINTER(C.c_float), vp,
+                                    vp, vp, vp]
+        L.gs_render_bwd.argtypes = [i64, vp, vp, vp, vp, vp, i32, C.POINTER(GsCamera), GsProjected, vp, vp, vp,
                                     C.POINTER(C.c_float), vp, vp, vp, GsGrads, vp, vp, vp]
         for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd"):
             getattr(L, name).restype = i32
@@ -149,15 +149,18 @@ def bin_tiles(proj: dict, cam, keys, vals, workspace, stream=None) -> tuple[int,
     return st, int(P.value)
 
 
-def sort_keys(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, ranges, workspace, stream=None):
+def sort_keys(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, ranges, workspace, order=None,
+              stream=None):
+    """gs_sort_keys; ``order`` (int32 [num_tiles], optional) receives the longest-first tile order."""
     _check(lib().gs_sort_keys(n_pairs, num_tiles, _ptr(keys), _ptr(vals), _ptr(keys_tmp), _ptr(vals_tmp),
-                              _ptr(ranges), _ptr(workspace), workspace.numel(), _stream(stream)), "gs_sort_keys")
+                              _ptr(ranges), _ptr(order), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "gs_sort_keys")
 
 
-def render_fwd(proj: dict, sorted_vals, ranges, cam, bg, image, final_T, n_contrib, stream=None):
+def render_fwd(proj: dict, sorted_vals, ranges, cam, bg, image, final_T, n_contrib, order=None, stream=None):
     camc = camera_struct(cam)
     _check(lib().gs_render_fwd(proj["rec"].shape[0], projected_struct(proj), _ptr(sorted_vals), _ptr(ranges),
-                               C.byref(camc), _bg(bg), _ptr(image), _ptr(final_T), _ptr(n_contrib),
+                               _ptr(order), C.byref(camc), _bg(bg), _ptr(image), _ptr(final_T), _ptr(n_contrib),
                                _stream(stream)), "gs_render_fwd")
 
 
@@ -171,7 +174,8 @@ def alloc_grads(n: int, sh_degree: int, device="cuda") -> dict:
 
 
 def render_bwd(means, scales, quats, opacities, sh, sh_degree, cam, proj, sorted_vals, ranges, bg, final_T,
-               n_contrib, dL_dimage, grads: dict | None = None, accum=None, denom=None, stream=None) -> dict:
+               n_contrib, dL_dimage, grads: dict | None = None, accum=None, denom=None, order=None,
+               stream=None) -> dict:
     n = means.shape[0]
     if grads is None:
         grads = alloc_grads(n, sh_degree, means.device)
@@ -180,7 +184,7 @@ def render_bwd(means, scales, quats, opacities, sh, sh_degree, cam, proj, sorted
                 _ptr(grads["dsh"]))
     _check(lib().gs_render_bwd(n, _ptr(means), _ptr(scales), _ptr(quats), _ptr(opacities), _ptr(sh),
                                int(sh_degree), C.byref(camc), projected_struct(proj), _ptr(sorted_vals),
-                               _ptr(ranges), _bg(bg), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), g,
+                               _ptr(ranges), _ptr(order), _bg(bg), _ptr(final_T), _ptr(n_contrib), _ptr(dL_dimage), g,
                                _ptr(accum), _ptr(denom), _stream(stream)), "gs_render_bwd")
     return grads
 
@@ -226,18 +230,20 @@ class Rasterizer:
             st, P = bin_tiles(self.proj, cam, self.keys, self.vals, self.workspace, stream)
             _check(st, "gs_bin_tiles")
         ranges = torch.empty((tiles, 2), dtype=torch.int64, device=self.device)
-        sort_keys(P, tiles, self.keys, self.vals, self.keys_tmp, self.vals_tmp, ranges, self.workspace, stream)
+        order = torch.empty(tiles, dtype=torch.int32, device=self.device)
+        sort_keys(P, tiles, self.keys, self.vals, self.keys_tmp, self.vals_tmp, ranges, self.workspace, order,
+                  stream)
         image = torch.empty((3, H, W), dtype=torch.float32, device=self.device)
         final_T = torch.empty((H, W), dtype=torch.float32, device=self.device)
         n_contrib = torch.empty((H, W), dtype=torch.int32, device=self.device)
-        render_fwd(self.proj, self.vals, ranges, cam, bg, image, final_T, n_contrib, stream)
-        return dict(image=image, final_T=final_T, n_contrib=n_contrib, ranges=ranges, n_pairs=P,
+        render_fwd(self.proj, self.vals, ranges, cam, bg, image, final_T, n_contrib, order, stream)
+        return dict(image=image, final_T=final_T, n_contrib=n_contrib, ranges=ranges, order=order, n_pairs=P,
                     keys=self.keys[:P], vals=self.vals[:P], proj=self.proj, cam=cam, bg=tuple(bg))
 
     def backward(self, fwd: dict, dL_dimage, accum=None, denom=None, stream=None) -> dict:
         return render_bwd(self.means, self.scales, self.quats, self.opac, self.sh, self.sh_degree, fwd["cam"],
                           fwd["proj"], self.vals, fwd["ranges"], fwd["bg"], fwd["final_T"], fwd["n_contrib"],
-                          dL_dimage, None, accum, denom, stream)
+                          dL_dimage, None, accum, denom, fwd.get("order"), stream)
 
 
 def scene_to_device(scene, device="cuda"):
