@@ -131,10 +131,13 @@ size_t gs_workspace_bytes(int64_t n, int64_t pair_capacity, int32_t num_tiles);
 
 /*
  * gs_bin_tiles -- duplicate every visible Gaussian once per covered tile ("Better Gaussian
- * Splatting in Julia" s3.2 assign_to_tiles).  Pairs come out in Gaussian-id order, tiles
- * row by row inside a Gaussian:
+ * Splatting in Julia" s3.2 assign_to_tiles):
  *   keys[p] = tile_id << 32 | bits(depth),  tile_id = ty * tiles_x + tx
  *   vals[p] = Gaussian id
+ * Pairs come out ordered by (bits(depth), Gaussian id) -- the visible Gaussians are
+ * radix-sorted by depth first -- with each Gaussian's tiles row by row.  So the keys are
+ * already stably ordered by their low 32 bits, and gs_sort_keys(sorted_low_bits = 32)
+ * completes the (tile, depth, id) order with passes over the tile bits only.
  * Writes the pair count P to *n_pairs [host] (this is the call's one device->host read and
  * stream synchronisation).  With keys == NULL only P is computed.  If P > capacity,
  * returns GS_ERR_CAPACITY with *n_pairs = P and writes no pairs.
@@ -145,11 +148,13 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
                        size_t workspace_bytes, void* stream);
 
 /*
- * gs_sort_keys -- stable LSD radix sort of (keys, vals) over the key's significant bits
- * (32 + ceil(log2(num_tiles))), 8 bits per pass, digits constant over all keys skipped
+ * gs_sort_keys -- stable LSD radix sort of (keys, vals) over key bits [sorted_low_bits,
+ * 32 + ceil(log2(num_tiles))), 8 bits per pass, digits constant over all keys skipped
  * ("Better Gaussian Splatting in Julia" s3.2 sort_by_depth!; "Implementing Better
- * Gaussian Splatting in Julia" s3.3 depth order).  Equal keys keep their input order, so
- * pairs emitted in id order come out with depth ties broken by Gaussian id.  The result is
+ * Gaussian Splatting in Julia" s3.3 depth order).  The input must already be stably
+ * ordered by its low sorted_low_bits bits (0 = no assumption: a full sort; 32 = the
+ * output of gs_bin_tiles).  Equal keys keep their input order, so depth ties stay broken
+ * by Gaussian id.  The result is
  * left in keys/vals; keys_tmp/vals_tmp are scratch of the same size.  Then writes
  * tile_ranges[num_tiles][2] = [first, last + 1) of each tile in the sorted order ([0, 0)
  * for an empty tile) and, when tile_order is non-NULL, tile_order[num_tiles] = every tile
@@ -157,9 +162,10 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
  * their results).  Keys must have tile_id < num_tiles.
  * Errors: INVALID_ARG, WORKSPACE, OVERFLOW, HIP.
  */
-gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, uint64_t* keys, uint32_t* vals,
-                       uint64_t* keys_tmp, uint32_t* vals_tmp, int64_t* tile_ranges,
-                       int32_t* tile_order, void* workspace, size_t workspace_bytes, void* stream);
+gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys,
+                       uint32_t* vals, uint64_t* keys_tmp, uint32_t* vals_tmp,
+                       int64_t* tile_ranges, int32_t* tile_order, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /*
  * gs_render_fwd -- composite every pixel front to back over its tile's sorted list

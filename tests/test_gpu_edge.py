@@ -126,7 +126,7 @@ def test_sort_adversarial_keys(kind):
     vd = torch.from_numpy(vals.view(np.int32)).to(dev)
     ws = torch.empty(raster.workspace_bytes(1, P, tiles), dtype=torch.uint8, device=dev)
     ranges = torch.empty((tiles, 2), dtype=torch.int64, device=dev)
-    raster.sort_keys(P, tiles, kd, vd, torch.empty_like(kd), torch.empty_like(vd), ranges, ws)
+    raster.sort_keys(P, tiles, kd, vd, torch.empty_like(kd), torch.empty_like(vd), ranges, ws, sorted_low_bits=0)
     torch.cuda.synchronize()
     order = np.lexsort((np.arange(P), keys))  # stable by key
     assert np.array_equal(kd.cpu().numpy().view(np.uint64), keys[order])

@@ -15,12 +15,13 @@ hipError_t launch_project_bwd(int64_t n, const float* means, const float* scales
                               const gs_grads& gr, float* accum, int32_t* denom, hipStream_t s);
 size_t bin_workspace_bytes(int64_t n);
 hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, void* ws, hipStream_t s);
-uint64_t* bin_total_ptr(int64_t n, void* ws);
-hipError_t launch_bin_emit(int64_t n, const gs_projected& proj, int tiles_x, const void* ws, uint64_t* keys,
+uint64_t* bin_totals_ptr(int64_t n, void* ws);
+hipError_t launch_bin_emit(int64_t n, int64_t v, const gs_projected& proj, int tiles_x, void* ws, uint64_t* keys,
                            uint32_t* vals, hipStream_t s);
-size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles);
+size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_bits);
 hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
-                       uint32_t* vals_tmp, int64_t* ranges, int32_t* order, void* ws, hipStream_t s);
+                       uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits, void* ws,
+                       hipStream_t s);
 hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
 hipError_t launch_render_fwd(const gs_projected& proj, const uint32_t* vals, const int64_t* ranges,
                              const int32_t* order, const DevCamera& cam, const float bg[3], float* image,
@@ -80,7 +81,7 @@ const char* gs_status_string(gs_status s) {
 size_t gs_workspace_bytes(int64_t n, int64_t pair_capacity, int32_t num_tiles) {
   if (n < 0 || pair_capacity < 0 || num_tiles < 1) return 0;
   const size_t a = bin_workspace_bytes(n);
-  const size_t b = sort_workspace_bytes(pair_capacity, num_tiles);
+  const size_t b = sort_workspace_bytes(pair_capacity, num_tiles, 0);
   return a > b ? a : b;
 }
 
@@ -107,27 +108,29 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_bin_count(n, proj.n_tiles, workspace, s);
   if (e != hipSuccess) return GS_ERR_HIP;
-  uint64_t total = 0;
-  if (hipMemcpyAsync(&total, bin_total_ptr(n, workspace), sizeof total, hipMemcpyDeviceToHost, s) != hipSuccess)
+  uint64_t totals[2] = {0, 0};  // pairs, visible Gaussians
+  if (hipMemcpyAsync(totals, bin_totals_ptr(n, workspace), sizeof totals, hipMemcpyDeviceToHost, s) != hipSuccess)
     return GS_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return GS_ERR_HIP;
-  if (total > (uint64_t)INT64_MAX) return GS_ERR_OVERFLOW;
-  *n_pairs = (int64_t)total;
+  if (totals[0] > (uint64_t)INT64_MAX) return GS_ERR_OVERFLOW;
+  *n_pairs = (int64_t)totals[0];
   if (!keys) return GS_OK;
-  if ((int64_t)total > capacity) return GS_ERR_CAPACITY;
+  if ((int64_t)totals[0] > capacity) return GS_ERR_CAPACITY;
   const DevCamera d = dev_camera(cam);
-  return hip_status(launch_bin_emit(n, proj, d.tiles_x, workspace, keys, vals, s));
+  return hip_status(launch_bin_emit(n, (int64_t)totals[1], proj, d.tiles_x, workspace, keys, vals, s));
 }
 
-gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
-                       uint32_t* vals_tmp, int64_t* tile_ranges, int32_t* tile_order, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  if (n_pairs < 0 || num_tiles < 1 || !tile_ranges) return GS_ERR_INVALID_ARG;
+gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys, uint32_t* vals,
+                       uint64_t* keys_tmp, uint32_t* vals_tmp, int64_t* tile_ranges, int32_t* tile_order,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_pairs < 0 || num_tiles < 1 || !tile_ranges || sorted_low_bits < 0 || sorted_low_bits > 64)
+    return GS_ERR_INVALID_ARG;
   if (n_pairs > 0 && (!keys || !vals || !keys_tmp || !vals_tmp)) return GS_ERR_INVALID_ARG;
   if (n_pairs >= ((int64_t)1 << 62)) return GS_ERR_OVERFLOW;
-  if (!workspace || workspace_bytes < sort_workspace_bytes(n_pairs, num_tiles)) return GS_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < sort_workspace_bytes(n_pairs, num_tiles, sorted_low_bits))
+    return GS_ERR_WORKSPACE;
   return hip_status(launch_sort(n_pairs, num_tiles, keys, vals, keys_tmp, vals_tmp, tile_ranges, tile_order,
-                                workspace, static_cast<hipStream_t>(stream)));
+                                sorted_low_bits, workspace, static_cast<hipStream_t>(stream)));
 }
 
 gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_vals, const int64_t* tile_ranges,

@@ -65,18 +65,25 @@ hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(kSortBlock) void k_sort_hist(const uint64_t* __restrict__ keys, int64_t P,
+template <typename K>
+__global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ keys, int64_t P, int lo,
                                                           int passes, uint64_t* __restrict__ hist) {
-  __shared__ uint32_t s_h[kMaxPasses * kRadix];
-  for (int i = threadIdx.x; i < passes * kRadix; i += kSortBlock) s_h[i] = 0;
+  // one LDS histogram per wavefront: atomics from different wavefronts never collide
+  __shared__ uint32_t s_h[kSortBlock / kWave][kMaxPasses * kRadix];
+  const int wave = threadIdx.x / kWave;
+  for (int i = threadIdx.x; i < (kSortBlock / kWave) * kMaxPasses * kRadix; i += kSortBlock) (&s_h[0][0])[i] = 0;
   __syncthreads();
   for (int64_t i = (int64_t)blockIdx.x * kSortBlock + threadIdx.x; i < P; i += (int64_t)gridDim.x * kSortBlock) {
-    const uint64_t k = keys[i];
-    for (int p = 0; p < passes; ++p) atomicAdd(&s_h[p * kRadix + ((k >> (8 * p)) & 0xFF)], 1u);
+    const uint64_t k = (uint64_t)keys[i] >> lo;
+    for (int p = 0; p < passes; ++p) atomicAdd(&s_h[wave][p * kRadix + ((k >> (8 * p)) & 0xFF)], 1u);
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < passes * kRadix; i += kSortBlock)
-    if (s_h[i]) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[i]), (unsigned long long)s_h[i]);
+  for (int i = threadIdx.x; i < passes * kRadix; i += kSortBlock) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < kSortBlock / kWave; ++w) c += s_h[w][i];
+    if (c) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[i]), (unsigned long long)c);
+  }
 }
 
 // plan[p] = -1 (skip), 0 (keys -> tmp) or 1 (tmp -> keys); plan[kMaxPasses] = buffer
@@ -108,20 +115,20 @@ __device__ __forceinline__ void status_store(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <typename K>
 __global__ __launch_bounds__(kSortBlock) void k_onesweep(
-    uint64_t* __restrict__ k0, uint32_t* __restrict__ v0, uint64_t* __restrict__ k1, uint32_t* __restrict__ v1,
-    int64_t P, int pass, int bits, const int32_t* __restrict__ plan, const uint64_t* __restrict__ dbase,
+    K* __restrict__ k0, uint32_t* __restrict__ v0, K* __restrict__ k1, uint32_t* __restrict__ v1,
+    int64_t P, int pass, int shift, int bits, const int32_t* __restrict__ plan, const uint64_t* __restrict__ dbase,
     uint64_t* __restrict__ status, uint32_t* __restrict__ tickets) {
   const int mode = plan[pass];
   if (mode < 0) return;  // digit constant over all keys: nothing to do
-  const uint64_t* kin = mode ? k1 : k0;
+  const K* kin = mode ? k1 : k0;
   const uint32_t* vin = mode ? v1 : v0;
-  uint64_t* kout = mode ? k0 : k1;
+  K* kout = mode ? k0 : k1;
   uint32_t* vout = mode ? v0 : v1;
-  const int shift = 8 * pass;
   const uint32_t dmask = (1u << bits) - 1u;
 
-  __shared__ uint64_t s_keys[kSortPart];
+  __shared__ K s_keys[kSortPart];
   __shared__ uint32_t s_vals[kSortPart];
   __shared__ uint32_t s_wh[kSortBlock / kWave][kRadix];  // per-wave digit counters, then offsets
   __shared__ uint32_t s_lbase[kRadix];                   // partition-local digit starts
@@ -137,13 +144,13 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   const int64_t base = part * kSortPart;
 
   // wave-striped: wave w owns keys [w*1024, (w+1)*1024) of the partition, in order
-  uint64_t key[kSortKPT];
+  K key[kSortKPT];
   uint32_t val[kSortKPT];
   uint32_t rank[kSortKPT];
 #pragma unroll
   for (int j = 0; j < kSortKPT; ++j) {
     const int64_t idx = base + wave * (kSortKPT * kWave) + j * kWave + lane;
-    key[j] = idx < P ? kin[idx] : ~0ull;
+    key[j] = idx < P ? kin[idx] : (K)~(K)0;
     val[j] = idx < P ? vin[idx] : 0u;
   }
 #pragma unroll
@@ -224,7 +231,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   // write each digit's run contiguously
   const int nvalid = (int)min((int64_t)kSortPart, P - base);
   for (int i = tid; i < nvalid; i += kSortBlock) {
-    const uint64_t k = s_keys[i];
+    const K k = s_keys[i];
     const uint32_t dd = (uint32_t)(k >> shift) & dmask;
     const uint64_t g = s_gbase[dd] + (uint64_t)(i - (int)s_lbase[dd]);
     kout[g] = k;
@@ -232,8 +239,9 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   }
 }
 
-__global__ void k_sort_copy(const int32_t* __restrict__ plan, const uint64_t* __restrict__ k1,
-                            const uint32_t* __restrict__ v1, uint64_t* __restrict__ k0, uint32_t* __restrict__ v0,
+template <typename K>
+__global__ void k_sort_copy(const int32_t* __restrict__ plan, const K* __restrict__ k1,
+                            const uint32_t* __restrict__ v1, K* __restrict__ k0, uint32_t* __restrict__ v0,
                             int64_t P) {
   if (plan[kMaxPasses] == 0) return;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < P; i += (int64_t)gridDim.x * blockDim.x) {
@@ -287,21 +295,16 @@ int sort_significant_bits(int64_t num_tiles) {
   return 32 + tb;
 }
 
-size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles) {
-  const int passes = (sort_significant_bits(num_tiles) + 7) / 8;
-  return sort_layout(n_pairs, passes).total;
-}
+static int radix_passes(int lo, int hi) { return hi > lo ? (hi - lo + 7) / 8 : 0; }
 
-hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
-                       uint32_t* vals_tmp, int64_t* ranges, int32_t* order, void* ws, hipStream_t s) {
-  hipError_t e = launch_fill_u32(ranges, 4 * num_tiles, 0u, s);
-  if (e != hipSuccess) return e;
-  if (P == 0) {
-    if (order) k_tile_order<<<1, 1024, 0, s>>>(ranges, num_tiles, order);
-    return hipGetLastError();
-  }
-  const int sig = sort_significant_bits(num_tiles);
-  const int passes = (sig + 7) / 8;
+size_t radix_workspace_bytes(int64_t P, int lo, int hi) { return sort_layout(P, radix_passes(lo, hi)).total; }
+
+// Stable LSD sort of (keys, vals) by key bits [lo, hi); the result ends in keys/vals.
+template <typename K>
+static hipError_t radix_sort(int64_t P, K* keys, uint32_t* vals, K* keys_tmp, uint32_t* vals_tmp, int lo, int hi,
+                             void* ws, hipStream_t s) {
+  const int passes = radix_passes(lo, hi);
+  if (P <= 1 || passes == 0) return hipSuccess;
   const SortLayout l = sort_layout(P, passes);
   char* w = static_cast<char*>(ws);
   uint64_t* hist = reinterpret_cast<uint64_t*>(w + l.hist);
@@ -310,25 +313,44 @@ hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* v
   uint32_t* tickets = reinterpret_cast<uint32_t*>(w + l.tickets);
   uint64_t* status = reinterpret_cast<uint64_t*>(w + l.status);
   // zero histograms, plan, tickets and every pass's status words (no memset: capture-safe)
-  if ((e = launch_fill_u32(w, (int64_t)(l.total / 4), 0u, s)) != hipSuccess) return e;
+  hipError_t e = launch_fill_u32(w, (int64_t)(l.total / 4), 0u, s);
+  if (e != hipSuccess) return e;
   {
     const int64_t want = (P + kSortBlock * 16 - 1) / (kSortBlock * 16);
     const unsigned blocks = (unsigned)(want < 2048 ? (want > 0 ? want : 1) : 2048);
-    k_sort_hist<<<blocks, kSortBlock, 0, s>>>(keys, P, passes, hist);
+    k_sort_hist<K><<<blocks, kSortBlock, 0, s>>>(keys, P, lo, passes, hist);
   }
   k_sort_plan<<<1, kRadix, 0, s>>>(hist, dbase, plan, passes, (uint64_t)P);
   for (int p = 0; p < passes; ++p) {
-    const int bits = sig - 8 * p < 8 ? sig - 8 * p : 8;
-    k_onesweep<<<(unsigned)l.parts, kSortBlock, 0, s>>>(keys, vals, keys_tmp, vals_tmp, P, p, bits, plan,
-                                                      dbase + p * kRadix, status + (size_t)p * l.parts * kRadix,
-                                                      tickets);
+    const int bits = hi - lo - 8 * p < 8 ? hi - lo - 8 * p : 8;
+    k_onesweep<K><<<(unsigned)l.parts, kSortBlock, 0, s>>>(keys, vals, keys_tmp, vals_tmp, P, p, lo + 8 * p, bits,
+                                                          plan, dbase + p * kRadix,
+                                                          status + (size_t)p * l.parts * kRadix, tickets);
   }
-  {
-    const int64_t want = (P + 255) / 256;
-    const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
-    k_sort_copy<<<blocks, 256, 0, s>>>(plan, keys_tmp, vals_tmp, keys, vals, P);
-  }
-  k_ranges<<<(unsigned)((P + 255) / 256), 256, 0, s>>>(keys, P, num_tiles, ranges);
+  const int64_t want = (P + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+  k_sort_copy<K><<<blocks, 256, 0, s>>>(plan, keys_tmp, vals_tmp, keys, vals, P);
+  return hipGetLastError();
+}
+
+hipError_t radix_sort_u32(int64_t P, uint32_t* keys, uint32_t* vals, uint32_t* keys_tmp, uint32_t* vals_tmp, int lo,
+                          int hi, void* ws, hipStream_t s) {
+  return radix_sort<uint32_t>(P, keys, vals, keys_tmp, vals_tmp, lo, hi, ws, s);
+}
+
+size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_bits) {
+  return radix_workspace_bytes(n_pairs, sorted_low_bits, sort_significant_bits(num_tiles));
+}
+
+hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
+                       uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits, void* ws,
+                       hipStream_t s) {
+  hipError_t e = launch_fill_u32(ranges, 4 * num_tiles, 0u, s);
+  if (e == hipSuccess && P > 0)
+    e = radix_sort<uint64_t>(P, keys, vals, keys_tmp, vals_tmp, sorted_low_bits, sort_significant_bits(num_tiles),
+                             ws, s);
+  if (e != hipSuccess) return e;
+  if (P > 0) k_ranges<<<(unsigned)((P + 255) / 256), 256, 0, s>>>(keys, P, num_tiles, ranges);
   if (order) k_tile_order<<<1, 1024, 0, s>>>(ranges, num_tiles, order);
   return hipGetLastError();
 }

@@ -60,7 +60,7 @@ def lib():
         L.gs_workspace_bytes.argtypes = [i64, i64, i32]
         L.gs_workspace_bytes.restype = sz
         L.gs_bin_tiles.argtypes = [i64, GsProjected, C.POINTER(GsCamera), vp, vp, i64, C.POINTER(i64), vp, sz, vp]
-        L.gs_sort_keys.argtypes = [i64, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gs_sort_keys.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.gs_render_fwd.argtypes = [i64, GsProjected, vp, vp, vp, C.POINTER(GsCamera), C.POINTER(C.c_float), vp,
                                     vp, vp, vp]
         L.gs_render_bwd.argtypes = [i64, vp, vp, vp, vp, vp, i32, C.POINTER(GsCamera), GsProjected, vp, vp, vp,
@@ -150,11 +150,14 @@ def bin_tiles(proj: dict, cam, keys, vals, workspace, stream=None) -> tuple[int,
 
 
 def sort_keys(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, ranges, workspace, order=None,
-              stream=None):
-    """gs_sort_keys; ``order`` (int32 [num_tiles], optional) receives the longest-first tile order."""
-    _check(lib().gs_sort_keys(n_pairs, num_tiles, _ptr(keys), _ptr(vals), _ptr(keys_tmp), _ptr(vals_tmp),
-                              _ptr(ranges), _ptr(order), _ptr(workspace), workspace.numel(), _stream(stream)),
-           "gs_sort_keys")
+              sorted_low_bits: int = 32, stream=None):
+    """gs_sort_keys; ``order`` (int32 [num_tiles], optional) receives the longest-first tile order.
+
+    ``sorted_low_bits`` = 32 for pairs from gs_bin_tiles (already in depth order), 0 for
+    arbitrary keys."""
+    _check(lib().gs_sort_keys(n_pairs, num_tiles, int(sorted_low_bits), _ptr(keys), _ptr(vals), _ptr(keys_tmp),
+                              _ptr(vals_tmp), _ptr(ranges), _ptr(order), _ptr(workspace), workspace.numel(),
+                              _stream(stream)), "gs_sort_keys")
 
 
 def render_fwd(proj: dict, sorted_vals, ranges, cam, bg, image, final_T, n_contrib, order=None, stream=None):
@@ -232,18 +235,18 @@ class Rasterizer:
         ranges = torch.empty((tiles, 2), dtype=torch.int64, device=self.device)
         order = torch.empty(tiles, dtype=torch.int32, device=self.device)
         sort_keys(P, tiles, self.keys, self.vals, self.keys_tmp, self.vals_tmp, ranges, self.workspace, order,
-                  stream)
+                  stream=stream)
         image = torch.empty((3, H, W), dtype=torch.float32, device=self.device)
         final_T = torch.empty((H, W), dtype=torch.float32, device=self.device)
         n_contrib = torch.empty((H, W), dtype=torch.int32, device=self.device)
-        render_fwd(self.proj, self.vals, ranges, cam, bg, image, final_T, n_contrib, order, stream)
+        render_fwd(self.proj, self.vals, ranges, cam, bg, image, final_T, n_contrib, order, stream=stream)
         return dict(image=image, final_T=final_T, n_contrib=n_contrib, ranges=ranges, order=order, n_pairs=P,
                     keys=self.keys[:P], vals=self.vals[:P], proj=self.proj, cam=cam, bg=tuple(bg))
 
     def backward(self, fwd: dict, dL_dimage, accum=None, denom=None, stream=None) -> dict:
         return render_bwd(self.means, self.scales, self.quats, self.opac, self.sh, self.sh_degree, fwd["cam"],
                           fwd["proj"], self.vals, fwd["ranges"], fwd["bg"], fwd["final_T"], fwd["n_contrib"],
-                          dL_dimage, None, accum, denom, fwd.get("order"), stream)
+                          dL_dimage, None, accum, denom, fwd.get("order"), stream=stream)
 
 
 def scene_to_device(scene, device="cuda"):
