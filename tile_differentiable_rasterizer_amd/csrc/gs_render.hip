@@ -11,13 +11,19 @@
 // L2 norms of every pixel's 2D-mean gradient (the absolute gradient).
 //
 // Mapping: one 256-lane workgroup per 16x16 tile, one pixel per lane; wavefront w owns the
-// 8x8 quadrant (w & 1, w >> 1).  The tile's list is gathered 256 records at a time (one
-// per lane, the next batch prefetched into registers) and staged in LDS; every wavefront
-// then reads the records back as uniform broadcasts and skips, with a scalar branch, any
-// record whose support box misses its quadrant.  A pixel stops once T < 1e-4, a
-// wavefront once its 64 pixels have, the tile once all four have.  Tiles run in the order
-// given by tile_order (longest lists first) so that the long tiles start early.
+// 8x8 quadrant (w & 1, w >> 1).  The tile's list is gathered a batch at a time (one record
+// per lane, the next batch prefetched into registers) and staged in LDS with a 4-bit mask
+// of the quadrants each record's support box touches.  Each wavefront ballots that mask
+// and visits only its set bits, reading records back as uniform broadcasts, one record
+// ahead of the arithmetic.  A pixel stops once T < 1e-4, a wavefront once its 64 pixels
+// have, the tile once all four have.  Tiles run in the order given by tile_order (longest
+// lists first) so that the long tiles start early.
+//
+// The backward walks each wavefront's records in reverse three at a time and sums the
+// three records' ten per-pixel gradient terms over the wavefront in one transposed
+// reduction; the four quadrants' sums meet in LDS and leave as one atomic per value.
 #include "gs_device.h"
+#include "gs_wave.h"
 
 namespace gs {
 
@@ -54,22 +60,42 @@ __device__ __forceinline__ uint32_t quadrant_mask(uint32_t bx, uint32_t by, int 
   return (cy & 1u ? cx : 0u) | (cy & 2u ? cx << 2 : 0u);
 }
 
-// Sum over the 64 lanes of a wavefront; the total lands in lane 63.  DPP row operations
-// reduce each row of 16, then row broadcasts fold the four rows.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ float dpp_add(float x) {
-  const int t = __builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xF, false);
-  return x + __int_as_float(t);
+// Largest value over the box [X0, X1] x [Y0, Y1] (offsets from the 2D mean) of the
+// negative-definite exponent f = a2 x^2 + b2 x y + c2 y^2: 0 if the box holds the mean,
+// else the best of the four edges (on an edge f is a 1D concave quadratic, maximised at
+// its vertex clamped to the edge).
+__device__ __forceinline__ float box_max_exponent(float a2, float b2, float c2, float X0, float X1, float Y0,
+                                                  float Y1) {
+  if (X0 <= 0.0f && X1 >= 0.0f && Y0 <= 0.0f && Y1 >= 0.0f) return 0.0f;
+  const float ia = __builtin_amdgcn_rcpf(a2), ic = __builtin_amdgcn_rcpf(c2);
+  float best = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float X = e ? X1 : X0, Y = e ? Y1 : Y0;
+    const float ys = fminf(fmaxf(-0.5f * b2 * X * ic, Y0), Y1);
+    best = fmaxf(best, a2 * X * X + b2 * X * ys + c2 * ys * ys);
+    const float xs = fminf(fmaxf(-0.5f * b2 * Y * ia, X0), X1);
+    best = fmaxf(best, a2 * xs * xs + b2 * xs * Y + c2 * Y * Y);
+  }
+  return best;
 }
 
-__device__ __forceinline__ float wave_reduce_to_last(float v) {
-  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
-  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
-  v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
-  v = dpp_add<0x140, 0xF>(v);  // row_mirror
-  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
-  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
-  return v;
+// The quadrants of a tile whose pixel centres the record can reach with alpha >= 1/255:
+// the support box test, refined by the exact ellipse-versus-quadrant test with a margin of
+// 0.01 in the base-2 exponent (so float32 rounding in the per-pixel evaluation can never
+// make a skipped pixel reach the threshold).  s0, s1 are the staged record words.
+__device__ __forceinline__ uint32_t reach_mask(const float4 s0, const float4 s1, uint32_t bx, uint32_t by, int tx0,
+                                               int ty0) {
+  uint32_t m = quadrant_mask(bx, by, tx0, ty0);
+  if (!m) return 0u;
+  const float thr = __builtin_amdgcn_logf(kAlphaMin) - __builtin_amdgcn_logf(s1.y) - 0.01f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (!((m >> q) & 1u)) continue;
+    const float X0 = (float)(tx0 + (q & 1) * 8) + 0.5f - s0.x, Y0 = (float)(ty0 + (q >> 1) * 8) + 0.5f - s0.y;
+    if (box_max_exponent(s0.z, s0.w, s1.x, X0, X0 + 7.0f, Y0, Y0 + 7.0f) < thr) m &= ~(1u << q);
+  }
+  return m;
 }
 
 __device__ __forceinline__ int tile_of(const int32_t* __restrict__ order, int b) { return order ? order[b] : b; }
@@ -104,8 +130,8 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
       float4 s0, s1;
       stage_transform(p0, p1, s0, s1);
       s_rec[3 * t] = s0; s_rec[3 * t + 1] = s1; s_rec[3 * t + 2] = p2;
-      s_qm[t] = t < cnt ? (uint8_t)quadrant_mask(__float_as_uint(p2.y), __float_as_uint(p2.z), tx * kTile,
-                                                  ty * kTile)
+      s_qm[t] = t < cnt ? (uint8_t)reach_mask(s0, s1, __float_as_uint(p2.y), __float_as_uint(p2.z), tx * kTile,
+                                              ty * kTile)
                         : (uint8_t)0;
     }
     __syncthreads();
@@ -113,31 +139,36 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
       const uint32_t id = vals[b + kRenderBlock + t];
       p0 = rec[3 * (size_t)id]; p1 = rec[3 * (size_t)id + 1]; p2 = rec[3 * (size_t)id + 2];
     }
-    if (!__ballot(live)) continue;  // this wavefront's pixels are all done
-    bool wave_done = false;
-    for (int c = 0; c < cnt && !wave_done; c += kWave) {
+    const uint32_t kb = (uint32_t)(b - start) + 1u;  // list position + 1 of staged record 0
+    for (int c = 0; c < cnt; c += kWave) {
+      if (!__ballot(live)) break;  // this wavefront's pixels are all done
       // the records of this chunk that touch this wavefront's quadrant, as a scalar mask
       uint64_t m = __ballot((s_qm[c + lane] >> wave) & 1u);
-      while (m) {
-        const int j = c + __builtin_ctzll(m);
+      if (!m) continue;
+      int j = c + __builtin_ctzll(m);
+      m &= m - 1;
+      float4 a = s_rec[3 * j], e1 = s_rec[3 * j + 1];
+      float bb = s_rec[3 * j + 2].x;
+      while (true) {
+        // read the next record while this one is evaluated
+        const bool more = m != 0;
+        const int jn = more ? c + __builtin_ctzll(m) : j;
         m &= m - 1;
-        const float4 s0 = s_rec[3 * j], s1 = s_rec[3 * j + 1], s2 = s_rec[3 * j + 2];
-        bool finished = false;
-        if (live) {
-          const float dx = fx - s0.x, dy = fy - s0.y;
-          const float e = gauss_exponent(s0.z, s0.w, s1.x, dx, dy);
-          const float alpha = fminf(kAlphaMax, s1.y * gauss_factor(e));
-          if (alpha >= kAlphaMin) {
-            const float w = alpha * T;
-            cr = fmaf(s1.z, w, cr);
-            cg = fmaf(s1.w, w, cg);
-            cb = fmaf(s2.x, w, cb);
-            T = T * (1.0f - alpha);
-            nc = (uint32_t)(b - start + j + 1);
-            if (T < kTMin) { live = false; finished = true; }
-          }
-        }
-        if (__ballot(finished) && !__ballot(live)) { wave_done = true; break; }
+        const float4 an = s_rec[3 * jn], e1n = s_rec[3 * jn + 1];
+        const float bbn = s_rec[3 * jn + 2].x;
+
+        const float dx = fx - a.x, dy = fy - a.y;
+        const float alpha = fminf(kAlphaMax, e1.y * gauss_factor(gauss_exponent(a.z, a.w, e1.x, dx, dy)));
+        const bool take = live && alpha >= kAlphaMin;
+        const float w = take ? alpha * T : 0.0f;
+        cr = fmaf(e1.z, w, cr);
+        cg = fmaf(e1.w, w, cg);
+        cb = fmaf(bb, w, cb);
+        T = take ? T * (1.0f - alpha) : T;
+        nc = take ? kb + (uint32_t)j : nc;
+        live = live && !(T < kTMin);
+        if (!more) break;
+        a = an; e1 = e1n; bb = bbn; j = jn;
       }
     }
   }
@@ -150,6 +181,54 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
     final_T[o] = T;
     n_contrib[o] = nc;
   }
+}
+
+// Per-lane state of the reverse walk for one pixel.
+struct BwdPixel {
+  float fx, fy;        // pixel centre
+  float T;             // transmittance behind the next record to visit
+  float hr, hg, hb;    // colour behind it (including the background's share)
+  float dr, dg, db;    // dL/dpixel
+  uint32_t nc;         // records at positions >= nc did not contribute
+};
+
+// One record's ten gradient terms at this lane's pixel (zeros if it did not contribute);
+// updates the walk state.  Returns whether it contributed.
+__device__ __forceinline__ bool bwd_record(const float4* __restrict__ s_rec, int j, uint32_t k, BwdPixel& p,
+                                           float (&g)[GS_GRAD_SCREEN]) {
+#pragma unroll
+  for (int e = 0; e < GS_GRAD_SCREEN; ++e) g[e] = 0.0f;
+  const float4 s0 = s_rec[4 * j], s1 = s_rec[4 * j + 1], s2 = s_rec[4 * j + 2], s3 = s_rec[4 * j + 3];
+  if (!(k < p.nc)) return false;
+  const float dx = p.fx - s0.x, dy = p.fy - s0.y;
+  const float G = gauss_factor(gauss_exponent(s0.z, s0.w, s1.x, dx, dy));
+  const float oG = s1.y * G;
+  const float alpha = fminf(kAlphaMax, oG);
+  if (!(alpha >= kAlphaMin)) return false;
+  // hardware reciprocal (about 1 ulp): T is recovered from the stored final T by repeated
+  // division, whose float32 error stays far below the gradient tolerance
+  const float iom = __builtin_amdgcn_rcpf(1.0f - alpha);
+  const float Tk = p.T * iom;  // transmittance in front of this Gaussian
+  const float w = alpha * Tk;
+  g[6] = p.dr * w;
+  g[7] = p.dg * w;
+  g[8] = p.db * w;
+  const float dalpha = p.dr * (s1.z * Tk - p.hr * iom) + p.dg * (s1.w * Tk - p.hg * iom) + p.db * (s2.x * Tk - p.hb * iom);
+  p.hr = fmaf(s1.z, w, p.hr);
+  p.hg = fmaf(s1.w, w, p.hg);
+  p.hb = fmaf(s2.x, w, p.hb);
+  p.T = Tk;
+  if (oG <= kAlphaMax) {  // the clamp at 0.99 stops the gradient
+    g[5] = dalpha * G;
+    const float dq = -0.5f * dalpha * oG;  // dL/dq, q = A dx^2 + 2 B dx dy + C dy^2
+    g[2] = dq * dx * dx;
+    g[3] = dq * 2.0f * dx * dy;
+    g[4] = dq * dy * dy;
+    g[0] = -2.0f * dq * fmaf(s3.x, dx, s3.y * dy);
+    g[1] = -2.0f * dq * fmaf(s3.y, dx, s3.z * dy);
+    g[9] = __builtin_amdgcn_sqrtf(fmaf(g[0], g[0], g[1] * g[1]));
+  }
+  return true;
 }
 
 __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
@@ -167,19 +246,19 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
   const int t = threadIdx.x, lane = __lane_id(), wave = t / kWave;
   const int qx0 = tx * kTile + (wave & 1) * 8, qy0 = ty * kTile + (wave >> 1) * 8;
   const int px = qx0 + (lane & 7), py = qy0 + (lane >> 3);
-  const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
   const size_t plane = (size_t)W * H;
-  float T = 1.0f, dr = 0.0f, dg = 0.0f, db = 0.0f;
-  uint32_t nc = 0;
+  BwdPixel p;
+  p.fx = (float)px + 0.5f;
+  p.fy = (float)py + 0.5f;
+  p.T = 1.0f; p.dr = p.dg = p.db = 0.0f; p.nc = 0;
   if (px < W && py < H) {
     const size_t o = (size_t)py * W + px;
-    T = final_T[o];
-    nc = n_contrib[o];
-    dr = dL[o]; dg = dL[plane + o]; db = dL[2 * plane + o];
+    p.T = final_T[o];
+    p.nc = n_contrib[o];
+    p.dr = dL[o]; p.dg = dL[plane + o]; p.db = dL[2 * plane + o];
   }
-  // colour behind the current contributor, starting with the background's share
-  float hr = bg0 * T, hg = bg1 * T, hb = bg2 * T;
-  const uint32_t wlast = wave_max(nc);  // this wavefront walks [0, wlast)
+  p.hr = bg0 * p.T; p.hg = bg1 * p.T; p.hb = bg2 * p.T;
+  const uint32_t wlast = wave_max(p.nc);  // this wavefront walks [0, wlast)
   if (lane == 0) s_last[wave] = wlast;
   __syncthreads();
   uint32_t last = 0;
@@ -199,7 +278,7 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
       s_rec[4 * t + 1] = s1;
       s_rec[4 * t + 2] = make_float4(r2.x, r2.y, r2.z, __uint_as_float(id));
       s_rec[4 * t + 3] = make_float4(r0.z, r0.w, r1.x, 0.0f);
-      s_qm[t] = (uint8_t)quadrant_mask(__float_as_uint(r2.y), __float_as_uint(r2.z), tx * kTile, ty * kTile);
+      s_qm[t] = (uint8_t)reach_mask(s0, s1, __float_as_uint(r2.y), __float_as_uint(r2.z), tx * kTile, ty * kTile);
     } else if (t < kBwdBatch) {
       s_qm[t] = 0;
     }
@@ -210,60 +289,47 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
     __syncthreads();
     const int jtop = (int)min((int64_t)cnt, (int64_t)wlast - (lo - start));  // records this wave may use
     for (int c = ((jtop - 1) / kWave) * kWave; c >= 0 && jtop > 0; c -= kWave) {
-     uint64_t m = __ballot(c + lane < jtop && ((s_qm[c + lane] >> wave) & 1u));
-     while (m) {  // highest position first: the reverse walk
-      const int bit = 63 - __builtin_clzll(m);
-      m &= ~(1ull << bit);
-      const int j = c + bit;
-      const uint32_t k = (uint32_t)(lo - start + j);  // position in the tile's list
-      const float4 s0 = s_rec[4 * j], s1 = s_rec[4 * j + 1], s2 = s_rec[4 * j + 2];
-      float g0 = 0.f, g1 = 0.f, g2 = 0.f, g3 = 0.f, g4 = 0.f, g5 = 0.f, g6 = 0.f, g7 = 0.f, g8 = 0.f, g9 = 0.f;
-      bool hit = false;
-      if (k < nc) {
-        const float dx = fx - s0.x, dy = fy - s0.y;
-        const float e = gauss_exponent(s0.z, s0.w, s1.x, dx, dy);
-        const float G = gauss_factor(e);
-        const float oG = s1.y * G;
-        const float alpha = fminf(kAlphaMax, oG);
-        if (alpha >= kAlphaMin) {
-          hit = true;
-          const float iom = 1.0f / (1.0f - alpha);
-          const float Tk = T * iom;  // transmittance in front of this Gaussian
-          const float w = alpha * Tk;
-          g6 = dr * w;
-          g7 = dg * w;
-          g8 = db * w;
-          const float dalpha = dr * (s1.z * Tk - hr * iom) + dg * (s1.w * Tk - hg * iom) + db * (s2.x * Tk - hb * iom);
-          hr = fmaf(s1.z, w, hr);
-          hg = fmaf(s1.w, w, hg);
-          hb = fmaf(s2.x, w, hb);
-          T = Tk;
-          if (oG <= kAlphaMax) {  // the clamp at 0.99 stops the gradient
-            const float4 s3 = s_rec[4 * j + 3];
-            g5 = dalpha * G;
-            const float dq = -0.5f * dalpha * oG;  // dL/dq, q = A dx^2 + 2 B dx dy + C dy^2
-            g2 = dq * dx * dx;
-            g3 = dq * 2.0f * dx * dy;
-            g4 = dq * dy * dy;
-            g0 = -2.0f * dq * fmaf(s3.x, dx, s3.y * dy);
-            g1 = -2.0f * dq * fmaf(s3.y, dx, s3.z * dy);
-            g9 = sqrtf(fmaf(g0, g0, g1 * g1));
+      uint64_t m = __ballot(c + lane < jtop && ((s_qm[c + lane] >> wave) & 1u));
+      while (m) {
+        // the next three records of the reverse walk (highest position first)
+        int js[3];
+        bool has[3];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          has[r] = m != 0;
+          js[r] = has[r] ? c + 63 - __builtin_clzll(m) : c;
+          if (has[r]) m &= ~(1ull << (js[r] - c));
+        }
+        float v[32];
+        bool hit[3];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          float g[GS_GRAD_SCREEN];
+          hit[r] = has[r] ? bwd_record(s_rec, js[r], (uint32_t)(lo - start + js[r]), p, g) : false;
+          if (!has[r]) {
+#pragma unroll
+            for (int e = 0; e < GS_GRAD_SCREEN; ++e) g[e] = 0.0f;
+          }
+#pragma unroll
+          for (int e = 0; e < GS_GRAD_SCREEN; ++e) v[GS_GRAD_SCREEN * r + e] = g[e];
+        }
+        v[30] = 0.0f;
+        v[31] = 0.0f;
+        const uint64_t h0 = __ballot(hit[0]), h1 = __ballot(hit[1]), h2 = __ballot(hit[2]);
+        if (h0 | h1 | h2) {
+          // lanes 2i and 2i + 1 now hold the wavefront's sum of v[i]
+          const float sum = wave_transpose_reduce32(v);
+          const int idx = lane >> 1, r = idx / GS_GRAD_SCREEN, e = idx - r * GS_GRAD_SCREEN;
+          const bool rec_hit = r == 0 ? h0 != 0 : r == 1 ? h1 != 0 : r == 2 ? h2 != 0 : false;
+          const int jr = r == 0 ? js[0] : r == 1 ? js[1] : js[2];
+          if ((lane & 1) == 0 && rec_hit) s_part[wave][jr][e] = sum;
+          if (lane == 0) {
+            if (h0) s_hit[wave][js[0]] = 1;
+            if (h1) s_hit[wave][js[1]] = 1;
+            if (h2) s_hit[wave][js[2]] = 1;
           }
         }
       }
-      if (__ballot(hit)) {
-        g0 = wave_reduce_to_last(g0); g1 = wave_reduce_to_last(g1); g2 = wave_reduce_to_last(g2);
-        g3 = wave_reduce_to_last(g3); g4 = wave_reduce_to_last(g4); g5 = wave_reduce_to_last(g5);
-        g6 = wave_reduce_to_last(g6); g7 = wave_reduce_to_last(g7); g8 = wave_reduce_to_last(g8);
-        g9 = wave_reduce_to_last(g9);
-        if (lane == kWave - 1) {
-          float* p = s_part[wave][j];
-          p[0] = g0; p[1] = g1; p[2] = g2; p[3] = g3; p[4] = g4;
-          p[5] = g5; p[6] = g6; p[7] = g7; p[8] = g8; p[9] = g9;
-          s_hit[wave][j] = 1;
-        }
-      }
-     }
     }
     __syncthreads();
     // one thread per record: combine the four quadrants, then one atomic per value

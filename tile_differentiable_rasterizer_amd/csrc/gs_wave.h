@@ -1,0 +1,64 @@
+// gs_wave.h -- wavefront-wide reductions for the 64-lane gfx950 wavefront.
+// Internal to libgsraster.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace gs {
+
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_get(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xF, false));
+}
+
+// Sum over the 64 lanes; the total lands in lane 63.  DPP row operations reduce each row
+// of 16, then row broadcasts fold the four rows.
+__device__ __forceinline__ float wave_reduce_to_last(float v) {
+  v += dpp_get<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_get<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_get<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_get<0x140, 0xF>(v);  // row_mirror
+  v += dpp_get<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_get<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Transposed reduction of 32 per-lane values: on return lanes 2i and 2i + 1 hold the sum
+// over all 64 lanes of v[i].  Each butterfly step halves the values a lane keeps:
+// bit 5 and bit 4 of the lane id with the gfx950 half/row swaps, bits 3, 2 and 1 with DPP
+// (row rotate by 8, half-row mirror, quad permute) and a select of the half to keep;
+// the last step (bit 0) adds the one remaining value of the neighbouring lane.
+// About 70 instructions for 32 sums, against 6 per value for independent reductions.
+__device__ __forceinline__ float wave_transpose_reduce32(const float (&v)[32]) {
+  const int lane = __lane_id();
+  float w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // lanes < 32 keep v[i], lanes >= 32 keep v[i + 16]
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 16]), false, false);
+    w[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // rows 0, 2 keep w[i]; rows 1, 3 keep w[i + 8]
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[i]), __float_as_uint(w[i + 8]), false, false);
+    x[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const bool b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1;
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // partner: lane ^ 8 (rotate by 8 inside the row)
+    const float keep = b3 ? x[i + 4] : x[i], send = b3 ? x[i] : x[i + 4];
+    y[i] = keep + dpp_get<0x128, 0xF>(send);
+  }
+  float z[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // partner: the mirror lane inside the half row (bit 2 differs)
+    const float keep = b2 ? y[i + 2] : y[i], send = b2 ? y[i] : y[i + 2];
+    z[i] = keep + dpp_get<0x141, 0xF>(send);
+  }
+  const float keep = b1 ? z[1] : z[0], send = b1 ? z[0] : z[1];
+  float t = keep + dpp_get<0x4E, 0xF>(send);  // partner: lane ^ 2
+  return t + dpp_get<0xB1, 0xF>(t);            // partner: lane ^ 1
+}
+
+}  // namespace gs
