@@ -29,11 +29,17 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 2.4e9 * 64 / 1e12   # non-packed fp32 lane-ops/s: 39.3 T
 TMIN = float(np.float32(1e-4))
 
-# Algorithmic VALU lane-operations per (pixel, list entry) evaluation of the plain
-# compositing rule: offset (2), quadratic form (5), exp (counted as 4 issue slots, the
-# transcendental rate is a quarter), opacity product and clamp (2), threshold test (1),
-# weight (1), colour accumulate (3), transmittance update (2), stop test (1).
+# Algorithmic VALU lane-operations of the plain per-pixel loops.
+# Forward, per (pixel, list entry) evaluation: offset (2), quadratic form (5), exp (counted
+# as 4 issue slots: the transcendental rate is a quarter), opacity product and clamp (2),
+# threshold test (1), weight (1), colour accumulate (3), transmittance update (2), stop
+# test (1).
 OPS_PER_EVAL_FWD = 21
+# Backward, per (pixel, contributor) of the reverse walk: the alpha re-evaluation (14),
+# transmittance recovery (reciprocal as 4 slots + 1), colour weights (4), d alpha (9),
+# colour-behind update (3), clamp test (1), the conic/mean/opacity terms (14) and the norm
+# of the mean gradient (sqrt as 4 slots + 1).
+OPS_PER_EVAL_BWD = 55
 
 
 def log(msg):
@@ -150,7 +156,7 @@ def main():
     # algorithmic work per launch (camera-averaged) for the roofline
     P_mean = float(np.mean(pairs))
     K = (sc.sh_degree + 1) ** 2
-    visited = []
+    visited, contrib = [], []
     for k, cam in enumerate(cams):
         rg = ranges[k]
         lens = (rg[:, 1] - rg[:, 0]).cpu().numpy()
@@ -158,33 +164,37 @@ def main():
         nc = ncon[k].cpu().numpy().astype(np.int64)
         stopped = finalT[k].cpu().numpy() < TMIN
         visited.append(float(np.where(stopped, nc, tl).sum()))
+        contrib.append(float(nc.sum()))
     evals = float(np.mean(visited))
-    passes = 6  # 32 depth bits + 13 tile bits, 8 bits per pass
+    walk = float(np.mean(contrib))
+    V = float(N)  # visible Gaussians bound the per-Gaussian binning work
     algo = {
         "project": ("hbm", N * (12 + 12 + 16 + 4 + 12 * K) + N * (48 + 4 + 8 + 4 + 1)),
-        "bin": ("hbm", N * 4 + N * (4 + 8 + 4) + 12 * P_mean),
-        "sort": ("hbm", 8 * P_mean + passes * 24 * P_mean + 8 * P_mean + 16 * tiles),
+        # count (4 B/G), compaction (8 read + 8 written per visible), depth sort (3 passes of
+        # 16 B per visible + 4 B histogram), emission (20 B read per visible + 12 B per pair)
+        "bin": ("hbm", 4 * N + 16 * V + (3 * 16 + 4) * V + 20 * V + 12 * P_mean),
+        # histogram (8 B/pair), 2 passes x 24 B/pair, ranges (8 B/pair + 16 B/tile)
+        "sort": ("hbm", 8 * P_mean + 2 * 24 * P_mean + 8 * P_mean + 16 * tiles),
         "render_fwd": ("alu", OPS_PER_EVAL_FWD * evals),
+        "render_bwd": ("alu", OPS_PER_EVAL_BWD * walk),
     }
     avg = {s: float(np.mean(times[s])) for s in stages if times[s]}
-    dom = max(("project", "bin", "sort", "render_fwd"), key=lambda s: avg[s])
-    bound, work = algo[dom]
-    if bound == "hbm":
-        ach = work / (avg[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
-    else:
-        ach = work / (avg[dom] * 1e-3) / 1e12
-        roof = {"bound": "alu", "kernel": dom, "achieved": round(ach, 2), "peak": round(VALU_PEAK_TOPS, 1),
-                "unit": "Tlane-op/s", "frac": round(ach / VALU_PEAK_TOPS, 4), "traffic": None}
-    stage_report = {}
-    for s in stages:
-        if not times[s]:
-            continue
-        d = {"ms": round(avg[s], 4)}
-        if s in algo and algo[s][0] == "hbm":
-            d["GB/s"] = round(algo[s][1] / (avg[s] * 1e-3) / 1e9, 1)
-        stage_report[s] = d
+
+    def roof(stage):
+        bound, work = algo[stage]
+        if bound == "hbm":
+            ach = work / (avg[stage] * 1e-3) / 1e9
+            return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4)}
+        ach = work / (avg[stage] * 1e-3) / 1e12
+        return {"bound": "alu", "achieved": round(ach, 2), "peak": round(VALU_PEAK_TOPS, 1),
+                "unit": "Tlane-op/s", "frac": round(ach / VALU_PEAK_TOPS, 4)}
+
+    dom = max(algo, key=lambda s: avg[s])
+    kernels = {"project": "k_project", "bin": "gs_bin_tiles kernels", "sort": "gs_sort_keys kernels",
+               "render_fwd": "k_render_fwd", "render_bwd": "gs_render_bwd (fill + k_render_bwd + k_project_bwd)"}
+    roof_dom = dict(roof(dom), kernel=kernels[dom], traffic=None)
+    stage_report = {s: dict(ms=round(avg[s], 4), **roof(s)) for s in algo}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -208,9 +218,10 @@ def main():
                    "mean_pairs_per_frame": int(P_mean)},
         "mpixels_per_s": round(value * W * H / 1e6, 1),
         "forward_only": {"frames_per_s": round(fwd_fps, 2), "mpixels_per_s": round(fwd_fps * W * H / 1e6, 1)},
-        "stages_ms": stage_report,
+        "stages": stage_report,
         "evaluations_per_frame": int(evals),
-        "roofline": roof,
+        "contributor_walk_per_frame": int(walk),
+        "roofline": roof_dom,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

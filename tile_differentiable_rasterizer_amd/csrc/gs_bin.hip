@@ -161,6 +161,8 @@ __global__ __launch_bounds__(kBinBlock) void k_emit(int64_t v, const uint32_t* _
                                                     uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
   __shared__ uint64_t s_off[kBinChunk + 1];  // exclusive offsets relative to the block
   __shared__ uint32_t s_id[kBinChunk];
+  __shared__ ushort4 s_rect[kBinChunk];      // the block's Gaussians, gathered once
+  __shared__ uint32_t s_depth[kBinChunk];
   __shared__ uint64_t s_w[kBinBlock / kWave];
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
@@ -173,6 +175,10 @@ __global__ __launch_bounds__(kBinBlock) void k_emit(int64_t v, const uint32_t* _
     const uint32_t g = i < v ? order[i] : 0u;
     s_id[tid * kBinPer + j] = g;
     cnt[j] = i < v ? n_tiles[g] : 0u;
+    if (i < v) {
+      s_rect[tid * kBinPer + j] = rect[g];
+      s_depth[tid * kBinPer + j] = __float_as_uint(depth[g]);
+    }
     tsum += cnt[j];
   }
   const uint64_t inc = wave_inclusive_scan(tsum);
@@ -190,23 +196,41 @@ __global__ __launch_bounds__(kBinBlock) void k_emit(int64_t v, const uint32_t* _
   const uint64_t total = s_off[kBinChunk];
   const uint64_t out0 = block_off[blockIdx.x];
   const int ng = (int)min((int64_t)kBinChunk, v - base);
-  for (uint64_t p = tid; p < total; p += kBinBlock) {
-    // last position lo with s_off[lo] <= p (its n_tiles > 0 since p < s_off[lo + 1])
-    int lo = 0, hi = ng;  // invariant: s_off[lo] <= p < s_off[hi]
+  // each lane writes kEmitRun consecutive pairs: one binary search for the first, then walk
+  // the Gaussians' tiles row by row; a wavefront's stores cover 64 * kEmitRun consecutive pairs
+  constexpr int kEmitRun = 8;
+  for (uint64_t chunk = 0; chunk < total; chunk += (uint64_t)kBinBlock * kEmitRun) {
+    const uint64_t p0 = chunk + (uint64_t)tid * kEmitRun;
+    if (p0 >= total) continue;
+    int lo = 0, hi = ng;  // invariant: s_off[lo] <= p0 < s_off[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (s_off[mid] <= p) lo = mid; else hi = mid;
+      if (s_off[mid] <= p0) lo = mid; else hi = mid;
     }
-    const uint32_t g = s_id[lo];
-    const uint32_t local = (uint32_t)(p - s_off[lo]);
-    const ushort4 r = rect[g];
-    const uint32_t w = (uint32_t)r.y - (uint32_t)r.x + 1u;
-    const uint32_t row = local / w;
-    const uint32_t tx = (uint32_t)r.x + (local - row * w);
-    const uint32_t ty = (uint32_t)r.z + row;
-    const uint64_t tile = (uint64_t)ty * (uint64_t)tiles_x + tx;
-    keys[out0 + p] = (tile << 32) | (uint64_t)__float_as_uint(depth[g]);
-    vals[out0 + p] = g;
+    uint32_t local = (uint32_t)(p0 - s_off[lo]);
+    ushort4 r = s_rect[lo];
+    uint32_t w = (uint32_t)r.y - (uint32_t)r.x + 1u;
+    uint32_t row = local / w, col = local - row * w;
+    uint64_t next = s_off[lo + 1];
+    const int run = (int)min((uint64_t)kEmitRun, total - p0);
+    for (int i = 0; i < run; ++i) {
+      const uint64_t p = p0 + (uint64_t)i;
+      while (p >= next) {  // on to the next Gaussian (every visible one has n_tiles > 0)
+        ++lo;
+        r = s_rect[lo];
+        w = (uint32_t)r.y - (uint32_t)r.x + 1u;
+        row = 0;
+        col = 0;
+        next = s_off[lo + 1];
+      }
+      const uint64_t tile = (uint64_t)((uint32_t)r.z + row) * (uint64_t)tiles_x + ((uint32_t)r.x + col);
+      keys[out0 + p] = (tile << 32) | (uint64_t)s_depth[lo];
+      vals[out0 + p] = s_id[lo];
+      if (++col == w) {
+        col = 0;
+        ++row;
+      }
+    }
   }
 }
 

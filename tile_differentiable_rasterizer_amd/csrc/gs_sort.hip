@@ -142,6 +142,9 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   __syncthreads();
   const int64_t part = s_part;
   const int64_t base = part * kSortPart;
+  // start the look-back now: the predecessor's word for this thread's digit is usually
+  // final by the time this partition has ranked its keys
+  uint64_t early = part > 0 ? status_load(status + (part - 1) * kRadix + tid) : 0;
 
   // wave-striped: wave w owns keys [w*1024, (w+1)*1024) of the partition, in order
   K key[kSortKPT];
@@ -214,7 +217,9 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   if (part > 0) {
     int64_t p = part - 1;
     while (true) {
-      const uint64_t sv = status_load(status + p * kRadix + d);
+      uint64_t sv = early;
+      early = 0;
+      if (!(sv & ~kValMask)) sv = status_load(status + p * kRadix + d);
       const uint64_t flag = sv & ~kValMask;
       if (flag == 0) {
         __builtin_amdgcn_s_sleep(1);
