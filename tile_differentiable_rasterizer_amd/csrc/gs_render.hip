@@ -192,43 +192,44 @@ struct BwdPixel {
   uint32_t nc;         // records at positions >= nc did not contribute
 };
 
-// One record's ten gradient terms at this lane's pixel (zeros if it did not contribute);
-// updates the walk state.  Returns whether it contributed.
+// One record's ten gradient terms at this lane's pixel, written to g[0..9]; zeros where the
+// record did not contribute (a later position than the pixel's last contributor, or
+// alpha < 1/255).  Branch-free: a non-contributing lane computes with a zero upstream
+// gradient and keeps its walk state.  Returns whether this lane's pixel contributed.
 __device__ __forceinline__ bool bwd_record(const float4* __restrict__ s_rec, int j, uint32_t k, BwdPixel& p,
-                                           float (&g)[GS_GRAD_SCREEN]) {
-#pragma unroll
-  for (int e = 0; e < GS_GRAD_SCREEN; ++e) g[e] = 0.0f;
+                                           float* __restrict__ g) {
   const float4 s0 = s_rec[4 * j], s1 = s_rec[4 * j + 1], s2 = s_rec[4 * j + 2], s3 = s_rec[4 * j + 3];
-  if (!(k < p.nc)) return false;
   const float dx = p.fx - s0.x, dy = p.fy - s0.y;
   const float G = gauss_factor(gauss_exponent(s0.z, s0.w, s1.x, dx, dy));
   const float oG = s1.y * G;
   const float alpha = fminf(kAlphaMax, oG);
-  if (!(alpha >= kAlphaMin)) return false;
+  const bool contrib = k < p.nc && alpha >= kAlphaMin;
+  const float dr = contrib ? p.dr : 0.0f, dg = contrib ? p.dg : 0.0f, db = contrib ? p.db : 0.0f;
   // hardware reciprocal (about 1 ulp): T is recovered from the stored final T by repeated
   // division, whose float32 error stays far below the gradient tolerance
   const float iom = __builtin_amdgcn_rcpf(1.0f - alpha);
   const float Tk = p.T * iom;  // transmittance in front of this Gaussian
   const float w = alpha * Tk;
-  g[6] = p.dr * w;
-  g[7] = p.dg * w;
-  g[8] = p.db * w;
-  const float dalpha = p.dr * (s1.z * Tk - p.hr * iom) + p.dg * (s1.w * Tk - p.hg * iom) + p.db * (s2.x * Tk - p.hb * iom);
-  p.hr = fmaf(s1.z, w, p.hr);
-  p.hg = fmaf(s1.w, w, p.hg);
-  p.hb = fmaf(s2.x, w, p.hb);
-  p.T = Tk;
-  if (oG <= kAlphaMax) {  // the clamp at 0.99 stops the gradient
-    g[5] = dalpha * G;
-    const float dq = -0.5f * dalpha * oG;  // dL/dq, q = A dx^2 + 2 B dx dy + C dy^2
-    g[2] = dq * dx * dx;
-    g[3] = dq * 2.0f * dx * dy;
-    g[4] = dq * dy * dy;
-    g[0] = -2.0f * dq * fmaf(s3.x, dx, s3.y * dy);
-    g[1] = -2.0f * dq * fmaf(s3.y, dx, s3.z * dy);
-    g[9] = __builtin_amdgcn_sqrtf(fmaf(g[0], g[0], g[1] * g[1]));
+  g[6] = dr * w;
+  g[7] = dg * w;
+  g[8] = db * w;
+  float dalpha = dr * (s1.z * Tk - p.hr * iom) + dg * (s1.w * Tk - p.hg * iom) + db * (s2.x * Tk - p.hb * iom);
+  if (contrib) {
+    p.hr = fmaf(s1.z, w, p.hr);
+    p.hg = fmaf(s1.w, w, p.hg);
+    p.hb = fmaf(s2.x, w, p.hb);
+    p.T = Tk;
   }
-  return true;
+  dalpha = oG <= kAlphaMax ? dalpha : 0.0f;  // the clamp at 0.99 stops the gradient
+  g[5] = dalpha * G;
+  const float dq = -0.5f * dalpha * oG;  // dL/dq, q = A dx^2 + 2 B dx dy + C dy^2
+  g[2] = dq * dx * dx;
+  g[3] = dq * 2.0f * dx * dy;
+  g[4] = dq * dy * dy;
+  g[0] = -2.0f * dq * fmaf(s3.x, dx, s3.y * dy);
+  g[1] = -2.0f * dq * fmaf(s3.y, dx, s3.z * dy);
+  g[9] = __builtin_amdgcn_sqrtf(fmaf(g[0], g[0], g[1] * g[1]));
+  return contrib;
 }
 
 __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
@@ -237,8 +238,6 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
     const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib, const float* __restrict__ dL,
     float* __restrict__ gscreen) {
   __shared__ float4 s_rec[kBwdBatch * 4];
-  __shared__ float s_part[kRenderWaves][kBwdBatch][GS_GRAD_SCREEN];
-  __shared__ uint8_t s_hit[kRenderWaves][kBwdBatch];
   __shared__ uint8_t s_qm[kBwdBatch];
   __shared__ uint32_t s_last[kRenderWaves];
   const int tile = tile_of(order, blockIdx.x);
@@ -265,13 +264,24 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
 #pragma unroll
   for (int w = 0; w < kRenderWaves; ++w) last = s_last[w] > last ? s_last[w] : last;
   const int64_t start = ranges[2 * tile];
+  // batches walk down from the last contributor; each one's records are gathered into
+  // registers while the previous batch is processed
+  uint32_t pid = 0;
+  float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0, q2 = q0;
+  {
+    const int64_t hi = start + last, lo = hi - kBwdBatch > start ? hi - kBwdBatch : start;
+    if (t < hi - lo) {
+      pid = vals[lo + t];
+      q0 = rec[3 * (size_t)pid]; q1 = rec[3 * (size_t)pid + 1]; q2 = rec[3 * (size_t)pid + 2];
+    }
+  }
   for (int64_t hi = start + last; hi > start; hi -= kBwdBatch) {
     const int64_t lo = hi - kBwdBatch > start ? hi - kBwdBatch : start;
     const int cnt = (int)(hi - lo);
-    __syncthreads();  // the previous batch's partial sums have been flushed
+    __syncthreads();  // every wavefront is done with the previous batch
     if (t < cnt) {
-      const uint32_t id = vals[lo + t];
-      const float4 r0 = rec[3 * (size_t)id], r1 = rec[3 * (size_t)id + 1], r2 = rec[3 * (size_t)id + 2];
+      const uint32_t id = pid;
+      const float4 r0 = q0, r1 = q1, r2 = q2;
       float4 s0, s1;
       stage_transform(r0, r1, s0, s1);
       s_rec[4 * t] = s0;
@@ -282,75 +292,56 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
     } else if (t < kBwdBatch) {
       s_qm[t] = 0;
     }
-    if (t < kBwdBatch) {
-#pragma unroll
-      for (int w = 0; w < kRenderWaves; ++w) s_hit[w][t] = 0;
-    }
     __syncthreads();
+    {  // prefetch the next (earlier) batch
+      const int64_t nhi = lo, nlo = nhi - kBwdBatch > start ? nhi - kBwdBatch : start;
+      if (t < nhi - nlo) {
+        pid = vals[nlo + t];
+        q0 = rec[3 * (size_t)pid]; q1 = rec[3 * (size_t)pid + 1]; q2 = rec[3 * (size_t)pid + 2];
+      }
+    }
     const int jtop = (int)min((int64_t)cnt, (int64_t)wlast - (lo - start));  // records this wave may use
     for (int c = ((jtop - 1) / kWave) * kWave; c >= 0 && jtop > 0; c -= kWave) {
       uint64_t m = __ballot(c + lane < jtop && ((s_qm[c + lane] >> wave) & 1u));
       while (m) {
-        // the next three records of the reverse walk (highest position first)
+        // the next three records of the reverse walk (highest position first); the bit
+        // positions stay scalar so the walk is a uniform loop
         int js[3];
         bool has[3];
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
           has[r] = m != 0;
-          js[r] = has[r] ? c + 63 - __builtin_clzll(m) : c;
-          if (has[r]) m &= ~(1ull << (js[r] - c));
+          const int bit = has[r] ? __builtin_amdgcn_readfirstlane(63 - __builtin_clzll(m)) : 0;
+          js[r] = c + bit;
+          if (has[r]) m &= ~(1ull << bit);
         }
         float v[32];
         bool hit[3];
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
-          float g[GS_GRAD_SCREEN];
-          hit[r] = has[r] ? bwd_record(s_rec, js[r], (uint32_t)(lo - start + js[r]), p, g) : false;
-          if (!has[r]) {
+          if (has[r]) {
+            hit[r] = bwd_record(s_rec, js[r], (uint32_t)(lo - start + js[r]), p, v + GS_GRAD_SCREEN * r);
+          } else {
+            hit[r] = false;
 #pragma unroll
-            for (int e = 0; e < GS_GRAD_SCREEN; ++e) g[e] = 0.0f;
+            for (int e = 0; e < GS_GRAD_SCREEN; ++e) v[GS_GRAD_SCREEN * r + e] = 0.0f;
           }
-#pragma unroll
-          for (int e = 0; e < GS_GRAD_SCREEN; ++e) v[GS_GRAD_SCREEN * r + e] = g[e];
         }
         v[30] = 0.0f;
         v[31] = 0.0f;
         const uint64_t h0 = __ballot(hit[0]), h1 = __ballot(hit[1]), h2 = __ballot(hit[2]);
         if (h0 | h1 | h2) {
-          // lanes 2i and 2i + 1 now hold the wavefront's sum of v[i]
+          // lanes 2i and 2i + 1 now hold the wavefront's sum of v[i]; the even lane of each
+          // (record, value) pair adds it to the Gaussian's gradient: one atomic instruction
           const float sum = wave_transpose_reduce32(v);
           const int idx = lane >> 1, r = idx / GS_GRAD_SCREEN, e = idx - r * GS_GRAD_SCREEN;
           const bool rec_hit = r == 0 ? h0 != 0 : r == 1 ? h1 != 0 : r == 2 ? h2 != 0 : false;
           const int jr = r == 0 ? js[0] : r == 1 ? js[1] : js[2];
-          if ((lane & 1) == 0 && rec_hit) s_part[wave][jr][e] = sum;
-          if (lane == 0) {
-            if (h0) s_hit[wave][js[0]] = 1;
-            if (h1) s_hit[wave][js[1]] = 1;
-            if (h2) s_hit[wave][js[2]] = 1;
+          if ((lane & 1) == 0 && rec_hit) {
+            const uint32_t id = __float_as_uint(s_rec[4 * jr + 2].w);
+            atomicAdd(gscreen + (size_t)GS_GRAD_SCREEN * id + e, sum);
           }
         }
-      }
-    }
-    __syncthreads();
-    // one thread per record: combine the four quadrants, then one atomic per value
-    if (t < cnt) {
-      float acc[GS_GRAD_SCREEN];
-#pragma unroll
-      for (int e = 0; e < GS_GRAD_SCREEN; ++e) acc[e] = 0.0f;
-      bool any = false;
-#pragma unroll
-      for (int w = 0; w < kRenderWaves; ++w) {
-        if (s_hit[w][t]) {
-          any = true;
-#pragma unroll
-          for (int e = 0; e < GS_GRAD_SCREEN; ++e) acc[e] += s_part[w][t][e];
-        }
-      }
-      if (any) {
-        const uint32_t id = __float_as_uint(s_rec[4 * t + 2].w);
-        float* out = gscreen + (size_t)GS_GRAD_SCREEN * id;
-#pragma unroll
-        for (int e = 0; e < GS_GRAD_SCREEN; ++e) atomicAdd(out + e, acc[e]);
       }
     }
   }
