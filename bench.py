@@ -120,6 +120,9 @@ def main():
 
     def run(steps, with_bwd):
         recs = []
+        # the library brackets every launch of the compositing kernel with HIP events on its stream
+        kern = "k_render_bwd" if with_bwd else "k_render_fwd"
+        assert raster.kernel_timer_start(kern) == raster.GS_OK
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
@@ -127,12 +130,15 @@ def main():
                 frame(k, cam, with_bwd, recs)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        st, launches, kms = raster.kernel_timer_stop()
+        assert st == raster.GS_OK and launches == len(recs), (st, launches)
         times = {s: [] for s in stages}
         for e, wb, _ in recs:
             for i, s in enumerate(stages[:4]):
                 times[s].append(e[i].elapsed_time(e[i + 1]))
             if wb:
                 times["render_bwd"].append(e[4].elapsed_time(e[5]))
+        times[kern] = [kms / launches] if launches else []
         return t1 - t0, times, [p for _, _, p in recs]
 
     if args.profile:
@@ -152,6 +158,7 @@ def main():
     log("timed: forward only")
     secs_f, times_f, _ = run(args.steps, False)
     fwd_fps = frames / secs_f
+    kernel_ms = {"k_render_bwd": times["k_render_bwd"][0], "k_render_fwd": times_f["k_render_fwd"][0]}
 
     # algorithmic work per launch (camera-averaged) for the roofline
     P_mean = float(np.mean(pairs))
@@ -180,21 +187,23 @@ def main():
     }
     avg = {s: float(np.mean(times[s])) for s in stages if times[s]}
 
-    def roof(stage):
-        bound, work = algo[stage]
+    def roof(work_kind, ms):
+        bound, work = work_kind
         if bound == "hbm":
-            ach = work / (avg[stage] * 1e-3) / 1e9
+            ach = work / (ms * 1e-3) / 1e9
             return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4)}
-        ach = work / (avg[stage] * 1e-3) / 1e12
+        ach = work / (ms * 1e-3) / 1e12
         return {"bound": "alu", "achieved": round(ach, 2), "peak": round(VALU_PEAK_TOPS, 1),
                 "unit": "Tlane-op/s", "frac": round(ach / VALU_PEAK_TOPS, 4)}
 
-    dom = max(algo, key=lambda s: avg[s])
-    kernels = {"project": "k_project", "bin": "gs_bin_tiles kernels", "sort": "gs_sort_keys kernels",
-               "render_fwd": "k_render_fwd", "render_bwd": "gs_render_bwd (fill + k_render_bwd + k_project_bwd)"}
-    roof_dom = dict(roof(dom), kernel=kernels[dom], traffic=None)
-    stage_report = {s: dict(ms=round(avg[s], 4), **roof(s)) for s in algo}
+    # stages are whole entry points (several kernels for bin, sort and render_bwd); the
+    # roofline object is for the single kernel that takes the most time, k_render_bwd
+    stage_report = {s: dict(ms=round(avg[s], 4), **roof(algo[s], avg[s])) for s in algo}
+    kernel_report = {k: dict(ms=round(v, 4), **roof(algo["render_" + k.split("_")[-1]], v))
+                     for k, v in kernel_ms.items()}
+    roof_dom = dict(kernel_report["k_render_bwd"], kernel="k_render_bwd", launches_timed=frames,
+                    traffic=traffic_bytes("k_render_bwd"))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -219,12 +228,38 @@ def main():
         "mpixels_per_s": round(value * W * H / 1e6, 1),
         "forward_only": {"frames_per_s": round(fwd_fps, 2), "mpixels_per_s": round(fwd_fps * W * H / 1e6, 1)},
         "stages": stage_report,
+        "kernels": kernel_report,
         "evaluations_per_frame": int(evals),
         "contributor_walk_per_frame": int(walk),
         "roofline": roof_dom,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+# HBM bytes per launch of k_render_bwd on this workload (camera average), from two rocprofv3
+# counter runs of `bench.py --profile` (FETCH_SIZE, then WRITE_SIZE), each scaled by the
+# ratio of the known bytes of a 1 GiB device copy to what the same counter read for that
+# copy.  Valid only for the kernel source it was taken on: the digest covers the
+# compositing kernels' source and the headers they include.
+TRAFFIC = {}
+
+
+def kernel_source_digest():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in ("gs_render.hip", "gs_device.h", "gs_wave.h"):
+        with open(os.path.join(ROOT, "tile_differentiable_rasterizer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(kernel):
+    t = TRAFFIC.get(kernel)
+    if not t or t["source_digest"] != kernel_source_digest():
+        return None
+    return t["bytes"]
 
 
 def cpu_baseline(sc, cam, dL, budget):

@@ -208,6 +208,24 @@ gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, cons
 /* Human-readable name of a status code (static string). */
 const char* gs_status_string(gs_status status);
 
+/*
+ * Measurement hooks (not part of the method): device time of one of the library's
+ * kernels, for comparing a kernel's rate with its roofline.
+ *
+ * gs_kernel_timer_start arms the timer for `kernel`, one of "k_project", "k_render_fwd",
+ * "k_render_bwd", "k_project_bwd" (the single kernel behind gs_project, gs_render_fwd and
+ * the two halves of gs_render_bwd).  From then on each launch of that kernel is bracketed
+ * by two HIP events recorded on the caller's stream; the events are created on first use
+ * and kept by the library until the process ends.
+ * gs_kernel_timer_stop disarms the timer, waits for the last recorded event and writes the
+ * number of timed launches and the sum of their durations in milliseconds.
+ * One timer per process; arming it while it is armed is an error.
+ * Errors: INVALID_ARG (unknown kernel name, already armed / not armed, NULL outputs),
+ * HIP (an event could not be created, recorded or read).
+ */
+gs_status gs_kernel_timer_start(const char* kernel);
+gs_status gs_kernel_timer_stop(int64_t* launches, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,20 @@ def test_host_only_calls():
     assert big >= 6 * 8 * 256 * (10_000_000 // 4096)
 
 
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libgsraster.so not built")
+def test_kernel_timer_host_logic():
+    # no launch happens between start and stop, so no HIP call is made
+    from tile_differentiable_rasterizer_amd import raster
+
+    assert raster.kernel_timer_stop()[0] == 1          # not armed
+    assert raster.kernel_timer_start("k_nothing") == 1  # unknown kernel
+    assert raster.kernel_timer_start("k_render_bwd") == 0
+    assert raster.kernel_timer_start("k_render_fwd") == 1  # already armed
+    assert raster.kernel_timer_stop() == (0, 0, 0.0)
+    assert raster.kernel_timer_start("k_project") == 0
+    assert raster.kernel_timer_stop() == (0, 0, 0.0)
+
+
 def test_binding_module_fails_loudly_without_library(tmp_path, monkeypatch):
     from tile_differentiable_rasterizer_amd import raster
 

@@ -4,6 +4,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+#include <vector>
+
 #include "gs_device.h"
 
 namespace gs {
@@ -62,6 +65,56 @@ bool projected_ok(const gs_projected& p) { return p.rec && p.depth && p.rect && 
 
 gs_status hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP; }
 
+// Kernel timer: while armed for one kernel, every launch of that kernel is bracketed by
+// two HIP events recorded on its launch stream.  The events are created on first use and
+// kept for the life of the process (they are reused by later arming).
+enum TimedKernel { kNone = 0, kProject, kRenderFwd, kRenderBwd, kProjectBwd };
+
+struct KernelTimer {
+  std::mutex mu;
+  TimedKernel armed = kNone;
+  std::vector<hipEvent_t> events;  // pairs: start, stop
+  size_t used = 0;                 // events recorded since arming
+  bool failed = false;
+};
+
+KernelTimer& timer() {
+  static KernelTimer t;
+  return t;
+}
+
+TimedKernel timed_kernel_id(const char* name) {
+  if (!name) return kNone;
+  if (!strcmp(name, "k_project")) return kProject;
+  if (!strcmp(name, "k_render_fwd")) return kRenderFwd;
+  if (!strcmp(name, "k_render_bwd")) return kRenderBwd;
+  if (!strcmp(name, "k_project_bwd")) return kProjectBwd;
+  return kNone;
+}
+
+// Records one event of the pair for kernel k when the timer is armed for it.
+void timer_mark(TimedKernel k, hipStream_t s) {
+  KernelTimer& t = timer();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (t.armed != k || t.failed) return;
+  if (t.used == t.events.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) { t.failed = true; return; }
+    t.events.push_back(e);
+  }
+  if (hipEventRecord(t.events[t.used], s) != hipSuccess) { t.failed = true; return; }
+  ++t.used;
+}
+
+// Launches through f with the timer's events around it.
+template <class F>
+hipError_t timed(TimedKernel k, hipStream_t s, F&& f) {
+  timer_mark(k, s);
+  const hipError_t e = f();
+  timer_mark(k, s);
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -93,8 +146,10 @@ gs_status gs_project(int64_t n, const float* means, const float* scales, const f
   if (n == 0) return GS_OK;
   if (!means || !scales || !quats || !opacities || !sh || !projected_ok(out)) return GS_ERR_INVALID_ARG;
   const DevCamera d = dev_camera(cam);
-  return hip_status(launch_project(n, means, scales, quats, opacities, sh, sh_degree, d, out,
-                                   static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed(kProject, s, [&] {
+    return launch_project(n, means, scales, quats, opacities, sh, sh_degree, d, out, s);
+  }));
 }
 
 gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint64_t* keys, uint32_t* vals,
@@ -140,8 +195,10 @@ gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_val
   if (n >= kMaxGaussians || !camera_fits(cam)) return GS_ERR_OVERFLOW;
   if (n > 0 && (!projected_ok(proj) || !sorted_vals)) return GS_ERR_INVALID_ARG;
   const DevCamera d = dev_camera(cam);
-  return hip_status(launch_render_fwd(proj, sorted_vals, tile_ranges, tile_order, d, bg, image, final_T, n_contrib,
-                                      static_cast<hipStream_t>(stream)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed(kRenderFwd, s, [&] {
+    return launch_render_fwd(proj, sorted_vals, tile_ranges, tile_order, d, bg, image, final_T, n_contrib, s);
+  }));
 }
 
 gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, const float* quats,
@@ -162,11 +219,49 @@ gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, cons
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_fill_u32(out.grad_screen, n * GS_GRAD_SCREEN, 0u, s);
   if (e == hipSuccess)
-    e = launch_render_bwd(proj, sorted_vals, tile_ranges, tile_order, d, bg, final_T, n_contrib, dL_dimage,
-                          out.grad_screen, s);
+    e = timed(kRenderBwd, s, [&] {
+      return launch_render_bwd(proj, sorted_vals, tile_ranges, tile_order, d, bg, final_T, n_contrib, dL_dimage,
+                               out.grad_screen, s);
+    });
   if (e == hipSuccess)
-    e = launch_project_bwd(n, means, scales, quats, sh, sh_degree, d, proj, out, densify_accum, densify_denom, s);
+    e = timed(kProjectBwd, s, [&] {
+      return launch_project_bwd(n, means, scales, quats, sh, sh_degree, d, proj, out, densify_accum, densify_denom,
+                                s);
+    });
   return hip_status(e);
+}
+
+gs_status gs_kernel_timer_start(const char* kernel) {
+  const TimedKernel k = timed_kernel_id(kernel);
+  if (k == kNone) return GS_ERR_INVALID_ARG;
+  KernelTimer& t = timer();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (t.armed != kNone) return GS_ERR_INVALID_ARG;
+  t.armed = k;
+  t.used = 0;
+  t.failed = false;
+  return GS_OK;
+}
+
+gs_status gs_kernel_timer_stop(int64_t* launches, double* total_ms) {
+  if (!launches || !total_ms) return GS_ERR_INVALID_ARG;
+  KernelTimer& t = timer();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (t.armed == kNone) return GS_ERR_INVALID_ARG;
+  t.armed = kNone;
+  *launches = 0;
+  *total_ms = 0.0;
+  if (t.failed) return GS_ERR_HIP;
+  double sum = 0.0;
+  for (size_t i = 0; i + 1 < t.used; i += 2) {
+    if (hipEventSynchronize(t.events[i + 1]) != hipSuccess) return GS_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, t.events[i], t.events[i + 1]) != hipSuccess) return GS_ERR_HIP;
+    sum += ms;
+  }
+  *launches = (int64_t)(t.used / 2);
+  *total_ms = sum;
+  return GS_OK;
 }
 
 }  // extern "C"

@@ -21,7 +21,7 @@
 //
 // The backward walks each wavefront's records in reverse three at a time and sums the
 // three records' ten per-pixel gradient terms over the wavefront in one transposed
-// reduction; the four quadrants' sums meet in LDS and leave as one atomic per value.
+// reduction; each wavefront adds its sums to the Gaussians' gradients with fp32 atomics.
 #include "gs_device.h"
 #include "gs_wave.h"
 
@@ -42,10 +42,9 @@ __device__ __forceinline__ void stage_transform(const float4 r0, const float4 r1
 // operation is spelled out so that the forward and the backward round identically.
 __device__ __forceinline__ float gauss_exponent(float a2, float b2, float c2, float dx, float dy) {
 #pragma clang fp contract(off)
-  const float tx = a2 * dx;
-  const float ty = c2 * dy;
-  const float bxy = b2 * dx;
-  return fmaf(tx, dx, fmaf(bxy, dy, ty * dy));
+  const float inner = fmaf(a2, dx, b2 * dy);  // a2 dx + b2 dy
+  const float cy = c2 * dy;
+  return fmaf(dx, inner, cy * dy);
 }
 
 __device__ __forceinline__ float gauss_factor(float e) { return __builtin_amdgcn_exp2f(e); }
@@ -187,15 +186,27 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
 struct BwdPixel {
   float fx, fy;        // pixel centre
   float T;             // transmittance behind the next record to visit
-  float hr, hg, hb;    // colour behind it (including the background's share)
+  float H;             // sum over channels of dL/dpixel * (colour behind it, background included)
   float dr, dg, db;    // dL/dpixel
   uint32_t nc;         // records at positions >= nc did not contribute
 };
 
-// One record's ten gradient terms at this lane's pixel, written to g[0..9]; zeros where the
-// record did not contribute (a later position than the pixel's last contributor, or
-// alpha < 1/255).  Branch-free: a non-contributing lane computes with a zero upstream
-// gradient and keeps its walk state.  Returns whether this lane's pixel contributed.
+// Exact scale of each reduced term to its gradient: terms 2..4 are summed as
+// dq' dx^2, dq' dx dy, dq' dy^2 with dq' = dL/dalpha * o G, while dL/dq = -dq' / 2 and
+// q = A dx^2 + 2 B dx dy + C dy^2.
+__device__ __forceinline__ float term_scale(int e) { return e == 2 || e == 4 ? -0.5f : e == 3 ? -1.0f : 1.0f; }
+
+// Even lanes that receive record r's ten sums (lanes 20 r .. 20 r + 19).
+constexpr uint64_t kRedLanes0 = 0x5555555555555555ull & ((1ull << 20) - 1);
+constexpr uint64_t kRedLanes1 = kRedLanes0 << 20;
+constexpr uint64_t kRedLanes2 = kRedLanes0 << 40;
+
+// One record's ten gradient terms at this lane's pixel, written to g[0..9] (terms 2..4
+// before term_scale); zeros where the record did not contribute (a later position than
+// the pixel's last contributor, or alpha < 1/255).  Branch-free: a non-contributing lane
+// computes with a zero weight and keeps its walk state.  Returns whether it contributed.
+//   dL/dalpha = T_k (dL . rgb) - H / (1 - alpha), with T_k = T / (1 - alpha) in front of
+//   the record and H the dL-weighted colour behind it; then H += (dL . rgb) alpha T_k.
 __device__ __forceinline__ bool bwd_record(const float4* __restrict__ s_rec, int j, uint32_t k, BwdPixel& p,
                                            float* __restrict__ g) {
   const float4 s0 = s_rec[4 * j], s1 = s_rec[4 * j + 1], s2 = s_rec[4 * j + 2], s3 = s_rec[4 * j + 3];
@@ -204,30 +215,26 @@ __device__ __forceinline__ bool bwd_record(const float4* __restrict__ s_rec, int
   const float oG = s1.y * G;
   const float alpha = fminf(kAlphaMax, oG);
   const bool contrib = k < p.nc && alpha >= kAlphaMin;
-  const float dr = contrib ? p.dr : 0.0f, dg = contrib ? p.dg : 0.0f, db = contrib ? p.db : 0.0f;
   // hardware reciprocal (about 1 ulp): T is recovered from the stored final T by repeated
   // division, whose float32 error stays far below the gradient tolerance
   const float iom = __builtin_amdgcn_rcpf(1.0f - alpha);
   const float Tk = p.T * iom;  // transmittance in front of this Gaussian
-  const float w = alpha * Tk;
-  g[6] = dr * w;
-  g[7] = dg * w;
-  g[8] = db * w;
-  float dalpha = dr * (s1.z * Tk - p.hr * iom) + dg * (s1.w * Tk - p.hg * iom) + db * (s2.x * Tk - p.hb * iom);
-  if (contrib) {
-    p.hr = fmaf(s1.z, w, p.hr);
-    p.hg = fmaf(s1.w, w, p.hg);
-    p.hb = fmaf(s2.x, w, p.hb);
-    p.T = Tk;
-  }
-  dalpha = oG <= kAlphaMax ? dalpha : 0.0f;  // the clamp at 0.99 stops the gradient
+  const float w = contrib ? alpha * Tk : 0.0f;
+  g[6] = p.dr * w;
+  g[7] = p.dg * w;
+  g[8] = p.db * w;
+  const float D = fmaf(p.db, s2.x, fmaf(p.dg, s1.w, p.dr * s1.z));
+  float dalpha = fmaf(Tk, D, -(iom * p.H));
+  p.H = fmaf(D, w, p.H);
+  p.T = contrib ? Tk : p.T;
+  dalpha = contrib && oG <= kAlphaMax ? dalpha : 0.0f;  // the clamp at 0.99 stops the gradient
   g[5] = dalpha * G;
-  const float dq = -0.5f * dalpha * oG;  // dL/dq, q = A dx^2 + 2 B dx dy + C dy^2
+  const float dq = dalpha * oG;
   g[2] = dq * dx * dx;
-  g[3] = dq * 2.0f * dx * dy;
+  g[3] = dq * dx * dy;
   g[4] = dq * dy * dy;
-  g[0] = -2.0f * dq * fmaf(s3.x, dx, s3.y * dy);
-  g[1] = -2.0f * dq * fmaf(s3.y, dx, s3.z * dy);
+  g[0] = dq * fmaf(s3.x, dx, s3.y * dy);
+  g[1] = dq * fmaf(s3.y, dx, s3.z * dy);
   g[9] = __builtin_amdgcn_sqrtf(fmaf(g[0], g[0], g[1] * g[1]));
   return contrib;
 }
@@ -249,15 +256,18 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
   BwdPixel p;
   p.fx = (float)px + 0.5f;
   p.fy = (float)py + 0.5f;
-  p.T = 1.0f; p.dr = p.dg = p.db = 0.0f; p.nc = 0;
+  p.T = 1.0f; p.H = 0.0f; p.dr = p.dg = p.db = 0.0f; p.nc = 0;
   if (px < W && py < H) {
     const size_t o = (size_t)py * W + px;
     p.T = final_T[o];
     p.nc = n_contrib[o];
     p.dr = dL[o]; p.dg = dL[plane + o]; p.db = dL[2 * plane + o];
   }
-  p.hr = bg0 * p.T; p.hg = bg1 * p.T; p.hb = bg2 * p.T;
+  p.H = fmaf(p.db, bg2, fmaf(p.dg, bg1, p.dr * bg0)) * p.T;
   const uint32_t wlast = wave_max(p.nc);  // this wavefront walks [0, wlast)
+  // the (record, term) whose wavefront sum this lane receives from the transposed reduction
+  const int red_r = (lane >> 1) / GS_GRAD_SCREEN, red_e = (lane >> 1) - red_r * GS_GRAD_SCREEN;
+  const float red_scale = term_scale(red_e);
   if (lane == 0) s_last[wave] = wlast;
   __syncthreads();
   uint32_t last = 0;
@@ -306,40 +316,34 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
       while (m) {
         // the next three records of the reverse walk (highest position first); the bit
         // positions stay scalar so the walk is a uniform loop
+        // a step short of three records repeats the first one at position 2^32 - 1, past
+        // every pixel's last contributor, so it adds zeros and leaves the walk unchanged
         int js[3];
-        bool has[3];
+        uint32_t ks[3];
 #pragma unroll
         for (int r = 0; r < 3; ++r) {
-          has[r] = m != 0;
-          const int bit = has[r] ? __builtin_amdgcn_readfirstlane(63 - __builtin_clzll(m)) : 0;
-          js[r] = c + bit;
-          if (has[r]) m &= ~(1ull << bit);
+          const bool has = m != 0;
+          const int bit = has ? __builtin_amdgcn_readfirstlane(63 - __builtin_clzll(m)) : 0;
+          js[r] = has ? c + bit : js[0];
+          ks[r] = has ? (uint32_t)(lo - start + c + bit) : 0xFFFFFFFFu;
+          if (has) m &= ~(1ull << bit);
         }
         float v[32];
         bool hit[3];
 #pragma unroll
-        for (int r = 0; r < 3; ++r) {
-          if (has[r]) {
-            hit[r] = bwd_record(s_rec, js[r], (uint32_t)(lo - start + js[r]), p, v + GS_GRAD_SCREEN * r);
-          } else {
-            hit[r] = false;
-#pragma unroll
-            for (int e = 0; e < GS_GRAD_SCREEN; ++e) v[GS_GRAD_SCREEN * r + e] = 0.0f;
-          }
-        }
+        for (int r = 0; r < 3; ++r) hit[r] = bwd_record(s_rec, js[r], ks[r], p, v + GS_GRAD_SCREEN * r);
         v[30] = 0.0f;
         v[31] = 0.0f;
         const uint64_t h0 = __ballot(hit[0]), h1 = __ballot(hit[1]), h2 = __ballot(hit[2]);
         if (h0 | h1 | h2) {
           // lanes 2i and 2i + 1 now hold the wavefront's sum of v[i]; the even lane of each
-          // (record, value) pair adds it to the Gaussian's gradient: one atomic instruction
+          // (record, term) pair of a record some pixel took adds it to the Gaussian's gradient
           const float sum = wave_transpose_reduce32(v);
-          const int idx = lane >> 1, r = idx / GS_GRAD_SCREEN, e = idx - r * GS_GRAD_SCREEN;
-          const bool rec_hit = r == 0 ? h0 != 0 : r == 1 ? h1 != 0 : r == 2 ? h2 != 0 : false;
-          const int jr = r == 0 ? js[0] : r == 1 ? js[1] : js[2];
-          if ((lane & 1) == 0 && rec_hit) {
+          const uint64_t act = (h0 ? kRedLanes0 : 0ull) | (h1 ? kRedLanes1 : 0ull) | (h2 ? kRedLanes2 : 0ull);
+          const int jr = red_r == 0 ? js[0] : red_r == 1 ? js[1] : js[2];
+          if ((act >> lane) & 1ull) {
             const uint32_t id = __float_as_uint(s_rec[4 * jr + 2].w);
-            atomicAdd(gscreen + (size_t)GS_GRAD_SCREEN * id + e, sum);
+            atomicAdd(gscreen + (size_t)GS_GRAD_SCREEN * id + red_e, sum * red_scale);
           }
         }
       }

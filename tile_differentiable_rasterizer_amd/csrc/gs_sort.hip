@@ -17,8 +17,8 @@
 //                 ranks its keys stably (wavefront ballots match equal digits; per-wave
 //                 digit counters in LDS), publishes per-digit counts and resolves its
 //                 global offsets by looking back over earlier partitions' published
-//                 counts, reorders the partition in LDS by digit and writes each digit's
-//                 run contiguously
+//                 counts (several earlier partitions per round trip), reorders the
+//                 partition in LDS by digit and writes each digit's run contiguously
 //   k_sort_copy   moves the result back to keys/vals after an odd number of passes
 //   k_ranges      [first, last + 1) of every tile from the sorted keys
 #include "gs_device.h"
@@ -30,6 +30,7 @@ constexpr int kSortKPT = 16;
 constexpr int kSortPart = kSortBlock * kSortKPT;  // keys per partition
 constexpr int kRadix = 256;
 constexpr int kMaxPasses = 8;
+constexpr int kLookBack = 4;                      // status words read per look-back round trip
 constexpr uint64_t kFlagAgg = 1ull << 62;    // partition's own count published
 constexpr uint64_t kFlagPre = 2ull << 62;    // inclusive prefix through this partition
 constexpr uint64_t kValMask = (1ull << 62) - 1;
@@ -63,6 +64,17 @@ hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s) {
   const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
   k_fill_u32<<<blocks, 256, 0, s>>>(static_cast<uint32_t*>(p), count, v);
   return hipGetLastError();
+}
+
+// Lanes of the calling wavefront (among `active`) whose `bits`-bit digit equals this lane's.
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, uint64_t active) {
+  uint64_t m = active;
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = (d >> b) & 1u;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
 }
 
 template <typename K>
@@ -161,13 +173,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
     const int64_t idx = base + wave * (kSortKPT * kWave) + j * kWave + lane;
     const bool valid = idx < P;
     const uint32_t d = (uint32_t)(key[j] >> shift) & dmask;
-    // lanes holding the same digit: intersect ballots of every digit bit
-    uint64_t m = __ballot(valid);
-    for (int b = 0; b < bits; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const uint64_t bb = __ballot(bit);
-      m &= bit ? bb : ~bb;
-    }
+    const uint64_t m = match_digit(d, bits, __ballot(valid));
     const uint32_t below = (uint32_t)__popcll(m & lanemask_lt());
     uint32_t prev = 0;
     if (valid) prev = s_wh[wave][d];
@@ -212,22 +218,32 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
       s_vals[pos] = val[j];
     }
   }
-  // look back over earlier partitions for this digit's global offset
+  // look back over earlier partitions for this digit's global offset, kLookBack words per
+  // round trip: sum published counts back to the first inclusive prefix; a word not yet
+  // published ends the round, and the next round starts at it
   uint64_t excl = 0;
   if (part > 0) {
     int64_t p = part - 1;
     while (true) {
-      uint64_t sv = early;
+      uint64_t sv[kLookBack];
+      sv[0] = (early & ~kValMask) ? early : status_load(status + p * kRadix + d);
       early = 0;
-      if (!(sv & ~kValMask)) sv = status_load(status + p * kRadix + d);
-      const uint64_t flag = sv & ~kValMask;
-      if (flag == 0) {
-        __builtin_amdgcn_s_sleep(1);
-        continue;
+#pragma unroll
+      for (int i = 1; i < kLookBack; ++i) sv[i] = p - i >= 0 ? status_load(status + (p - i) * kRadix + d) : 0;
+      int used = 0;
+      bool done = false;
+#pragma unroll
+      for (int i = 0; i < kLookBack; ++i) {
+        if (done || used < i) continue;  // stopped at an inclusive prefix or an unpublished word
+        const uint64_t flag = sv[i] & ~kValMask;
+        if (flag == 0) continue;
+        excl += sv[i] & kValMask;
+        used = i + 1;
+        done = flag == kFlagPre;
       }
-      excl += sv & kValMask;
-      if (flag == kFlagPre) break;
-      --p;
+      if (done) break;
+      p -= used;
+      if (used < kLookBack) __builtin_amdgcn_s_sleep(1);
     }
     status_store(my_status, kFlagPre | (excl + tot));
   }
@@ -255,14 +271,23 @@ __global__ void k_sort_copy(const int32_t* __restrict__ plan, const K* __restric
   }
 }
 
+// Four consecutive keys per thread; a tile's first and last positions are where its id
+// differs from the neighbour's.
 __global__ void k_ranges(const uint64_t* __restrict__ keys, int64_t P, int64_t num_tiles,
                          int64_t* __restrict__ ranges) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= P) return;
-  const uint64_t t = keys[i] >> 32;
-  if (t >= (uint64_t)num_tiles) return;
-  if (i == 0 || (keys[i - 1] >> 32) != t) ranges[2 * t] = i;
-  if (i == P - 1 || (keys[i + 1] >> 32) != t) ranges[2 * t + 1] = i + 1;
+  const int64_t i0 = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (i0 >= P) return;
+  uint64_t t[6];  // tiles of keys i0 - 1 .. i0 + 4 (~0 outside [0, P))
+  t[0] = i0 > 0 ? keys[i0 - 1] >> 32 : ~0ull;
+#pragma unroll
+  for (int j = 0; j < 5; ++j) t[j + 1] = i0 + j < P ? keys[i0 + j] >> 32 : ~0ull;
+#pragma unroll
+  for (int j = 1; j <= 4; ++j) {
+    const int64_t i = i0 + j - 1;
+    if (i >= P || t[j] >= (uint64_t)num_tiles) continue;
+    if (t[j - 1] != t[j]) ranges[2 * t[j]] = i;
+    if (t[j + 1] != t[j]) ranges[2 * t[j] + 1] = i + 1;
+  }
 }
 
 // tile_order: tile ids by decreasing list length (counting sort over 128 buckets, four per
@@ -355,7 +380,7 @@ hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* v
     e = radix_sort<uint64_t>(P, keys, vals, keys_tmp, vals_tmp, sorted_low_bits, sort_significant_bits(num_tiles),
                              ws, s);
   if (e != hipSuccess) return e;
-  if (P > 0) k_ranges<<<(unsigned)((P + 255) / 256), 256, 0, s>>>(keys, P, num_tiles, ranges);
+  if (P > 0) k_ranges<<<(unsigned)((P + 1023) / 1024), 256, 0, s>>>(keys, P, num_tiles, ranges);
   if (order) k_tile_order<<<1, 1024, 0, s>>>(ranges, num_tiles, order);
   return hipGetLastError();
 }

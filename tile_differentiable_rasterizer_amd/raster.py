@@ -69,8 +69,25 @@ def lib():
             getattr(L, name).restype = i32
         L.gs_status_string.argtypes = [i32]
         L.gs_status_string.restype = C.c_char_p
+        L.gs_kernel_timer_start.argtypes = [C.c_char_p]
+        L.gs_kernel_timer_start.restype = i32
+        L.gs_kernel_timer_stop.argtypes = [C.POINTER(i64), C.POINTER(C.c_double)]
+        L.gs_kernel_timer_stop.restype = i32
         _lib = L
     return _lib
+
+
+def kernel_timer_start(kernel):
+    """Arm the library's event timer for one kernel ("k_project", "k_render_fwd",
+    "k_render_bwd", "k_project_bwd"); returns the status code."""
+    return lib().gs_kernel_timer_start(kernel.encode())
+
+
+def kernel_timer_stop():
+    """Disarm the timer: (status, launches timed, summed device milliseconds)."""
+    n, ms = C.c_int64(0), C.c_double(0.0)
+    st = lib().gs_kernel_timer_stop(C.byref(n), C.byref(ms))
+    return st, n.value, ms.value
 
 
 def _ptr(t):
