@@ -134,13 +134,15 @@ size_t gs_workspace_bytes(int64_t n, int64_t pair_capacity, int32_t num_tiles);
  * Splatting in Julia" s3.2 assign_to_tiles):
  *   keys[p] = tile_id << 32 | bits(depth),  tile_id = ty * tiles_x + tx
  *   vals[p] = Gaussian id
- * Pairs come out ordered by (bits(depth), Gaussian id) -- the visible Gaussians are
- * radix-sorted by depth first -- with each Gaussian's tiles row by row.  So the keys are
- * already stably ordered by their low 32 bits, and gs_sort_keys(sorted_low_bits = 32)
- * completes the (tile, depth, id) order with passes over the tile bits only.
+ * Pairs come out ordered by (tile_id & 255, bits(depth), Gaussian id): the visible
+ * Gaussians are radix-sorted by depth, and their expansion into tiles performs the first
+ * 8-bit digit pass over the tile id.  So the keys are already stably ordered by their low
+ * 40 bits, and gs_sort_keys(sorted_low_bits = 40) completes the (tile, depth, id) order
+ * with passes over the tile bits above the low byte only (none when num_tiles <= 256).
  * Writes the pair count P to *n_pairs [host] (this is the call's one device->host read and
  * stream synchronisation).  With keys == NULL only P is computed.  If P > capacity,
- * returns GS_ERR_CAPACITY with *n_pairs = P and writes no pairs.
+ * returns GS_ERR_CAPACITY with *n_pairs = P and writes no pairs.  The workspace must hold
+ * gs_workspace_bytes(n, P, num_tiles) bytes (checked before and after P is known).
  * Errors: INVALID_ARG, WORKSPACE, CAPACITY, OVERFLOW, HIP.
  */
 gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint64_t* keys,
@@ -152,7 +154,7 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
  * 32 + ceil(log2(num_tiles))), 8 bits per pass, digits constant over all keys skipped
  * ("Better Gaussian Splatting in Julia" s3.2 sort_by_depth!; "Implementing Better
  * Gaussian Splatting in Julia" s3.3 depth order).  The input must already be stably
- * ordered by its low sorted_low_bits bits (0 = no assumption: a full sort; 32 = the
+ * ordered by its low sorted_low_bits bits (0 = no assumption: a full sort; 40 = the
  * output of gs_bin_tiles).  Equal keys keep their input order, so depth ties stay broken
  * by Gaussian id.  The result is
  * left in keys/vals; keys_tmp/vals_tmp are scratch of the same size.  Then writes

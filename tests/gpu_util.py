@@ -121,11 +121,13 @@ def check_binning(cam, g, label=""):
     k, v = oracle.emit_pairs(trect, g["n_tiles"].astype(np.int64), g["depth_bits"], cam.tiles_x)
     assert k.shape[0] == g["P"], f"{label}: pair count {g['P']} vs {k.shape[0]}"
     if "keys_unsorted" in g:
-        # gs_bin_tiles emits in (depth bits, id) order: the oracle's id-order emission,
-        # stably reordered by depth, must match it pair for pair
-        by_depth = np.argsort((k & np.uint64(0xFFFFFFFF)).astype(np.uint32), kind="stable")
-        assert np.array_equal(g["keys_unsorted"], k[by_depth]), f"{label}: emitted keys differ"
-        assert np.array_equal(g["vals_unsorted"], v[by_depth]), f"{label}: emitted ids differ"
+        # gs_bin_tiles emits in (tile & 255, depth bits, id) order: the oracle's id-order
+        # emission, stably reordered by (tile low byte, depth), must match it pair for pair
+        low = ((k >> np.uint64(32)) & np.uint64(0xFF)).astype(np.uint32)
+        dbits = (k & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+        perm = np.lexsort((dbits, low))
+        assert np.array_equal(g["keys_unsorted"], k[perm]), f"{label}: emitted keys differ"
+        assert np.array_equal(g["vals_unsorted"], v[perm]), f"{label}: emitted ids differ"
     sk, sv = oracle.sort_pairs(k, v)
     assert np.array_equal(g["keys"], sk), f"{label}: sorted keys differ"
     assert np.array_equal(g["vals"], sv), f"{label}: sorted ids differ"

@@ -16,10 +16,10 @@ hipError_t launch_project(int64_t n, const float* means, const float* scales, co
 hipError_t launch_project_bwd(int64_t n, const float* means, const float* scales, const float* quats,
                               const float* sh, int L, const DevCamera& cam, const gs_projected& proj,
                               const gs_grads& gr, float* accum, int32_t* denom, hipStream_t s);
-size_t bin_workspace_bytes(int64_t n);
+size_t bin_workspace_bytes(int64_t n, int64_t n_pairs);
 hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, void* ws, hipStream_t s);
 uint64_t* bin_totals_ptr(int64_t n, void* ws);
-hipError_t launch_bin_emit(int64_t n, int64_t v, const gs_projected& proj, int tiles_x, void* ws, uint64_t* keys,
+hipError_t launch_bin_emit(int64_t n, int64_t v, int64_t P, const gs_projected& proj, int tiles_x, void* ws, uint64_t* keys,
                            uint32_t* vals, hipStream_t s);
 size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_bits);
 hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
@@ -133,7 +133,7 @@ const char* gs_status_string(gs_status s) {
 
 size_t gs_workspace_bytes(int64_t n, int64_t pair_capacity, int32_t num_tiles) {
   if (n < 0 || pair_capacity < 0 || num_tiles < 1) return 0;
-  const size_t a = bin_workspace_bytes(n);
+  const size_t a = bin_workspace_bytes(n, pair_capacity);
   const size_t b = sort_workspace_bytes(pair_capacity, num_tiles, 0);
   return a > b ? a : b;
 }
@@ -159,7 +159,7 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
   if (n >= kMaxGaussians || !camera_fits(cam)) return GS_ERR_OVERFLOW;
   if (n > 0 && !projected_ok(proj)) return GS_ERR_INVALID_ARG;
   if (keys && !vals) return GS_ERR_INVALID_ARG;
-  if (!workspace || workspace_bytes < bin_workspace_bytes(n)) return GS_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < bin_workspace_bytes(n, 0)) return GS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_bin_count(n, proj.n_tiles, workspace, s);
   if (e != hipSuccess) return GS_ERR_HIP;
@@ -171,8 +171,10 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
   *n_pairs = (int64_t)totals[0];
   if (!keys) return GS_OK;
   if ((int64_t)totals[0] > capacity) return GS_ERR_CAPACITY;
+  if (workspace_bytes < bin_workspace_bytes(n, (int64_t)totals[0])) return GS_ERR_WORKSPACE;
   const DevCamera d = dev_camera(cam);
-  return hip_status(launch_bin_emit(n, (int64_t)totals[1], proj, d.tiles_x, workspace, keys, vals, s));
+  return hip_status(
+      launch_bin_emit(n, (int64_t)totals[1], (int64_t)totals[0], proj, d.tiles_x, workspace, keys, vals, s));
 }
 
 gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys, uint32_t* vals,

@@ -7,24 +7,30 @@
 // efficiency" (mhpq.cn) is why every count and offset here is 64-bit; its visibility
 // bitmap section is the model for the wavefront-ballot compaction below.
 //
-// Pairs are written in depth order (ties by Gaussian id): the visible Gaussians are
-// compacted (ballot + popcount per wavefront, in id order), radix-sorted once by the bit
-// pattern of their fp32 depth (a stable sort, so equal depths stay in id order), and then
-// expanded into their tiles.  Every tile's pairs are therefore already in (depth, id)
-// order, and the pair sort only has to order the tile bits stably: 2 digit passes over
-// the pairs instead of 6.
+// Pairs are written in the order (tile & 255, depth, id): the visible Gaussians are
+// compacted (ballot + popcount per wavefront, in id order) and radix-sorted once by the
+// bit pattern of their fp32 depth (a stable sort, so equal depths stay in id order).
+// Their tiles are then expanded in that order, and the expansion itself performs the
+// first digit pass of the tile sort: a counting pass gives every partition of 2048 pairs
+// its count per value of the tile's low byte, a column scan turns those into offsets, and
+// the scattering pass writes each pair at its place.  The keys leave ordered by their low
+// 40 bits, so the pair sort is left with the tile bits above the low byte: one digit pass
+// at 1080p instead of six over unsorted keys.
 //
 // Kernels:
 //   k_count_blocks   per 1024 Gaussians: pair count and visible count
 //   k_scan_blocks    one workgroup: exclusive scan of per-block sums, and the total
 //   k_compact        visible Gaussians' (depth bits, id), in id order
 //   (radix sort of the compacted depths, gs_sort.hip)
-//   k_count_sorted   per 1024 depth-sorted Gaussians: pair count
-//   k_emit           per 1024 depth-sorted Gaussians: in-LDS exclusive scan of n_tiles,
-//                    then every lane writes consecutive output pairs (its Gaussian found by
-//                    binary search over the scanned offsets), so the 12 B/pair stores are
-//                    fully coalesced and a Gaussian covering many tiles is spread over
-//                    many lanes.
+//   k_count_sorted   per 1024 depth-sorted Gaussians: pair count; gathers their tile
+//                    rectangles into depth order
+//   k_offsets        per depth-sorted Gaussian: its first pair; per partition: its first
+//                    Gaussian
+//   k_emit_count     per chunk of 8 partitions: counts of the tile's low byte, per
+//                    partition as prefixes inside the chunk, and the chunk's totals
+//   k_digit_scan     per digit: exclusive scan of the chunk totals, and the digit's total
+//   k_emit_scatter   per partition: regenerate the pairs, rank them stably by digit in
+//                    LDS, write one contiguous run per digit
 #include "gs_device.h"
 
 namespace gs {
@@ -36,6 +42,15 @@ size_t radix_workspace_bytes(int64_t P, int lo, int hi);
 constexpr int kBinBlock = 256;
 constexpr int kBinPer = 4;                      // Gaussians per thread
 constexpr int kBinChunk = kBinBlock * kBinPer;  // Gaussians per workgroup
+constexpr int kEmitPer = 8;                       // pairs per lane in the emission passes
+constexpr int kEmitPart = kBinBlock * kEmitPer;  // pairs per emission partition
+constexpr int kDigits = 256;                      // values of the tile's low byte
+constexpr int kCountParts = 8;                    // partitions per counting workgroup
+
+// Tiles in a rectangle (x0, x1, y0, y1), inclusive bounds.
+__device__ __forceinline__ uint32_t rect_tiles(ushort4 r) {
+  return ((uint32_t)r.y - (uint32_t)r.x + 1u) * ((uint32_t)r.w - (uint32_t)r.z + 1u);
+}
 
 __global__ __launch_bounds__(kBinBlock) void k_count_blocks(int64_t n, const uint32_t* __restrict__ n_tiles,
                                                             uint64_t* __restrict__ pair_sums,
@@ -129,8 +144,11 @@ __global__ __launch_bounds__(kBinBlock) void k_compact(int64_t n, const uint32_t
   }
 }
 
+// Per 1024 depth-sorted Gaussians: their pair count; also gathers each one's tile
+// rectangle into depth order (srect), the one random-access pass over the Gaussians.
 __global__ __launch_bounds__(kBinBlock) void k_count_sorted(int64_t v, const uint32_t* __restrict__ order,
-                                                            const uint32_t* __restrict__ n_tiles,
+                                                            const ushort4* __restrict__ rect,
+                                                            ushort4* __restrict__ srect,
                                                             uint64_t* __restrict__ sums) {
   __shared__ uint64_t s_p[kBinBlock / kWave];
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
@@ -138,7 +156,11 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(int64_t v, const uin
 #pragma unroll
   for (int j = 0; j < kBinPer; ++j) {
     const int64_t i = base + j * kBinBlock + threadIdx.x;
-    if (i < v) acc += n_tiles[order[i]];
+    if (i < v) {
+      const ushort4 r = rect[order[i]];
+      srect[i] = r;
+      acc += rect_tiles(r);
+    }
   }
   acc = wave_sum(acc);
   if (__lane_id() == 0) s_p[threadIdx.x / kWave] = acc;
@@ -151,100 +173,309 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(int64_t v, const uin
   }
 }
 
-// Expand the depth-sorted Gaussians order[0, v) into their tiles (rows outer, columns
-// inner): keys[p] = tile << 32 | depth bits, vals[p] = Gaussian id.
-__global__ __launch_bounds__(kBinBlock) void k_emit(int64_t v, const uint32_t* __restrict__ order,
-                                                    const uint32_t* __restrict__ n_tiles,
-                                                    const ushort4* __restrict__ rect,
-                                                    const float* __restrict__ depth,
-                                                    const uint64_t* __restrict__ block_off, int tiles_x,
-                                                    uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
-  __shared__ uint64_t s_off[kBinChunk + 1];  // exclusive offsets relative to the block
-  __shared__ uint32_t s_id[kBinChunk];
-  __shared__ ushort4 s_rect[kBinChunk];      // the block's Gaussians, gathered once
-  __shared__ uint32_t s_depth[kBinChunk];
+// Per-Gaussian pair offsets in depth order and the first Gaussian of every emission
+// partition: goff[i] = pairs of the depth-sorted Gaussians before i (i in [0, v]);
+// gstart[b] = the Gaussian holding pair b * kEmitPart.  Every visible Gaussian has at
+// least one pair, so each partition start falls inside exactly one Gaussian's range.
+__global__ __launch_bounds__(kBinBlock) void k_offsets(int64_t v, const ushort4* __restrict__ srect,
+                                                       const uint64_t* __restrict__ block_off,
+                                                       uint64_t* __restrict__ goff, uint32_t* __restrict__ gstart) {
   __shared__ uint64_t s_w[kBinBlock / kWave];
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  // each thread owns kBinPer consecutive sorted positions
   uint32_t cnt[kBinPer];
   uint64_t tsum = 0;
 #pragma unroll
-  for (int j = 0; j < kBinPer; ++j) {
+  for (int j = 0; j < kBinPer; ++j) {  // each thread owns kBinPer consecutive positions
     const int64_t i = base + (int64_t)tid * kBinPer + j;
-    const uint32_t g = i < v ? order[i] : 0u;
-    s_id[tid * kBinPer + j] = g;
-    cnt[j] = i < v ? n_tiles[g] : 0u;
-    if (i < v) {
-      s_rect[tid * kBinPer + j] = rect[g];
-      s_depth[tid * kBinPer + j] = __float_as_uint(depth[g]);
-    }
+    cnt[j] = i < v ? rect_tiles(srect[i]) : 0u;
     tsum += cnt[j];
   }
   const uint64_t inc = wave_inclusive_scan(tsum);
   if (lane == kWave - 1) s_w[wave] = inc;
   __syncthreads();
-  uint64_t pre = inc - tsum;
+  uint64_t pre = block_off[blockIdx.x] + inc - tsum;
   for (int w = 0; w < wave; ++w) pre += s_w[w];
 #pragma unroll
   for (int j = 0; j < kBinPer; ++j) {
-    s_off[tid * kBinPer + j] = pre;
+    const int64_t i = base + (int64_t)tid * kBinPer + j;
+    if (i >= v) break;
+    goff[i] = pre;
+    for (uint64_t pb = (pre + kEmitPart - 1) / kEmitPart; pb * kEmitPart < pre + cnt[j]; ++pb)
+      gstart[pb] = (uint32_t)i;
     pre += cnt[j];
+    if (i == v - 1) goff[v] = pre;
   }
-  if (tid == kBinBlock - 1) s_off[kBinChunk] = pre;  // block total
-  __syncthreads();
-  const uint64_t total = s_off[kBinChunk];
-  const uint64_t out0 = block_off[blockIdx.x];
-  const int ng = (int)min((int64_t)kBinChunk, v - base);
-  // each lane writes kEmitRun consecutive pairs: one binary search for the first, then walk
-  // the Gaussians' tiles row by row; a wavefront's stores cover 64 * kEmitRun consecutive pairs
-  constexpr int kEmitRun = 8;
-  for (uint64_t chunk = 0; chunk < total; chunk += (uint64_t)kBinBlock * kEmitRun) {
-    const uint64_t p0 = chunk + (uint64_t)tid * kEmitRun;
-    if (p0 >= total) continue;
-    int lo = 0, hi = ng;  // invariant: s_off[lo] <= p0 < s_off[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_off[mid] <= p0) lo = mid; else hi = mid;
+}
+
+// The pairs of emission partition b, [b C, min(P, (b + 1) C)) in depth order, as the
+// counting and the scattering kernels both generate them: lane t takes kEmitPer
+// consecutive pairs, finds the Gaussian of its first one by binary search over the
+// partition's staged offsets, then walks the Gaussians' tile rectangles (rows outer).
+struct EmitPart {
+  int64_t base;  // first pair of the partition
+  int n;         // pairs in the partition
+  uint32_t g0;   // its first Gaussian (depth-sorted position)
+  int ng;        // its Gaussians: g0 .. g0 + ng - 1
+};
+
+// Stages s_rel[i] = goff[g0 + i] - base for i in [0, ng] (the last one is the end of the
+// partition's last Gaussian).  Call from every thread; the caller synchronises.
+__device__ __forceinline__ EmitPart stage_partition(int64_t b, int64_t nparts, int64_t v, int64_t P,
+                                                    const uint64_t* __restrict__ goff,
+                                                    const uint32_t* __restrict__ gstart, int32_t* s_rel) {
+  EmitPart e;
+  e.base = b * kEmitPart;
+  e.n = (int)min((int64_t)kEmitPart, P - e.base);
+  e.g0 = gstart[b];
+  const uint32_t g1 = b + 1 < nparts ? gstart[b + 1] : (uint32_t)(v - 1);
+  e.ng = (int)(g1 - e.g0) + 1;
+  for (int i = threadIdx.x; i <= e.ng; i += kBinBlock) s_rel[i] = (int32_t)((int64_t)goff[e.g0 + i] - e.base);
+  return e;
+}
+
+// Generates this lane's pairs; emit(k, tile, id, dbits) receives the pair's slot in the
+// lane's run (0 .. kEmitPer - 1), its tile, its Gaussian's id and the bit pattern of that
+// Gaussian's depth.  srect, sdepth and sid are the depth-sorted Gaussians' rectangles,
+// depth bits and ids (read only when kPayload).
+template <bool kPayload, typename F>
+__device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_rel, const ushort4* __restrict__ srect,
+                                           const uint32_t* __restrict__ sdepth, const uint32_t* __restrict__ sid,
+                                           int tiles_x, F&& emit) {
+  const int p0 = (int)threadIdx.x * kEmitPer;
+  if (p0 >= e.n) return;
+  int lo = 0, hi = e.ng;  // invariant: s_rel[lo] <= p0 < s_rel[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_rel[mid] <= p0) lo = mid; else hi = mid;
+  }
+  uint32_t g = e.g0 + (uint32_t)lo;
+  ushort4 r = srect[g];
+  uint32_t dbits = kPayload ? sdepth[g] : 0u, id = kPayload ? sid[g] : 0u;
+  uint32_t w = (uint32_t)r.y - (uint32_t)r.x + 1u;
+  const uint32_t local = (uint32_t)(p0 - s_rel[lo]);
+  uint32_t row = local / w, col = local - row * w;
+  int next = s_rel[lo + 1];
+  const int run = min(kEmitPer, e.n - p0);
+  for (int k = 0; k < run; ++k) {
+    while (p0 + k >= next) {  // on to the next Gaussian
+      ++lo;
+      ++g;
+      r = srect[g];
+      if (kPayload) {
+        dbits = sdepth[g];
+        id = sid[g];
+      }
+      w = (uint32_t)r.y - (uint32_t)r.x + 1u;
+      row = 0;
+      col = 0;
+      next = s_rel[lo + 1];
     }
-    uint32_t local = (uint32_t)(p0 - s_off[lo]);
-    ushort4 r = s_rect[lo];
-    uint32_t w = (uint32_t)r.y - (uint32_t)r.x + 1u;
-    uint32_t row = local / w, col = local - row * w;
-    uint64_t next = s_off[lo + 1];
-    const int run = (int)min((uint64_t)kEmitRun, total - p0);
-    for (int i = 0; i < run; ++i) {
-      const uint64_t p = p0 + (uint64_t)i;
-      while (p >= next) {  // on to the next Gaussian (every visible one has n_tiles > 0)
-        ++lo;
-        r = s_rect[lo];
-        w = (uint32_t)r.y - (uint32_t)r.x + 1u;
-        row = 0;
-        col = 0;
-        next = s_off[lo + 1];
-      }
-      const uint64_t tile = (uint64_t)((uint32_t)r.z + row) * (uint64_t)tiles_x + ((uint32_t)r.x + col);
-      keys[out0 + p] = (tile << 32) | (uint64_t)s_depth[lo];
-      vals[out0 + p] = s_id[lo];
-      if (++col == w) {
-        col = 0;
-        ++row;
-      }
+    emit(k, ((uint32_t)r.z + row) * (uint32_t)tiles_x + ((uint32_t)r.x + col), id, dbits);
+    if (++col == w) {
+      col = 0;
+      ++row;
     }
   }
 }
 
-// Workspace layout (bytes).
+// Counting pass: per partition, how many of its pairs have each value of the tile's low
+// byte.  A workgroup takes kCountParts consecutive partitions and writes, per partition,
+// the counts of the chunk's earlier partitions (cnt_pre[b][d]) and, per chunk, its totals
+// (csum[c][d]); both are contiguous rows.
+__global__ __launch_bounds__(kBinBlock) void k_emit_count(int64_t v, int64_t P, int64_t nparts,
+                                                          const ushort4* __restrict__ srect,
+                                                          const uint64_t* __restrict__ goff,
+                                                          const uint32_t* __restrict__ gstart, int tiles_x,
+                                                          uint32_t* __restrict__ cnt_pre,
+                                                          uint64_t* __restrict__ csum) {
+  __shared__ int32_t s_rel[kEmitPart + 2];
+  __shared__ uint32_t s_h[kBinBlock / kWave][kDigits];
+  const int tid = threadIdx.x, wave = tid / kWave;
+  uint32_t running = 0;  // digit tid's count in the chunk's earlier partitions
+  for (int q = 0; q < kCountParts; ++q) {
+    const int64_t b = (int64_t)blockIdx.x * kCountParts + q;
+    if (b >= nparts) break;
+    for (int i = tid; i < (kBinBlock / kWave) * kDigits; i += kBinBlock) (&s_h[0][0])[i] = 0;
+    const EmitPart e = stage_partition(b, nparts, v, P, goff, gstart, s_rel);
+    __syncthreads();
+    lane_pairs<false>(e, s_rel, srect, nullptr, nullptr, tiles_x, [&](int, uint32_t tile, uint32_t, uint32_t) {
+      atomicAdd(&s_h[wave][tile & (kDigits - 1)], 1u);
+    });
+    __syncthreads();
+    uint32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < kBinBlock / kWave; ++w) c += s_h[w][tid];
+    cnt_pre[b * kDigits + tid] = running;
+    running += c;
+    __syncthreads();  // the next partition reuses s_rel and s_h
+  }
+  csum[(int64_t)blockIdx.x * kDigits + tid] = running;
+}
+
+// One workgroup per digit: exclusive scan over chunks of the digit's chunk totals
+// (csum[c][d], in place) and the digit's total.
+__global__ __launch_bounds__(kBinBlock) void k_digit_scan(int64_t nchunks, uint64_t* __restrict__ csum,
+                                                          uint64_t* __restrict__ totals) {
+  __shared__ uint64_t s_w[kBinBlock / kWave];
+  __shared__ uint64_t s_carry;
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const int d = blockIdx.x;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  constexpr int kPer = 4;
+  for (int64_t off = 0; off < nchunks; off += kBinBlock * kPer) {
+    uint64_t x[kPer], sum = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int64_t c = off + (int64_t)tid * kPer + j;
+      x[j] = c < nchunks ? csum[c * kDigits + d] : 0;
+      sum += x[j];
+    }
+    const uint64_t inc = wave_inclusive_scan(sum);
+    if (lane == kWave - 1) s_w[wave] = inc;
+    __syncthreads();
+    uint64_t pre = s_carry + inc - sum;
+    for (int w = 0; w < wave; ++w) pre += s_w[w];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int64_t c = off + (int64_t)tid * kPer + j;
+      if (c < nchunks) csum[c * kDigits + d] = pre;
+      pre += x[j];
+    }
+    __syncthreads();
+    if (tid == kBinBlock - 1) s_carry = pre;
+    __syncthreads();
+  }
+  if (tid == 0) totals[d] = s_carry;
+}
+
+// Scattering pass: writes the partition's pairs, keys[p] = tile << 32 | depth bits and
+// vals[p] = Gaussian id, at their place in the order (tile & 255, depth, id).  The pairs
+// are generated as in the counting pass, moved through LDS into wavefront-striped order,
+// ranked stably by digit (wavefront ballots match equal digits), regrouped by digit in
+// LDS and written as one contiguous run per digit; a run starts at the digit's global
+// base plus the digit's count in earlier partitions.
+__global__ __launch_bounds__(kBinBlock) void k_emit_scatter(int64_t v, int64_t P, int64_t nparts,
+                                                            const ushort4* __restrict__ srect,
+                                                            const uint32_t* __restrict__ sdepth,
+                                                            const uint32_t* __restrict__ sid,
+                                                            const uint64_t* __restrict__ goff,
+                                                            const uint32_t* __restrict__ gstart, int tiles_x,
+                                                            const uint32_t* __restrict__ cnt_pre,
+                                                            const uint64_t* __restrict__ cpre,
+                                                            const uint64_t* __restrict__ totals,
+                                                            uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+  constexpr int kPad = kEmitPart + kEmitPart / kEmitPer;  // one pad slot per lane run
+  __shared__ int32_t s_rel[kEmitPart + 2];
+  __shared__ uint64_t s_keys[kPad];
+  __shared__ uint32_t s_vals[kPad];
+  __shared__ uint32_t s_wh[kBinBlock / kWave][kDigits];  // per-wave digit counters, then offsets
+  __shared__ uint32_t s_lbase[kDigits];                    // partition-local digit starts
+  __shared__ uint64_t s_gbase[kDigits];                    // global digit starts for this partition
+  __shared__ uint64_t s_w[kBinBlock / kWave];
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  for (int i = tid; i < (kBinBlock / kWave) * kDigits; i += kBinBlock) (&s_wh[0][0])[i] = 0;
+  const EmitPart e = stage_partition(blockIdx.x, nparts, v, P, goff, gstart, s_rel);
+  {  // global start of this partition's run of digit d = tid: the digit's base plus its
+     // count in earlier partitions
+    const uint64_t tot = totals[tid];
+    const uint64_t inc = wave_inclusive_scan(tot);
+    if (lane == kWave - 1) s_w[wave] = inc;
+    __syncthreads();
+    uint64_t pre = inc - tot;
+    for (int w = 0; w < wave; ++w) pre += s_w[w];
+    const int64_t b = blockIdx.x;
+    s_gbase[tid] = pre + cpre[(b / kCountParts) * kDigits + tid] + cnt_pre[b * kDigits + tid];
+  }
+  // generate: lane-consecutive, one pad slot per lane so that a wavefront's 8-byte
+  // stores spread over the LDS banks
+  lane_pairs<true>(e, s_rel, srect, sdepth, sid, tiles_x, [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
+    const int slot = tid * (kEmitPer + 1) + k;
+    s_keys[slot] = ((uint64_t)tile << 32) | (uint64_t)dbits;
+    s_vals[slot] = id;
+  });
+  __syncthreads();
+  // wavefront-striped: wave w owns pairs [w * 512, (w + 1) * 512) of the partition
+  constexpr int kWavePart = kEmitPer * kWave;
+  uint64_t key[kEmitPer];
+  uint32_t val[kEmitPer], rank[kEmitPer];
+#pragma unroll
+  for (int j = 0; j < kEmitPer; ++j) {
+    const int p = wave * kWavePart + j * kWave + lane;
+    const int slot = p + p / kEmitPer;
+    key[j] = p < e.n ? s_keys[slot] : ~0ull;
+    val[j] = p < e.n ? s_vals[slot] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kEmitPer; ++j) {
+    const int p = wave * kWavePart + j * kWave + lane;
+    const bool valid = p < e.n;
+    const uint32_t d = (uint32_t)(key[j] >> 32) & (kDigits - 1);
+    const uint64_t m = match_digit(d, 8, __ballot(valid));
+    const uint32_t below = (uint32_t)__popcll(m & lanemask_lt());
+    uint32_t prev = 0;
+    if (valid) prev = s_wh[wave][d];
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    rank[j] = prev + below;
+    if (valid && below == 0) s_wh[wave][d] = prev + (uint32_t)__popcll(m);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  {  // thread d owns digit d: per-wave offsets, then the partition-local digit starts
+    const int d = tid;
+    uint32_t tot = 0;
+#pragma unroll
+    for (int w = 0; w < kBinBlock / kWave; ++w) {
+      const uint32_t c = s_wh[w][d];
+      s_wh[w][d] = tot;
+      tot += c;
+    }
+    const uint64_t inc = wave_inclusive_scan((uint64_t)tot);
+    if (lane == kWave - 1) s_w[wave] = inc;
+    __syncthreads();
+    uint64_t pre = inc - tot;
+    for (int w = 0; w < wave; ++w) pre += s_w[w];
+    s_lbase[d] = (uint32_t)pre;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kEmitPer; ++j) {  // regroup by digit (stable)
+    const int p = wave * kWavePart + j * kWave + lane;
+    if (p < e.n) {
+      const uint32_t d = (uint32_t)(key[j] >> 32) & (kDigits - 1);
+      const uint32_t pos = s_lbase[d] + s_wh[wave][d] + rank[j];
+      s_keys[pos] = key[j];
+      s_vals[pos] = val[j];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < e.n; i += kBinBlock) {
+    const uint64_t k = s_keys[i];
+    const uint32_t d = (uint32_t)(k >> 32) & (kDigits - 1);
+    const uint64_t g = s_gbase[d] + (uint64_t)(i - (int)s_lbase[d]);
+    keys[g] = k;
+    vals[g] = s_vals[i];
+  }
+}
+
+// Workspace layout (bytes).  The arrays sized by the pair count come last, so the count
+// phase (which runs before P is known) and the emission phase agree on every offset.
 struct BinLayout {
-  size_t pair_sums, vis_sums, sorted_sums, totals, dk0, dv0, dk1, dv1, sort, total;
-  int64_t nb;
+  size_t pair_sums, vis_sums, sorted_sums, totals, dk0, dv0, dk1, dv1, sort, goff, srect, dtotals, gstart, cnt_pre,
+      csum, total;
+  int64_t nb, nparts, nchunks;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-static BinLayout bin_layout(int64_t n) {
+static BinLayout bin_layout(int64_t n, int64_t P) {
   BinLayout l;
   l.nb = (n + kBinChunk - 1) / kBinChunk;
+  l.nparts = (P + kEmitPart - 1) / kEmitPart;
+  l.nchunks = (l.nparts + kCountParts - 1) / kCountParts;
   const size_t sums = align256(sizeof(uint64_t) * (size_t)(l.nb + 1));
   const size_t ids = align256(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
   l.pair_sums = 0;
@@ -256,15 +487,21 @@ static BinLayout bin_layout(int64_t n) {
   l.dk1 = l.dv0 + ids;
   l.dv1 = l.dk1 + ids;
   l.sort = l.dv1 + ids;
-  l.total = l.sort + align256(radix_workspace_bytes(n, 0, 32));
+  l.goff = l.sort + align256(radix_workspace_bytes(n, 0, 32));
+  l.srect = l.goff + align256(sizeof(uint64_t) * (size_t)(n + 1));
+  l.dtotals = l.srect + align256(sizeof(uint64_t) * (size_t)(n > 0 ? n : 1));
+  l.gstart = l.dtotals + sizeof(uint64_t) * kDigits;
+  l.cnt_pre = l.gstart + align256(sizeof(uint32_t) * (size_t)(l.nparts + 1));
+  l.csum = l.cnt_pre + align256(sizeof(uint32_t) * kDigits * (size_t)l.nparts);
+  l.total = l.csum + sizeof(uint64_t) * kDigits * (size_t)l.nchunks;
   return l;
 }
 
-size_t bin_workspace_bytes(int64_t n) { return bin_layout(n).total; }
+size_t bin_workspace_bytes(int64_t n, int64_t P) { return bin_layout(n, P).total; }
 
 // Phase 1: per-block sums, their scans, P and the visible count V (device, totals[0..1]).
 hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, void* ws, hipStream_t s) {
-  const BinLayout l = bin_layout(n);
+  const BinLayout l = bin_layout(n, 0);
   char* w = static_cast<char*>(ws);
   uint64_t* ps = reinterpret_cast<uint64_t*>(w + l.pair_sums);
   uint64_t* vs = reinterpret_cast<uint64_t*>(w + l.vis_sums);
@@ -276,14 +513,15 @@ hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, void* ws, hipStr
 }
 
 uint64_t* bin_totals_ptr(int64_t n, void* ws) {
-  return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + bin_layout(n).totals);
+  return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + bin_layout(n, 0).totals);
 }
 
-// Phase 2 (after the host read P and V): compact, depth-sort, emit.
-hipError_t launch_bin_emit(int64_t n, int64_t v, const gs_projected& proj, int tiles_x, void* ws, uint64_t* keys,
-                           uint32_t* vals, hipStream_t s) {
-  if (v == 0) return hipSuccess;
-  const BinLayout l = bin_layout(n);
+// Phase 2 (after the host read P and V): compact, depth-sort, then the two emission
+// passes over partitions of kEmitPart pairs.
+hipError_t launch_bin_emit(int64_t n, int64_t v, int64_t P, const gs_projected& proj, int tiles_x, void* ws,
+                           uint64_t* keys, uint32_t* vals, hipStream_t s) {
+  if (v == 0 || P == 0) return hipSuccess;
+  const BinLayout l = bin_layout(n, P);
   char* w = static_cast<char*>(ws);
   uint32_t* dk0 = reinterpret_cast<uint32_t*>(w + l.dk0);
   uint32_t* dv0 = reinterpret_cast<uint32_t*>(w + l.dv0);
@@ -291,15 +529,25 @@ hipError_t launch_bin_emit(int64_t n, int64_t v, const gs_projected& proj, int t
   uint32_t* dv1 = reinterpret_cast<uint32_t*>(w + l.dv1);
   uint64_t* ss = reinterpret_cast<uint64_t*>(w + l.sorted_sums);
   uint64_t* totals = reinterpret_cast<uint64_t*>(w + l.totals);
+  uint64_t* goff = reinterpret_cast<uint64_t*>(w + l.goff);
+  uint64_t* dtotals = reinterpret_cast<uint64_t*>(w + l.dtotals);
+  uint32_t* gstart = reinterpret_cast<uint32_t*>(w + l.gstart);
+  ushort4* srect = reinterpret_cast<ushort4*>(w + l.srect);
+  const ushort4* rect = reinterpret_cast<const ushort4*>(proj.rect);
+  uint32_t* cnt_pre = reinterpret_cast<uint32_t*>(w + l.cnt_pre);
+  uint64_t* csum = reinterpret_cast<uint64_t*>(w + l.csum);
   k_compact<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, proj.n_tiles, proj.depth,
                                                  reinterpret_cast<const uint64_t*>(w + l.vis_sums), dk0, dv0);
   hipError_t e = radix_sort_u32(v, dk0, dv0, dk1, dv1, 0, 32, w + l.sort, s);
   if (e != hipSuccess) return e;
   const int64_t nbv = (v + kBinChunk - 1) / kBinChunk;
-  k_count_sorted<<<(unsigned)nbv, kBinBlock, 0, s>>>(v, dv0, proj.n_tiles, ss);
+  k_count_sorted<<<(unsigned)nbv, kBinBlock, 0, s>>>(v, dv0, rect, srect, ss);
   k_scan_blocks<<<1, 1024, 0, s>>>(nbv, ss, totals + 2);
-  k_emit<<<(unsigned)nbv, kBinBlock, 0, s>>>(v, dv0, proj.n_tiles, reinterpret_cast<const ushort4*>(proj.rect),
-                                             proj.depth, ss, tiles_x, keys, vals);
+  k_offsets<<<(unsigned)nbv, kBinBlock, 0, s>>>(v, srect, ss, goff, gstart);
+  k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(v, P, l.nparts, srect, goff, gstart, tiles_x, cnt_pre, csum);
+  k_digit_scan<<<kDigits, kBinBlock, 0, s>>>(l.nchunks, csum, dtotals);
+  k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(v, P, l.nparts, srect, dk0, dv0, goff, gstart, tiles_x,
+                                                          cnt_pre, csum, dtotals, keys, vals);
   return hipGetLastError();
 }
 

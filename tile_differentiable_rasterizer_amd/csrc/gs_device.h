@@ -45,6 +45,18 @@ __device__ __forceinline__ T wave_inclusive_scan(T x) {
   return x;
 }
 
+// Lanes of the calling wavefront (among `active`) whose `bits`-bit digit equals this lane's:
+// the intersection of one ballot per digit bit.
+__device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, uint64_t active) {
+  uint64_t m = active;
+  for (int b = 0; b < bits; ++b) {
+    const bool bit = (d >> b) & 1u;
+    const uint64_t bb = __ballot(bit);
+    m &= bit ? bb : ~bb;
+  }
+  return m;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T x) {
 #pragma unroll

@@ -20,7 +20,9 @@
 //                 counts (several earlier partitions per round trip), reorders the
 //                 partition in LDS by digit and writes each digit's run contiguously
 //   k_sort_copy   moves the result back to keys/vals after an odd number of passes
-//   k_ranges      [first, last + 1) of every tile from the sorted keys
+//                 (the depth sort of the binning stage)
+//   k_ranges      [first, last + 1) of every tile from the sorted keys; for the pair sort
+//                 it also does k_sort_copy's move on the way
 #include "gs_device.h"
 
 namespace gs {
@@ -31,6 +33,7 @@ constexpr int kSortPart = kSortBlock * kSortKPT;  // keys per partition
 constexpr int kRadix = 256;
 constexpr int kMaxPasses = 8;
 constexpr int kLookBack = 4;                      // status words read per look-back round trip
+constexpr int kHistCopies = 16;                   // global histogram copies (spreads the atomics)
 constexpr uint64_t kFlagAgg = 1ull << 62;    // partition's own count published
 constexpr uint64_t kFlagPre = 2ull << 62;    // inclusive prefix through this partition
 constexpr uint64_t kValMask = (1ull << 62) - 1;
@@ -45,7 +48,7 @@ SortLayout sort_layout(int64_t n_pairs, int passes) {
   SortLayout l;
   l.parts = (n_pairs + kSortPart - 1) / kSortPart;
   l.hist = 0;
-  l.base = l.hist + sizeof(uint64_t) * kMaxPasses * kRadix;
+  l.base = l.hist + sizeof(uint64_t) * kHistCopies * kMaxPasses * kRadix;
   l.plan = l.base + sizeof(uint64_t) * kMaxPasses * kRadix;
   l.tickets = l.plan + 256;
   l.status = l.tickets + 256;
@@ -66,17 +69,6 @@ hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Lanes of the calling wavefront (among `active`) whose `bits`-bit digit equals this lane's.
-__device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, uint64_t active) {
-  uint64_t m = active;
-  for (int b = 0; b < bits; ++b) {
-    const bool bit = (d >> b) & 1u;
-    const uint64_t bb = __ballot(bit);
-    m &= bit ? bb : ~bb;
-  }
-  return m;
-}
-
 template <typename K>
 __global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ keys, int64_t P, int lo,
                                                           int passes, uint64_t* __restrict__ hist) {
@@ -85,16 +77,30 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ 
   const int wave = threadIdx.x / kWave;
   for (int i = threadIdx.x; i < (kSortBlock / kWave) * kMaxPasses * kRadix; i += kSortBlock) (&s_h[0][0])[i] = 0;
   __syncthreads();
-  for (int64_t i = (int64_t)blockIdx.x * kSortBlock + threadIdx.x; i < P; i += (int64_t)gridDim.x * kSortBlock) {
-    const uint64_t k = (uint64_t)keys[i] >> lo;
-    for (int p = 0; p < passes; ++p) atomicAdd(&s_h[wave][p * kRadix + ((k >> (8 * p)) & 0xFF)], 1u);
+  for (int64_t b = (int64_t)blockIdx.x * kSortPart; b < P; b += (int64_t)gridDim.x * kSortPart) {
+    K k[kSortKPT];  // all loads in flight before the first atomic
+#pragma unroll
+    for (int j = 0; j < kSortKPT; ++j) {
+      const int64_t i = b + j * kSortBlock + threadIdx.x;
+      k[j] = i < P ? keys[i] : (K)0;
+    }
+#pragma unroll
+    for (int j = 0; j < kSortKPT; ++j) {
+      if (b + j * kSortBlock + threadIdx.x >= P) break;
+      const uint64_t kk = (uint64_t)k[j] >> lo;
+      for (int p = 0; p < passes; ++p) atomicAdd(&s_h[wave][p * kRadix + ((kk >> (8 * p)) & 0xFF)], 1u);
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < passes * kRadix; i += kSortBlock) {
     uint32_t c = 0;
 #pragma unroll
     for (int w = 0; w < kSortBlock / kWave; ++w) c += s_h[w][i];
-    if (c) atomicAdd(reinterpret_cast<unsigned long long*>(&hist[i]), (unsigned long long)c);
+    // workgroup b adds into copy b % kHistCopies, so no address sees more than
+    // 1/kHistCopies of the workgroups' atomics
+    if (c)
+      atomicAdd(reinterpret_cast<unsigned long long*>(&hist[(blockIdx.x % kHistCopies) * kMaxPasses * kRadix + i]),
+                (unsigned long long)c);
   }
 }
 
@@ -106,7 +112,9 @@ __global__ __launch_bounds__(kRadix) void k_sort_plan(const uint64_t* __restrict
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   int cur = 0;
   for (int p = 0; p < passes; ++p) {
-    const uint64_t h = hist[p * kRadix + tid];
+    uint64_t h = 0;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) h += hist[c * kMaxPasses * kRadix + p * kRadix + tid];
     const uint64_t inc = wave_inclusive_scan(h);
     if (lane == kWave - 1) s_w[wave] = inc;
     __syncthreads();
@@ -272,21 +280,52 @@ __global__ void k_sort_copy(const int32_t* __restrict__ plan, const K* __restric
 }
 
 // Four consecutive keys per thread; a tile's first and last positions are where its id
-// differs from the neighbour's.
-__global__ void k_ranges(const uint64_t* __restrict__ keys, int64_t P, int64_t num_tiles,
-                         int64_t* __restrict__ ranges) {
+// differs from the neighbour's.  With a plan (the sort ran), the sorted pairs are read
+// from the buffer the last pass wrote and, when that is the scratch buffer, moved back to
+// keys/vals on the way.
+__global__ void k_ranges(const int32_t* __restrict__ plan, const uint64_t* __restrict__ ktmp,
+                         const uint32_t* __restrict__ vtmp, uint64_t* __restrict__ keys, uint32_t* __restrict__ vals,
+                         int64_t P, int64_t num_tiles, int64_t* __restrict__ ranges) {
   const int64_t i0 = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   if (i0 >= P) return;
-  uint64_t t[6];  // tiles of keys i0 - 1 .. i0 + 4 (~0 outside [0, P))
-  t[0] = i0 > 0 ? keys[i0 - 1] >> 32 : ~0ull;
+  const bool in_tmp = plan && plan[kMaxPasses] != 0;
+  const uint64_t* src = in_tmp ? ktmp : keys;
+  // 16-byte accesses when every buffer allows them (i0 is a multiple of 4)
+  const bool vec16 = ((reinterpret_cast<uintptr_t>(ktmp) | reinterpret_cast<uintptr_t>(vtmp) |
+                       reinterpret_cast<uintptr_t>(keys) | reinterpret_cast<uintptr_t>(vals)) & 15) == 0;
+  uint64_t k[6];  // keys i0 - 1 .. i0 + 4 (~0 outside [0, P))
+  k[0] = i0 > 0 ? src[i0 - 1] : ~0ull;
+  if (vec16 && i0 + 4 <= P) {
+    const ulonglong2 a = reinterpret_cast<const ulonglong2*>(src + i0)[0];
+    const ulonglong2 c = reinterpret_cast<const ulonglong2*>(src + i0)[1];
+    k[1] = a.x; k[2] = a.y; k[3] = c.x; k[4] = c.y;
+    k[5] = i0 + 4 < P ? src[i0 + 4] : ~0ull;
+  } else {
 #pragma unroll
-  for (int j = 0; j < 5; ++j) t[j + 1] = i0 + j < P ? keys[i0 + j] >> 32 : ~0ull;
+    for (int j = 0; j < 5; ++j) k[j + 1] = i0 + j < P ? src[i0 + j] : ~0ull;
+  }
+  if (in_tmp) {
+    if (vec16 && i0 + 4 <= P) {  // 16-byte moves
+      reinterpret_cast<ulonglong2*>(keys + i0)[0] = make_ulonglong2(k[1], k[2]);
+      reinterpret_cast<ulonglong2*>(keys + i0)[1] = make_ulonglong2(k[3], k[4]);
+      reinterpret_cast<uint4*>(vals + i0)[0] = reinterpret_cast<const uint4*>(vtmp + i0)[0];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (i0 + j < P) {
+          keys[i0 + j] = k[j + 1];
+          vals[i0 + j] = vtmp[i0 + j];
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int j = 1; j <= 4; ++j) {
     const int64_t i = i0 + j - 1;
-    if (i >= P || t[j] >= (uint64_t)num_tiles) continue;
-    if (t[j - 1] != t[j]) ranges[2 * t[j]] = i;
-    if (t[j + 1] != t[j]) ranges[2 * t[j] + 1] = i + 1;
+    const uint64_t t = k[j] >> 32;
+    if (i >= P || t >= (uint64_t)num_tiles) continue;
+    if ((k[j - 1] >> 32) != t) ranges[2 * t] = i;
+    if ((k[j + 1] >> 32) != t) ranges[2 * t + 1] = i + 1;
   }
 }
 
@@ -329,10 +368,11 @@ static int radix_passes(int lo, int hi) { return hi > lo ? (hi - lo + 7) / 8 : 0
 
 size_t radix_workspace_bytes(int64_t P, int lo, int hi) { return sort_layout(P, radix_passes(lo, hi)).total; }
 
-// Stable LSD sort of (keys, vals) by key bits [lo, hi); the result ends in keys/vals.
+// Stable LSD sort of (keys, vals) by key bits [lo, hi).  The result ends in keys/vals, or
+// with copy_back = false in the buffer that plan[kMaxPasses] names (0 keys, 1 tmp).
 template <typename K>
 static hipError_t radix_sort(int64_t P, K* keys, uint32_t* vals, K* keys_tmp, uint32_t* vals_tmp, int lo, int hi,
-                             void* ws, hipStream_t s) {
+                             void* ws, hipStream_t s, bool copy_back = true) {
   const int passes = radix_passes(lo, hi);
   if (P <= 1 || passes == 0) return hipSuccess;
   const SortLayout l = sort_layout(P, passes);
@@ -346,7 +386,7 @@ static hipError_t radix_sort(int64_t P, K* keys, uint32_t* vals, K* keys_tmp, ui
   hipError_t e = launch_fill_u32(w, (int64_t)(l.total / 4), 0u, s);
   if (e != hipSuccess) return e;
   {
-    const int64_t want = (P + kSortBlock * 16 - 1) / (kSortBlock * 16);
+    const int64_t want = (P + kSortPart - 1) / kSortPart;
     const unsigned blocks = (unsigned)(want < 2048 ? (want > 0 ? want : 1) : 2048);
     k_sort_hist<K><<<blocks, kSortBlock, 0, s>>>(keys, P, lo, passes, hist);
   }
@@ -357,9 +397,11 @@ static hipError_t radix_sort(int64_t P, K* keys, uint32_t* vals, K* keys_tmp, ui
                                                           plan, dbase + p * kRadix,
                                                           status + (size_t)p * l.parts * kRadix, tickets);
   }
-  const int64_t want = (P + 255) / 256;
-  const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
-  k_sort_copy<K><<<blocks, 256, 0, s>>>(plan, keys_tmp, vals_tmp, keys, vals, P);
+  if (copy_back) {
+    const int64_t want = (P + 255) / 256;
+    const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+    k_sort_copy<K><<<blocks, 256, 0, s>>>(plan, keys_tmp, vals_tmp, keys, vals, P);
+  }
   return hipGetLastError();
 }
 
@@ -376,11 +418,15 @@ hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* v
                        uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits, void* ws,
                        hipStream_t s) {
   hipError_t e = launch_fill_u32(ranges, 4 * num_tiles, 0u, s);
-  if (e == hipSuccess && P > 0)
-    e = radix_sort<uint64_t>(P, keys, vals, keys_tmp, vals_tmp, sorted_low_bits, sort_significant_bits(num_tiles),
-                             ws, s);
+  const int hi = sort_significant_bits(num_tiles);
+  const bool sorts = P > 1 && radix_passes(sorted_low_bits, hi) > 0;
+  if (e == hipSuccess && sorts)
+    e = radix_sort<uint64_t>(P, keys, vals, keys_tmp, vals_tmp, sorted_low_bits, hi, ws, s, false);
   if (e != hipSuccess) return e;
-  if (P > 0) k_ranges<<<(unsigned)((P + 1023) / 1024), 256, 0, s>>>(keys, P, num_tiles, ranges);
+  const int32_t* plan = sorts ? reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + sort_layout(P, 0).plan)
+                              : nullptr;
+  if (P > 0)
+    k_ranges<<<(unsigned)((P + 1023) / 1024), 256, 0, s>>>(plan, keys_tmp, vals_tmp, keys, vals, P, num_tiles, ranges);
   if (order) k_tile_order<<<1, 1024, 0, s>>>(ranges, num_tiles, order);
   return hipGetLastError();
 }

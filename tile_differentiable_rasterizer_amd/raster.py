@@ -167,11 +167,11 @@ def bin_tiles(proj: dict, cam, keys, vals, workspace, stream=None) -> tuple[int,
 
 
 def sort_keys(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, ranges, workspace, order=None,
-              sorted_low_bits: int = 32, stream=None):
+              sorted_low_bits: int = 40, stream=None):
     """gs_sort_keys; ``order`` (int32 [num_tiles], optional) receives the longest-first tile order.
 
-    ``sorted_low_bits`` = 32 for pairs from gs_bin_tiles (already in depth order), 0 for
-    arbitrary keys."""
+    ``sorted_low_bits`` = 40 for pairs from gs_bin_tiles (already ordered by tile low byte,
+    then depth), 0 for arbitrary keys."""
     _check(lib().gs_sort_keys(n_pairs, num_tiles, int(sorted_low_bits), _ptr(keys), _ptr(vals), _ptr(keys_tmp),
                               _ptr(vals_tmp), _ptr(ranges), _ptr(order), _ptr(workspace), workspace.numel(),
                               _stream(stream)), "gs_sort_keys")
