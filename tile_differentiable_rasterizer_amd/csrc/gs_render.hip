@@ -11,17 +11,20 @@
 // L2 norms of every pixel's 2D-mean gradient (the absolute gradient).
 //
 // Mapping: one 256-lane workgroup per 16x16 tile, one pixel per lane; wavefront w owns the
-// 8x8 quadrant (w & 1, w >> 1).  The tile's list is gathered a batch at a time (one record
-// per lane, the next batch prefetched into registers) and staged in LDS with a 4-bit mask
-// of the quadrants each record's support box touches.  Each wavefront ballots that mask
-// and visits only its set bits, reading records back as uniform broadcasts, one record
-// ahead of the arithmetic.  A pixel stops once T < 1e-4, a wavefront once its 64 pixels
-// have, the tile once all four have.  Tiles run in the order given by tile_order (longest
-// lists first) so that the long tiles start early.
+// 8x8 quadrant (w & 1, w >> 1) and walks the tile's list on its own, 64 records at a time:
+// each lane gathers one record (the next chunk is prefetched into registers), tests it
+// against the quadrant (support box, then the exact ellipse bound) and stages it in the
+// wavefront's slice of LDS.  The wavefront ballots the test and visits only the set bits,
+// reading records back as uniform broadcasts, one record ahead of the arithmetic.  No
+// workgroup barrier couples the four quadrants, so a quadrant with a short list does not
+// wait for the others.  A pixel stops once T < 1e-4, a wavefront once its 64 pixels have.
+// Tiles run in the order given by tile_order (longest lists first) so that the long tiles
+// start early.
 //
-// The backward walks each wavefront's records in reverse three at a time and sums the
-// three records' ten per-pixel gradient terms over the wavefront in one transposed
-// reduction; each wavefront adds its sums to the Gaussians' gradients with fp32 atomics.
+// The backward walks each wavefront's records [0, last contributor) in reverse three at a
+// time and sums the three records' ten per-pixel gradient terms over the wavefront in one
+// transposed reduction; each wavefront adds its sums to the Gaussians' gradients with
+// fp32 atomics.
 #include "gs_device.h"
 #include "gs_wave.h"
 
@@ -29,7 +32,6 @@ namespace gs {
 
 constexpr int kRenderBlock = 256;
 constexpr int kRenderWaves = kRenderBlock / kWave;
-constexpr int kBwdBatch = 128;  // records staged per backward batch (bounds LDS use)
 
 // Staged record: (u, v, a2, b2) (c2, opacity, r, g) (b, box x, box y, id) [A, B, C, 0].
 // a2, b2, c2 are the conic scaled to the base-2 exponent: -log2(e)/2 * (A, 2B, C).
@@ -48,16 +50,6 @@ __device__ __forceinline__ float gauss_exponent(float a2, float b2, float c2, fl
 }
 
 __device__ __forceinline__ float gauss_factor(float e) { return __builtin_amdgcn_exp2f(e); }
-
-// Which 8x8 quadrants of the tile at pixel (tx0, ty0) does the record's pixel box
-// [x0, x1] x [y0, y1] (packed u16 pairs) touch?  Bit q = quadrant (q & 1, q >> 1).
-__device__ __forceinline__ uint32_t quadrant_mask(uint32_t bx, uint32_t by, int tx0, int ty0) {
-  const int x0 = (int)(bx & 0xFFFFu), x1 = (int)(bx >> 16);
-  const int y0 = (int)(by & 0xFFFFu), y1 = (int)(by >> 16);
-  const uint32_t cx = (x0 <= tx0 + 7 && x1 >= tx0 ? 1u : 0u) | (x0 <= tx0 + 15 && x1 >= tx0 + 8 ? 2u : 0u);
-  const uint32_t cy = (y0 <= ty0 + 7 && y1 >= ty0 ? 1u : 0u) | (y0 <= ty0 + 15 && y1 >= ty0 + 8 ? 2u : 0u);
-  return (cy & 1u ? cx : 0u) | (cy & 2u ? cx << 2 : 0u);
-}
 
 // Largest value over the box [X0, X1] x [Y0, Y1] (offsets from the 2D mean) of the
 // negative-definite exponent f = a2 x^2 + b2 x y + c2 y^2: 0 if the box holds the mean,
@@ -79,22 +71,20 @@ __device__ __forceinline__ float box_max_exponent(float a2, float b2, float c2, 
   return best;
 }
 
-// The quadrants of a tile whose pixel centres the record can reach with alpha >= 1/255:
-// the support box test, refined by the exact ellipse-versus-quadrant test with a margin of
-// 0.01 in the base-2 exponent (so float32 rounding in the per-pixel evaluation can never
-// make a skipped pixel reach the threshold).  s0, s1 are the staged record words.
-__device__ __forceinline__ uint32_t reach_mask(const float4 s0, const float4 s1, uint32_t bx, uint32_t by, int tx0,
-                                               int ty0) {
-  uint32_t m = quadrant_mask(bx, by, tx0, ty0);
-  if (!m) return 0u;
+// Can the record reach a pixel centre of the 8x8 quadrant with top-left pixel (qx0, qy0)
+// with alpha >= 1/255?  The record's pixel box (packed u16 pairs bx, by) must meet the
+// quadrant, and the exact maximum of its exponent over the quadrant must clear the
+// threshold with a margin of 0.01 in the base-2 exponent (so float32 rounding in the
+// per-pixel evaluation can never make a skipped pixel reach it).  s0, s1 are the staged
+// record words.
+__device__ __forceinline__ bool quadrant_reach(const float4 s0, const float4 s1, uint32_t bx, uint32_t by, int qx0,
+                                               int qy0) {
+  const int x0 = (int)(bx & 0xFFFFu), x1 = (int)(bx >> 16);
+  const int y0 = (int)(by & 0xFFFFu), y1 = (int)(by >> 16);
+  if (!(x0 <= qx0 + 7 && x1 >= qx0 && y0 <= qy0 + 7 && y1 >= qy0)) return false;
   const float thr = __builtin_amdgcn_logf(kAlphaMin) - __builtin_amdgcn_logf(s1.y) - 0.01f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (!((m >> q) & 1u)) continue;
-    const float X0 = (float)(tx0 + (q & 1) * 8) + 0.5f - s0.x, Y0 = (float)(ty0 + (q >> 1) * 8) + 0.5f - s0.y;
-    if (box_max_exponent(s0.z, s0.w, s1.x, X0, X0 + 7.0f, Y0, Y0 + 7.0f) < thr) m &= ~(1u << q);
-  }
-  return m;
+  const float X0 = (float)qx0 + 0.5f - s0.x, Y0 = (float)qy0 + 0.5f - s0.y;
+  return box_max_exponent(s0.z, s0.w, s1.x, X0, X0 + 7.0f, Y0, Y0 + 7.0f) >= thr;
 }
 
 __device__ __forceinline__ int tile_of(const int32_t* __restrict__ order, int b) { return order ? order[b] : b; }
@@ -103,11 +93,10 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
     const float4* __restrict__ rec, const uint32_t* __restrict__ vals, const int64_t* __restrict__ ranges,
     const int32_t* __restrict__ order, int W, int H, int tiles_x, float bg0, float bg1, float bg2,
     float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ n_contrib) {
-  __shared__ float4 s_rec[kRenderBlock * 3];
-  __shared__ uint8_t s_qm[kRenderBlock];  // quadrants each staged record touches
+  __shared__ float4 s_rec[kRenderWaves][kWave * 3];  // each wavefront's staged chunk
   const int tile = tile_of(order, blockIdx.x);
   const int tx = tile % tiles_x, ty = tile / tiles_x;
-  const int t = threadIdx.x, lane = __lane_id(), wave = t / kWave;
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
   const int qx0 = tx * kTile + (wave & 1) * 8, qy0 = ty * kTile + (wave >> 1) * 8;
   const int px = qx0 + (lane & 7), py = qy0 + (lane >> 3);
   const float fx = (float)px + 0.5f, fy = (float)py + 0.5f;
@@ -116,59 +105,74 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
   float T = 1.0f, cr = 0.0f, cg = 0.0f, cb = 0.0f;
   uint32_t nc = 0;
   const int64_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
+  float4* my = s_rec[wave];
 
+  // Each wavefront walks the whole list on its own, 64 records at a time: lane l gathers
+  // record c + l (the next chunk is prefetched into registers while this one is
+  // composited), tests it against the wavefront's quadrant and stages it in the
+  // wavefront's LDS slice.  No workgroup barrier: a wavefront never waits for the others.
   float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0, p2 = p0;
-  if (start + t < end) {
-    const uint32_t id = vals[start + t];
+  if (start + lane < end) {
+    const uint32_t id = vals[start + lane];
     p0 = rec[3 * (size_t)id]; p1 = rec[3 * (size_t)id + 1]; p2 = rec[3 * (size_t)id + 2];
   }
-  for (int64_t b = start; b < end; b += kRenderBlock) {
-    if (__syncthreads_count(live) == 0) break;  // also fences the previous batch's reads
-    const int cnt = (int)min((int64_t)kRenderBlock, end - b);
-    {
-      float4 s0, s1;
-      stage_transform(p0, p1, s0, s1);
-      s_rec[3 * t] = s0; s_rec[3 * t + 1] = s1; s_rec[3 * t + 2] = p2;
-      s_qm[t] = t < cnt ? (uint8_t)reach_mask(s0, s1, __float_as_uint(p2.y), __float_as_uint(p2.z), tx * kTile,
-                                              ty * kTile)
-                        : (uint8_t)0;
-    }
-    __syncthreads();
-    if (b + kRenderBlock + t < end) {  // prefetch the next batch
-      const uint32_t id = vals[b + kRenderBlock + t];
+  for (int64_t b = start; b < end; b += kWave) {
+    if (!__ballot(live)) break;  // this wavefront's pixels are all done
+    float4 s0, s1;
+    stage_transform(p0, p1, s0, s1);
+    const bool reach =
+        b + lane < end && quadrant_reach(s0, s1, __float_as_uint(p2.y), __float_as_uint(p2.z), qx0, qy0);
+    // the previous chunk's reads are done before these writes, which are done before the
+    // reads below (LDS operations of one wavefront stay in order once issued)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    my[3 * lane] = s0; my[3 * lane + 1] = s1; my[3 * lane + 2] = p2;
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    uint64_t m = __ballot(reach);
+    if (b + kWave + lane < end) {  // prefetch the next chunk
+      const uint32_t id = vals[b + kWave + lane];
       p0 = rec[3 * (size_t)id]; p1 = rec[3 * (size_t)id + 1]; p2 = rec[3 * (size_t)id + 2];
     }
+    if (!m) continue;
     const uint32_t kb = (uint32_t)(b - start) + 1u;  // list position + 1 of staged record 0
-    for (int c = 0; c < cnt; c += kWave) {
-      if (!__ballot(live)) break;  // this wavefront's pixels are all done
-      // the records of this chunk that touch this wavefront's quadrant, as a scalar mask
-      uint64_t m = __ballot((s_qm[c + lane] >> wave) & 1u);
-      if (!m) continue;
-      int j = c + __builtin_ctzll(m);
+    // one record's contribution; a record this lane does not take gets alpha 0, which
+    // leaves T, the colour and nc exactly as they were
+    auto blend = [&](const float4 a, const float4 e1, float bb, uint32_t pos) {
+      const float dx = fx - a.x, dy = fy - a.y;
+      const float alpha = fminf(kAlphaMax, e1.y * gauss_factor(gauss_exponent(a.z, a.w, e1.x, dx, dy)));
+      const bool take = live && alpha >= kAlphaMin;
+      const float at = take ? alpha : 0.0f;
+      const float w = at * T;
+      cr = fmaf(e1.z, w, cr);
+      cg = fmaf(e1.w, w, cg);
+      cb = fmaf(bb, w, cb);
+      T = T * (1.0f - at);
+      nc = take ? pos : nc;
+      live = live && !(T < kTMin);
+    };
+    // two records per iteration in alternating registers: each one's LDS reads are
+    // issued while the previous one is evaluated
+    int j = __builtin_ctzll(m);
+    m &= m - 1;
+    float4 a0 = my[3 * j], b0 = my[3 * j + 1];
+    float c0 = my[3 * j + 2].x;
+    while (true) {
+      const bool more1 = m != 0;
+      const int j1 = more1 ? __builtin_ctzll(m) : j;
       m &= m - 1;
-      float4 a = s_rec[3 * j], e1 = s_rec[3 * j + 1];
-      float bb = s_rec[3 * j + 2].x;
-      while (true) {
-        // read the next record while this one is evaluated
-        const bool more = m != 0;
-        const int jn = more ? c + __builtin_ctzll(m) : j;
-        m &= m - 1;
-        const float4 an = s_rec[3 * jn], e1n = s_rec[3 * jn + 1];
-        const float bbn = s_rec[3 * jn + 2].x;
-
-        const float dx = fx - a.x, dy = fy - a.y;
-        const float alpha = fminf(kAlphaMax, e1.y * gauss_factor(gauss_exponent(a.z, a.w, e1.x, dx, dy)));
-        const bool take = live && alpha >= kAlphaMin;
-        const float w = take ? alpha * T : 0.0f;
-        cr = fmaf(e1.z, w, cr);
-        cg = fmaf(e1.w, w, cg);
-        cb = fmaf(bb, w, cb);
-        T = take ? T * (1.0f - alpha) : T;
-        nc = take ? kb + (uint32_t)j : nc;
-        live = live && !(T < kTMin);
-        if (!more) break;
-        a = an; e1 = e1n; bb = bbn; j = jn;
-      }
+      const float4 a1 = my[3 * j1], b1 = my[3 * j1 + 1];
+      const float c1 = my[3 * j1 + 2].x;
+      blend(a0, b0, c0, kb + (uint32_t)j);
+      if (!more1) break;
+      const bool more2 = m != 0;
+      j = more2 ? __builtin_ctzll(m) : j1;
+      m &= m - 1;
+      a0 = my[3 * j];
+      b0 = my[3 * j + 1];
+      c0 = my[3 * j + 2].x;
+      blend(a1, b1, c1, kb + (uint32_t)j1);
+      if (!more2) break;
     }
   }
   if (inside) {
@@ -244,12 +248,10 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
     const int32_t* __restrict__ order, int W, int H, int tiles_x, float bg0, float bg1, float bg2,
     const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib, const float* __restrict__ dL,
     float* __restrict__ gscreen) {
-  __shared__ float4 s_rec[kBwdBatch * 4];
-  __shared__ uint8_t s_qm[kBwdBatch];
-  __shared__ uint32_t s_last[kRenderWaves];
+  __shared__ float4 s_rec[kRenderWaves][kWave * 4];  // each wavefront's staged chunk
   const int tile = tile_of(order, blockIdx.x);
   const int tx = tile % tiles_x, ty = tile / tiles_x;
-  const int t = threadIdx.x, lane = __lane_id(), wave = t / kWave;
+  const int lane = __lane_id(), wave = threadIdx.x / kWave;
   const int qx0 = tx * kTile + (wave & 1) * 8, qy0 = ty * kTile + (wave >> 1) * 8;
   const int px = qx0 + (lane & 7), py = qy0 + (lane >> 3);
   const size_t plane = (size_t)W * H;
@@ -268,83 +270,79 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
   // the (record, term) whose wavefront sum this lane receives from the transposed reduction
   const int red_r = (lane >> 1) / GS_GRAD_SCREEN, red_e = (lane >> 1) - red_r * GS_GRAD_SCREEN;
   const float red_scale = term_scale(red_e);
-  if (lane == 0) s_last[wave] = wlast;
-  __syncthreads();
-  uint32_t last = 0;
-#pragma unroll
-  for (int w = 0; w < kRenderWaves; ++w) last = s_last[w] > last ? s_last[w] : last;
   const int64_t start = ranges[2 * tile];
-  // batches walk down from the last contributor; each one's records are gathered into
-  // registers while the previous batch is processed
+  float4* my = s_rec[wave];
+  // Each wavefront walks its own records [0, wlast) down from the top, 64 at a time:
+  // lane l gathers record lo + l (the next, earlier chunk is prefetched into registers
+  // while this one is processed), tests it against the wavefront's quadrant and stages it
+  // in the wavefront's LDS slice.  No workgroup barrier: a wavefront never waits for the
+  // others.
   uint32_t pid = 0;
   float4 q0 = make_float4(0.f, 0.f, 0.f, 0.f), q1 = q0, q2 = q0;
   {
-    const int64_t hi = start + last, lo = hi - kBwdBatch > start ? hi - kBwdBatch : start;
-    if (t < hi - lo) {
-      pid = vals[lo + t];
+    const int64_t hi = start + wlast, lo = hi - kWave > start ? hi - kWave : start;
+    if (lo + lane < hi) {
+      pid = vals[lo + lane];
       q0 = rec[3 * (size_t)pid]; q1 = rec[3 * (size_t)pid + 1]; q2 = rec[3 * (size_t)pid + 2];
     }
   }
-  for (int64_t hi = start + last; hi > start; hi -= kBwdBatch) {
-    const int64_t lo = hi - kBwdBatch > start ? hi - kBwdBatch : start;
-    const int cnt = (int)(hi - lo);
-    __syncthreads();  // every wavefront is done with the previous batch
-    if (t < cnt) {
-      const uint32_t id = pid;
-      const float4 r0 = q0, r1 = q1, r2 = q2;
+  for (int64_t hi = start + wlast; hi > start; hi -= kWave) {
+    const int64_t lo = hi - kWave > start ? hi - kWave : start;
+    bool reach;
+    {
       float4 s0, s1;
-      stage_transform(r0, r1, s0, s1);
-      s_rec[4 * t] = s0;
-      s_rec[4 * t + 1] = s1;
-      s_rec[4 * t + 2] = make_float4(r2.x, r2.y, r2.z, __uint_as_float(id));
-      s_rec[4 * t + 3] = make_float4(r0.z, r0.w, r1.x, 0.0f);
-      s_qm[t] = (uint8_t)reach_mask(s0, s1, __float_as_uint(r2.y), __float_as_uint(r2.z), tx * kTile, ty * kTile);
-    } else if (t < kBwdBatch) {
-      s_qm[t] = 0;
+      stage_transform(q0, q1, s0, s1);
+      reach = lo + lane < hi && quadrant_reach(s0, s1, __float_as_uint(q2.y), __float_as_uint(q2.z), qx0, qy0);
+      // the previous chunk's reads are done before these writes, which are done before
+      // the reads below (LDS operations of one wavefront stay in order once issued)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      my[4 * lane] = s0;
+      my[4 * lane + 1] = s1;
+      my[4 * lane + 2] = make_float4(q2.x, q2.y, q2.z, __uint_as_float(pid));
+      my[4 * lane + 3] = make_float4(q0.z, q0.w, q1.x, 0.0f);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();
-    {  // prefetch the next (earlier) batch
-      const int64_t nhi = lo, nlo = nhi - kBwdBatch > start ? nhi - kBwdBatch : start;
-      if (t < nhi - nlo) {
-        pid = vals[nlo + t];
+    uint64_t m = __ballot(reach);
+    {  // prefetch the next (earlier) chunk
+      const int64_t nhi = lo, nlo = nhi - kWave > start ? nhi - kWave : start;
+      if (nlo + lane < nhi) {
+        pid = vals[nlo + lane];
         q0 = rec[3 * (size_t)pid]; q1 = rec[3 * (size_t)pid + 1]; q2 = rec[3 * (size_t)pid + 2];
       }
     }
-    const int jtop = (int)min((int64_t)cnt, (int64_t)wlast - (lo - start));  // records this wave may use
-    for (int c = ((jtop - 1) / kWave) * kWave; c >= 0 && jtop > 0; c -= kWave) {
-      uint64_t m = __ballot(c + lane < jtop && ((s_qm[c + lane] >> wave) & 1u));
-      while (m) {
-        // the next three records of the reverse walk (highest position first); the bit
-        // positions stay scalar so the walk is a uniform loop
-        // a step short of three records repeats the first one at position 2^32 - 1, past
-        // every pixel's last contributor, so it adds zeros and leaves the walk unchanged
-        int js[3];
-        uint32_t ks[3];
+    while (m) {
+      // the next three records of the reverse walk (highest position first); the bit
+      // positions stay scalar so the walk is a uniform loop.  A step short of three
+      // records repeats the first one at position 2^32 - 1, past every pixel's last
+      // contributor, so it adds zeros and leaves the walk unchanged.
+      int js[3];
+      uint32_t ks[3];
 #pragma unroll
-        for (int r = 0; r < 3; ++r) {
-          const bool has = m != 0;
-          const int bit = has ? __builtin_amdgcn_readfirstlane(63 - __builtin_clzll(m)) : 0;
-          js[r] = has ? c + bit : js[0];
-          ks[r] = has ? (uint32_t)(lo - start + c + bit) : 0xFFFFFFFFu;
-          if (has) m &= ~(1ull << bit);
-        }
-        float v[32];
-        bool hit[3];
+      for (int r = 0; r < 3; ++r) {
+        const bool has = m != 0;
+        const int bit = has ? __builtin_amdgcn_readfirstlane(63 - __builtin_clzll(m)) : 0;
+        js[r] = has ? bit : js[0];
+        ks[r] = has ? (uint32_t)(lo - start + bit) : 0xFFFFFFFFu;
+        if (has) m &= ~(1ull << bit);
+      }
+      float v[32];
+      bool hit[3];
 #pragma unroll
-        for (int r = 0; r < 3; ++r) hit[r] = bwd_record(s_rec, js[r], ks[r], p, v + GS_GRAD_SCREEN * r);
-        v[30] = 0.0f;
-        v[31] = 0.0f;
-        const uint64_t h0 = __ballot(hit[0]), h1 = __ballot(hit[1]), h2 = __ballot(hit[2]);
-        if (h0 | h1 | h2) {
-          // lanes 2i and 2i + 1 now hold the wavefront's sum of v[i]; the even lane of each
-          // (record, term) pair of a record some pixel took adds it to the Gaussian's gradient
-          const float sum = wave_transpose_reduce32(v);
-          const uint64_t act = (h0 ? kRedLanes0 : 0ull) | (h1 ? kRedLanes1 : 0ull) | (h2 ? kRedLanes2 : 0ull);
-          const int jr = red_r == 0 ? js[0] : red_r == 1 ? js[1] : js[2];
-          if ((act >> lane) & 1ull) {
-            const uint32_t id = __float_as_uint(s_rec[4 * jr + 2].w);
-            atomicAdd(gscreen + (size_t)GS_GRAD_SCREEN * id + red_e, sum * red_scale);
-          }
+      for (int r = 0; r < 3; ++r) hit[r] = bwd_record(my, js[r], ks[r], p, v + GS_GRAD_SCREEN * r);
+      v[30] = 0.0f;
+      v[31] = 0.0f;
+      const uint64_t h0 = __ballot(hit[0]), h1 = __ballot(hit[1]), h2 = __ballot(hit[2]);
+      if (h0 | h1 | h2) {
+        // lanes 2i and 2i + 1 now hold the wavefront's sum of v[i]; the even lane of each
+        // (record, term) pair of a record some pixel took adds it to the Gaussian's gradient
+        const float sum = wave_transpose_reduce32(v);
+        const uint64_t act = (h0 ? kRedLanes0 : 0ull) | (h1 ? kRedLanes1 : 0ull) | (h2 ? kRedLanes2 : 0ull);
+        const int jr = red_r == 0 ? js[0] : red_r == 1 ? js[1] : js[2];
+        if ((act >> lane) & 1ull) {
+          const uint32_t id = __float_as_uint(my[4 * jr + 2].w);
+          atomicAdd(gscreen + (size_t)GS_GRAD_SCREEN * id + red_e, sum * red_scale);
         }
       }
     }
