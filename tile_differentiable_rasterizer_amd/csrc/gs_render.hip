@@ -116,6 +116,9 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
     const uint32_t id = vals[start + lane];
     p0 = rec[3 * (size_t)id]; p1 = rec[3 * (size_t)id + 1]; p2 = rec[3 * (size_t)id + 2];
   }
+  // ids run one chunk ahead of the records, so a chunk's record gathers wait on one
+  // memory round trip instead of two
+  uint32_t nid = start + kWave + lane < end ? vals[start + kWave + lane] : 0u;
   for (int64_t b = start; b < end; b += kWave) {
     if (!__ballot(live)) break;  // this wavefront's pixels are all done
     float4 s0, s1;
@@ -131,9 +134,9 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
     __builtin_amdgcn_wave_barrier();
     uint64_t m = __ballot(reach);
     if (b + kWave + lane < end) {  // prefetch the next chunk
-      const uint32_t id = vals[b + kWave + lane];
-      p0 = rec[3 * (size_t)id]; p1 = rec[3 * (size_t)id + 1]; p2 = rec[3 * (size_t)id + 2];
+      p0 = rec[3 * (size_t)nid]; p1 = rec[3 * (size_t)nid + 1]; p2 = rec[3 * (size_t)nid + 2];
     }
+    nid = b + 2 * kWave + lane < end ? vals[b + 2 * kWave + lane] : 0u;
     if (!m) continue;
     const uint32_t kb = (uint32_t)(b - start) + 1u;  // list position + 1 of staged record 0
     // one record's contribution; a record this lane does not take gets alpha 0, which
