@@ -284,7 +284,7 @@ def cpu_baseline(sc, cams, dLs, budget):
         dL = dL.astype(np.float64)
         t0 = time.perf_counter()
         proj = oracle.project(sc, cam)
-        keys, vals = oracle.emit_pairs(proj["trect"], proj["n_tiles"], proj["depth_bits"], cam.tiles_x)
+        keys, vals = oracle.emit_projected(proj, cam.tiles_x)
         skeys, svals = oracle.sort_pairs(keys, vals)
         ranges = oracle.tile_ranges(skeys, cam.num_tiles)
         rec = oracle.records(proj)

@@ -51,6 +51,8 @@ def _load():
             build(force=True)
         _lib = C.CDLL(_LIB)
         _lib.orc_count_pairs.restype = C.c_int64
+        _lib.orc_emit_pairs.restype = C.c_int64
+        _lib.orc_box_min_q.restype = C.c_double
         _lib.orc_forward.restype = C.c_uint64
     return _lib
 
@@ -119,19 +121,80 @@ def records(proj: dict) -> np.ndarray:
         [proj["uv"], proj["conic"], proj["opacity"][:, None], proj["rgb"]], axis=1))
 
 
-def emit_pairs(trect, n_tiles, depth_bits, tiles_x: int):
-    """Pairs in id order: key = tile_id << 32 | depth bits, value = Gaussian id."""
+def ellipses(uv, conic, opacity):
+    """Per Gaussian (u, v, A, B, C, tau): the support ellipse the tile test uses."""
+    lib = _load()
+    uv = np.ascontiguousarray(uv, dtype=np.float64)
+    conic = np.ascontiguousarray(conic, dtype=np.float64)
+    opacity = np.ascontiguousarray(opacity, dtype=np.float64)
+    n = opacity.shape[0]
+    ell = np.zeros((n, 6))
+    lib.orc_ellipses(C.c_int64(n), _p(uv), _p(conic), _p(opacity), _p(ell))
+    return ell
+
+
+def box_min_q(A, B, C_, X0, X1, Y0, Y1):
+    """Smallest A x^2 + 2 B x y + C y^2 over [X0, X1] x [Y0, Y1], and its minimiser."""
+    lib = _load()
+    xm, ym = C.c_double(), C.c_double()
+    q = lib.orc_box_min_q(C.c_double(A), C.c_double(B), C.c_double(C_), C.c_double(X0), C.c_double(X1),
+                          C.c_double(Y0), C.c_double(Y1), C.byref(xm), C.byref(ym))
+    return q, (xm.value, ym.value)
+
+
+def tile_keeps(ell, pxrect, tx: int, ty: int):
+    """Ellipse test of one tile for each Gaussian: (keeps, near-threshold flag) arrays."""
+    lib = _load()
+    ell = np.ascontiguousarray(ell, dtype=np.float64).reshape(-1, 6)
+    pxrect = np.ascontiguousarray(pxrect, dtype=np.int64).reshape(-1, 4)
+    n = ell.shape[0]
+    keep = np.zeros(n, np.int32)
+    near = np.zeros(n, np.int32)
+    for i in range(n):
+        f = C.c_int(0)
+        keep[i] = lib.orc_tile_keeps(*(C.c_double(x) for x in ell[i]), _p(pxrect[i]), C.c_int64(tx),
+                                     C.c_int64(ty), C.byref(f))
+        near[i] = f.value
+    return keep.astype(bool), near.astype(bool)
+
+
+def count_kept(trect, pxrect, ell):
+    """Tiles of each rectangle kept by the ellipse test."""
+    lib = _load()
+    trect = np.ascontiguousarray(trect, dtype=np.int32)
+    pxrect = np.ascontiguousarray(pxrect, dtype=np.int32)
+    ell = np.ascontiguousarray(ell, dtype=np.float64)
+    n = trect.shape[0]
+    out = np.zeros(n, np.int64)
+    lib.orc_count_kept(C.c_int64(n), _p(trect), _p(pxrect), _p(ell), _p(out))
+    return out
+
+
+def emit_pairs(trect, n_tiles, depth_bits, tiles_x: int, pxrect=None, ell=None):
+    """Pairs in id order: key = tile_id << 32 | depth bits, value = Gaussian id, for every
+    tile of each rectangle that passes the ellipse test of ell (u, v, A, B, C, tau) inside
+    the pixel box pxrect; every tile of the rectangle when ell is None."""
     lib = _load()
     trect = np.ascontiguousarray(trect, dtype=np.int32)
     n_tiles = np.ascontiguousarray(n_tiles, dtype=np.int64)
     depth_bits = np.ascontiguousarray(depth_bits, dtype=np.uint32)
     n = n_tiles.shape[0]
+    if ell is not None:
+        pxrect = np.ascontiguousarray(pxrect, dtype=np.int32)
+        ell = np.ascontiguousarray(ell, dtype=np.float64)
     P = int(lib.orc_count_pairs(C.c_int64(n), _p(n_tiles)))
     keys = np.zeros(max(P, 1), np.uint64)
     vals = np.zeros(max(P, 1), np.uint32)
-    lib.orc_emit_pairs(C.c_int64(n), _p(trect), _p(n_tiles), _p(depth_bits), C.c_int64(tiles_x),
-                       _p(keys), _p(vals))
+    got = lib.orc_emit_pairs(C.c_int64(n), _p(trect), _p(pxrect), _p(ell), _p(n_tiles), _p(depth_bits),
+                             C.c_int64(tiles_x), _p(keys), _p(vals), C.c_int64(P))
+    assert got == P, f"{got} tiles kept for {P} counted"
     return keys[:P], vals[:P]
+
+
+def emit_projected(proj: dict, tiles_x: int):
+    """emit_pairs for an oracle projection (its rectangles, pixel boxes and ellipses)."""
+    ell = ellipses(proj["uv"], proj["conic"], proj["opacity"])
+    return emit_pairs(proj["trect"], proj["n_tiles"], proj["depth_bits"], tiles_x, proj["pxrect"], ell)
 
 
 def sort_pairs(keys, vals):
@@ -256,7 +319,7 @@ def forward_raw(means, scales, quats, opac, sh, L, cam, bg=(0.0, 0.0, 0.0)):
 def end_to_end(scene, cam, bg=(0.0, 0.0, 0.0), pix=None) -> dict:
     """Project, bin, sort and composite from raw parameters; keeps every stage's output."""
     proj = project(scene, cam)
-    keys, vals = emit_pairs(proj["trect"], proj["n_tiles"], proj["depth_bits"], cam.tiles_x)
+    keys, vals = emit_projected(proj, cam.tiles_x)
     skeys, svals = sort_pairs(keys, vals)
     ranges = tile_ranges(skeys, cam.num_tiles)
     rec = records(proj)

@@ -14,6 +14,9 @@
  *             (SH coefficients per degree), s3.2 the rasterize pipeline.
  *  [ABSGRAD]  "Enabling the absolute-gradient strategy in 3D Gaussian Splatting"
  *             (jsqmd.com) -- s1 densification statistics, s2 the two gradient norms.
+ *  [SPIRULA]  "Training 10M Gaussians in 8 GB: Spirula Studio's VRAM efficiency"
+ *             (mhpq.cn) -- the 16-bit AABB section: a conservative screen box followed by
+ *             an ellipse test as a second cull leaves the rendered image unchanged.
  *
  * The pages omit the covariance and SH formulas ([JULIA-1] s3.2 points at "the original
  * paper's Jacobian approximation").  The readings used here are the textbook ones:
@@ -186,13 +189,70 @@ typedef struct {
   double dir[3], dist;   /* unit view direction and camera distance             */
   double raw[3], rgb[3];
   int clamp[3];
-  int flags;             /* bit0 depth rounding tie, bit1 rect edge, bit2 colour sign */
+  int flags;             /* bit0 depth rounding tie, bit1 rect edge, bit2 colour sign,
+                            bit3 a tile-ellipse decision near its threshold          */
 } orc_gauss;
 
 /* Is x within tol of an integer? */
 static int near_integer(double x, double tol) {
   double r = x - floor(x + 0.5);
   return fabs(r) <= tol;
+}
+
+/*
+ * Smallest value of the positive-definite form q = A x^2 + 2 B x y + C y^2 over the box
+ * [X0, X1] x [Y0, Y1]: 0 when the box holds the origin; otherwise it lies on the boundary,
+ * and on each edge q is a convex quadratic in one variable, smallest at its vertex clamped
+ * to the edge.  (xm, ym) receive the minimising point.
+ */
+static double clampd(double x, double lo, double hi) { return x < lo ? lo : x > hi ? hi : x; }
+
+double orc_box_min_q(double A, double B, double C, double X0, double X1, double Y0, double Y1,
+                     double* xm, double* ym) {
+  if (X0 <= 0 && 0 <= X1 && Y0 <= 0 && 0 <= Y1) {
+    if (xm) { *xm = 0; *ym = 0; }
+    return 0.0;
+  }
+  double best = INFINITY, bx = 0, by = 0;
+  for (int e = 0; e < 2; ++e) {
+    const double X = e ? X1 : X0;             /* edge x = X */
+    const double y = clampd(-B * X / C, Y0, Y1);
+    const double qx = A * X * X + 2 * B * X * y + C * y * y;
+    if (qx < best) { best = qx; bx = X; by = y; }
+    const double Y = e ? Y1 : Y0;             /* edge y = Y */
+    const double x = clampd(-B * Y / A, X0, X1);
+    const double qy = A * x * x + 2 * B * x * Y + C * Y * Y;
+    if (qy < best) { best = qy; bx = x; by = Y; }
+  }
+  if (xm) { *xm = bx; *ym = by; }
+  return best;
+}
+
+/*
+ * The ellipse test of [SPIRULA] (16-bit AABB section), read as an exact test: tile (tx, ty)
+ * of the rectangle stays in the Gaussian's list iff the box spanned by its pixel centres
+ * (inside the Gaussian's pixel box) meets the support ellipse {q <= tau} around (u, v).
+ * A pixel of a dropped tile has q > tau, so alpha < 1/255: the list only loses Gaussians
+ * that cannot contribute.  With margin_flag non-NULL it is set when q's minimum lies
+ * within the bound on how far rounding the record to float32 (the 2D mean and the conic)
+ * can move it: such decisions may legitimately go either way in an implementation that
+ * tests the rounded record.
+ */
+int orc_tile_keeps(double u, double v, double A, double B, double C, double tau, const int64_t px[4],
+                   int64_t tx, int64_t ty, int* margin_flag) {
+  const double X0 = (double)(tx * ORC_TILE > px[0] ? tx * ORC_TILE : px[0]) + 0.5 - u;
+  const double X1 = (double)(tx * ORC_TILE + ORC_TILE - 1 < px[1] ? tx * ORC_TILE + ORC_TILE - 1 : px[1]) + 0.5 - u;
+  const double Y0 = (double)(ty * ORC_TILE > px[2] ? ty * ORC_TILE : px[2]) + 0.5 - v;
+  const double Y1 = (double)(ty * ORC_TILE + ORC_TILE - 1 < px[3] ? ty * ORC_TILE + ORC_TILE - 1 : px[3]) + 0.5 - v;
+  double x, y;
+  const double qmin = orc_box_min_q(A, B, C, X0, X1, Y0, Y1, &x, &y);
+  if (margin_flag) {
+    const double terms = fabs(A) * x * x + 2 * fabs(B * x * y) + fabs(C) * y * y;
+    const double grad = 2 * fabs(A * x + B * y) * (fabs(u) + 1) + 2 * fabs(B * x + C * y) * (fabs(v) + 1);
+    const double bound = 8 * ORC_EPS32 * (terms + grad + tau) + 1e-12 * tau;
+    if (fabs(qmin - tau) <= bound) *margin_flag = 1;
+  }
+  return qmin <= tau;
 }
 
 /*
@@ -305,8 +365,15 @@ static void project_one(const orc_camera* cam, const double mu[3], const double 
   g->py0 = (int64_t)ly; g->py1 = (int64_t)hy;
   g->tx0 = g->px0 / ORC_TILE; g->tx1 = g->px1 / ORC_TILE;
   g->ty0 = g->py0 / ORC_TILE; g->ty1 = g->py1 / ORC_TILE;
-  g->n_tiles = (g->tx1 - g->tx0 + 1) * (g->ty1 - g->ty0 + 1);
-  g->visible = 1;
+  /* the tiles of the rectangle that pass the ellipse test ([SPIRULA], 16-bit AABB section) */
+  const int64_t px[4] = {g->px0, g->px1, g->py0, g->py1};
+  int near = 0;
+  g->n_tiles = 0;
+  for (int64_t ty = g->ty0; ty <= g->ty1; ++ty)
+    for (int64_t tx = g->tx0; tx <= g->tx1; ++tx)
+      g->n_tiles += orc_tile_keeps(g->u, g->v, g->A, g->B, g->C, g->tau, px, tx, ty, &near);
+  if (near) g->flags |= 8;
+  g->visible = g->n_tiles > 0;
 }
 
 /*
@@ -357,22 +424,56 @@ int64_t orc_count_pairs(int64_t n, const int64_t* n_tiles) {
 }
 
 /*
- * Emit one (key, id) pair per covered tile, Gaussians in id order, rows (ty) outer and
+ * Emit one (key, id) pair per kept tile, Gaussians in id order, rows (ty) outer and
  * columns (tx) inner.  key = tile_id * 2^32 + float32 depth bits, tile_id = ty*tiles_x+tx.
+ * A tile of the rectangle is kept when it passes the ellipse test for the Gaussian's
+ * ell[i] = (u, v, A, B, C, tau) and pixel box pxrect[i] (every tile when ell is NULL, for
+ * hand-built lists); Gaussians with n_tiles = 0 are skipped.  Writes at most capacity pairs; returns the number of kept tiles.
  */
-void orc_emit_pairs(int64_t n, const int32_t* trect, const int64_t* n_tiles,
-                    const uint32_t* depth_bits, int64_t tiles_x, uint64_t* keys,
-                    uint32_t* vals) {
+int64_t orc_emit_pairs(int64_t n, const int32_t* trect, const int32_t* pxrect, const double* ell,
+                       const int64_t* n_tiles, const uint32_t* depth_bits, int64_t tiles_x, uint64_t* keys,
+                       uint32_t* vals, int64_t capacity) {
   int64_t p = 0;
   for (int64_t i = 0; i < n; ++i) {
     if (n_tiles[i] <= 0) continue;
+    const double* e = ell ? ell + 6 * i : NULL;
+    const int64_t px[4] = {pxrect ? pxrect[4 * i] : 0, pxrect ? pxrect[4 * i + 1] : 0,
+                           pxrect ? pxrect[4 * i + 2] : 0, pxrect ? pxrect[4 * i + 3] : 0};
     for (int64_t ty = trect[4 * i + 2]; ty <= trect[4 * i + 3]; ++ty)
       for (int64_t tx = trect[4 * i]; tx <= trect[4 * i + 1]; ++tx) {
-        uint64_t tile = (uint64_t)(ty * tiles_x + tx);
-        keys[p] = (tile << 32) | (uint64_t)depth_bits[i];
-        vals[p] = (uint32_t)i;
+        if (e && !orc_tile_keeps(e[0], e[1], e[2], e[3], e[4], e[5], px, tx, ty, NULL)) continue;
+        if (p < capacity) {
+          uint64_t tile = (uint64_t)(ty * tiles_x + tx);
+          keys[p] = (tile << 32) | (uint64_t)depth_bits[i];
+          vals[p] = (uint32_t)i;
+        }
         ++p;
       }
+  }
+  return p;
+}
+
+/* ell[i] = (u, v, A, B, C, tau) from 2D means, conics and opacities, with the support level
+ * tau = 2 ln(o / AMIN) of project_one. */
+void orc_ellipses(int64_t n, const double* uv, const double* conic, const double* opac, double* ell) {
+  for (int64_t i = 0; i < n; ++i) {
+    ell[6 * i] = uv[2 * i]; ell[6 * i + 1] = uv[2 * i + 1];
+    for (int k = 0; k < 3; ++k) ell[6 * i + 2 + k] = conic[3 * i + k];
+    ell[6 * i + 5] = opac[i] >= ORC_AMIN ? 2.0 * log(opac[i] / ORC_AMIN) : 0.0;
+  }
+}
+
+/* Tiles kept by the ellipse test, per Gaussian (as orc_emit_pairs counts them). */
+void orc_count_kept(int64_t n, const int32_t* trect, const int32_t* pxrect, const double* ell, int64_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const double* e = ell + 6 * i;
+    const int64_t px[4] = {pxrect[4 * i], pxrect[4 * i + 1], pxrect[4 * i + 2], pxrect[4 * i + 3]};
+    int64_t c = 0;
+    for (int64_t ty = trect[4 * i + 2]; ty <= trect[4 * i + 3]; ++ty)
+      for (int64_t tx = trect[4 * i]; tx <= trect[4 * i + 1]; ++tx)
+        c += orc_tile_keeps(e[0], e[1], e[2], e[3], e[4], e[5], px, tx, ty, NULL);
+    out[i] = c;
   }
 }
 
@@ -790,15 +891,18 @@ uint64_t orc_forward(int64_t n, const double* means, const double* scales, const
   double* rgb = (double*)malloc(sizeof(double) * 3 * n);
   uint32_t* db = (uint32_t*)malloc(sizeof(uint32_t) * n);
   int32_t* trect = (int32_t*)malloc(sizeof(int32_t) * 4 * n);
+  int32_t* pxrect = (int32_t*)malloc(sizeof(int32_t) * 4 * n);
   int64_t* nt = (int64_t*)malloc(sizeof(int64_t) * n);
   double* rec = (double*)malloc(sizeof(double) * ORC_REC * n);
+  double* ell = (double*)malloc(sizeof(double) * 6 * n);
   orc_project(n, means, scales, quats, opac, sh, L, cam, uv, NULL, db, NULL, conic, rgb, NULL,
-              NULL, trect, nt, NULL);
+              pxrect, trect, nt, NULL);
   orc_make_records(n, uv, conic, opac, rgb, rec);
+  orc_ellipses(n, uv, conic, opac, ell);
   const int64_t P = orc_count_pairs(n, nt);
   uint64_t* keys = (uint64_t*)malloc(sizeof(uint64_t) * (P > 0 ? P : 1));
   uint32_t* vals = (uint32_t*)malloc(sizeof(uint32_t) * (P > 0 ? P : 1));
-  orc_emit_pairs(n, trect, nt, db, tiles_x, keys, vals);
+  orc_emit_pairs(n, trect, pxrect, ell, nt, db, tiles_x, keys, vals, P);
   orc_sort_pairs(P, keys, vals);
   int64_t* ranges = (int64_t*)malloc(sizeof(int64_t) * 2 * tiles_x * tiles_y);
   orc_tile_ranges(P, keys, tiles_x * tiles_y, ranges);
@@ -827,7 +931,7 @@ uint64_t orc_forward(int64_t n, const double* means, const double* scales, const
     }
   }
 #undef ORC_MIX
-  free(uv); free(conic); free(rgb); free(db); free(trect); free(nt); free(rec);
+  free(uv); free(conic); free(rgb); free(db); free(trect); free(pxrect); free(nt); free(rec); free(ell);
   free(keys); free(vals); free(ranges); free(col);
   return h;
 }

@@ -14,7 +14,7 @@ def _setup(orc, name="tiny_1k_sh0_64", n=None):
     sc, cams, _ = scenes.workload(name, n)
     cam = cams[0]
     proj = orc.project(sc, cam)
-    keys, vals = orc.emit_pairs(proj["trect"], proj["n_tiles"], proj["depth_bits"], cam.tiles_x)
+    keys, vals = orc.emit_projected(proj, cam.tiles_x)
     return sc, cam, proj, keys, vals
 
 
@@ -24,14 +24,17 @@ def test_pair_count_and_emission_order(orc):
     # ids non-decreasing in emission order, each id emitted n_tiles times
     assert np.all(np.diff(vals.astype(np.int64)) >= 0)
     assert np.array_equal(np.bincount(vals, minlength=sc.n), proj["n_tiles"])
-    # each Gaussian's tiles are exactly its rect, rows outer and columns inner
+    # each Gaussian's tiles are the tiles of its rect that pass the ellipse test, rows
+    # outer and columns inner
+    ell = orc.ellipses(proj["uv"], proj["conic"], proj["opacity"])
     start = 0
     for g in range(sc.n):
         nt = proj["n_tiles"][g]
         if nt == 0:
             continue
         tx0, tx1, ty0, ty1 = proj["trect"][g]
-        expect = [ty * cam.tiles_x + tx for ty in range(ty0, ty1 + 1) for tx in range(tx0, tx1 + 1)]
+        expect = [ty * cam.tiles_x + tx for ty in range(ty0, ty1 + 1) for tx in range(tx0, tx1 + 1)
+                  if orc.tile_keeps(ell[g], proj["pxrect"][g], tx, ty)[0][0]]
         got = (keys[start:start + nt] >> np.uint64(32)).astype(np.int64)
         assert list(got) == expect
         assert np.all((keys[start:start + nt] & np.uint64(0xFFFFFFFF)) == proj["depth_bits"][g])
@@ -68,12 +71,15 @@ def test_ranges_partition_the_sorted_list(orc):
             assert (a, b) == (0, 0)
         else:
             assert a == sel[0] and b == sel[-1] + 1 and b - a == sel.size
-    # a tile's list = every Gaussian whose rect covers it, sorted by (depth bits, id)
+    # a tile's list = every Gaussian whose rect covers it and whose ellipse meets it,
+    # sorted by (depth bits, id)
+    ell = orc.ellipses(proj["uv"], proj["conic"], proj["opacity"])
     for t in range(cam.num_tiles):
         tx, ty = t % cam.tiles_x, t // cam.tiles_x
         r = proj["trect"]
-        cover = np.nonzero((proj["n_tiles"] > 0) & (r[:, 0] <= tx) & (r[:, 1] >= tx)
-                           & (r[:, 2] <= ty) & (r[:, 3] >= ty))[0]
+        inrect = np.nonzero((proj["n_tiles"] > 0) & (r[:, 0] <= tx) & (r[:, 1] >= tx)
+                            & (r[:, 2] <= ty) & (r[:, 3] >= ty))[0]
+        cover = inrect[orc.tile_keeps(ell[inrect], proj["pxrect"][inrect], tx, ty)[0]]
         expect = cover[np.lexsort((cover, proj["depth_bits"][cover]))]
         a, b = rg[t]
         assert np.array_equal(sv[a:b], expect)

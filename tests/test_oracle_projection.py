@@ -154,7 +154,10 @@ def test_rect_contains_every_supported_pixel_and_is_the_ellipse_aabb(orc):
                 assert qq.min() <= tau * (1 + 1e-6)
         tx0, tx1, ty0, ty1 = p["trect"][0]
         assert (tx0, tx1, ty0, ty1) == (x0 // 16, x1 // 16, y0 // 16, y1 // 16)
-        assert p["n_tiles"][0] == (tx1 - tx0 + 1) * (ty1 - ty0 + 1)
+        # the ellipse test keeps at least every tile holding a supported pixel, and at most
+        # the rect
+        need = set(zip((jj[inside] // 16).astype(int), (ii[inside] // 16).astype(int)))
+        assert len(need) <= p["n_tiles"][0] <= (tx1 - tx0 + 1) * (ty1 - ty0 + 1)
         checked += 1
     assert checked > 20
 
