@@ -75,14 +75,24 @@ typedef struct gs_camera {
  *              bit patterns); word 11 = 0.  All zero for a culled Gaussian.
  *  depth[n]:   camera-space z rounded once to fp32 (sort keys use its bit pattern).
  *  rect[n][4]: tile rectangle tx0, tx1, ty0, ty1 (inclusive); zero when culled.
- *  n_tiles[n]: (tx1 - tx0 + 1) * (ty1 - ty0 + 1), or 0 when culled.
- *  clamp[n]:   bit c set when colour channel c was negative before the clamp at 0. */
+ *  n_tiles[n]: tiles of the rectangle whose pixel-centre box (inside the pixel box) meets
+ *              the record's support ellipse q <= tau ("Training 10M Gaussians in 8 GB:
+ *              Spirula Studio's VRAM efficiency", 16-bit AABB section: an ellipse test
+ *              after the box), for rectangles of at most 8 tile rows and 255 tile columns;
+ *              a larger rectangle keeps all its tiles.  0 when culled or no tile passes.
+ *  clamp[n]:   bit c set when colour channel c was negative before the clamp at 0.
+ *  runs[n][8]: the tile record gs_bin_tiles expands, 32 bytes per Gaussian: words 0-3
+ *              the kept tiles of each tile row of a tested rectangle, two bytes per row
+ *              (first kept column - tx0, kept count), rows in order from ty0, all bytes
+ *              0xFF for a rectangle the test does not apply to; word 4 = tx0 | tx1 << 16;
+ *              word 5 = ty0 | ty1 << 16; word 6 = n_tiles; word 7 = 0. */
 typedef struct gs_projected {
   float* rec;
   float* depth;
   uint16_t* rect;
   uint32_t* n_tiles;
   uint8_t* clamp;
+  uint32_t* runs;
 } gs_projected;
 
 /* Gradients written by gs_render_bwd (all overwritten, N rows each).

@@ -150,16 +150,21 @@ def tile_keeps(ell, pxrect, tx: int, ty: int):
     n = ell.shape[0]
     keep = np.zeros(n, np.int32)
     near = np.zeros(n, np.int32)
-    for i in range(n):
-        f = C.c_int(0)
-        keep[i] = lib.orc_tile_keeps(*(C.c_double(x) for x in ell[i]), _p(pxrect[i]), C.c_int64(tx),
-                                     C.c_int64(ty), C.byref(f))
-        near[i] = f.value
+    lib.orc_tile_keeps_batch(C.c_int64(n), _p(ell), _p(pxrect), C.c_int64(tx), C.c_int64(ty), _p(keep), _p(near))
     return keep.astype(bool), near.astype(bool)
 
 
+def rect_tested(trect) -> np.ndarray:
+    """Whether the ellipse test applies to each tile rectangle (larger ones keep every tile)."""
+    lib = _load()
+    trect = np.ascontiguousarray(np.asarray(trect).reshape(-1, 4), dtype=np.int32)
+    out = np.zeros(trect.shape[0], np.int32)
+    lib.orc_rect_tested_batch(C.c_int64(trect.shape[0]), _p(trect), _p(out))
+    return out.astype(bool)
+
+
 def count_kept(trect, pxrect, ell):
-    """Tiles of each rectangle kept by the ellipse test."""
+    """Tiles of each rectangle kept (by the ellipse test where it applies)."""
     lib = _load()
     trect = np.ascontiguousarray(trect, dtype=np.int32)
     pxrect = np.ascontiguousarray(pxrect, dtype=np.int32)

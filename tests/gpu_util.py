@@ -89,7 +89,9 @@ def check_projection(scene, cam, g, label=""):
     flags = p["flags"]
     vis_o = p["n_tiles"] > 0
     vis_g = g["n_tiles"] > 0
-    edge = (flags & 2) != 0
+    # decisions the oracle flags as within float64 / float32 rounding of their thresholds:
+    # the rect edges (bit 1) and the tile tests (bit 3) may go either way
+    edge = (flags & (2 | 8)) != 0
     bad_vis = np.nonzero((vis_o != vis_g) & ~edge)[0]
     assert bad_vis.size == 0, f"{label}: visibility differs for ids {bad_vis[:10]}"
     both = vis_o & vis_g & ~edge
@@ -116,9 +118,27 @@ def check_projection(scene, cam, g, label=""):
     return dict(visible=int(vis_g.sum()), edge=int(edge.sum()), ties=int(tie.sum()))
 
 
+def gpu_ellipses(g):
+    """The oracle's tile-test ellipses (u, v, A, B, C, tau) of the GPU's records, exact in f64."""
+    r = g["rec"].astype(np.float64)
+    return oracle.ellipses(r[:, 0:2], r[:, 2:5], r[:, 5])
+
+
+def gpu_pxrect(g):
+    bx, by = g["bbox"][:, 0], g["bbox"][:, 1]
+    return np.stack([bx & 0xFFFF, bx >> 16, by & 0xFFFF, by >> 16], 1).astype(np.int32)
+
+
 def check_binning(cam, g, label=""):
+    """The oracle's emission from the GPU's records (rects, pixel boxes, ellipses, depths):
+    its tile counts must be the GPU's, and its sorted pairs and ranges the GPU's, bit for bit."""
     trect = np.ascontiguousarray(g["rect"].astype(np.int32))
-    k, v = oracle.emit_pairs(trect, g["n_tiles"].astype(np.int64), g["depth_bits"], cam.tiles_x)
+    ell, pxr = gpu_ellipses(g), gpu_pxrect(g)
+    vis = g["n_tiles"] > 0
+    kept = oracle.count_kept(trect[vis], pxr[vis], ell[vis])
+    bad = np.nonzero(kept != g["n_tiles"][vis])[0]
+    assert bad.size == 0, f"{label}: tile counts differ for {bad.size} Gaussians, e.g. {np.nonzero(vis)[0][bad[:5]]}"
+    k, v = oracle.emit_pairs(trect, g["n_tiles"].astype(np.int64), g["depth_bits"], cam.tiles_x, pxr, ell)
     assert k.shape[0] == g["P"], f"{label}: pair count {g['P']} vs {k.shape[0]}"
     if "keys_unsorted" in g:
         # gs_bin_tiles emits in (tile & 255, depth bits, id) order: the oracle's id-order

@@ -6,7 +6,8 @@ At this size the oracle checks every Gaussian's projection, and the rest on prop
 hold at any size plus exact samples: the sorted keys are non-decreasing with equal keys in
 id order, the tile ranges bound each tile's run, the pair count is the sum of the tile
 counts, every list of 24 sampled tiles equals the depth-ordered set of Gaussians whose
-(oracle-checked) rectangles cover the tile, and every pixel of those tiles matches the
+(oracle-checked) rectangles cover the tile and whose records pass the oracle's ellipse
+test for it, and every pixel of those tiles matches the
 oracle's compositing of the GPU's own lists.  The test prints the pair count and the peak
 device memory.
 """
@@ -18,7 +19,8 @@ from tile_differentiable_rasterizer_amd import scenes
 
 pytestmark = pytest.mark.gpu
 
-from gpu_util import check_projection, check_render_chained, gpu_stages, say
+import oracle
+from gpu_util import check_projection, check_render_chained, gpu_ellipses, gpu_pxrect, gpu_stages, say
 
 
 @pytest.fixture(scope="module")
@@ -57,12 +59,16 @@ def test_aniso_10m_1080p_forward(big):
     rect = g["rect"]  # (x0, x1, y0, y1) in tiles
     vis = np.nonzero(g["n_tiles"] > 0)[0]
     rv, dv = rect[vis], g["depth_bits"][vis]
+    ell, pxr = gpu_ellipses(g), gpu_pxrect(g)
     pix = []
     for t in tiles:
         tx, ty = int(t % cam.tiles_x), int(t // cam.tiles_x)
         cover = (rv[:, 0] <= tx) & (rv[:, 1] >= tx) & (rv[:, 2] <= ty) & (rv[:, 3] >= ty)
         ids = vis[cover]
-        want = ids[np.lexsort((ids, dv[cover]))]
+        keep, _ = oracle.tile_keeps(ell[ids], pxr[ids], tx, ty)
+        keep |= ~oracle.rect_tested(rect[ids])  # larger rectangles keep every tile
+        ids, dsel = ids[keep], dv[cover][keep]
+        want = ids[np.lexsort((ids, dsel))]
         got = vals[rg[t, 0]:rg[t, 1]]
         assert np.array_equal(got, want.astype(np.uint32)), f"aniso10m: tile {t} list differs"
         for j in range(ty * 16, min(ty * 16 + 16, cam.height)):

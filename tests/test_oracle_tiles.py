@@ -118,3 +118,27 @@ def test_thin_diagonal_ellipse_keeps_the_tiles_its_axis_crosses(orc):
     assert {(k, k) for k in range(1, 7)} <= kept
     assert all(abs(ty - tx) <= 1 for ty, tx in kept)
     assert (1, 6) not in kept and (6, 1) not in kept
+
+
+def test_rectangles_taller_than_eight_tile_rows_keep_every_tile(orc):
+    """The ellipse test applies to rectangles of at most 8 tile rows and 255 columns; a
+    larger one keeps every tile (conservative).  A thin ellipse tilted across 10 tile rows
+    keeps its whole rectangle; the same ellipse scaled to fit 6 rows is culled."""
+    for half_len, tested in ((75.0, False), (45.0, True)):
+        u = v = 96.0
+        t = math.pi / 3
+        R = np.array([[math.cos(t), -math.sin(t)], [math.sin(t), math.cos(t)]])
+        Cov = R @ np.diag([(half_len / 3) ** 2, (0.6 / 3) ** 2]) @ R.T
+        M = np.linalg.inv(Cov)
+        ell = np.array([[u, v, M[0, 0], M[0, 1], M[1, 1], 9.0]])
+        ex, ey = math.sqrt(9.0 * Cov[0, 0]), math.sqrt(9.0 * Cov[1, 1])
+        px = np.array([[math.ceil(u - ex - 0.5), math.floor(u + ex - 0.5), math.ceil(v - ey - 0.5),
+                        math.floor(v + ey - 0.5)]], np.int32)
+        tr = (px // 16).astype(np.int32)
+        area = int((tr[0, 1] - tr[0, 0] + 1) * (tr[0, 3] - tr[0, 2] + 1))
+        assert orc.rect_tested(tr)[0] == tested
+        kept = int(orc.count_kept(tr, px, ell)[0])
+        if tested:
+            assert kept < area
+        else:
+            assert tr[0, 3] - tr[0, 2] + 1 > 8 and kept == area

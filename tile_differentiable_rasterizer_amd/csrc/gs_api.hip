@@ -61,7 +61,7 @@ DevCamera dev_camera(const gs_camera* c) {
   return d;
 }
 
-bool projected_ok(const gs_projected& p) { return p.rec && p.depth && p.rect && p.n_tiles && p.clamp; }
+bool projected_ok(const gs_projected& p) { return p.rec && p.depth && p.rect && p.n_tiles && p.clamp && p.runs; }
 
 gs_status hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP; }
 

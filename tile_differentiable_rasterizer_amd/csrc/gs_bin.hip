@@ -23,7 +23,7 @@
 //   k_compact        visible Gaussians' (depth bits, id), in id order
 //   (radix sort of the compacted depths, gs_sort.hip)
 //   k_count_sorted   per 1024 depth-sorted Gaussians: pair count; gathers their tile
-//                    rectangles into depth order
+//                    records (kept runs, rectangle, count) into depth order
 //   k_offsets        per depth-sorted Gaussian: its first pair; per partition: its first
 //                    Gaussian
 //   k_emit_count     per chunk of 8 partitions: counts of the tile's low byte, per
@@ -32,6 +32,7 @@
 //   k_emit_scatter   per partition: regenerate the pairs, rank them stably by digit in
 //                    LDS, write one contiguous run per digit
 #include "gs_device.h"
+#include "gs_tiles.h"
 
 namespace gs {
 
@@ -47,10 +48,6 @@ constexpr int kEmitPart = kBinBlock * kEmitPer;  // pairs per emission partition
 constexpr int kDigits = 256;                      // values of the tile's low byte
 constexpr int kCountParts = 8;                    // partitions per counting workgroup
 
-// Tiles in a rectangle (x0, x1, y0, y1), inclusive bounds.
-__device__ __forceinline__ uint32_t rect_tiles(ushort4 r) {
-  return ((uint32_t)r.y - (uint32_t)r.x + 1u) * ((uint32_t)r.w - (uint32_t)r.z + 1u);
-}
 
 __global__ __launch_bounds__(kBinBlock) void k_count_blocks(int64_t n, const uint32_t* __restrict__ n_tiles,
                                                             uint64_t* __restrict__ pair_sums,
@@ -144,11 +141,12 @@ __global__ __launch_bounds__(kBinBlock) void k_compact(int64_t n, const uint32_t
   }
 }
 
-// Per 1024 depth-sorted Gaussians: their pair count; also gathers each one's tile
-// rectangle into depth order (srect), the one random-access pass over the Gaussians.
+// Per 1024 depth-sorted Gaussians: their pair count; also gathers their tile records
+// (32 bytes: kept runs, rectangle, count) into depth order for the emission (the one
+// random-access pass over the Gaussians).
 __global__ __launch_bounds__(kBinBlock) void k_count_sorted(int64_t v, const uint32_t* __restrict__ order,
-                                                            const ushort4* __restrict__ rect,
-                                                            ushort4* __restrict__ srect,
+                                                            const uint4* __restrict__ runs,
+                                                            uint4* __restrict__ sruns, uint32_t* __restrict__ sn,
                                                             uint64_t* __restrict__ sums) {
   __shared__ uint64_t s_p[kBinBlock / kWave];
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
@@ -157,9 +155,12 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(int64_t v, const uin
   for (int j = 0; j < kBinPer; ++j) {
     const int64_t i = base + j * kBinBlock + threadIdx.x;
     if (i < v) {
-      const ushort4 r = rect[order[i]];
-      srect[i] = r;
-      acc += rect_tiles(r);
+      const uint32_t id = order[i];
+      const uint4 a = runs[2 * (size_t)id], b = runs[2 * (size_t)id + 1];
+      sruns[2 * i] = a;
+      sruns[2 * i + 1] = b;
+      sn[i] = b.z;
+      acc += b.z;
     }
   }
   acc = wave_sum(acc);
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(int64_t v, const uin
 // partition: goff[i] = pairs of the depth-sorted Gaussians before i (i in [0, v]);
 // gstart[b] = the Gaussian holding pair b * kEmitPart.  Every visible Gaussian has at
 // least one pair, so each partition start falls inside exactly one Gaussian's range.
-__global__ __launch_bounds__(kBinBlock) void k_offsets(int64_t v, const ushort4* __restrict__ srect,
+__global__ __launch_bounds__(kBinBlock) void k_offsets(int64_t v, const uint32_t* __restrict__ sn,
                                                        const uint64_t* __restrict__ block_off,
                                                        uint64_t* __restrict__ goff, uint32_t* __restrict__ gstart) {
   __shared__ uint64_t s_w[kBinBlock / kWave];
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kBinBlock) void k_offsets(int64_t v, const ushort4*
 #pragma unroll
   for (int j = 0; j < kBinPer; ++j) {  // each thread owns kBinPer consecutive positions
     const int64_t i = base + (int64_t)tid * kBinPer + j;
-    cnt[j] = i < v ? rect_tiles(srect[i]) : 0u;
+    cnt[j] = i < v ? sn[i] : 0u;
     tsum += cnt[j];
   }
   const uint64_t inc = wave_inclusive_scan(tsum);
@@ -236,10 +237,13 @@ __device__ __forceinline__ EmitPart stage_partition(int64_t b, int64_t nparts, i
 
 // Generates this lane's pairs; emit(k, tile, id, dbits) receives the pair's slot in the
 // lane's run (0 .. kEmitPer - 1), its tile, its Gaussian's id and the bit pattern of that
-// Gaussian's depth.  srect, sdepth and sid are the depth-sorted Gaussians' rectangles,
-// depth bits and ids (read only when kPayload).
+// Gaussian's depth.  sruns, sdepth and sid are the depth-sorted Gaussians' tile records,
+// depth bits and ids.  A Gaussian's pairs are the tiles its
+// ellipse test keeps (every tile of a rectangle the test does not apply to), rows outer and
+// columns inner, read from the runs the projection stored.  Every loop stays inside the
+// rectangle.
 template <bool kPayload, typename F>
-__device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_rel, const ushort4* __restrict__ srect,
+__device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_rel, const uint4* __restrict__ sruns,
                                            const uint32_t* __restrict__ sdepth, const uint32_t* __restrict__ sid,
                                            int tiles_x, F&& emit) {
   const int p0 = (int)threadIdx.x * kEmitPer;
@@ -249,32 +253,59 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
     const int mid = (lo + hi) >> 1;
     if (s_rel[mid] <= p0) lo = mid; else hi = mid;
   }
-  uint32_t g = e.g0 + (uint32_t)lo;
-  ushort4 r = srect[g];
-  uint32_t dbits = kPayload ? sdepth[g] : 0u, id = kPayload ? sid[g] : 0u;
-  uint32_t w = (uint32_t)r.y - (uint32_t)r.x + 1u;
-  const uint32_t local = (uint32_t)(p0 - s_rel[lo]);
-  uint32_t row = local / w, col = local - row * w;
+  ushort4 r;  // tile rectangle x0, x1, y0, y1
+  uint4 sp;   // packed kept runs
+  int ty = 0, c0 = 0, c1 = -1;  // current row and its kept columns [c0, c1]
+  uint32_t dbits = 0, id = 0;
+  auto row = [&]() {
+    if (spans_packed(sp)) {
+      packed_row(sp, ty - (int)r.z, (int)r.x, c0, c1);
+    } else {  // a rectangle the test does not apply to keeps every tile
+      c0 = (int)r.x;
+      c1 = (int)r.y;
+    }
+  };
+  auto skip_empty = [&]() {
+    while (c1 < c0 && ty < (int)r.w) {
+      ++ty;
+      row();
+    }
+  };
+  auto start = [&](uint32_t g) {  // the Gaussian's first kept tile
+    sp = sruns[2 * (size_t)g];
+    const uint4 b = sruns[2 * (size_t)g + 1];
+    r = make_ushort4((uint16_t)(b.x & 0xFFFFu), (uint16_t)(b.x >> 16), (uint16_t)(b.y & 0xFFFFu), (uint16_t)(b.y >> 16));
+    if (kPayload) {
+      id = sid[g];
+      dbits = sdepth[g];
+    }
+    ty = (int)r.z;
+    row();
+    skip_empty();
+  };
+  start(e.g0 + (uint32_t)lo);
+  int local = p0 - s_rel[lo];  // pairs of this Gaussian before the lane's first
+  while (local > c1 - c0 && ty < (int)r.w) {
+    local -= c1 >= c0 ? c1 - c0 + 1 : 0;
+    ++ty;
+    row();
+  }
+  int col = min(c0 + local, c1);
   int next = s_rel[lo + 1];
   const int run = min(kEmitPer, e.n - p0);
   for (int k = 0; k < run; ++k) {
     while (p0 + k >= next) {  // on to the next Gaussian
       ++lo;
-      ++g;
-      r = srect[g];
-      if (kPayload) {
-        dbits = sdepth[g];
-        id = sid[g];
-      }
-      w = (uint32_t)r.y - (uint32_t)r.x + 1u;
-      row = 0;
-      col = 0;
+      start(e.g0 + (uint32_t)lo);
+      col = c0;
       next = s_rel[lo + 1];
     }
-    emit(k, ((uint32_t)r.z + row) * (uint32_t)tiles_x + ((uint32_t)r.x + col), id, dbits);
-    if (++col == w) {
-      col = 0;
-      ++row;
+    emit(k, (uint32_t)ty * (uint32_t)tiles_x + (uint32_t)col, id, dbits);
+    if (++col > c1 && ty < (int)r.w) {
+      ++ty;
+      row();
+      skip_empty();
+      col = c0;
     }
   }
 }
@@ -284,7 +315,7 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
 // the counts of the chunk's earlier partitions (cnt_pre[b][d]) and, per chunk, its totals
 // (csum[c][d]); both are contiguous rows.
 __global__ __launch_bounds__(kBinBlock) void k_emit_count(int64_t v, int64_t P, int64_t nparts,
-                                                          const ushort4* __restrict__ srect,
+                                                          const uint4* __restrict__ sruns,
                                                           const uint64_t* __restrict__ goff,
                                                           const uint32_t* __restrict__ gstart, int tiles_x,
                                                           uint32_t* __restrict__ cnt_pre,
@@ -299,7 +330,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_count(int64_t v, int64_t P, 
     for (int i = tid; i < (kBinBlock / kWave) * kDigits; i += kBinBlock) (&s_h[0][0])[i] = 0;
     const EmitPart e = stage_partition(b, nparts, v, P, goff, gstart, s_rel);
     __syncthreads();
-    lane_pairs<false>(e, s_rel, srect, nullptr, nullptr, tiles_x, [&](int, uint32_t tile, uint32_t, uint32_t) {
+    lane_pairs<false>(e, s_rel, sruns, nullptr, nullptr, tiles_x, [&](int, uint32_t tile, uint32_t, uint32_t) {
       atomicAdd(&s_h[wave][tile & (kDigits - 1)], 1u);
     });
     __syncthreads();
@@ -357,7 +388,7 @@ __global__ __launch_bounds__(kBinBlock) void k_digit_scan(int64_t nchunks, uint6
 // LDS and written as one contiguous run per digit; a run starts at the digit's global
 // base plus the digit's count in earlier partitions.
 __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(int64_t v, int64_t P, int64_t nparts,
-                                                            const ushort4* __restrict__ srect,
+                                                            const uint4* __restrict__ sruns,
                                                             const uint32_t* __restrict__ sdepth,
                                                             const uint32_t* __restrict__ sid,
                                                             const uint64_t* __restrict__ goff,
@@ -390,7 +421,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(int64_t v, int64_t P
   }
   // generate: lane-consecutive, one pad slot per lane so that a wavefront's 8-byte
   // stores spread over the LDS banks
-  lane_pairs<true>(e, s_rel, srect, sdepth, sid, tiles_x, [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
+  lane_pairs<true>(e, s_rel, sruns, sdepth, sid, tiles_x, [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
     const int slot = tid * (kEmitPer + 1) + k;
     s_keys[slot] = ((uint64_t)tile << 32) | (uint64_t)dbits;
     s_vals[slot] = id;
@@ -464,7 +495,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(int64_t v, int64_t P
 // Workspace layout (bytes).  The arrays sized by the pair count come last, so the count
 // phase (which runs before P is known) and the emission phase agree on every offset.
 struct BinLayout {
-  size_t pair_sums, vis_sums, sorted_sums, totals, dk0, dv0, dk1, dv1, sort, goff, srect, dtotals, gstart, cnt_pre,
+  size_t pair_sums, vis_sums, sorted_sums, totals, dk0, dv0, dk1, dv1, sort, goff, sruns, sn, dtotals, gstart, cnt_pre,
       csum, total;
   int64_t nb, nparts, nchunks;
 };
@@ -488,8 +519,9 @@ static BinLayout bin_layout(int64_t n, int64_t P) {
   l.dv1 = l.dk1 + ids;
   l.sort = l.dv1 + ids;
   l.goff = l.sort + align256(radix_workspace_bytes(n, 0, 32));
-  l.srect = l.goff + align256(sizeof(uint64_t) * (size_t)(n + 1));
-  l.dtotals = l.srect + align256(sizeof(uint64_t) * (size_t)(n > 0 ? n : 1));
+  l.sruns = l.goff + align256(sizeof(uint64_t) * (size_t)(n + 1));
+  l.sn = l.sruns + align256(2 * sizeof(uint4) * (size_t)(n > 0 ? n : 1));
+  l.dtotals = l.sn + align256(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
   l.gstart = l.dtotals + sizeof(uint64_t) * kDigits;
   l.cnt_pre = l.gstart + align256(sizeof(uint32_t) * (size_t)(l.nparts + 1));
   l.csum = l.cnt_pre + align256(sizeof(uint32_t) * kDigits * (size_t)l.nparts);
@@ -532,8 +564,8 @@ hipError_t launch_bin_emit(int64_t n, int64_t v, int64_t P, const gs_projected& 
   uint64_t* goff = reinterpret_cast<uint64_t*>(w + l.goff);
   uint64_t* dtotals = reinterpret_cast<uint64_t*>(w + l.dtotals);
   uint32_t* gstart = reinterpret_cast<uint32_t*>(w + l.gstart);
-  ushort4* srect = reinterpret_cast<ushort4*>(w + l.srect);
-  const ushort4* rect = reinterpret_cast<const ushort4*>(proj.rect);
+  uint4* sruns = reinterpret_cast<uint4*>(w + l.sruns);
+  uint32_t* sn = reinterpret_cast<uint32_t*>(w + l.sn);
   uint32_t* cnt_pre = reinterpret_cast<uint32_t*>(w + l.cnt_pre);
   uint64_t* csum = reinterpret_cast<uint64_t*>(w + l.csum);
   k_compact<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, proj.n_tiles, proj.depth,
@@ -541,12 +573,12 @@ hipError_t launch_bin_emit(int64_t n, int64_t v, int64_t P, const gs_projected& 
   hipError_t e = radix_sort_u32(v, dk0, dv0, dk1, dv1, 0, 32, w + l.sort, s);
   if (e != hipSuccess) return e;
   const int64_t nbv = (v + kBinChunk - 1) / kBinChunk;
-  k_count_sorted<<<(unsigned)nbv, kBinBlock, 0, s>>>(v, dv0, rect, srect, ss);
+  k_count_sorted<<<(unsigned)nbv, kBinBlock, 0, s>>>(v, dv0, reinterpret_cast<const uint4*>(proj.runs), sruns, sn, ss);
   k_scan_blocks<<<1, 1024, 0, s>>>(nbv, ss, totals + 2);
-  k_offsets<<<(unsigned)nbv, kBinBlock, 0, s>>>(v, srect, ss, goff, gstart);
-  k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(v, P, l.nparts, srect, goff, gstart, tiles_x, cnt_pre, csum);
+  k_offsets<<<(unsigned)nbv, kBinBlock, 0, s>>>(v, sn, ss, goff, gstart);
+  k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(v, P, l.nparts, sruns, goff, gstart, tiles_x, cnt_pre, csum);
   k_digit_scan<<<kDigits, kBinBlock, 0, s>>>(l.nchunks, csum, dtotals);
-  k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(v, P, l.nparts, srect, dk0, dv0, goff, gstart, tiles_x,
+  k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(v, P, l.nparts, sruns, dk0, dv0, goff, gstart, tiles_x,
                                                           cnt_pre, csum, dtotals, keys, vals);
   return hipGetLastError();
 }

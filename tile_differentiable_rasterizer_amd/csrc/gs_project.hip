@@ -15,6 +15,7 @@
 // support, pixel box) is evaluated in float64 and rounded once; colour is float32.
 #include "gs_device.h"
 #include "gs_sh.h"
+#include "gs_tiles.h"
 
 namespace gs {
 
@@ -171,7 +172,8 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
     int64_t n, const float* __restrict__ means, const float* __restrict__ scales,
     const float4* __restrict__ quats, const float* __restrict__ opac, const float* __restrict__ sh,
     const DevCamera cam, float4* __restrict__ rec, float* __restrict__ depth_out,
-    ushort4* __restrict__ rect_out, uint32_t* __restrict__ ntiles_out, uint8_t* __restrict__ clamp_out) {
+    ushort4* __restrict__ rect_out, uint32_t* __restrict__ ntiles_out, uint8_t* __restrict__ clamp_out,
+    uint4* __restrict__ runs_out) {
   using S = ShLayout<L>;
   __shared__ float s_sh[kProjBlock * S::STRIDE];
   const int64_t base = (int64_t)blockIdx.x * kProjBlock;
@@ -209,6 +211,7 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
 
   float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0, r2 = r0;
   ushort4 rc = make_ushort4(0, 0, 0, 0);
+  uint4 sp = make_uint4(0u, 0u, 0u, 0u);
   uint32_t nt = 0;
   if (g.t[2] > cam.near_z) {  // NaN fails
     double t0[3], t1[3], St0[3], St1[3];
@@ -240,7 +243,27 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
         r1 = make_float4((float)(a * idet), (float)o, col[0], col[1]);
         r2 = make_float4(col[2], __uint_as_float(px0 | (px1 << 16)), __uint_as_float(py0 | (py1 << 16)), 0.0f);
         rc = make_ushort4((uint16_t)(px0 >> 4), (uint16_t)(px1 >> 4), (uint16_t)(py0 >> 4), (uint16_t)(py1 >> 4));
-        nt = ((px1 >> 4) - (px0 >> 4) + 1) * ((py1 >> 4) - (py0 >> 4) + 1);
+        // tiles of the rectangle that pass the ellipse test of the record as stored, and
+        // their runs packed for the emission
+        const TileEllipse te = tile_ellipse(r0.x, r0.y, r0.z, r0.w, r1.x, tau, __float_as_uint(r2.y),
+                                            __float_as_uint(r2.z));
+        const int tx0 = (int)(px0 >> 4), tx1 = (int)(px1 >> 4), ty0 = (int)(py0 >> 4), ty1 = (int)(py1 >> 4);
+        if (rect_tested(tx0, tx1, ty0, ty1)) {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+          for (int ty = ty0; ty <= ty1; ++ty) {
+            int lo, hi;
+            tile_row_span(te, ty, tx0, tx1, lo, hi);
+            const uint32_t cnt = hi >= lo ? (uint32_t)(hi - lo + 1) : 0u;
+            nt += cnt;
+            const int k = ty - ty0;
+            const uint32_t half = (cnt ? (uint32_t)(lo - tx0) : 0u) | (cnt << 8);
+            w[k >> 1] |= half << (16 * (k & 1));
+          }
+          sp = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+          nt = (uint32_t)(tx1 - tx0 + 1) * (uint32_t)(ty1 - ty0 + 1);
+          sp = make_uint4(kNoSpans, kNoSpans, kNoSpans, kNoSpans);
+        }
       }
     }
   }
@@ -249,6 +272,9 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
   rec[3 * i + 2] = r2;
   rect_out[i] = rc;
   ntiles_out[i] = nt;
+  runs_out[2 * i] = sp;
+  runs_out[2 * i + 1] = make_uint4((uint32_t)rc.x | ((uint32_t)rc.y << 16), (uint32_t)rc.z | ((uint32_t)rc.w << 16),
+                                   nt, 0u);
 }
 
 // Backward of the projection for one Gaussian (float64 geometry), plus the densification
@@ -420,7 +446,7 @@ static hipError_t launch_project_L(int64_t n, const float* means, const float* s
   k_project<L><<<blocks, kProjBlock, 0, s>>>(
       n, means, scales, reinterpret_cast<const float4*>(quats), opac, sh, cam,
       reinterpret_cast<float4*>(out.rec), out.depth, reinterpret_cast<ushort4*>(out.rect), out.n_tiles,
-      out.clamp);
+      out.clamp, reinterpret_cast<uint4*>(out.runs));
   return hipGetLastError();
 }
 

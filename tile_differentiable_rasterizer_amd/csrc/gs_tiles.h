@@ -1,0 +1,95 @@
+// gs_tiles.h -- which tiles of a Gaussian's rectangle stay in its list.
+// Internal to libgsraster.
+//
+// "Training 10M Gaussians in 8 GB: Spirula Studio's VRAM efficiency" (mhpq.cn), 16-bit
+// AABB section: after the conservative screen box, an ellipse test culls a second time
+// and the image is unchanged.  A tile stays when the box spanned by its pixel centres
+// (inside the Gaussian's pixel box) meets the support ellipse q <= tau of the record as
+// stored (float32 2D mean, conic and opacity), evaluated here in float64.
+//
+// Per tile row the kept tiles are one run of columns: the part of the ellipse inside the
+// row's band of pixel-centre ys is convex, so its x-extent is an interval [xl, xr], and a
+// tile stays iff its x-range meets it.  The rightmost x of the ellipse at height y,
+// x_r(y) = (-B y + sqrt(tau A - det y^2)) / A (det = AC - B^2), is concave in y with its
+// peak at the ellipse's rightmost point y_r = -B e_x / C, so xr = x_r(y_r clamped to the
+// band); xl is symmetric.  A band beyond the ellipse's vertical extent keeps nothing.
+//
+// The projection computes the runs once per Gaussian and stores them in the tile record
+// that the emission expands.  Float contraction is off so that the float64 evaluation
+// rounds as written.
+#pragma once
+
+#include "gs_device.h"
+
+namespace gs {
+
+struct TileEllipse {
+  double u, v, B, det, tauA, iA, yr;  // det = AC - B^2, tauA = tau A, iA = 1 / A
+  int px0, px1, py0, py1;             // pixel box
+  bool whole;                         // degenerate float32 conic: keep the whole rectangle
+};
+
+// tau = 2 ln(opacity / (1/255)), the support level of the record's opacity.
+__device__ __forceinline__ TileEllipse tile_ellipse(float u, float v, float A, float B, float C, double tau,
+                                                    uint32_t bx, uint32_t by) {
+#pragma clang fp contract(off)
+  TileEllipse e;
+  const double a = A, b = B, c = C;
+  e.u = u; e.v = v; e.B = b;
+  e.px0 = (int)(bx & 0xFFFFu); e.px1 = (int)(bx >> 16);
+  e.py0 = (int)(by & 0xFFFFu); e.py1 = (int)(by >> 16);
+  e.det = a * c - b * b;
+  e.whole = !(e.det > 0.0 && a > 0.0 && c > 0.0);
+  e.tauA = tau * a;
+  e.iA = 1.0 / a;
+  e.yr = e.whole ? 0.0 : -b * sqrt(tau * c / e.det) / c;
+  return e;
+}
+
+// Kept columns [lo, hi] of tile row ty inside [tx0, tx1] (hi < lo: none).  The half-width
+// of the ellipse at height y is sqrt(tau A - det y^2) / A around its centre line -B y / A.
+__device__ __forceinline__ void tile_row_span(const TileEllipse& e, int ty, int tx0, int tx1, int& lo, int& hi) {
+#pragma clang fp contract(off)
+  lo = tx0;
+  hi = tx1;
+  if (e.whole) return;
+  const double Y0 = (double)max(kTile * ty, e.py0) + 0.5 - e.v;
+  const double Y1 = (double)min(kTile * ty + kTile - 1, e.py1) + 0.5 - e.v;
+  const double yc = fmin(fmax(e.yr, Y0), Y1);
+  const double yl = fmin(fmax(-e.yr, Y0), Y1);
+  const double Dr = e.tauA - e.det * (yc * yc);
+  const double Dl = e.tauA - e.det * (yl * yl);
+  if (!(Dr >= 0.0) || !(Dl >= 0.0)) {  // the band misses the ellipse
+    hi = tx0 - 1;
+    return;
+  }
+  const double xr = (sqrt(Dr) - e.B * yc) * e.iA;
+  const double xl = (-sqrt(Dl) - e.B * yl) * e.iA;
+  while (lo <= hi && (double)min(kTile * lo + kTile - 1, e.px1) + 0.5 - e.u < xl) ++lo;
+  while (hi >= lo && (double)max(kTile * hi, e.px0) + 0.5 - e.u > xr) --hi;
+}
+
+// The test applies to rectangles of at most kSpanRows tile rows and 255 tile columns, whose
+// kept runs the projection stores in 16 bytes, two per row (first kept column - tx0,
+// count); a larger rectangle keeps every tile (conservative; such Gaussians are more than
+// 8 tiles tall on screen) and stores kNoSpans.  The tile record (32 bytes) adds the
+// rectangle (tx0 | tx1 << 16, ty0 | ty1 << 16) and the tile count.
+constexpr int kSpanRows = 8;
+constexpr int kSpanCols = 255;
+constexpr uint32_t kNoSpans = 0xFFFFFFFFu;
+
+__device__ __forceinline__ bool rect_tested(int tx0, int tx1, int ty0, int ty1) {
+  return ty1 - ty0 + 1 <= kSpanRows && tx1 - tx0 + 1 <= kSpanCols;
+}
+
+__device__ __forceinline__ bool spans_packed(const uint4 sp) { return sp.x != kNoSpans; }
+
+// Kept columns [c0, c1] of row k (0-based from ty0) of packed spans.
+__device__ __forceinline__ void packed_row(const uint4 sp, int k, int tx0, int& c0, int& c1) {
+  const uint32_t word = k < 2 ? sp.x : k < 4 ? sp.y : k < 6 ? sp.z : sp.w;
+  const uint32_t half = (word >> (16 * (k & 1))) & 0xFFFFu;
+  c0 = tx0 + (int)(half & 0xFFu);
+  c1 = c0 + (int)(half >> 8) - 1;
+}
+
+}  // namespace gs

@@ -37,7 +37,7 @@ class GsCamera(C.Structure):
 
 class GsProjected(C.Structure):
     _fields_ = [("rec", C.c_void_p), ("depth", C.c_void_p), ("rect", C.c_void_p),
-                ("n_tiles", C.c_void_p), ("clamp", C.c_void_p)]
+                ("n_tiles", C.c_void_p), ("clamp", C.c_void_p), ("runs", C.c_void_p)]
 
 
 class GsGrads(C.Structure):
@@ -131,11 +131,13 @@ def alloc_projected(n: int, device="cuda") -> dict:
                 depth=torch.empty(n, dtype=torch.float32, device=device),
                 rect=torch.empty((n, 4), dtype=torch.int16, device=device),
                 n_tiles=torch.empty(n, dtype=torch.int32, device=device),
-                clamp=torch.empty(n, dtype=torch.uint8, device=device))
+                clamp=torch.empty(n, dtype=torch.uint8, device=device),
+                runs=torch.empty((n, 8), dtype=torch.int32, device=device))
 
 
 def projected_struct(p: dict) -> GsProjected:
-    return GsProjected(_ptr(p["rec"]), _ptr(p["depth"]), _ptr(p["rect"]), _ptr(p["n_tiles"]), _ptr(p["clamp"]))
+    return GsProjected(_ptr(p["rec"]), _ptr(p["depth"]), _ptr(p["rect"]), _ptr(p["n_tiles"]), _ptr(p["clamp"]),
+                       _ptr(p["runs"]))
 
 
 def project(means, scales, quats, opacities, sh, sh_degree: int, cam, out: dict | None = None, stream=None) -> dict:
