@@ -438,22 +438,25 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(int64_t v, int64_t P
     key[j] = p < e.n ? s_keys[slot] : ~0ull;
     val[j] = p < e.n ? s_vals[slot] : 0u;
   }
+  // stable ranking as in the onesweep passes: the lowest lane of each group of equal digits
+  // advances the wavefront's counter with a returning LDS atomic (in issue order), and a
+  // shuffle hands the group its base
+  uint32_t prev[kEmitPer];
+  int lead[kEmitPer];
 #pragma unroll
   for (int j = 0; j < kEmitPer; ++j) {
     const int p = wave * kWavePart + j * kWave + lane;
     const bool valid = p < e.n;
     const uint32_t d = (uint32_t)(key[j] >> 32) & (kDigits - 1);
     const uint64_t m = match_digit(d, 8, __ballot(valid));
-    const uint32_t below = (uint32_t)__popcll(m & lanemask_lt());
-    uint32_t prev = 0;
-    if (valid) prev = s_wh[wave][d];
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    rank[j] = prev + below;
-    if (valid && below == 0) s_wh[wave][d] = prev + (uint32_t)__popcll(m);
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    const uint64_t lower = m & lanemask_lt();
+    rank[j] = (uint32_t)__popcll(lower);
+    lead[j] = valid ? (int)__builtin_ctzll(m) : lane;
+    prev[j] = 0;
+    if (valid && lower == 0) prev[j] = atomicAdd(&s_wh[wave][d], (uint32_t)__popcll(m));
   }
+#pragma unroll
+  for (int j = 0; j < kEmitPer; ++j) rank[j] += (uint32_t)__shfl((int)prev[j], lead[j], kWave);
   __syncthreads();
   {  // thread d owns digit d: per-wave offsets, then the partition-local digit starts
     const int d = tid;

@@ -15,7 +15,8 @@
 //                 ping-pong buffers on the device, so no host round trip is needed
 //   k_onesweep    per pass: each workgroup takes a 4096-key partition by atomic ticket,
 //                 ranks its keys stably (wavefront ballots match equal digits; per-wave
-//                 digit counters in LDS), publishes per-digit counts and resolves its
+//                 digit counters in LDS, advanced with pipelined LDS atomics), publishes
+//                 per-digit counts and resolves its
 //                 global offsets by looking back over earlier partitions' published
 //                 counts (several earlier partitions per round trip), reorders the
 //                 partition in LDS by digit and writes each digit's run contiguously
@@ -165,6 +166,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   // start the look-back now: the predecessor's word for this thread's digit is usually
   // final by the time this partition has ranked its keys
   uint64_t early = part > 0 ? status_load(status + (part - 1) * kRadix + tid) : 0;
+  const uint64_t my_dbase = dbase[tid];  // this thread's digit's global base
 
   // wave-striped: wave w owns keys [w*1024, (w+1)*1024) of the partition, in order
   K key[kSortKPT];
@@ -176,22 +178,26 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
     key[j] = idx < P ? kin[idx] : (K)~(K)0;
     val[j] = idx < P ? vin[idx] : 0u;
   }
+  // rank stably: lanes holding equal digits are matched by ballots; the lowest of them adds
+  // the group's size to the wavefront's counter for that digit and gets the count before
+  // it.  LDS atomics of one wavefront run in issue order, so the kSortKPT rounds pipeline
+  // without waiting on each other, and a shuffle then hands each lane its group's base.
+  uint32_t prev[kSortKPT];
+  int lead[kSortKPT];
 #pragma unroll
   for (int j = 0; j < kSortKPT; ++j) {
     const int64_t idx = base + wave * (kSortKPT * kWave) + j * kWave + lane;
     const bool valid = idx < P;
     const uint32_t d = (uint32_t)(key[j] >> shift) & dmask;
     const uint64_t m = match_digit(d, bits, __ballot(valid));
-    const uint32_t below = (uint32_t)__popcll(m & lanemask_lt());
-    uint32_t prev = 0;
-    if (valid) prev = s_wh[wave][d];
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    rank[j] = prev + below;
-    if (valid && below == 0) s_wh[wave][d] = prev + (uint32_t)__popcll(m);
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    const uint64_t lower = m & lanemask_lt();
+    rank[j] = (uint32_t)__popcll(lower);
+    lead[j] = valid ? (int)__builtin_ctzll(m) : lane;
+    prev[j] = 0;
+    if (valid && lower == 0) prev[j] = atomicAdd(&s_wh[wave][d], (uint32_t)__popcll(m));
   }
+#pragma unroll
+  for (int j = 0; j < kSortKPT; ++j) rank[j] += (uint32_t)__shfl((int)prev[j], lead[j], kWave);
   __syncthreads();
 
   // thread d owns digit d: wave offsets, publish the partition's count
@@ -255,7 +261,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
     }
     status_store(my_status, kFlagPre | (excl + tot));
   }
-  s_gbase[d] = dbase[d] + excl;
+  s_gbase[d] = my_dbase + excl;
   __syncthreads();
   // write each digit's run contiguously
   const int nvalid = (int)min((int64_t)kSortPart, P - base);
