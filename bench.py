@@ -99,26 +99,34 @@ def main():
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    def frame(k, cam, with_bwd, rec):
-        e = [ev() for _ in range(6)]
-        e[0].record(stream)
+    def frame(k, cam, with_bwd, rec, staged):
+        # staged: an event between the stages for the per-stage breakdown (each costs the
+        # stream a few microseconds, so the throughput runs go without them)
+        e = [ev() for _ in range(6)] if staged else None
+
+        def mark(i):
+            if staged:
+                e[i].record(stream)
+
+        mark(0)
         raster.project(means, scales, quats, opac, sh, sc.sh_degree, cam, rz.proj)
-        e[1].record(stream)
+        mark(1)
         st, P = raster.bin_tiles(rz.proj, cam, rz.keys, rz.vals, rz.workspace)
         assert st == raster.GS_OK
-        e[2].record(stream)
-        raster.sort_keys(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, ranges[k], rz.workspace, orders[k])
-        e[3].record(stream)
-        raster.render_fwd(rz.proj, rz.vals, ranges[k], cam, (0.0, 0.0, 0.0), images[k], finalT[k], ncon[k],
-                          orders[k])
-        e[4].record(stream)
+        mark(2)
+        in_tmp = raster.sort_keys(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, ranges[k], rz.workspace,
+                                  orders[k], leave_in_tmp=True)
+        sv = rz.vals_tmp if in_tmp else rz.vals
+        mark(3)
+        raster.render_fwd(rz.proj, sv, ranges[k], cam, (0.0, 0.0, 0.0), images[k], finalT[k], ncon[k], orders[k])
+        mark(4)
         if with_bwd:
-            raster.render_bwd(means, scales, quats, opac, sh, sc.sh_degree, cam, rz.proj, rz.vals, ranges[k],
+            raster.render_bwd(means, scales, quats, opac, sh, sc.sh_degree, cam, rz.proj, sv, ranges[k],
                               (0.0, 0.0, 0.0), finalT[k], ncon[k], dLs[k], grads, accum, denom, orders[k])
-            e[5].record(stream)
+            mark(5)
         rec.append((e, with_bwd, P))
 
-    def run(steps, with_bwd):
+    def run(steps, with_bwd, staged=False):
         recs = []
         # the library brackets every launch of the compositing kernel with HIP events on its stream
         kern = "k_render_bwd" if with_bwd else "k_render_fwd"
@@ -127,13 +135,15 @@ def main():
         t0 = time.perf_counter()
         for _ in range(steps):
             for k, cam in enumerate(cams):
-                frame(k, cam, with_bwd, recs)
+                frame(k, cam, with_bwd, recs, staged)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         st, launches, kms = raster.kernel_timer_stop()
         assert st == raster.GS_OK and launches == len(recs), (st, launches)
         times = {s: [] for s in stages}
         for e, wb, _ in recs:
+            if e is None:
+                continue
             for i, s in enumerate(stages[:4]):
                 times[s].append(e[i].elapsed_time(e[i + 1]))
             if wb:
@@ -152,13 +162,16 @@ def main():
     log("warm-up")
     run(args.warmup, True)
     log(f"timed: {args.steps} steps x {len(cams)} cameras, forward + backward")
-    secs, times, pairs = run(args.steps, True)
+    secs, times_t, pairs = run(args.steps, True)
     frames = args.steps * len(cams)
     value = frames / secs
     log("timed: forward only")
     secs_f, times_f, _ = run(args.steps, False)
     fwd_fps = frames / secs_f
-    kernel_ms = {"k_render_bwd": times["k_render_bwd"][0], "k_render_fwd": times_f["k_render_fwd"][0]}
+    kernel_ms = {"k_render_bwd": times_t["k_render_bwd"][0], "k_render_fwd": times_f["k_render_fwd"][0]}
+    # per-stage breakdown: a separate pass with events between the stages
+    log("stage breakdown")
+    _, times, _ = run(max(1, args.steps // 2), True, staged=True)
 
     # algorithmic work per launch (camera-averaged) for the roofline
     P_mean = float(np.mean(pairs))
@@ -184,9 +197,9 @@ def main():
         # 16 B per visible + 4 B histogram), the depth-ordered gather (20 B per visible),
         # pairs written (12 B each)
         "bin": ("hbm", 4 * N + 16 * V + (4 * 16 + 4) * V + 20 * V + 12 * P_mean),
-        # histogram (8 B/pair), 24 B/pair per pass, ranges (8 B/pair, or 24 B/pair when an
-        # odd pass count leaves the result in scratch to move back) + 16 B/tile
-        "sort": ("hbm", (8 + 24 * passes + (24 if passes % 2 else 8)) * P_mean + 16 * tiles),
+        # histogram (8 B/pair), 24 B/pair per pass, ranges (8 B/pair: the result is read
+        # where the last pass left it) + 16 B/tile
+        "sort": ("hbm", (8 + 24 * passes + 8) * P_mean + 16 * tiles),
         "render_fwd": ("alu", OPS_PER_EVAL_FWD * evals),
         "render_bwd": ("alu", OPS_PER_EVAL_BWD * walk),
     }
@@ -233,6 +246,7 @@ def main():
         "mpixels_per_s": round(value * W * H / 1e6, 1),
         "forward_only": {"frames_per_s": round(fwd_fps, 2), "mpixels_per_s": round(fwd_fps * W * H / 1e6, 1)},
         "stages": stage_report,
+        "stages_timing": "separate forward+backward pass with an event between stages",
         "kernels": kernel_report,
         "evaluations_per_frame": int(evals),
         "contributor_walk_per_frame": int(walk),

@@ -23,7 +23,7 @@
  *    gs_workspace_bytes().  Arrays are dense, row major, naturally aligned (16 bytes for
  *    float arrays read as vectors: means/scales/quats/sh/rec).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued on it; only
- *    gs_bin_tiles synchronises it, once, to read the pair count back.
+ *    gs_bin_tiles waits on it, once, to read the pair count back.
  *  - Every call validates its arguments before touching the GPU and returns a gs_status.
  *  - Calls keep no global state and may run concurrently on different streams with
  *    different buffers.
@@ -149,8 +149,13 @@ size_t gs_workspace_bytes(int64_t n, int64_t pair_capacity, int32_t num_tiles);
  * 8-bit digit pass over the tile id.  So the keys are already stably ordered by their low
  * 40 bits, and gs_sort_keys(sorted_low_bits = 40) completes the (tile, depth, id) order
  * with passes over the tile bits above the low byte only (none when num_tiles <= 256).
- * Writes the pair count P to *n_pairs [host] (this is the call's one device->host read and
- * stream synchronisation).  With keys == NULL only P is computed.  If P > capacity,
+ * Writes the pair count P to *n_pairs [host], the call's one device->host read.  When
+ * n_pairs points to page-locked host memory (hipHostMalloc, a pinned torch tensor) the
+ * count is copied straight into it and the call waits for that copy only: the depth
+ * ordering of the Gaussians, which needs no host value, is already queued behind it and
+ * keeps the GPU busy meanwhile.  Otherwise the call synchronises the stream before the
+ * depth ordering is queued.  Results are the same either way.  With keys == NULL only P
+ * is computed.  If P > capacity,
  * returns GS_ERR_CAPACITY with *n_pairs = P and writes no pairs.  The workspace must hold
  * gs_workspace_bytes(n, P, num_tiles) bytes (checked before and after P is known).
  * Errors: INVALID_ARG, WORKSPACE, CAPACITY, OVERFLOW, HIP.
@@ -161,23 +166,26 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
 
 /*
  * gs_sort_keys -- stable LSD radix sort of (keys, vals) over key bits [sorted_low_bits,
- * 32 + ceil(log2(num_tiles))), 8 bits per pass, digits constant over all keys skipped
- * ("Better Gaussian Splatting in Julia" s3.2 sort_by_depth!; "Implementing Better
- * Gaussian Splatting in Julia" s3.3 depth order).  The input must already be stably
- * ordered by its low sorted_low_bits bits (0 = no assumption: a full sort; 40 = the
- * output of gs_bin_tiles).  Equal keys keep their input order, so depth ties stay broken
- * by Gaussian id.  The result is
- * left in keys/vals; keys_tmp/vals_tmp are scratch of the same size.  Then writes
- * tile_ranges[num_tiles][2] = [first, last + 1) of each tile in the sorted order ([0, 0)
- * for an empty tile) and, when tile_order is non-NULL, tile_order[num_tiles] = every tile
- * id once, longest lists first (a schedule for the compositing calls; it does not change
- * their results).  Keys must have tile_id < num_tiles.
+ * 32 + ceil(log2(num_tiles))), 8 bits per pass ("Better Gaussian Splatting in Julia" s3.2
+ * sort_by_depth!; "Implementing Better Gaussian Splatting in Julia" s3.3 depth order).
+ * The input must already be stably ordered by its low sorted_low_bits bits (0 = no
+ * assumption: a full sort; 40 = the output of gs_bin_tiles).  Equal keys keep their input
+ * order, so depth ties stay broken by Gaussian id.  The passes ping-pong between
+ * keys/vals and keys_tmp/vals_tmp (same sizes), so an odd pass count ends in the _tmp
+ * pair.  result_in_tmp [host]: NULL = the result is moved back to keys/vals; non-NULL =
+ * the result stays where the last pass wrote it and *result_in_tmp is set to 1 when that
+ * is keys_tmp/vals_tmp, else 0 (the other pair then holds scratch).  The pass count, and
+ * so *result_in_tmp, depends only on n_pairs > 1, num_tiles and sorted_low_bits.  Then
+ * writes tile_ranges[num_tiles][2] = [first, last + 1) of each tile in the sorted order
+ * ([0, 0) for an empty tile) and, when tile_order is non-NULL, tile_order[num_tiles] =
+ * every tile id once, longest lists first (a schedule for the compositing calls; it does
+ * not change their results).  Keys must have tile_id < num_tiles.
  * Errors: INVALID_ARG, WORKSPACE, OVERFLOW, HIP.
  */
 gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys,
                        uint32_t* vals, uint64_t* keys_tmp, uint32_t* vals_tmp,
-                       int64_t* tile_ranges, int32_t* tile_order, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       int64_t* tile_ranges, int32_t* tile_order, int32_t* result_in_tmp,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gs_render_fwd -- composite every pixel front to back over its tile's sorted list

@@ -85,6 +85,44 @@ def test_capacity_error_reports_required_count():
     assert out["n_pairs"] == P
 
 
+def test_pageable_count_word_gives_the_same_pairs():
+    """gs_bin_tiles reads the pair count into pinned memory (the binding's path: the depth
+    ordering is queued before the host waits) or into an ordinary host word (the stream is
+    synchronised first); both must emit the same pairs, and both report a short buffer."""
+    import ctypes as C
+    sc, cams, _ = scenes.workload("spheres_100k_sh3_800", 30000)
+    cam = cams[0]
+    dev = torch.device("cuda")
+    arrs = raster.scene_to_device(sc, dev)
+    proj = raster.project(*arrs, sc.sh_degree, cam)
+    st, P = raster.bin_tiles(proj, cam, None, None,
+                             torch.empty(raster.workspace_bytes(sc.n, 1, cam.num_tiles), dtype=torch.uint8,
+                                         device=dev))
+    assert st == raster.GS_OK and P > 0
+    ws = torch.empty(raster.workspace_bytes(sc.n, P, cam.num_tiles), dtype=torch.uint8, device=dev)
+    k1 = torch.empty(P, dtype=torch.int64, device=dev)
+    v1 = torch.empty(P, dtype=torch.int32, device=dev)
+    st, P1 = raster.bin_tiles(proj, cam, k1, v1, ws)
+    assert st == raster.GS_OK and P1 == P
+    k2 = torch.full_like(k1, -1)
+    v2 = torch.full_like(v1, -1)
+    word = C.c_int64(-5)
+    camc = raster.camera_struct(cam)
+    L = raster.lib()
+    assert L.gs_bin_tiles(sc.n, raster.projected_struct(proj), C.byref(camc), k2.data_ptr(), v2.data_ptr(), P,
+                          C.byref(word), ws.data_ptr(), ws.numel(), None) == raster.GS_OK
+    torch.cuda.synchronize()
+    assert word.value == P
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    word.value = 0
+    assert L.gs_bin_tiles(sc.n, raster.projected_struct(proj), C.byref(camc), k2.data_ptr(), v2.data_ptr(), P - 1,
+                          C.byref(word), ws.data_ptr(), ws.numel(), None) == raster.GS_ERR_CAPACITY
+    assert word.value == P
+    st, P3 = raster.bin_tiles(proj, cam, k2[:P - 1], v2[:P - 1], ws)
+    assert st == raster.GS_ERR_CAPACITY and P3 == P
+    torch.cuda.synchronize()
+
+
 def test_invalid_arguments_are_rejected_before_launch():
     L = raster.lib()
     cam = raster.camera_struct(_cam())
@@ -100,10 +138,13 @@ def test_invalid_arguments_are_rejected_before_launch():
     assert L.gs_bin_tiles(0, proj, C.byref(cam), None, None, 0, C.byref(P), None, 0, None) == raster.GS_ERR_WORKSPACE
 
 
+@pytest.mark.parametrize("leave_in_tmp", [False, True])
 @pytest.mark.parametrize("kind", ["equal_keys", "one_tile", "many_tiles_random", "partition_edges"])
-def test_sort_adversarial_keys(kind):
+def test_sort_adversarial_keys(kind, leave_in_tmp):
     """The radix sort alone on keys the binning never makes: all equal, one tile, random
-    over 2^13 tiles, and counts at partition boundaries; stable order checked with lexsort."""
+    over 2^13 tiles, and counts at partition boundaries; stable order checked with lexsort.
+    The result is either moved back to keys/vals or left where the last pass wrote it, which
+    the pass count alone decides (no pass is skipped, even over a constant digit)."""
     rng = np.random.default_rng(5)
     if kind == "equal_keys":
         P, tiles = 20000, 4
@@ -126,10 +167,14 @@ def test_sort_adversarial_keys(kind):
     vd = torch.from_numpy(vals.view(np.int32)).to(dev)
     ws = torch.empty(raster.workspace_bytes(1, P, tiles), dtype=torch.uint8, device=dev)
     ranges = torch.empty((tiles, 2), dtype=torch.int64, device=dev)
-    raster.sort_keys(P, tiles, kd, vd, torch.empty_like(kd), torch.empty_like(vd), ranges, ws, sorted_low_bits=0)
+    kt, vt = torch.empty_like(kd), torch.empty_like(vd)
+    in_tmp = raster.sort_keys(P, tiles, kd, vd, kt, vt, ranges, ws, sorted_low_bits=0, leave_in_tmp=leave_in_tmp)
     torch.cuda.synchronize()
+    passes = -(-(32 + max(0, int(np.ceil(np.log2(tiles))))) // 8)
+    assert in_tmp == (leave_in_tmp and passes % 2 == 1)
+    ks, vs = (kt, vt) if in_tmp else (kd, vd)
     order = np.lexsort((np.arange(P), keys))  # stable by key
-    assert np.array_equal(kd.cpu().numpy().view(np.uint64), keys[order])
-    assert np.array_equal(vd.cpu().numpy().view(np.uint32), vals[order])
+    assert np.array_equal(ks.cpu().numpy().view(np.uint64), keys[order])
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), vals[order])
     assert np.array_equal(ranges.cpu().numpy(), oracle.tile_ranges(keys[order], tiles))
     say(f"sort {kind}: ok")

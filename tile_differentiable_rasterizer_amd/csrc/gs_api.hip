@@ -19,12 +19,13 @@ hipError_t launch_project_bwd(int64_t n, const float* means, const float* scales
 size_t bin_workspace_bytes(int64_t n, int64_t n_pairs);
 hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, void* ws, hipStream_t s);
 uint64_t* bin_totals_ptr(int64_t n, void* ws);
-hipError_t launch_bin_emit(int64_t n, int64_t v, int64_t P, const gs_projected& proj, int tiles_x, void* ws, uint64_t* keys,
+hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, void* ws, hipStream_t s);
+hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int tiles_x, void* ws, uint64_t* keys,
                            uint32_t* vals, hipStream_t s);
 size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_bits);
 hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
-                       uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits, void* ws,
-                       hipStream_t s);
+                       uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits,
+                       int32_t* result_in_tmp, void* ws, hipStream_t s);
 hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
 hipError_t launch_render_fwd(const gs_projected& proj, const uint32_t* vals, const int64_t* ranges,
                              const int32_t* order, const DevCamera& cam, const float bg[3], float* image,
@@ -152,6 +153,17 @@ gs_status gs_project(int64_t n, const float* means, const float* scales, const f
   }));
 }
 
+// True when p is page-locked host memory (hipHostMalloc, or a pinned torch tensor): a
+// device-to-host copy into it completes without the host draining the whole stream.
+static bool host_pinned(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // an ordinary host pointer: not an error of this call
+    return false;
+  }
+  return a.type == hipMemoryTypeHost;
+}
+
 gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint64_t* keys, uint32_t* vals,
                        int64_t capacity, int64_t* n_pairs, void* workspace, size_t workspace_bytes,
                        void* stream) {
@@ -161,25 +173,41 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
   if (keys && !vals) return GS_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < bin_workspace_bytes(n, 0)) return GS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_bin_count(n, proj.n_tiles, workspace, s);
-  if (e != hipSuccess) return GS_ERR_HIP;
-  uint64_t totals[2] = {0, 0};  // pairs, visible Gaussians
-  if (hipMemcpyAsync(totals, bin_totals_ptr(n, workspace), sizeof totals, hipMemcpyDeviceToHost, s) != hipSuccess)
-    return GS_ERR_HIP;
-  if (hipStreamSynchronize(s) != hipSuccess) return GS_ERR_HIP;
-  if (totals[0] > (uint64_t)INT64_MAX) return GS_ERR_OVERFLOW;
-  *n_pairs = (int64_t)totals[0];
-  if (!keys) return GS_OK;
-  if ((int64_t)totals[0] > capacity) return GS_ERR_CAPACITY;
-  if (workspace_bytes < bin_workspace_bytes(n, (int64_t)totals[0])) return GS_ERR_WORKSPACE;
+  if (launch_bin_count(n, proj.n_tiles, workspace, s) != hipSuccess) return GS_ERR_HIP;
+  const uint64_t* dP = bin_totals_ptr(n, workspace);
+  int64_t P = 0;
+  if (keys && host_pinned(n_pairs)) {
+    // the count lands in the caller's pinned word; the depth phase is queued behind the
+    // copy and runs while the host waits for the copy alone
+    hipEvent_t ev;
+    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return GS_ERR_HIP;
+    hipError_t e = hipMemcpyAsync(n_pairs, dP, sizeof(int64_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipEventRecord(ev, s);
+    if (e == hipSuccess) e = launch_bin_depth(n, proj, workspace, s);
+    if (e == hipSuccess) e = hipEventSynchronize(ev);
+    (void)hipEventDestroy(ev);
+    if (e != hipSuccess) return GS_ERR_HIP;
+    P = *n_pairs;
+    if (P < 0) return GS_ERR_OVERFLOW;  // a count past INT64_MAX
+  } else {
+    uint64_t total = 0;
+    if (hipMemcpyAsync(&total, dP, sizeof total, hipMemcpyDeviceToHost, s) != hipSuccess) return GS_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return GS_ERR_HIP;
+    if (total > (uint64_t)INT64_MAX) return GS_ERR_OVERFLOW;
+    P = (int64_t)total;
+    *n_pairs = P;
+    if (!keys) return GS_OK;
+    if (launch_bin_depth(n, proj, workspace, s) != hipSuccess) return GS_ERR_HIP;
+  }
+  if (P > capacity) return GS_ERR_CAPACITY;
+  if (workspace_bytes < bin_workspace_bytes(n, P)) return GS_ERR_WORKSPACE;
   const DevCamera d = dev_camera(cam);
-  return hip_status(
-      launch_bin_emit(n, (int64_t)totals[1], (int64_t)totals[0], proj, d.tiles_x, workspace, keys, vals, s));
+  return hip_status(launch_bin_emit(n, P, proj, d.tiles_x, workspace, keys, vals, s));
 }
 
 gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys, uint32_t* vals,
                        uint64_t* keys_tmp, uint32_t* vals_tmp, int64_t* tile_ranges, int32_t* tile_order,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       int32_t* result_in_tmp, void* workspace, size_t workspace_bytes, void* stream) {
   if (n_pairs < 0 || num_tiles < 1 || !tile_ranges || sorted_low_bits < 0 || sorted_low_bits > 64)
     return GS_ERR_INVALID_ARG;
   if (n_pairs > 0 && (!keys || !vals || !keys_tmp || !vals_tmp)) return GS_ERR_INVALID_ARG;
@@ -187,7 +215,7 @@ gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bi
   if (!workspace || workspace_bytes < sort_workspace_bytes(n_pairs, num_tiles, sorted_low_bits))
     return GS_ERR_WORKSPACE;
   return hip_status(launch_sort(n_pairs, num_tiles, keys, vals, keys_tmp, vals_tmp, tile_ranges, tile_order,
-                                sorted_low_bits, workspace, static_cast<hipStream_t>(stream)));
+                                sorted_low_bits, result_in_tmp, workspace, static_cast<hipStream_t>(stream)));
 }
 
 gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_vals, const int64_t* tile_ranges,

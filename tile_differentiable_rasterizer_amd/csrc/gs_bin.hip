@@ -17,6 +17,11 @@
 // 40 bits, so the pair sort is left with the tile bits above the low byte: one digit pass
 // at 1080p instead of six over unsorted keys.
 //
+// Two phases around the one host read of the pair count: the depth phase (compaction,
+// depth sort, records gathered into depth order) reads the visible count on the device,
+// so it can be queued before the host has the pair count; the emission phase, whose grids
+// depend on the pair count, follows.
+//
 // Kernels:
 //   k_count_blocks   per 1024 Gaussians: pair count and visible count
 //   k_scan_blocks    one workgroup: exclusive scan of per-block sums, and the total
@@ -36,8 +41,8 @@
 
 namespace gs {
 
-hipError_t radix_sort_u32(int64_t P, uint32_t* keys, uint32_t* vals, uint32_t* keys_tmp, uint32_t* vals_tmp, int lo,
-                          int hi, void* ws, hipStream_t s);
+hipError_t radix_sort_u32(int64_t P, const uint64_t* dcount, uint32_t* keys, uint32_t* vals, uint32_t* keys_tmp,
+                          uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s);
 size_t radix_workspace_bytes(int64_t P, int lo, int hi);
 
 constexpr int kBinBlock = 256;
@@ -144,11 +149,13 @@ __global__ __launch_bounds__(kBinBlock) void k_compact(int64_t n, const uint32_t
 // Per 1024 depth-sorted Gaussians: their pair count; also gathers their tile records
 // (32 bytes: kept runs, rectangle, count) into depth order for the emission (the one
 // random-access pass over the Gaussians).
-__global__ __launch_bounds__(kBinBlock) void k_count_sorted(int64_t v, const uint32_t* __restrict__ order,
+__global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __restrict__ vcount,
+                                                            const uint32_t* __restrict__ order,
                                                             const uint4* __restrict__ runs,
                                                             uint4* __restrict__ sruns, uint32_t* __restrict__ sn,
                                                             uint64_t* __restrict__ sums) {
   __shared__ uint64_t s_p[kBinBlock / kWave];
+  const int64_t v = (int64_t)*vcount;  // visible Gaussians (the grid covers all of them)
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
   uint64_t acc = 0;
 #pragma unroll
@@ -178,10 +185,12 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(int64_t v, const uin
 // partition: goff[i] = pairs of the depth-sorted Gaussians before i (i in [0, v]);
 // gstart[b] = the Gaussian holding pair b * kEmitPart.  Every visible Gaussian has at
 // least one pair, so each partition start falls inside exactly one Gaussian's range.
-__global__ __launch_bounds__(kBinBlock) void k_offsets(int64_t v, const uint32_t* __restrict__ sn,
+__global__ __launch_bounds__(kBinBlock) void k_offsets(const uint64_t* __restrict__ vcount,
+                                                       const uint32_t* __restrict__ sn,
                                                        const uint64_t* __restrict__ block_off,
                                                        uint64_t* __restrict__ goff, uint32_t* __restrict__ gstart) {
   __shared__ uint64_t s_w[kBinBlock / kWave];
+  const int64_t v = (int64_t)*vcount;
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   uint32_t cnt[kBinPer];
@@ -314,7 +323,8 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
 // byte.  A workgroup takes kCountParts consecutive partitions and writes, per partition,
 // the counts of the chunk's earlier partitions (cnt_pre[b][d]) and, per chunk, its totals
 // (csum[c][d]); both are contiguous rows.
-__global__ __launch_bounds__(kBinBlock) void k_emit_count(int64_t v, int64_t P, int64_t nparts,
+__global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __restrict__ vcount, int64_t P,
+                                                          int64_t nparts,
                                                           const uint4* __restrict__ sruns,
                                                           const uint64_t* __restrict__ goff,
                                                           const uint32_t* __restrict__ gstart, int tiles_x,
@@ -323,6 +333,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_count(int64_t v, int64_t P, 
   __shared__ int32_t s_rel[kEmitPart + 2];
   __shared__ uint32_t s_h[kBinBlock / kWave][kDigits];
   const int tid = threadIdx.x, wave = tid / kWave;
+  const int64_t v = (int64_t)*vcount;
   uint32_t running = 0;  // digit tid's count in the chunk's earlier partitions
   for (int q = 0; q < kCountParts; ++q) {
     const int64_t b = (int64_t)blockIdx.x * kCountParts + q;
@@ -381,13 +392,24 @@ __global__ __launch_bounds__(kBinBlock) void k_digit_scan(int64_t nchunks, uint6
   if (tid == 0) totals[d] = s_carry;
 }
 
+// Logical partition of workgroup i when the dispatcher deals workgroups to the 8 XCDs
+// in turn (i on XCD i mod 8): XCD x takes one contiguous range of partitions, so the
+// short digit runs that neighbouring partitions write next to each other meet in the same
+// L2 and leave it as whole lines.  A bijection of [0, n).
+__device__ __forceinline__ int64_t xcd_contiguous(int64_t i, int64_t n) {
+  constexpr int64_t kXcds = 8;
+  const int64_t x = i % kXcds, q = n / kXcds, r = n % kXcds;
+  return x * q + (x < r ? x : r) + i / kXcds;
+}
+
 // Scattering pass: writes the partition's pairs, keys[p] = tile << 32 | depth bits and
 // vals[p] = Gaussian id, at their place in the order (tile & 255, depth, id).  The pairs
 // are generated as in the counting pass, moved through LDS into wavefront-striped order,
 // ranked stably by digit (wavefront ballots match equal digits), regrouped by digit in
 // LDS and written as one contiguous run per digit; a run starts at the digit's global
 // base plus the digit's count in earlier partitions.
-__global__ __launch_bounds__(kBinBlock) void k_emit_scatter(int64_t v, int64_t P, int64_t nparts,
+__global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __restrict__ vcount, int64_t P,
+                                                            int64_t nparts,
                                                             const uint4* __restrict__ sruns,
                                                             const uint32_t* __restrict__ sdepth,
                                                             const uint32_t* __restrict__ sid,
@@ -406,8 +428,10 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(int64_t v, int64_t P
   __shared__ uint64_t s_gbase[kDigits];                    // global digit starts for this partition
   __shared__ uint64_t s_w[kBinBlock / kWave];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const int64_t v = (int64_t)*vcount;
   for (int i = tid; i < (kBinBlock / kWave) * kDigits; i += kBinBlock) (&s_wh[0][0])[i] = 0;
-  const EmitPart e = stage_partition(blockIdx.x, nparts, v, P, goff, gstart, s_rel);
+  const int64_t b = xcd_contiguous(blockIdx.x, nparts);
+  const EmitPart e = stage_partition(b, nparts, v, P, goff, gstart, s_rel);
   {  // global start of this partition's run of digit d = tid: the digit's base plus its
      // count in earlier partitions
     const uint64_t tot = totals[tid];
@@ -416,7 +440,6 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(int64_t v, int64_t P
     __syncthreads();
     uint64_t pre = inc - tot;
     for (int w = 0; w < wave; ++w) pre += s_w[w];
-    const int64_t b = blockIdx.x;
     s_gbase[tid] = pre + cpre[(b / kCountParts) * kDigits + tid] + cnt_pre[b * kDigits + tid];
   }
   // generate: lane-consecutive, one pad slot per lane so that a wavefront's 8-byte
@@ -551,12 +574,13 @@ uint64_t* bin_totals_ptr(int64_t n, void* ws) {
   return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + bin_layout(n, 0).totals);
 }
 
-// Phase 2 (after the host read P and V): compact, depth-sort, then the two emission
-// passes over partitions of kEmitPart pairs.
-hipError_t launch_bin_emit(int64_t n, int64_t v, int64_t P, const gs_projected& proj, int tiles_x, void* ws,
-                           uint64_t* keys, uint32_t* vals, hipStream_t s) {
-  if (v == 0 || P == 0) return hipSuccess;
-  const BinLayout l = bin_layout(n, P);
+// Depth phase, queued right after the count: compact the visible Gaussians, sort them by
+// depth and gather their tile records into depth order, with per-block pair sums and
+// their scan.  The visible count V is read on the device (totals[1]); every grid is sized
+// for all n Gaussians, so no host value is needed.
+hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, void* ws, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const BinLayout l = bin_layout(n, 0);
   char* w = static_cast<char*>(ws);
   uint32_t* dk0 = reinterpret_cast<uint32_t*>(w + l.dk0);
   uint32_t* dv0 = reinterpret_cast<uint32_t*>(w + l.dv0);
@@ -564,6 +588,31 @@ hipError_t launch_bin_emit(int64_t n, int64_t v, int64_t P, const gs_projected& 
   uint32_t* dv1 = reinterpret_cast<uint32_t*>(w + l.dv1);
   uint64_t* ss = reinterpret_cast<uint64_t*>(w + l.sorted_sums);
   uint64_t* totals = reinterpret_cast<uint64_t*>(w + l.totals);
+  uint4* sruns = reinterpret_cast<uint4*>(w + l.sruns);
+  uint32_t* sn = reinterpret_cast<uint32_t*>(w + l.sn);
+  k_compact<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, proj.n_tiles, proj.depth,
+                                                 reinterpret_cast<const uint64_t*>(w + l.vis_sums), dk0, dv0);
+  hipError_t e = radix_sort_u32(n, totals + 1, dk0, dv0, dk1, dv1, 0, 32, w + l.sort, s);
+  if (e != hipSuccess) return e;
+  k_count_sorted<<<(unsigned)l.nb, kBinBlock, 0, s>>>(totals + 1, dv0, reinterpret_cast<const uint4*>(proj.runs),
+                                                      sruns, sn, ss);
+  k_scan_blocks<<<1, 1024, 0, s>>>(l.nb, ss, totals + 2);
+  return hipGetLastError();
+}
+
+// Emission phase (the host has read P, and the workspace holds the P-sized arrays): pair
+// offsets and partition starts, then the two emission passes over partitions of
+// kEmitPart pairs.
+hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int tiles_x, void* ws, uint64_t* keys,
+                           uint32_t* vals, hipStream_t s) {
+  (void)proj;
+  if (n == 0 || P == 0) return hipSuccess;
+  const BinLayout l = bin_layout(n, P);
+  char* w = static_cast<char*>(ws);
+  uint32_t* dk0 = reinterpret_cast<uint32_t*>(w + l.dk0);
+  uint32_t* dv0 = reinterpret_cast<uint32_t*>(w + l.dv0);
+  uint64_t* ss = reinterpret_cast<uint64_t*>(w + l.sorted_sums);
+  const uint64_t* vcount = reinterpret_cast<uint64_t*>(w + l.totals) + 1;
   uint64_t* goff = reinterpret_cast<uint64_t*>(w + l.goff);
   uint64_t* dtotals = reinterpret_cast<uint64_t*>(w + l.dtotals);
   uint32_t* gstart = reinterpret_cast<uint32_t*>(w + l.gstart);
@@ -571,17 +620,11 @@ hipError_t launch_bin_emit(int64_t n, int64_t v, int64_t P, const gs_projected& 
   uint32_t* sn = reinterpret_cast<uint32_t*>(w + l.sn);
   uint32_t* cnt_pre = reinterpret_cast<uint32_t*>(w + l.cnt_pre);
   uint64_t* csum = reinterpret_cast<uint64_t*>(w + l.csum);
-  k_compact<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, proj.n_tiles, proj.depth,
-                                                 reinterpret_cast<const uint64_t*>(w + l.vis_sums), dk0, dv0);
-  hipError_t e = radix_sort_u32(v, dk0, dv0, dk1, dv1, 0, 32, w + l.sort, s);
-  if (e != hipSuccess) return e;
-  const int64_t nbv = (v + kBinChunk - 1) / kBinChunk;
-  k_count_sorted<<<(unsigned)nbv, kBinBlock, 0, s>>>(v, dv0, reinterpret_cast<const uint4*>(proj.runs), sruns, sn, ss);
-  k_scan_blocks<<<1, 1024, 0, s>>>(nbv, ss, totals + 2);
-  k_offsets<<<(unsigned)nbv, kBinBlock, 0, s>>>(v, sn, ss, goff, gstart);
-  k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(v, P, l.nparts, sruns, goff, gstart, tiles_x, cnt_pre, csum);
+  k_offsets<<<(unsigned)l.nb, kBinBlock, 0, s>>>(vcount, sn, ss, goff, gstart);
+  k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, goff, gstart, tiles_x, cnt_pre,
+                                                         csum);
   k_digit_scan<<<kDigits, kBinBlock, 0, s>>>(l.nchunks, csum, dtotals);
-  k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(v, P, l.nparts, sruns, dk0, dv0, goff, gstart, tiles_x,
+  k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, dk0, dv0, goff, gstart, tiles_x,
                                                           cnt_pre, csum, dtotals, keys, vals);
   return hipGetLastError();
 }

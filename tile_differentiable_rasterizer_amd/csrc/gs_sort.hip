@@ -22,8 +22,8 @@
 //                 partition in LDS by digit and writes each digit's run contiguously
 //   k_sort_copy   moves the result back to keys/vals after an odd number of passes
 //                 (the depth sort of the binning stage)
-//   k_ranges      [first, last + 1) of every tile from the sorted keys; for the pair sort
-//                 it also does k_sort_copy's move on the way
+//   k_ranges      [first, last + 1) of every tile from the sorted keys; for a pair sort
+//                 whose caller wants the result in keys/vals it also moves it there
 #include "gs_device.h"
 
 namespace gs {
@@ -57,6 +57,14 @@ SortLayout sort_layout(int64_t n_pairs, int passes) {
   return l;
 }
 
+// The key count of a sort: *dcount when the count lives on the device (then Pmax, which
+// sizes the grids and the workspace, bounds it), else Pmax itself.
+__device__ __forceinline__ int64_t sort_count(int64_t Pmax, const uint64_t* dcount) {
+  if (!dcount) return Pmax;
+  const uint64_t c = *dcount;
+  return c < (uint64_t)Pmax ? (int64_t)c : Pmax;
+}
+
 __global__ void k_fill_u32(uint32_t* __restrict__ p, int64_t count, uint32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
     p[i] = v;
@@ -71,8 +79,10 @@ hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s) {
 }
 
 template <typename K>
-__global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ keys, int64_t P, int lo,
-                                                          int passes, uint64_t* __restrict__ hist) {
+__global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ keys, int64_t Pmax,
+                                                          const uint64_t* __restrict__ dcount, int lo, int passes,
+                                                          uint64_t* __restrict__ hist) {
+  const int64_t P = sort_count(Pmax, dcount);
   // one LDS histogram per wavefront: atomics from different wavefronts never collide
   __shared__ uint32_t s_h[kSortBlock / kWave][kMaxPasses * kRadix];
   const int wave = threadIdx.x / kWave;
@@ -106,9 +116,13 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ 
 }
 
 // plan[p] = -1 (skip), 0 (keys -> tmp) or 1 (tmp -> keys); plan[kMaxPasses] = buffer
-// holding the result (0 = keys, 1 = tmp).
+// holding the result (0 = keys, 1 = tmp).  With keep_all no pass is skipped (a pass over a
+// constant digit moves the keys unchanged), so the result's buffer follows from the pass
+// count alone and the host knows it.
 __global__ __launch_bounds__(kRadix) void k_sort_plan(const uint64_t* __restrict__ hist, uint64_t* __restrict__ base,
-                                                      int32_t* __restrict__ plan, int passes, uint64_t P) {
+                                                      int32_t* __restrict__ plan, int passes, int64_t Pmax,
+                                                      const uint64_t* __restrict__ dcount, int keep_all) {
+  const uint64_t P = (uint64_t)sort_count(Pmax, dcount);
   __shared__ uint64_t s_w[kRadix / kWave];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   int cur = 0;
@@ -122,7 +136,7 @@ __global__ __launch_bounds__(kRadix) void k_sort_plan(const uint64_t* __restrict
     uint64_t pre = inc - h;
     for (int w = 0; w < wave; ++w) pre += s_w[w];
     base[p * kRadix + tid] = pre;
-    const bool trivial = __syncthreads_or(h == P) != 0;
+    const bool trivial = __syncthreads_or(h == P) != 0 && !keep_all;
     if (tid == 0) plan[p] = trivial ? -1 : cur;
     if (!trivial) cur ^= 1;
   }
@@ -139,8 +153,9 @@ __device__ __forceinline__ void status_store(uint64_t* p, uint64_t v) {
 template <typename K>
 __global__ __launch_bounds__(kSortBlock) void k_onesweep(
     K* __restrict__ k0, uint32_t* __restrict__ v0, K* __restrict__ k1, uint32_t* __restrict__ v1,
-    int64_t P, int pass, int shift, int bits, const int32_t* __restrict__ plan, const uint64_t* __restrict__ dbase,
-    uint64_t* __restrict__ status, uint32_t* __restrict__ tickets) {
+    int64_t Pmax, const uint64_t* __restrict__ dcount, int pass, int shift, int bits,
+    const int32_t* __restrict__ plan, const uint64_t* __restrict__ dbase, uint64_t* __restrict__ status,
+    uint32_t* __restrict__ tickets) {
   const int mode = plan[pass];
   if (mode < 0) return;  // digit constant over all keys: nothing to do
   const K* kin = mode ? k1 : k0;
@@ -158,11 +173,15 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   __shared__ uint32_t s_part;
 
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const int64_t P = sort_count(Pmax, dcount);
   if (tid == 0) s_part = atomicAdd(tickets + pass, 1u);
   for (int i = tid; i < (kSortBlock / kWave) * kRadix; i += kSortBlock) (&s_wh[0][0])[i] = 0;
   __syncthreads();
   const int64_t part = s_part;
   const int64_t base = part * kSortPart;
+  // a grid sized for Pmax keys: tickets past the last partition of P keys have no work
+  // (tickets go out in order, so every partition below them is taken)
+  if (base >= P) return;
   // start the look-back now: the predecessor's word for this thread's digit is usually
   // final by the time this partition has ranked its keys
   uint64_t early = part > 0 ? status_load(status + (part - 1) * kRadix + tid) : 0;
@@ -277,8 +296,9 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
 template <typename K>
 __global__ void k_sort_copy(const int32_t* __restrict__ plan, const K* __restrict__ k1,
                             const uint32_t* __restrict__ v1, K* __restrict__ k0, uint32_t* __restrict__ v0,
-                            int64_t P) {
+                            int64_t Pmax, const uint64_t* __restrict__ dcount) {
   if (plan[kMaxPasses] == 0) return;
+  const int64_t P = sort_count(Pmax, dcount);
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < P; i += (int64_t)gridDim.x * blockDim.x) {
     k0[i] = k1[i];
     v0[i] = v1[i];
@@ -286,19 +306,16 @@ __global__ void k_sort_copy(const int32_t* __restrict__ plan, const K* __restric
 }
 
 // Four consecutive keys per thread; a tile's first and last positions are where its id
-// differs from the neighbour's.  With a plan (the sort ran), the sorted pairs are read
-// from the buffer the last pass wrote and, when that is the scratch buffer, moved back to
-// keys/vals on the way.
-__global__ void k_ranges(const int32_t* __restrict__ plan, const uint64_t* __restrict__ ktmp,
-                         const uint32_t* __restrict__ vtmp, uint64_t* __restrict__ keys, uint32_t* __restrict__ vals,
-                         int64_t P, int64_t num_tiles, int64_t* __restrict__ ranges) {
+// differs from the neighbour's.  The sorted pairs are read from (src, vsrc); with kdst
+// non-NULL they are also moved to (kdst, vdst) on the way.
+__global__ void k_ranges(const uint64_t* __restrict__ src, const uint32_t* __restrict__ vsrc,
+                         uint64_t* __restrict__ kdst, uint32_t* __restrict__ vdst, int64_t P, int64_t num_tiles,
+                         int64_t* __restrict__ ranges) {
   const int64_t i0 = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   if (i0 >= P) return;
-  const bool in_tmp = plan && plan[kMaxPasses] != 0;
-  const uint64_t* src = in_tmp ? ktmp : keys;
   // 16-byte accesses when every buffer allows them (i0 is a multiple of 4)
-  const bool vec16 = ((reinterpret_cast<uintptr_t>(ktmp) | reinterpret_cast<uintptr_t>(vtmp) |
-                       reinterpret_cast<uintptr_t>(keys) | reinterpret_cast<uintptr_t>(vals)) & 15) == 0;
+  const bool vec16 = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(vsrc) |
+                       reinterpret_cast<uintptr_t>(kdst) | reinterpret_cast<uintptr_t>(vdst)) & 15) == 0;
   uint64_t k[6];  // keys i0 - 1 .. i0 + 4 (~0 outside [0, P))
   k[0] = i0 > 0 ? src[i0 - 1] : ~0ull;
   if (vec16 && i0 + 4 <= P) {
@@ -310,17 +327,17 @@ __global__ void k_ranges(const int32_t* __restrict__ plan, const uint64_t* __res
 #pragma unroll
     for (int j = 0; j < 5; ++j) k[j + 1] = i0 + j < P ? src[i0 + j] : ~0ull;
   }
-  if (in_tmp) {
+  if (kdst) {
     if (vec16 && i0 + 4 <= P) {  // 16-byte moves
-      reinterpret_cast<ulonglong2*>(keys + i0)[0] = make_ulonglong2(k[1], k[2]);
-      reinterpret_cast<ulonglong2*>(keys + i0)[1] = make_ulonglong2(k[3], k[4]);
-      reinterpret_cast<uint4*>(vals + i0)[0] = reinterpret_cast<const uint4*>(vtmp + i0)[0];
+      reinterpret_cast<ulonglong2*>(kdst + i0)[0] = make_ulonglong2(k[1], k[2]);
+      reinterpret_cast<ulonglong2*>(kdst + i0)[1] = make_ulonglong2(k[3], k[4]);
+      reinterpret_cast<uint4*>(vdst + i0)[0] = reinterpret_cast<const uint4*>(vsrc + i0)[0];
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (i0 + j < P) {
-          keys[i0 + j] = k[j + 1];
-          vals[i0 + j] = vtmp[i0 + j];
+          kdst[i0 + j] = k[j + 1];
+          vdst[i0 + j] = vsrc[i0 + j];
         }
       }
     }
@@ -375,10 +392,14 @@ static int radix_passes(int lo, int hi) { return hi > lo ? (hi - lo + 7) / 8 : 0
 size_t radix_workspace_bytes(int64_t P, int lo, int hi) { return sort_layout(P, radix_passes(lo, hi)).total; }
 
 // Stable LSD sort of (keys, vals) by key bits [lo, hi).  The result ends in keys/vals, or
-// with copy_back = false in the buffer that plan[kMaxPasses] names (0 keys, 1 tmp).
+// with copy_back = false in the buffer that plan[kMaxPasses] names (0 keys, 1 tmp).  With
+// dcount non-NULL the key count is read on the device from *dcount, and P (which sizes
+// the grids and the workspace) only bounds it, so the sort can be queued before the host
+// knows the count.
 template <typename K>
-static hipError_t radix_sort(int64_t P, K* keys, uint32_t* vals, K* keys_tmp, uint32_t* vals_tmp, int lo, int hi,
-                             void* ws, hipStream_t s, bool copy_back = true) {
+static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_t* vals, K* keys_tmp,
+                             uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back = true,
+                             bool keep_all = false) {
   const int passes = radix_passes(lo, hi);
   if (P <= 1 || passes == 0) return hipSuccess;
   const SortLayout l = sort_layout(P, passes);
@@ -394,46 +415,52 @@ static hipError_t radix_sort(int64_t P, K* keys, uint32_t* vals, K* keys_tmp, ui
   {
     const int64_t want = (P + kSortPart - 1) / kSortPart;
     const unsigned blocks = (unsigned)(want < 2048 ? (want > 0 ? want : 1) : 2048);
-    k_sort_hist<K><<<blocks, kSortBlock, 0, s>>>(keys, P, lo, passes, hist);
+    k_sort_hist<K><<<blocks, kSortBlock, 0, s>>>(keys, P, dcount, lo, passes, hist);
   }
-  k_sort_plan<<<1, kRadix, 0, s>>>(hist, dbase, plan, passes, (uint64_t)P);
+  k_sort_plan<<<1, kRadix, 0, s>>>(hist, dbase, plan, passes, P, dcount, keep_all ? 1 : 0);
   for (int p = 0; p < passes; ++p) {
     const int bits = hi - lo - 8 * p < 8 ? hi - lo - 8 * p : 8;
-    k_onesweep<K><<<(unsigned)l.parts, kSortBlock, 0, s>>>(keys, vals, keys_tmp, vals_tmp, P, p, lo + 8 * p, bits,
+    k_onesweep<K><<<(unsigned)l.parts, kSortBlock, 0, s>>>(keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p,
+                                                          bits,
                                                           plan, dbase + p * kRadix,
                                                           status + (size_t)p * l.parts * kRadix, tickets);
   }
   if (copy_back) {
     const int64_t want = (P + 255) / 256;
     const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
-    k_sort_copy<K><<<blocks, 256, 0, s>>>(plan, keys_tmp, vals_tmp, keys, vals, P);
+    k_sort_copy<K><<<blocks, 256, 0, s>>>(plan, keys_tmp, vals_tmp, keys, vals, P, dcount);
   }
   return hipGetLastError();
 }
 
-hipError_t radix_sort_u32(int64_t P, uint32_t* keys, uint32_t* vals, uint32_t* keys_tmp, uint32_t* vals_tmp, int lo,
-                          int hi, void* ws, hipStream_t s) {
-  return radix_sort<uint32_t>(P, keys, vals, keys_tmp, vals_tmp, lo, hi, ws, s);
+hipError_t radix_sort_u32(int64_t P, const uint64_t* dcount, uint32_t* keys, uint32_t* vals, uint32_t* keys_tmp,
+                          uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s) {
+  return radix_sort<uint32_t>(P, dcount, keys, vals, keys_tmp, vals_tmp, lo, hi, ws, s);
 }
 
 size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_bits) {
   return radix_workspace_bytes(n_pairs, sorted_low_bits, sort_significant_bits(num_tiles));
 }
 
+// The pair sort.  No digit pass is skipped, so an odd pass count leaves the result in
+// keys_tmp/vals_tmp: with result_in_tmp [host] non-NULL it stays there and the call
+// reports where it is; with NULL, k_ranges moves it back to keys/vals.
 hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
-                       uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits, void* ws,
-                       hipStream_t s) {
+                       uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits,
+                       int32_t* result_in_tmp, void* ws, hipStream_t s) {
   hipError_t e = launch_fill_u32(ranges, 4 * num_tiles, 0u, s);
   const int hi = sort_significant_bits(num_tiles);
-  const bool sorts = P > 1 && radix_passes(sorted_low_bits, hi) > 0;
-  if (e == hipSuccess && sorts)
-    e = radix_sort<uint64_t>(P, keys, vals, keys_tmp, vals_tmp, sorted_low_bits, hi, ws, s, false);
+  const int passes = P > 1 ? radix_passes(sorted_low_bits, hi) : 0;
+  const bool in_tmp = passes % 2 == 1;
+  if (e == hipSuccess && passes > 0)
+    e = radix_sort<uint64_t>(P, nullptr, keys, vals, keys_tmp, vals_tmp, sorted_low_bits, hi, ws, s, false, true);
   if (e != hipSuccess) return e;
-  const int32_t* plan = sorts ? reinterpret_cast<const int32_t*>(static_cast<char*>(ws) + sort_layout(P, 0).plan)
-                              : nullptr;
+  const bool move = in_tmp && !result_in_tmp;
   if (P > 0)
-    k_ranges<<<(unsigned)((P + 1023) / 1024), 256, 0, s>>>(plan, keys_tmp, vals_tmp, keys, vals, P, num_tiles, ranges);
+    k_ranges<<<(unsigned)((P + 1023) / 1024), 256, 0, s>>>(in_tmp ? keys_tmp : keys, vals_tmp, move ? keys : nullptr,
+                                                           move ? vals : nullptr, P, num_tiles, ranges);
   if (order) k_tile_order<<<1, 1024, 0, s>>>(ranges, num_tiles, order);
+  if (result_in_tmp) *result_in_tmp = in_tmp ? 1 : 0;
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import threading
 
 import numpy as np
 import torch
@@ -60,7 +61,7 @@ def lib():
         L.gs_workspace_bytes.argtypes = [i64, i64, i32]
         L.gs_workspace_bytes.restype = sz
         L.gs_bin_tiles.argtypes = [i64, GsProjected, C.POINTER(GsCamera), vp, vp, i64, C.POINTER(i64), vp, sz, vp]
-        L.gs_sort_keys.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.gs_sort_keys.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, C.POINTER(i32), vp, sz, vp]
         L.gs_render_fwd.argtypes = [i64, GsProjected, vp, vp, vp, C.POINTER(GsCamera), C.POINTER(C.c_float), vp,
                                     vp, vp, vp]
         L.gs_render_bwd.argtypes = [i64, vp, vp, vp, vp, vp, i32, C.POINTER(GsCamera), GsProjected, vp, vp, vp,
@@ -155,28 +156,44 @@ def workspace_bytes(n: int, pair_capacity: int, num_tiles: int) -> int:
     return int(lib().gs_workspace_bytes(n, pair_capacity, num_tiles))
 
 
+_tls = threading.local()
+
+
+def _pinned_count():
+    """One page-locked int64 per thread for gs_bin_tiles' pair count."""
+    t = getattr(_tls, "count", None)
+    if t is None:
+        t = _tls.count = torch.zeros(1, dtype=torch.int64, pin_memory=True)
+    return t
+
+
 def bin_tiles(proj: dict, cam, keys, vals, workspace, stream=None) -> tuple[int, int]:
     """gs_bin_tiles.  Returns (status, P); status is GS_OK or GS_ERR_CAPACITY."""
     n = proj["rec"].shape[0]
     camc = camera_struct(cam)
-    P = C.c_int64(0)
+    P = _pinned_count()  # page-locked, so the call waits for the count copy alone
     cap = keys.shape[0] if keys is not None else 0
-    st = lib().gs_bin_tiles(n, projected_struct(proj), C.byref(camc), _ptr(keys), _ptr(vals), cap, C.byref(P),
-                            _ptr(workspace), workspace.numel() if workspace is not None else 0, _stream(stream))
+    st = lib().gs_bin_tiles(n, projected_struct(proj), C.byref(camc), _ptr(keys), _ptr(vals), cap,
+                            C.cast(P.data_ptr(), C.POINTER(C.c_int64)), _ptr(workspace),
+                            workspace.numel() if workspace is not None else 0, _stream(stream))
     if st not in (GS_OK, GS_ERR_CAPACITY):
         _check(st, "gs_bin_tiles")
-    return st, int(P.value)
+    return st, int(P[0])
 
 
 def sort_keys(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, ranges, workspace, order=None,
-              sorted_low_bits: int = 40, stream=None):
+              sorted_low_bits: int = 40, stream=None, leave_in_tmp: bool = False):
     """gs_sort_keys; ``order`` (int32 [num_tiles], optional) receives the longest-first tile order.
 
     ``sorted_low_bits`` = 40 for pairs from gs_bin_tiles (already ordered by tile low byte,
-    then depth), 0 for arbitrary keys."""
+    then depth), 0 for arbitrary keys.  With ``leave_in_tmp`` the result stays where the
+    last pass wrote it and the call returns True when that is keys_tmp/vals_tmp; otherwise
+    the result is in keys/vals and the call returns False."""
+    where = C.c_int32(-1)
     _check(lib().gs_sort_keys(n_pairs, num_tiles, int(sorted_low_bits), _ptr(keys), _ptr(vals), _ptr(keys_tmp),
-                              _ptr(vals_tmp), _ptr(ranges), _ptr(order), _ptr(workspace), workspace.numel(),
-                              _stream(stream)), "gs_sort_keys")
+                              _ptr(vals_tmp), _ptr(ranges), _ptr(order), C.byref(where) if leave_in_tmp else None,
+                              _ptr(workspace), workspace.numel(), _stream(stream)), "gs_sort_keys")
+    return bool(where.value == 1) if leave_in_tmp else False
 
 
 def render_fwd(proj: dict, sorted_vals, ranges, cam, bg, image, final_T, n_contrib, order=None, stream=None):
@@ -253,18 +270,19 @@ class Rasterizer:
             _check(st, "gs_bin_tiles")
         ranges = torch.empty((tiles, 2), dtype=torch.int64, device=self.device)
         order = torch.empty(tiles, dtype=torch.int32, device=self.device)
-        sort_keys(P, tiles, self.keys, self.vals, self.keys_tmp, self.vals_tmp, ranges, self.workspace, order,
-                  stream=stream)
+        in_tmp = sort_keys(P, tiles, self.keys, self.vals, self.keys_tmp, self.vals_tmp, ranges, self.workspace,
+                           order, stream=stream, leave_in_tmp=True)
+        sk, sv = (self.keys_tmp, self.vals_tmp) if in_tmp else (self.keys, self.vals)
         image = torch.empty((3, H, W), dtype=torch.float32, device=self.device)
         final_T = torch.empty((H, W), dtype=torch.float32, device=self.device)
         n_contrib = torch.empty((H, W), dtype=torch.int32, device=self.device)
-        render_fwd(self.proj, self.vals, ranges, cam, bg, image, final_T, n_contrib, order, stream=stream)
+        render_fwd(self.proj, sv, ranges, cam, bg, image, final_T, n_contrib, order, stream=stream)
         return dict(image=image, final_T=final_T, n_contrib=n_contrib, ranges=ranges, order=order, n_pairs=P,
-                    keys=self.keys[:P], vals=self.vals[:P], proj=self.proj, cam=cam, bg=tuple(bg))
+                    keys=sk[:P], vals=sv[:P], sorted_vals=sv, proj=self.proj, cam=cam, bg=tuple(bg))
 
     def backward(self, fwd: dict, dL_dimage, accum=None, denom=None, stream=None) -> dict:
         return render_bwd(self.means, self.scales, self.quats, self.opac, self.sh, self.sh_degree, fwd["cam"],
-                          fwd["proj"], self.vals, fwd["ranges"], fwd["bg"], fwd["final_T"], fwd["n_contrib"],
+                          fwd["proj"], fwd["sorted_vals"], fwd["ranges"], fwd["bg"], fwd["final_T"], fwd["n_contrib"],
                           dL_dimage, None, accum, denom, fwd.get("order"), stream=stream)
 
 
