@@ -9,10 +9,13 @@
 // coefficients whose count depends on the degree.  The formulas (EWA 2D covariance, real
 // SH) are the textbook ones; the pages omit them.
 //
-// Memory: SoA inputs read once, coalesced.  SH rows (up to 192 B per Gaussian) are staged
-// through LDS with an odd float4 row stride so each lane then reads its own row without
-// bank conflicts.  The binning-critical geometry (camera-space mean, 2D covariance,
-// support, pixel box) is evaluated in float64 and rounded once; colour is float32.
+// Memory: every input is read once per call.  Each lane reads its own SH row (up to 192 B)
+// with 16-byte loads; the cache assembles the rows' lines, which measured faster than
+// staging them through LDS (the LDS would cap occupancy).  The backward writes its dL/dsh
+// rows through LDS instead (odd float4 row stride, no bank conflicts) so the stores leave
+// as whole lines: per-lane strided stores of them measured far slower.  The
+// binning-critical geometry (camera-space mean, 2D covariance, support, pixel box) is
+// evaluated in float64 and rounded once; colour is float32.
 #include "gs_device.h"
 #include "gs_sh.h"
 #include "gs_tiles.h"
@@ -29,40 +32,6 @@ struct ShLayout {
   // odd stride in the unit the rows are read with (float4 or float): conflict-free
   static constexpr int STRIDE = V4 ? (((ROW / 4) & 1) ? ROW : ROW + 4) : ((ROW & 1) ? ROW : ROW + 1);
 };
-
-// Coalesced copy of `cnt` SH rows from global memory into LDS rows of STRIDE floats.
-template <int L>
-__device__ __forceinline__ void load_sh_rows(const float* __restrict__ src, int cnt, float* s_sh) {
-  using S = ShLayout<L>;
-  if constexpr (S::V4) {
-    constexpr int R4 = S::ROW / 4;
-    const float4* s4 = reinterpret_cast<const float4*>(src);
-    const int total = cnt * R4;
-    float4 tmp[R4];
-#pragma unroll
-    for (int it = 0; it < R4; ++it) {
-      const int f = it * kProjBlock + (int)threadIdx.x;
-      tmp[it] = f < total ? s4[f] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int it = 0; it < R4; ++it) {
-      const int f = it * kProjBlock + (int)threadIdx.x;
-      if (f < total) {
-        const int g = f / R4, c = f - g * R4;
-        *reinterpret_cast<float4*>(s_sh + g * S::STRIDE + 4 * c) = tmp[it];
-      }
-    }
-  } else {
-    const int total = cnt * S::ROW;
-    for (int it = 0; it < S::ROW; ++it) {
-      const int f = it * kProjBlock + (int)threadIdx.x;
-      if (f < total) {
-        const int g = f / S::ROW, c = f - g * S::ROW;
-        s_sh[g * S::STRIDE + c] = src[f];
-      }
-    }
-  }
-}
 
 // Coalesced copy of `cnt` LDS rows back to global memory.
 template <int L>
@@ -92,11 +61,25 @@ __device__ __forceinline__ void store_sh_rows(float* __restrict__ dst, int cnt, 
   }
 }
 
-// This lane's SH row from LDS into registers.
+// This lane's row into its LDS row (float4 stores when rows allow them: with the odd
+// float4 stride they are conflict-free).
 template <int L>
-__device__ __forceinline__ void read_row(const float* s_sh, int tid, float* coef) {
+__device__ __forceinline__ void put_row(float* my_row, const float* v) {
   using S = ShLayout<L>;
-  const float* row = s_sh + tid * S::STRIDE;
+  if constexpr (S::V4) {
+#pragma unroll
+    for (int c = 0; c < S::ROW / 4; ++c)
+      reinterpret_cast<float4*>(my_row)[c] = make_float4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < S::ROW; ++c) my_row[c] = v[c];
+  }
+}
+
+// This lane's SH row (ROW floats) from global memory into registers.
+template <int L>
+__device__ __forceinline__ void load_row(const float* __restrict__ row, float* coef) {
+  using S = ShLayout<L>;
   if constexpr (S::V4) {
 #pragma unroll
     for (int c = 0; c < S::ROW / 4; ++c) {
@@ -175,11 +158,8 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
     ushort4* __restrict__ rect_out, uint32_t* __restrict__ ntiles_out, uint8_t* __restrict__ clamp_out,
     uint4* __restrict__ runs_out) {
   using S = ShLayout<L>;
-  __shared__ float s_sh[kProjBlock * S::STRIDE];
   const int64_t base = (int64_t)blockIdx.x * kProjBlock;
   const int cnt = (int)min((int64_t)kProjBlock, n - base);
-  load_sh_rows<L>(sh + base * S::ROW, cnt, s_sh);
-  __syncthreads();
   const int tid = threadIdx.x;
   if (tid >= cnt) return;
   const int64_t i = base + tid;
@@ -192,7 +172,7 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
 
   // view-dependent colour: 0.5 + sum_k Y_k(d) sh_k, clamped at 0
   float coef[S::ROW];
-  read_row<L>(s_sh, tid, coef);
+  load_row<L>(sh + i * S::ROW, coef);
   const double vx = mx - cam.campos[0], vy = my - cam.campos[1], vz = mz - cam.campos[2];
   const double il = 1.0 / sqrt(vx * vx + vy * vy + vz * vz);
   float Y[S::K];
@@ -293,9 +273,8 @@ __global__ __launch_bounds__(kProjBlock) void k_project_bwd(
   __shared__ float s_sh[kProjBlock * S::STRIDE];
   const int64_t base = (int64_t)blockIdx.x * kProjBlock;
   const int cnt = (int)min((int64_t)kProjBlock, n - base);
-  load_sh_rows<L>(sh + base * S::ROW, cnt, s_sh);
-  __syncthreads();
   const int tid = threadIdx.x;
+  float* my_row = s_sh + tid * S::STRIDE;
   if (tid < cnt) {
     const int64_t i = base + tid;
     const bool vis = ntiles[i] > 0;
@@ -303,7 +282,7 @@ __global__ __launch_bounds__(kProjBlock) void k_project_bwd(
 #pragma unroll
     for (int e = 0; e < GS_GRAD_SCREEN; ++e) gsv[e] = gscreen[GS_GRAD_SCREEN * i + e];
     float coef[S::ROW];
-    read_row<L>(s_sh, tid, coef);
+    load_row<L>(sh + i * S::ROW, coef);
     float drow[S::ROW];
     double dmu[3] = {0.0, 0.0, 0.0}, ds[3] = {0.0, 0.0, 0.0}, dq[4] = {0.0, 0.0, 0.0, 0.0};
     const double mx = means[3 * i], my = means[3 * i + 1], mz = means[3 * i + 2];
@@ -339,6 +318,7 @@ __global__ __launch_bounds__(kProjBlock) void k_project_bwd(
       dmu[0] = ((double)dd[0] - pr * dx) * il;
       dmu[1] = ((double)dd[1] - pr * dy) * il;
       dmu[2] = ((double)dd[2] - pr * dz) * il;
+      put_row<L>(my_row, drow);  // now, so the row is not held in registers below
 
       const double sc[3] = {scales[3 * i], scales[3 * i + 1], scales[3 * i + 2]};
       Geom g;
@@ -422,6 +402,7 @@ __global__ __launch_bounds__(kProjBlock) void k_project_bwd(
     } else {
 #pragma unroll
       for (int k = 0; k < S::ROW; ++k) drow[k] = 0.0f;
+      put_row<L>(my_row, drow);
     }
 #pragma unroll
     for (int e = 0; e < 3; ++e) {
@@ -429,10 +410,6 @@ __global__ __launch_bounds__(kProjBlock) void k_project_bwd(
       dscales[3 * i + e] = (float)ds[e];
     }
     dquats[i] = make_float4((float)dq[0], (float)dq[1], (float)dq[2], (float)dq[3]);
-    // this lane's dsh row replaces its own (already read) SH row in LDS
-    float* row = s_sh + tid * S::STRIDE;
-#pragma unroll
-    for (int k = 0; k < S::ROW; ++k) row[k] = drow[k];
   }
   __syncthreads();
   store_sh_rows<L>(dsh + base * S::ROW, cnt, s_sh);
