@@ -42,7 +42,8 @@
 namespace gs {
 
 hipError_t radix_sort_u32(int64_t P, const uint64_t* dcount, uint32_t* keys, uint32_t* vals, uint32_t* keys_tmp,
-                          uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s);
+                          uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back);
+const int32_t* radix_result_in_tmp(const void* ws);
 size_t radix_workspace_bytes(int64_t P, int lo, int hi);
 
 constexpr int kBinBlock = 256;
@@ -82,15 +83,16 @@ __global__ __launch_bounds__(kBinBlock) void k_count_blocks(int64_t n, const uin
   }
 }
 
-// Exclusive scan of nb block sums in place; total written to *total.
-__global__ __launch_bounds__(1024) void k_scan_blocks(int64_t nb, uint64_t* __restrict__ sums,
-                                                      uint64_t* __restrict__ total) {
-  __shared__ uint64_t s_w[16];
+// Exclusive scan of nb block sums in place by one workgroup of NT threads; the total goes
+// to *total.
+template <int NT>
+__device__ __forceinline__ void scan_sums(int64_t nb, uint64_t* __restrict__ sums, uint64_t* __restrict__ total) {
+  __shared__ uint64_t s_w[NT / kWave];
   __shared__ uint64_t s_carry;
   if (threadIdx.x == 0) s_carry = 0;
   __syncthreads();
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
-  for (int64_t off = 0; off < nb; off += 1024) {
+  for (int64_t off = 0; off < nb; off += NT) {
     const int64_t i = off + threadIdx.x;
     const uint64_t x = i < nb ? sums[i] : 0;
     const uint64_t inc = wave_inclusive_scan(x);
@@ -101,10 +103,23 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(int64_t nb, uint64_t* __re
     const uint64_t carry = s_carry;
     if (i < nb) sums[i] = carry + wpre + inc - x;
     __syncthreads();
-    if (threadIdx.x == 1023) s_carry = carry + wpre + inc;
+    if (threadIdx.x == NT - 1) s_carry = carry + wpre + inc;
     __syncthreads();
   }
   if (threadIdx.x == 0) *total = s_carry;
+}
+
+__global__ __launch_bounds__(1024) void k_scan_blocks(int64_t nb, uint64_t* __restrict__ sums,
+                                                      uint64_t* __restrict__ total) {
+  scan_sums<1024>(nb, sums, total);
+}
+
+// The count phase's two scans (pair sums, visible sums) in one launch.
+__global__ __launch_bounds__(1024) void k_scan_blocks2(int64_t nb, uint64_t* __restrict__ a,
+                                                       uint64_t* __restrict__ b, uint64_t* __restrict__ totals) {
+  scan_sums<1024>(nb, a, totals);
+  __syncthreads();
+  scan_sums<1024>(nb, b, totals + 1);
 }
 
 // Visible Gaussians' (depth bits, id) in id order.  Round r of a workgroup covers ids
@@ -147,15 +162,23 @@ __global__ __launch_bounds__(kBinBlock) void k_compact(int64_t n, const uint32_t
 }
 
 // Per 1024 depth-sorted Gaussians: their pair count; also gathers their tile records
-// (32 bytes: kept runs, rectangle, count) into depth order for the emission (the one
-// random-access pass over the Gaussians).
+// into depth order for the emission (the one random-access pass over the Gaussians), with
+// words 6 and 7 (the count, and zero) replaced by the Gaussian's id and depth bits.  The
+// depth sort leaves its result in (dk0, dv0) or (dk1, dv1), as *in_tmp says.
 __global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __restrict__ vcount,
-                                                            const uint32_t* __restrict__ order,
+                                                            const int32_t* __restrict__ in_tmp,
+                                                            const uint32_t* __restrict__ dk0,
+                                                            const uint32_t* __restrict__ dv0,
+                                                            const uint32_t* __restrict__ dk1,
+                                                            const uint32_t* __restrict__ dv1,
                                                             const uint4* __restrict__ runs,
                                                             uint4* __restrict__ sruns, uint32_t* __restrict__ sn,
                                                             uint64_t* __restrict__ sums) {
   __shared__ uint64_t s_p[kBinBlock / kWave];
   const int64_t v = (int64_t)*vcount;  // visible Gaussians (the grid covers all of them)
+  const bool tmp = *in_tmp != 0;
+  const uint32_t* dbits = tmp ? dk1 : dk0;
+  const uint32_t* order = tmp ? dv1 : dv0;
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
   uint64_t acc = 0;
 #pragma unroll
@@ -165,7 +188,7 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __re
       const uint32_t id = order[i];
       const uint4 a = runs[2 * (size_t)id], b = runs[2 * (size_t)id + 1];
       sruns[2 * i] = a;
-      sruns[2 * i + 1] = b;
+      sruns[2 * i + 1] = make_uint4(b.x, b.y, id, dbits[i]);
       sn[i] = b.z;
       acc += b.z;
     }
@@ -246,14 +269,13 @@ __device__ __forceinline__ EmitPart stage_partition(int64_t b, int64_t nparts, i
 
 // Generates this lane's pairs; emit(k, tile, id, dbits) receives the pair's slot in the
 // lane's run (0 .. kEmitPer - 1), its tile, its Gaussian's id and the bit pattern of that
-// Gaussian's depth.  sruns, sdepth and sid are the depth-sorted Gaussians' tile records,
-// depth bits and ids.  A Gaussian's pairs are the tiles its
+// Gaussian's depth.  sruns holds the depth-sorted Gaussians' tile records (words 6 and 7:
+// id and depth bits).  A Gaussian's pairs are the tiles its
 // ellipse test keeps (every tile of a rectangle the test does not apply to), rows outer and
 // columns inner, read from the runs the projection stored.  Every loop stays inside the
 // rectangle.
 template <bool kPayload, typename F>
 __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_rel, const uint4* __restrict__ sruns,
-                                           const uint32_t* __restrict__ sdepth, const uint32_t* __restrict__ sid,
                                            int tiles_x, F&& emit) {
   const int p0 = (int)threadIdx.x * kEmitPer;
   if (p0 >= e.n) return;
@@ -285,8 +307,8 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
     const uint4 b = sruns[2 * (size_t)g + 1];
     r = make_ushort4((uint16_t)(b.x & 0xFFFFu), (uint16_t)(b.x >> 16), (uint16_t)(b.y & 0xFFFFu), (uint16_t)(b.y >> 16));
     if (kPayload) {
-      id = sid[g];
-      dbits = sdepth[g];
+      id = b.z;
+      dbits = b.w;
     }
     ty = (int)r.z;
     row();
@@ -341,7 +363,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __rest
     for (int i = tid; i < (kBinBlock / kWave) * kDigits; i += kBinBlock) (&s_h[0][0])[i] = 0;
     const EmitPart e = stage_partition(b, nparts, v, P, goff, gstart, s_rel);
     __syncthreads();
-    lane_pairs<false>(e, s_rel, sruns, nullptr, nullptr, tiles_x, [&](int, uint32_t tile, uint32_t, uint32_t) {
+    lane_pairs<false>(e, s_rel, sruns, tiles_x, [&](int, uint32_t tile, uint32_t, uint32_t) {
       atomicAdd(&s_h[wave][tile & (kDigits - 1)], 1u);
     });
     __syncthreads();
@@ -411,8 +433,6 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t i, int64_t n) {
 __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __restrict__ vcount, int64_t P,
                                                             int64_t nparts,
                                                             const uint4* __restrict__ sruns,
-                                                            const uint32_t* __restrict__ sdepth,
-                                                            const uint32_t* __restrict__ sid,
                                                             const uint64_t* __restrict__ goff,
                                                             const uint32_t* __restrict__ gstart, int tiles_x,
                                                             const uint32_t* __restrict__ cnt_pre,
@@ -444,7 +464,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
   }
   // generate: lane-consecutive, one pad slot per lane so that a wavefront's 8-byte
   // stores spread over the LDS banks
-  lane_pairs<true>(e, s_rel, sruns, sdepth, sid, tiles_x, [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
+  lane_pairs<true>(e, s_rel, sruns, tiles_x, [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
     const int slot = tid * (kEmitPer + 1) + k;
     s_keys[slot] = ((uint64_t)tile << 32) | (uint64_t)dbits;
     s_vals[slot] = id;
@@ -565,8 +585,7 @@ hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, void* ws, hipStr
   uint64_t* vs = reinterpret_cast<uint64_t*>(w + l.vis_sums);
   uint64_t* totals = reinterpret_cast<uint64_t*>(w + l.totals);
   if (l.nb > 0) k_count_blocks<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, n_tiles, ps, vs);
-  k_scan_blocks<<<1, 1024, 0, s>>>(l.nb, ps, totals);
-  k_scan_blocks<<<1, 1024, 0, s>>>(l.nb, vs, totals + 1);
+  k_scan_blocks2<<<1, 1024, 0, s>>>(l.nb, ps, vs, totals);
   return hipGetLastError();
 }
 
@@ -592,10 +611,11 @@ hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, void* ws, hipSt
   uint32_t* sn = reinterpret_cast<uint32_t*>(w + l.sn);
   k_compact<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, proj.n_tiles, proj.depth,
                                                  reinterpret_cast<const uint64_t*>(w + l.vis_sums), dk0, dv0);
-  hipError_t e = radix_sort_u32(n, totals + 1, dk0, dv0, dk1, dv1, 0, 32, w + l.sort, s);
+  // the sorted depths stay where the last pass wrote them: k_count_sorted picks the buffer
+  hipError_t e = radix_sort_u32(n, totals + 1, dk0, dv0, dk1, dv1, 0, 32, w + l.sort, s, false);
   if (e != hipSuccess) return e;
-  k_count_sorted<<<(unsigned)l.nb, kBinBlock, 0, s>>>(totals + 1, dv0, reinterpret_cast<const uint4*>(proj.runs),
-                                                      sruns, sn, ss);
+  k_count_sorted<<<(unsigned)l.nb, kBinBlock, 0, s>>>(totals + 1, radix_result_in_tmp(w + l.sort), dk0, dv0, dk1,
+                                                      dv1, reinterpret_cast<const uint4*>(proj.runs), sruns, sn, ss);
   k_scan_blocks<<<1, 1024, 0, s>>>(l.nb, ss, totals + 2);
   return hipGetLastError();
 }
@@ -609,8 +629,6 @@ hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int t
   if (n == 0 || P == 0) return hipSuccess;
   const BinLayout l = bin_layout(n, P);
   char* w = static_cast<char*>(ws);
-  uint32_t* dk0 = reinterpret_cast<uint32_t*>(w + l.dk0);
-  uint32_t* dv0 = reinterpret_cast<uint32_t*>(w + l.dv0);
   uint64_t* ss = reinterpret_cast<uint64_t*>(w + l.sorted_sums);
   const uint64_t* vcount = reinterpret_cast<uint64_t*>(w + l.totals) + 1;
   uint64_t* goff = reinterpret_cast<uint64_t*>(w + l.goff);
@@ -624,8 +642,8 @@ hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int t
   k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, goff, gstart, tiles_x, cnt_pre,
                                                          csum);
   k_digit_scan<<<kDigits, kBinBlock, 0, s>>>(l.nchunks, csum, dtotals);
-  k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, dk0, dv0, goff, gstart, tiles_x,
-                                                          cnt_pre, csum, dtotals, keys, vals);
+  k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, goff, gstart, tiles_x, cnt_pre,
+                                                          csum, dtotals, keys, vals);
   return hipGetLastError();
 }
 

@@ -11,8 +11,9 @@
 // sort of Adinets & Merrill, re-designed for 64-wide wavefronts):
 //   k_sort_hist   one read of the keys: histograms of every 8-bit digit at once
 //   k_sort_plan   exclusive scan of each histogram (global digit bases); marks digits that
-//                 are constant over all keys (those passes are skipped) and assigns the
-//                 ping-pong buffers on the device, so no host round trip is needed
+//                 are constant over all keys (those passes are skipped unless the caller
+//                 needs every pass) and assigns the ping-pong buffers on the device, so no
+//                 host round trip is needed
 //   k_onesweep    per pass: each workgroup takes a 4096-key partition by atomic ticket,
 //                 ranks its keys stably (wavefront ballots match equal digits; per-wave
 //                 digit counters in LDS, advanced with pipelined LDS atomics), publishes
@@ -20,8 +21,8 @@
 //                 global offsets by looking back over earlier partitions' published
 //                 counts (several earlier partitions per round trip), reorders the
 //                 partition in LDS by digit and writes each digit's run contiguously
-//   k_sort_copy   moves the result back to keys/vals after an odd number of passes
-//                 (the depth sort of the binning stage)
+//   k_sort_copy   moves the result back to keys/vals after an odd number of passes, for
+//                 callers that need it there
 //   k_ranges      [first, last + 1) of every tile from the sorted keys; for a pair sort
 //                 whose caller wants the result in keys/vals it also moves it there
 #include "gs_device.h"
@@ -78,6 +79,33 @@ hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
+// plan[p] = -1 (skip), 0 (keys -> tmp) or 1 (tmp -> keys); plan[kMaxPasses] = buffer
+// holding the result (0 = keys, 1 = tmp).  With keep_all no pass is skipped (a pass over a
+// constant digit moves the keys unchanged), so the result's buffer follows from the pass
+// count alone and the host knows it.  Global digit bases: base[p][d] = exclusive scan of
+// pass p's histogram.  Run by one workgroup of kRadix threads.
+__device__ __forceinline__ void sort_plan(const uint64_t* __restrict__ hist, uint64_t* __restrict__ base,
+                                          int32_t* __restrict__ plan, int passes, uint64_t P, int keep_all) {
+  __shared__ uint64_t s_w[kRadix / kWave];
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  int cur = 0;
+  for (int p = 0; p < passes; ++p) {
+    uint64_t h = 0;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) h += hist[c * kMaxPasses * kRadix + p * kRadix + tid];
+    const uint64_t inc = wave_inclusive_scan(h);
+    if (lane == kWave - 1) s_w[wave] = inc;
+    __syncthreads();
+    uint64_t pre = inc - h;
+    for (int w = 0; w < wave; ++w) pre += s_w[w];
+    base[p * kRadix + tid] = pre;
+    const bool trivial = __syncthreads_or(h == P) != 0 && !keep_all;
+    if (tid == 0) plan[p] = trivial ? -1 : cur;
+    if (!trivial) cur ^= 1;
+  }
+  if (tid == 0) plan[kMaxPasses] = cur;
+}
+
 template <typename K>
 __global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ keys, int64_t Pmax,
                                                           const uint64_t* __restrict__ dcount, int lo, int passes,
@@ -115,32 +143,10 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ 
   }
 }
 
-// plan[p] = -1 (skip), 0 (keys -> tmp) or 1 (tmp -> keys); plan[kMaxPasses] = buffer
-// holding the result (0 = keys, 1 = tmp).  With keep_all no pass is skipped (a pass over a
-// constant digit moves the keys unchanged), so the result's buffer follows from the pass
-// count alone and the host knows it.
 __global__ __launch_bounds__(kRadix) void k_sort_plan(const uint64_t* __restrict__ hist, uint64_t* __restrict__ base,
                                                       int32_t* __restrict__ plan, int passes, int64_t Pmax,
                                                       const uint64_t* __restrict__ dcount, int keep_all) {
-  const uint64_t P = (uint64_t)sort_count(Pmax, dcount);
-  __shared__ uint64_t s_w[kRadix / kWave];
-  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  int cur = 0;
-  for (int p = 0; p < passes; ++p) {
-    uint64_t h = 0;
-#pragma unroll
-    for (int c = 0; c < kHistCopies; ++c) h += hist[c * kMaxPasses * kRadix + p * kRadix + tid];
-    const uint64_t inc = wave_inclusive_scan(h);
-    if (lane == kWave - 1) s_w[wave] = inc;
-    __syncthreads();
-    uint64_t pre = inc - h;
-    for (int w = 0; w < wave; ++w) pre += s_w[w];
-    base[p * kRadix + tid] = pre;
-    const bool trivial = __syncthreads_or(h == P) != 0 && !keep_all;
-    if (tid == 0) plan[p] = trivial ? -1 : cur;
-    if (!trivial) cur ^= 1;
-  }
-  if (tid == 0) plan[kMaxPasses] = cur;
+  sort_plan(hist, base, plan, passes, (uint64_t)sort_count(Pmax, dcount), keep_all);
 }
 
 __device__ __forceinline__ uint64_t status_load(const uint64_t* p) {
@@ -401,9 +407,11 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
                              uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back = true,
                              bool keep_all = false) {
   const int passes = radix_passes(lo, hi);
-  if (P <= 1 || passes == 0) return hipSuccess;
-  const SortLayout l = sort_layout(P, passes);
   char* w = static_cast<char*>(ws);
+  if (P <= 1 || passes == 0)  // nothing moves: the result is in keys/vals, as the word says
+    return copy_back ? hipSuccess
+                     : launch_fill_u32(w + sort_layout(0, 0).plan + sizeof(int32_t) * kMaxPasses, 1, 0u, s);
+  const SortLayout l = sort_layout(P, passes);
   uint64_t* hist = reinterpret_cast<uint64_t*>(w + l.hist);
   uint64_t* dbase = reinterpret_cast<uint64_t*>(w + l.base);
   int32_t* plan = reinterpret_cast<int32_t*>(w + l.plan);
@@ -434,8 +442,14 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
 }
 
 hipError_t radix_sort_u32(int64_t P, const uint64_t* dcount, uint32_t* keys, uint32_t* vals, uint32_t* keys_tmp,
-                          uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s) {
-  return radix_sort<uint32_t>(P, dcount, keys, vals, keys_tmp, vals_tmp, lo, hi, ws, s);
+                          uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back) {
+  return radix_sort<uint32_t>(P, dcount, keys, vals, keys_tmp, vals_tmp, lo, hi, ws, s, copy_back);
+}
+
+// Device word that a sort run with copy_back = false sets to 1 when its result is in the
+// _tmp buffers (0: in keys/vals).  Its place in the workspace does not depend on the count.
+const int32_t* radix_result_in_tmp(const void* ws) {
+  return reinterpret_cast<const int32_t*>(static_cast<const char*>(ws) + sort_layout(0, 0).plan) + kMaxPasses;
 }
 
 size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_bits) {
