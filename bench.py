@@ -192,7 +192,8 @@ def main():
     tile_bits = max(1, math.ceil(math.log2(tiles)))
     passes = max(0, math.ceil((32 + tile_bits - 40) / 8))
     algo = {
-        "project": ("hbm", N * (12 + 12 + 16 + 4 + 12 * K) + N * (48 + 4 + 8 + 4 + 1)),
+        # inputs; record, depth, rect, count, clamp byte and the 32-byte tile record
+        "project": ("hbm", N * (12 + 12 + 16 + 4 + 12 * K) + N * (48 + 4 + 8 + 4 + 1 + 32)),
         # count (4 B/G), compaction (8 read + 8 written per visible), depth sort (4 passes of
         # 16 B per visible + 4 B histogram), the depth-ordered gather (20 B per visible),
         # pairs written (12 B each)
@@ -261,7 +262,7 @@ def main():
 # ratio of the known bytes of a 1 GiB device copy to what the same counter read for that
 # copy.  Valid only for the kernel source it was taken on: the digest covers the
 # compositing kernels' source and the headers they include.
-TRAFFIC = {"k_render_bwd": {"bytes": 641710433, "source_digest": "5c6cb2efdd05c25f"}}
+TRAFFIC = {"k_render_bwd": {"bytes": 544219703, "source_digest": "f623fd8a005646a0"}}
 
 
 def kernel_source_digest():
