@@ -52,7 +52,7 @@ constexpr int kBinChunk = kBinBlock * kBinPer;  // Gaussians per workgroup
 constexpr int kEmitPer = 8;                       // pairs per lane in the emission passes
 constexpr int kEmitPart = kBinBlock * kEmitPer;  // pairs per emission partition
 constexpr int kDigits = 256;                      // values of the tile's low byte
-constexpr int kCountParts = 8;                    // partitions per counting workgroup
+constexpr int kCountParts = 4;                    // partitions per counting workgroup
 
 
 __global__ __launch_bounds__(kBinBlock) void k_count_blocks(int64_t n, const uint32_t* __restrict__ n_tiles,

@@ -237,11 +237,12 @@ __device__ __forceinline__ bool bwd_record(const float4* __restrict__ s_rec, int
   dalpha = contrib && oG <= kAlphaMax ? dalpha : 0.0f;  // the clamp at 0.99 stops the gradient
   g[5] = dalpha * G;
   const float dq = dalpha * oG;
-  g[2] = dq * dx * dx;
-  g[3] = dq * dx * dy;
-  g[4] = dq * dy * dy;
-  g[0] = dq * fmaf(s3.x, dx, s3.y * dy);
-  g[1] = dq * fmaf(s3.y, dx, s3.z * dy);
+  const float dqx = dq * dx, dqy = dq * dy;
+  g[2] = dqx * dx;
+  g[3] = dqx * dy;
+  g[4] = dqy * dy;
+  g[0] = fmaf(s3.x, dqx, s3.y * dqy);
+  g[1] = fmaf(s3.y, dqx, s3.z * dqy);
   g[9] = __builtin_amdgcn_sqrtf(fmaf(g[0], g[0], g[1] * g[1]));
   return contrib;
 }

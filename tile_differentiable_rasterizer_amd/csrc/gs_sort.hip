@@ -30,8 +30,17 @@
 namespace gs {
 
 constexpr int kSortBlock = 256;
-constexpr int kSortKPT = 16;
-constexpr int kSortPart = kSortBlock * kSortKPT;  // keys per partition
+constexpr int kSortKPT = 16;                      // keys per thread of the histogram
+constexpr int kSortPart = kSortBlock * kSortKPT;  // keys per histogram round
+// Keys per thread of a onesweep partition, by key width (LDS holds the partition's keys
+// and values, so wider keys take smaller partitions and more workgroups fit a CU).
+constexpr int kOnesweepKpt32 = 16, kOnesweepKpt64 = 16;
+template <typename K>
+struct Onesweep {
+  static constexpr int kpt = sizeof(K) == 8 ? kOnesweepKpt64 : kOnesweepKpt32;
+  static constexpr int part = kSortBlock * kpt;
+};
+constexpr int kMinPart = kSortBlock * (kOnesweepKpt64 < kOnesweepKpt32 ? kOnesweepKpt64 : kOnesweepKpt32);
 constexpr int kRadix = 256;
 constexpr int kMaxPasses = 8;
 constexpr int kLookBack = 4;                      // status words read per look-back round trip
@@ -48,7 +57,7 @@ struct SortLayout {
 
 SortLayout sort_layout(int64_t n_pairs, int passes) {
   SortLayout l;
-  l.parts = (n_pairs + kSortPart - 1) / kSortPart;
+  l.parts = (n_pairs + kMinPart - 1) / kMinPart;  // enough status rows for either key width
   l.hist = 0;
   l.base = l.hist + sizeof(uint64_t) * kHistCopies * kMaxPasses * kRadix;
   l.plan = l.base + sizeof(uint64_t) * kMaxPasses * kRadix;
@@ -111,10 +120,12 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ 
                                                           const uint64_t* __restrict__ dcount, int lo, int passes,
                                                           uint64_t* __restrict__ hist) {
   const int64_t P = sort_count(Pmax, dcount);
-  // one LDS histogram per wavefront: atomics from different wavefronts never collide
-  __shared__ uint32_t s_h[kSortBlock / kWave][kMaxPasses * kRadix];
+  // one LDS histogram per wavefront (atomics from different wavefronts never collide),
+  // passes * kRadix words each: the launch sizes the LDS by the pass count
+  extern __shared__ uint32_t s_hist[];
   const int wave = threadIdx.x / kWave;
-  for (int i = threadIdx.x; i < (kSortBlock / kWave) * kMaxPasses * kRadix; i += kSortBlock) (&s_h[0][0])[i] = 0;
+  uint32_t* s_hw = s_hist + wave * passes * kRadix;
+  for (int i = threadIdx.x; i < (kSortBlock / kWave) * passes * kRadix; i += kSortBlock) s_hist[i] = 0;
   __syncthreads();
   for (int64_t b = (int64_t)blockIdx.x * kSortPart; b < P; b += (int64_t)gridDim.x * kSortPart) {
     K k[kSortKPT];  // all loads in flight before the first atomic
@@ -127,14 +138,14 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ 
     for (int j = 0; j < kSortKPT; ++j) {
       if (b + j * kSortBlock + threadIdx.x >= P) break;
       const uint64_t kk = (uint64_t)k[j] >> lo;
-      for (int p = 0; p < passes; ++p) atomicAdd(&s_h[wave][p * kRadix + ((kk >> (8 * p)) & 0xFF)], 1u);
+      for (int p = 0; p < passes; ++p) atomicAdd(&s_hw[p * kRadix + ((kk >> (8 * p)) & 0xFF)], 1u);
     }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < passes * kRadix; i += kSortBlock) {
     uint32_t c = 0;
 #pragma unroll
-    for (int w = 0; w < kSortBlock / kWave; ++w) c += s_h[w][i];
+    for (int w = 0; w < kSortBlock / kWave; ++w) c += s_hist[w * passes * kRadix + i];
     // workgroup b adds into copy b % kHistCopies, so no address sees more than
     // 1/kHistCopies of the workgroups' atomics
     if (c)
@@ -169,9 +180,10 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   K* kout = mode ? k0 : k1;
   uint32_t* vout = mode ? v0 : v1;
   const uint32_t dmask = (1u << bits) - 1u;
+  constexpr int kKPT = Onesweep<K>::kpt, kPart = Onesweep<K>::part;
 
-  __shared__ K s_keys[kSortPart];
-  __shared__ uint32_t s_vals[kSortPart];
+  __shared__ K s_keys[kPart];
+  __shared__ uint32_t s_vals[kPart];
   __shared__ uint32_t s_wh[kSortBlock / kWave][kRadix];  // per-wave digit counters, then offsets
   __shared__ uint32_t s_lbase[kRadix];                   // partition-local digit starts
   __shared__ uint64_t s_gbase[kRadix];                   // global digit starts for this partition
@@ -184,7 +196,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   for (int i = tid; i < (kSortBlock / kWave) * kRadix; i += kSortBlock) (&s_wh[0][0])[i] = 0;
   __syncthreads();
   const int64_t part = s_part;
-  const int64_t base = part * kSortPart;
+  const int64_t base = part * kPart;
   // a grid sized for Pmax keys: tickets past the last partition of P keys have no work
   // (tickets go out in order, so every partition below them is taken)
   if (base >= P) return;
@@ -193,25 +205,25 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   uint64_t early = part > 0 ? status_load(status + (part - 1) * kRadix + tid) : 0;
   const uint64_t my_dbase = dbase[tid];  // this thread's digit's global base
 
-  // wave-striped: wave w owns keys [w*1024, (w+1)*1024) of the partition, in order
-  K key[kSortKPT];
-  uint32_t val[kSortKPT];
-  uint32_t rank[kSortKPT];
+  // wave-striped: wave w owns keys [w * 64 kKPT, (w + 1) * 64 kKPT) of the partition, in order
+  K key[kKPT];
+  uint32_t val[kKPT];
+  uint32_t rank[kKPT];
 #pragma unroll
-  for (int j = 0; j < kSortKPT; ++j) {
-    const int64_t idx = base + wave * (kSortKPT * kWave) + j * kWave + lane;
+  for (int j = 0; j < kKPT; ++j) {
+    const int64_t idx = base + wave * (kKPT * kWave) + j * kWave + lane;
     key[j] = idx < P ? kin[idx] : (K)~(K)0;
     val[j] = idx < P ? vin[idx] : 0u;
   }
   // rank stably: lanes holding equal digits are matched by ballots; the lowest of them adds
   // the group's size to the wavefront's counter for that digit and gets the count before
-  // it.  LDS atomics of one wavefront run in issue order, so the kSortKPT rounds pipeline
+  // it.  LDS atomics of one wavefront run in issue order, so the kKPT rounds pipeline
   // without waiting on each other, and a shuffle then hands each lane its group's base.
-  uint32_t prev[kSortKPT];
-  int lead[kSortKPT];
+  uint32_t prev[kKPT];
+  int lead[kKPT];
 #pragma unroll
-  for (int j = 0; j < kSortKPT; ++j) {
-    const int64_t idx = base + wave * (kSortKPT * kWave) + j * kWave + lane;
+  for (int j = 0; j < kKPT; ++j) {
+    const int64_t idx = base + wave * (kKPT * kWave) + j * kWave + lane;
     const bool valid = idx < P;
     const uint32_t d = (uint32_t)(key[j] >> shift) & dmask;
     const uint64_t m = match_digit(d, bits, __ballot(valid));
@@ -222,7 +234,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
     if (valid && lower == 0) prev[j] = atomicAdd(&s_wh[wave][d], (uint32_t)__popcll(m));
   }
 #pragma unroll
-  for (int j = 0; j < kSortKPT; ++j) rank[j] += (uint32_t)__shfl((int)prev[j], lead[j], kWave);
+  for (int j = 0; j < kKPT; ++j) rank[j] += (uint32_t)__shfl((int)prev[j], lead[j], kWave);
   __syncthreads();
 
   // thread d owns digit d: wave offsets, publish the partition's count
@@ -248,8 +260,8 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   __syncthreads();
   // reorder the partition by digit in LDS (stable)
 #pragma unroll
-  for (int j = 0; j < kSortKPT; ++j) {
-    const int64_t idx = base + wave * (kSortKPT * kWave) + j * kWave + lane;
+  for (int j = 0; j < kKPT; ++j) {
+    const int64_t idx = base + wave * (kKPT * kWave) + j * kWave + lane;
     if (idx < P) {
       const uint32_t dd = (uint32_t)(key[j] >> shift) & dmask;
       const uint32_t pos = s_lbase[dd] + s_wh[wave][dd] + rank[j];
@@ -289,7 +301,7 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   s_gbase[d] = my_dbase + excl;
   __syncthreads();
   // write each digit's run contiguously
-  const int nvalid = (int)min((int64_t)kSortPart, P - base);
+  const int nvalid = (int)min((int64_t)kPart, P - base);
   for (int i = tid; i < nvalid; i += kSortBlock) {
     const K k = s_keys[i];
     const uint32_t dd = (uint32_t)(k >> shift) & dmask;
@@ -423,12 +435,13 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
   {
     const int64_t want = (P + kSortPart - 1) / kSortPart;
     const unsigned blocks = (unsigned)(want < 2048 ? (want > 0 ? want : 1) : 2048);
-    k_sort_hist<K><<<blocks, kSortBlock, 0, s>>>(keys, P, dcount, lo, passes, hist);
+    k_sort_hist<K><<<blocks, kSortBlock, sizeof(uint32_t) * (kSortBlock / kWave) * passes * kRadix, s>>>(
+        keys, P, dcount, lo, passes, hist);
   }
   k_sort_plan<<<1, kRadix, 0, s>>>(hist, dbase, plan, passes, P, dcount, keep_all ? 1 : 0);
   for (int p = 0; p < passes; ++p) {
     const int bits = hi - lo - 8 * p < 8 ? hi - lo - 8 * p : 8;
-    k_onesweep<K><<<(unsigned)l.parts, kSortBlock, 0, s>>>(keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p,
+    k_onesweep<K><<<(unsigned)((P + Onesweep<K>::part - 1) / Onesweep<K>::part), kSortBlock, 0, s>>>(keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p,
                                                           bits,
                                                           plan, dbase + p * kRadix,
                                                           status + (size_t)p * l.parts * kRadix, tickets);
