@@ -5,7 +5,8 @@ package.  The product path never calls it.  It loads ``liboracle.so``, built fro
 ``gs_oracle.c`` with plain gcc (``build()``); nothing here is shared with the HIP library.
 
 Every function lifts float32 inputs to float64 exactly and returns float64 (or integer)
-NumPy arrays.  See ``gs_oracle.c`` for the definitions and the passages they follow.
+NumPy arrays.  See ``gs_oracle.c`` for the definitions and the passages they follow;
+densify-and-prune, plain array logic, is NumPy in ``densify.py``.
 
 Parity pins (tests/test_oracle_*.py) tie each stage to something outside the oracle:
 closed forms of single and paired Gaussians, the SH addition theorem and SciPy's
@@ -341,3 +342,6 @@ def cov3d(scale, quat) -> np.ndarray:
     out = np.zeros(9)
     lib.orc_cov3d(_p(s), _p(q), _p(out))
     return out.reshape(3, 3)
+
+
+from .densify import densify, quat_to_rot  # noqa: E402,F401
