@@ -226,6 +226,50 @@ gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, cons
                         gs_grads out, float* densify_accum, int32_t* densify_denom, void* stream);
 
 /* Human-readable name of a status code (static string). */
+/* Parameters of gs_densify (values, host). */
+typedef struct gs_densify_params {
+  float grad_threshold;  /* average view-space gradient (pixel units) above which a Gaussian densifies */
+  int32_t use_abs;       /* 1: average the absolute-gradient column densify_accum[:, 1]; 0: column 0 */
+  float scale_threshold; /* largest axis scale <= this: clone; above: split (world units) */
+  int32_t split_n;       /* children per split, 2..4 */
+  float split_shrink;    /* children's scales = parent's / split_shrink (> 0) */
+  float min_opacity;     /* outputs with opacity below this are pruned */
+  float max_scale;       /* outputs whose largest scale exceeds this are pruned; <= 0: no such test */
+} gs_densify_params;
+
+/*
+ * gs_densify -- densify and prune N Gaussians from the statistics gs_render_bwd accumulated
+ * ("Enabling the absolute-gradient strategy in 3D Gaussian Splatting" s1, s3.3; "Better
+ * Gaussian Splatting in Julia" s3.4; "Implementing Better Gaussian Splatting in Julia"
+ * s4.2).  Per Gaussian, average = accum[col] / denom in float64 (col = use_abs; denom = 0
+ * never densifies).  average > grad_threshold and largest scale <= scale_threshold: the
+ * Gaussian is kept and cloned (an exact copy right after it); average > grad_threshold and
+ * a larger scale: it is replaced by split_n children, child j centred at
+ * mean + R(q / |q|) (scale * normals[i][j]) (float64, rounded once), scales = scale /
+ * split_shrink, quaternion, opacity and SH copied; otherwise it is kept as is.  Every
+ * output whose opacity < min_opacity, or (max_scale > 0) whose largest scale > max_scale,
+ * is pruned.
+ *  accum[n][2], denom[n]  the statistics (read only; the caller resets them)
+ *  normals[n][split_n][3] standard normal samples for the children (read for split inputs)
+ *  out_*                  the new set, same layouts as the inputs; out_src[m] = the input
+ *                         index output m comes from.  Outputs keep input order, each input's
+ *                         outputs contiguous.  Output buffers must not alias the inputs.
+ *  capacity, n_out [host] as gs_bin_tiles: *n_out = the output count (one device->host
+ *                         read and stream synchronisation); with out_means == NULL only the
+ *                         count is computed; n_out > capacity: GS_ERR_CAPACITY, nothing written.
+ *  workspace              gs_densify_workspace_bytes(n) bytes.
+ * Errors: INVALID_ARG (null pointer, sh_degree or split_n out of range, split_shrink <= 0),
+ * OVERFLOW, CAPACITY, WORKSPACE, HIP.
+ */
+size_t gs_densify_workspace_bytes(int64_t n);
+gs_status gs_densify(int64_t n, const float* means, const float* scales, const float* quats,
+                     const float* opacities, const float* sh, int32_t sh_degree,
+                     const float* densify_accum, const int32_t* densify_denom, const float* normals,
+                     const gs_densify_params* params, float* out_means, float* out_scales,
+                     float* out_quats, float* out_opacities, float* out_sh, uint32_t* out_src,
+                     int64_t capacity, int64_t* n_out, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 const char* gs_status_string(gs_status status);
 
 /*
@@ -233,8 +277,8 @@ const char* gs_status_string(gs_status status);
  * kernels, for comparing a kernel's rate with its roofline.
  *
  * gs_kernel_timer_start arms the timer for `kernel`, one of "k_project", "k_render_fwd",
- * "k_render_bwd", "k_project_bwd" (the single kernel behind gs_project, gs_render_fwd and
- * the two halves of gs_render_bwd).  From then on each launch of that kernel is bracketed
+ * "k_render_bwd", "k_project_bwd", "k_densify_emit" (the single kernel behind gs_project,
+ * gs_render_fwd, the two halves of gs_render_bwd and the writing pass of gs_densify).  From then on each launch of that kernel is bracketed
  * by two HIP events recorded on the caller's stream; the events are created on first use
  * and kept by the library until the process ends.
  * gs_kernel_timer_stop disarms the timer, waits for the last recorded event and writes the

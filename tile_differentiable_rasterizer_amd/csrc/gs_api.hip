@@ -27,6 +27,14 @@ hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* v
                        uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits,
                        int32_t* result_in_tmp, void* ws, hipStream_t s);
 hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
+size_t densify_workspace_bytes(int64_t n);
+hipError_t launch_densify_count(int64_t n, const float* scales, const float* opac, const float* accum,
+                                const int32_t* denom, const gs_densify_params& q, void* ws, uint64_t** total,
+                                hipStream_t s);
+hipError_t launch_densify_emit(int64_t n, const float* means, const float* scales, const float* quats,
+                               const float* opac, const float* sh, int L, const float* accum, const int32_t* denom,
+                               const float* normals, const gs_densify_params& q, const void* ws, float* om,
+                               float* os, float* oq, float* oo, float* osh, uint32_t* osrc, hipStream_t s);
 hipError_t launch_render_fwd(const gs_projected& proj, const uint32_t* vals, const int64_t* ranges,
                              const int32_t* order, const DevCamera& cam, const float bg[3], float* image,
                              float* final_T, uint32_t* n_contrib, hipStream_t s);
@@ -69,7 +77,7 @@ gs_status hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP
 // Kernel timer: while armed for one kernel, every launch of that kernel is bracketed by
 // two HIP events recorded on its launch stream.  The events are created on first use and
 // kept for the life of the process (they are reused by later arming).
-enum TimedKernel { kNone = 0, kProject, kRenderFwd, kRenderBwd, kProjectBwd };
+enum TimedKernel { kNone = 0, kProject, kRenderFwd, kRenderBwd, kProjectBwd, kDensifyEmit };
 
 struct KernelTimer {
   std::mutex mu;
@@ -90,6 +98,7 @@ TimedKernel timed_kernel_id(const char* name) {
   if (!strcmp(name, "k_render_fwd")) return kRenderFwd;
   if (!strcmp(name, "k_render_bwd")) return kRenderBwd;
   if (!strcmp(name, "k_project_bwd")) return kProjectBwd;
+  if (!strcmp(name, "k_densify_emit")) return kDensifyEmit;
   return kNone;
 }
 
@@ -119,6 +128,40 @@ hipError_t timed(TimedKernel k, hipStream_t s, F&& f) {
 }  // namespace
 
 extern "C" {
+
+size_t gs_densify_workspace_bytes(int64_t n) { return n < 0 ? 0 : densify_workspace_bytes(n); }
+
+gs_status gs_densify(int64_t n, const float* means, const float* scales, const float* quats, const float* opacities,
+                     const float* sh, int32_t sh_degree, const float* densify_accum, const int32_t* densify_denom,
+                     const float* normals, const gs_densify_params* params, float* out_means, float* out_scales,
+                     float* out_quats, float* out_opacities, float* out_sh, uint32_t* out_src, int64_t capacity,
+                     int64_t* n_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n < 0 || capacity < 0 || !params || !n_out || sh_degree < 0 || sh_degree > 3) return GS_ERR_INVALID_ARG;
+  const gs_densify_params q = *params;
+  if (q.split_n < 2 || q.split_n > 4 || !(q.split_shrink > 0.0f)) return GS_ERR_INVALID_ARG;
+  if (n >= kMaxGaussians) return GS_ERR_OVERFLOW;
+  if (n > 0 && (!means || !scales || !quats || !opacities || !sh || !densify_accum || !densify_denom || !normals))
+    return GS_ERR_INVALID_ARG;
+  if (out_means && (!out_scales || !out_quats || !out_opacities || !out_sh || !out_src)) return GS_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < densify_workspace_bytes(n)) return GS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint64_t* dtotal = nullptr;
+  if (launch_densify_count(n, scales, opacities, densify_accum, densify_denom, q, workspace, &dtotal, s) !=
+      hipSuccess)
+    return GS_ERR_HIP;
+  uint64_t total = 0;
+  if (hipMemcpyAsync(&total, dtotal, sizeof total, hipMemcpyDeviceToHost, s) != hipSuccess) return GS_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return GS_ERR_HIP;
+  if (total >= (uint64_t)kMaxGaussians) return GS_ERR_OVERFLOW;
+  *n_out = (int64_t)total;
+  if (!out_means) return GS_OK;
+  if ((int64_t)total > capacity) return GS_ERR_CAPACITY;
+  return hip_status(timed(kDensifyEmit, s, [&] {
+    return launch_densify_emit(n, means, scales, quats, opacities, sh, sh_degree, densify_accum, densify_denom,
+                               normals, q, workspace, out_means, out_scales, out_quats, out_opacities, out_sh,
+                               out_src, s);
+  }));
+}
 
 const char* gs_status_string(gs_status s) {
   switch (s) {

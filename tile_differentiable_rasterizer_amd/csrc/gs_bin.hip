@@ -589,6 +589,12 @@ hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, void* ws, hipStr
   return hipGetLastError();
 }
 
+// Exclusive scan of nb per-workgroup sums in place by one workgroup; the total to *total.
+hipError_t launch_scan_sums(int64_t nb, uint64_t* sums, uint64_t* total, hipStream_t s) {
+  k_scan_blocks<<<1, 1024, 0, s>>>(nb, sums, total);
+  return hipGetLastError();
+}
+
 uint64_t* bin_totals_ptr(int64_t n, void* ws) {
   return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + bin_layout(n, 0).totals);
 }

@@ -21,7 +21,7 @@ REC_FLOATS = 12
 GRAD_SCREEN = 10
 
 EXPORTS = ("gs_project", "gs_workspace_bytes", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd",
-           "gs_render_bwd", "gs_status_string")
+           "gs_render_bwd", "gs_densify", "gs_densify_workspace_bytes", "gs_status_string")
 
 
 class GsError(RuntimeError):
@@ -39,6 +39,12 @@ class GsCamera(C.Structure):
 class GsProjected(C.Structure):
     _fields_ = [("rec", C.c_void_p), ("depth", C.c_void_p), ("rect", C.c_void_p),
                 ("n_tiles", C.c_void_p), ("clamp", C.c_void_p), ("runs", C.c_void_p)]
+
+
+class GsDensifyParams(C.Structure):
+    _fields_ = [("grad_threshold", C.c_float), ("use_abs", C.c_int32), ("scale_threshold", C.c_float),
+                ("split_n", C.c_int32), ("split_shrink", C.c_float), ("min_opacity", C.c_float),
+                ("max_scale", C.c_float)]
 
 
 class GsGrads(C.Structure):
@@ -66,7 +72,11 @@ def lib():
                                     vp, vp, vp]
         L.gs_render_bwd.argtypes = [i64, vp, vp, vp, vp, vp, i32, C.POINTER(GsCamera), GsProjected, vp, vp, vp,
                                     C.POINTER(C.c_float), vp, vp, vp, GsGrads, vp, vp, vp]
-        for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd"):
+        L.gs_densify_workspace_bytes.argtypes = [i64]
+        L.gs_densify_workspace_bytes.restype = sz
+        L.gs_densify.argtypes = [i64, vp, vp, vp, vp, vp, i32, vp, vp, vp, C.POINTER(GsDensifyParams), vp, vp, vp,
+                                 vp, vp, vp, i64, C.POINTER(i64), vp, sz, vp]
+        for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_densify"):
             getattr(L, name).restype = i32
         L.gs_status_string.argtypes = [i32]
         L.gs_status_string.restype = C.c_char_p
@@ -290,3 +300,45 @@ def scene_to_device(scene, device="cuda"):
     """Upload a scenes.Scene's arrays once (float32, contiguous)."""
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
     return f(scene.means), f(scene.scales), f(scene.quats), f(scene.opacities), f(scene.sh)
+
+
+def densify_params(grad_threshold: float, scale_threshold: float, use_abs: bool = False, split_n: int = 2,
+                   split_shrink: float = 1.6, min_opacity: float = 0.005, max_scale: float = 0.0) -> GsDensifyParams:
+    return GsDensifyParams(grad_threshold, 1 if use_abs else 0, scale_threshold, split_n, split_shrink, min_opacity,
+                           max_scale)
+
+
+def densify(means, scales, quats, opacities, sh, sh_degree: int, accum, denom, normals, params: GsDensifyParams,
+            out: dict | None = None, stream=None) -> dict:
+    """gs_densify.  Sizes the outputs with a count-only call unless ``out`` (dict of output
+    tensors, capacity = out["src"].shape[0]) is given; returns the outputs trimmed to the
+    new count, plus ``n_out``."""
+    L = lib()
+    n = means.shape[0]
+    dev = means.device
+    ws = torch.empty(max(int(L.gs_densify_workspace_bytes(n)), 8), dtype=torch.uint8, device=dev)
+    cnt = C.c_int64(0)
+    args = (n, _ptr(means), _ptr(scales), _ptr(quats), _ptr(opacities), _ptr(sh), int(sh_degree), _ptr(accum),
+            _ptr(denom), _ptr(normals), C.byref(params))
+    if out is None:
+        _check(L.gs_densify(*args, None, None, None, None, None, None, 0, C.byref(cnt), _ptr(ws), ws.numel(),
+                            _stream(stream)), "gs_densify")
+        m = max(int(cnt.value), 1)
+        K = (sh_degree + 1) ** 2
+        out = dict(means=torch.empty((m, 3), dtype=torch.float32, device=dev),
+                   scales=torch.empty((m, 3), dtype=torch.float32, device=dev),
+                   quats=torch.empty((m, 4), dtype=torch.float32, device=dev),
+                   opacities=torch.empty(m, dtype=torch.float32, device=dev),
+                   sh=torch.empty((m, K, 3), dtype=torch.float32, device=dev),
+                   src=torch.empty(m, dtype=torch.int32, device=dev))
+    st = L.gs_densify(*args, _ptr(out["means"]), _ptr(out["scales"]), _ptr(out["quats"]), _ptr(out["opacities"]),
+                      _ptr(out["sh"]), _ptr(out["src"]), out["src"].shape[0], C.byref(cnt), _ptr(ws), ws.numel(),
+                      _stream(stream))
+    if st == GS_ERR_CAPACITY:
+        return dict(status=st, n_out=int(cnt.value))
+    _check(st, "gs_densify")
+    k = int(cnt.value)
+    res = {key: v[:k] for key, v in out.items()}
+    res["n_out"] = k
+    res["status"] = st
+    return res
