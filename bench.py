@@ -224,6 +224,10 @@ def main():
     roof_dom = dict(kernel_report["k_render_bwd"], kernel="k_render_bwd", launches_timed=frames,
                     traffic=traffic_bytes("k_render_bwd"))
 
+    log("densify")
+    dens = densify_measure(raster, means, scales, quats, opac, sh, sc.sh_degree, accum, denom, stream,
+                           with_oracle=not args.no_cpu_baseline)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(sc, cams, [d.cpu().numpy() for d in dLs], args.cpu_budget)
@@ -253,6 +257,7 @@ def main():
         "contributor_walk_per_frame": int(walk),
         "roofline": roof_dom,
         "cpu_baseline": cpu,
+        "densify": dens,
     }
     print(json.dumps(line), flush=True)
 
@@ -280,6 +285,66 @@ def traffic_bytes(kernel):
     if not t or t["source_digest"] != kernel_source_digest():
         return None
     return t["bytes"]
+
+
+def densify_measure(raster, means, scales, quats, opac, sh, L, accum, denom, stream, with_oracle, reps=5):
+    """gs_densify on the statistics the timed steps accumulated (every camera's backward).
+    Thresholds from those statistics: the 90th percentile of the seen Gaussians' average
+    gradient, the median largest scale; split into 2 children at 1/1.6 scale; prune below
+    opacity 0.005.  Times the whole call (count, scan, count read-back, emission) with HIP
+    events and the emission kernel with the library's kernel timer; the emission's rate is
+    its algorithmic bytes over its time."""
+    import torch
+
+    a = accum.cpu().numpy()
+    d = denom.cpu().numpy()
+    seen = d > 0
+    avg = a[seen, 0] / d[seen]
+    thr = float(np.quantile(avg, 0.9)) if avg.size else 1.0
+    smax = scales.max(dim=1).values
+    sthr = float(smax.median())
+    params = raster.densify_params(thr, sthr, use_abs=False, split_n=2, split_shrink=1.6, min_opacity=0.005)
+    gen = torch.Generator(device=means.device).manual_seed(17)
+    normals = torch.randn((means.shape[0], 2, 3), generator=gen, device=means.device)
+    out = raster.densify(means, scales, quats, opac, sh, L, accum, denom, normals, params)  # sizes the outputs
+    n, m = int(means.shape[0]), int(out["n_out"])
+    full = {k: v for k, v in out.items() if torch.is_tensor(v)}
+    full = {k: v.new_empty((m,) + tuple(v.shape[1:])) for k, v in full.items()}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    assert raster.kernel_timer_start("k_densify_emit") == raster.GS_OK
+    e0.record(stream)
+    for _ in range(reps):
+        r = raster.densify(means, scales, quats, opac, sh, L, accum, denom, normals, params, out=full)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    st, launches, kms = raster.kernel_timer_stop()
+    assert st == raster.GS_OK and launches == reps and r["n_out"] == m
+    call_ms = e0.elapsed_time(e1) / reps
+    emit_ms = kms / launches
+    K = (L + 1) ** 2
+    # children are the rows whose scales differ from their source's (scale / 1.6)
+    child_rows = int((r["scales"] != scales[r["src"].long()]).any(dim=1).sum().item()) if m else 0
+    n_split = child_rows // 2
+    # emission: decisions (28 B per input), the kept inputs' rows, normals of split inputs,
+    # every output row (centre, scales, quaternion, opacity, SH, source index)
+    emit_bytes = n * (28 + 12 + 16 + 12 * K) + n_split * 2 * 12 + m * (12 + 12 + 16 + 4 + 12 * K + 4)
+    ach = emit_bytes / (emit_ms * 1e-3) / 1e9
+    res = {"n_in": n, "n_out": m, "grad_threshold": thr, "scale_threshold": sthr, "call_ms": round(call_ms, 4),
+           "emit_ms": round(emit_ms, 4),
+           "emit_roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(ach / HBM_PEAK_GBS, 4), "bytes": int(emit_bytes)}}
+    if with_oracle:
+        import time as _t
+
+        import oracle
+
+        args = [x.cpu().numpy() for x in (means, scales, quats, opac, sh, accum, denom, normals)]
+        t0 = _t.perf_counter()
+        o = oracle.densify(*args, grad_threshold=thr, use_abs=False, scale_threshold=sthr, split_n=2,
+                           split_shrink=1.6, min_opacity=0.005, max_scale=0.0)
+        res["cpu_oracle_ms"] = round(1e3 * (_t.perf_counter() - t0), 1)
+        res["matches_oracle_count"] = bool(o["n_out"] == m)
+    return res
 
 
 def cpu_baseline(sc, cams, dLs, budget):
