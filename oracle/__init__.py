@@ -6,7 +6,8 @@ package.  The product path never calls it.  It loads ``liboracle.so``, built fro
 
 Every function lifts float32 inputs to float64 exactly and returns float64 (or integer)
 NumPy arrays.  See ``gs_oracle.c`` for the definitions and the passages they follow;
-densify-and-prune, plain array logic, is NumPy in ``densify.py``.
+densify-and-prune and the fused Adam step with 16-bit moments, plain array logic, are NumPy
+in ``densify.py`` and ``adam.py``.
 
 Parity pins (tests/test_oracle_*.py) tie each stage to something outside the oracle:
 closed forms of single and paired Gaussians, the SH addition theorem and SciPy's
@@ -344,4 +345,5 @@ def cov3d(scale, quat) -> np.ndarray:
     return out.reshape(3, 3)
 
 
+from .adam import adam_q16  # noqa: E402,F401
 from .densify import densify, quat_to_rot  # noqa: E402,F401
