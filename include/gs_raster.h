@@ -270,6 +270,33 @@ gs_status gs_densify(int64_t n, const float* means, const float* scales, const f
                      int64_t capacity, int64_t* n_out, void* workspace, size_t workspace_bytes,
                      void* stream);
 
+/* Hyper-parameters of gs_adam_q16 (values, host). */
+typedef struct gs_adam_params {
+  float lr, beta1, beta2, eps; /* learning rate, moment decays in [0, 1), epsilon */
+  int64_t step;                /* 1-based step number (bias correction 1 - beta^step) */
+} gs_adam_params;
+
+/*
+ * gs_adam_q16 -- one fused Adam step over n float32 parameters whose two moments are kept as
+ * 16-bit codes ("Training 10M Gaussians in 8 GB: Spirula Studio's VRAM efficiency",
+ * quantised training section: 16-bit moments packed side by side in a transposed layout,
+ * bounds per 256 units, float32 gradients).
+ *  params[n]   float32, updated in place
+ *  grads[n]    float32 gradients
+ *  state[n]    uint32 per unit: m code | v code << 16 (unit-major, so 64 lanes read 256
+ *              contiguous bytes), updated in place
+ *  bounds[ceil(n/256)][4]  float32 (m_lo, m_hi, v_lo, v_hi) of each 256-unit block, updated
+ *              in place.  A zero state with zero bounds is the start (both moments 0).
+ * A moment decodes as lo + code * ((hi - lo) / 65535).  The step, in float64: m = b1 m +
+ * (1 - b1) g, v = b2 v + (1 - b2) g^2, param -= lr (m / (1 - b1^step)) /
+ * (sqrt(v / (1 - b2^step)) + eps), the parameter rounded once to float32.  Each block's new
+ * bounds are its moments' minimum and maximum rounded to float32, and a code is
+ * rint((x - lo) / (hi - lo) * 65535) clamped to [0, 65535] (0 when hi == lo).
+ * Errors: INVALID_ARG (null pointer with n > 0, step < 1, beta outside [0, 1)), HIP.
+ */
+gs_status gs_adam_q16(int64_t n, float* params, const float* grads, uint32_t* state, float* bounds,
+                      const gs_adam_params* hyper, void* stream);
+
 const char* gs_status_string(gs_status status);
 
 /*
@@ -277,8 +304,9 @@ const char* gs_status_string(gs_status status);
  * kernels, for comparing a kernel's rate with its roofline.
  *
  * gs_kernel_timer_start arms the timer for `kernel`, one of "k_project", "k_render_fwd",
- * "k_render_bwd", "k_project_bwd", "k_densify_emit" (the single kernel behind gs_project,
- * gs_render_fwd, the two halves of gs_render_bwd and the writing pass of gs_densify).  From then on each launch of that kernel is bracketed
+ * "k_render_bwd", "k_project_bwd", "k_densify_emit", "k_adam_q16" (the single kernel behind
+ * gs_project, gs_render_fwd, the two halves of gs_render_bwd, the writing pass of gs_densify
+ * and gs_adam_q16).  From then on each launch of that kernel is bracketed
  * by two HIP events recorded on the caller's stream; the events are created on first use
  * and kept by the library until the process ends.
  * gs_kernel_timer_stop disarms the timer, waits for the last recorded event and writes the

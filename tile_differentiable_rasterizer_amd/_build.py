@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgsraster.so")
-SOURCES = ["gs_project.hip", "gs_bin.hip", "gs_sort.hip", "gs_render.hip", "gs_densify.hip", "gs_api.hip"]
+SOURCES = ["gs_project.hip", "gs_bin.hip", "gs_sort.hip", "gs_render.hip", "gs_densify.hip", "gs_adam.hip",
+           "gs_api.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-munsafe-fp-atomics",

@@ -28,6 +28,8 @@ hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* v
                        int32_t* result_in_tmp, void* ws, hipStream_t s);
 hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
 size_t densify_workspace_bytes(int64_t n);
+hipError_t launch_adam_q16(int64_t U, float* params, const float* grads, uint32_t* state, float* bounds,
+                           const gs_adam_params& p, hipStream_t s);
 hipError_t launch_densify_count(int64_t n, const float* scales, const float* opac, const float* accum,
                                 const int32_t* denom, const gs_densify_params& q, void* ws, uint64_t** total,
                                 hipStream_t s);
@@ -77,7 +79,7 @@ gs_status hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP
 // Kernel timer: while armed for one kernel, every launch of that kernel is bracketed by
 // two HIP events recorded on its launch stream.  The events are created on first use and
 // kept for the life of the process (they are reused by later arming).
-enum TimedKernel { kNone = 0, kProject, kRenderFwd, kRenderBwd, kProjectBwd, kDensifyEmit };
+enum TimedKernel { kNone = 0, kProject, kRenderFwd, kRenderBwd, kProjectBwd, kDensifyEmit, kAdamQ16 };
 
 struct KernelTimer {
   std::mutex mu;
@@ -99,6 +101,7 @@ TimedKernel timed_kernel_id(const char* name) {
   if (!strcmp(name, "k_render_bwd")) return kRenderBwd;
   if (!strcmp(name, "k_project_bwd")) return kProjectBwd;
   if (!strcmp(name, "k_densify_emit")) return kDensifyEmit;
+  if (!strcmp(name, "k_adam_q16")) return kAdamQ16;
   return kNone;
 }
 
@@ -161,6 +164,18 @@ gs_status gs_densify(int64_t n, const float* means, const float* scales, const f
                                normals, q, workspace, out_means, out_scales, out_quats, out_opacities, out_sh,
                                out_src, s);
   }));
+}
+
+gs_status gs_adam_q16(int64_t n, float* params, const float* grads, uint32_t* state, float* bounds,
+                      const gs_adam_params* hyper, void* stream) {
+  if (n < 0 || !hyper) return GS_ERR_INVALID_ARG;
+  const gs_adam_params p = *hyper;
+  if (p.step < 1 || !(p.beta1 >= 0.0f && p.beta1 < 1.0f) || !(p.beta2 >= 0.0f && p.beta2 < 1.0f))
+    return GS_ERR_INVALID_ARG;
+  if (n > 0 && (!params || !grads || !state || !bounds)) return GS_ERR_INVALID_ARG;
+  if (n >= ((int64_t)1 << 40)) return GS_ERR_OVERFLOW;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed(kAdamQ16, s, [&] { return launch_adam_q16(n, params, grads, state, bounds, p, s); }));
 }
 
 const char* gs_status_string(gs_status s) {

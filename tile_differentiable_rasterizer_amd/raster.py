@@ -21,7 +21,7 @@ REC_FLOATS = 12
 GRAD_SCREEN = 10
 
 EXPORTS = ("gs_project", "gs_workspace_bytes", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd",
-           "gs_render_bwd", "gs_densify", "gs_densify_workspace_bytes", "gs_status_string")
+           "gs_render_bwd", "gs_densify", "gs_densify_workspace_bytes", "gs_adam_q16", "gs_status_string")
 
 
 class GsError(RuntimeError):
@@ -45,6 +45,11 @@ class GsDensifyParams(C.Structure):
     _fields_ = [("grad_threshold", C.c_float), ("use_abs", C.c_int32), ("scale_threshold", C.c_float),
                 ("split_n", C.c_int32), ("split_shrink", C.c_float), ("min_opacity", C.c_float),
                 ("max_scale", C.c_float)]
+
+
+class GsAdamParams(C.Structure):
+    _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
+                ("step", C.c_int64)]
 
 
 class GsGrads(C.Structure):
@@ -76,7 +81,9 @@ def lib():
         L.gs_densify_workspace_bytes.restype = sz
         L.gs_densify.argtypes = [i64, vp, vp, vp, vp, vp, i32, vp, vp, vp, C.POINTER(GsDensifyParams), vp, vp, vp,
                                  vp, vp, vp, i64, C.POINTER(i64), vp, sz, vp]
-        for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_densify"):
+        L.gs_adam_q16.argtypes = [i64, vp, vp, vp, vp, C.POINTER(GsAdamParams), vp]
+        for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_densify",
+                     "gs_adam_q16"):
             getattr(L, name).restype = i32
         L.gs_status_string.argtypes = [i32]
         L.gs_status_string.restype = C.c_char_p
@@ -342,3 +349,17 @@ def densify(means, scales, quats, opacities, sh, sh_degree: int, accum, denom, n
     res["n_out"] = k
     res["status"] = st
     return res
+
+
+def adam_state(n_units: int, device="cuda") -> tuple:
+    """Zero Adam state for gs_adam_q16: (state uint32 as int32 [n], bounds float32 [ceil(n/256)][4])."""
+    return (torch.zeros(n_units, dtype=torch.int32, device=device),
+            torch.zeros(((n_units + 255) // 256, 4), dtype=torch.float32, device=device))
+
+
+def adam_q16(params, grads, state, bounds, lr: float, step: int, beta1: float = 0.9, beta2: float = 0.999,
+             eps: float = 1e-8, stream=None):
+    """gs_adam_q16 on flat float32 tensors (params and state updated in place)."""
+    h = GsAdamParams(lr, beta1, beta2, eps, int(step))
+    _check(lib().gs_adam_q16(params.numel(), _ptr(params), _ptr(grads), _ptr(state), _ptr(bounds), C.byref(h),
+                             _stream(stream)), "gs_adam_q16")
