@@ -287,11 +287,11 @@ typedef struct gs_adam_params {
  *              contiguous bytes), updated in place
  *  bounds[ceil(n/256)][4]  float32 (m_lo, m_hi, v_lo, v_hi) of each 256-unit block, updated
  *              in place.  A zero state with zero bounds is the start (both moments 0).
- * A moment decodes as lo + code * ((hi - lo) / 65535).  The step, in float64: m = b1 m +
- * (1 - b1) g, v = b2 v + (1 - b2) g^2, param -= lr (m / (1 - b1^step)) /
- * (sqrt(v / (1 - b2^step)) + eps), the parameter rounded once to float32.  Each block's new
+ * A moment decodes as lo + code * ((hi - lo) * (1 / 65535)).  The step, in float64:
+ * m = b1 m + (1 - b1) g, v = b2 v + (1 - b2) g^2, param -= lr (m * ib1) / (sqrt(v * ib2) + eps)
+ * with ib = 1 / (1 - beta^step), the parameter rounded once to float32.  Each block's new
  * bounds are its moments' minimum and maximum rounded to float32, and a code is
- * rint((x - lo) / (hi - lo) * 65535) clamped to [0, 65535] (0 when hi == lo).
+ * rint((x - lo) * (65535 / (hi - lo))) clamped to [0, 65535] (0 when hi == lo).
  * Errors: INVALID_ARG (null pointer with n > 0, step < 1, beta outside [0, 1)), HIP.
  */
 gs_status gs_adam_q16(int64_t n, float* params, const float* grads, uint32_t* state, float* bounds,

@@ -7,10 +7,14 @@
 // state, with one (min, max) bounds pair per 256 units; gradients stay float32.  The update
 // is Adam (Kingma and Ba) with bias correction.
 //
-// One workgroup per 256-unit block, one unit per lane, one pass: decode both moments from
+// One wavefront per block of 256 units, four contiguous units per lane, one pass: decode
+// both moments from
 // the block's bounds, update them and the parameter in float64, reduce the block's new
-// minimum and maximum of each moment across the workgroup, and re-encode.  The arithmetic
-// is written in the order of its definition with contraction off, so the codes (integers
+// minimum and maximum of each moment (in the lane, then across the wavefront), and
+// re-encode.  Constants enter
+// as reciprocals computed once (1/65535, 1/(1 - beta^t), and 65535/(hi - lo) per block by one
+// lane), which leaves one float64 division and one square root per unit.  The arithmetic is
+// written in the order of its definition with contraction off, so the codes (integers
 // decided by floating point) and the parameters are bit-exact against a float64 reference.
 #include "gs_device.h"
 
@@ -18,74 +22,122 @@ namespace gs {
 
 constexpr int kAdamBlock = 256;  // units per bounds block = lanes per workgroup
 constexpr double kQMax = 65535.0;
+constexpr double kInvQMax = 1.0 / 65535.0;
 
 struct AdamConsts {
-  double lr, b1, b2, eps, bc1, bc2;  // bc = 1 - beta^step
+  double lr, b1, b2, eps, ib1, ib2;  // ib = 1 / (1 - beta^step)
 };
 
 __device__ __forceinline__ double decode_q16(uint32_t code, float lo, float hi) {
 #pragma clang fp contract(off)
   const double l = lo, h = hi;
-  return l + (double)code * ((h - l) / kQMax);
+  return l + (double)code * ((h - l) * kInvQMax);
 }
 
-__device__ __forceinline__ uint32_t encode_q16(double x, float lo, float hi) {
+// scale = 65535 / (hi - lo) of the block; unused when hi == lo
+__device__ __forceinline__ uint32_t encode_q16(double x, float lo, float hi, double scale) {
 #pragma clang fp contract(off)
   const double l = lo, h = hi;
   if (h == l) return 0u;
-  const double c = rint((x - l) / (h - l) * kQMax);
+  const double c = rint((x - l) * scale);
   return c <= 0.0 ? 0u : c >= kQMax ? 65535u : (uint32_t)c;
 }
 
-// Minimum and maximum over the workgroup (valid lanes only), returned to every lane.
-__device__ __forceinline__ void block_minmax(double& mn, double& mx, double* s_mn, double* s_mx) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    mn = fmin(mn, __shfl_xor(mn, d, kWave));
-    mx = fmax(mx, __shfl_xor(mx, d, kWave));
-  }
-  const int wave = threadIdx.x / kWave;
-  if (__lane_id() == 0) {
-    s_mn[wave] = mn;
-    s_mx[wave] = mx;
-  }
-  __syncthreads();
-  mn = s_mn[0];
-  mx = s_mx[0];
-#pragma unroll
-  for (int w = 1; w < kAdamBlock / kWave; ++w) {
-    mn = fmin(mn, s_mn[w]);
-    mx = fmax(mx, s_mx[w]);
-  }
+// float32 <-> int32 keys whose signed order is the floats' order (negative floats have
+// their magnitude bits flipped), so extremes reduce with integer min / max.
+__device__ __forceinline__ int order_key(float f) {
+  const int b = __float_as_int(f);
+  return b < 0 ? b ^ 0x7FFFFFFF : b;
+}
+__device__ __forceinline__ float key_float(int k) { return __int_as_float(k < 0 ? k ^ 0x7FFFFFFF : k); }
+
+// Minimum (kMax = false) or maximum key over the wavefront, in every lane: DPP steps within
+// rows, row broadcasts across them (the result gathers in lane 63), then a read of lane 63.
+// Lanes a row mask leaves out take the identity, so only lane 63's value matters.
+template <bool kMax>
+__device__ __forceinline__ int wave_minmax(int v) {
+  constexpr int id = kMax ? INT32_MIN : INT32_MAX;
+  auto step = [](int x, int y) { return kMax ? max(x, y) : min(x, y); };
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xA, 0xF, false));  // row_bcast:15 into rows 1, 3
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xC, 0xF, false));  // row_bcast:31 into rows 2, 3
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
+constexpr int kUnitsPerLane = kAdamBlock / kWave;  // 4: one wavefront owns one block
+
+// Wavefront w of workgroup g owns block 4 g + w; lane l owns its units 4 l .. 4 l + 3 (16-byte
+// accesses).  The block's extremes are the float32 roundings of its float64 moments (rounding
+// is monotonic, so this rounds the float64 extremes; the values are finite), reduced inside
+// the lane and then across the wavefront: no LDS, no barrier.
 __global__ __launch_bounds__(kAdamBlock) void k_adam_q16(int64_t U, float* __restrict__ params,
                                                          const float* __restrict__ grads,
                                                          uint32_t* __restrict__ state, float4* __restrict__ bounds,
                                                          AdamConsts k) {
 #pragma clang fp contract(off)
-  __shared__ double s_m[2][kAdamBlock / kWave], s_v[2][kAdamBlock / kWave];
-  const int64_t u = (int64_t)blockIdx.x * kAdamBlock + threadIdx.x;
-  const bool valid = u < U;
-  const float4 bd = bounds[blockIdx.x];  // m_lo, m_hi, v_lo, v_hi
-  double m = 0.0, v = 0.0;
-  if (valid) {
-    const uint32_t w = state[u];
-    const double g = grads[u];
-    m = decode_q16(w & 0xFFFFu, bd.x, bd.y);
-    v = decode_q16(w >> 16, bd.z, bd.w);
-    m = k.b1 * m + (1.0 - k.b1) * g;
-    v = k.b2 * v + (1.0 - k.b2) * (g * g);
-    const double upd = k.lr * (m / k.bc1) / (sqrt(v / k.bc2) + k.eps);
-    params[u] = (float)((double)params[u] - upd);
+  constexpr int R = kUnitsPerLane;
+  const int64_t nb = (U + kAdamBlock - 1) / kAdamBlock;
+  const int64_t blk = (int64_t)blockIdx.x * (kAdamBlock / kWave) + threadIdx.x / kWave;
+  if (blk >= nb) return;  // uniform per wavefront
+  const int64_t u0 = blk * kAdamBlock + (int64_t)__lane_id() * R;
+  const float4 bd = bounds[blk];  // m_lo, m_hi, v_lo, v_hi
+  float pv[R], gv[R];
+  uint32_t wv[R];
+  const bool full = u0 + R <= U;
+  if (full) {
+    const float4 p4 = *reinterpret_cast<const float4*>(params + u0);
+    const float4 g4 = *reinterpret_cast<const float4*>(grads + u0);
+    const uint4 w4 = *reinterpret_cast<const uint4*>(state + u0);
+    pv[0] = p4.x; pv[1] = p4.y; pv[2] = p4.z; pv[3] = p4.w;
+    gv[0] = g4.x; gv[1] = g4.y; gv[2] = g4.z; gv[3] = g4.w;
+    wv[0] = w4.x; wv[1] = w4.y; wv[2] = w4.z; wv[3] = w4.w;
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const bool ok = u0 + r < U;
+      pv[r] = ok ? params[u0 + r] : 0.0f;
+      gv[r] = ok ? grads[u0 + r] : 0.0f;
+      wv[r] = ok ? state[u0 + r] : 0u;
+    }
   }
-  double mn = valid ? m : INFINITY, mx = valid ? m : -INFINITY;
-  block_minmax(mn, mx, s_m[0], s_m[1]);
-  double vn = valid ? v : INFINITY, vx = valid ? v : -INFINITY;
-  block_minmax(vn, vx, s_v[0], s_v[1]);
-  const float mlo = (float)mn, mhi = (float)mx, vlo = (float)vn, vhi = (float)vx;
-  if (valid) state[u] = encode_q16(m, mlo, mhi) | (encode_q16(v, vlo, vhi) << 16);
-  if (threadIdx.x == 0) bounds[blockIdx.x] = make_float4(mlo, mhi, vlo, vhi);
+  double m[R], v[R];
+  int mn = INT32_MAX, mx = INT32_MIN, vn = INT32_MAX, vx = INT32_MIN;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const double g = gv[r];
+    m[r] = decode_q16(wv[r] & 0xFFFFu, bd.x, bd.y);
+    v[r] = decode_q16(wv[r] >> 16, bd.z, bd.w);
+    m[r] = k.b1 * m[r] + (1.0 - k.b1) * g;
+    v[r] = k.b2 * v[r] + (1.0 - k.b2) * (g * g);
+    const double upd = k.lr * (m[r] * k.ib1) / (sqrt(v[r] * k.ib2) + k.eps);
+    pv[r] = (float)((double)pv[r] - upd);
+    if (u0 + r < U) {
+      const int km = order_key((float)m[r]), kv = order_key((float)v[r]);
+      mn = min(mn, km); mx = max(mx, km);
+      vn = min(vn, kv); vx = max(vx, kv);
+    }
+  }
+  const float mlo = key_float(wave_minmax<false>(mn)), mhi = key_float(wave_minmax<true>(mx));
+  const float vlo = key_float(wave_minmax<false>(vn)), vhi = key_float(wave_minmax<true>(vx));
+  const double sm = mhi == mlo ? 0.0 : kQMax / ((double)mhi - (double)mlo);
+  const double sv = vhi == vlo ? 0.0 : kQMax / ((double)vhi - (double)vlo);
+#pragma unroll
+  for (int r = 0; r < R; ++r) wv[r] = encode_q16(m[r], mlo, mhi, sm) | (encode_q16(v[r], vlo, vhi, sv) << 16);
+  if (full) {
+    *reinterpret_cast<float4*>(params + u0) = make_float4(pv[0], pv[1], pv[2], pv[3]);
+    *reinterpret_cast<uint4*>(state + u0) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (u0 + r < U) {
+        params[u0 + r] = pv[r];
+        state[u0 + r] = wv[r];
+      }
+  }
+  if (__lane_id() == 0) bounds[blk] = make_float4(mlo, mhi, vlo, vhi);
 }
 
 hipError_t launch_adam_q16(int64_t U, float* params, const float* grads, uint32_t* state, float* bounds,
@@ -96,10 +148,11 @@ hipError_t launch_adam_q16(int64_t U, float* params, const float* grads, uint32_
   k.b1 = (double)p.beta1;
   k.b2 = (double)p.beta2;
   k.eps = (double)p.eps;
-  k.bc1 = 1.0 - pow(k.b1, (double)p.step);
-  k.bc2 = 1.0 - pow(k.b2, (double)p.step);
+  k.ib1 = 1.0 / (1.0 - pow(k.b1, (double)p.step));
+  k.ib2 = 1.0 / (1.0 - pow(k.b2, (double)p.step));
   const int64_t nb = (U + kAdamBlock - 1) / kAdamBlock;
-  k_adam_q16<<<(unsigned)nb, kAdamBlock, 0, s>>>(U, params, grads, state, reinterpret_cast<float4*>(bounds), k);
+  const int64_t groups = (nb + kAdamBlock / kWave - 1) / (kAdamBlock / kWave);
+  k_adam_q16<<<(unsigned)groups, kAdamBlock, 0, s>>>(U, params, grads, state, reinterpret_cast<float4*>(bounds), k);
   return hipGetLastError();
 }
 
