@@ -6,8 +6,8 @@ package.  The product path never calls it.  It loads ``liboracle.so``, built fro
 
 Every function lifts float32 inputs to float64 exactly and returns float64 (or integer)
 NumPy arrays.  See ``gs_oracle.c`` for the definitions and the passages they follow;
-densify-and-prune and the fused Adam step with 16-bit moments, plain array logic, are NumPy
-in ``densify.py`` and ``adam.py``.
+densify-and-prune, the fused Adam step with 16-bit moments and the q8/q16 SH codes, plain
+array logic, are NumPy in ``densify.py``, ``adam.py`` and ``qsh.py``.
 
 Parity pins (tests/test_oracle_*.py) tie each stage to something outside the oracle:
 closed forms of single and paired Gaussians, the SH addition theorem and SciPy's
