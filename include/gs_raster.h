@@ -133,6 +133,33 @@ gs_status gs_project(int64_t n, const float* means, const float* scales, const f
                      const gs_camera* cam, gs_projected out, void* stream);
 
 /*
+ * gs_quantize_sh -- q8 / q16 codes of SH coefficients ("Training 10M Gaussians in 8 GB:
+ * Spirula Studio's VRAM efficiency", quantised training section: 8/16-bit fixed-point SH with a
+ * (min, max) table, one pair per 256 units).  Units are the coefficients of sh[n][K][3] in
+ * that order; block b = units [256 b, 256 b + 256).
+ *  codes[n][K][3]  uint8 (bits 8) or uint16 (bits 16): rint((x - lo) * (qmax / (hi - lo)))
+ *                  evaluated in float64, clamped to [0, qmax] (0 when hi == lo), qmax = 2^bits - 1
+ *  bounds[ceil(3 K n / 256)][2]  float32 (lo, hi) = the block's minimum and maximum
+ * Errors: INVALID_ARG (bits not 8 or 16, null pointer with n > 0), OVERFLOW, HIP.
+ */
+gs_status gs_quantize_sh(int64_t n, const float* sh, int32_t sh_degree, int32_t bits, void* codes,
+                         float* bounds, void* stream);
+
+/*
+ * gs_project_qsh -- gs_project with the SH coefficients given as gs_quantize_sh's codes and
+ * bounds (sh_bits 8 or 16).  Each coefficient decodes, in float32 with every operation
+ * rounded, as lo + code * ((hi - lo) * (1 / qmax)); the rest is gs_project unchanged, and the
+ * outputs feed gs_bin_tiles and the compositing calls as they are.  (The backward reads
+ * float32 SH: gs_render_bwd.)  Reads 96 (q16) or 48 (q8) instead of 192 bytes of SH per
+ * degree-3 Gaussian.
+ * Errors: as gs_project, and INVALID_ARG for sh_bits not 8 or 16.
+ */
+gs_status gs_project_qsh(int64_t n, const float* means, const float* scales, const float* quats,
+                         const float* opacities, const void* sh_codes, const float* sh_bounds,
+                         int32_t sh_bits, int32_t sh_degree, const gs_camera* cam, gs_projected out,
+                         void* stream);
+
+/*
  * gs_workspace_bytes -- bytes of device workspace that gs_bin_tiles and gs_sort_keys need
  * for n Gaussians, up to pair_capacity pairs and num_tiles tiles (the largest stage; the
  * two calls reuse the same workspace).  Returns 0 for invalid arguments.

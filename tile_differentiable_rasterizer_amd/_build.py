@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgsraster.so")
-SOURCES = ["gs_project.hip", "gs_bin.hip", "gs_sort.hip", "gs_render.hip", "gs_densify.hip", "gs_adam.hip",
+SOURCES = ["gs_project.hip", "gs_bin.hip", "gs_sort.hip", "gs_render.hip", "gs_densify.hip", "gs_adam.hip", "gs_qsh.hip",
            "gs_api.hip"]
 
 HIPCC_FLAGS = [

@@ -17,6 +17,7 @@
 // written in the order of its definition with contraction off, so the codes (integers
 // decided by floating point) and the parameters are bit-exact against a float64 reference.
 #include "gs_device.h"
+#include "gs_wave.h"
 
 namespace gs {
 
@@ -41,30 +42,6 @@ __device__ __forceinline__ uint32_t encode_q16(double x, float lo, float hi, dou
   if (h == l) return 0u;
   const double c = rint((x - l) * scale);
   return c <= 0.0 ? 0u : c >= kQMax ? 65535u : (uint32_t)c;
-}
-
-// float32 <-> int32 keys whose signed order is the floats' order (negative floats have
-// their magnitude bits flipped), so extremes reduce with integer min / max.
-__device__ __forceinline__ int order_key(float f) {
-  const int b = __float_as_int(f);
-  return b < 0 ? b ^ 0x7FFFFFFF : b;
-}
-__device__ __forceinline__ float key_float(int k) { return __int_as_float(k < 0 ? k ^ 0x7FFFFFFF : k); }
-
-// Minimum (kMax = false) or maximum key over the wavefront, in every lane: DPP steps within
-// rows, row broadcasts across them (the result gathers in lane 63), then a read of lane 63.
-// Lanes a row mask leaves out take the identity, so only lane 63's value matters.
-template <bool kMax>
-__device__ __forceinline__ int wave_minmax(int v) {
-  constexpr int id = kMax ? INT32_MIN : INT32_MAX;
-  auto step = [](int x, int y) { return kMax ? max(x, y) : min(x, y); };
-  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
-  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
-  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x140, 0xF, 0xF, false));  // row_mirror
-  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xA, 0xF, false));  // row_bcast:15 into rows 1, 3
-  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xC, 0xF, false));  // row_bcast:31 into rows 2, 3
-  return __builtin_amdgcn_readlane(v, 63);
 }
 
 constexpr int kUnitsPerLane = kAdamBlock / kWave;  // 4: one wavefront owns one block

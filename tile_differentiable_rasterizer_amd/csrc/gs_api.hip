@@ -28,6 +28,10 @@ hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* v
                        int32_t* result_in_tmp, void* ws, hipStream_t s);
 hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
 size_t densify_workspace_bytes(int64_t n);
+hipError_t launch_quantize_sh(int64_t U, const float* sh, int bits, void* codes, float* bounds, hipStream_t s);
+hipError_t launch_project_qsh(int64_t n, const float* means, const float* scales, const float* quats,
+                              const float* opac, const void* shq, const float* shb, int bits, int L,
+                              const DevCamera& cam, const gs_projected& out, hipStream_t s);
 hipError_t launch_adam_q16(int64_t U, float* params, const float* grads, uint32_t* state, float* bounds,
                            const gs_adam_params& p, hipStream_t s);
 hipError_t launch_densify_count(int64_t n, const float* scales, const float* opac, const float* accum,
@@ -208,6 +212,33 @@ gs_status gs_project(int64_t n, const float* means, const float* scales, const f
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(timed(kProject, s, [&] {
     return launch_project(n, means, scales, quats, opacities, sh, sh_degree, d, out, s);
+  }));
+}
+
+gs_status gs_quantize_sh(int64_t n, const float* sh, int32_t sh_degree, int32_t bits, void* codes, float* bounds,
+                         void* stream) {
+  if (n < 0 || sh_degree < 0 || sh_degree > 3 || (bits != 8 && bits != 16)) return GS_ERR_INVALID_ARG;
+  if (n >= kMaxGaussians) return GS_ERR_OVERFLOW;
+  if (n == 0) return GS_OK;
+  if (!sh || !codes || !bounds) return GS_ERR_INVALID_ARG;
+  const int64_t units = n * 3 * (int64_t)(sh_degree + 1) * (sh_degree + 1);
+  return hip_status(launch_quantize_sh(units, sh, bits, codes, bounds, static_cast<hipStream_t>(stream)));
+}
+
+gs_status gs_project_qsh(int64_t n, const float* means, const float* scales, const float* quats,
+                         const float* opacities, const void* sh_codes, const float* sh_bounds, int32_t sh_bits,
+                         int32_t sh_degree, const gs_camera* cam, gs_projected out, void* stream) {
+  if (n < 0 || sh_degree < 0 || sh_degree > 3 || (sh_bits != 8 && sh_bits != 16) || !camera_ok(cam))
+    return GS_ERR_INVALID_ARG;
+  if (n >= kMaxGaussians || !camera_fits(cam)) return GS_ERR_OVERFLOW;
+  if (n == 0) return GS_OK;
+  if (!means || !scales || !quats || !opacities || !sh_codes || !sh_bounds || !projected_ok(out))
+    return GS_ERR_INVALID_ARG;
+  const DevCamera d = dev_camera(cam);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed(kProject, s, [&] {
+    return launch_project_qsh(n, means, scales, quats, opacities, sh_codes, sh_bounds, sh_bits, sh_degree, d, out,
+                              s);
   }));
 }
 

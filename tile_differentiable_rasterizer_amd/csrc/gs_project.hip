@@ -92,6 +92,54 @@ __device__ __forceinline__ void load_row(const float* __restrict__ row, float* c
   }
 }
 
+// This lane's SH row from q8 / q16 codes (QB bits) with (lo, hi) bounds per 256 units ("Training
+// 10M Gaussians in 8 GB: Spirula Studio's VRAM efficiency", quantised training section): unit
+// u = i ROW + c lies in block u / 256, so a row spans one or two blocks.  Decoded in float32,
+// each operation rounded: lo + code * ((hi - lo) * (1 / qmax)).  Degree 3 rows (48 codes) are
+// read with 16-byte loads (96 or 48 bytes, 16-byte aligned).
+template <int L, int QB>
+__device__ __forceinline__ void load_row_q(const void* __restrict__ codes, const float2* __restrict__ bounds,
+                                           int64_t i, float* coef) {
+#pragma clang fp contract(off)
+  using S = ShLayout<L>;
+  using Code = typename std::conditional<QB == 16, uint16_t, uint8_t>::type;
+  constexpr float kInvQ = QB == 16 ? 1.0f / 65535.0f : 1.0f / 255.0f;
+  const int64_t u0 = i * S::ROW;
+  const int64_t b0 = u0 >> 8;
+  const int split = (int)(((b0 + 1) << 8) - u0);  // coefficients c < split are in block b0
+  const float2 B0 = bounds[b0];
+  const float2 B1 = split < S::ROW ? bounds[b0 + 1] : B0;
+  const float st0 = (B0.y - B0.x) * kInvQ, st1 = (B1.y - B1.x) * kInvQ;
+  uint32_t code[S::ROW];
+  const Code* row = static_cast<const Code*>(codes) + u0;
+  if constexpr (L == 3) {
+    constexpr int kVec = S::ROW * sizeof(Code) / 16;  // 6 (q16) or 3 (q8) 16-byte loads
+#pragma unroll
+    for (int q = 0; q < kVec; ++q) {
+      const uint4 w = reinterpret_cast<const uint4*>(row)[q];
+      const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (QB == 16) {
+          code[8 * q + 2 * k] = wv[k] & 0xFFFFu;
+          code[8 * q + 2 * k + 1] = wv[k] >> 16;
+        } else {
+#pragma unroll
+          for (int by = 0; by < 4; ++by) code[16 * q + 4 * k + by] = (wv[k] >> (8 * by)) & 0xFFu;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < S::ROW; ++c) code[c] = row[c];
+  }
+#pragma unroll
+  for (int c = 0; c < S::ROW; ++c) {
+    const bool first = c < split;
+    coef[c] = (first ? B0.x : B1.x) + (float)code[c] * (first ? st0 : st1);
+  }
+}
+
 // Geometry shared by the forward and the backward, float64.
 struct Geom {
   double t[3];      // camera-space mean
@@ -150,10 +198,12 @@ __device__ __forceinline__ void proj_rows(const DevCamera& cam, const double t[3
   }
 }
 
-template <int L>
+// QB = 0: float32 SH rows in `sh`; QB = 8 / 16: codes in `shq` with bounds `shb`.
+template <int L, int QB>
 __global__ __launch_bounds__(kProjBlock) void k_project(
     int64_t n, const float* __restrict__ means, const float* __restrict__ scales,
     const float4* __restrict__ quats, const float* __restrict__ opac, const float* __restrict__ sh,
+    const void* __restrict__ shq, const float2* __restrict__ shb,
     const DevCamera cam, float4* __restrict__ rec, float* __restrict__ depth_out,
     ushort4* __restrict__ rect_out, uint32_t* __restrict__ ntiles_out, uint8_t* __restrict__ clamp_out,
     uint4* __restrict__ runs_out) {
@@ -172,7 +222,10 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
 
   // view-dependent colour: 0.5 + sum_k Y_k(d) sh_k, clamped at 0
   float coef[S::ROW];
-  load_row<L>(sh + i * S::ROW, coef);
+  if constexpr (QB == 0)
+    load_row<L>(sh + i * S::ROW, coef);
+  else
+    load_row_q<L, QB>(shq, shb, i, coef);
   const double vx = mx - cam.campos[0], vy = my - cam.campos[1], vz = mz - cam.campos[2];
   const double il = 1.0 / sqrt(vx * vx + vy * vy + vz * vz);
   float Y[S::K];
@@ -415,27 +468,42 @@ __global__ __launch_bounds__(kProjBlock) void k_project_bwd(
   store_sh_rows<L>(dsh + base * S::ROW, cnt, s_sh);
 }
 
-template <int L>
+template <int L, int QB>
 static hipError_t launch_project_L(int64_t n, const float* means, const float* scales,
-                                   const float* quats, const float* opac, const float* sh,
-                                   const DevCamera& cam, const gs_projected& out, hipStream_t s) {
+                                   const float* quats, const float* opac, const float* sh, const void* shq,
+                                   const float* shb, const DevCamera& cam, const gs_projected& out, hipStream_t s) {
   const unsigned blocks = (unsigned)((n + kProjBlock - 1) / kProjBlock);
-  k_project<L><<<blocks, kProjBlock, 0, s>>>(
-      n, means, scales, reinterpret_cast<const float4*>(quats), opac, sh, cam,
-      reinterpret_cast<float4*>(out.rec), out.depth, reinterpret_cast<ushort4*>(out.rect), out.n_tiles,
+  k_project<L, QB><<<blocks, kProjBlock, 0, s>>>(
+      n, means, scales, reinterpret_cast<const float4*>(quats), opac, sh, shq, reinterpret_cast<const float2*>(shb),
+      cam, reinterpret_cast<float4*>(out.rec), out.depth, reinterpret_cast<ushort4*>(out.rect), out.n_tiles,
       out.clamp, reinterpret_cast<uint4*>(out.runs));
   return hipGetLastError();
+}
+
+template <int QB>
+static hipError_t launch_project_Q(int64_t n, const float* means, const float* scales, const float* quats,
+                                   const float* opac, const float* sh, const void* shq, const float* shb, int L,
+                                   const DevCamera& cam, const gs_projected& out, hipStream_t s) {
+  switch (L) {
+    case 0: return launch_project_L<0, QB>(n, means, scales, quats, opac, sh, shq, shb, cam, out, s);
+    case 1: return launch_project_L<1, QB>(n, means, scales, quats, opac, sh, shq, shb, cam, out, s);
+    case 2: return launch_project_L<2, QB>(n, means, scales, quats, opac, sh, shq, shb, cam, out, s);
+    default: return launch_project_L<3, QB>(n, means, scales, quats, opac, sh, shq, shb, cam, out, s);
+  }
 }
 
 hipError_t launch_project(int64_t n, const float* means, const float* scales, const float* quats,
                           const float* opac, const float* sh, int L, const DevCamera& cam,
                           const gs_projected& out, hipStream_t s) {
-  switch (L) {
-    case 0: return launch_project_L<0>(n, means, scales, quats, opac, sh, cam, out, s);
-    case 1: return launch_project_L<1>(n, means, scales, quats, opac, sh, cam, out, s);
-    case 2: return launch_project_L<2>(n, means, scales, quats, opac, sh, cam, out, s);
-    default: return launch_project_L<3>(n, means, scales, quats, opac, sh, cam, out, s);
-  }
+  return launch_project_Q<0>(n, means, scales, quats, opac, sh, nullptr, nullptr, L, cam, out, s);
+}
+
+// The projection with q8 / q16 SH codes (bits 8 or 16) and their bounds per 256 units.
+hipError_t launch_project_qsh(int64_t n, const float* means, const float* scales, const float* quats,
+                              const float* opac, const void* shq, const float* shb, int bits, int L,
+                              const DevCamera& cam, const gs_projected& out, hipStream_t s) {
+  return bits == 16 ? launch_project_Q<16>(n, means, scales, quats, opac, nullptr, shq, shb, L, cam, out, s)
+                    : launch_project_Q<8>(n, means, scales, quats, opac, nullptr, shq, shb, L, cam, out, s);
 }
 
 template <int L>

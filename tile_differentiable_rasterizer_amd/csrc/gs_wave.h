@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace gs {
 
@@ -59,6 +60,30 @@ __device__ __forceinline__ float wave_transpose_reduce32(const float (&v)[32]) {
   const float keep = b1 ? z[1] : z[0], send = b1 ? z[0] : z[1];
   float t = keep + dpp_get<0x4E, 0xF>(send);  // partner: lane ^ 2
   return t + dpp_get<0xB1, 0xF>(t);            // partner: lane ^ 1
+}
+
+// float32 <-> int32 keys whose signed order is the floats' order (negative floats have
+// their magnitude bits flipped), so extremes reduce with integer min / max.
+__device__ __forceinline__ int order_key(float f) {
+  const int b = __float_as_int(f);
+  return b < 0 ? b ^ 0x7FFFFFFF : b;
+}
+__device__ __forceinline__ float key_float(int k) { return __int_as_float(k < 0 ? k ^ 0x7FFFFFFF : k); }
+
+// Minimum (kMax = false) or maximum key over the wavefront, in every lane: DPP steps within
+// rows, row broadcasts across them (the result gathers in lane 63), then a read of lane 63.
+// Lanes a row mask leaves out take the identity, so only lane 63's value matters.
+template <bool kMax>
+__device__ __forceinline__ int wave_minmax(int v) {
+  constexpr int id = kMax ? INT32_MIN : INT32_MAX;
+  auto step = [](int x, int y) { return kMax ? max(x, y) : min(x, y); };
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x140, 0xF, 0xF, false));  // row_mirror
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xA, 0xF, false));  // row_bcast:15 into rows 1, 3
+  v = step(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xC, 0xF, false));  // row_bcast:31 into rows 2, 3
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 }  // namespace gs

@@ -21,7 +21,8 @@ REC_FLOATS = 12
 GRAD_SCREEN = 10
 
 EXPORTS = ("gs_project", "gs_workspace_bytes", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd",
-           "gs_render_bwd", "gs_densify", "gs_densify_workspace_bytes", "gs_adam_q16", "gs_status_string")
+           "gs_render_bwd", "gs_densify", "gs_densify_workspace_bytes", "gs_adam_q16", "gs_quantize_sh",
+           "gs_project_qsh", "gs_status_string")
 
 
 class GsError(RuntimeError):
@@ -82,8 +83,10 @@ def lib():
         L.gs_densify.argtypes = [i64, vp, vp, vp, vp, vp, i32, vp, vp, vp, C.POINTER(GsDensifyParams), vp, vp, vp,
                                  vp, vp, vp, i64, C.POINTER(i64), vp, sz, vp]
         L.gs_adam_q16.argtypes = [i64, vp, vp, vp, vp, C.POINTER(GsAdamParams), vp]
+        L.gs_quantize_sh.argtypes = [i64, vp, i32, i32, vp, vp, vp]
+        L.gs_project_qsh.argtypes = [i64, vp, vp, vp, vp, vp, vp, i32, i32, C.POINTER(GsCamera), GsProjected, vp]
         for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_densify",
-                     "gs_adam_q16"):
+                     "gs_adam_q16", "gs_quantize_sh", "gs_project_qsh"):
             getattr(L, name).restype = i32
         L.gs_status_string.argtypes = [i32]
         L.gs_status_string.restype = C.c_char_p
@@ -363,3 +366,28 @@ def adam_q16(params, grads, state, bounds, lr: float, step: int, beta1: float = 
     h = GsAdamParams(lr, beta1, beta2, eps, int(step))
     _check(lib().gs_adam_q16(params.numel(), _ptr(params), _ptr(grads), _ptr(state), _ptr(bounds), C.byref(h),
                              _stream(stream)), "gs_adam_q16")
+
+
+def quantize_sh(sh, sh_degree: int, bits: int, stream=None) -> tuple:
+    """gs_quantize_sh: (codes uint8 / int16-typed uint16 [n][K][3], bounds float32 [nb][2])."""
+    n = sh.shape[0]
+    K = (sh_degree + 1) ** 2
+    units = n * K * 3
+    codes = torch.empty((n, K, 3), dtype=torch.uint8 if bits == 8 else torch.int16, device=sh.device)
+    bounds = torch.empty(((units + 255) // 256, 2), dtype=torch.float32, device=sh.device)
+    _check(lib().gs_quantize_sh(n, _ptr(sh), int(sh_degree), int(bits), _ptr(codes), _ptr(bounds), _stream(stream)),
+           "gs_quantize_sh")
+    return codes, bounds
+
+
+def project_qsh(means, scales, quats, opacities, codes, bounds, bits: int, sh_degree: int, cam,
+                out: dict | None = None, stream=None) -> dict:
+    """gs_project_qsh into ``out`` (allocated if None)."""
+    n = means.shape[0]
+    if out is None:
+        out = alloc_projected(n, means.device)
+    camc = camera_struct(cam)
+    _check(lib().gs_project_qsh(n, _ptr(means), _ptr(scales), _ptr(quats), _ptr(opacities), _ptr(codes),
+                                _ptr(bounds), int(bits), int(sh_degree), C.byref(camc), projected_struct(out),
+                                _stream(stream)), "gs_project_qsh")
+    return out
