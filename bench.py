@@ -230,6 +230,8 @@ def main():
 
     log("adam")
     adam = adam_measure(raster, dev, with_oracle=not args.no_cpu_baseline)
+    log("quantised SH projection")
+    qsh = qsh_measure(raster, means, scales, quats, opac, sh, sc.sh_degree, cams, rz.proj)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -262,6 +264,7 @@ def main():
         "cpu_baseline": cpu,
         "densify": dens,
         "adam": adam,
+        "project_qsh": qsh,
     }
     print(json.dumps(line), flush=True)
 
@@ -348,6 +351,41 @@ def densify_measure(raster, means, scales, quats, opac, sh, L, accum, denom, str
                            split_shrink=1.6, min_opacity=0.005, max_scale=0.0)
         res["cpu_oracle_ms"] = round(1e3 * (_t.perf_counter() - t0), 1)
         res["matches_oracle_count"] = bool(o["n_out"] == m)
+    return res
+
+
+def qsh_measure(raster, means, scales, quats, opac, sh, L, cams, proj, reps=3):
+    """gs_project against gs_project_qsh (q16, q8) on the bench scene and cameras, each timed
+    with the library's kernel timer over `reps` passes of the 8 cameras; the rate is the
+    algorithmic bytes (inputs with the SH at their stored width, plus the bounds, and the
+    97 B of outputs) over the kernel time."""
+    import torch
+
+    N = int(means.shape[0])
+    K = (L + 1) ** 2
+    res = {}
+    for bits in (0, 16, 8):
+        if bits:
+            codes, bounds = raster.quantize_sh(sh, L, bits)
+        torch.cuda.synchronize()
+        assert raster.kernel_timer_start("k_project") == raster.GS_OK
+        for _ in range(reps):
+            for cam in cams:
+                if bits:
+                    raster.project_qsh(means, scales, quats, opac, codes, bounds, bits, L, cam, proj)
+                else:
+                    raster.project(means, scales, quats, opac, sh, L, cam, proj)
+        torch.cuda.synchronize()
+        st, launches, kms = raster.kernel_timer_stop()
+        assert st == raster.GS_OK and launches == reps * len(cams)
+        ms = kms / launches
+        sh_bytes = 12 * K if not bits else 3 * K * bits // 8 + 8 * (3 * K) / 256
+        nbytes = N * (12 + 12 + 16 + 4 + sh_bytes + 48 + 4 + 8 + 4 + 1 + 32)
+        ach = nbytes / (ms * 1e-3) / 1e9
+        res["fp32" if not bits else f"q{bits}"] = {
+            "ms": round(ms, 4), "sh_bytes_per_gaussian": round(sh_bytes, 2),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4)}}
     return res
 
 
