@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to aim for")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration report")
+    ap.add_argument("--frames", type=int, default=20, help="timed frames per camera in the per-configuration report")
+    ap.add_argument("--oracle-10m", action="store_true",
+                    help="also time the oracle on the 10M-Gaussian configuration (about a minute per thread count)")
     ap.add_argument("--profile", action="store_true",
                     help="profiler run: no CPU baseline, plus a 1 GiB device copy that calibrates HBM counters")
     return ap.parse_args()
@@ -176,33 +180,16 @@ def main():
     # algorithmic work per launch (camera-averaged) for the roofline
     P_mean = float(np.mean(pairs))
     K = (sc.sh_degree + 1) ** 2
-    visited, contrib = [], []
-    for k, cam in enumerate(cams):
-        rg = ranges[k]
-        lens = (rg[:, 1] - rg[:, 0]).cpu().numpy()
-        tl = lens.reshape(cam.tiles_y, cam.tiles_x).repeat(16, 0).repeat(16, 1)[:H, :W]
-        nc = ncon[k].cpu().numpy().astype(np.int64)
-        stopped = finalT[k].cpu().numpy() < TMIN
-        visited.append(float(np.where(stopped, nc, tl).sum()))
-        contrib.append(float(nc.sum()))
-    evals = float(np.mean(visited))
-    walk = float(np.mean(contrib))
-    V = float(N)  # visible Gaussians bound the per-Gaussian binning work
-    # digit passes left to gs_sort_keys after the emission's own pass over the tile's low byte
-    tile_bits = max(1, math.ceil(math.log2(tiles)))
-    passes = max(0, math.ceil((32 + tile_bits - 40) / 8))
+    counts = [work_counts(cam, ranges[k], ncon[k], finalT[k]) for k, cam in enumerate(cams)]
+    evals = float(np.mean([c[0] for c in counts]))
+    walk = float(np.mean([c[1] for c in counts]))
+    work = stage_work(N, K, P_mean, tiles, evals, walk, W * H, with_bwd=True)
     algo = {
-        # inputs; record, depth, rect, count, clamp byte and the 32-byte tile record
-        "project": ("hbm", N * (12 + 12 + 16 + 4 + 12 * K) + N * (48 + 4 + 8 + 4 + 1 + 32)),
-        # count (4 B/G), compaction (8 read + 8 written per visible), depth sort (4 passes of
-        # 16 B per visible + 4 B histogram), the depth-ordered gather (20 B per visible),
-        # pairs written (12 B each)
-        "bin": ("hbm", 4 * N + 16 * V + (4 * 16 + 4) * V + 20 * V + 12 * P_mean),
-        # histogram (8 B/pair), 24 B/pair per pass, ranges (8 B/pair: the result is read
-        # where the last pass left it) + 16 B/tile
-        "sort": ("hbm", (8 + 24 * passes + 8) * P_mean + 16 * tiles),
-        "render_fwd": ("alu", OPS_PER_EVAL_FWD * evals),
-        "render_bwd": ("alu", OPS_PER_EVAL_BWD * walk),
+        "project": ("hbm", work["project"][0]),
+        "bin": ("hbm", work["bin"][0]),
+        "sort": ("hbm", work["sort"][0]),
+        "render_fwd": ("alu", work["render_fwd"][1]),
+        "render_bwd": ("alu", work["render_bwd"][1]),
     }
     avg = {s: float(np.mean(times[s])) for s in stages if times[s]}
 
@@ -235,7 +222,15 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        log("float64 oracle on the host cores")
         cpu = cpu_baseline(sc, cams, [d.cpu().numpy() for d in dLs], args.cpu_budget)
+
+    configs = None
+    if not args.profile and not args.no_configs:
+        del rz, grads, accum, denom, images, finalT, ncon, ranges, orders, dLs
+        del means, scales, quats, opac, sh
+        torch.cuda.empty_cache()
+        configs = config_report(args, raster, scenes, dev, sc, cams)
 
     line = {
         "metric": "frames/s + Mpixels/s fwd(+bwd) at 1M SH3 Gaussians 1080p; % HBM/VALU peak",
@@ -265,8 +260,257 @@ def main():
         "densify": dens,
         "adam": adam,
         "project_qsh": qsh,
+        "configs": configs,
     }
     print(json.dumps(line), flush=True)
+
+
+def work_counts(cam, ranges, n_contrib, final_T):
+    """(evaluations, contributor walk) of one frame: a pixel evaluates its tile's list up to
+    its stop (the whole list when it never stops); the reverse walk visits n_contrib entries."""
+    H, W = cam.height, cam.width
+    lens = (ranges[:, 1] - ranges[:, 0]).cpu().numpy()
+    tl = lens.reshape(cam.tiles_y, cam.tiles_x).repeat(16, 0).repeat(16, 1)[:H, :W]
+    nc = n_contrib.cpu().numpy().astype(np.int64)
+    stopped = final_T.cpu().numpy() < TMIN
+    return float(np.where(stopped, nc, tl).sum()), float(nc.sum())
+
+
+def stage_work(N, K, P, tiles, evals, walk, pixels, with_bwd):
+    """Algorithmic work per stage of one frame: {stage: (HBM bytes, VALU lane-op slots)}.
+    N Gaussians with K SH coefficients per channel, P pairs, `tiles` tiles, `pixels` pixels;
+    `evals` and `walk` as in work_counts.  Every Gaussian is counted as visible where that
+    bounds the binning work."""
+    V = float(N)
+    # digit passes left to gs_sort_keys after the emission's own pass over the tile's low byte
+    tile_bits = max(1, math.ceil(math.log2(max(tiles, 2))))
+    passes = max(0, math.ceil((32 + tile_bits - 40) / 8))
+    w = {
+        # inputs; record, depth, rect, count, clamp byte and the 32-byte tile record
+        "project": (N * (12 + 12 + 16 + 4 + 12 * K) + N * (48 + 4 + 8 + 4 + 1 + 32), 0.0),
+        # count (4 B/G), compaction (8 read + 8 written per visible), depth sort (4 passes of
+        # 16 B per visible + 4 B histogram), the depth-ordered gather (20 B per visible),
+        # pairs written (12 B each)
+        "bin": (4 * N + 16 * V + (4 * 16 + 4) * V + 20 * V + 12 * P, 0.0),
+        # histogram (8 B/pair), 24 B/pair per pass, ranges (8 B/pair) + 16 B/tile
+        "sort": ((8 + 24 * passes + 8) * P + 16 * tiles, 0.0),
+        # list entries read once per tile; colour, transmittance and count written per pixel
+        "render_fwd": (4 * P + 20 * pixels, OPS_PER_EVAL_FWD * evals),
+    }
+    if with_bwd:
+        # upstream gradient, transmittance and count read per pixel; list entries once per
+        # tile; the screen-space gradient block cleared (40 B/G)
+        w["render_bwd"] = (20 * pixels + 4 * P + 40 * N, OPS_PER_EVAL_BWD * walk)
+        # inputs, count, clamp byte and screen-space gradient read; parameter gradients
+        # written; densification statistics read and written
+        w["project_bwd"] = (N * (12 + 12 + 16 + 12 * K + 4 + 1 + 40) + N * (12 + 12 + 16 + 12 * K) + 2 * 12 * N, 0.0)
+    return w
+
+
+def frame_bound_ms(work, hbm_gbs):
+    """Lower bound of a frame: each stage takes at least the longer of its bytes at `hbm_gbs`
+    and its lane-op slots at the VALU peak; the stages run one after another."""
+    return 1e3 * sum(max(b / (hbm_gbs * 1e9), a / (VALU_PEAK_TOPS * 1e12)) for b, a in work.values())
+
+
+def copy_bandwidth(dev, reps=5):
+    """GB/s of a 1 GiB device-to-device copy (1 GiB read + 1 GiB written), median of `reps`."""
+    import torch
+
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * (1 << 30) / (float(np.median(ts)) * 1e-3) / 1e9
+
+
+def config_frames(raster, scenes, dev, sc, cams, dLs, nframes, warm=3):
+    """Per camera: the median wall time of `nframes` frames, each project -> bin (with the
+    pair-count read-back) -> sort -> composite (-> backward when `dLs` is given), bracketed
+    by device synchronisations; plus the frame's pairs and work counts."""
+    import torch
+
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    means, scales, quats, opac, sh = raster.scene_to_device(sc, dev)
+    rz = raster.Rasterizer(means, scales, quats, opac, sh, sc.sh_degree)
+    N, L = sc.n, sc.sh_degree
+    with_bwd = dLs is not None
+    grads = raster.alloc_grads(N, L, dev) if with_bwd else None
+    accum = torch.zeros((N, 2), dtype=torch.float32, device=dev) if with_bwd else None
+    denom = torch.zeros(N, dtype=torch.int32, device=dev) if with_bwd else None
+    out = []
+    for k, cam in enumerate(cams):
+        rz.forward(cam)  # sizes the pair buffers
+        H, W, tiles = cam.height, cam.width, cam.num_tiles
+        rg = torch.empty((tiles, 2), dtype=torch.int64, device=dev)
+        order = torch.empty(tiles, dtype=torch.int32, device=dev)
+        img = torch.empty((3, H, W), dtype=torch.float32, device=dev)
+        fT = torch.empty((H, W), dtype=torch.float32, device=dev)
+        nc = torch.empty((H, W), dtype=torch.int32, device=dev)
+        dL = torch.from_numpy(dLs[k]).to(dev) if with_bwd else None
+        ts, Ps = [], []
+        for f in range(warm + nframes):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            raster.project(means, scales, quats, opac, sh, L, cam, rz.proj)
+            st, P = raster.bin_tiles(rz.proj, cam, rz.keys, rz.vals, rz.workspace)
+            assert st == raster.GS_OK
+            in_tmp = raster.sort_keys(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, rg, rz.workspace, order,
+                                      leave_in_tmp=True)
+            sv = rz.vals_tmp if in_tmp else rz.vals
+            raster.render_fwd(rz.proj, sv, rg, cam, (0.0, 0.0, 0.0), img, fT, nc, order)
+            if with_bwd:
+                raster.render_bwd(means, scales, quats, opac, sh, L, cam, rz.proj, sv, rg, (0.0, 0.0, 0.0), fT, nc,
+                                  dL, grads, accum, denom, order)
+            torch.cuda.synchronize()
+            if f >= warm:
+                ts.append(time.perf_counter() - t0)
+                Ps.append(P)
+        evals, walk = work_counts(cam, rg, nc, fT)
+        out.append(dict(ms=1e3 * float(np.median(ts)), P=int(Ps[-1]), evals=evals, walk=walk, cam=cam))
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    del rz, means, scales, quats, opac, sh, grads, accum, denom
+    torch.cuda.empty_cache()
+    return out, peak
+
+
+def oracle_frame(sc, cam, dL, budget, round_tiles=100):
+    """Seconds of one frame of the float64 oracle: projection, binning, sort and ranges on all
+    Gaussians (and the projection backward when `dL` is given), then compositing (forward, and
+    backward with `dL`) on rounds of `round_tiles` random tiles until `budget` seconds have
+    gone into the frame or every tile is done; the compositing time is scaled to the frame."""
+    import oracle
+
+    W, H = cam.width, cam.height
+    t0 = time.perf_counter()
+    proj = oracle.project(sc, cam)
+    keys, vals = oracle.emit_projected(proj, cam.tiles_x)
+    skeys, svals = oracle.sort_pairs(keys, vals)
+    ranges = oracle.tile_ranges(skeys, cam.num_tiles)
+    rec = oracle.records(proj)
+    if dL is not None:
+        oracle.project_bwd(sc, cam, np.zeros((sc.n, 10)))  # its cost does not depend on the values
+        dL = dL.astype(np.float64)
+    t_fixed = time.perf_counter() - t0
+    tiles = np.random.default_rng(0).permutation(cam.num_tiles)
+    done, npix, t_sample = 0, 0, 0.0
+    while done < tiles.size and (done == 0 or time.perf_counter() - t0 < budget):
+        pix = []
+        for t in tiles[done:done + round_tiles]:
+            tx, ty = t % cam.tiles_x, t // cam.tiles_x
+            ys = np.arange(ty * 16, min(ty * 16 + 16, H))
+            xs = np.arange(tx * 16, min(tx * 16 + 16, W))
+            pix.append((ys[:, None] * W + xs[None, :]).reshape(-1))
+        pix = np.concatenate(pix)
+        t1 = time.perf_counter()
+        oracle.render_pixels(W, H, (0, 0, 0), rec, svals, ranges, pix)
+        if dL is not None:
+            oracle.render_bwd(W, H, (0, 0, 0), rec, svals, ranges, sc.n, dL, pix=pix)
+        t_sample += time.perf_counter() - t1
+        done = min(done + round_tiles, tiles.size)
+        npix += pix.shape[0]
+    return t_fixed + t_sample * (W * H / npix), f"{done}/{tiles.size} tiles"
+
+
+def host_cpu():
+    """(logical CPUs usable by this process, CPU model name)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return usable, model
+
+
+def config_report(args, raster, scenes, dev, sc3, cams3):
+    """frames/s and Mpixels/s of every configuration (median of `--frames` frames per camera,
+    each project -> bin with the P read-back -> sort -> composite; configuration 5 adds the
+    backward), with the whole-frame roofline fraction against the spec peaks and against the
+    copy bandwidth measured here, and the float64 oracle's seconds per frame with every host
+    thread and with one."""
+    import torch
+
+    import oracle
+
+    copy_gbs = copy_bandwidth(dev)
+    threads = oracle.num_threads()
+    usable, model = host_cpu()
+    specs = [("tiny_1k_sh0_64", False), ("spheres_100k_sh3_800", False), ("aniso_1m_sh3_1080p_8cam", False),
+             ("aniso_10m_sh3_1080p", False), ("aniso_1m_sh3_720p_bwd", True)]
+    rep = {"copy_gbs": round(copy_gbs, 1), "frames_per_camera": args.frames,
+           "timing": "median wall time per frame between device synchronisations, pair-count read-back included",
+           "roofline": "sum over stages of max(HBM bytes / rate, VALU lane-op slots / 39.3 T/s) / measured time",
+           "oracle_threads": threads, "host_cpus": usable, "host_cpu_model": model, "per_config": {}}
+    for name, with_bwd in specs:
+        log(f"configuration {name}")
+        if name == "aniso_1m_sh3_1080p_8cam":
+            sc, cams, extra = sc3, cams3, {}
+        else:
+            sc, cams, extra = scenes.workload(name)
+        dLs = None
+        if with_bwd:
+            # upstream gradient sign(render - target), from a forward pass of the GPU path
+            means, scales, quats, opac, sh = raster.scene_to_device(sc, dev)
+            rz = raster.Rasterizer(means, scales, quats, opac, sh, sc.sh_degree)
+            img = rz.forward(cams[0])["image"]
+            dLs = [torch.sign(img - torch.from_numpy(extra["target"]).to(dev)).contiguous().cpu().numpy()]
+            del rz, means, scales, quats, opac, sh, img
+            torch.cuda.empty_cache()
+        per_cam, peak = config_frames(raster, scenes, dev, sc, cams, dLs, args.frames)
+        K = (sc.sh_degree + 1) ** 2
+        cams_out = []
+        for c in per_cam:
+            cam = c["cam"]
+            work = stage_work(sc.n, K, c["P"], cam.num_tiles, c["evals"], c["walk"], cam.width * cam.height, with_bwd)
+            fps = 1e3 / c["ms"]
+            cams_out.append({"ms": round(c["ms"], 4), "frames_per_s": round(fps, 1),
+                             "mpixels_per_s": round(fps * cam.width * cam.height / 1e6, 1), "pairs": c["P"],
+                             "frac_spec": round(frame_bound_ms(work, HBM_PEAK_GBS) / c["ms"], 4),
+                             "frac_copy": round(frame_bound_ms(work, copy_gbs) / c["ms"], 4)})
+        cam = cams[0]
+        mean_ms = float(np.mean([c["ms"] for c in cams_out]))
+        entry = {"gaussians": sc.n, "sh_degree": sc.sh_degree, "width": cam.width, "height": cam.height,
+                 "step": "forward+backward" if with_bwd else "forward", "frames_per_s": round(1e3 / mean_ms, 1),
+                 "mpixels_per_s": round(1e3 / mean_ms * cam.width * cam.height / 1e6, 1),
+                 "frac_spec": round(float(np.mean([c["frac_spec"] for c in cams_out])), 4),
+                 "frac_copy": round(float(np.mean([c["frac_copy"] for c in cams_out])), 4),
+                 "pairs": int(np.mean([c["pairs"] for c in cams_out])), "peak_alloc_bytes": int(peak)}
+        if len(cams_out) > 1:
+            entry["cameras"] = cams_out
+        # the oracle on the first camera: every tile for the small scenes, sampled tiles beyond
+        big = name == "aniso_10m_sh3_1080p"
+        if not args.no_cpu_baseline and (not big or args.oracle_10m):
+            orc = {}
+            for th in (threads, 1):
+                oracle.set_threads(th)
+                secs, desc = oracle_frame(sc, cam, dLs[0] if with_bwd else None, budget=8.0)
+                orc[f"{th}_threads"] = {"s_per_frame": round(secs, 3), "tiles": desc,
+                                        "gpu_speedup": round(secs * 1e3 / mean_ms, 1)}
+            oracle.set_threads(threads)
+            entry["oracle"] = orc
+        elif big:
+            entry["oracle"] = "not timed by default (--oracle-10m)"
+        rep["per_config"][name] = entry
+        del sc
+    return rep
 
 
 # HBM bytes per launch of k_render_bwd on this workload (camera average), from two rocprofv3
@@ -448,36 +692,12 @@ def cpu_baseline(sc, cams, dLs, budget):
     t_start = time.perf_counter()
     per_frame, desc = [], []
     for cam, dL in zip(cams, dLs):
-        if per_frame and time.perf_counter() - t_start >= budget:
+        left = budget - (time.perf_counter() - t_start)
+        if per_frame and left <= 0:
             break
-        W, H = cam.width, cam.height
-        dL = dL.astype(np.float64)
-        t0 = time.perf_counter()
-        proj = oracle.project(sc, cam)
-        keys, vals = oracle.emit_projected(proj, cam.tiles_x)
-        skeys, svals = oracle.sort_pairs(keys, vals)
-        ranges = oracle.tile_ranges(skeys, cam.num_tiles)
-        rec = oracle.records(proj)
-        oracle.project_bwd(sc, cam, np.zeros((sc.n, 10)))  # its cost does not depend on the values
-        t_fixed = time.perf_counter() - t0
-        tiles = np.random.default_rng(0).permutation(cam.num_tiles)
-        done, npix, t_sample = 0, 0, 0.0
-        while done < tiles.size and (done == 0 or time.perf_counter() - t_start < budget):
-            pix = []
-            for t in tiles[done:done + 400]:
-                tx, ty = t % cam.tiles_x, t // cam.tiles_x
-                ys = np.arange(ty * 16, min(ty * 16 + 16, H))
-                xs = np.arange(tx * 16, min(tx * 16 + 16, W))
-                pix.append((ys[:, None] * W + xs[None, :]).reshape(-1))
-            pix = np.concatenate(pix)
-            t1 = time.perf_counter()
-            oracle.render_pixels(W, H, (0, 0, 0), rec, svals, ranges, pix)
-            oracle.render_bwd(W, H, (0, 0, 0), rec, svals, ranges, sc.n, dL, pix=pix)
-            t_sample += time.perf_counter() - t1
-            done = min(done + 400, tiles.size)
-            npix += pix.shape[0]
-        per_frame.append(t_fixed + t_sample * (W * H / npix))
-        desc.append(f"{done}/{tiles.size} tiles")
+        secs, d = oracle_frame(sc, cam, dL, budget=left, round_tiles=400)
+        per_frame.append(secs)
+        desc.append(d)
     cam = cams[0]
     return {"value": round(len(per_frame) / sum(per_frame), 5), "unit": "frames/s", "cores": oracle.num_threads(),
             "kind": "oracle",

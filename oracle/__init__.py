@@ -263,6 +263,11 @@ def num_threads() -> int:
     return int(_load().orc_num_threads())
 
 
+def set_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops from now on."""
+    _load().orc_set_threads(C.c_int(int(n)))
+
+
 def render_bwd(W: int, H: int, bg, rec, vals, ranges, n: int, dL_dimg, with_abs: bool = False, pix=None):
     """grad_screen (n, 10): dL/d(u, v, A, B, C, opacity, r, g, b), sum_p ||dL_p/d(u, v)||.
 

@@ -43,6 +43,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Thread count of the OpenMP loops from now on (timing the oracle single-threaded). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 #define ORC_AMAX ((double)0.99f)              /* alpha clamp                         */
 #define ORC_AMIN ((double)(float)(1.0 / 255.0)) /* skip contributions below this alpha */
 #define ORC_TMIN ((double)1e-4f)              /* stop a pixel below this transmittance */
