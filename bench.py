@@ -115,11 +115,11 @@ def main():
         mark(0)
         raster.project(means, scales, quats, opac, sh, sc.sh_degree, cam, rz.proj)
         mark(1)
-        st, P = raster.bin_tiles(rz.proj, cam, rz.keys, rz.vals, rz.workspace)
+        st, P = raster.bin_tiles(rz.proj, cam, rz.keys, rz.vals, rz.workspace, digit_counts=rz.digit_counts)
         assert st == raster.GS_OK
         mark(2)
         in_tmp = raster.sort_keys(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, ranges[k], rz.workspace,
-                                  orders[k], leave_in_tmp=True)
+                                  orders[k], leave_in_tmp=True, digit_counts=rz.digit_counts)
         sv = rz.vals_tmp if in_tmp else rz.vals
         mark(3)
         raster.render_fwd(rz.proj, sv, ranges[k], cam, (0.0, 0.0, 0.0), images[k], finalT[k], ncon[k], orders[k])
@@ -292,8 +292,9 @@ def stage_work(N, K, P, tiles, evals, walk, pixels, with_bwd):
         # 16 B per visible + 4 B histogram), the depth-ordered gather (20 B per visible),
         # pairs written (12 B each)
         "bin": (4 * N + 16 * V + (4 * 16 + 4) * V + 20 * V + 12 * P, 0.0),
-        # histogram (8 B/pair), 24 B/pair per pass, ranges (8 B/pair) + 16 B/tile
-        "sort": ((8 + 24 * passes + 8) * P + 16 * tiles, 0.0),
+        # 24 B/pair per pass, ranges (8 B/pair) + 16 B/tile (the digit counts come from the
+        # binning, so there is no counting read)
+        "sort": ((24 * passes + 8) * P + 16 * tiles, 0.0),
         # list entries read once per tile; colour, transmittance and count written per pixel
         "render_fwd": (4 * P + 20 * pixels, OPS_PER_EVAL_FWD * evals),
     }
@@ -363,10 +364,10 @@ def config_frames(raster, scenes, dev, sc, cams, dLs, nframes, warm=3):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             raster.project(means, scales, quats, opac, sh, L, cam, rz.proj)
-            st, P = raster.bin_tiles(rz.proj, cam, rz.keys, rz.vals, rz.workspace)
+            st, P = raster.bin_tiles(rz.proj, cam, rz.keys, rz.vals, rz.workspace, digit_counts=rz.digit_counts)
             assert st == raster.GS_OK
             in_tmp = raster.sort_keys(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, rg, rz.workspace, order,
-                                      leave_in_tmp=True)
+                                      leave_in_tmp=True, digit_counts=rz.digit_counts)
             sv = rz.vals_tmp if in_tmp else rz.vals
             raster.render_fwd(rz.proj, sv, rg, cam, (0.0, 0.0, 0.0), img, fT, nc, order)
             if with_bwd:

@@ -54,6 +54,7 @@ enum {
 #define GS_TILE 16       /* tiles are 16x16 pixels                                          */
 #define GS_REC_FLOATS 12 /* floats per projected render record                            */
 #define GS_GRAD_SCREEN 10 /* floats per Gaussian in the screen-space gradient block        */
+#define GS_TILE_DIGIT_COUNTS 512 /* uint64 words of gs_bin_tiles' tile-digit counts (2 x 256) */
 
 /* Pinhole camera, OpenCV frame: x right, y down, z forward.  x_cam = R x_world + t with
  * R row major.  Pixel (i, j) has its centre at (i + 0.5, j + 0.5).  Gaussians with
@@ -185,11 +186,17 @@ size_t gs_workspace_bytes(int64_t n, int64_t pair_capacity, int32_t num_tiles);
  * is computed.  If P > capacity,
  * returns GS_ERR_CAPACITY with *n_pairs = P and writes no pairs.  The workspace must hold
  * gs_workspace_bytes(n, P, num_tiles) bytes (checked before and after P is known).
+ * tile_digit_counts [device, optional, GS_TILE_DIGIT_COUNTS uint64]: when the call writes
+ * pairs, receives [p][d] = the number of pairs whose tile id has bits [8 + 8p, 16 + 8p)
+ * equal to d, for the digit passes gs_sort_keys will make (rows it will not use are 0),
+ * counted by the expansion's counting pass.  Passed to gs_sort_keys(sorted_low_bits
+ * = 40) with the same pairs, it replaces that call's counting read of every key.
  * Errors: INVALID_ARG, WORKSPACE, CAPACITY, OVERFLOW, HIP.
  */
 gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint64_t* keys,
-                       uint32_t* vals, int64_t capacity, int64_t* n_pairs, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       uint32_t* vals, int64_t capacity, int64_t* n_pairs,
+                       uint64_t* tile_digit_counts, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /*
  * gs_sort_keys -- stable LSD radix sort of (keys, vals) over key bits [sorted_low_bits,
@@ -207,12 +214,17 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
  * ([0, 0) for an empty tile) and, when tile_order is non-NULL, tile_order[num_tiles] =
  * every tile id once, longest lists first (a schedule for the compositing calls; it does
  * not change their results).  Keys must have tile_id < num_tiles.
+ * digit_counts [device, optional]: [p][256] counts of each pass's digit (key bits
+ * [sorted_low_bits + 8p, + 8)) over the keys, one row per pass; NULL = the call counts
+ * them with one read of the keys.  gs_bin_tiles' tile_digit_counts are exactly this for
+ * its pairs and sorted_low_bits = 40.  Counts that do not match the keys give an
+ * unspecified order, but every write stays inside the n_pairs slots.
  * Errors: INVALID_ARG, WORKSPACE, OVERFLOW, HIP.
  */
 gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys,
                        uint32_t* vals, uint64_t* keys_tmp, uint32_t* vals_tmp,
-                       int64_t* tile_ranges, int32_t* tile_order, int32_t* result_in_tmp,
-                       void* workspace, size_t workspace_bytes, void* stream);
+                       int64_t* tile_ranges, int32_t* tile_order, const uint64_t* digit_counts,
+                       int32_t* result_in_tmp, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gs_render_fwd -- composite every pixel front to back over its tile's sorted list
@@ -223,7 +235,9 @@ gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bi
  *   image = C + T * bg.
  *  image[3][H][W] (planar), final_T[H][W], n_contrib[H][W] = 1 + the tile-list position
  *  of the last contributor (0 if none), which gs_render_bwd needs.  tile_order (nullable)
- *  is the schedule written by gs_sort_keys; NULL processes tiles in id order.
+ *  is the schedule written by gs_sort_keys; NULL processes tiles in id order.  Ids in the
+ *  lists are clamped to n - 1 (as in gs_render_bwd): lists holding ids >= n give
+ *  unspecified pixels but no read outside the records.
  * Errors: INVALID_ARG, HIP.
  */
 gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_vals,

@@ -28,14 +28,17 @@ def test_empty_scene():
     assert st == raster.GS_OK and P == 0
     keys = torch.empty(1, dtype=torch.int64, device=dev)
     vals = torch.empty(1, dtype=torch.int32, device=dev)
+    dc = torch.full((raster.TILE_DIGIT_COUNTS,), -1, dtype=torch.int64, device=dev)
+    st, P = raster.bin_tiles(proj, cam, keys, vals, ws, digit_counts=dc)
+    assert st == raster.GS_OK and P == 0
     ranges = torch.full((tiles, 2), 7, dtype=torch.int64, device=dev)
-    raster.sort_keys(0, tiles, keys, vals, keys.clone(), vals.clone(), ranges, ws)
+    raster.sort_keys(0, tiles, keys, vals, keys.clone(), vals.clone(), ranges, ws, digit_counts=dc)
     image = torch.empty((3, cam.height, cam.width), device=dev)
     T = torch.empty((cam.height, cam.width), device=dev)
     nc = torch.empty((cam.height, cam.width), dtype=torch.int32, device=dev)
     raster.render_fwd(proj, vals, ranges, cam, (0.1, 0.2, 0.3), image, T, nc)
     torch.cuda.synchronize()
-    assert torch.all(ranges == 0)
+    assert torch.all(ranges == 0) and torch.all(dc == 0)
     assert torch.allclose(image[0], torch.full_like(image[0], 0.1)) and torch.all(T == 1) and torch.all(nc == 0)
 
 
@@ -110,13 +113,13 @@ def test_pageable_count_word_gives_the_same_pairs():
     camc = raster.camera_struct(cam)
     L = raster.lib()
     assert L.gs_bin_tiles(sc.n, raster.projected_struct(proj), C.byref(camc), k2.data_ptr(), v2.data_ptr(), P,
-                          C.byref(word), ws.data_ptr(), ws.numel(), None) == raster.GS_OK
+                          C.byref(word), None, ws.data_ptr(), ws.numel(), None) == raster.GS_OK
     torch.cuda.synchronize()
     assert word.value == P
     assert torch.equal(k1, k2) and torch.equal(v1, v2)
     word.value = 0
     assert L.gs_bin_tiles(sc.n, raster.projected_struct(proj), C.byref(camc), k2.data_ptr(), v2.data_ptr(), P - 1,
-                          C.byref(word), ws.data_ptr(), ws.numel(), None) == raster.GS_ERR_CAPACITY
+                          C.byref(word), None, ws.data_ptr(), ws.numel(), None) == raster.GS_ERR_CAPACITY
     assert word.value == P
     st, P3 = raster.bin_tiles(proj, cam, k2[:P - 1], v2[:P - 1], ws)
     assert st == raster.GS_ERR_CAPACITY and P3 == P
@@ -135,7 +138,7 @@ def test_invalid_arguments_are_rejected_before_launch():
     bad.near_z = 0.0
     assert L.gs_project(0, None, None, None, None, None, 0, C.byref(bad), proj, None) == raster.GS_ERR_INVALID_ARG
     P = C.c_int64(0)
-    assert L.gs_bin_tiles(0, proj, C.byref(cam), None, None, 0, C.byref(P), None, 0, None) == raster.GS_ERR_WORKSPACE
+    assert L.gs_bin_tiles(0, proj, C.byref(cam), None, None, 0, C.byref(P), None, None, 0, None) == raster.GS_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("leave_in_tmp", [False, True])

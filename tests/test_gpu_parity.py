@@ -115,3 +115,29 @@ def test_background_and_ragged_image():
     e2e = oracle.end_to_end(sc, cam, bg)
     compare_pixels(g["image"].reshape(3, -1).T, g["final_T"].reshape(-1),
                    g["n_contrib"].reshape(-1).astype(np.int64), e2e["render"], "ragged end-to-end")
+
+
+def test_sort_counts_its_own_digits_the_same(spheres):
+    """gs_sort_keys without the binning's tile-digit counts (its own counting read) sorts to
+    the same pairs and ranges as with them (the longest-first schedule may order tiles of
+    one length bucket differently from run to run; the image does not depend on it)."""
+    sc, cam = spheres
+    a = gpu_stages(sc, cam, keep_unsorted=False, digit_counts=True)
+    b = gpu_stages(sc, cam, keep_unsorted=False, digit_counts=False)
+    for k in ("keys", "vals", "ranges", "image"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_large_image_two_tile_digit_passes():
+    """4200x4150 pixels = 263x260 tiles: tile ids take 17 bits, so the pair sort makes two
+    digit passes above the low byte and the binning counts both digits.  Large footprints
+    (many Gaussians span more than 8 tile rows) take the whole-rectangle path."""
+    sc, _ = scenes.tiny_scene(11, 2000)
+    cam = scenes.Camera(np.eye(3, dtype=np.float32), np.zeros(3, np.float32), 4400.0, 4400.0, 2100.0, 2075.0,
+                        4200, 4150, 0.2)
+    assert cam.num_tiles > 65536
+    g = gpu_stages(sc, cam)
+    say(f"large image: P={g['P']}, pass-1 digits {int((g['digit_counts'][1] > 0).sum())}")
+    assert g["digit_counts"][1][1] > 0  # pairs with tile ids >= 65536 exist
+    check_projection(sc, cam, g, "large image")
+    check_binning(cam, g, "large image")

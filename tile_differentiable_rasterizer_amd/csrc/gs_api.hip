@@ -19,13 +19,14 @@ hipError_t launch_project_bwd(int64_t n, const float* means, const float* scales
 size_t bin_workspace_bytes(int64_t n, int64_t n_pairs);
 hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, void* ws, hipStream_t s);
 uint64_t* bin_totals_ptr(int64_t n, void* ws);
-hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, void* ws, hipStream_t s);
-hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int tiles_x, void* ws, uint64_t* keys,
-                           uint32_t* vals, hipStream_t s);
+hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, uint64_t* digit_counts, void* ws, hipStream_t s);
+hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int tiles_x, int tile_bits,
+                           uint64_t* digit_counts, void* ws, uint64_t* keys, uint32_t* vals, hipStream_t s);
 size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_bits);
+int sort_significant_bits(int64_t num_tiles);
 hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
                        uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits,
-                       int32_t* result_in_tmp, void* ws, hipStream_t s);
+                       const uint64_t* digit_counts, int32_t* result_in_tmp, void* ws, hipStream_t s);
 hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
 size_t densify_workspace_bytes(int64_t n);
 hipError_t launch_quantize_sh(int64_t U, const float* sh, int bits, void* codes, float* bounds, hipStream_t s);
@@ -41,10 +42,10 @@ hipError_t launch_densify_emit(int64_t n, const float* means, const float* scale
                                const float* opac, const float* sh, int L, const float* accum, const int32_t* denom,
                                const float* normals, const gs_densify_params& q, const void* ws, float* om,
                                float* os, float* oq, float* oo, float* osh, uint32_t* osrc, hipStream_t s);
-hipError_t launch_render_fwd(const gs_projected& proj, const uint32_t* vals, const int64_t* ranges,
+hipError_t launch_render_fwd(const gs_projected& proj, const uint32_t* vals, uint32_t id_max, const int64_t* ranges,
                              const int32_t* order, const DevCamera& cam, const float bg[3], float* image,
                              float* final_T, uint32_t* n_contrib, hipStream_t s);
-hipError_t launch_render_bwd(const gs_projected& proj, const uint32_t* vals, const int64_t* ranges,
+hipError_t launch_render_bwd(const gs_projected& proj, const uint32_t* vals, uint32_t id_max, const int64_t* ranges,
                              const int32_t* order, const DevCamera& cam, const float bg[3], const float* final_T,
                              const uint32_t* n_contrib, const float* dL, float* gscreen, hipStream_t s);
 }  // namespace gs
@@ -254,14 +255,17 @@ static bool host_pinned(const void* p) {
 }
 
 gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint64_t* keys, uint32_t* vals,
-                       int64_t capacity, int64_t* n_pairs, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       int64_t capacity, int64_t* n_pairs, uint64_t* tile_digit_counts, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   if (n < 0 || capacity < 0 || !n_pairs || !camera_ok(cam)) return GS_ERR_INVALID_ARG;
   if (n >= kMaxGaussians || !camera_fits(cam)) return GS_ERR_OVERFLOW;
   if (n > 0 && !projected_ok(proj)) return GS_ERR_INVALID_ARG;
   if (keys && !vals) return GS_ERR_INVALID_ARG;
   if (!workspace || workspace_bytes < bin_workspace_bytes(n, 0)) return GS_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const DevCamera d = dev_camera(cam);
+  const int tile_bits = sort_significant_bits((int64_t)d.tiles_x * d.tiles_y) - 32;
+  uint64_t* dc = keys ? tile_digit_counts : nullptr;
   if (launch_bin_count(n, proj.n_tiles, workspace, s) != hipSuccess) return GS_ERR_HIP;
   const uint64_t* dP = bin_totals_ptr(n, workspace);
   int64_t P = 0;
@@ -272,7 +276,7 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
     if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return GS_ERR_HIP;
     hipError_t e = hipMemcpyAsync(n_pairs, dP, sizeof(int64_t), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipEventRecord(ev, s);
-    if (e == hipSuccess) e = launch_bin_depth(n, proj, workspace, s);
+    if (e == hipSuccess) e = launch_bin_depth(n, proj, dc, workspace, s);
     if (e == hipSuccess) e = hipEventSynchronize(ev);
     (void)hipEventDestroy(ev);
     if (e != hipSuccess) return GS_ERR_HIP;
@@ -286,17 +290,17 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
     P = (int64_t)total;
     *n_pairs = P;
     if (!keys) return GS_OK;
-    if (launch_bin_depth(n, proj, workspace, s) != hipSuccess) return GS_ERR_HIP;
+    if (launch_bin_depth(n, proj, dc, workspace, s) != hipSuccess) return GS_ERR_HIP;
   }
   if (P > capacity) return GS_ERR_CAPACITY;
   if (workspace_bytes < bin_workspace_bytes(n, P)) return GS_ERR_WORKSPACE;
-  const DevCamera d = dev_camera(cam);
-  return hip_status(launch_bin_emit(n, P, proj, d.tiles_x, workspace, keys, vals, s));
+  return hip_status(launch_bin_emit(n, P, proj, d.tiles_x, tile_bits, dc, workspace, keys, vals, s));
 }
 
 gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys, uint32_t* vals,
                        uint64_t* keys_tmp, uint32_t* vals_tmp, int64_t* tile_ranges, int32_t* tile_order,
-                       int32_t* result_in_tmp, void* workspace, size_t workspace_bytes, void* stream) {
+                       const uint64_t* digit_counts, int32_t* result_in_tmp, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   if (n_pairs < 0 || num_tiles < 1 || !tile_ranges || sorted_low_bits < 0 || sorted_low_bits > 64)
     return GS_ERR_INVALID_ARG;
   if (n_pairs > 0 && (!keys || !vals || !keys_tmp || !vals_tmp)) return GS_ERR_INVALID_ARG;
@@ -304,7 +308,8 @@ gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bi
   if (!workspace || workspace_bytes < sort_workspace_bytes(n_pairs, num_tiles, sorted_low_bits))
     return GS_ERR_WORKSPACE;
   return hip_status(launch_sort(n_pairs, num_tiles, keys, vals, keys_tmp, vals_tmp, tile_ranges, tile_order,
-                                sorted_low_bits, result_in_tmp, workspace, static_cast<hipStream_t>(stream)));
+                                sorted_low_bits, digit_counts, result_in_tmp, workspace,
+                                static_cast<hipStream_t>(stream)));
 }
 
 gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_vals, const int64_t* tile_ranges,
@@ -316,7 +321,8 @@ gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_val
   const DevCamera d = dev_camera(cam);
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(timed(kRenderFwd, s, [&] {
-    return launch_render_fwd(proj, sorted_vals, tile_ranges, tile_order, d, bg, image, final_T, n_contrib, s);
+    return launch_render_fwd(proj, sorted_vals, (uint32_t)(n - 1), tile_ranges, tile_order, d, bg, image, final_T,
+                             n_contrib, s);
   }));
 }
 
@@ -339,8 +345,8 @@ gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, cons
   hipError_t e = launch_fill_u32(out.grad_screen, n * GS_GRAD_SCREEN, 0u, s);
   if (e == hipSuccess)
     e = timed(kRenderBwd, s, [&] {
-      return launch_render_bwd(proj, sorted_vals, tile_ranges, tile_order, d, bg, final_T, n_contrib, dL_dimage,
-                               out.grad_screen, s);
+      return launch_render_bwd(proj, sorted_vals, (uint32_t)(n - 1), tile_ranges, tile_order, d, bg, final_T, n_contrib,
+                               dL_dimage, out.grad_screen, s);
     });
   if (e == hipSuccess)
     e = timed(kProjectBwd, s, [&] {

@@ -11,7 +11,7 @@
 // compacted (ballot + popcount per wavefront, in id order) and radix-sorted once by the
 // bit pattern of their fp32 depth (a stable sort, so equal depths stay in id order).
 // Their tiles are then expanded in that order, and the expansion itself performs the
-// first digit pass of the tile sort: a counting pass gives every partition of 2048 pairs
+// first digit pass of the tile sort: a counting pass gives every partition of 1024 pairs
 // its count per value of the tile's low byte, a column scan turns those into offsets, and
 // the scattering pass writes each pair at its place.  The keys leave ordered by their low
 // 40 bits, so the pair sort is left with the tile bits above the low byte: one digit pass
@@ -44,15 +44,17 @@ namespace gs {
 hipError_t radix_sort_u32(int64_t P, const uint64_t* dcount, uint32_t* keys, uint32_t* vals, uint32_t* keys_tmp,
                           uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back);
 const int32_t* radix_result_in_tmp(const void* ws);
+hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
 size_t radix_workspace_bytes(int64_t P, int lo, int hi);
 
 constexpr int kBinBlock = 256;
 constexpr int kBinPer = 4;                      // Gaussians per thread
 constexpr int kBinChunk = kBinBlock * kBinPer;  // Gaussians per workgroup
-constexpr int kEmitPer = 8;                       // pairs per lane in the emission passes
+constexpr int kEmitPer = 4;                       // pairs per lane in the emission passes
 constexpr int kEmitPart = kBinBlock * kEmitPer;  // pairs per emission partition
 constexpr int kDigits = 256;                      // values of the tile's low byte
-constexpr int kCountParts = 4;                    // partitions per counting workgroup
+constexpr int kCountParts = 8;                    // partitions per counting workgroup
+constexpr int kDigitCopies = 16;                  // copies of the tile-digit counts (spreads the atomics)
 
 
 __global__ __launch_bounds__(kBinBlock) void k_count_blocks(int64_t n, const uint32_t* __restrict__ n_tiles,
@@ -127,10 +129,15 @@ __global__ __launch_bounds__(1024) void k_scan_blocks2(int64_t nb, uint64_t* __r
 __global__ __launch_bounds__(kBinBlock) void k_compact(int64_t n, const uint32_t* __restrict__ n_tiles,
                                                        const float* __restrict__ depth,
                                                        const uint64_t* __restrict__ vis_off,
-                                                       uint32_t* __restrict__ dkeys, uint32_t* __restrict__ dvals) {
+                                                       uint32_t* __restrict__ dkeys, uint32_t* __restrict__ dvals,
+                                                       uint64_t* __restrict__ dcopies) {
   __shared__ uint32_t s_w[kBinPer][kBinBlock / kWave];
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  if (dcopies)  // cleared here (spread over the grid), added to by k_emit_count
+    for (int i = (int)blockIdx.x * kBinBlock + tid; i < kDigitCopies * GS_TILE_DIGIT_COUNTS;
+         i += (int)gridDim.x * kBinBlock)
+      dcopies[i] = 0;
   bool vis[kBinPer];
   uint32_t below[kBinPer];
 #pragma unroll
@@ -180,17 +187,33 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __re
   const uint32_t* dbits = tmp ? dk1 : dk0;
   const uint32_t* order = tmp ? dv1 : dv0;
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
+  // every gather in flight before any is used
+  uint32_t id[kBinPer], db[kBinPer];
+  uint4 a[kBinPer], b[kBinPer];
+#pragma unroll
+  for (int j = 0; j < kBinPer; ++j) {
+    const int64_t i = base + j * kBinBlock + threadIdx.x;
+    id[j] = i < v ? order[i] : 0u;
+    db[j] = i < v ? dbits[i] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kBinPer; ++j) {
+    const int64_t i = base + j * kBinBlock + threadIdx.x;
+    a[j] = b[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (i < v) {
+      a[j] = runs[2 * (size_t)id[j]];
+      b[j] = runs[2 * (size_t)id[j] + 1];
+    }
+  }
   uint64_t acc = 0;
 #pragma unroll
   for (int j = 0; j < kBinPer; ++j) {
     const int64_t i = base + j * kBinBlock + threadIdx.x;
     if (i < v) {
-      const uint32_t id = order[i];
-      const uint4 a = runs[2 * (size_t)id], b = runs[2 * (size_t)id + 1];
-      sruns[2 * i] = a;
-      sruns[2 * i + 1] = make_uint4(b.x, b.y, id, dbits[i]);
-      sn[i] = b.z;
-      acc += b.z;
+      sruns[2 * i] = a[j];
+      sruns[2 * i + 1] = make_uint4(b[j].x, b[j].y, id[j], db[j]);
+      sn[i] = b[j].z;
+      acc += b[j].z;
     }
   }
   acc = wave_sum(acc);
@@ -344,18 +367,26 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
 // Counting pass: per partition, how many of its pairs have each value of the tile's low
 // byte.  A workgroup takes kCountParts consecutive partitions and writes, per partition,
 // the counts of the chunk's earlier partitions (cnt_pre[b][d]) and, per chunk, its totals
-// (csum[c][d]); both are contiguous rows.
+// (csum[c][d]); both are contiguous rows.  With hp > 0 it also counts the tile-id digits
+// above the low byte (bits [8 + 8q, 16 + 8q), q < hp) for the pair sort and adds the
+// chunk's counts to copy (chunk mod kDigitCopies) of them in dcopies (one copy takes too
+// many atomics per address).  A lane's consecutive pairs
+// mostly share those digits (they lie along tile rows), so each lane sums its run of
+// equal values in a register and adds it when the value changes.
 __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __restrict__ vcount, int64_t P,
                                                           int64_t nparts,
                                                           const uint4* __restrict__ sruns,
                                                           const uint64_t* __restrict__ goff,
                                                           const uint32_t* __restrict__ gstart, int tiles_x,
                                                           uint32_t* __restrict__ cnt_pre,
-                                                          uint64_t* __restrict__ csum) {
+                                                          uint64_t* __restrict__ csum, int hp,
+                                                          uint64_t* __restrict__ dcopies) {
   __shared__ int32_t s_rel[kEmitPart + 2];
   __shared__ uint32_t s_h[kBinBlock / kWave][kDigits];
+  __shared__ uint32_t s_hi[GS_TILE_DIGIT_COUNTS];  // the chunk's counts of the higher digits
   const int tid = threadIdx.x, wave = tid / kWave;
   const int64_t v = (int64_t)*vcount;
+  for (int i = tid; i < hp * kDigits; i += kBinBlock) s_hi[i] = 0;
   uint32_t running = 0;  // digit tid's count in the chunk's earlier partitions
   for (int q = 0; q < kCountParts; ++q) {
     const int64_t b = (int64_t)blockIdx.x * kCountParts + q;
@@ -363,9 +394,24 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __rest
     for (int i = tid; i < (kBinBlock / kWave) * kDigits; i += kBinBlock) (&s_h[0][0])[i] = 0;
     const EmitPart e = stage_partition(b, nparts, v, P, goff, gstart, s_rel);
     __syncthreads();
+    uint32_t cur[2] = {0xFFFFFFFFu, 0xFFFFFFFFu}, run[2] = {0u, 0u};  // this lane's current run per digit
     lane_pairs<false>(e, s_rel, sruns, tiles_x, [&](int, uint32_t tile, uint32_t, uint32_t) {
       atomicAdd(&s_h[wave][tile & (kDigits - 1)], 1u);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (q >= hp) break;
+        const uint32_t h = (tile >> (8 + 8 * q)) & (kDigits - 1);
+        if (h != cur[q]) {
+          if (run[q]) atomicAdd(&s_hi[q * kDigits + cur[q]], run[q]);
+          cur[q] = h;
+          run[q] = 0;
+        }
+        ++run[q];
+      }
     });
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (q < hp && run[q]) atomicAdd(&s_hi[q * kDigits + cur[q]], run[q]);
     __syncthreads();
     uint32_t c = 0;
 #pragma unroll
@@ -375,12 +421,26 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __rest
     __syncthreads();  // the next partition reuses s_rel and s_h
   }
   csum[(int64_t)blockIdx.x * kDigits + tid] = running;
+  // s_hi is complete: the partition loop ended on a barrier
+  uint64_t* dc = dcopies + (blockIdx.x % kDigitCopies) * GS_TILE_DIGIT_COUNTS;
+  for (int i = tid; i < hp * kDigits; i += kBinBlock)
+    if (s_hi[i]) atomicAdd(reinterpret_cast<unsigned long long*>(dc + i), (unsigned long long)s_hi[i]);
 }
 
 // One workgroup per digit: exclusive scan over chunks of the digit's chunk totals
-// (csum[c][d], in place) and the digit's total.
+// (csum[c][d], in place) and the digit's total.  With digit_counts non-NULL, workgroup d
+// also sums the copies of the higher tile-digit counts [0][d] and [1][d] into it.
 __global__ __launch_bounds__(kBinBlock) void k_digit_scan(int64_t nchunks, uint64_t* __restrict__ csum,
-                                                          uint64_t* __restrict__ totals) {
+                                                          uint64_t* __restrict__ totals,
+                                                          const uint64_t* __restrict__ dcopies,
+                                                          uint64_t* __restrict__ digit_counts) {
+  if (digit_counts && threadIdx.x < GS_TILE_DIGIT_COUNTS / kDigits) {
+    const int i = (int)threadIdx.x * kDigits + (int)blockIdx.x;
+    uint64_t t = 0;
+#pragma unroll
+    for (int c = 0; c < kDigitCopies; ++c) t += dcopies[c * GS_TILE_DIGIT_COUNTS + i];
+    digit_counts[i] = t;
+  }
   __shared__ uint64_t s_w[kBinBlock / kWave];
   __shared__ uint64_t s_carry;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
@@ -470,7 +530,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
     s_vals[slot] = id;
   });
   __syncthreads();
-  // wavefront-striped: wave w owns pairs [w * 512, (w + 1) * 512) of the partition
+  // wavefront-striped: wave w owns pairs [w * kWavePart, (w + 1) * kWavePart) of the partition
   constexpr int kWavePart = kEmitPer * kWave;
   uint64_t key[kEmitPer];
   uint32_t val[kEmitPer], rank[kEmitPer];
@@ -541,7 +601,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
 // Workspace layout (bytes).  The arrays sized by the pair count come last, so the count
 // phase (which runs before P is known) and the emission phase agree on every offset.
 struct BinLayout {
-  size_t pair_sums, vis_sums, sorted_sums, totals, dk0, dv0, dk1, dv1, sort, goff, sruns, sn, dtotals, gstart, cnt_pre,
+  size_t pair_sums, vis_sums, sorted_sums, totals, dcopies, dk0, dv0, dk1, dv1, sort, goff, sruns, sn, dtotals, gstart, cnt_pre,
       csum, total;
   int64_t nb, nparts, nchunks;
 };
@@ -559,7 +619,8 @@ static BinLayout bin_layout(int64_t n, int64_t P) {
   l.vis_sums = l.pair_sums + sums;
   l.sorted_sums = l.vis_sums + sums;
   l.totals = l.sorted_sums + sums;
-  l.dk0 = l.totals + 256;
+  l.dcopies = l.totals + 256;
+  l.dk0 = l.dcopies + sizeof(uint64_t) * kDigitCopies * GS_TILE_DIGIT_COUNTS;
   l.dv0 = l.dk0 + ids;
   l.dk1 = l.dv0 + ids;
   l.dv1 = l.dk1 + ids;
@@ -603,7 +664,7 @@ uint64_t* bin_totals_ptr(int64_t n, void* ws) {
 // depth and gather their tile records into depth order, with per-block pair sums and
 // their scan.  The visible count V is read on the device (totals[1]); every grid is sized
 // for all n Gaussians, so no host value is needed.
-hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, void* ws, hipStream_t s) {
+hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, uint64_t* digit_counts, void* ws, hipStream_t s) {
   if (n == 0) return hipSuccess;
   const BinLayout l = bin_layout(n, 0);
   char* w = static_cast<char*>(ws);
@@ -616,7 +677,8 @@ hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, void* ws, hipSt
   uint4* sruns = reinterpret_cast<uint4*>(w + l.sruns);
   uint32_t* sn = reinterpret_cast<uint32_t*>(w + l.sn);
   k_compact<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, proj.n_tiles, proj.depth,
-                                                 reinterpret_cast<const uint64_t*>(w + l.vis_sums), dk0, dv0);
+                                                 reinterpret_cast<const uint64_t*>(w + l.vis_sums), dk0, dv0,
+                                                 digit_counts ? reinterpret_cast<uint64_t*>(w + l.dcopies) : nullptr);
   // the sorted depths stay where the last pass wrote them: k_count_sorted picks the buffer
   hipError_t e = radix_sort_u32(n, totals + 1, dk0, dv0, dk1, dv1, 0, 32, w + l.sort, s, false);
   if (e != hipSuccess) return e;
@@ -629,10 +691,11 @@ hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, void* ws, hipSt
 // Emission phase (the host has read P, and the workspace holds the P-sized arrays): pair
 // offsets and partition starts, then the two emission passes over partitions of
 // kEmitPart pairs.
-hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int tiles_x, void* ws, uint64_t* keys,
-                           uint32_t* vals, hipStream_t s) {
+hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int tiles_x, int tile_bits,
+                           uint64_t* digit_counts, void* ws, uint64_t* keys, uint32_t* vals, hipStream_t s) {
   (void)proj;
-  if (n == 0 || P == 0) return hipSuccess;
+  if (n == 0 || P == 0)
+    return digit_counts ? launch_fill_u32(digit_counts, 2 * GS_TILE_DIGIT_COUNTS, 0u, s) : hipSuccess;
   const BinLayout l = bin_layout(n, P);
   char* w = static_cast<char*>(ws);
   uint64_t* ss = reinterpret_cast<uint64_t*>(w + l.sorted_sums);
@@ -645,9 +708,12 @@ hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int t
   uint32_t* cnt_pre = reinterpret_cast<uint32_t*>(w + l.cnt_pre);
   uint64_t* csum = reinterpret_cast<uint64_t*>(w + l.csum);
   k_offsets<<<(unsigned)l.nb, kBinBlock, 0, s>>>(vcount, sn, ss, goff, gstart);
+  // digit passes of the pair sort above the low byte (tile ids have at most 24 bits)
+  const int hp = digit_counts ? (tile_bits > 8 ? (tile_bits - 1) / 8 : 0) : 0;
+  uint64_t* dcopies = reinterpret_cast<uint64_t*>(w + l.dcopies);
   k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, goff, gstart, tiles_x, cnt_pre,
-                                                         csum);
-  k_digit_scan<<<kDigits, kBinBlock, 0, s>>>(l.nchunks, csum, dtotals);
+                                                         csum, hp, dcopies);
+  k_digit_scan<<<kDigits, kBinBlock, 0, s>>>(l.nchunks, csum, dtotals, dcopies, digit_counts);
   k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, goff, gstart, tiles_x, cnt_pre,
                                                           csum, dtotals, keys, vals);
   return hipGetLastError();

@@ -19,7 +19,8 @@
 // workgroup barrier couples the four quadrants, so a quadrant with a short list does not
 // wait for the others.  A pixel stops once T < 1e-4, a wavefront once its 64 pixels have.
 // Tiles run in the order given by tile_order (longest lists first) so that the long tiles
-// start early.
+// start early.  Ids read from the lists are clamped to n - 1, so lists that do not hold
+// valid ids give wrong pixels but never a read outside the records.
 //
 // The backward walks each wavefront's records [0, last contributor) in reverse three at a
 // time and sums the three records' ten per-pixel gradient terms over the wavefront in one
@@ -90,7 +91,8 @@ __device__ __forceinline__ bool quadrant_reach(const float4 s0, const float4 s1,
 __device__ __forceinline__ int tile_of(const int32_t* __restrict__ order, int b) { return order ? order[b] : b; }
 
 __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
-    const float4* __restrict__ rec, const uint32_t* __restrict__ vals, const int64_t* __restrict__ ranges,
+    const float4* __restrict__ rec, const uint32_t* __restrict__ vals, uint32_t id_max,
+    const int64_t* __restrict__ ranges,
     const int32_t* __restrict__ order, int W, int H, int tiles_x, float bg0, float bg1, float bg2,
     float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ n_contrib) {
   __shared__ float4 s_rec[kRenderWaves][kWave * 3];  // each wavefront's staged chunk
@@ -112,12 +114,12 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
   // wavefront's LDS slice.  No workgroup barrier: a wavefront never waits for the others.
   float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0, p2 = p0;
   if (start + lane < end) {
-    const uint32_t id = vals[start + lane];
+    const uint32_t id = min(vals[start + lane], id_max);
     p0 = rec[3 * (size_t)id]; p1 = rec[3 * (size_t)id + 1]; p2 = rec[3 * (size_t)id + 2];
   }
   // ids run one chunk ahead of the records, so a chunk's record gathers wait on one
   // memory round trip instead of two
-  uint32_t nid = start + kWave + lane < end ? vals[start + kWave + lane] : 0u;
+  uint32_t nid = start + kWave + lane < end ? min(vals[start + kWave + lane], id_max) : 0u;
   float livef = inside ? 1.0f : 0.0f;
   for (int64_t b = start; b < end; b += kWave) {
     if (!__ballot(livef != 0.0f)) break;  // this wavefront's pixels are all done
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
     if (b + kWave + lane < end) {  // prefetch the next chunk
       p0 = rec[3 * (size_t)nid]; p1 = rec[3 * (size_t)nid + 1]; p2 = rec[3 * (size_t)nid + 2];
     }
-    nid = b + 2 * kWave + lane < end ? vals[b + 2 * kWave + lane] : 0u;
+    nid = b + 2 * kWave + lane < end ? min(vals[b + 2 * kWave + lane], id_max) : 0u;
     if (!m) continue;
     const uint32_t kb = (uint32_t)(b - start) + 1u;  // list position + 1 of staged record 0
     // one record's contribution; a record this lane does not take gets alpha 0, which
@@ -248,7 +250,8 @@ __device__ __forceinline__ bool bwd_record(const float4* __restrict__ s_rec, int
 }
 
 __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
-    const float4* __restrict__ rec, const uint32_t* __restrict__ vals, const int64_t* __restrict__ ranges,
+    const float4* __restrict__ rec, const uint32_t* __restrict__ vals, uint32_t id_max,
+    const int64_t* __restrict__ ranges,
     const int32_t* __restrict__ order, int W, int H, int tiles_x, float bg0, float bg1, float bg2,
     const float* __restrict__ final_T, const uint32_t* __restrict__ n_contrib, const float* __restrict__ dL,
     float* __restrict__ gscreen) {
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
   {
     const int64_t hi = start + wlast, lo = hi - kWave > start ? hi - kWave : start;
     if (lo + lane < hi) {
-      pid = vals[lo + lane];
+      pid = min(vals[lo + lane], id_max);
       q0 = rec[3 * (size_t)pid]; q1 = rec[3 * (size_t)pid + 1]; q2 = rec[3 * (size_t)pid + 2];
     }
   }
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
     {  // prefetch the next (earlier) chunk
       const int64_t nhi = lo, nlo = nhi - kWave > start ? nhi - kWave : start;
       if (nlo + lane < nhi) {
-        pid = vals[nlo + lane];
+        pid = min(vals[nlo + lane], id_max);
         q0 = rec[3 * (size_t)pid]; q1 = rec[3 * (size_t)pid + 1]; q2 = rec[3 * (size_t)pid + 2];
       }
     }
@@ -353,21 +356,21 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
   }
 }
 
-hipError_t launch_render_fwd(const gs_projected& proj, const uint32_t* vals, const int64_t* ranges,
+hipError_t launch_render_fwd(const gs_projected& proj, const uint32_t* vals, uint32_t id_max, const int64_t* ranges,
                              const int32_t* order, const DevCamera& cam, const float bg[3], float* image,
                              float* final_T, uint32_t* n_contrib, hipStream_t s) {
   const unsigned tiles = (unsigned)(cam.tiles_x * cam.tiles_y);
-  k_render_fwd<<<tiles, kRenderBlock, 0, s>>>(reinterpret_cast<const float4*>(proj.rec), vals, ranges, order,
+  k_render_fwd<<<tiles, kRenderBlock, 0, s>>>(reinterpret_cast<const float4*>(proj.rec), vals, id_max, ranges, order,
                                              cam.width, cam.height, cam.tiles_x, bg[0], bg[1], bg[2], image, final_T,
                                              n_contrib);
   return hipGetLastError();
 }
 
-hipError_t launch_render_bwd(const gs_projected& proj, const uint32_t* vals, const int64_t* ranges,
+hipError_t launch_render_bwd(const gs_projected& proj, const uint32_t* vals, uint32_t id_max, const int64_t* ranges,
                              const int32_t* order, const DevCamera& cam, const float bg[3], const float* final_T,
                              const uint32_t* n_contrib, const float* dL, float* gscreen, hipStream_t s) {
   const unsigned tiles = (unsigned)(cam.tiles_x * cam.tiles_y);
-  k_render_bwd<<<tiles, kRenderBlock, 0, s>>>(reinterpret_cast<const float4*>(proj.rec), vals, ranges, order,
+  k_render_bwd<<<tiles, kRenderBlock, 0, s>>>(reinterpret_cast<const float4*>(proj.rec), vals, id_max, ranges, order,
                                              cam.width, cam.height, cam.tiles_x, bg[0], bg[1], bg[2], final_T,
                                              n_contrib, dL, gscreen);
   return hipGetLastError();

@@ -92,16 +92,21 @@ hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s) {
 // holding the result (0 = keys, 1 = tmp).  With keep_all no pass is skipped (a pass over a
 // constant digit moves the keys unchanged), so the result's buffer follows from the pass
 // count alone and the host knows it.  Global digit bases: base[p][d] = exclusive scan of
-// pass p's histogram.  Run by one workgroup of kRadix threads.
-__device__ __forceinline__ void sort_plan(const uint64_t* __restrict__ hist, uint64_t* __restrict__ base,
+// pass p's histogram, the sum of `copies` copies kMaxPasses * kRadix words apart (pass p's
+// counts at p * kRadix in each).  Run by one workgroup of kRadix threads.
+__device__ __forceinline__ void sort_plan(const uint64_t* __restrict__ hist, int copies, uint64_t* __restrict__ base,
                                           int32_t* __restrict__ plan, int passes, uint64_t P, int keep_all) {
   __shared__ uint64_t s_w[kRadix / kWave];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   int cur = 0;
   for (int p = 0; p < passes; ++p) {
     uint64_t h = 0;
+    if (copies == kHistCopies) {
 #pragma unroll
-    for (int c = 0; c < kHistCopies; ++c) h += hist[c * kMaxPasses * kRadix + p * kRadix + tid];
+      for (int c = 0; c < kHistCopies; ++c) h += hist[c * kMaxPasses * kRadix + p * kRadix + tid];
+    } else {
+      for (int c = 0; c < copies; ++c) h += hist[c * kMaxPasses * kRadix + p * kRadix + tid];
+    }
     const uint64_t inc = wave_inclusive_scan(h);
     if (lane == kWave - 1) s_w[wave] = inc;
     __syncthreads();
@@ -154,10 +159,11 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ 
   }
 }
 
-__global__ __launch_bounds__(kRadix) void k_sort_plan(const uint64_t* __restrict__ hist, uint64_t* __restrict__ base,
-                                                      int32_t* __restrict__ plan, int passes, int64_t Pmax,
-                                                      const uint64_t* __restrict__ dcount, int keep_all) {
-  sort_plan(hist, base, plan, passes, (uint64_t)sort_count(Pmax, dcount), keep_all);
+__global__ __launch_bounds__(kRadix) void k_sort_plan(const uint64_t* __restrict__ hist, int copies,
+                                                      uint64_t* __restrict__ base, int32_t* __restrict__ plan,
+                                                      int passes, int64_t Pmax, const uint64_t* __restrict__ dcount,
+                                                      int keep_all) {
+  sort_plan(hist, copies, base, plan, passes, (uint64_t)sort_count(Pmax, dcount), keep_all);
 }
 
 __device__ __forceinline__ uint64_t status_load(const uint64_t* p) {
@@ -306,8 +312,10 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
     const K k = s_keys[i];
     const uint32_t dd = (uint32_t)(k >> shift) & dmask;
     const uint64_t g = s_gbase[dd] + (uint64_t)(i - (int)s_lbase[dd]);
-    kout[g] = k;
-    vout[g] = s_vals[i];
+    if (g < (uint64_t)P) {  // always, given exact digit counts; caller-supplied ones are not trusted
+      kout[g] = k;
+      vout[g] = s_vals[i];
+    }
   }
 }
 
@@ -417,7 +425,7 @@ size_t radix_workspace_bytes(int64_t P, int lo, int hi) { return sort_layout(P, 
 template <typename K>
 static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_t* vals, K* keys_tmp,
                              uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back = true,
-                             bool keep_all = false) {
+                             bool keep_all = false, const uint64_t* digit_counts = nullptr) {
   const int passes = radix_passes(lo, hi);
   char* w = static_cast<char*>(ws);
   if (P <= 1 || passes == 0)  // nothing moves: the result is in keys/vals, as the word says
@@ -432,13 +440,15 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
   // zero histograms, plan, tickets and every pass's status words (no memset: capture-safe)
   hipError_t e = launch_fill_u32(w, (int64_t)(l.total / 4), 0u, s);
   if (e != hipSuccess) return e;
-  {
+  if (!digit_counts) {
     const int64_t want = (P + kSortPart - 1) / kSortPart;
     const unsigned blocks = (unsigned)(want < 2048 ? (want > 0 ? want : 1) : 2048);
     k_sort_hist<K><<<blocks, kSortBlock, sizeof(uint32_t) * (kSortBlock / kWave) * passes * kRadix, s>>>(
         keys, P, dcount, lo, passes, hist);
   }
-  k_sort_plan<<<1, kRadix, 0, s>>>(hist, dbase, plan, passes, P, dcount, keep_all ? 1 : 0);
+  // counts the caller already has ([pass][digit], one copy) replace the counting read
+  k_sort_plan<<<1, kRadix, 0, s>>>(digit_counts ? digit_counts : hist, digit_counts ? 1 : kHistCopies, dbase, plan,
+                                   passes, P, dcount, keep_all ? 1 : 0);
   for (int p = 0; p < passes; ++p) {
     const int bits = hi - lo - 8 * p < 8 ? hi - lo - 8 * p : 8;
     k_onesweep<K><<<(unsigned)((P + Onesweep<K>::part - 1) / Onesweep<K>::part), kSortBlock, 0, s>>>(keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p,
@@ -474,13 +484,14 @@ size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_b
 // reports where it is; with NULL, k_ranges moves it back to keys/vals.
 hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
                        uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits,
-                       int32_t* result_in_tmp, void* ws, hipStream_t s) {
+                       const uint64_t* digit_counts, int32_t* result_in_tmp, void* ws, hipStream_t s) {
   hipError_t e = launch_fill_u32(ranges, 4 * num_tiles, 0u, s);
   const int hi = sort_significant_bits(num_tiles);
   const int passes = P > 1 ? radix_passes(sorted_low_bits, hi) : 0;
   const bool in_tmp = passes % 2 == 1;
   if (e == hipSuccess && passes > 0)
-    e = radix_sort<uint64_t>(P, nullptr, keys, vals, keys_tmp, vals_tmp, sorted_low_bits, hi, ws, s, false, true);
+    e = radix_sort<uint64_t>(P, nullptr, keys, vals, keys_tmp, vals_tmp, sorted_low_bits, hi, ws, s, false, true,
+                             digit_counts);
   if (e != hipSuccess) return e;
   const bool move = in_tmp && !result_in_tmp;
   if (P > 0)

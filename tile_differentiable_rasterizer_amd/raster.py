@@ -19,6 +19,7 @@ GS_OK, GS_ERR_INVALID_ARG, GS_ERR_CAPACITY, GS_ERR_OVERFLOW, GS_ERR_HIP, GS_ERR_
 TILE = 16
 REC_FLOATS = 12
 GRAD_SCREEN = 10
+TILE_DIGIT_COUNTS = 512  # GS_TILE_DIGIT_COUNTS
 
 EXPORTS = ("gs_project", "gs_workspace_bytes", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd",
            "gs_render_bwd", "gs_densify", "gs_densify_workspace_bytes", "gs_adam_q16", "gs_quantize_sh",
@@ -72,8 +73,8 @@ def lib():
         L.gs_project.argtypes = [i64, vp, vp, vp, vp, vp, i32, C.POINTER(GsCamera), GsProjected, vp]
         L.gs_workspace_bytes.argtypes = [i64, i64, i32]
         L.gs_workspace_bytes.restype = sz
-        L.gs_bin_tiles.argtypes = [i64, GsProjected, C.POINTER(GsCamera), vp, vp, i64, C.POINTER(i64), vp, sz, vp]
-        L.gs_sort_keys.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, C.POINTER(i32), vp, sz, vp]
+        L.gs_bin_tiles.argtypes = [i64, GsProjected, C.POINTER(GsCamera), vp, vp, i64, C.POINTER(i64), vp, vp, sz, vp]
+        L.gs_sort_keys.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, C.POINTER(i32), vp, sz, vp]
         L.gs_render_fwd.argtypes = [i64, GsProjected, vp, vp, vp, C.POINTER(GsCamera), C.POINTER(C.c_float), vp,
                                     vp, vp, vp]
         L.gs_render_bwd.argtypes = [i64, vp, vp, vp, vp, vp, i32, C.POINTER(GsCamera), GsProjected, vp, vp, vp,
@@ -187,14 +188,18 @@ def _pinned_count():
     return t
 
 
-def bin_tiles(proj: dict, cam, keys, vals, workspace, stream=None) -> tuple[int, int]:
-    """gs_bin_tiles.  Returns (status, P); status is GS_OK or GS_ERR_CAPACITY."""
+def bin_tiles(proj: dict, cam, keys, vals, workspace, stream=None, digit_counts=None) -> tuple[int, int]:
+    """gs_bin_tiles.  Returns (status, P); status is GS_OK or GS_ERR_CAPACITY.
+    ``digit_counts`` (int64 [GS_TILE_DIGIT_COUNTS], optional) receives the tile-digit
+    counts that sort_keys(digit_counts=...) takes in place of its own counting read."""
     n = proj["rec"].shape[0]
     camc = camera_struct(cam)
     P = _pinned_count()  # page-locked, so the call waits for the count copy alone
     cap = keys.shape[0] if keys is not None else 0
+    if digit_counts is not None:
+        assert digit_counts.numel() >= TILE_DIGIT_COUNTS and digit_counts.dtype == torch.int64
     st = lib().gs_bin_tiles(n, projected_struct(proj), C.byref(camc), _ptr(keys), _ptr(vals), cap,
-                            C.cast(P.data_ptr(), C.POINTER(C.c_int64)), _ptr(workspace),
+                            C.cast(P.data_ptr(), C.POINTER(C.c_int64)), _ptr(digit_counts), _ptr(workspace),
                             workspace.numel() if workspace is not None else 0, _stream(stream))
     if st not in (GS_OK, GS_ERR_CAPACITY):
         _check(st, "gs_bin_tiles")
@@ -202,16 +207,18 @@ def bin_tiles(proj: dict, cam, keys, vals, workspace, stream=None) -> tuple[int,
 
 
 def sort_keys(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, ranges, workspace, order=None,
-              sorted_low_bits: int = 40, stream=None, leave_in_tmp: bool = False):
+              sorted_low_bits: int = 40, stream=None, leave_in_tmp: bool = False, digit_counts=None):
     """gs_sort_keys; ``order`` (int32 [num_tiles], optional) receives the longest-first tile order.
 
     ``sorted_low_bits`` = 40 for pairs from gs_bin_tiles (already ordered by tile low byte,
     then depth), 0 for arbitrary keys.  With ``leave_in_tmp`` the result stays where the
     last pass wrote it and the call returns True when that is keys_tmp/vals_tmp; otherwise
-    the result is in keys/vals and the call returns False."""
+    the result is in keys/vals and the call returns False.  ``digit_counts``: per-pass digit
+    counts of the keys (bin_tiles' for its pairs), or None to count them."""
     where = C.c_int32(-1)
     _check(lib().gs_sort_keys(n_pairs, num_tiles, int(sorted_low_bits), _ptr(keys), _ptr(vals), _ptr(keys_tmp),
-                              _ptr(vals_tmp), _ptr(ranges), _ptr(order), C.byref(where) if leave_in_tmp else None,
+                              _ptr(vals_tmp), _ptr(ranges), _ptr(order), _ptr(digit_counts),
+                              C.byref(where) if leave_in_tmp else None,
                               _ptr(workspace), workspace.numel(), _stream(stream)), "gs_sort_keys")
     return bool(where.value == 1) if leave_in_tmp else False
 
@@ -261,6 +268,7 @@ class Rasterizer:
         self.n = int(means.shape[0])
         self.device = means.device
         self.proj = alloc_projected(self.n, self.device)
+        self.digit_counts = torch.empty(TILE_DIGIT_COUNTS, dtype=torch.int64, device=self.device)
         self.capacity = 0
         self.keys = self.vals = self.keys_tmp = self.vals_tmp = None
         self.workspace = None
@@ -283,15 +291,15 @@ class Rasterizer:
         tiles = ((W + TILE - 1) // TILE) * ((H + TILE - 1) // TILE)
         self._ensure_pairs(self.capacity, tiles)
         project(self.means, self.scales, self.quats, self.opac, self.sh, self.sh_degree, cam, self.proj, stream)
-        st, P = bin_tiles(self.proj, cam, self.keys, self.vals, self.workspace, stream)
+        st, P = bin_tiles(self.proj, cam, self.keys, self.vals, self.workspace, stream, self.digit_counts)
         if st == GS_ERR_CAPACITY:
             self._ensure_pairs(P + P // 4 + 1, tiles)
-            st, P = bin_tiles(self.proj, cam, self.keys, self.vals, self.workspace, stream)
+            st, P = bin_tiles(self.proj, cam, self.keys, self.vals, self.workspace, stream, self.digit_counts)
             _check(st, "gs_bin_tiles")
         ranges = torch.empty((tiles, 2), dtype=torch.int64, device=self.device)
         order = torch.empty(tiles, dtype=torch.int32, device=self.device)
         in_tmp = sort_keys(P, tiles, self.keys, self.vals, self.keys_tmp, self.vals_tmp, ranges, self.workspace,
-                           order, stream=stream, leave_in_tmp=True)
+                           order, stream=stream, leave_in_tmp=True, digit_counts=self.digit_counts)
         sk, sv = (self.keys_tmp, self.vals_tmp) if in_tmp else (self.keys, self.vals)
         image = torch.empty((3, H, W), dtype=torch.float32, device=self.device)
         final_T = torch.empty((H, W), dtype=torch.float32, device=self.device)
