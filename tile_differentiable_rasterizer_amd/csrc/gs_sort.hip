@@ -389,21 +389,50 @@ __device__ __forceinline__ int length_bucket(int64_t len) {
 
 __global__ __launch_bounds__(1024) void k_tile_order(const int64_t* __restrict__ ranges, int64_t num_tiles,
                                                     int32_t* __restrict__ order) {
+  constexpr int kPer = 8;  // tiles per thread per round, their loads all in flight together
   __shared__ uint32_t s_cnt[128];
   __shared__ uint32_t s_cur[128];
-  if (threadIdx.x < 128) s_cnt[threadIdx.x] = 0;
+  __shared__ uint32_t s_w[2];
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  if (tid < 128) s_cnt[tid] = 0;
   __syncthreads();
-  for (int64_t t = threadIdx.x; t < num_tiles; t += 1024)
-    atomicAdd(&s_cnt[length_bucket(ranges[2 * t + 1] - ranges[2 * t])], 1u);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t acc = 0;
-    for (int b = 127; b >= 0; --b) { s_cur[b] = acc; acc += s_cnt[b]; }
+  // a single round (num_tiles <= 8192, 1080p and below) keeps its buckets in registers
+  int bk[kPer];
+  for (int64_t t0 = 0; t0 < num_tiles; t0 += 1024 * kPer) {
+    int64_t a[kPer], b[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int64_t t = t0 + j * 1024 + tid;
+      a[j] = t < num_tiles ? ranges[2 * t] : 0;
+      b[j] = t < num_tiles ? ranges[2 * t + 1] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      bk[j] = length_bucket(b[j] - a[j]);
+      if (t0 + j * 1024 + tid < num_tiles) atomicAdd(&s_cnt[bk[j]], 1u);
+    }
   }
   __syncthreads();
-  for (int64_t t = threadIdx.x; t < num_tiles; t += 1024) {
-    const uint32_t pos = atomicAdd(&s_cur[length_bucket(ranges[2 * t + 1] - ranges[2 * t])], 1u);
-    order[pos] = (int32_t)t;
+  // exclusive scan in decreasing bucket order: lane j of the first two wavefronts takes
+  // bucket 127 - j
+  uint32_t c = 0, inc = 0;
+  if (tid < 128) {
+    c = s_cnt[127 - tid];
+    inc = wave_inclusive_scan(c);
+    if (lane == kWave - 1) s_w[wave] = inc;
+  }
+  __syncthreads();
+  if (tid < 128) s_cur[127 - tid] = inc - c + (wave == 1 ? s_w[0] : 0u);
+  __syncthreads();
+  const bool cached = num_tiles <= 1024 * kPer;
+  for (int64_t t0 = 0; t0 < num_tiles; t0 += 1024 * kPer) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int64_t t = t0 + j * 1024 + tid;
+      if (t >= num_tiles) break;
+      const int bucket = cached ? bk[j] : length_bucket(ranges[2 * t + 1] - ranges[2 * t]);
+      order[atomicAdd(&s_cur[bucket], 1u)] = (int32_t)t;
+    }
   }
 }
 
