@@ -32,15 +32,18 @@ namespace gs {
 constexpr int kSortBlock = 256;
 constexpr int kSortKPT = 16;                      // keys per thread of the histogram
 constexpr int kSortPart = kSortBlock * kSortKPT;  // keys per histogram round
-// Keys per thread of a onesweep partition, by key width (LDS holds the partition's keys
-// and values, so wider keys take smaller partitions and more workgroups fit a CU).
-constexpr int kOnesweepKpt32 = 16, kOnesweepKpt64 = 16;
+// A onesweep partition holds 4096 keys.  Its workgroup size, by key width: with more lanes
+// each holds fewer keys, and the ranking (a chain of dependent ballots per key) has more
+// wavefronts per SIMD to interleave.
+constexpr int kOnesweepPart = 4096;
+constexpr int kOnesweepThreads32 = 1024, kOnesweepThreads64 = 1024;
 template <typename K>
 struct Onesweep {
-  static constexpr int kpt = sizeof(K) == 8 ? kOnesweepKpt64 : kOnesweepKpt32;
-  static constexpr int part = kSortBlock * kpt;
+  static constexpr int threads = sizeof(K) == 8 ? kOnesweepThreads64 : kOnesweepThreads32;
+  static constexpr int part = kOnesweepPart;
+  static constexpr int kpt = part / threads;
 };
-constexpr int kMinPart = kSortBlock * (kOnesweepKpt64 < kOnesweepKpt32 ? kOnesweepKpt64 : kOnesweepKpt32);
+constexpr int kMinPart = kOnesweepPart;
 constexpr int kRadix = 256;
 constexpr int kMaxPasses = 8;
 constexpr int kLookBack = 4;                      // status words read per look-back round trip
@@ -174,7 +177,7 @@ __device__ __forceinline__ void status_store(uint64_t* p, uint64_t v) {
 }
 
 template <typename K>
-__global__ __launch_bounds__(kSortBlock) void k_onesweep(
+__global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
     K* __restrict__ k0, uint32_t* __restrict__ v0, K* __restrict__ k1, uint32_t* __restrict__ v1,
     int64_t Pmax, const uint64_t* __restrict__ dcount, int pass, int shift, int bits,
     const int32_t* __restrict__ plan, const uint64_t* __restrict__ dbase, uint64_t* __restrict__ status,
@@ -186,20 +189,23 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   K* kout = mode ? k0 : k1;
   uint32_t* vout = mode ? v0 : v1;
   const uint32_t dmask = (1u << bits) - 1u;
-  constexpr int kKPT = Onesweep<K>::kpt, kPart = Onesweep<K>::part;
+  constexpr int kNT = Onesweep<K>::threads, kKPT = Onesweep<K>::kpt, kPart = Onesweep<K>::part;
+  constexpr int kWaves = kNT / kWave;
+  static_assert(kNT >= kRadix && kPart % kNT == 0, "one thread per digit, whole keys per lane");
 
   __shared__ K s_keys[kPart];
   __shared__ uint32_t s_vals[kPart];
-  __shared__ uint32_t s_wh[kSortBlock / kWave][kRadix];  // per-wave digit counters, then offsets
-  __shared__ uint32_t s_lbase[kRadix];                   // partition-local digit starts
-  __shared__ uint64_t s_gbase[kRadix];                   // global digit starts for this partition
-  __shared__ uint32_t s_w[kSortBlock / kWave];
+  __shared__ uint32_t s_wh[kWaves][kRadix];  // per-wave digit counters, then offsets
+  __shared__ uint32_t s_lbase[kRadix];       // partition-local digit starts
+  __shared__ uint64_t s_gbase[kRadix];       // global digit starts for this partition
+  __shared__ uint32_t s_w[kRadix / kWave];
   __shared__ uint32_t s_part;
 
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  const bool owner = tid < kRadix;  // thread d < kRadix owns digit d
   const int64_t P = sort_count(Pmax, dcount);
   if (tid == 0) s_part = atomicAdd(tickets + pass, 1u);
-  for (int i = tid; i < (kSortBlock / kWave) * kRadix; i += kSortBlock) (&s_wh[0][0])[i] = 0;
+  for (int i = tid; i < kWaves * kRadix; i += kNT) (&s_wh[0][0])[i] = 0;
   __syncthreads();
   const int64_t part = s_part;
   const int64_t base = part * kPart;
@@ -208,8 +214,8 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   if (base >= P) return;
   // start the look-back now: the predecessor's word for this thread's digit is usually
   // final by the time this partition has ranked its keys
-  uint64_t early = part > 0 ? status_load(status + (part - 1) * kRadix + tid) : 0;
-  const uint64_t my_dbase = dbase[tid];  // this thread's digit's global base
+  uint64_t early = owner && part > 0 ? status_load(status + (part - 1) * kRadix + tid) : 0;
+  const uint64_t my_dbase = owner ? dbase[tid] : 0;  // this thread's digit's global base
 
   // wave-striped: wave w owns keys [w * 64 kKPT, (w + 1) * 64 kKPT) of the partition, in order
   K key[kKPT];
@@ -243,22 +249,24 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   for (int j = 0; j < kKPT; ++j) rank[j] += (uint32_t)__shfl((int)prev[j], lead[j], kWave);
   __syncthreads();
 
-  // thread d owns digit d: wave offsets, publish the partition's count
+  // digit owners: wave offsets, publish the partition's count, partition-local exclusive
+  // scan over digits
   const int d = tid;
-  uint32_t tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSortBlock / kWave; ++w) {
-    const uint32_t c = s_wh[w][d];
-    s_wh[w][d] = tot;
-    tot += c;
-  }
   uint64_t* my_status = status + part * kRadix + d;
-  status_store(my_status, (part == 0 ? kFlagPre : kFlagAgg) | (uint64_t)tot);
-  // partition-local exclusive scan over digits
-  {
-    const uint32_t inc = wave_inclusive_scan(tot);
+  uint32_t tot = 0, inc = 0;
+  if (owner) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const uint32_t c = s_wh[w][d];
+      s_wh[w][d] = tot;
+      tot += c;
+    }
+    status_store(my_status, (part == 0 ? kFlagPre : kFlagAgg) | (uint64_t)tot);
+    inc = wave_inclusive_scan(tot);
     if (lane == kWave - 1) s_w[wave] = inc;
-    __syncthreads();
+  }
+  __syncthreads();
+  if (owner) {
     uint32_t pre = inc - tot;
     for (int w = 0; w < wave; ++w) pre += s_w[w];
     s_lbase[d] = pre;
@@ -278,37 +286,39 @@ __global__ __launch_bounds__(kSortBlock) void k_onesweep(
   // look back over earlier partitions for this digit's global offset, kLookBack words per
   // round trip: sum published counts back to the first inclusive prefix; a word not yet
   // published ends the round, and the next round starts at it
-  uint64_t excl = 0;
-  if (part > 0) {
-    int64_t p = part - 1;
-    while (true) {
-      uint64_t sv[kLookBack];
-      sv[0] = (early & ~kValMask) ? early : status_load(status + p * kRadix + d);
-      early = 0;
+  if (owner) {
+    uint64_t excl = 0;
+    if (part > 0) {
+      int64_t p = part - 1;
+      while (true) {
+        uint64_t sv[kLookBack];
+        sv[0] = (early & ~kValMask) ? early : status_load(status + p * kRadix + d);
+        early = 0;
 #pragma unroll
-      for (int i = 1; i < kLookBack; ++i) sv[i] = p - i >= 0 ? status_load(status + (p - i) * kRadix + d) : 0;
-      int used = 0;
-      bool done = false;
+        for (int i = 1; i < kLookBack; ++i) sv[i] = p - i >= 0 ? status_load(status + (p - i) * kRadix + d) : 0;
+        int used = 0;
+        bool done = false;
 #pragma unroll
-      for (int i = 0; i < kLookBack; ++i) {
-        if (done || used < i) continue;  // stopped at an inclusive prefix or an unpublished word
-        const uint64_t flag = sv[i] & ~kValMask;
-        if (flag == 0) continue;
-        excl += sv[i] & kValMask;
-        used = i + 1;
-        done = flag == kFlagPre;
+        for (int i = 0; i < kLookBack; ++i) {
+          if (done || used < i) continue;  // stopped at an inclusive prefix or an unpublished word
+          const uint64_t flag = sv[i] & ~kValMask;
+          if (flag == 0) continue;
+          excl += sv[i] & kValMask;
+          used = i + 1;
+          done = flag == kFlagPre;
+        }
+        if (done) break;
+        p -= used;
+        if (used < kLookBack) __builtin_amdgcn_s_sleep(1);
       }
-      if (done) break;
-      p -= used;
-      if (used < kLookBack) __builtin_amdgcn_s_sleep(1);
+      status_store(my_status, kFlagPre | (excl + tot));
     }
-    status_store(my_status, kFlagPre | (excl + tot));
+    s_gbase[d] = my_dbase + excl;
   }
-  s_gbase[d] = my_dbase + excl;
   __syncthreads();
   // write each digit's run contiguously
   const int nvalid = (int)min((int64_t)kPart, P - base);
-  for (int i = tid; i < nvalid; i += kSortBlock) {
+  for (int i = tid; i < nvalid; i += kNT) {
     const K k = s_keys[i];
     const uint32_t dd = (uint32_t)(k >> shift) & dmask;
     const uint64_t g = s_gbase[dd] + (uint64_t)(i - (int)s_lbase[dd]);
@@ -382,7 +392,7 @@ __global__ void k_ranges(const uint64_t* __restrict__ src, const uint32_t* __res
 // octave; order inside a bucket is arbitrary).  The compositing kernels take tiles in this
 // order so that the longest lists start first.
 __device__ __forceinline__ int length_bucket(int64_t len) {
-  if (len < 4) return (int)len;
+  if (len < 4) return len > 0 ? (int)len : 0;
   const int lg = 63 - __clzll((unsigned long long)len);
   return min(127, 4 * lg + (int)((len >> (lg - 2)) & 3));
 }
@@ -480,10 +490,9 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
                                    passes, P, dcount, keep_all ? 1 : 0);
   for (int p = 0; p < passes; ++p) {
     const int bits = hi - lo - 8 * p < 8 ? hi - lo - 8 * p : 8;
-    k_onesweep<K><<<(unsigned)((P + Onesweep<K>::part - 1) / Onesweep<K>::part), kSortBlock, 0, s>>>(keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p,
-                                                          bits,
-                                                          plan, dbase + p * kRadix,
-                                                          status + (size_t)p * l.parts * kRadix, tickets);
+    k_onesweep<K><<<(unsigned)((P + Onesweep<K>::part - 1) / Onesweep<K>::part), Onesweep<K>::threads, 0, s>>>(
+        keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p, bits, plan, dbase + p * kRadix,
+        status + (size_t)p * l.parts * kRadix, tickets);
   }
   if (copy_back) {
     const int64_t want = (P + 255) / 256;
