@@ -33,6 +33,56 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Decoupled look-back (the chained scan of Merrill & Garland) over per-partition status
+// words, one column per counter: a word holds a 62-bit value and a flag, 0 while
+// unpublished, kFlagAgg for the partition's own count, kFlagPre for the inclusive prefix
+// through it.  Status words are read and written at device scope, with no fences: a word
+// carries its own flag.
+constexpr uint64_t kFlagAgg = 1ull << 62;
+constexpr uint64_t kFlagPre = 2ull << 62;
+constexpr uint64_t kValMask = (1ull << 62) - 1;
+constexpr int kLookBack = 4;  // status words read per look-back round trip
+
+__device__ __forceinline__ uint64_t status_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void status_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Exclusive prefix of partition `part` (> 0) in one column: sums the published values of
+// the partitions before it, kLookBack words per round trip, back to the first inclusive
+// prefix; a word not yet published ends the round and the next round starts at it.
+// `col` points at the column's word of partition 0, `stride` words apart per partition;
+// `early` is the predecessor's word if already read (else 0).  Every partition before
+// `part` must already be running (partitions go out in order, by ticket).
+__device__ __forceinline__ uint64_t lookback_exclusive(const uint64_t* col, int64_t stride, int64_t part,
+                                                       uint64_t early) {
+  uint64_t excl = 0;
+  int64_t p = part - 1;
+  while (true) {
+    uint64_t sv[kLookBack];
+    sv[0] = (early & ~kValMask) ? early : status_load(col + p * stride);
+    early = 0;
+#pragma unroll
+    for (int i = 1; i < kLookBack; ++i) sv[i] = p - i >= 0 ? status_load(col + (p - i) * stride) : 0;
+    int used = 0;
+    bool done = false;
+#pragma unroll
+    for (int i = 0; i < kLookBack; ++i) {
+      if (done || used < i) continue;  // stopped at an inclusive prefix or an unpublished word
+      const uint64_t flag = sv[i] & ~kValMask;
+      if (flag == 0) continue;
+      excl += sv[i] & kValMask;
+      used = i + 1;
+      done = flag == kFlagPre;
+    }
+    if (done) return excl;
+    p -= used;
+    if (used < kLookBack) __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 // Inclusive prefix sum across a 64-wide wavefront.
 template <typename T>
 __device__ __forceinline__ T wave_inclusive_scan(T x) {

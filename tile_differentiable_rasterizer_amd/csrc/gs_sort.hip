@@ -30,8 +30,9 @@
 namespace gs {
 
 constexpr int kSortBlock = 256;
-constexpr int kSortKPT = 16;                      // keys per thread of the histogram
-constexpr int kSortPart = kSortBlock * kSortKPT;  // keys per histogram round
+constexpr int kHistThreads = 1024;                  // histogram workgroup: 16 wavefronts
+constexpr int kSortKPT = 4;                         // keys per thread of the histogram
+constexpr int kSortPart = kHistThreads * kSortKPT;  // keys per histogram round
 // A onesweep partition holds 4096 keys.  Its workgroup size, by key width: with more lanes
 // each holds fewer keys, and the ranking (a chain of dependent ballots per key) has more
 // wavefronts per SIMD to interleave.
@@ -46,11 +47,7 @@ struct Onesweep {
 constexpr int kMinPart = kOnesweepPart;
 constexpr int kRadix = 256;
 constexpr int kMaxPasses = 8;
-constexpr int kLookBack = 4;                      // status words read per look-back round trip
 constexpr int kHistCopies = 16;                   // global histogram copies (spreads the atomics)
-constexpr uint64_t kFlagAgg = 1ull << 62;    // partition's own count published
-constexpr uint64_t kFlagPre = 2ull << 62;    // inclusive prefix through this partition
-constexpr uint64_t kValMask = (1ull << 62) - 1;
 
 // Workspace layout (bytes from the workspace start).
 struct SortLayout {
@@ -124,7 +121,7 @@ __device__ __forceinline__ void sort_plan(const uint64_t* __restrict__ hist, int
 }
 
 template <typename K>
-__global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ keys, int64_t Pmax,
+__global__ __launch_bounds__(kHistThreads) void k_sort_hist(const K* __restrict__ keys, int64_t Pmax,
                                                           const uint64_t* __restrict__ dcount, int lo, int passes,
                                                           uint64_t* __restrict__ hist) {
   const int64_t P = sort_count(Pmax, dcount);
@@ -133,27 +130,27 @@ __global__ __launch_bounds__(kSortBlock) void k_sort_hist(const K* __restrict__ 
   extern __shared__ uint32_t s_hist[];
   const int wave = threadIdx.x / kWave;
   uint32_t* s_hw = s_hist + wave * passes * kRadix;
-  for (int i = threadIdx.x; i < (kSortBlock / kWave) * passes * kRadix; i += kSortBlock) s_hist[i] = 0;
+  for (int i = threadIdx.x; i < (kHistThreads / kWave) * passes * kRadix; i += kHistThreads) s_hist[i] = 0;
   __syncthreads();
   for (int64_t b = (int64_t)blockIdx.x * kSortPart; b < P; b += (int64_t)gridDim.x * kSortPart) {
     K k[kSortKPT];  // all loads in flight before the first atomic
 #pragma unroll
     for (int j = 0; j < kSortKPT; ++j) {
-      const int64_t i = b + j * kSortBlock + threadIdx.x;
+      const int64_t i = b + j * kHistThreads + threadIdx.x;
       k[j] = i < P ? keys[i] : (K)0;
     }
 #pragma unroll
     for (int j = 0; j < kSortKPT; ++j) {
-      if (b + j * kSortBlock + threadIdx.x >= P) break;
+      if (b + j * kHistThreads + threadIdx.x >= P) break;
       const uint64_t kk = (uint64_t)k[j] >> lo;
       for (int p = 0; p < passes; ++p) atomicAdd(&s_hw[p * kRadix + ((kk >> (8 * p)) & 0xFF)], 1u);
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < passes * kRadix; i += kSortBlock) {
+  for (int i = threadIdx.x; i < passes * kRadix; i += kHistThreads) {
     uint32_t c = 0;
 #pragma unroll
-    for (int w = 0; w < kSortBlock / kWave; ++w) c += s_hist[w * passes * kRadix + i];
+    for (int w = 0; w < kHistThreads / kWave; ++w) c += s_hist[w * passes * kRadix + i];
     // workgroup b adds into copy b % kHistCopies, so no address sees more than
     // 1/kHistCopies of the workgroups' atomics
     if (c)
@@ -169,12 +166,6 @@ __global__ __launch_bounds__(kRadix) void k_sort_plan(const uint64_t* __restrict
   sort_plan(hist, copies, base, plan, passes, (uint64_t)sort_count(Pmax, dcount), keep_all);
 }
 
-__device__ __forceinline__ uint64_t status_load(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void status_store(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 template <typename K>
 __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
@@ -283,34 +274,11 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
       s_vals[pos] = val[j];
     }
   }
-  // look back over earlier partitions for this digit's global offset, kLookBack words per
-  // round trip: sum published counts back to the first inclusive prefix; a word not yet
-  // published ends the round, and the next round starts at it
+  // look back over earlier partitions for this digit's global offset
   if (owner) {
     uint64_t excl = 0;
     if (part > 0) {
-      int64_t p = part - 1;
-      while (true) {
-        uint64_t sv[kLookBack];
-        sv[0] = (early & ~kValMask) ? early : status_load(status + p * kRadix + d);
-        early = 0;
-#pragma unroll
-        for (int i = 1; i < kLookBack; ++i) sv[i] = p - i >= 0 ? status_load(status + (p - i) * kRadix + d) : 0;
-        int used = 0;
-        bool done = false;
-#pragma unroll
-        for (int i = 0; i < kLookBack; ++i) {
-          if (done || used < i) continue;  // stopped at an inclusive prefix or an unpublished word
-          const uint64_t flag = sv[i] & ~kValMask;
-          if (flag == 0) continue;
-          excl += sv[i] & kValMask;
-          used = i + 1;
-          done = flag == kFlagPre;
-        }
-        if (done) break;
-        p -= used;
-        if (used < kLookBack) __builtin_amdgcn_s_sleep(1);
-      }
+      excl = lookback_exclusive(status + d, kRadix, part, early);
       status_store(my_status, kFlagPre | (excl + tot));
     }
     s_gbase[d] = my_dbase + excl;
@@ -482,7 +450,7 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
   if (!digit_counts) {
     const int64_t want = (P + kSortPart - 1) / kSortPart;
     const unsigned blocks = (unsigned)(want < 2048 ? (want > 0 ? want : 1) : 2048);
-    k_sort_hist<K><<<blocks, kSortBlock, sizeof(uint32_t) * (kSortBlock / kWave) * passes * kRadix, s>>>(
+    k_sort_hist<K><<<blocks, kHistThreads, sizeof(uint32_t) * (kHistThreads / kWave) * passes * kRadix, s>>>(
         keys, P, dcount, lo, passes, hist);
   }
   // counts the caller already has ([pass][digit], one copy) replace the counting read
