@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
   }
   // ids run one chunk ahead of the records, so a chunk's record gathers wait on one
   // memory round trip instead of two
-  uint32_t nid = start + kWave + lane < end ? min(vals[start + kWave + lane], id_max) : 0u;
+  uint32_t nid = start + kWave + lane < end ? vals[start + kWave + lane] : 0u;  // clamped where used
   float livef = inside ? 1.0f : 0.0f;
   for (int64_t b = start; b < end; b += kWave) {
     if (!__ballot(livef != 0.0f)) break;  // this wavefront's pixels are all done
@@ -136,9 +136,10 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
     __builtin_amdgcn_wave_barrier();
     uint64_t m = __ballot(reach);
     if (b + kWave + lane < end) {  // prefetch the next chunk
-      p0 = rec[3 * (size_t)nid]; p1 = rec[3 * (size_t)nid + 1]; p2 = rec[3 * (size_t)nid + 2];
+      const uint32_t id = min(nid, id_max);
+      p0 = rec[3 * (size_t)id]; p1 = rec[3 * (size_t)id + 1]; p2 = rec[3 * (size_t)id + 2];
     }
-    nid = b + 2 * kWave + lane < end ? min(vals[b + 2 * kWave + lane], id_max) : 0u;
+    nid = b + 2 * kWave + lane < end ? vals[b + 2 * kWave + lane] : 0u;
     if (!m) continue;
     const uint32_t kb = (uint32_t)(b - start) + 1u;  // list position + 1 of staged record 0
     // one record's contribution; a record this lane does not take gets alpha 0, which
