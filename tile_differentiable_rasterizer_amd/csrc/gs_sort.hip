@@ -171,9 +171,11 @@ template <typename K>
 __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
     K* __restrict__ k0, uint32_t* __restrict__ v0, K* __restrict__ k1, uint32_t* __restrict__ v1,
     int64_t Pmax, const uint64_t* __restrict__ dcount, int pass, int shift, int bits,
-    const int32_t* __restrict__ plan, const uint64_t* __restrict__ dbase, uint64_t* __restrict__ status,
-    uint32_t* __restrict__ tickets) {
-  const int mode = plan[pass];
+    const int32_t* __restrict__ plan, int mode_arg, const uint64_t* __restrict__ dbase,
+    const uint64_t* __restrict__ counts, uint64_t* __restrict__ status, uint32_t* __restrict__ tickets) {
+  // the buffers this pass reads and writes: given by the host when it knows them (no pass
+  // skipped), else from the plan, which also marks passes to skip
+  const int mode = mode_arg >= 0 ? mode_arg : plan[pass];
   if (mode < 0) return;  // digit constant over all keys: nothing to do
   const K* kin = mode ? k1 : k0;
   const uint32_t* vin = mode ? v1 : v0;
@@ -190,13 +192,23 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
   __shared__ uint32_t s_lbase[kRadix];       // partition-local digit starts
   __shared__ uint64_t s_gbase[kRadix];       // global digit starts for this partition
   __shared__ uint32_t s_w[kRadix / kWave];
+  __shared__ uint64_t s_cw[kRadix / kWave];
   __shared__ uint32_t s_part;
 
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  const bool owner = tid < kRadix;  // thread d < kRadix owns digit d
+  const bool owner = tid < kRadix;         // thread d < kRadix owns digit d
+  const int nd = 1 << bits;                // digits of this pass: the status words' stride
+  const bool live = owner && tid < nd;     // a digit keys can have
   const int64_t P = sort_count(Pmax, dcount);
   if (tid == 0) s_part = atomicAdd(tickets + pass, 1u);
   for (int i = tid; i < kWaves * kRadix; i += kNT) (&s_wh[0][0])[i] = 0;
+  // with the digit counts given, the digit bases are their exclusive scan, computed here
+  uint64_t cnt = 0, cinc = 0;
+  if (counts && owner) {
+    cnt = live ? counts[tid] : 0;
+    cinc = wave_inclusive_scan(cnt);
+    if (lane == kWave - 1) s_cw[wave] = cinc;
+  }
   __syncthreads();
   const int64_t part = s_part;
   const int64_t base = part * kPart;
@@ -205,8 +217,16 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
   if (base >= P) return;
   // start the look-back now: the predecessor's word for this thread's digit is usually
   // final by the time this partition has ranked its keys
-  uint64_t early = owner && part > 0 ? status_load(status + (part - 1) * kRadix + tid) : 0;
-  const uint64_t my_dbase = owner ? dbase[tid] : 0;  // this thread's digit's global base
+  uint64_t early = live && part > 0 ? status_load(status + (part - 1) * nd + tid) : 0;
+  uint64_t my_dbase = 0;  // this thread's digit's global base
+  if (owner) {
+    if (counts) {
+      my_dbase = cinc - cnt;
+      for (int w = 0; w < wave; ++w) my_dbase += s_cw[w];
+    } else {
+      my_dbase = dbase[tid];
+    }
+  }
 
   // wave-striped: wave w owns keys [w * 64 kKPT, (w + 1) * 64 kKPT) of the partition, in order
   K key[kKPT];
@@ -243,7 +263,7 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
   // digit owners: wave offsets, publish the partition's count, partition-local exclusive
   // scan over digits
   const int d = tid;
-  uint64_t* my_status = status + part * kRadix + d;
+  uint64_t* my_status = status + part * nd + d;
   uint32_t tot = 0, inc = 0;
   if (owner) {
 #pragma unroll
@@ -252,7 +272,7 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
       s_wh[w][d] = tot;
       tot += c;
     }
-    status_store(my_status, (part == 0 ? kFlagPre : kFlagAgg) | (uint64_t)tot);
+    if (live) status_store(my_status, (part == 0 ? kFlagPre : kFlagAgg) | (uint64_t)tot);
     inc = wave_inclusive_scan(tot);
     if (lane == kWave - 1) s_w[wave] = inc;
   }
@@ -277,8 +297,8 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
   // look back over earlier partitions for this digit's global offset
   if (owner) {
     uint64_t excl = 0;
-    if (part > 0) {
-      excl = lookback_exclusive(status + d, kRadix, part, early);
+    if (live && part > 0) {
+      excl = lookback_exclusive(status + d, nd, part, early);
       status_store(my_status, kFlagPre | (excl + tot));
     }
     s_gbase[d] = my_dbase + excl;
@@ -444,8 +464,22 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
   int32_t* plan = reinterpret_cast<int32_t*>(w + l.plan);
   uint32_t* tickets = reinterpret_cast<uint32_t*>(w + l.tickets);
   uint64_t* status = reinterpret_cast<uint64_t*>(w + l.status);
-  // zero histograms, plan, tickets and every pass's status words (no memset: capture-safe)
-  hipError_t e = launch_fill_u32(w, (int64_t)(l.total / 4), 0u, s);
+  // each pass's status words: one per partition and digit of that pass, packed
+  int pbits[kMaxPasses];
+  size_t poff[kMaxPasses], nstatus = 0;
+  for (int p = 0; p < passes; ++p) {
+    pbits[p] = hi - lo - 8 * p < 8 ? hi - lo - 8 * p : 8;
+    poff[p] = nstatus;
+    nstatus += (size_t)l.parts << pbits[p];
+  }
+  // given counts and every pass kept, the buffers and digit bases are known without the
+  // plan: the passes compute the bases from the counts (plan[kMaxPasses], the result's
+  // buffer, is then not written: the caller knows it from the pass count)
+  const bool planless = digit_counts && keep_all && !copy_back;
+  // zero what this sort reads before writing: histograms (unless counts are given), plan,
+  // tickets and the status words in use (no memset: capture-safe)
+  const size_t zfrom = digit_counts ? l.plan : l.hist;
+  hipError_t e = launch_fill_u32(w + zfrom, (int64_t)((l.status + sizeof(uint64_t) * nstatus - zfrom) / 4), 0u, s);
   if (e != hipSuccess) return e;
   if (!digit_counts) {
     const int64_t want = (P + kSortPart - 1) / kSortPart;
@@ -454,13 +488,13 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
         keys, P, dcount, lo, passes, hist);
   }
   // counts the caller already has ([pass][digit], one copy) replace the counting read
-  k_sort_plan<<<1, kRadix, 0, s>>>(digit_counts ? digit_counts : hist, digit_counts ? 1 : kHistCopies, dbase, plan,
-                                   passes, P, dcount, keep_all ? 1 : 0);
+  if (!planless)
+    k_sort_plan<<<1, kRadix, 0, s>>>(digit_counts ? digit_counts : hist, digit_counts ? 1 : kHistCopies, dbase, plan,
+                                     passes, P, dcount, keep_all ? 1 : 0);
   for (int p = 0; p < passes; ++p) {
-    const int bits = hi - lo - 8 * p < 8 ? hi - lo - 8 * p : 8;
     k_onesweep<K><<<(unsigned)((P + Onesweep<K>::part - 1) / Onesweep<K>::part), Onesweep<K>::threads, 0, s>>>(
-        keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p, bits, plan, dbase + p * kRadix,
-        status + (size_t)p * l.parts * kRadix, tickets);
+        keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p, pbits[p], plan, planless ? p % 2 : -1,
+        dbase + p * kRadix, planless ? digit_counts + p * kRadix : nullptr, status + poff[p], tickets);
   }
   if (copy_back) {
     const int64_t want = (P + 255) / 256;
