@@ -42,7 +42,8 @@
 namespace gs {
 
 hipError_t radix_sort_u32(int64_t P, const uint64_t* dcount, uint32_t* keys, uint32_t* vals, uint32_t* keys_tmp,
-                          uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back);
+                          uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back, bool ws_zeroed);
+size_t radix_zero_bytes(int64_t P, int lo, int hi);
 const int32_t* radix_result_in_tmp(const void* ws);
 hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
 size_t radix_workspace_bytes(int64_t P, int lo, int hi);
@@ -130,10 +131,14 @@ __global__ __launch_bounds__(kBinBlock) void k_compact(int64_t n, const uint32_t
                                                        const float* __restrict__ depth,
                                                        const uint64_t* __restrict__ vis_off,
                                                        uint32_t* __restrict__ dkeys, uint32_t* __restrict__ dvals,
-                                                       uint64_t* __restrict__ dcopies) {
+                                                       uint64_t* __restrict__ dcopies,
+                                                       uint32_t* __restrict__ sort_ws, int64_t sort_words) {
   __shared__ uint32_t s_w[kBinPer][kBinBlock / kWave];
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  // the depth sort's counters and look-back words start cleared (spread over the grid)
+  for (int64_t i = (int64_t)blockIdx.x * kBinBlock + tid; i < sort_words; i += (int64_t)gridDim.x * kBinBlock)
+    sort_ws[i] = 0;
   if (dcopies)  // cleared here (spread over the grid), added to by k_emit_count
     for (int i = (int)blockIdx.x * kBinBlock + tid; i < kDigitCopies * GS_TILE_DIGIT_COUNTS;
          i += (int)gridDim.x * kBinBlock)
@@ -678,9 +683,11 @@ hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, uint64_t* digit
   uint32_t* sn = reinterpret_cast<uint32_t*>(w + l.sn);
   k_compact<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, proj.n_tiles, proj.depth,
                                                  reinterpret_cast<const uint64_t*>(w + l.vis_sums), dk0, dv0,
-                                                 digit_counts ? reinterpret_cast<uint64_t*>(w + l.dcopies) : nullptr);
+                                                 digit_counts ? reinterpret_cast<uint64_t*>(w + l.dcopies) : nullptr,
+                                                 reinterpret_cast<uint32_t*>(w + l.sort),
+                                                 (int64_t)(radix_zero_bytes(n, 0, 32) / 4));
   // the sorted depths stay where the last pass wrote them: k_count_sorted picks the buffer
-  hipError_t e = radix_sort_u32(n, totals + 1, dk0, dv0, dk1, dv1, 0, 32, w + l.sort, s, false);
+  hipError_t e = radix_sort_u32(n, totals + 1, dk0, dv0, dk1, dv1, 0, 32, w + l.sort, s, false, true);
   if (e != hipSuccess) return e;
   k_count_sorted<<<(unsigned)l.nb, kBinBlock, 0, s>>>(totals + 1, radix_result_in_tmp(w + l.sort), dk0, dv0, dk1,
                                                       dv1, reinterpret_cast<const uint4*>(proj.runs), sruns, sn, ss);

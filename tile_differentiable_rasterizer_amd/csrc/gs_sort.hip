@@ -172,7 +172,8 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
     K* __restrict__ k0, uint32_t* __restrict__ v0, K* __restrict__ k1, uint32_t* __restrict__ v1,
     int64_t Pmax, const uint64_t* __restrict__ dcount, int pass, int shift, int bits,
     const int32_t* __restrict__ plan, int mode_arg, const uint64_t* __restrict__ dbase,
-    const uint64_t* __restrict__ counts, uint64_t* __restrict__ status, uint32_t* __restrict__ tickets) {
+    const uint64_t* __restrict__ counts, int copies, int32_t* __restrict__ result_word,
+    uint64_t* __restrict__ status, uint32_t* __restrict__ tickets) {
   // the buffers this pass reads and writes: given by the host when it knows them (no pass
   // skipped), else from the plan, which also marks passes to skip
   const int mode = mode_arg >= 0 ? mode_arg : plan[pass];
@@ -202,13 +203,20 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
   const int64_t P = sort_count(Pmax, dcount);
   if (tid == 0) s_part = atomicAdd(tickets + pass, 1u);
   for (int i = tid; i < kWaves * kRadix; i += kNT) (&s_wh[0][0])[i] = 0;
-  // with the digit counts given, the digit bases are their exclusive scan, computed here
-  uint64_t cnt = 0, cinc = 0;
-  if (counts && owner) {
-    cnt = live ? counts[tid] : 0;
-    cinc = wave_inclusive_scan(cnt);
-    if (lane == kWave - 1) s_cw[wave] = cinc;
+  // with the digit counts given (the sum of `copies` copies, kMaxPasses * kRadix words
+  // apart), the digit bases are their exclusive scan, computed with the partition's own
+  // digit scan below; the loads are issued now and complete behind the ranking
+  uint64_t cnt = 0;
+  if (counts && live) {
+    if (copies == kHistCopies) {
+#pragma unroll
+      for (int c = 0; c < kHistCopies; ++c) cnt += counts[c * kMaxPasses * kRadix + tid];
+    } else {
+      for (int c = 0; c < copies; ++c) cnt += counts[c * kMaxPasses * kRadix + tid];
+    }
   }
+  // without a plan, the last pass records which buffer holds the result
+  if (result_word && blockIdx.x == 0 && tid == 0) *result_word = mode ? 0 : 1;
   __syncthreads();
   const int64_t part = s_part;
   const int64_t base = part * kPart;
@@ -218,15 +226,7 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
   // start the look-back now: the predecessor's word for this thread's digit is usually
   // final by the time this partition has ranked its keys
   uint64_t early = live && part > 0 ? status_load(status + (part - 1) * nd + tid) : 0;
-  uint64_t my_dbase = 0;  // this thread's digit's global base
-  if (owner) {
-    if (counts) {
-      my_dbase = cinc - cnt;
-      for (int w = 0; w < wave; ++w) my_dbase += s_cw[w];
-    } else {
-      my_dbase = dbase[tid];
-    }
-  }
+  uint64_t my_dbase = owner && !counts ? dbase[tid] : 0;  // this thread's digit's global base
 
   // wave-striped: wave w owns keys [w * 64 kKPT, (w + 1) * 64 kKPT) of the partition, in order
   K key[kKPT];
@@ -275,12 +275,19 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
     if (live) status_store(my_status, (part == 0 ? kFlagPre : kFlagAgg) | (uint64_t)tot);
     inc = wave_inclusive_scan(tot);
     if (lane == kWave - 1) s_w[wave] = inc;
+    if (counts) {
+      const uint64_t cinc = wave_inclusive_scan(cnt);
+      if (lane == kWave - 1) s_cw[wave] = cinc;
+      my_dbase = cinc - cnt;
+    }
   }
   __syncthreads();
   if (owner) {
     uint32_t pre = inc - tot;
     for (int w = 0; w < wave; ++w) pre += s_w[w];
     s_lbase[d] = pre;
+    if (counts)
+      for (int w = 0; w < wave; ++w) my_dbase += s_cw[w];
   }
   __syncthreads();
   // reorder the partition by digit in LDS (stable)
@@ -452,7 +459,8 @@ size_t radix_workspace_bytes(int64_t P, int lo, int hi) { return sort_layout(P, 
 template <typename K>
 static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_t* vals, K* keys_tmp,
                              uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back = true,
-                             bool keep_all = false, const uint64_t* digit_counts = nullptr) {
+                             bool keep_all = false, const uint64_t* digit_counts = nullptr,
+                             bool ws_zeroed = false) {
   const int passes = radix_passes(lo, hi);
   char* w = static_cast<char*>(ws);
   if (P <= 1 || passes == 0)  // nothing moves: the result is in keys/vals, as the word says
@@ -472,14 +480,18 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
     poff[p] = nstatus;
     nstatus += (size_t)l.parts << pbits[p];
   }
-  // given counts and every pass kept, the buffers and digit bases are known without the
-  // plan: the passes compute the bases from the counts (plan[kMaxPasses], the result's
-  // buffer, is then not written: the caller knows it from the pass count)
+  // with the digit counts given and every pass kept, the buffers are known without the
+  // plan and the passes compute the digit bases from the counts; the last pass writes the
+  // result's buffer word.  (Scanning the histogram's 16 copies in every workgroup instead
+  // of once in the plan measured slower: 15.9 -> 18.8 us per 32-bit pass at 1M keys.)
   const bool planless = digit_counts && keep_all && !copy_back;
   // zero what this sort reads before writing: histograms (unless counts are given), plan,
   // tickets and the status words in use (no memset: capture-safe)
+  // (ws_zeroed: the caller's previous kernel cleared radix_zero_bytes of the workspace)
   const size_t zfrom = digit_counts ? l.plan : l.hist;
-  hipError_t e = launch_fill_u32(w + zfrom, (int64_t)((l.status + sizeof(uint64_t) * nstatus - zfrom) / 4), 0u, s);
+  hipError_t e = hipSuccess;
+  if (!ws_zeroed)
+    e = launch_fill_u32(w + zfrom, (int64_t)((l.status + sizeof(uint64_t) * nstatus - zfrom) / 4), 0u, s);
   if (e != hipSuccess) return e;
   if (!digit_counts) {
     const int64_t want = (P + kSortPart - 1) / kSortPart;
@@ -494,7 +506,8 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
   for (int p = 0; p < passes; ++p) {
     k_onesweep<K><<<(unsigned)((P + Onesweep<K>::part - 1) / Onesweep<K>::part), Onesweep<K>::threads, 0, s>>>(
         keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p, pbits[p], plan, planless ? p % 2 : -1,
-        dbase + p * kRadix, planless ? digit_counts + p * kRadix : nullptr, status + poff[p], tickets);
+        dbase + p * kRadix, planless ? digit_counts + p * kRadix : nullptr, 1,
+        planless && p == passes - 1 ? plan + kMaxPasses : nullptr, status + poff[p], tickets);
   }
   if (copy_back) {
     const int64_t want = (P + 255) / 256;
@@ -505,8 +518,36 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
 }
 
 hipError_t radix_sort_u32(int64_t P, const uint64_t* dcount, uint32_t* keys, uint32_t* vals, uint32_t* keys_tmp,
-                          uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back) {
-  return radix_sort<uint32_t>(P, dcount, keys, vals, keys_tmp, vals_tmp, lo, hi, ws, s, copy_back);
+                          uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back, bool ws_zeroed) {
+  return radix_sort<uint32_t>(P, dcount, keys, vals, keys_tmp, vals_tmp, lo, hi, ws, s, copy_back, false, nullptr,
+                              ws_zeroed);
+}
+
+// The part of a sort workspace that a sort of P keys over bits [lo, hi) reads before it
+// writes, and so needs cleared: [*off, *off + *len) bytes.  Histograms (only when the sort
+// counts the digits itself), plan, tickets and the status words in use.
+void radix_zero_span(int64_t P, int lo, int hi, bool counts_given, size_t* off, size_t* len) {
+  const int passes = radix_passes(lo, hi);
+  const SortLayout l = sort_layout(P, passes);
+  size_t nstatus = 0;
+  for (int p = 0; p < passes; ++p) nstatus += (size_t)l.parts << (hi - lo - 8 * p < 8 ? hi - lo - 8 * p : 8);
+  *off = counts_given ? l.plan : l.hist;
+  *len = l.status + sizeof(uint64_t) * nstatus - *off;
+}
+size_t radix_zero_bytes(int64_t P, int lo, int hi) {
+  size_t off, len;
+  radix_zero_span(P, lo, hi, false, &off, &len);
+  return off + len;
+}
+
+// Two regions of 32-bit words set to zero in one launch.
+__global__ void k_zero2(uint32_t* __restrict__ a, int64_t na, uint32_t* __restrict__ b, int64_t nb) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < na + nb; i += (int64_t)gridDim.x * blockDim.x) {
+    if (i < na)
+      a[i] = 0u;
+    else
+      b[i - na] = 0u;
+  }
 }
 
 // Device word that a sort run with copy_back = false sets to 1 when its result is in the
@@ -525,13 +566,22 @@ size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_b
 hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
                        uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits,
                        const uint64_t* digit_counts, int32_t* result_in_tmp, void* ws, hipStream_t s) {
-  hipError_t e = launch_fill_u32(ranges, 4 * num_tiles, 0u, s);
   const int hi = sort_significant_bits(num_tiles);
   const int passes = P > 1 ? radix_passes(sorted_low_bits, hi) : 0;
   const bool in_tmp = passes % 2 == 1;
-  if (e == hipSuccess && passes > 0)
+  hipError_t e = hipSuccess;
+  if (passes > 0) {  // the ranges and the sort's counters and look-back words, cleared together
+    size_t off, len;
+    radix_zero_span(P, sorted_low_bits, hi, digit_counts != nullptr, &off, &len);
+    const int64_t words = 4 * num_tiles + (int64_t)(len / 4);
+    const unsigned blocks = (unsigned)min((words + 255) / 256, (int64_t)4096);
+    k_zero2<<<blocks, 256, 0, s>>>(reinterpret_cast<uint32_t*>(ranges), 4 * num_tiles,
+                                   reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + off), (int64_t)(len / 4));
     e = radix_sort<uint64_t>(P, nullptr, keys, vals, keys_tmp, vals_tmp, sorted_low_bits, hi, ws, s, false, true,
-                             digit_counts);
+                             digit_counts, true);
+  } else {
+    e = launch_fill_u32(ranges, 4 * num_tiles, 0u, s);
+  }
   if (e != hipSuccess) return e;
   const bool move = in_tmp && !result_in_tmp;
   if (P > 0)
