@@ -36,15 +36,15 @@ constexpr int kSortPart = kHistThreads * kSortKPT;  // keys per histogram round
 // A onesweep partition holds 4096 keys.  Its workgroup size, by key width: with more lanes
 // each holds fewer keys, and the ranking (a chain of dependent ballots per key) has more
 // wavefronts per SIMD to interleave.
-constexpr int kOnesweepPart = 4096;
+constexpr int kOnesweepPart32 = 4096, kOnesweepPart64 = 4096;
 constexpr int kOnesweepThreads32 = 1024, kOnesweepThreads64 = 1024;
 template <typename K>
 struct Onesweep {
   static constexpr int threads = sizeof(K) == 8 ? kOnesweepThreads64 : kOnesweepThreads32;
-  static constexpr int part = kOnesweepPart;
+  static constexpr int part = sizeof(K) == 8 ? kOnesweepPart64 : kOnesweepPart32;
   static constexpr int kpt = part / threads;
 };
-constexpr int kMinPart = kOnesweepPart;
+constexpr int kMinPart = kOnesweepPart32 < kOnesweepPart64 ? kOnesweepPart32 : kOnesweepPart64;
 constexpr int kRadix = 256;
 constexpr int kMaxPasses = 8;
 constexpr int kHistCopies = 16;                   // global histogram copies (spreads the atomics)
