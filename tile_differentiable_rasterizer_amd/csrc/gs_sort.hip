@@ -9,18 +9,20 @@
 //
 // Structure (the decoupled look-back scheme of Merrill & Garland, and the single-pass radix
 // sort of Adinets & Merrill, re-designed for 64-wide wavefronts):
-//   k_sort_hist   one read of the keys: histograms of every 8-bit digit at once
+//   k_sort_hist   one read of the keys: histograms of every 8-bit digit at once (skipped
+//                 when the caller has the digit counts, as the binning does for its pairs)
 //   k_sort_plan   exclusive scan of each histogram (global digit bases); marks digits that
 //                 are constant over all keys (those passes are skipped unless the caller
 //                 needs every pass) and assigns the ping-pong buffers on the device, so no
-//                 host round trip is needed
-//   k_onesweep    per pass: each workgroup takes a 4096-key partition by atomic ticket,
-//                 ranks its keys stably (wavefront ballots match equal digits; per-wave
-//                 digit counters in LDS, advanced with pipelined LDS atomics), publishes
-//                 per-digit counts and resolves its
-//                 global offsets by looking back over earlier partitions' published
-//                 counts (several earlier partitions per round trip), reorders the
-//                 partition in LDS by digit and writes each digit's run contiguously
+//                 host round trip is needed.  Not launched when the counts are given and
+//                 every pass is kept: the passes then scan the counts themselves
+//   k_onesweep    per pass: each 1024-lane workgroup takes a 4096-key partition by atomic
+//                 ticket, ranks its keys stably (wavefront ballots match equal digits;
+//                 per-wave digit counters in LDS, advanced with pipelined LDS atomics),
+//                 publishes per-digit counts and resolves its global offsets by looking
+//                 back over earlier partitions' published counts (several earlier
+//                 partitions per round trip), reorders the partition in LDS by digit and
+//                 writes each digit's run contiguously
 //   k_sort_copy   moves the result back to keys/vals after an odd number of passes, for
 //                 callers that need it there
 //   k_ranges      [first, last + 1) of every tile from the sorted keys; for a pair sort
@@ -29,13 +31,13 @@
 
 namespace gs {
 
-constexpr int kSortBlock = 256;
+constexpr int kSortBlock = 256;                     // digit-wide kernels: one lane per digit value
 constexpr int kHistThreads = 1024;                  // histogram workgroup: 16 wavefronts
 constexpr int kSortKPT = 4;                         // keys per thread of the histogram
 constexpr int kSortPart = kHistThreads * kSortKPT;  // keys per histogram round
-// A onesweep partition holds 4096 keys.  Its workgroup size, by key width: with more lanes
-// each holds fewer keys, and the ranking (a chain of dependent ballots per key) has more
-// wavefronts per SIMD to interleave.
+// Onesweep partition and workgroup sizes, by key width: with more lanes each holds fewer
+// keys, and the ranking (a chain of dependent ballots per key) has more wavefronts per
+// SIMD to interleave.
 constexpr int kOnesweepPart32 = 4096, kOnesweepPart64 = 4096;
 constexpr int kOnesweepThreads32 = 1024, kOnesweepThreads64 = 1024;
 template <typename K>
