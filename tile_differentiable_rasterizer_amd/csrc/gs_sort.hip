@@ -31,7 +31,6 @@
 
 namespace gs {
 
-constexpr int kSortBlock = 256;                     // digit-wide kernels: one lane per digit value
 constexpr int kHistThreads = 1024;                  // histogram workgroup: 16 wavefronts
 constexpr int kSortKPT = 4;                         // keys per thread of the histogram
 constexpr int kSortPart = kHistThreads * kSortKPT;  // keys per histogram round
