@@ -369,15 +369,53 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
   }
 }
 
+// Adds the pairs [sa, sb) of a Gaussian's kept tiles that lie on one row, tile ids
+// t0 .. t0 + (sb - sa) - 1 (consecutive), to the counts of the partitions they fall in: the
+// tile's low byte through a difference array per partition (a circular run of digits adds
+// 1 at its start and -1 past its end; whole turns of 256 add to every digit), the higher
+// tile digits directly.
+__device__ __forceinline__ void count_row_segment(int64_t sa, int64_t sb, uint32_t t0, int64_t chunk_first_part,
+                                                  int hp, int32_t (*s_diff)[kDigits + 1], uint32_t* s_uni,
+                                                  uint32_t* s_hi) {
+  while (sa < sb) {
+    const int64_t q = sa / kEmitPart;  // partition
+    const int64_t end = min(sb, (q + 1) * kEmitPart);
+    const uint32_t L = (uint32_t)(end - sa);
+    const int qi = (int)(q - chunk_first_part);
+    if (L >> 8) atomicAdd(&s_uni[qi], L >> 8);
+    const uint32_t rem = L & (kDigits - 1);
+    if (rem) {
+      const uint32_t a = t0 & (kDigits - 1), b = a + rem;
+      atomicAdd(&s_diff[qi][a], 1);
+      if (b <= (uint32_t)kDigits) {
+        atomicAdd(&s_diff[qi][b], -1);
+      } else {
+        atomicAdd(&s_diff[qi][0], 1);
+        atomicAdd(&s_diff[qi][b - kDigits], -1);
+      }
+    }
+    const uint32_t t1 = t0 + L - 1;
+    for (int p = 0; p < hp; ++p) {
+      const int sh = 8 + 8 * p;
+      for (uint32_t h = t0 >> sh; h <= t1 >> sh; ++h) {
+        const uint32_t lo = max(t0, h << sh), hi = min(t1, ((h + 1) << sh) - 1u);
+        atomicAdd(&s_hi[p * kDigits + (h & (kDigits - 1))], hi - lo + 1);
+      }
+    }
+    t0 += L;
+    sa = end;
+  }
+}
+
 // Counting pass: per partition, how many of its pairs have each value of the tile's low
-// byte.  A workgroup takes kCountParts consecutive partitions and writes, per partition,
-// the counts of the chunk's earlier partitions (cnt_pre[b][d]) and, per chunk, its totals
-// (csum[c][d]); both are contiguous rows.  With hp > 0 it also counts the tile-id digits
-// above the low byte (bits [8 + 8q, 16 + 8q), q < hp) for the pair sort and adds the
-// chunk's counts to copy (chunk mod kDigitCopies) of them in dcopies (one copy takes too
-// many atomics per address).  A lane's consecutive pairs
-// mostly share those digits (they lie along tile rows), so each lane sums its run of
-// equal values in a register and adds it when the value changes.
+// byte.  A workgroup takes kCountParts consecutive partitions (a chunk) and writes, per
+// partition, the counts of the chunk's earlier partitions (cnt_pre[b][d]) and, per chunk,
+// its totals (csum[c][d]); both are contiguous rows.  The pairs are not generated one by
+// one: each lane takes whole Gaussians of the chunk and walks their kept tile rows (the
+// same records and order the scattering pass expands), adding each row's run of
+// consecutive tile ids at once.  With hp > 0 it also counts the tile-id digits above the
+// low byte (bits [8 + 8q, 16 + 8q), q < hp) for the pair sort, into copy (chunk mod
+// kDigitCopies) of them in dcopies.
 __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __restrict__ vcount, int64_t P,
                                                           int64_t nparts,
                                                           const uint4* __restrict__ sruns,
@@ -386,47 +424,73 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __rest
                                                           uint32_t* __restrict__ cnt_pre,
                                                           uint64_t* __restrict__ csum, int hp,
                                                           uint64_t* __restrict__ dcopies) {
-  __shared__ int32_t s_rel[kEmitPart + 2];
-  __shared__ uint32_t s_h[kBinBlock / kWave][kDigits];
+  __shared__ int32_t s_diff[kCountParts][kDigits + 1];
+  __shared__ uint32_t s_uni[kCountParts];
   __shared__ uint32_t s_hi[GS_TILE_DIGIT_COUNTS];  // the chunk's counts of the higher digits
-  const int tid = threadIdx.x, wave = tid / kWave;
+  __shared__ uint32_t s_w[kCountParts][kBinBlock / kWave];
+  const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   const int64_t v = (int64_t)*vcount;
+  const int64_t b0 = (int64_t)blockIdx.x * kCountParts;
+  const int nq = (int)min((int64_t)kCountParts, nparts - b0);
+  for (int i = tid; i < kCountParts * (kDigits + 1); i += kBinBlock) (&s_diff[0][0])[i] = 0;
+  if (tid < kCountParts) s_uni[tid] = 0;
   for (int i = tid; i < hp * kDigits; i += kBinBlock) s_hi[i] = 0;
-  uint32_t running = 0;  // digit tid's count in the chunk's earlier partitions
-  for (int q = 0; q < kCountParts; ++q) {
-    const int64_t b = (int64_t)blockIdx.x * kCountParts + q;
-    if (b >= nparts) break;
-    for (int i = tid; i < (kBinBlock / kWave) * kDigits; i += kBinBlock) (&s_h[0][0])[i] = 0;
-    const EmitPart e = stage_partition(b, nparts, v, P, goff, gstart, s_rel);
-    __syncthreads();
-    uint32_t cur[2] = {0xFFFFFFFFu, 0xFFFFFFFFu}, run[2] = {0u, 0u};  // this lane's current run per digit
-    lane_pairs<false>(e, s_rel, sruns, tiles_x, [&](int, uint32_t tile, uint32_t, uint32_t) {
-      atomicAdd(&s_h[wave][tile & (kDigits - 1)], 1u);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        if (q >= hp) break;
-        const uint32_t h = (tile >> (8 + 8 * q)) & (kDigits - 1);
-        if (h != cur[q]) {
-          if (run[q]) atomicAdd(&s_hi[q * kDigits + cur[q]], run[q]);
-          cur[q] = h;
-          run[q] = 0;
-        }
-        ++run[q];
+  __syncthreads();
+  // the chunk's pairs [r0, r1) and the Gaussians holding them
+  const int64_t r0 = b0 * kEmitPart, r1 = min((b0 + nq) * kEmitPart, P);
+  const int64_t g_first = gstart[b0];
+  const int64_t g_last = b0 + nq < nparts ? (int64_t)gstart[b0 + nq] : v - 1;
+  for (int64_t g = g_first + tid; g <= g_last; g += kBinBlock) {
+    const int64_t G0 = (int64_t)goff[g], G1 = (int64_t)goff[g + 1];
+    const int64_t lo = max(G0, r0), hi = min(G1, r1);  // this Gaussian's pairs in the chunk
+    if (lo >= hi) continue;
+    const uint4 sp = sruns[2 * g], rb = sruns[2 * g + 1];
+    const int tx0 = (int)(rb.x & 0xFFFFu), tx1 = (int)(rb.x >> 16);
+    const int ty0 = (int)(rb.y & 0xFFFFu), ty1 = (int)(rb.y >> 16);
+    if (spans_packed(sp)) {  // at most kSpanRows rows, each its own run of kept columns
+      int64_t off = G0;
+      for (int ty = ty0; ty <= ty1 && off < hi; ++ty) {
+        int c0, c1;
+        packed_row(sp, ty - ty0, tx0, c0, c1);
+        if (c1 < c0) continue;
+        const int64_t len = c1 - c0 + 1;
+        const int64_t sa = max(off, lo), sb = min(off + len, hi);
+        if (sa < sb)
+          count_row_segment(sa, sb, (uint32_t)ty * (uint32_t)tiles_x + (uint32_t)c0 + (uint32_t)(sa - off), b0, hp,
+                            s_diff, s_uni, s_hi);
+        off += len;
       }
-    });
+    } else {  // every tile of the rectangle: rows of equal length, so start at the first row in range
+      const int64_t w = tx1 - tx0 + 1;
+      for (int64_t r = (lo - G0) / w; G0 + r * w < hi; ++r) {
+        const int64_t off = G0 + r * w;
+        const int64_t sa = max(off, lo), sb = min(off + w, hi);
+        count_row_segment(sa, sb, (uint32_t)(ty0 + r) * (uint32_t)tiles_x + (uint32_t)tx0 + (uint32_t)(sa - off), b0,
+                          hp, s_diff, s_uni, s_hi);
+      }
+    }
+  }
+  __syncthreads();
+  // counts per partition: the inclusive scan of its difference array over digits
+  uint32_t cnt[kCountParts];
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (q < hp && run[q]) atomicAdd(&s_hi[q * kDigits + cur[q]], run[q]);
-    __syncthreads();
-    uint32_t c = 0;
+  for (int q = 0; q < kCountParts; ++q) {
+    const uint32_t x = (uint32_t)s_diff[q][tid];
+    const uint32_t inc = wave_inclusive_scan(x);
+    if (lane == kWave - 1) s_w[q][wave] = inc;
+    cnt[q] = inc;
+  }
+  __syncthreads();
+  uint32_t running = 0;  // digit tid's count in the chunk's earlier partitions
 #pragma unroll
-    for (int w = 0; w < kBinBlock / kWave; ++w) c += s_h[w][tid];
-    cnt_pre[b * kDigits + tid] = running;
+  for (int q = 0; q < kCountParts; ++q) {
+    if (q >= nq) break;
+    uint32_t c = cnt[q] + s_uni[q];
+    for (int w = 0; w < wave; ++w) c += s_w[q][w];
+    cnt_pre[(b0 + q) * kDigits + tid] = running;
     running += c;
-    __syncthreads();  // the next partition reuses s_rel and s_h
   }
   csum[(int64_t)blockIdx.x * kDigits + tid] = running;
-  // s_hi is complete: the partition loop ended on a barrier
   uint64_t* dc = dcopies + (blockIdx.x % kDigitCopies) * GS_TILE_DIGIT_COUNTS;
   for (int i = tid; i < hp * kDigits; i += kBinBlock)
     if (s_hi[i]) atomicAdd(reinterpret_cast<unsigned long long*>(dc + i), (unsigned long long)s_hi[i]);
@@ -598,8 +662,10 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
     const uint64_t k = s_keys[i];
     const uint32_t d = (uint32_t)(k >> 32) & (kDigits - 1);
     const uint64_t g = s_gbase[d] + (uint64_t)(i - (int)s_lbase[d]);
-    keys[g] = k;
-    vals[g] = s_vals[i];
+    if (g < (uint64_t)P) {  // always, given the counting pass's counts
+      keys[g] = k;
+      vals[g] = s_vals[i];
+    }
   }
 }
 
