@@ -214,10 +214,11 @@ constexpr uint64_t kRedLanes2 = kRedLanes0 << 40;
 // One record's ten gradient terms at this lane's pixel, written to g[0..9] (terms 2..4
 // before term_scale); zeros where the record did not contribute (a later position than
 // the pixel's last contributor, or alpha < 1/255).  Branch-free: a non-contributing lane
-// computes with a zero weight and keeps its walk state.  Returns whether it contributed.
+// computes with a zero weight and keeps its walk state.  Returns the wavefront's lanes that
+// contributed (taken from the compare's lane mask where it is formed).
 //   dL/dalpha = T_k (dL . rgb) - H / (1 - alpha), with T_k = T / (1 - alpha) in front of
 //   the record and H the dL-weighted colour behind it; then H += (dL . rgb) alpha T_k.
-__device__ __forceinline__ bool bwd_record(const float4* __restrict__ s_rec, int j, uint32_t k, BwdPixel& p,
+__device__ __forceinline__ uint64_t bwd_record(const float4* __restrict__ s_rec, int j, uint32_t k, BwdPixel& p,
                                            float* __restrict__ g) {
   const float4 s0 = s_rec[4 * j], s1 = s_rec[4 * j + 1], s2 = s_rec[4 * j + 2], s3 = s_rec[4 * j + 3];
   const float dx = p.fx - s0.x, dy = p.fy - s0.y;
@@ -225,6 +226,9 @@ __device__ __forceinline__ bool bwd_record(const float4* __restrict__ s_rec, int
   const float oG = s1.y * G;
   const float alpha = fminf(kAlphaMax, oG);
   const bool contrib = k < p.nc && alpha >= kAlphaMin;
+  // the same two compares as lane masks (ICmp ULT = 36, FCmp OGE = 3), so the wavefront's
+  // contributing lanes come straight from them
+  const uint64_t hits = __builtin_amdgcn_uicmp(k, p.nc, 36) & __builtin_amdgcn_fcmpf(alpha, kAlphaMin, 3);
   // hardware reciprocal (about 1 ulp): T is recovered from the stored final T by repeated
   // division, whose float32 error stays far below the gradient tolerance
   const float iom = __builtin_amdgcn_rcpf(1.0f - alpha);
@@ -247,7 +251,7 @@ __device__ __forceinline__ bool bwd_record(const float4* __restrict__ s_rec, int
   g[0] = fmaf(s3.x, dqx, s3.y * dqy);
   g[1] = fmaf(s3.y, dqx, s3.z * dqy);
   g[9] = __builtin_amdgcn_sqrtf(fmaf(g[0], g[0], g[1] * g[1]));
-  return contrib;
+  return hits;
 }
 
 __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
@@ -336,12 +340,12 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
         if (has) m &= ~(1ull << bit);
       }
       float v[32];
-      bool hit[3];
+      uint64_t hm[3];
 #pragma unroll
-      for (int r = 0; r < 3; ++r) hit[r] = bwd_record(my, js[r], ks[r], p, v + GS_GRAD_SCREEN * r);
+      for (int r = 0; r < 3; ++r) hm[r] = bwd_record(my, js[r], ks[r], p, v + GS_GRAD_SCREEN * r);
       v[30] = 0.0f;
       v[31] = 0.0f;
-      const uint64_t h0 = __ballot(hit[0]), h1 = __ballot(hit[1]), h2 = __ballot(hit[2]);
+      const uint64_t h0 = hm[0], h1 = hm[1], h2 = hm[2];
       if (h0 | h1 | h2) {
         // lanes 2i and 2i + 1 now hold the wavefront's sum of v[i]; the even lane of each
         // (record, term) pair of a record some pixel took adds it to the Gaussian's gradient
