@@ -219,8 +219,9 @@ constexpr uint64_t kRedLanes2 = kRedLanes0 << 40;
 //   dL/dalpha = T_k (dL . rgb) - H / (1 - alpha), with T_k = T / (1 - alpha) in front of
 //   the record and H the dL-weighted colour behind it; then H += (dL . rgb) alpha T_k.
 __device__ __forceinline__ uint64_t bwd_record(const float4* __restrict__ s_rec, int j, uint32_t k, BwdPixel& p,
-                                           float* __restrict__ g) {
+                                               float* __restrict__ g, uint32_t& id) {
   const float4 s0 = s_rec[4 * j], s1 = s_rec[4 * j + 1], s2 = s_rec[4 * j + 2], s3 = s_rec[4 * j + 3];
+  id = __float_as_uint(s2.w);  // the Gaussian the record belongs to
   const float dx = p.fx - s0.x, dy = p.fy - s0.y;
   const float G = gauss_factor(gauss_exponent(s0.z, s0.w, s1.x, dx, dy));
   const float oG = s1.y * G;
@@ -341,8 +342,9 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
       }
       float v[32];
       uint64_t hm[3];
+      uint32_t ids[3];
 #pragma unroll
-      for (int r = 0; r < 3; ++r) hm[r] = bwd_record(my, js[r], ks[r], p, v + GS_GRAD_SCREEN * r);
+      for (int r = 0; r < 3; ++r) hm[r] = bwd_record(my, js[r], ks[r], p, v + GS_GRAD_SCREEN * r, ids[r]);
       v[30] = 0.0f;
       v[31] = 0.0f;
       const uint64_t h0 = hm[0], h1 = hm[1], h2 = hm[2];
@@ -351,11 +353,8 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
         // (record, term) pair of a record some pixel took adds it to the Gaussian's gradient
         const float sum = wave_transpose_reduce32(v);
         const uint64_t act = (h0 ? kRedLanes0 : 0ull) | (h1 ? kRedLanes1 : 0ull) | (h2 ? kRedLanes2 : 0ull);
-        const int jr = red_r == 0 ? js[0] : red_r == 1 ? js[1] : js[2];
-        if ((act >> lane) & 1ull) {
-          const uint32_t id = __float_as_uint(my[4 * jr + 2].w);
-          atomicAdd(gscreen + (size_t)GS_GRAD_SCREEN * id + red_e, sum * red_scale);
-        }
+        const uint32_t id = red_r == 0 ? ids[0] : red_r == 1 ? ids[1] : ids[2];
+        if ((act >> lane) & 1ull) atomicAdd(gscreen + (size_t)GS_GRAD_SCREEN * id + red_e, sum * red_scale);
       }
     }
   }
