@@ -199,6 +199,7 @@ struct BwdPixel {
   float H;             // sum over channels of dL/dpixel * (colour behind it, background included)
   float dr, dg, db;    // dL/dpixel
   uint32_t nc;         // records at positions >= nc did not contribute
+  int32_t ncr;         // nc relative to the first position of the chunk being walked
 };
 
 // Exact scale of each reduced term to its gradient: terms 2..4 are summed as
@@ -213,12 +214,13 @@ constexpr uint64_t kRedLanes2 = kRedLanes0 << 40;
 
 // One record's ten gradient terms at this lane's pixel, written to g[0..9] (terms 2..4
 // before term_scale); zeros where the record did not contribute (a later position than
-// the pixel's last contributor, or alpha < 1/255).  Branch-free: a non-contributing lane
+// the pixel's last contributor, or alpha < 1/255).  kr is the record's position relative
+// to the chunk's first (p.ncr is the pixel's count on the same scale).  Branch-free: a non-contributing lane
 // computes with a zero weight and keeps its walk state.  Returns the wavefront's lanes that
 // contributed (taken from the compare's lane mask where it is formed).
 //   dL/dalpha = T_k (dL . rgb) - H / (1 - alpha), with T_k = T / (1 - alpha) in front of
 //   the record and H the dL-weighted colour behind it; then H += (dL . rgb) alpha T_k.
-__device__ __forceinline__ uint64_t bwd_record(const float4* __restrict__ s_rec, int j, uint32_t k, BwdPixel& p,
+__device__ __forceinline__ uint64_t bwd_record(const float4* __restrict__ s_rec, int j, int32_t kr, BwdPixel& p,
                                                float* __restrict__ g, uint32_t& id) {
   const float4 s0 = s_rec[4 * j], s1 = s_rec[4 * j + 1], s2 = s_rec[4 * j + 2], s3 = s_rec[4 * j + 3];
   id = __float_as_uint(s2.w);  // the Gaussian the record belongs to
@@ -226,10 +228,10 @@ __device__ __forceinline__ uint64_t bwd_record(const float4* __restrict__ s_rec,
   const float G = gauss_factor(gauss_exponent(s0.z, s0.w, s1.x, dx, dy));
   const float oG = s1.y * G;
   const float alpha = fminf(kAlphaMax, oG);
-  const bool contrib = k < p.nc && alpha >= kAlphaMin;
-  // the same two compares as lane masks (ICmp ULT = 36, FCmp OGE = 3), so the wavefront's
+  const bool contrib = kr < p.ncr && alpha >= kAlphaMin;
+  // the same two compares as lane masks (ICmp SLT = 40, FCmp OGE = 3), so the wavefront's
   // contributing lanes come straight from them
-  const uint64_t hits = __builtin_amdgcn_uicmp(k, p.nc, 36) & __builtin_amdgcn_fcmpf(alpha, kAlphaMin, 3);
+  const uint64_t hits = __builtin_amdgcn_sicmp(kr, p.ncr, 40) & __builtin_amdgcn_fcmpf(alpha, kAlphaMin, 3);
   // hardware reciprocal (about 1 ulp): T is recovered from the stored final T by repeated
   // division, whose float32 error stays far below the gradient tolerance
   const float iom = __builtin_amdgcn_rcpf(1.0f - alpha);
@@ -318,6 +320,7 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
       __builtin_amdgcn_wave_barrier();
     }
     uint64_t m = __ballot(reach);
+    p.ncr = (int32_t)p.nc - (int32_t)(lo - start);
     {  // prefetch the next (earlier) chunk
       const int64_t nhi = lo, nlo = nhi - kWave > start ? nhi - kWave : start;
       if (nlo + lane < nhi) {
@@ -328,16 +331,16 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
     while (m) {
       // the next three records of the reverse walk (highest position first); the bit
       // positions stay scalar so the walk is a uniform loop.  A step short of three
-      // records repeats the first one at position 2^32 - 1, past every pixel's last
-      // contributor, so it adds zeros and leaves the walk unchanged.
+      // records repeats the first one at relative position 2^31 - 1, past every pixel's
+      // last contributor, so it adds zeros and leaves the walk unchanged.
       int js[3];
-      uint32_t ks[3];
+      int32_t ks[3];
 #pragma unroll
       for (int r = 0; r < 3; ++r) {
         const bool has = m != 0;
         const int bit = has ? __builtin_amdgcn_readfirstlane(63 - __builtin_clzll(m)) : 0;
         js[r] = has ? bit : js[0];
-        ks[r] = has ? (uint32_t)(lo - start + bit) : 0xFFFFFFFFu;
+        ks[r] = has ? bit : INT32_MAX;
         if (has) m &= ~(1ull << bit);
       }
       float v[32];
