@@ -576,21 +576,17 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
   __shared__ uint32_t s_lbase[kDigits];                    // partition-local digit starts
   __shared__ uint64_t s_gbase[kDigits];                    // global digit starts for this partition
   __shared__ uint64_t s_w[kBinBlock / kWave];
+  __shared__ uint64_t s_gw[kBinBlock / kWave];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   const int64_t v = (int64_t)*vcount;
   for (int i = tid; i < (kBinBlock / kWave) * kDigits; i += kBinBlock) (&s_wh[0][0])[i] = 0;
   const int64_t b = xcd_contiguous(blockIdx.x, nparts);
+  // digit tid's total and its count in earlier partitions: loaded now, used once the pairs
+  // are ranked (the global start of this partition's run of the digit)
+  const uint64_t gtot = totals[tid];
+  const uint64_t gpart = cpre[(b / kCountParts) * kDigits + tid] + cnt_pre[b * kDigits + tid];
   const EmitPart e = stage_partition(b, nparts, v, P, goff, gstart, s_rel);
-  {  // global start of this partition's run of digit d = tid: the digit's base plus its
-     // count in earlier partitions
-    const uint64_t tot = totals[tid];
-    const uint64_t inc = wave_inclusive_scan(tot);
-    if (lane == kWave - 1) s_w[wave] = inc;
-    __syncthreads();
-    uint64_t pre = inc - tot;
-    for (int w = 0; w < wave; ++w) pre += s_w[w];
-    s_gbase[tid] = pre + cpre[(b / kCountParts) * kDigits + tid] + cnt_pre[b * kDigits + tid];
-  }
+  __syncthreads();
   // generate: lane-consecutive, one pad slot per lane so that a wavefront's 8-byte
   // stores spread over the LDS banks
   lane_pairs<true>(e, s_rel, sruns, tiles_x, [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
@@ -630,7 +626,9 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
 #pragma unroll
   for (int j = 0; j < kEmitPer; ++j) rank[j] += (uint32_t)__shfl((int)prev[j], lead[j], kWave);
   __syncthreads();
-  {  // thread d owns digit d: per-wave offsets, then the partition-local digit starts
+  {  // thread d owns digit d: per-wave offsets, the partition-local digit starts, and the
+     // global start of the partition's run of d (the digit's base over all digits before it,
+     // plus its count in earlier partitions)
     const int d = tid;
     uint32_t tot = 0;
 #pragma unroll
@@ -640,11 +638,19 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
       tot += c;
     }
     const uint64_t inc = wave_inclusive_scan((uint64_t)tot);
-    if (lane == kWave - 1) s_w[wave] = inc;
+    const uint64_t ginc = wave_inclusive_scan(gtot);
+    if (lane == kWave - 1) {
+      s_w[wave] = inc;
+      s_gw[wave] = ginc;
+    }
     __syncthreads();
-    uint64_t pre = inc - tot;
-    for (int w = 0; w < wave; ++w) pre += s_w[w];
+    uint64_t pre = inc - tot, gpre = ginc - gtot;
+    for (int w = 0; w < wave; ++w) {
+      pre += s_w[w];
+      gpre += s_gw[w];
+    }
     s_lbase[d] = (uint32_t)pre;
+    s_gbase[d] = gpre + gpart;
   }
   __syncthreads();
 #pragma unroll
