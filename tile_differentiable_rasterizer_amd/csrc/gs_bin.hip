@@ -33,7 +33,8 @@
 //                    Gaussian
 //   k_emit_count     per chunk of 8 partitions: counts of the tile's low byte, per
 //                    partition as prefixes inside the chunk, and the chunk's totals
-//   k_digit_scan     per digit: exclusive scan of the chunk totals, and the digit's total
+//   k_group_scan,    exclusive scan of the chunk totals over chunks, per digit, in two
+//   k_digit_scan     levels (groups of chunks, then the groups); the digits' totals
 //   k_emit_scatter   per partition: regenerate the pairs, rank them stably by digit in
 //                    LDS, write one contiguous run per digit
 #include "gs_device.h"
@@ -496,10 +497,34 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __rest
     if (s_hi[i]) atomicAdd(reinterpret_cast<unsigned long long*>(dc + i), (unsigned long long)s_hi[i]);
 }
 
-// One workgroup per digit: exclusive scan over chunks of the digit's chunk totals
-// (csum[c][d], in place) and the digit's total.  With digit_counts non-NULL, workgroup d
-// also sums the copies of the higher tile-digit counts [0][d] and [1][d] into it.
-__global__ __launch_bounds__(kBinBlock) void k_digit_scan(int64_t nchunks, uint64_t* __restrict__ csum,
+// The chunk totals' exclusive scan over chunks, per digit, in two levels so that every
+// read of csum is a whole row (all 256 digits of one chunk, contiguous):
+//   k_group_scan  per group of kScanGroup chunks: the scan inside the group (csum in place)
+//                 and the group's total per digit (gsum[g][d])
+//   k_digit_scan  per digit: exclusive scan of the group totals (gsum in place) and the
+//                 digit's total; with digit_counts non-NULL, workgroup d also sums the
+//                 copies of the higher tile-digit counts [0][d] and [1][d] into it
+// A chunk's count of digit d in all earlier chunks is then csum[c][d] + gsum[c / kScanGroup][d].
+constexpr int kScanGroup = 32;
+
+__global__ __launch_bounds__(kBinBlock) void k_group_scan(int64_t nchunks, uint64_t* __restrict__ csum,
+                                                          uint64_t* __restrict__ gsum) {
+  const int d = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * kScanGroup;
+  const int n = (int)min((int64_t)kScanGroup, nchunks - c0);
+  uint64_t x[kScanGroup];
+#pragma unroll
+  for (int i = 0; i < kScanGroup; ++i) x[i] = i < n ? csum[(c0 + i) * kDigits + d] : 0;  // all loads in flight
+  uint64_t run = 0;
+#pragma unroll
+  for (int i = 0; i < kScanGroup; ++i) {
+    if (i < n) csum[(c0 + i) * kDigits + d] = run;
+    run += x[i];
+  }
+  gsum[blockIdx.x * kDigits + d] = run;
+}
+
+__global__ __launch_bounds__(kBinBlock) void k_digit_scan(int64_t ngroups, uint64_t* __restrict__ gsum,
                                                           uint64_t* __restrict__ totals,
                                                           const uint64_t* __restrict__ dcopies,
                                                           uint64_t* __restrict__ digit_counts) {
@@ -516,28 +541,17 @@ __global__ __launch_bounds__(kBinBlock) void k_digit_scan(int64_t nchunks, uint6
   const int d = blockIdx.x;
   if (tid == 0) s_carry = 0;
   __syncthreads();
-  constexpr int kPer = 4;
-  for (int64_t off = 0; off < nchunks; off += kBinBlock * kPer) {
-    uint64_t x[kPer], sum = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int64_t c = off + (int64_t)tid * kPer + j;
-      x[j] = c < nchunks ? csum[c * kDigits + d] : 0;
-      sum += x[j];
-    }
-    const uint64_t inc = wave_inclusive_scan(sum);
+  for (int64_t off = 0; off < ngroups; off += kBinBlock) {
+    const int64_t g = off + tid;
+    const uint64_t x = g < ngroups ? gsum[g * kDigits + d] : 0;
+    const uint64_t inc = wave_inclusive_scan(x);
     if (lane == kWave - 1) s_w[wave] = inc;
     __syncthreads();
-    uint64_t pre = s_carry + inc - sum;
+    uint64_t pre = s_carry + inc - x;
     for (int w = 0; w < wave; ++w) pre += s_w[w];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int64_t c = off + (int64_t)tid * kPer + j;
-      if (c < nchunks) csum[c * kDigits + d] = pre;
-      pre += x[j];
-    }
+    if (g < ngroups) gsum[g * kDigits + d] = pre;
     __syncthreads();
-    if (tid == kBinBlock - 1) s_carry = pre;
+    if (tid == kBinBlock - 1) s_carry = pre + x;
     __syncthreads();
   }
   if (tid == 0) totals[d] = s_carry;
@@ -566,6 +580,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
                                                             const uint32_t* __restrict__ gstart, int tiles_x,
                                                             const uint32_t* __restrict__ cnt_pre,
                                                             const uint64_t* __restrict__ cpre,
+                                                            const uint64_t* __restrict__ gpre,
                                                             const uint64_t* __restrict__ totals,
                                                             uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
   constexpr int kPad = kEmitPart + kEmitPart / kEmitPer;  // one pad slot per lane run
@@ -584,7 +599,9 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
   // digit tid's total and its count in earlier partitions: loaded now, used once the pairs
   // are ranked (the global start of this partition's run of the digit)
   const uint64_t gtot = totals[tid];
-  const uint64_t gpart = cpre[(b / kCountParts) * kDigits + tid] + cnt_pre[b * kDigits + tid];
+  const int64_t chunk = b / kCountParts;
+  const uint64_t gpart = gpre[(chunk / kScanGroup) * kDigits + tid] + cpre[chunk * kDigits + tid] +
+                         cnt_pre[b * kDigits + tid];
   const EmitPart e = stage_partition(b, nparts, v, P, goff, gstart, s_rel);
   __syncthreads();
   // generate: lane-consecutive, one pad slot per lane so that a wavefront's 8-byte
@@ -679,8 +696,8 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
 // phase (which runs before P is known) and the emission phase agree on every offset.
 struct BinLayout {
   size_t pair_sums, vis_sums, sorted_sums, totals, dcopies, dk0, dv0, dk1, dv1, sort, goff, sruns, sn, dtotals, gstart, cnt_pre,
-      csum, total;
-  int64_t nb, nparts, nchunks;
+      csum, gsum, total;
+  int64_t nb, nparts, nchunks, ngroups;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -709,7 +726,9 @@ static BinLayout bin_layout(int64_t n, int64_t P) {
   l.gstart = l.dtotals + sizeof(uint64_t) * kDigits;
   l.cnt_pre = l.gstart + align256(sizeof(uint32_t) * (size_t)(l.nparts + 1));
   l.csum = l.cnt_pre + align256(sizeof(uint32_t) * kDigits * (size_t)l.nparts);
-  l.total = l.csum + sizeof(uint64_t) * kDigits * (size_t)l.nchunks;
+  l.ngroups = (l.nchunks + kScanGroup - 1) / kScanGroup;
+  l.gsum = l.csum + align256(sizeof(uint64_t) * kDigits * (size_t)l.nchunks);
+  l.total = l.gsum + sizeof(uint64_t) * kDigits * (size_t)(l.ngroups > 0 ? l.ngroups : 1);
   return l;
 }
 
@@ -786,15 +805,17 @@ hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int t
   uint32_t* sn = reinterpret_cast<uint32_t*>(w + l.sn);
   uint32_t* cnt_pre = reinterpret_cast<uint32_t*>(w + l.cnt_pre);
   uint64_t* csum = reinterpret_cast<uint64_t*>(w + l.csum);
+  uint64_t* gsum = reinterpret_cast<uint64_t*>(w + l.gsum);
   k_offsets<<<(unsigned)l.nb, kBinBlock, 0, s>>>(vcount, sn, ss, goff, gstart);
   // digit passes of the pair sort above the low byte (tile ids have at most 24 bits)
   const int hp = digit_counts ? (tile_bits > 8 ? (tile_bits - 1) / 8 : 0) : 0;
   uint64_t* dcopies = reinterpret_cast<uint64_t*>(w + l.dcopies);
   k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, goff, gstart, tiles_x, cnt_pre,
                                                          csum, hp, dcopies);
-  k_digit_scan<<<kDigits, kBinBlock, 0, s>>>(l.nchunks, csum, dtotals, dcopies, digit_counts);
+  k_group_scan<<<(unsigned)l.ngroups, kBinBlock, 0, s>>>(l.nchunks, csum, gsum);
+  k_digit_scan<<<kDigits, kBinBlock, 0, s>>>(l.ngroups, gsum, dtotals, dcopies, digit_counts);
   k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, goff, gstart, tiles_x, cnt_pre,
-                                                          csum, dtotals, keys, vals);
+                                                          csum, gsum, dtotals, keys, vals);
   return hipGetLastError();
 }
 
