@@ -88,7 +88,10 @@ __global__ __launch_bounds__(kBinBlock) void k_count_blocks(int64_t n, const uin
 }
 
 // Exclusive scan of nb block sums in place by one workgroup of NT threads; the total goes
-// to *total.
+// to *total.  Rounds of NT * kScanPer sums: thread t takes kScanPer consecutive ones (loads
+// all in flight), sums them, the workgroup scans the threads' sums, and each thread writes
+// its run's prefixes.
+constexpr int kScanPer = 8;
 template <int NT>
 __device__ __forceinline__ void scan_sums(int64_t nb, uint64_t* __restrict__ sums, uint64_t* __restrict__ total) {
   __shared__ uint64_t s_w[NT / kWave];
@@ -96,18 +99,26 @@ __device__ __forceinline__ void scan_sums(int64_t nb, uint64_t* __restrict__ sum
   if (threadIdx.x == 0) s_carry = 0;
   __syncthreads();
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
-  for (int64_t off = 0; off < nb; off += NT) {
-    const int64_t i = off + threadIdx.x;
-    const uint64_t x = i < nb ? sums[i] : 0;
-    const uint64_t inc = wave_inclusive_scan(x);
+  for (int64_t off = 0; off < nb; off += (int64_t)NT * kScanPer) {
+    const int64_t i0 = off + (int64_t)threadIdx.x * kScanPer;
+    uint64_t x[kScanPer], t = 0;
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      x[k] = i0 + k < nb ? sums[i0 + k] : 0;
+      t += x[k];
+    }
+    const uint64_t inc = wave_inclusive_scan(t);
     if (lane == kWave - 1) s_w[wave] = inc;
     __syncthreads();
-    uint64_t wpre = 0;
-    for (int w = 0; w < wave; ++w) wpre += s_w[w];
-    const uint64_t carry = s_carry;
-    if (i < nb) sums[i] = carry + wpre + inc - x;
+    uint64_t pre = s_carry + inc - t;
+    for (int w = 0; w < wave; ++w) pre += s_w[w];
+#pragma unroll
+    for (int k = 0; k < kScanPer; ++k) {
+      if (i0 + k < nb) sums[i0 + k] = pre;
+      pre += x[k];
+    }
     __syncthreads();
-    if (threadIdx.x == NT - 1) s_carry = carry + wpre + inc;
+    if (threadIdx.x == NT - 1) s_carry = pre;
     __syncthreads();
   }
   if (threadIdx.x == 0) *total = s_carry;
