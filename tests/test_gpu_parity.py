@@ -133,10 +133,16 @@ def test_large_image_two_tile_digit_passes():
     digit passes above the low byte and the binning counts both digits.  Large footprints
     (many Gaussians span more than 8 tile rows) take the whole-rectangle path."""
     sc, _ = scenes.tiny_scene(11, 2000)
+    # three Gaussians wider than the image: tile rows of 263 tiles, more than a turn of the
+    # low byte's 256 values in one row
+    sc.means[:3] = np.array([[0.0, 0.0, 3.0], [0.3, -0.2, 3.5], [-0.4, 0.1, 2.5]], np.float32)
+    sc.scales[:3] = 1.5
+    sc.opacities[:3] = 0.9
     cam = scenes.Camera(np.eye(3, dtype=np.float32), np.zeros(3, np.float32), 4400.0, 4400.0, 2100.0, 2075.0,
                         4200, 4150, 0.2)
     assert cam.num_tiles > 65536
     g = gpu_stages(sc, cam)
+    assert np.all(g["n_tiles"][:3] == cam.num_tiles)  # every tile of the image
     say(f"large image: P={g['P']}, pass-1 digits {int((g['digit_counts'][1] > 0).sum())}")
     assert g["digit_counts"][1][1] > 0  # pairs with tile ids >= 65536 exist
     check_projection(sc, cam, g, "large image")
