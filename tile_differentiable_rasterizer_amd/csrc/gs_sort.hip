@@ -22,11 +22,15 @@
 //                 publishes per-digit counts and resolves its global offsets by looking
 //                 back over earlier partitions' published counts (several earlier
 //                 partitions per round trip), reorders the partition in LDS by digit and
-//                 writes each digit's run contiguously
+//                 writes each digit's run contiguously; the last pass of a pair sort also
+//                 records each tile's first and last positions (atomic maxima at the two
+//                 ends of each run of equal tiles in the partition)
 //   k_sort_copy   moves the result back to keys/vals after an odd number of passes, for
 //                 callers that need it there
-//   k_ranges      [first, last + 1) of every tile from the sorted keys; for a pair sort
-//                 whose caller wants the result in keys/vals it also moves it there
+//   k_ranges      [first, last + 1) of every tile from the sorted keys, where no pass ran
+//                 or where a pair sort's result is moved back to keys/vals on the way
+//   k_tile_order  decodes the recorded starts, and orders the tiles by decreasing list
+//                 length
 #include "gs_device.h"
 
 namespace gs {
@@ -174,7 +178,8 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
     int64_t Pmax, const uint64_t* __restrict__ dcount, int pass, int shift, int bits,
     const int32_t* __restrict__ plan, int mode_arg, const uint64_t* __restrict__ dbase,
     const uint64_t* __restrict__ counts, int copies, int32_t* __restrict__ result_word,
-    uint64_t* __restrict__ status, uint32_t* __restrict__ tickets) {
+    uint64_t* __restrict__ status, uint32_t* __restrict__ tickets, int64_t* __restrict__ tile_ranges,
+    int64_t num_tiles) {
   // the buffers this pass reads and writes: given by the host when it knows them (no pass
   // skipped), else from the plan, which also marks passes to skip
   const int mode = mode_arg >= 0 ? mode_arg : plan[pass];
@@ -321,6 +326,22 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
     if (g < (uint64_t)P) {  // always, given exact digit counts; caller-supplied ones are not trusted
       kout[g] = k;
       vout[g] = s_vals[i];
+      if constexpr (sizeof(K) == 8) {
+        // the last pass of a pair sort: the partition is in final order here, so a tile's
+        // first and last pairs anywhere in the output start and end runs of its tile in
+        // some partition.  The largest run end is the tile's end; the smallest run start
+        // is recorded as the largest complement, so that cleared words (0) stay below
+        // every position and an empty tile keeps 0.
+        if (tile_ranges) {
+          const uint64_t t = (uint64_t)k >> 32;
+          if (t < (uint64_t)num_tiles) {
+            if (i == 0 || ((uint64_t)s_keys[i - 1] >> 32) != t)
+              atomicMax(reinterpret_cast<unsigned long long*>(tile_ranges + 2 * t), ~(unsigned long long)g);
+            if (i + 1 == nvalid || ((uint64_t)s_keys[i + 1] >> 32) != t)
+              atomicMax(reinterpret_cast<unsigned long long*>(tile_ranges + 2 * t + 1), (unsigned long long)(g + 1));
+          }
+        }
+      }
     }
   }
 }
@@ -393,8 +414,11 @@ __device__ __forceinline__ int length_bucket(int64_t len) {
   return min(127, 4 * lg + (int)((len >> (lg - 2)) & 3));
 }
 
-__global__ __launch_bounds__(1024) void k_tile_order(const int64_t* __restrict__ ranges, int64_t num_tiles,
-                                                    int32_t* __restrict__ order) {
+// With decode_starts the starts hold the bitwise complement of each tile's first position
+// (0 for an empty tile), as the last sort pass wrote them: they are decoded in place.  With
+// order NULL only that is done.
+__global__ __launch_bounds__(1024) void k_tile_order(int64_t* __restrict__ ranges, int64_t num_tiles,
+                                                    int decode_starts, int32_t* __restrict__ order) {
   constexpr int kPer = 8;  // tiles per thread per round, their loads all in flight together
   __shared__ uint32_t s_cnt[128];
   __shared__ uint32_t s_cur[128];
@@ -412,12 +436,22 @@ __global__ __launch_bounds__(1024) void k_tile_order(const int64_t* __restrict__
       a[j] = t < num_tiles ? ranges[2 * t] : 0;
       b[j] = t < num_tiles ? ranges[2 * t + 1] : 0;
     }
+    if (decode_starts) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int64_t t = t0 + j * 1024 + tid;
+        a[j] = a[j] ? ~a[j] : 0;
+        if (t < num_tiles) ranges[2 * t] = a[j];
+      }
+    }
+    if (!order) continue;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       bk[j] = length_bucket(b[j] - a[j]);
       if (t0 + j * 1024 + tid < num_tiles) atomicAdd(&s_cnt[bk[j]], 1u);
     }
   }
+  if (!order) return;
   __syncthreads();
   // exclusive scan in decreasing bucket order: lane j of the first two wavefronts takes
   // bucket 127 - j
@@ -456,12 +490,14 @@ size_t radix_workspace_bytes(int64_t P, int lo, int hi) { return sort_layout(P, 
 // with copy_back = false in the buffer that plan[kMaxPasses] names (0 keys, 1 tmp).  With
 // dcount non-NULL the key count is read on the device from *dcount, and P (which sizes
 // the grids and the workspace) only bounds it, so the sort can be queued before the host
-// knows the count.
+// knows the count.  With tile_ranges non-NULL (64-bit keys with the tile in the high word,
+// and keep_all, so that the last pass runs) the last pass also writes into cleared ranges
+// each tile's end and the complement of its start.
 template <typename K>
 static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_t* vals, K* keys_tmp,
                              uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back = true,
                              bool keep_all = false, const uint64_t* digit_counts = nullptr,
-                             bool ws_zeroed = false) {
+                             bool ws_zeroed = false, int64_t* tile_ranges = nullptr, int64_t num_tiles = 0) {
   const int passes = radix_passes(lo, hi);
   char* w = static_cast<char*>(ws);
   if (P <= 1 || passes == 0)  // nothing moves: the result is in keys/vals, as the word says
@@ -508,7 +544,8 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
     k_onesweep<K><<<(unsigned)((P + Onesweep<K>::part - 1) / Onesweep<K>::part), Onesweep<K>::threads, 0, s>>>(
         keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p, pbits[p], plan, planless ? p % 2 : -1,
         dbase + p * kRadix, planless ? digit_counts + p * kRadix : nullptr, 1,
-        planless && p == passes - 1 ? plan + kMaxPasses : nullptr, status + poff[p], tickets);
+        planless && p == passes - 1 ? plan + kMaxPasses : nullptr, status + poff[p], tickets,
+        p == passes - 1 ? tile_ranges : nullptr, num_tiles);
   }
   if (copy_back) {
     const int64_t want = (P + 255) / 256;
@@ -579,16 +616,19 @@ hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* v
     k_zero2<<<blocks, 256, 0, s>>>(reinterpret_cast<uint32_t*>(ranges), 4 * num_tiles,
                                    reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + off), (int64_t)(len / 4));
     e = radix_sort<uint64_t>(P, nullptr, keys, vals, keys_tmp, vals_tmp, sorted_low_bits, hi, ws, s, false, true,
-                             digit_counts, true);
+                             digit_counts, true, ranges, num_tiles);
   } else {
     e = launch_fill_u32(ranges, 4 * num_tiles, 0u, s);
   }
   if (e != hipSuccess) return e;
+  // the last pass wrote every tile's first and last positions; k_ranges finds them from
+  // the sorted keys where nothing was sorted, or where it also moves the result back
   const bool move = in_tmp && !result_in_tmp;
-  if (P > 0)
+  const bool recorded = passes > 0 && !move;
+  if (P > 0 && !recorded)
     k_ranges<<<(unsigned)((P + 1023) / 1024), 256, 0, s>>>(in_tmp ? keys_tmp : keys, vals_tmp, move ? keys : nullptr,
                                                            move ? vals : nullptr, P, num_tiles, ranges);
-  if (order) k_tile_order<<<1, 1024, 0, s>>>(ranges, num_tiles, order);
+  if (order || recorded) k_tile_order<<<1, 1024, 0, s>>>(ranges, num_tiles, recorded ? 1 : 0, order);
   if (result_in_tmp) *result_in_tmp = in_tmp ? 1 : 0;
   return hipGetLastError();
 }
