@@ -87,54 +87,67 @@ __global__ __launch_bounds__(kBinBlock) void k_count_blocks(int64_t n, const uin
   }
 }
 
-// Exclusive scan of nb block sums in place by one workgroup of NT threads; the total goes
-// to *total.  Rounds of NT * kScanPer sums: thread t takes kScanPer consecutive ones (loads
-// all in flight), sums them, the workgroup scans the threads' sums, and each thread writes
-// its run's prefixes.
+// Exclusive scans of nb block sums in place, of NA arrays side by side, by one workgroup of
+// NT threads; array a's total goes to total[a].  Rounds of NT * kScanPer sums: thread t
+// takes kScanPer consecutive ones of every array (loads all in flight), sums them, the
+// workgroup scans the threads' sums, and each thread writes its run's prefixes.
 constexpr int kScanPer = 8;
-template <int NT>
-__device__ __forceinline__ void scan_sums(int64_t nb, uint64_t* __restrict__ sums, uint64_t* __restrict__ total) {
-  __shared__ uint64_t s_w[NT / kWave];
-  __shared__ uint64_t s_carry;
-  if (threadIdx.x == 0) s_carry = 0;
+template <int NT, int NA>
+__device__ __forceinline__ void scan_sums(int64_t nb, uint64_t* const (&sums)[NA], uint64_t* __restrict__ total) {
+  __shared__ uint64_t s_w[NA][NT / kWave];
+  __shared__ uint64_t s_carry[NA];
+  if (threadIdx.x < NA) s_carry[threadIdx.x] = 0;
   __syncthreads();
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
   for (int64_t off = 0; off < nb; off += (int64_t)NT * kScanPer) {
     const int64_t i0 = off + (int64_t)threadIdx.x * kScanPer;
-    uint64_t x[kScanPer], t = 0;
+    uint64_t x[NA][kScanPer], t[NA], inc[NA];
 #pragma unroll
-    for (int k = 0; k < kScanPer; ++k) {
-      x[k] = i0 + k < nb ? sums[i0 + k] : 0;
-      t += x[k];
-    }
-    const uint64_t inc = wave_inclusive_scan(t);
-    if (lane == kWave - 1) s_w[wave] = inc;
-    __syncthreads();
-    uint64_t pre = s_carry + inc - t;
-    for (int w = 0; w < wave; ++w) pre += s_w[w];
+    for (int a = 0; a < NA; ++a) {
+      t[a] = 0;
 #pragma unroll
-    for (int k = 0; k < kScanPer; ++k) {
-      if (i0 + k < nb) sums[i0 + k] = pre;
-      pre += x[k];
+      for (int k = 0; k < kScanPer; ++k) {
+        x[a][k] = i0 + k < nb ? sums[a][i0 + k] : 0;
+        t[a] += x[a][k];
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      inc[a] = wave_inclusive_scan(t[a]);
+      if (lane == kWave - 1) s_w[a][wave] = inc[a];
     }
     __syncthreads();
-    if (threadIdx.x == NT - 1) s_carry = pre;
+    uint64_t pre[NA];
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      pre[a] = s_carry[a] + inc[a] - t[a];
+      for (int w = 0; w < wave; ++w) pre[a] += s_w[a][w];
+#pragma unroll
+      for (int k = 0; k < kScanPer; ++k) {
+        if (i0 + k < nb) sums[a][i0 + k] = pre[a];
+        pre[a] += x[a][k];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == NT - 1)
+#pragma unroll
+      for (int a = 0; a < NA; ++a) s_carry[a] = pre[a];
     __syncthreads();
   }
-  if (threadIdx.x == 0) *total = s_carry;
+  if (threadIdx.x < NA) total[threadIdx.x] = s_carry[threadIdx.x];
 }
 
 __global__ __launch_bounds__(1024) void k_scan_blocks(int64_t nb, uint64_t* __restrict__ sums,
                                                       uint64_t* __restrict__ total) {
-  scan_sums<1024>(nb, sums, total);
+  uint64_t* const arrays[1] = {sums};
+  scan_sums<1024, 1>(nb, arrays, total);
 }
 
-// The count phase's two scans (pair sums, visible sums) in one launch.
+// The count phase's two scans (pair sums, visible sums) side by side in one launch.
 __global__ __launch_bounds__(1024) void k_scan_blocks2(int64_t nb, uint64_t* __restrict__ a,
                                                        uint64_t* __restrict__ b, uint64_t* __restrict__ totals) {
-  scan_sums<1024>(nb, a, totals);
-  __syncthreads();
-  scan_sums<1024>(nb, b, totals + 1);
+  uint64_t* const arrays[2] = {a, b};
+  scan_sums<1024, 2>(nb, arrays, totals);
 }
 
 // Visible Gaussians' (depth bits, id) in id order.  Round r of a workgroup covers ids
