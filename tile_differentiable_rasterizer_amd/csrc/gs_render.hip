@@ -120,9 +120,11 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
   // ids run one chunk ahead of the records, so a chunk's record gathers wait on one
   // memory round trip instead of two
   uint32_t nid = start + kWave + lane < end ? vals[start + kWave + lane] : 0u;  // clamped where used
-  float livef = inside ? 1.0f : 0.0f;
+  // the alpha a record must reach to be taken: 1/255 while the pixel is live, +inf once it
+  // is done (outside the image, or T < 1e-4), so that a done pixel takes nothing
+  float thr = inside ? kAlphaMin : INFINITY;
   for (int64_t b = start; b < end; b += kWave) {
-    if (!__ballot(livef != 0.0f)) break;  // this wavefront's pixels are all done
+    if (!__ballot(thr != INFINITY)) break;  // this wavefront's pixels are all done
     float4 s0, s1;
     stage_transform(p0, p1, s0, s1);
     const bool reach =
@@ -143,19 +145,19 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
     if (!m) continue;
     const uint32_t kb = (uint32_t)(b - start) + 1u;  // list position + 1 of staged record 0
     // one record's contribution; a record this lane does not take gets alpha 0, which
-    // leaves T, the colour and nc exactly as they were (livef is exactly 1 or 0, so the
-    // take decision stays in vector registers)
+    // leaves T and the colour exactly as they were; one compare decides the take and nc
     auto blend = [&](const float4 a, const float4 e1, float bb, uint32_t pos) {
       const float dx = fx - a.x, dy = fy - a.y;
       const float alpha = fminf(kAlphaMax, e1.y * gauss_factor(gauss_exponent(a.z, a.w, e1.x, dx, dy)));
-      const float at = alpha >= kAlphaMin ? alpha * livef : 0.0f;
+      const bool take = alpha >= thr;
+      const float at = take ? alpha : 0.0f;
       const float w = at * T;
       cr = fmaf(e1.z, w, cr);
       cg = fmaf(e1.w, w, cg);
       cb = fmaf(bb, w, cb);
       T = T * (1.0f - at);
-      nc = at > 0.0f ? pos : nc;
-      livef = T < kTMin ? 0.0f : livef;
+      nc = take ? pos : nc;
+      thr = T < kTMin ? INFINITY : thr;
     };
     // two records per iteration in alternating registers: each one's LDS reads are
     // issued while the previous one is evaluated
