@@ -292,8 +292,9 @@ def stage_work(N, K, P, tiles, evals, walk, pixels, with_bwd):
         # 16 B per visible + 4 B histogram), the depth-ordered gather (20 B per visible),
         # pairs written (12 B each)
         "bin": (4 * N + 16 * V + (4 * 16 + 4) * V + 20 * V + 12 * P, 0.0),
-        # 24 B/pair per pass, ranges (8 B/pair) + 16 B/tile (the digit counts come from the
-        # binning, so there is no counting read)
+        # 24 B/pair per pass, ranges (8 B/pair: the step's read of the sorted keys, counted as
+        # the step's work although the last pass records the ranges without it) + 16 B/tile
+        # (the digit counts come from the binning, so there is no counting read)
         "sort": ((24 * passes + 8) * P + 16 * tiles, 0.0),
         # list entries read once per tile; colour, transmittance and count written per pixel
         "render_fwd": (4 * P + 20 * pixels, OPS_PER_EVAL_FWD * evals),
