@@ -369,10 +369,19 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
   };
   start(e.g0 + (uint32_t)lo);
   int local = p0 - s_rel[lo];  // pairs of this Gaussian before the lane's first
-  while (local > c1 - c0 && ty < (int)r.w) {
-    local -= c1 >= c0 ? c1 - c0 + 1 : 0;
-    ++ty;
-    row();
+  if (!spans_packed(sp)) {
+    // every row of the rectangle is whole: the lane's row follows by one division instead
+    // of a walk over the rows before it (the long walks are in these large rectangles)
+    const int wdt = c1 - c0 + 1;
+    const int dr = min(local / wdt, (int)r.w - ty);
+    ty += dr;
+    local -= dr * wdt;
+  } else {
+    while (local > c1 - c0 && ty < (int)r.w) {
+      local -= c1 >= c0 ? c1 - c0 + 1 : 0;
+      ++ty;
+      row();
+    }
   }
   int col = min(c0 + local, c1);
   int next = s_rel[lo + 1];
