@@ -156,17 +156,8 @@ def tile_keeps(ell, pxrect, tx: int, ty: int):
     return keep.astype(bool), near.astype(bool)
 
 
-def rect_tested(trect) -> np.ndarray:
-    """Whether the ellipse test applies to each tile rectangle (larger ones keep every tile)."""
-    lib = _load()
-    trect = np.ascontiguousarray(np.asarray(trect).reshape(-1, 4), dtype=np.int32)
-    out = np.zeros(trect.shape[0], np.int32)
-    lib.orc_rect_tested_batch(C.c_int64(trect.shape[0]), _p(trect), _p(out))
-    return out.astype(bool)
-
-
 def count_kept(trect, pxrect, ell):
-    """Tiles of each rectangle kept (by the ellipse test where it applies)."""
+    """Tiles of each rectangle kept by the ellipse test."""
     lib = _load()
     trect = np.ascontiguousarray(trect, dtype=np.int32)
     pxrect = np.ascontiguousarray(pxrect, dtype=np.int32)

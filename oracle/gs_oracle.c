@@ -56,8 +56,6 @@ void orc_set_threads(int n) {
 #define ORC_AMIN ((double)(float)(1.0 / 255.0)) /* skip contributions below this alpha */
 #define ORC_TMIN ((double)1e-4f)              /* stop a pixel below this transmittance */
 #define ORC_TILE 16                          /* 16x16 tiles, [JULIA-1] s4.3           */
-#define ORC_TEST_MAX_ROWS 8                  /* the ellipse test applies to rectangles  */
-#define ORC_TEST_MAX_COLS 255                /* of at most this many tile rows/columns  */
 #define ORC_EPS32 (1.0 / 16777216.0)          /* 2^-24: unit roundoff of float32        */
 
 typedef struct {
@@ -266,17 +264,6 @@ int orc_tile_keeps(double u, double v, double A, double B, double C, double tau,
   return qmin <= tau;
 }
 
-/* Does the ellipse test apply to this tile rectangle?  Larger rectangles keep every tile:
- * conservative, and rare (a Gaussian more than 8 tiles tall on screen). */
-int orc_rect_tested(int64_t tx0, int64_t tx1, int64_t ty0, int64_t ty1) {
-  return ty1 - ty0 + 1 <= ORC_TEST_MAX_ROWS && tx1 - tx0 + 1 <= ORC_TEST_MAX_COLS;
-}
-
-void orc_rect_tested_batch(int64_t n, const int32_t* trect, int32_t* out) {
-  for (int64_t i = 0; i < n; ++i)
-    out[i] = orc_rect_tested(trect[4 * i], trect[4 * i + 1], trect[4 * i + 2], trect[4 * i + 3]);
-}
-
 /*
  * The forward projection of one Gaussian ([JULIA-1] s3.1-3.2; [JULIA-2] s3.1-3.2).
  * Culled Gaussians get visible = 0 and n_tiles = 0.
@@ -387,14 +374,14 @@ static void project_one(const orc_camera* cam, const double mu[3], const double 
   g->py0 = (int64_t)ly; g->py1 = (int64_t)hy;
   g->tx0 = g->px0 / ORC_TILE; g->tx1 = g->px1 / ORC_TILE;
   g->ty0 = g->py0 / ORC_TILE; g->ty1 = g->py1 / ORC_TILE;
-  /* the tiles of the rectangle that pass the ellipse test ([SPIRULA], 16-bit AABB section) */
+  /* the tiles of the rectangle that pass the ellipse test ([SPIRULA], 16-bit AABB section),
+     applied to every rectangle whatever its size: the page sets no limit */
   const int64_t px[4] = {g->px0, g->px1, g->py0, g->py1};
   int near = 0;
   g->n_tiles = 0;
-  const int tested = orc_rect_tested(g->tx0, g->tx1, g->ty0, g->ty1);
   for (int64_t ty = g->ty0; ty <= g->ty1; ++ty)
     for (int64_t tx = g->tx0; tx <= g->tx1; ++tx)
-      g->n_tiles += tested ? orc_tile_keeps(g->u, g->v, g->A, g->B, g->C, g->tau, px, tx, ty, &near) : 1;
+      g->n_tiles += orc_tile_keeps(g->u, g->v, g->A, g->B, g->C, g->tau, px, tx, ty, &near);
   if (near) g->flags |= 8;
   g->visible = g->n_tiles > 0;
 }
@@ -450,8 +437,8 @@ int64_t orc_count_pairs(int64_t n, const int64_t* n_tiles) {
  * Emit one (key, id) pair per kept tile, Gaussians in id order, rows (ty) outer and
  * columns (tx) inner.  key = tile_id * 2^32 + float32 depth bits, tile_id = ty*tiles_x+tx.
  * A tile of the rectangle is kept when it passes the ellipse test for the Gaussian's
- * ell[i] = (u, v, A, B, C, tau) and pixel box pxrect[i] (every tile of a rectangle the test
- * does not apply to, and every tile when ell is NULL, for hand-built lists); Gaussians with
+ * ell[i] = (u, v, A, B, C, tau) and pixel box pxrect[i] (every tile when ell is NULL, for
+ * hand-built lists); Gaussians with
  * n_tiles = 0 are skipped.  Writes at most capacity pairs; returns the number of kept tiles.
  */
 int64_t orc_emit_pairs(int64_t n, const int32_t* trect, const int32_t* pxrect, const double* ell,
@@ -460,8 +447,7 @@ int64_t orc_emit_pairs(int64_t n, const int32_t* trect, const int32_t* pxrect, c
   int64_t p = 0;
   for (int64_t i = 0; i < n; ++i) {
     if (n_tiles[i] <= 0) continue;
-    const int tested = orc_rect_tested(trect[4 * i], trect[4 * i + 1], trect[4 * i + 2], trect[4 * i + 3]);
-    const double* e = ell && tested ? ell + 6 * i : NULL;
+    const double* e = ell ? ell + 6 * i : NULL;
     const int64_t px[4] = {pxrect ? pxrect[4 * i] : 0, pxrect ? pxrect[4 * i + 1] : 0,
                            pxrect ? pxrect[4 * i + 2] : 0, pxrect ? pxrect[4 * i + 3] : 0};
     for (int64_t ty = trect[4 * i + 2]; ty <= trect[4 * i + 3]; ++ty)
@@ -506,11 +492,10 @@ void orc_count_kept(int64_t n, const int32_t* trect, const int32_t* pxrect, cons
   for (int64_t i = 0; i < n; ++i) {
     const double* e = ell + 6 * i;
     const int64_t px[4] = {pxrect[4 * i], pxrect[4 * i + 1], pxrect[4 * i + 2], pxrect[4 * i + 3]};
-    const int tested = orc_rect_tested(trect[4 * i], trect[4 * i + 1], trect[4 * i + 2], trect[4 * i + 3]);
     int64_t c = 0;
     for (int64_t ty = trect[4 * i + 2]; ty <= trect[4 * i + 3]; ++ty)
       for (int64_t tx = trect[4 * i]; tx <= trect[4 * i + 1]; ++tx)
-        c += tested ? orc_tile_keeps(e[0], e[1], e[2], e[3], e[4], e[5], px, tx, ty, NULL) : 1;
+        c += orc_tile_keeps(e[0], e[1], e[2], e[3], e[4], e[5], px, tx, ty, NULL);
     out[i] = c;
   }
 }

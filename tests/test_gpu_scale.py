@@ -66,7 +66,6 @@ def test_aniso_10m_1080p_forward(big):
         cover = (rv[:, 0] <= tx) & (rv[:, 1] >= tx) & (rv[:, 2] <= ty) & (rv[:, 3] >= ty)
         ids = vis[cover]
         keep, _ = oracle.tile_keeps(ell[ids], pxr[ids], tx, ty)
-        keep |= ~oracle.rect_tested(rect[ids])  # larger rectangles keep every tile
         ids, dsel = ids[keep], dv[cover][keep]
         want = ids[np.lexsort((ids, dsel))]
         got = vals[rg[t, 0]:rg[t, 1]]

@@ -120,25 +120,40 @@ def test_thin_diagonal_ellipse_keeps_the_tiles_its_axis_crosses(orc):
     assert (1, 6) not in kept and (6, 1) not in kept
 
 
-def test_rectangles_taller_than_eight_tile_rows_keep_every_tile(orc):
-    """The ellipse test applies to rectangles of at most 8 tile rows and 255 columns; a
-    larger one keeps every tile (conservative).  A thin ellipse tilted across 10 tile rows
-    keeps its whole rectangle; the same ellipse scaled to fit 6 rows is culled."""
-    for half_len, tested in ((75.0, False), (45.0, True)):
-        u = v = 96.0
-        t = math.pi / 3
-        R = np.array([[math.cos(t), -math.sin(t)], [math.sin(t), math.cos(t)]])
-        Cov = R @ np.diag([(half_len / 3) ** 2, (0.6 / 3) ** 2]) @ R.T
-        M = np.linalg.inv(Cov)
-        ell = np.array([[u, v, M[0, 0], M[0, 1], M[1, 1], 9.0]])
-        ex, ey = math.sqrt(9.0 * Cov[0, 0]), math.sqrt(9.0 * Cov[1, 1])
-        px = np.array([[math.ceil(u - ex - 0.5), math.floor(u + ex - 0.5), math.ceil(v - ey - 0.5),
-                        math.floor(v + ey - 0.5)]], np.int32)
-        tr = (px // 16).astype(np.int32)
-        area = int((tr[0, 1] - tr[0, 0] + 1) * (tr[0, 3] - tr[0, 2] + 1))
-        assert orc.rect_tested(tr)[0] == tested
-        kept = int(orc.count_kept(tr, px, ell)[0])
-        if tested:
-            assert kept < area
-        else:
-            assert tr[0, 3] - tr[0, 2] + 1 > 8 and kept == area
+def _brute_tiles(ell, px):
+    """Tiles holding a pixel centre with q <= tau (brute force over the pixel box)."""
+    u, v, A, B, C, tau = ell
+    xs, ys = np.meshgrid(np.arange(px[0], px[1] + 1) + 0.5, np.arange(px[2], px[3] + 1) + 0.5)
+    inside = _q(A, B, C, xs - u, ys - v) <= tau
+    return set(zip((ys[inside] // 16).astype(int).tolist(), (xs[inside] // 16).astype(int).tolist()))
+
+
+@pytest.mark.parametrize("half_len,angle,center", [(75.0, math.pi / 3, 96.0), (300.0, 0.4, 400.0),
+                                                    (2600.0, 0.02, 2400.0)])
+def test_ellipse_test_applies_to_rectangles_of_any_size(orc, half_len, angle, center):
+    """The page sets no size limit on the ellipse test: a thin tilted ellipse whose rectangle
+    spans 10 to 40 tile rows, or more than 255 tile columns, keeps only the tiles near its
+    axis.  Every tile holding a supporting pixel centre is kept (brute force); every kept tile
+    is within one tile of the axis's path, and the count is well below the rectangle's area."""
+    u = v = center
+    R = np.array([[math.cos(angle), -math.sin(angle)], [math.sin(angle), math.cos(angle)]])
+    Cov = R @ np.diag([(half_len / 3) ** 2, (0.6 / 3) ** 2]) @ R.T
+    M = np.linalg.inv(Cov)
+    ell = np.array([u, v, M[0, 0], M[0, 1], M[1, 1], 9.0])
+    ex, ey = math.sqrt(9.0 * Cov[0, 0]), math.sqrt(9.0 * Cov[1, 1])
+    px = np.array([max(0, math.ceil(u - ex - 0.5)), math.floor(u + ex - 0.5), max(0, math.ceil(v - ey - 0.5)),
+                   math.floor(v + ey - 0.5)], np.int32)
+    tr = (px // 16).astype(np.int32)
+    rows, cols = int(tr[3] - tr[2] + 1), int(tr[1] - tr[0] + 1)
+    assert rows > 8 or cols > 255
+    kept = {(ty, tx) for ty in range(tr[2], tr[3] + 1) for tx in range(tr[0], tr[1] + 1)
+            if orc.tile_keeps(ell, px, tx, ty)[0][0]}
+    assert _brute_tiles(ell, px) <= kept
+    assert int(orc.count_kept(tr[None], px[None], ell[None])[0]) == len(kept)
+    # the axis through (u, v) along (cos, sin): a kept tile's centre lies within a tile
+    # diagonal plus the ellipse's half-width of it
+    d = np.array([math.cos(angle), math.sin(angle)])
+    for ty, tx in kept:
+        cx, cy = 16 * tx + 8.0 - u, 16 * ty + 8.0 - v
+        assert abs(-d[1] * cx + d[0] * cy) <= 8 * math.sqrt(2) + 1.0
+    assert len(kept) < rows * cols // 2
