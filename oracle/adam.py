@@ -7,15 +7,16 @@ transposed (unit-major) layout, with one (min, max) bounds pair per 256 units; g
 float32.  The update itself is Adam (Kingma and Ba): m = b1 m + (1 - b1) g,
 v = b2 v + (1 - b2) g^2, theta -= lr * (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps).
 
-Readings (the page leaves the code format and the precision open):
+Readings (the page leaves the code format and the precision open); every formula is the
+defining one, written as it reads, in float64:
   * a unit is one float32 parameter; word[u] = m code | v code << 16;
   * bounds[b] = (m_lo, m_hi, v_lo, v_hi), float32, for units [256 b, 256 b + 256);
-  * decode: x = lo + code * ((hi - lo) * (1 / 65535)), in float64;
-  * the update runs in float64, with the bias corrections applied as the reciprocals
-    1 / (1 - b^t) (b^t from the host's pow); the new parameter is rounded once to float32;
+  * decode: x = lo + code (hi - lo) / 65535;
+  * update: m = b1 m + (1 - b1) g, v = b2 v + (1 - b2) g^2, m_hat = m / (1 - b1^t),
+    v_hat = v / (1 - b2^t), theta = theta - lr m_hat / (sqrt(v_hat) + eps); the new
+    parameter is rounded once to float32;
   * encode: the block's new bounds are the float32 roundings of its min and max; code =
-    rint((x - lo) * (65535 / (hi - lo))) clamped to [0, 65535] (0 when hi == lo).
-  Scaling by reciprocals computed once keeps the device pass to one division per unit.
+    rint((x - lo) / (hi - lo) * 65535) clamped to [0, 65535] (0 when hi == lo).
 """
 from __future__ import annotations
 
@@ -25,14 +26,13 @@ import numpy as np
 
 BLOCK = 256
 QMAX = 65535.0
-INV_QMAX = 1.0 / QMAX
 
 
 def decode(codes, lo, hi):
     """Codes (per unit) with the bounds of their block (per unit) -> float64 values."""
     lo = np.asarray(lo, np.float64)
     hi = np.asarray(hi, np.float64)
-    return lo + np.asarray(codes, np.float64) * ((hi - lo) * INV_QMAX)
+    return lo + np.asarray(codes, np.float64) * (hi - lo) / QMAX
 
 
 def encode_blocks(x):
@@ -51,14 +51,16 @@ def encode_blocks(x):
         if h == l:
             c = np.zeros(seg.shape[0])
         else:
-            c = np.rint((seg - l) * (QMAX / (h - l)))
+            c = np.rint((seg - l) / (h - l) * QMAX)
         codes[b * BLOCK:(b + 1) * BLOCK] = np.clip(c, 0.0, QMAX).astype(np.uint16)
     return codes, lo, hi
 
 
-def adam_q16(params, grads, state, bounds, *, lr: float, beta1: float, beta2: float, eps: float, step: int):
+def adam_q16(params, grads, state, bounds, *, lr: float, beta1: float, beta2: float, eps: float, step: int,
+             full: bool = False):
     """One Adam step.  params float32 [U], grads float32 [U], state uint32 [U], bounds float32
-    [nb][4].  Returns (params, state, bounds) after the step (new arrays)."""
+    [nb][4].  Returns (params, state, bounds) after the step (new arrays); with ``full`` also a
+    dict of the float64 moments m, v and the update of each parameter (for tolerances)."""
     p = np.asarray(params, np.float32)
     g = np.asarray(grads, np.float32).astype(np.float64)
     w = np.asarray(state, np.uint32)
@@ -70,12 +72,14 @@ def adam_q16(params, grads, state, bounds, *, lr: float, beta1: float, beta2: fl
     b1, b2 = np.float64(np.float32(beta1)), np.float64(np.float32(beta2))
     m = b1 * m + (1.0 - b1) * g
     v = b2 * v + (1.0 - b2) * (g * g)
-    ib1 = 1.0 / (1.0 - math.pow(float(b1), step))
-    ib2 = 1.0 / (1.0 - math.pow(float(b2), step))
-    upd = np.float64(np.float32(lr)) * (m * ib1) / (np.sqrt(v * ib2) + np.float64(np.float32(eps)))
+    m_hat = m / (1.0 - math.pow(float(b1), step))
+    v_hat = v / (1.0 - math.pow(float(b2), step))
+    upd = np.float64(np.float32(lr)) * m_hat / (np.sqrt(v_hat) + np.float64(np.float32(eps)))
     new_p = (p.astype(np.float64) - upd).astype(np.float32)
     mc, mlo, mhi = encode_blocks(m)
     vc, vlo, vhi = encode_blocks(v)
     new_w = mc.astype(np.uint32) | (vc.astype(np.uint32) << np.uint32(16))
     new_b = np.stack([mlo, mhi, vlo, vhi], axis=1).astype(np.float32)
+    if full:
+        return new_p, new_w, new_b, dict(m=m, v=v, update=upd)
     return new_p, new_w, new_b
