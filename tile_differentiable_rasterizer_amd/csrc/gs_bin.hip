@@ -323,13 +323,13 @@ __device__ __forceinline__ EmitPart stage_partition(int64_t b, int64_t nparts, i
 // Generates this lane's pairs; emit(k, tile, id, dbits) receives the pair's slot in the
 // lane's run (0 .. kEmitPer - 1), its tile, its Gaussian's id and the bit pattern of that
 // Gaussian's depth.  sruns holds the depth-sorted Gaussians' tile records (words 6 and 7:
-// id and depth bits).  A Gaussian's pairs are the tiles its
-// ellipse test keeps (every tile of a rectangle the test does not apply to), rows outer and
-// columns inner, read from the runs the projection stored.  Every loop stays inside the
-// rectangle.
-template <bool kPayload, typename F>
+// id and depth bits).  A Gaussian's pairs are the tiles its ellipse test keeps, rows outer
+// and columns inner: read from the runs the projection stored, or, for a rectangle too
+// large for the record, computed row by row from its render record (rec, by id).  Every
+// loop stays inside the rectangle.
+template <typename F>
 __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_rel, const uint4* __restrict__ sruns,
-                                           int tiles_x, F&& emit) {
+                                           const float4* __restrict__ rec, int tiles_x, F&& emit) {
   const int p0 = (int)threadIdx.x * kEmitPer;
   if (p0 >= e.n) return;
   int lo = 0, hi = e.ng;  // invariant: s_rel[lo] <= p0 < s_rel[hi]
@@ -339,15 +339,14 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
   }
   ushort4 r;  // tile rectangle x0, x1, y0, y1
   uint4 sp;   // packed kept runs
+  TileEllipse te;  // the ellipse of a rectangle without packed runs
   int ty = 0, c0 = 0, c1 = -1;  // current row and its kept columns [c0, c1]
   uint32_t dbits = 0, id = 0;
   auto row = [&]() {
-    if (spans_packed(sp)) {
+    if (spans_packed(sp))
       packed_row(sp, ty - (int)r.z, (int)r.x, c0, c1);
-    } else {  // a rectangle the test does not apply to keeps every tile
-      c0 = (int)r.x;
-      c1 = (int)r.y;
-    }
+    else
+      tile_row_span(te, ty, (int)r.x, (int)r.y, c0, c1);
   };
   auto skip_empty = [&]() {
     while (c1 < c0 && ty < (int)r.w) {
@@ -359,29 +358,19 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
     sp = sruns[2 * (size_t)g];
     const uint4 b = sruns[2 * (size_t)g + 1];
     r = make_ushort4((uint16_t)(b.x & 0xFFFFu), (uint16_t)(b.x >> 16), (uint16_t)(b.y & 0xFFFFu), (uint16_t)(b.y >> 16));
-    if (kPayload) {
-      id = b.z;
-      dbits = b.w;
-    }
+    id = b.z;
+    dbits = b.w;
+    if (!spans_packed(sp)) te = tile_ellipse_rec(rec[3 * (size_t)id], rec[3 * (size_t)id + 1], rec[3 * (size_t)id + 2]);
     ty = (int)r.z;
     row();
     skip_empty();
   };
   start(e.g0 + (uint32_t)lo);
   int local = p0 - s_rel[lo];  // pairs of this Gaussian before the lane's first
-  if (!spans_packed(sp)) {
-    // every row of the rectangle is whole: the lane's row follows by one division instead
-    // of a walk over the rows before it (the long walks are in these large rectangles)
-    const int wdt = c1 - c0 + 1;
-    const int dr = min(local / wdt, (int)r.w - ty);
-    ty += dr;
-    local -= dr * wdt;
-  } else {
-    while (local > c1 - c0 && ty < (int)r.w) {
-      local -= c1 >= c0 ? c1 - c0 + 1 : 0;
-      ++ty;
-      row();
-    }
+  while (local > c1 - c0 && ty < (int)r.w) {
+    local -= c1 >= c0 ? c1 - c0 + 1 : 0;
+    ++ty;
+    row();
   }
   int col = min(c0 + local, c1);
   int next = s_rel[lo + 1];
@@ -453,6 +442,7 @@ __device__ __forceinline__ void count_row_segment(int64_t sa, int64_t sb, uint32
 __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __restrict__ vcount, int64_t P,
                                                           int64_t nparts,
                                                           const uint4* __restrict__ sruns,
+                                                          const float4* __restrict__ rec,
                                                           const uint64_t* __restrict__ goff,
                                                           const uint32_t* __restrict__ gstart, int tiles_x,
                                                           uint32_t* __restrict__ cnt_pre,
@@ -481,27 +471,23 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __rest
     const uint4 sp = sruns[2 * g], rb = sruns[2 * g + 1];
     const int tx0 = (int)(rb.x & 0xFFFFu), tx1 = (int)(rb.x >> 16);
     const int ty0 = (int)(rb.y & 0xFFFFu), ty1 = (int)(rb.y >> 16);
-    if (spans_packed(sp)) {  // at most kSpanRows rows, each its own run of kept columns
-      int64_t off = G0;
-      for (int ty = ty0; ty <= ty1 && off < hi; ++ty) {
-        int c0, c1;
+    const bool packed = spans_packed(sp);
+    TileEllipse te;
+    if (!packed) te = tile_ellipse_rec(rec[3 * (size_t)rb.z], rec[3 * (size_t)rb.z + 1], rec[3 * (size_t)rb.z + 2]);
+    int64_t off = G0;
+    for (int ty = ty0; ty <= ty1 && off < hi; ++ty) {
+      int c0, c1;
+      if (packed)
         packed_row(sp, ty - ty0, tx0, c0, c1);
-        if (c1 < c0) continue;
-        const int64_t len = c1 - c0 + 1;
-        const int64_t sa = max(off, lo), sb = min(off + len, hi);
-        if (sa < sb)
-          count_row_segment(sa, sb, (uint32_t)ty * (uint32_t)tiles_x + (uint32_t)c0 + (uint32_t)(sa - off), b0, hp,
-                            s_diff, s_uni, s_hi);
-        off += len;
-      }
-    } else {  // every tile of the rectangle: rows of equal length, so start at the first row in range
-      const int64_t w = tx1 - tx0 + 1;
-      for (int64_t r = (lo - G0) / w; G0 + r * w < hi; ++r) {
-        const int64_t off = G0 + r * w;
-        const int64_t sa = max(off, lo), sb = min(off + w, hi);
-        count_row_segment(sa, sb, (uint32_t)(ty0 + r) * (uint32_t)tiles_x + (uint32_t)tx0 + (uint32_t)(sa - off), b0,
-                          hp, s_diff, s_uni, s_hi);
-      }
+      else
+        tile_row_span(te, ty, tx0, tx1, c0, c1);
+      if (c1 < c0) continue;
+      const int64_t len = c1 - c0 + 1;
+      const int64_t sa = max(off, lo), sb = min(off + len, hi);
+      if (sa < sb)
+        count_row_segment(sa, sb, (uint32_t)ty * (uint32_t)tiles_x + (uint32_t)c0 + (uint32_t)(sa - off), b0, hp,
+                          s_diff, s_uni, s_hi);
+      off += len;
     }
   }
   __syncthreads();
@@ -609,6 +595,7 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t i, int64_t n) {
 __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __restrict__ vcount, int64_t P,
                                                             int64_t nparts,
                                                             const uint4* __restrict__ sruns,
+                                                            const float4* __restrict__ rec,
                                                             const uint64_t* __restrict__ goff,
                                                             const uint32_t* __restrict__ gstart, int tiles_x,
                                                             const uint32_t* __restrict__ cnt_pre,
@@ -639,7 +626,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
   __syncthreads();
   // generate: lane-consecutive, one pad slot per lane so that a wavefront's 8-byte
   // stores spread over the LDS banks
-  lane_pairs<true>(e, s_rel, sruns, tiles_x, [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
+  lane_pairs(e, s_rel, sruns, rec, tiles_x, [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
     const int slot = tid * (kEmitPer + 1) + k;
     s_keys[slot] = ((uint64_t)tile << 32) | (uint64_t)dbits;
     s_vals[slot] = id;
@@ -824,7 +811,6 @@ hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, uint64_t* digit
 // kEmitPart pairs.
 hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int tiles_x, int tile_bits,
                            uint64_t* digit_counts, void* ws, uint64_t* keys, uint32_t* vals, hipStream_t s) {
-  (void)proj;
   if (n == 0 || P == 0)
     return digit_counts ? launch_fill_u32(digit_counts, 2 * GS_TILE_DIGIT_COUNTS, 0u, s) : hipSuccess;
   const BinLayout l = bin_layout(n, P);
@@ -843,12 +829,13 @@ hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int t
   // digit passes of the pair sort above the low byte (tile ids have at most 24 bits)
   const int hp = digit_counts ? (tile_bits > 8 ? (tile_bits - 1) / 8 : 0) : 0;
   uint64_t* dcopies = reinterpret_cast<uint64_t*>(w + l.dcopies);
-  k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, goff, gstart, tiles_x, cnt_pre,
-                                                         csum, hp, dcopies);
+  const float4* rec = reinterpret_cast<const float4*>(proj.rec);
+  k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, rec, goff, gstart, tiles_x,
+                                                         cnt_pre, csum, hp, dcopies);
   k_group_scan<<<(unsigned)l.ngroups, kBinBlock, 0, s>>>(l.nchunks, csum, gsum);
   k_digit_scan<<<kDigits, kBinBlock, 0, s>>>(l.ngroups, gsum, dtotals, dcopies, digit_counts);
-  k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, goff, gstart, tiles_x, cnt_pre,
-                                                          csum, gsum, dtotals, keys, vals);
+  k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, rec, goff, gstart, tiles_x,
+                                                          cnt_pre, csum, gsum, dtotals, keys, vals);
   return hipGetLastError();
 }
 

@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
         const TileEllipse te = tile_ellipse(r0.x, r0.y, r0.z, r0.w, r1.x, tau, __float_as_uint(r2.y),
                                             __float_as_uint(r2.z));
         const int tx0 = (int)(px0 >> 4), tx1 = (int)(px1 >> 4), ty0 = (int)(py0 >> 4), ty1 = (int)(py1 >> 4);
-        if (rect_tested(tx0, tx1, ty0, ty1)) {
+        if (spans_fit(tx0, tx1, ty0, ty1)) {
           uint32_t w[4] = {0u, 0u, 0u, 0u};
           for (int ty = ty0; ty <= ty1; ++ty) {
             int lo, hi;
@@ -293,8 +293,12 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
             w[k >> 1] |= half << (16 * (k & 1));
           }
           sp = make_uint4(w[0], w[1], w[2], w[3]);
-        } else {
-          nt = (uint32_t)(tx1 - tx0 + 1) * (uint32_t)(ty1 - ty0 + 1);
+        } else {  // the same test; the emission recomputes the runs from the record
+          for (int ty = ty0; ty <= ty1; ++ty) {
+            int lo, hi;
+            tile_row_span(te, ty, tx0, tx1, lo, hi);
+            nt += hi >= lo ? (uint32_t)(hi - lo + 1) : 0u;
+          }
           sp = make_uint4(kNoSpans, kNoSpans, kNoSpans, kNoSpans);
         }
       }

@@ -15,8 +15,9 @@
 // band); xl is symmetric.  A band beyond the ellipse's vertical extent keeps nothing.
 //
 // The projection computes the runs once per Gaussian and stores them in the tile record
-// that the emission expands.  Float contraction is off so that the float64 evaluation
-// rounds as written.
+// that the emission expands (for rectangles too large for the record, the emission
+// computes them again from the render record).  Float contraction is off so that the
+// float64 evaluation rounds as written.
 #pragma once
 
 #include "gs_device.h"
@@ -46,8 +47,21 @@ __device__ __forceinline__ TileEllipse tile_ellipse(float u, float v, float A, f
   return e;
 }
 
+// Record form of tile_ellipse: the render record as gs_project stores it (u, v, A, B | C,
+// opacity, r, g | b, pixel box x, pixel box y, 0), with tau = 2 ln(opacity / (1/255))
+// evaluated as the projection evaluates it.
+__device__ __forceinline__ TileEllipse tile_ellipse_rec(const float4 r0, const float4 r1, const float4 r2) {
+  const double tau = 2.0 * log((double)r1.y / (double)kAlphaMin);
+  return tile_ellipse(r0.x, r0.y, r0.z, r0.w, r1.x, tau, __float_as_uint(r2.y), __float_as_uint(r2.z));
+}
+
 // Kept columns [lo, hi] of tile row ty inside [tx0, tx1] (hi < lo: none).  The half-width
 // of the ellipse at height y is sqrt(tau A - det y^2) / A around its centre line -B y / A.
+// A column stays when its pixel-centre x-range meets [xl, xr]: its right edge
+// min(16 c + 15, px1) + 0.5 - u is at least xl and its left edge max(16 c, px0) + 0.5 - u at
+// most xr.  Both edges are nondecreasing in c, so lo is the first column passing the first
+// test and hi the last passing the second; each is found from a guess by the exact tests
+// (a step or two), which gives the columns a walk from tx0 and from tx1 would give.
 __device__ __forceinline__ void tile_row_span(const TileEllipse& e, int ty, int tx0, int tx1, int& lo, int& hi) {
 #pragma clang fp contract(off)
   lo = tx0;
@@ -65,20 +79,27 @@ __device__ __forceinline__ void tile_row_span(const TileEllipse& e, int ty, int 
   }
   const double xr = (sqrt(Dr) - e.B * yc) * e.iA;
   const double xl = (-sqrt(Dl) - e.B * yl) * e.iA;
-  while (lo <= hi && (double)min(kTile * lo + kTile - 1, e.px1) + 0.5 - e.u < xl) ++lo;
-  while (hi >= lo && (double)max(kTile * hi, e.px0) + 0.5 - e.u > xr) --hi;
+  auto right_edge = [&](int c) { return (double)min(kTile * c + kTile - 1, e.px1) + 0.5 - e.u; };
+  auto left_edge = [&](int c) { return (double)max(kTile * c, e.px0) + 0.5 - e.u; };
+  lo = (int)fmin(fmax(ceil((xl + e.u - 15.5) * 0.0625), (double)tx0), (double)(tx1 + 1));
+  while (lo > tx0 && right_edge(lo - 1) >= xl) --lo;
+  while (lo <= tx1 && right_edge(lo) < xl) ++lo;
+  hi = (int)fmin(fmax(floor((xr + e.u - 0.5) * 0.0625), (double)(lo - 1)), (double)tx1);
+  while (hi < tx1 && left_edge(hi + 1) <= xr) ++hi;
+  while (hi >= lo && left_edge(hi) > xr) --hi;
 }
 
-// The test applies to rectangles of at most kSpanRows tile rows and 255 tile columns, whose
-// kept runs the projection stores in 16 bytes, two per row (first kept column - tx0,
-// count); a larger rectangle keeps every tile (conservative; such Gaussians are more than
-// 8 tiles tall on screen) and stores kNoSpans.  The tile record (32 bytes) adds the
-// rectangle (tx0 | tx1 << 16, ty0 | ty1 << 16) and the tile count.
+// Tile record (32 bytes per Gaussian, written by the projection, expanded by the
+// emission): words 0-3 the kept runs of a rectangle of at most kSpanRows tile rows and
+// kSpanCols tile columns, two bytes per row (first kept column - tx0, count); then the
+// rectangle (tx0 | tx1 << 16, ty0 | ty1 << 16) and the tile count.  A larger rectangle
+// stores kNoSpans in words 0-3 and its runs are computed from the render record, row by
+// row with tile_row_span, where the emission needs them: the same test, so the same tiles.
 constexpr int kSpanRows = 8;
 constexpr int kSpanCols = 255;
 constexpr uint32_t kNoSpans = 0xFFFFFFFFu;
 
-__device__ __forceinline__ bool rect_tested(int tx0, int tx1, int ty0, int ty1) {
+__device__ __forceinline__ bool spans_fit(int tx0, int tx1, int ty0, int ty1) {
   return ty1 - ty0 + 1 <= kSpanRows && tx1 - tx0 + 1 <= kSpanCols;
 }
 
