@@ -79,14 +79,15 @@ typedef struct gs_camera {
  *  n_tiles[n]: tiles of the rectangle whose pixel-centre box (inside the pixel box) meets
  *              the record's support ellipse q <= tau ("Training 10M Gaussians in 8 GB:
  *              Spirula Studio's VRAM efficiency", 16-bit AABB section: an ellipse test
- *              after the box), for rectangles of at most 8 tile rows and 255 tile columns;
- *              a larger rectangle keeps all its tiles.  0 when culled or no tile passes.
+ *              after the box), for every rectangle whatever its size.  0 when culled or no
+ *              tile passes.
  *  clamp[n]:   bit c set when colour channel c was negative before the clamp at 0.
  *  runs[n][8]: the tile record gs_bin_tiles expands, 32 bytes per Gaussian: words 0-3
- *              the kept tiles of each tile row of a tested rectangle, two bytes per row
- *              (first kept column - tx0, kept count), rows in order from ty0, all bytes
- *              0xFF for a rectangle the test does not apply to; word 4 = tx0 | tx1 << 16;
- *              word 5 = ty0 | ty1 << 16; word 6 = n_tiles; word 7 = 0. */
+ *              the kept tiles of each tile row of a rectangle of at most 8 tile rows and
+ *              255 tile columns, two bytes per row (first kept column - tx0, kept count),
+ *              rows in order from ty0; all bytes 0xFF for a larger rectangle, whose kept
+ *              tiles gs_bin_tiles recomputes from rec by the same test; word 4 =
+ *              tx0 | tx1 << 16; word 5 = ty0 | ty1 << 16; word 6 = n_tiles; word 7 = 0. */
 typedef struct gs_projected {
   float* rec;
   float* depth;
@@ -328,11 +329,14 @@ typedef struct gs_adam_params {
  *              contiguous bytes), updated in place
  *  bounds[ceil(n/256)][4]  float32 (m_lo, m_hi, v_lo, v_hi) of each 256-unit block, updated
  *              in place.  A zero state with zero bounds is the start (both moments 0).
- * A moment decodes as lo + code * ((hi - lo) * (1 / 65535)).  The step, in float64:
- * m = b1 m + (1 - b1) g, v = b2 v + (1 - b2) g^2, param -= lr (m * ib1) / (sqrt(v * ib2) + eps)
- * with ib = 1 / (1 - beta^step), the parameter rounded once to float32.  Each block's new
- * bounds are its moments' minimum and maximum rounded to float32, and a code is
- * rint((x - lo) * (65535 / (hi - lo))) clamped to [0, 65535] (0 when hi == lo).
+ * Adam (Kingma and Ba) with bias correction: m = b1 m + (1 - b1) g, v = b2 v + (1 - b2) g^2,
+ * param -= lr (m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + eps).  A moment decodes as
+ * lo + code (hi - lo) / 65535; the moments are updated in float64, the parameter's step in
+ * float32 (about 5e-7 relative) and the parameter rounded once.  Each block's new bounds are
+ * its moments' minimum and maximum rounded to float32, and a code is
+ * rint((x - lo) / (hi - lo) * 65535) clamped to [0, 65535] (0 when hi == lo).  Constants
+ * enter as reciprocals computed once, so a code decided within a few float64 roundings of
+ * a half-integer can differ by one from the definition's.
  * Errors: INVALID_ARG (null pointer with n > 0, step < 1, beta outside [0, 1)), HIP.
  */
 gs_status gs_adam_q16(int64_t n, float* params, const float* grads, uint32_t* state, float* bounds,

@@ -8,14 +8,14 @@
 // is Adam (Kingma and Ba) with bias correction.
 //
 // One wavefront per block of 256 units, four contiguous units per lane, one pass: decode
-// both moments from
-// the block's bounds, update them and the parameter in float64, reduce the block's new
-// minimum and maximum of each moment (in the lane, then across the wavefront), and
-// re-encode.  Constants enter
-// as reciprocals computed once (1/65535, 1/(1 - beta^t), and 65535/(hi - lo) per block by one
-// lane), which leaves one float64 division and one square root per unit.  The arithmetic is
-// written in the order of its definition with contraction off, so the codes (integers
-// decided by floating point) and the parameters are bit-exact against a float64 reference.
+// both moments from the block's bounds and update them in float64 (the codes are decided on
+// these values, so they stay within a few float64 roundings of the definition's), update
+// the parameter in float32 (it is stored in float32: the bias-corrected moments rounded to
+// float32, the hardware square root and reciprocal, about 5e-7 relative), reduce the
+// block's new minimum and maximum of each moment (in the lane, then across the wavefront)
+// and re-encode.  Constants enter as reciprocals computed once (1/65535, 1/(1 - beta^t), and
+// 65535/(hi - lo) per block), so no unit pays a division or a float64 square root: the
+// pass is bound by its 20 bytes per unit.
 #include "gs_device.h"
 #include "gs_wave.h"
 
@@ -26,13 +26,14 @@ constexpr double kQMax = 65535.0;
 constexpr double kInvQMax = 1.0 / 65535.0;
 
 struct AdamConsts {
-  double lr, b1, b2, eps, ib1, ib2;  // ib = 1 / (1 - beta^step)
+  double b1, b2, c1, c2, ib1, ib2;  // c = 1 - beta, ib = 1 / (1 - beta^step)
+  float lr, eps;
 };
 
-__device__ __forceinline__ double decode_q16(uint32_t code, float lo, float hi) {
+// step = (hi - lo) / 65535 of the block, as (hi - lo) * (1 / 65535)
+__device__ __forceinline__ double decode_q16(uint32_t code, float lo, double step) {
 #pragma clang fp contract(off)
-  const double l = lo, h = hi;
-  return l + (double)code * ((h - l) * kInvQMax);
+  return (double)lo + (double)code * step;
 }
 
 // scale = 65535 / (hi - lo) of the block; unused when hi == lo
@@ -82,15 +83,20 @@ __global__ __launch_bounds__(kAdamBlock) void k_adam_q16(int64_t U, float* __res
   }
   double m[R], v[R];
   int mn = INT32_MAX, mx = INT32_MIN, vn = INT32_MAX, vx = INT32_MIN;
+  const double mstep = ((double)bd.y - (double)bd.x) * kInvQMax;
+  const double vstep = ((double)bd.w - (double)bd.z) * kInvQMax;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const double g = gv[r];
-    m[r] = decode_q16(wv[r] & 0xFFFFu, bd.x, bd.y);
-    v[r] = decode_q16(wv[r] >> 16, bd.z, bd.w);
-    m[r] = k.b1 * m[r] + (1.0 - k.b1) * g;
-    v[r] = k.b2 * v[r] + (1.0 - k.b2) * (g * g);
-    const double upd = k.lr * (m[r] * k.ib1) / (sqrt(v[r] * k.ib2) + k.eps);
-    pv[r] = (float)((double)pv[r] - upd);
+    m[r] = decode_q16(wv[r] & 0xFFFFu, bd.x, mstep);
+    v[r] = decode_q16(wv[r] >> 16, bd.z, vstep);
+    m[r] = k.b1 * m[r] + k.c1 * g;
+    v[r] = k.b2 * v[r] + k.c2 * (g * g);
+    // the parameter's step in float32: lr m_hat / (sqrt(v_hat) + eps)
+    const float mh = (float)(m[r] * k.ib1), vh = (float)(v[r] * k.ib2);
+    const float den = __builtin_amdgcn_sqrtf(vh) + k.eps;
+    const float upd = k.lr * mh * __builtin_amdgcn_rcpf(den);
+    pv[r] = (float)((double)pv[r] - (double)upd);
     if (u0 + r < U) {
       const int km = order_key((float)m[r]), kv = order_key((float)v[r]);
       mn = min(mn, km); mx = max(mx, km);
@@ -121,10 +127,12 @@ hipError_t launch_adam_q16(int64_t U, float* params, const float* grads, uint32_
                            const gs_adam_params& p, hipStream_t s) {
   if (U == 0) return hipSuccess;
   AdamConsts k;
-  k.lr = (double)p.lr;
+  k.lr = p.lr;
+  k.eps = p.eps;
   k.b1 = (double)p.beta1;
   k.b2 = (double)p.beta2;
-  k.eps = (double)p.eps;
+  k.c1 = 1.0 - k.b1;
+  k.c2 = 1.0 - k.b2;
   k.ib1 = 1.0 / (1.0 - pow(k.b1, (double)p.step));
   k.ib2 = 1.0 / (1.0 - pow(k.b2, (double)p.step));
   const int64_t nb = (U + kAdamBlock - 1) / kAdamBlock;
