@@ -181,3 +181,31 @@ def test_sort_adversarial_keys(kind, leave_in_tmp):
     assert np.array_equal(vs.cpu().numpy().view(np.uint32), vals[order])
     assert np.array_equal(ranges.cpu().numpy(), oracle.tile_ranges(keys[order], tiles))
     say(f"sort {kind}: ok")
+
+
+def test_backward_counts_past_the_lists_stay_inside_them():
+    """gs_render_bwd walks a tile's list up to the pixels' contributor counts and never past
+    the list: with every count 1000 above its tile's list length it evaluates exactly the
+    records of a call whose counts are the list lengths, so the gradients agree (up to the
+    order of the float atomics).  Opacities are low so the transmittance recovered in the
+    reverse walk stays finite over whole lists."""
+    sc, _ = scenes.tiny_scene(21, 1000)
+    sc.opacities[:] = np.random.default_rng(21).uniform(0.02, 0.1, sc.n).astype(np.float32)
+    cam = scenes.Camera(np.eye(3, dtype=np.float32), np.zeros(3, np.float32), 64.0, 64.0, 32.0, 32.0, 64, 64, 0.2)
+    g = gpu_stages(sc, cam, keep_unsorted=False)
+    d = g["dev"]
+    lens = g["ranges"][:, 1] - g["ranges"][:, 0]
+    jj, ii = np.mgrid[0:cam.height, 0:cam.width]
+    per_pixel = lens[(jj // 16) * cam.tiles_x + ii // 16].astype(np.int32)
+    dL = torch.from_numpy(np.random.default_rng(22).choice([-1.0, 1.0], (3, cam.height, cam.width)).astype(np.float32)).cuda()
+    out = []
+    for extra in (0, 1000):
+        nc = torch.from_numpy(per_pixel + extra).cuda()
+        gr = raster.render_bwd(d["means"], d["scales"], d["quats"], d["opac"], d["sh"], sc.sh_degree, cam, d["proj"],
+                               d["vals"], d["ranges"], (0.0, 0.0, 0.0), d["final_T"], nc, dL, None, None, None,
+                               order=d["order"])
+        torch.cuda.synchronize()
+        out.append(gr["grad_screen"].cpu().numpy().astype(np.float64))
+    a, b = out
+    assert np.all(np.isfinite(a)) and np.abs(a).max() > 0
+    assert np.allclose(b, a, rtol=1e-4, atol=1e-6 * np.abs(a).max()), np.abs(b - a).max()

@@ -283,11 +283,13 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
     p.dr = dL[o]; p.dg = dL[plane + o]; p.db = dL[2 * plane + o];
   }
   p.H = fmaf(p.db, bg2, fmaf(p.dg, bg1, p.dr * bg0)) * p.T;
-  const uint32_t wlast = wave_max(p.nc);  // this wavefront walks [0, wlast)
+  const int64_t start = ranges[2 * tile], end = ranges[2 * tile + 1];
+  // this wavefront walks [0, wlast): up to its last contributor, and never past the tile's
+  // list (contributor counts that do not belong to these lists stay inside them)
+  const uint32_t wlast = (uint32_t)min((int64_t)wave_max(p.nc), end - start);
   // the (record, term) whose wavefront sum this lane receives from the transposed reduction
   const int red_r = (lane >> 1) / GS_GRAD_SCREEN, red_e = (lane >> 1) - red_r * GS_GRAD_SCREEN;
   const float red_scale = term_scale(red_e);
-  const int64_t start = ranges[2 * tile];
   float4* my = s_rec[wave];
   // Each wavefront walks its own records [0, wlast) down from the top, 64 at a time:
   // lane l gathers record lo + l (the next, earlier chunk is prefetched into registers
