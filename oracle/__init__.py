@@ -215,8 +215,8 @@ def tile_ranges(keys, num_tiles: int) -> np.ndarray:
 def render_pixels(W: int, H: int, bg, rec, vals, ranges, pix=None) -> dict:
     """Tiled compositing of the listed pixels (all when ``pix`` is None).
 
-    Returns col (npix, 3), T, n, branches (npix, 4, 5) = (r, g, b, T, n) per branch,
-    nbranch (1, 2, 4, or 0 when too ambiguous) and amb flags.
+    Returns col (npix, 3), T, n, branches (npix, 8, 5) = (r, g, b, T, n) per branch,
+    nbranch (1, 2, 4, 8, or 0 with more than three near-threshold decisions) and amb flags.
     """
     lib = _load()
     rec = np.ascontiguousarray(rec, dtype=np.float64)
@@ -230,7 +230,7 @@ def render_pixels(W: int, H: int, bg, rec, vals, ranges, pix=None) -> dict:
         pixa = np.ascontiguousarray(pix, dtype=np.int64)
         npix = pixa.shape[0]
     out = dict(col=np.zeros((npix, 3)), T=np.zeros(npix), n=np.zeros(npix, np.int64),
-               branches=np.zeros((npix, 4, 5)), nbranch=np.zeros(npix, np.int32),
+               branches=np.zeros((npix, 8, 5)), nbranch=np.zeros(npix, np.int32),
                amb=np.zeros(npix, np.uint8))
     lib.orc_render_pixels(C.c_int64(W), C.c_int64(H), _p(bg), _p(rec), _p(vals), _p(ranges),
                           C.c_int64(npix), _p(pixa), _p(out["col"]), _p(out["T"]), _p(out["n"]),

@@ -535,7 +535,7 @@ void orc_tile_ranges(int64_t p, const uint64_t* keys, int64_t num_tiles, int64_t
 /* ------------------------------------------------------------------------------------ */
 
 #define ORC_REC 9
-#define ORC_MAXBR 4
+#define ORC_MAXBR 8
 
 typedef struct {
   double col[3], T;
@@ -606,8 +606,8 @@ static void tile_list(int64_t i, int64_t j, int64_t tiles_x, const int64_t* rang
  * Tiled render of the pixels in pix[] (linear index j*W + i), or of every pixel when
  * pix == NULL (then npix must be W*H).  Per pixel it writes the natural result
  * (out_col[3], out_T, out_n) and, in branches[npix][ORC_MAXBR][5] (r, g, b, T, n), the
- * results of all flips of up to two ambiguous decisions; nbranch = 1, 2 or 4, or 0 when
- * the pixel has more than two ambiguous decisions.  amb_flags: bit0 any ambiguous
+ * results of all flips of up to three ambiguous decisions; nbranch = 1, 2, 4 or 8, or 0
+ * when the pixel has more than three ambiguous decisions.  amb_flags: bit0 any ambiguous
  * threshold decision, bit1 an alpha near the 0.99 clamp.
  * Output arrays are indexed by position in pix[] (or by the pixel when pix == NULL).
  */
@@ -631,7 +631,7 @@ void orc_render_pixels(int64_t W, int64_t H, const double bg[3], const double* r
     out_n[p] = r0.n;
     if (amb_flags) amb_flags[p] = (uint8_t)((r0.n_amb > 0) | ((r0.n_clamp_amb > 0) << 1));
     if (branches) {
-      int nb = r0.n_amb == 0 ? 1 : r0.n_amb == 1 ? 2 : r0.n_amb == 2 ? 4 : 0;
+      int nb = r0.n_amb <= 3 ? 1 << r0.n_amb : 0;
       nbranch[p] = nb;
       double* br = branches + (size_t)p * ORC_MAXBR * 5;
       for (int m = 0; m < ORC_MAXBR; ++m)
