@@ -26,7 +26,7 @@
  *    gs_bin_tiles waits on it, once, to read the pair count back.
  *  - Every call validates its arguments before touching the GPU and returns a gs_status.
  *  - Calls keep no global state and may run concurrently on different streams with
- *    different buffers.
+ *    different buffers (gs_sort_keys_noalloc excepted: its fixed scratch is per GPU).
  *  - Numbers: fp32 storage; the projection evaluates the binning-critical geometry
  *    (camera-space mean, 2D covariance, support, pixel box) in float64 and rounds once.
  *  - Gaussians with NaN/Inf inputs are culled (every visibility test fails on NaN).
@@ -226,6 +226,28 @@ gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bi
                        uint32_t* vals, uint64_t* keys_tmp, uint32_t* vals_tmp,
                        int64_t* tile_ranges, int32_t* tile_order, const uint64_t* digit_counts,
                        int32_t* result_in_tmp, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gs_sort_keys_noalloc -- gs_sort_keys for callers that cannot allocate device memory or
+ * hand over a workspace: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, results and errors as gs_sort_keys, without the
+ * workspace.  Its scratch is a fixed device array of GS_SORT_NOALLOC_SCRATCH_BYTES inside
+ * the library, one copy per GPU, which that GPU holds until the process ends; its address
+ * is looked up on the first call on the GPU the stream belongs to.  The call allocates
+ * nothing.  A sort needs 279,040 bytes plus 2 KiB per digit pass per started 4096 pairs
+ * (gs_workspace_bytes' sort part): one pass (gs_bin_tiles' pairs for up to 65,536 tiles,
+ * sorted_low_bits = 40) fits up to 66,551,808 pairs, a full six-pass sort up to about 11M;
+ * a larger sort returns GS_ERR_WORKSPACE before any HIP call.  Every call on one GPU uses
+ * that GPU's array and clears what it reads before writing it, so calls run one after
+ * another on one GPU give the results of gs_sort_keys; calls that overlap on one GPU
+ * (other streams, other threads) race on the array and must be serialised by the caller.
+ * Errors: INVALID_ARG, WORKSPACE (the sort needs more than the fixed scratch), OVERFLOW, HIP.
+ */
+#define GS_SORT_NOALLOC_SCRATCH_BYTES (32u << 20)
+gs_status gs_sort_keys_noalloc(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys,
+                               uint32_t* vals, uint64_t* keys_tmp, uint32_t* vals_tmp, int64_t* tile_ranges,
+                               int32_t* tile_order, const uint64_t* digit_counts, int32_t* result_in_tmp,
+                               void* stream);
 
 /*
  * gs_render_fwd -- composite every pixel front to back over its tile's sorted list

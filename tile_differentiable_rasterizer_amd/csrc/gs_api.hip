@@ -312,6 +312,65 @@ gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bi
                                 static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch of gs_sort_keys_noalloc: a fixed device array, one copy per GPU, held until the
+// process ends.  Host code never passes `scratch` itself (its host-side name is not a
+// device address): sort_scratch() looks up this GPU's address once, with the GPU current.
+static __device__ __align__(256) unsigned char scratch[GS_SORT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the GPU that `stream` belongs to (looked up on the first
+// call on that GPU, with it current, and kept).
+hipError_t sort_scratch(hipStream_t stream, void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t r = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (r != hipSuccess) return r;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+gs_status gs_sort_keys_noalloc(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys,
+                               uint32_t* vals, uint64_t* keys_tmp, uint32_t* vals_tmp, int64_t* tile_ranges,
+                               int32_t* tile_order, const uint64_t* digit_counts, int32_t* result_in_tmp,
+                               void* stream) {
+  if (n_pairs < 0 || num_tiles < 1 || !tile_ranges || sorted_low_bits < 0 || sorted_low_bits > 64)
+    return GS_ERR_INVALID_ARG;
+  if (n_pairs > 0 && (!keys || !vals || !keys_tmp || !vals_tmp)) return GS_ERR_INVALID_ARG;
+  if (n_pairs >= ((int64_t)1 << 62)) return GS_ERR_OVERFLOW;
+  if (sort_workspace_bytes(n_pairs, num_tiles, sorted_low_bits) > (size_t)GS_SORT_NOALLOC_SCRATCH_BYTES)
+    return GS_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (sort_scratch(s, &ws) != hipSuccess) return GS_ERR_HIP;
+  return hip_status(launch_sort(n_pairs, num_tiles, keys, vals, keys_tmp, vals_tmp, tile_ranges, tile_order,
+                                sorted_low_bits, digit_counts, result_in_tmp, ws, s));
+}
+
 gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_vals, const int64_t* tile_ranges,
                         const int32_t* tile_order, const gs_camera* cam, const float bg[3], float* image,
                         float* final_T, uint32_t* n_contrib, void* stream) {

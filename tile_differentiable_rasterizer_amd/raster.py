@@ -75,6 +75,7 @@ def lib():
         L.gs_workspace_bytes.restype = sz
         L.gs_bin_tiles.argtypes = [i64, GsProjected, C.POINTER(GsCamera), vp, vp, i64, C.POINTER(i64), vp, vp, sz, vp]
         L.gs_sort_keys.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, C.POINTER(i32), vp, sz, vp]
+        L.gs_sort_keys_noalloc.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, C.POINTER(i32), vp]
         L.gs_render_fwd.argtypes = [i64, GsProjected, vp, vp, vp, C.POINTER(GsCamera), C.POINTER(C.c_float), vp,
                                     vp, vp, vp]
         L.gs_render_bwd.argtypes = [i64, vp, vp, vp, vp, vp, i32, C.POINTER(GsCamera), GsProjected, vp, vp, vp,
@@ -86,7 +87,8 @@ def lib():
         L.gs_adam_q16.argtypes = [i64, vp, vp, vp, vp, C.POINTER(GsAdamParams), vp]
         L.gs_quantize_sh.argtypes = [i64, vp, i32, i32, vp, vp, vp]
         L.gs_project_qsh.argtypes = [i64, vp, vp, vp, vp, vp, vp, i32, i32, C.POINTER(GsCamera), GsProjected, vp]
-        for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd", "gs_render_bwd", "gs_densify",
+        for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_sort_keys_noalloc", "gs_render_fwd",
+                     "gs_render_bwd", "gs_densify",
                      "gs_adam_q16", "gs_quantize_sh", "gs_project_qsh"):
             getattr(L, name).restype = i32
         L.gs_status_string.argtypes = [i32]
@@ -221,6 +223,19 @@ def sort_keys(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, rang
                               C.byref(where) if leave_in_tmp else None,
                               _ptr(workspace), workspace.numel(), _stream(stream)), "gs_sort_keys")
     return bool(where.value == 1) if leave_in_tmp else False
+
+
+def sort_keys_noalloc(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, ranges, order=None,
+                      sorted_low_bits: int = 40, stream=None, leave_in_tmp: bool = False, digit_counts=None):
+    """gs_sort_keys_noalloc: sort_keys without a workspace (the library's fixed per-GPU
+    scratch; no allocation).  Returns the gs_status instead of raising, so that callers can
+    tell a sort too large for the scratch (GS_ERR_WORKSPACE) from other errors; with
+    ``leave_in_tmp``, also whether the result is in keys_tmp/vals_tmp."""
+    where = C.c_int32(-1)
+    st = lib().gs_sort_keys_noalloc(n_pairs, num_tiles, int(sorted_low_bits), _ptr(keys), _ptr(vals), _ptr(keys_tmp),
+                                    _ptr(vals_tmp), _ptr(ranges), _ptr(order), _ptr(digit_counts),
+                                    C.byref(where) if leave_in_tmp else None, _stream(stream))
+    return (st, bool(where.value == 1)) if leave_in_tmp else st
 
 
 def render_fwd(proj: dict, sorted_vals, ranges, cam, bg, image, final_T, n_contrib, order=None, stream=None):
