@@ -57,6 +57,13 @@ constexpr int kEmitPart = kBinBlock * kEmitPer;  // pairs per emission partition
 constexpr int kDigits = 256;                      // values of the tile's low byte
 constexpr int kCountParts = 8;                    // partitions per counting workgroup
 constexpr int kDigitCopies = 16;                  // copies of the tile-digit counts (spreads the atomics)
+// Bit of a depth-ordered pair count (sn) marking a Gaussian whose rectangle has no packed
+// runs.  The emission passes come in two variants: the common one expands packed runs with
+// integer work only; the other also derives rows from the render record (float64), and
+// runs for the partitions (counting chunks) that hold such a Gaussian.  Keeping the
+// float64 path out of the common variant keeps its registers, and so its occupancy, low.
+constexpr uint32_t kLargeRect = 0x80000000u;
+constexpr int kLargeGrid = 512;  // workgroups of the large variants (persistent over their lists)
 
 
 __global__ __launch_bounds__(kBinBlock) void k_count_blocks(int64_t n, const uint32_t* __restrict__ n_tiles,
@@ -157,10 +164,12 @@ __global__ __launch_bounds__(kBinBlock) void k_compact(int64_t n, const uint32_t
                                                        const uint64_t* __restrict__ vis_off,
                                                        uint32_t* __restrict__ dkeys, uint32_t* __restrict__ dvals,
                                                        uint64_t* __restrict__ dcopies,
-                                                       uint32_t* __restrict__ sort_ws, int64_t sort_words) {
+                                                       uint32_t* __restrict__ sort_ws, int64_t sort_words,
+                                                       uint64_t* __restrict__ lctr) {
   __shared__ uint32_t s_w[kBinPer][kBinBlock / kWave];
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
+  if (blockIdx.x == 0 && tid < 2) lctr[tid] = 0;  // large-rectangle list length, table rows used
   // the depth sort's counters and look-back words start cleared (spread over the grid)
   for (int64_t i = (int64_t)blockIdx.x * kBinBlock + tid; i < sort_words; i += (int64_t)gridDim.x * kBinBlock)
     sort_ws[i] = 0;
@@ -200,8 +209,9 @@ __global__ __launch_bounds__(kBinBlock) void k_compact(int64_t n, const uint32_t
 
 // Per 1024 depth-sorted Gaussians: their pair count; also gathers their tile records
 // into depth order for the emission (the one random-access pass over the Gaussians), with
-// words 6 and 7 (the count, and zero) replaced by the Gaussian's id and depth bits.  The
-// depth sort leaves its result in (dk0, dv0) or (dk1, dv1), as *in_tmp says.
+// words 6 and 7 (the count, and zero) replaced by the Gaussian's id and depth bits, and
+// the count in sn; the positions of rectangles without packed runs go to llist (lctr[0]
+// of them).  The depth sort leaves its result in (dk0, dv0) or (dk1, dv1), as *in_tmp says.
 __global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __restrict__ vcount,
                                                             const int32_t* __restrict__ in_tmp,
                                                             const uint32_t* __restrict__ dk0,
@@ -210,7 +220,8 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __re
                                                             const uint32_t* __restrict__ dv1,
                                                             const uint4* __restrict__ runs,
                                                             uint4* __restrict__ sruns, uint32_t* __restrict__ sn,
-                                                            uint64_t* __restrict__ sums) {
+                                                            uint64_t* __restrict__ sums, uint64_t* __restrict__ lctr,
+                                                            uint32_t* __restrict__ llist) {
   __shared__ uint64_t s_p[kBinBlock / kWave];
   const int64_t v = (int64_t)*vcount;  // visible Gaussians (the grid covers all of them)
   const bool tmp = *in_tmp != 0;
@@ -243,6 +254,8 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __re
       sruns[2 * i] = a[j];
       sruns[2 * i + 1] = make_uint4(b[j].x, b[j].y, id[j], db[j]);
       sn[i] = b[j].z;
+      if (!spans_packed(a[j]))
+        llist[atomicAdd(reinterpret_cast<unsigned long long*>(&lctr[0]), 1ull)] = (uint32_t)i;
       acc += b[j].z;
     }
   }
@@ -257,24 +270,81 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __re
   }
 }
 
+// Row table of the large rectangles (those without packed runs), one wavefront per
+// rectangle: its rows' kept columns by the ellipse test of its render record (float64,
+// rows in parallel) and each row's kept tiles before it, so that the emission passes find
+// a pair's row by a binary search and expand the rows with integer work only.  The
+// rectangle's depth-ordered record then points at its first row (kTableSpans).  A
+// rectangle that does not fit in the table keeps its record and gets kLargeRect in sn:
+// the emission's float64 variants expand it.  Runs while the host waits for the pair
+// count.
+constexpr int kRowsBlock = 256;
+__global__ __launch_bounds__(kRowsBlock) void k_large_rows(const uint64_t* __restrict__ lctr_list,
+                                                           uint64_t* __restrict__ lctr_rows,
+                                                           const uint32_t* __restrict__ llist,
+                                                           const float4* __restrict__ rec, uint4* __restrict__ sruns,
+                                                           uint32_t* __restrict__ sn, uint2* __restrict__ table,
+                                                           int64_t table_rows) {
+  const uint64_t nl = *lctr_list;
+  const int lane = __lane_id();
+  const uint64_t waves = (uint64_t)gridDim.x * (kRowsBlock / kWave);
+  for (uint64_t it = (uint64_t)blockIdx.x * (kRowsBlock / kWave) + threadIdx.x / kWave; it < nl; it += waves) {
+    const uint32_t i = llist[it];
+    const uint4 b = sruns[2 * (size_t)i + 1];
+    const int tx0 = (int)(b.x & 0xFFFFu), tx1 = (int)(b.x >> 16);
+    const int ty0 = (int)(b.y & 0xFFFFu), ty1 = (int)(b.y >> 16);
+    const int rows = ty1 - ty0 + 1;
+    // 64-bit row counter: it keeps growing past the table's end without wrapping
+    uint64_t off = 0;
+    if (lane == 0) off = atomicAdd(reinterpret_cast<unsigned long long*>(lctr_rows), (unsigned long long)rows);
+    off = __shfl(off, 0, kWave);
+    if (off + (uint64_t)rows > (uint64_t)table_rows) {  // no room: the float64 variants expand it
+      if (lane == 0) sn[i] |= kLargeRect;
+      continue;
+    }
+    const TileEllipse te = tile_ellipse_rec(rec[3 * (size_t)b.z], rec[3 * (size_t)b.z + 1], rec[3 * (size_t)b.z + 2]);
+    uint32_t carry = 0;  // kept tiles of the rows before this round
+    for (int r0 = 0; r0 < rows; r0 += kWave) {
+      const int r = r0 + lane;
+      int c0 = 0, c1 = -1;
+      if (r < rows) tile_row_span(te, ty0 + r, tx0, tx1, c0, c1);
+      const uint32_t cnt = c1 >= c0 ? (uint32_t)(c1 - c0 + 1) : 0u;
+      const uint32_t inc = wave_inclusive_scan(cnt);
+      if (r < rows) table[off + r] = make_uint2((uint32_t)(cnt ? c0 : 0) | (cnt << 16), carry + inc - cnt);
+      carry += (uint32_t)__shfl((int)inc, kWave - 1, kWave);
+    }
+    if (lane == 0) sruns[2 * (size_t)i] = make_uint4(kTableSpans, (uint32_t)off, 0u, 0u);
+  }
+}
+
 // Per-Gaussian pair offsets in depth order and the first Gaussian of every emission
 // partition: goff[i] = pairs of the depth-sorted Gaussians before i (i in [0, v]);
 // gstart[b] = the Gaussian holding pair b * kEmitPart.  Every visible Gaussian has at
 // least one pair, so each partition start falls inside exactly one Gaussian's range.
+// A Gaussian marked kLargeRect flags the partitions and counting chunks its pairs fall
+// in (pflag, cflag, cleared beforehand) and appends each one, once, to the lists that
+// the large variants of the emission passes walk: plist / clist, with their lengths in
+// lcount[0] / lcount[1] (the lists' order does not matter).
 __global__ __launch_bounds__(kBinBlock) void k_offsets(const uint64_t* __restrict__ vcount,
                                                        const uint32_t* __restrict__ sn,
                                                        const uint64_t* __restrict__ block_off,
-                                                       uint64_t* __restrict__ goff, uint32_t* __restrict__ gstart) {
+                                                       uint64_t* __restrict__ goff, uint32_t* __restrict__ gstart,
+                                                       uint32_t* __restrict__ pflag, uint32_t* __restrict__ cflag,
+                                                       uint32_t* __restrict__ plist, uint32_t* __restrict__ clist,
+                                                       uint32_t* __restrict__ lcount) {
   __shared__ uint64_t s_w[kBinBlock / kWave];
   const int64_t v = (int64_t)*vcount;
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
   uint32_t cnt[kBinPer];
+  uint32_t large = 0;  // bit j: position j holds a large rectangle
   uint64_t tsum = 0;
 #pragma unroll
   for (int j = 0; j < kBinPer; ++j) {  // each thread owns kBinPer consecutive positions
     const int64_t i = base + (int64_t)tid * kBinPer + j;
-    cnt[j] = i < v ? sn[i] : 0u;
+    const uint32_t c = i < v ? sn[i] : 0u;
+    cnt[j] = c & ~kLargeRect;
+    large |= (c & kLargeRect) ? 1u << j : 0u;
     tsum += cnt[j];
   }
   const uint64_t inc = wave_inclusive_scan(tsum);
@@ -289,6 +359,13 @@ __global__ __launch_bounds__(kBinBlock) void k_offsets(const uint64_t* __restric
     goff[i] = pre;
     for (uint64_t pb = (pre + kEmitPart - 1) / kEmitPart; pb * kEmitPart < pre + cnt[j]; ++pb)
       gstart[pb] = (uint32_t)i;
+    if ((large >> j) & 1u) {
+      for (uint64_t pb = pre / kEmitPart; pb * kEmitPart < pre + cnt[j]; ++pb) {
+        if (atomicExch(&pflag[pb], 1u) == 0u) plist[atomicAdd(&lcount[0], 1u)] = (uint32_t)pb;
+        const uint64_t cb = pb / kCountParts;
+        if (atomicExch(&cflag[cb], 1u) == 0u) clist[atomicAdd(&lcount[1], 1u)] = (uint32_t)cb;
+      }
+    }
     pre += cnt[j];
     if (i == v - 1) goff[v] = pre;
   }
@@ -320,6 +397,23 @@ __device__ __forceinline__ EmitPart stage_partition(int64_t b, int64_t nparts, i
   return e;
 }
 
+// Kept columns [c0, c1] of a row-table entry (first kept column | count << 16).
+__device__ __forceinline__ void table_row(const uint2 t, int& c0, int& c1) {
+  c0 = (int)(t.x & 0xFFFFu);
+  c1 = c0 + (int)(t.x >> 16) - 1;
+}
+
+// Last row k of a rectangle's `rows` table entries whose earlier rows hold at most `pair`
+// kept tiles (entry k's .y); when pair is below the rectangle's total, row k holds it.
+__device__ __forceinline__ int table_find(const uint2* __restrict__ t, int rows, uint32_t pair) {
+  int a = 0, b = rows - 1;  // t[0].y = 0 <= pair
+  while (a < b) {
+    const int m = (a + b + 1) >> 1;
+    if (t[m].y <= pair) a = m; else b = m - 1;
+  }
+  return a;
+}
+
 // Generates this lane's pairs; emit(k, tile, id, dbits) receives the pair's slot in the
 // lane's run (0 .. kEmitPer - 1), its tile, its Gaussian's id and the bit pattern of that
 // Gaussian's depth.  sruns holds the depth-sorted Gaussians' tile records (words 6 and 7:
@@ -327,9 +421,10 @@ __device__ __forceinline__ EmitPart stage_partition(int64_t b, int64_t nparts, i
 // and columns inner: read from the runs the projection stored, or, for a rectangle too
 // large for the record, computed row by row from its render record (rec, by id).  Every
 // loop stays inside the rectangle.
-template <typename F>
+template <bool kLarge, typename F>
 __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_rel, const uint4* __restrict__ sruns,
-                                           const float4* __restrict__ rec, int tiles_x, F&& emit) {
+                                           const uint2* __restrict__ table, const float4* __restrict__ rec,
+                                           int tiles_x, F&& emit) {
   const int p0 = (int)threadIdx.x * kEmitPer;
   if (p0 >= e.n) return;
   int lo = 0, hi = e.ng;  // invariant: s_rel[lo] <= p0 < s_rel[hi]
@@ -343,10 +438,16 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
   int ty = 0, c0 = 0, c1 = -1;  // current row and its kept columns [c0, c1]
   uint32_t dbits = 0, id = 0;
   auto row = [&]() {
-    if (spans_packed(sp))
+    if (spans_packed(sp)) {
       packed_row(sp, ty - (int)r.z, (int)r.x, c0, c1);
-    else
+    } else if (sp.x == kTableSpans) {
+      table_row(table[sp.y + (uint32_t)(ty - (int)r.z)], c0, c1);
+    } else if (kLarge) {
       tile_row_span(te, ty, (int)r.x, (int)r.y, c0, c1);
+    } else {  // never: such a Gaussian's partitions run in the float64 variant
+      c0 = (int)r.x;
+      c1 = c0 - 1;
+    }
   };
   auto skip_empty = [&]() {
     while (c1 < c0 && ty < (int)r.w) {
@@ -360,13 +461,22 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
     r = make_ushort4((uint16_t)(b.x & 0xFFFFu), (uint16_t)(b.x >> 16), (uint16_t)(b.y & 0xFFFFu), (uint16_t)(b.y >> 16));
     id = b.z;
     dbits = b.w;
-    if (!spans_packed(sp)) te = tile_ellipse_rec(rec[3 * (size_t)id], rec[3 * (size_t)id + 1], rec[3 * (size_t)id + 2]);
+    if (kLarge && !spans_packed(sp))
+      te = tile_ellipse_rec(rec[3 * (size_t)id], rec[3 * (size_t)id + 1], rec[3 * (size_t)id + 2]);
     ty = (int)r.z;
     row();
     skip_empty();
   };
   start(e.g0 + (uint32_t)lo);
   int local = p0 - s_rel[lo];  // pairs of this Gaussian before the lane's first
+  if (sp.x == kTableSpans) {
+    // the row holding pair `local`: the last row whose earlier rows hold at most `local`
+    // pairs (such a row is never empty)
+    const int k = table_find(table + sp.y, (int)r.w - (int)r.z + 1, (uint32_t)local);
+    ty = (int)r.z + k;
+    local -= (int)table[sp.y + (uint32_t)k].y;
+    row();
+  }
   while (local > c1 - c0 && ty < (int)r.w) {
     local -= c1 >= c0 ? c1 - c0 + 1 : 0;
     ++ty;
@@ -439,22 +549,20 @@ __device__ __forceinline__ void count_row_segment(int64_t sa, int64_t sb, uint32
 // consecutive tile ids at once.  With hp > 0 it also counts the tile-id digits above the
 // low byte (bits [8 + 8q, 16 + 8q), q < hp) for the pair sort, into copy (chunk mod
 // kDigitCopies) of them in dcopies.
-__global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __restrict__ vcount, int64_t P,
-                                                          int64_t nparts,
-                                                          const uint4* __restrict__ sruns,
-                                                          const float4* __restrict__ rec,
-                                                          const uint64_t* __restrict__ goff,
-                                                          const uint32_t* __restrict__ gstart, int tiles_x,
-                                                          uint32_t* __restrict__ cnt_pre,
-                                                          uint64_t* __restrict__ csum, int hp,
-                                                          uint64_t* __restrict__ dcopies) {
+template <bool kLarge>
+__device__ __forceinline__ void emit_count_chunk(int64_t chunk, int64_t v, int64_t P, int64_t nparts,
+                                                 const uint4* __restrict__ sruns, const uint2* __restrict__ table,
+                                                 const float4* __restrict__ rec,
+                                                 const uint64_t* __restrict__ goff,
+                                                 const uint32_t* __restrict__ gstart, int tiles_x,
+                                                 uint32_t* __restrict__ cnt_pre, uint64_t* __restrict__ csum, int hp,
+                                                 uint64_t* __restrict__ dcopies) {
   __shared__ int32_t s_diff[kCountParts][kDigits + 1];
   __shared__ uint32_t s_uni[kCountParts];
   __shared__ uint32_t s_hi[GS_TILE_DIGIT_COUNTS];  // the chunk's counts of the higher digits
   __shared__ uint32_t s_w[kCountParts][kBinBlock / kWave];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  const int64_t v = (int64_t)*vcount;
-  const int64_t b0 = (int64_t)blockIdx.x * kCountParts;
+  const int64_t b0 = chunk * kCountParts;
   const int nq = (int)min((int64_t)kCountParts, nparts - b0);
   for (int i = tid; i < kCountParts * (kDigits + 1); i += kBinBlock) (&s_diff[0][0])[i] = 0;
   if (tid < kCountParts) s_uni[tid] = 0;
@@ -471,16 +579,27 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __rest
     const uint4 sp = sruns[2 * g], rb = sruns[2 * g + 1];
     const int tx0 = (int)(rb.x & 0xFFFFu), tx1 = (int)(rb.x >> 16);
     const int ty0 = (int)(rb.y & 0xFFFFu), ty1 = (int)(rb.y >> 16);
-    const bool packed = spans_packed(sp);
+    const bool packed = spans_packed(sp), tabled = sp.x == kTableSpans;
     TileEllipse te;
-    if (!packed) te = tile_ellipse_rec(rec[3 * (size_t)rb.z], rec[3 * (size_t)rb.z + 1], rec[3 * (size_t)rb.z + 2]);
+    if (kLarge && !packed && !tabled)
+      te = tile_ellipse_rec(rec[3 * (size_t)rb.z], rec[3 * (size_t)rb.z + 1], rec[3 * (size_t)rb.z + 2]);
     int64_t off = G0;
-    for (int ty = ty0; ty <= ty1 && off < hi; ++ty) {
+    int ty = ty0;
+    if (tabled && lo > G0) {  // start at the row holding the chunk's first pair of this Gaussian
+      const int k = table_find(table + sp.y, ty1 - ty0 + 1, (uint32_t)(lo - G0));
+      ty = ty0 + k;
+      off = G0 + table[sp.y + (uint32_t)k].y;
+    }
+    for (; ty <= ty1 && off < hi; ++ty) {
       int c0, c1;
       if (packed)
         packed_row(sp, ty - ty0, tx0, c0, c1);
-      else
+      else if (tabled)
+        table_row(table[sp.y + (uint32_t)(ty - ty0)], c0, c1);
+      else if (kLarge)
         tile_row_span(te, ty, tx0, tx1, c0, c1);
+      else  // never: such a Gaussian's chunks run in the float64 variant
+        c1 = (c0 = tx0) - 1;
       if (c1 < c0) continue;
       const int64_t len = c1 - c0 + 1;
       const int64_t sa = max(off, lo), sb = min(off + len, hi);
@@ -510,10 +629,41 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __rest
     cnt_pre[(b0 + q) * kDigits + tid] = running;
     running += c;
   }
-  csum[(int64_t)blockIdx.x * kDigits + tid] = running;
-  uint64_t* dc = dcopies + (blockIdx.x % kDigitCopies) * GS_TILE_DIGIT_COUNTS;
+  csum[chunk * kDigits + tid] = running;
+  uint64_t* dc = dcopies + (chunk % kDigitCopies) * GS_TILE_DIGIT_COUNTS;
   for (int i = tid; i < hp * kDigits; i += kBinBlock)
     if (s_hi[i]) atomicAdd(reinterpret_cast<unsigned long long*>(dc + i), (unsigned long long)s_hi[i]);
+}
+
+// The common variant: one workgroup per chunk; a chunk in the large list is left to
+// k_emit_count_large.
+__global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __restrict__ vcount, int64_t P,
+                                                          int64_t nparts, const uint4* __restrict__ sruns,
+                                                          const uint2* __restrict__ table,
+                                                          const uint32_t* __restrict__ cflag,
+                                                          const uint64_t* __restrict__ goff,
+                                                          const uint32_t* __restrict__ gstart, int tiles_x,
+                                                          uint32_t* __restrict__ cnt_pre, uint64_t* __restrict__ csum,
+                                                          int hp, uint64_t* __restrict__ dcopies) {
+  if (cflag[blockIdx.x]) return;
+  emit_count_chunk<false>(blockIdx.x, (int64_t)*vcount, P, nparts, sruns, table, nullptr, goff, gstart, tiles_x,
+                          cnt_pre, csum, hp, dcopies);
+}
+
+// The chunks of the large list (lcount[1] of them), taken in turn by a small grid.
+__global__ __launch_bounds__(kBinBlock) void k_emit_count_large(
+    const uint64_t* __restrict__ vcount, int64_t P, int64_t nparts, const uint4* __restrict__ sruns,
+    const uint2* __restrict__ table, const float4* __restrict__ rec, const uint32_t* __restrict__ clist,
+    const uint32_t* __restrict__ lcount,
+    const uint64_t* __restrict__ goff, const uint32_t* __restrict__ gstart, int tiles_x,
+    uint32_t* __restrict__ cnt_pre, uint64_t* __restrict__ csum, int hp, uint64_t* __restrict__ dcopies) {
+  const uint32_t n = lcount[1];
+  const int64_t v = (int64_t)*vcount;
+  for (uint32_t it = blockIdx.x; it < n; it += gridDim.x) {
+    emit_count_chunk<true>(clist[it], v, P, nparts, sruns, table, rec, goff, gstart, tiles_x, cnt_pre, csum, hp,
+                           dcopies);
+    __syncthreads();  // the next chunk reuses the shared arrays
+  }
 }
 
 // The chunk totals' exclusive scan over chunks, per digit, in two levels so that every
@@ -592,17 +742,16 @@ __device__ __forceinline__ int64_t xcd_contiguous(int64_t i, int64_t n) {
 // ranked stably by digit (wavefront ballots match equal digits), regrouped by digit in
 // LDS and written as one contiguous run per digit; a run starts at the digit's global
 // base plus the digit's count in earlier partitions.
-__global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __restrict__ vcount, int64_t P,
-                                                            int64_t nparts,
-                                                            const uint4* __restrict__ sruns,
-                                                            const float4* __restrict__ rec,
-                                                            const uint64_t* __restrict__ goff,
-                                                            const uint32_t* __restrict__ gstart, int tiles_x,
-                                                            const uint32_t* __restrict__ cnt_pre,
-                                                            const uint64_t* __restrict__ cpre,
-                                                            const uint64_t* __restrict__ gpre,
-                                                            const uint64_t* __restrict__ totals,
-                                                            uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+template <bool kLarge>
+__device__ __forceinline__ void emit_scatter_part(int64_t b, int64_t v, int64_t P, int64_t nparts,
+                                                  const uint4* __restrict__ sruns, const uint2* __restrict__ table,
+                                                  const float4* __restrict__ rec,
+                                                  const uint64_t* __restrict__ goff,
+                                                  const uint32_t* __restrict__ gstart, int tiles_x,
+                                                  const uint32_t* __restrict__ cnt_pre,
+                                                  const uint64_t* __restrict__ cpre, const uint64_t* __restrict__ gpre,
+                                                  const uint64_t* __restrict__ totals, uint64_t* __restrict__ keys,
+                                                  uint32_t* __restrict__ vals) {
   constexpr int kPad = kEmitPart + kEmitPart / kEmitPer;  // one pad slot per lane run
   __shared__ int32_t s_rel[kEmitPart + 2];
   __shared__ uint64_t s_keys[kPad];
@@ -613,9 +762,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
   __shared__ uint64_t s_w[kBinBlock / kWave];
   __shared__ uint64_t s_gw[kBinBlock / kWave];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  const int64_t v = (int64_t)*vcount;
   for (int i = tid; i < (kBinBlock / kWave) * kDigits; i += kBinBlock) (&s_wh[0][0])[i] = 0;
-  const int64_t b = xcd_contiguous(blockIdx.x, nparts);
   // digit tid's total and its count in earlier partitions: loaded now, used once the pairs
   // are ranked (the global start of this partition's run of the digit)
   const uint64_t gtot = totals[tid];
@@ -626,7 +773,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
   __syncthreads();
   // generate: lane-consecutive, one pad slot per lane so that a wavefront's 8-byte
   // stores spread over the LDS banks
-  lane_pairs(e, s_rel, sruns, rec, tiles_x, [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
+  lane_pairs<kLarge>(e, s_rel, sruns, table, rec, tiles_x, [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
     const int slot = tid * (kEmitPer + 1) + k;
     s_keys[slot] = ((uint64_t)tile << 32) | (uint64_t)dbits;
     s_vals[slot] = id;
@@ -712,15 +859,52 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(const uint64_t* __re
   }
 }
 
+// The common variant: one workgroup per partition (XCD-contiguous); a partition in the
+// large list is left to k_emit_scatter_large.
+__global__ __launch_bounds__(kBinBlock) void k_emit_scatter(
+    const uint64_t* __restrict__ vcount, int64_t P, int64_t nparts, const uint4* __restrict__ sruns,
+    const uint2* __restrict__ table, const uint32_t* __restrict__ pflag, const uint64_t* __restrict__ goff,
+    const uint32_t* __restrict__ gstart,
+    int tiles_x, const uint32_t* __restrict__ cnt_pre, const uint64_t* __restrict__ cpre,
+    const uint64_t* __restrict__ gpre, const uint64_t* __restrict__ totals, uint64_t* __restrict__ keys,
+    uint32_t* __restrict__ vals) {
+  const int64_t b = xcd_contiguous(blockIdx.x, nparts);
+  if (pflag[b]) return;
+  emit_scatter_part<false>(b, (int64_t)*vcount, P, nparts, sruns, table, nullptr, goff, gstart, tiles_x, cnt_pre,
+                           cpre, gpre, totals, keys, vals);
+}
+
+// The partitions of the large list (lcount[0] of them), taken in turn by a small grid.
+__global__ __launch_bounds__(kBinBlock) void k_emit_scatter_large(
+    const uint64_t* __restrict__ vcount, int64_t P, int64_t nparts, const uint4* __restrict__ sruns,
+    const uint2* __restrict__ table, const float4* __restrict__ rec, const uint32_t* __restrict__ plist,
+    const uint32_t* __restrict__ lcount,
+    const uint64_t* __restrict__ goff, const uint32_t* __restrict__ gstart, int tiles_x,
+    const uint32_t* __restrict__ cnt_pre, const uint64_t* __restrict__ cpre, const uint64_t* __restrict__ gpre,
+    const uint64_t* __restrict__ totals, uint64_t* __restrict__ keys, uint32_t* __restrict__ vals) {
+  const uint32_t n = lcount[0];
+  const int64_t v = (int64_t)*vcount;
+  for (uint32_t it = blockIdx.x; it < n; it += gridDim.x) {
+    emit_scatter_part<true>(plist[it], v, P, nparts, sruns, table, rec, goff, gstart, tiles_x, cnt_pre, cpre, gpre,
+                            totals, keys, vals);
+    __syncthreads();  // the next partition reuses the shared arrays
+  }
+}
+
 // Workspace layout (bytes).  The arrays sized by the pair count come last, so the count
 // phase (which runs before P is known) and the emission phase agree on every offset.
 struct BinLayout {
-  size_t pair_sums, vis_sums, sorted_sums, totals, dcopies, dk0, dv0, dk1, dv1, sort, goff, sruns, sn, dtotals, gstart, cnt_pre,
-      csum, gsum, total;
+  size_t pair_sums, vis_sums, sorted_sums, totals, dcopies, dk0, dv0, dk1, dv1, sort, goff, sruns, sn, lctr, llist,
+      ltable, dtotals, gstart, cnt_pre, csum, gsum, flags, plist, clist, total;
   int64_t nb, nparts, nchunks, ngroups;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Rows of the large-rectangle table: a quarter row per Gaussian, at least 256.  Large
+// rectangles are a small fraction of the visible Gaussians (well under 0.1% in the 1M and
+// 10M workloads, at most 11 tile rows there); those that do not fit take the float64 path.
+static int64_t large_table_rows(int64_t n) { return n / 4 > 256 ? n / 4 : 256; }
 
 static BinLayout bin_layout(int64_t n, int64_t P) {
   BinLayout l;
@@ -742,13 +926,23 @@ static BinLayout bin_layout(int64_t n, int64_t P) {
   l.goff = l.sort + align256(radix_workspace_bytes(n, 0, 32));
   l.sruns = l.goff + align256(sizeof(uint64_t) * (size_t)(n + 1));
   l.sn = l.sruns + align256(2 * sizeof(uint4) * (size_t)(n > 0 ? n : 1));
-  l.dtotals = l.sn + align256(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
+  // large rectangles: counters (list length, table rows used), the list of their
+  // depth-ordered positions, and the row table
+  l.lctr = l.sn + align256(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
+  l.llist = l.lctr + 256;
+  l.ltable = l.llist + align256(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
+  l.dtotals = l.ltable + align256(sizeof(uint2) * (size_t)large_table_rows(n));
   l.gstart = l.dtotals + sizeof(uint64_t) * kDigits;
   l.cnt_pre = l.gstart + align256(sizeof(uint32_t) * (size_t)(l.nparts + 1));
   l.csum = l.cnt_pre + align256(sizeof(uint32_t) * kDigits * (size_t)l.nparts);
   l.ngroups = (l.nchunks + kScanGroup - 1) / kScanGroup;
   l.gsum = l.csum + align256(sizeof(uint64_t) * kDigits * (size_t)l.nchunks);
-  l.total = l.gsum + sizeof(uint64_t) * kDigits * (size_t)(l.ngroups > 0 ? l.ngroups : 1);
+  // partition flags [nparts], chunk flags [nchunks] and the two list lengths, contiguous
+  // (one clearing launch); then the lists of large partitions and chunks
+  l.flags = l.gsum + align256(sizeof(uint64_t) * kDigits * (size_t)(l.ngroups > 0 ? l.ngroups : 1));
+  l.plist = l.flags + align256(sizeof(uint32_t) * (size_t)(l.nparts + l.nchunks + 2));
+  l.clist = l.plist + align256(sizeof(uint32_t) * (size_t)(l.nparts > 0 ? l.nparts : 1));
+  l.total = l.clist + sizeof(uint32_t) * (size_t)(l.nchunks > 0 ? l.nchunks : 1);
   return l;
 }
 
@@ -792,16 +986,22 @@ hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, uint64_t* digit
   uint64_t* totals = reinterpret_cast<uint64_t*>(w + l.totals);
   uint4* sruns = reinterpret_cast<uint4*>(w + l.sruns);
   uint32_t* sn = reinterpret_cast<uint32_t*>(w + l.sn);
+  uint64_t* lctr = reinterpret_cast<uint64_t*>(w + l.lctr);
+  uint32_t* llist = reinterpret_cast<uint32_t*>(w + l.llist);
   k_compact<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, proj.n_tiles, proj.depth,
                                                  reinterpret_cast<const uint64_t*>(w + l.vis_sums), dk0, dv0,
                                                  digit_counts ? reinterpret_cast<uint64_t*>(w + l.dcopies) : nullptr,
                                                  reinterpret_cast<uint32_t*>(w + l.sort),
-                                                 (int64_t)(radix_zero_bytes(n, 0, 32) / 4));
+                                                 (int64_t)(radix_zero_bytes(n, 0, 32) / 4), lctr);
   // the sorted depths stay where the last pass wrote them: k_count_sorted picks the buffer
   hipError_t e = radix_sort_u32(n, totals + 1, dk0, dv0, dk1, dv1, 0, 32, w + l.sort, s, false, true);
   if (e != hipSuccess) return e;
   k_count_sorted<<<(unsigned)l.nb, kBinBlock, 0, s>>>(totals + 1, radix_result_in_tmp(w + l.sort), dk0, dv0, dk1,
-                                                      dv1, reinterpret_cast<const uint4*>(proj.runs), sruns, sn, ss);
+                                                      dv1, reinterpret_cast<const uint4*>(proj.runs), sruns, sn, ss,
+                                                      lctr, llist);
+  k_large_rows<<<kLargeGrid / 4, kRowsBlock, 0, s>>>(lctr, lctr + 1, llist, reinterpret_cast<const float4*>(proj.rec),
+                                                     sruns, sn, reinterpret_cast<uint2*>(w + l.ltable),
+                                                     large_table_rows(n));
   k_scan_blocks<<<1, 1024, 0, s>>>(l.nb, ss, totals + 2);
   return hipGetLastError();
 }
@@ -825,17 +1025,33 @@ hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int t
   uint32_t* cnt_pre = reinterpret_cast<uint32_t*>(w + l.cnt_pre);
   uint64_t* csum = reinterpret_cast<uint64_t*>(w + l.csum);
   uint64_t* gsum = reinterpret_cast<uint64_t*>(w + l.gsum);
-  k_offsets<<<(unsigned)l.nb, kBinBlock, 0, s>>>(vcount, sn, ss, goff, gstart);
+  uint32_t* pflag = reinterpret_cast<uint32_t*>(w + l.flags);
+  uint32_t* cflag = pflag + l.nparts;
+  uint32_t* lcount = cflag + l.nchunks;
+  uint32_t* plist = reinterpret_cast<uint32_t*>(w + l.plist);
+  uint32_t* clist = reinterpret_cast<uint32_t*>(w + l.clist);
+  hipError_t e = launch_fill_u32(pflag, l.nparts + l.nchunks + 2, 0u, s);
+  if (e != hipSuccess) return e;
+  k_offsets<<<(unsigned)l.nb, kBinBlock, 0, s>>>(vcount, sn, ss, goff, gstart, pflag, cflag, plist, clist, lcount);
   // digit passes of the pair sort above the low byte (tile ids have at most 24 bits)
   const int hp = digit_counts ? (tile_bits > 8 ? (tile_bits - 1) / 8 : 0) : 0;
   uint64_t* dcopies = reinterpret_cast<uint64_t*>(w + l.dcopies);
   const float4* rec = reinterpret_cast<const float4*>(proj.rec);
-  k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, rec, goff, gstart, tiles_x,
-                                                         cnt_pre, csum, hp, dcopies);
+  // a chunk / partition holding a Gaussian with a large rectangle runs in the large
+  // variant (small persistent grids over the lists k_offsets built), every other one in
+  // the common variant
+  const uint2* table = reinterpret_cast<const uint2*>(w + l.ltable);
+  k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, table, cflag, goff, gstart,
+                                                         tiles_x, cnt_pre, csum, hp, dcopies);
+  k_emit_count_large<<<(unsigned)min(l.nchunks, (int64_t)kLargeGrid), kBinBlock, 0, s>>>(
+      vcount, P, l.nparts, sruns, table, rec, clist, lcount, goff, gstart, tiles_x, cnt_pre, csum, hp, dcopies);
   k_group_scan<<<(unsigned)l.ngroups, kBinBlock, 0, s>>>(l.nchunks, csum, gsum);
   k_digit_scan<<<kDigits, kBinBlock, 0, s>>>(l.ngroups, gsum, dtotals, dcopies, digit_counts);
-  k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, rec, goff, gstart, tiles_x,
-                                                          cnt_pre, csum, gsum, dtotals, keys, vals);
+  k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, table, pflag, goff, gstart,
+                                                          tiles_x, cnt_pre, csum, gsum, dtotals, keys, vals);
+  k_emit_scatter_large<<<(unsigned)min(l.nparts, (int64_t)kLargeGrid), kBinBlock, 0, s>>>(
+      vcount, P, l.nparts, sruns, table, rec, plist, lcount, goff, gstart, tiles_x, cnt_pre, csum, gsum, dtotals, keys,
+      vals);
   return hipGetLastError();
 }
 

@@ -98,12 +98,17 @@ __device__ __forceinline__ void tile_row_span(const TileEllipse& e, int ty, int 
 constexpr int kSpanRows = 8;
 constexpr int kSpanCols = 255;
 constexpr uint32_t kNoSpans = 0xFFFFFFFFu;
+// The emission's depth-ordered copy of a larger rectangle's record may instead point into
+// a row table the binning builds once per frame: words 0-1 = kTableSpans, the index of the
+// rectangle's first row.  A row entry is (first kept column | kept count << 16, kept tiles
+// of the rectangle's earlier rows).
+constexpr uint32_t kTableSpans = 0xFFFFFFFEu;
 
 __device__ __forceinline__ bool spans_fit(int tx0, int tx1, int ty0, int ty1) {
   return ty1 - ty0 + 1 <= kSpanRows && tx1 - tx0 + 1 <= kSpanCols;
 }
 
-__device__ __forceinline__ bool spans_packed(const uint4 sp) { return sp.x != kNoSpans; }
+__device__ __forceinline__ bool spans_packed(const uint4 sp) { return sp.x < kTableSpans; }
 
 // Kept columns [c0, c1] of row k (0-based from ty0) of packed spans.
 __device__ __forceinline__ void packed_row(const uint4 sp, int k, int tx0, int& c0, int& c1) {
