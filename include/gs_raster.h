@@ -26,7 +26,9 @@
  *    gs_bin_tiles waits on it, once, to read the pair count back.
  *  - Every call validates its arguments before touching the GPU and returns a gs_status.
  *  - Calls keep no global state and may run concurrently on different streams with
- *    different buffers (gs_sort_keys_noalloc excepted: its fixed scratch is per GPU).
+ *    different buffers; the exceptions are gs_sort_keys_noalloc (its fixed scratch is per
+ *    GPU) and the one HIP event per host thread and GPU that gs_bin_tiles creates once and
+ *    keeps.  The kernel timer of gs_measure.h is measurement state, outside the method.
  *  - Numbers: fp32 storage; the projection evaluates the binning-critical geometry
  *    (camera-space mean, 2D covariance, support, pixel box) in float64 and rounds once.
  *  - Gaussians with NaN/Inf inputs are culled (every visibility test fails on NaN).
@@ -182,8 +184,10 @@ size_t gs_workspace_bytes(int64_t n, int64_t pair_capacity, int32_t num_tiles);
  * n_pairs points to page-locked host memory (hipHostMalloc, a pinned torch tensor) the
  * count is copied straight into it and the call waits for that copy only: the depth
  * ordering of the Gaussians, which needs no host value, is already queued behind it and
- * keeps the GPU busy meanwhile.  Otherwise the call synchronises the stream before the
- * depth ordering is queued.  Results are the same either way.  With keys == NULL only P
+ * keeps the GPU busy meanwhile.  Into pageable memory HIP performs the copy synchronously,
+ * so the depth ordering is queued after it.  Results are the same either way.  The wait
+ * uses one HIP event per host thread and GPU, created on the thread's first call on that
+ * GPU and kept by the library: a call creates nothing.  With keys == NULL only P
  * is computed.  If P > capacity,
  * returns GS_ERR_CAPACITY with *n_pairs = P and writes no pairs.  The workspace must hold
  * gs_workspace_bytes(n, P, num_tiles) bytes (checked before and after P is known).
@@ -289,7 +293,6 @@ gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, cons
                         const float* final_T, const uint32_t* n_contrib, const float* dL_dimage,
                         gs_grads out, float* densify_accum, int32_t* densify_denom, void* stream);
 
-/* Human-readable name of a status code (static string). */
 /* Parameters of gs_densify (values, host). */
 typedef struct gs_densify_params {
   float grad_threshold;  /* average view-space gradient (pixel units) above which a Gaussian densifies */
@@ -364,26 +367,8 @@ typedef struct gs_adam_params {
 gs_status gs_adam_q16(int64_t n, float* params, const float* grads, uint32_t* state, float* bounds,
                       const gs_adam_params* hyper, void* stream);
 
+/* Human-readable name of a status code (static string). */
 const char* gs_status_string(gs_status status);
-
-/*
- * Measurement hooks (not part of the method): device time of one of the library's
- * kernels, for comparing a kernel's rate with its roofline.
- *
- * gs_kernel_timer_start arms the timer for `kernel`, one of "k_project", "k_render_fwd",
- * "k_render_bwd", "k_project_bwd", "k_densify_emit", "k_adam_q16" (the single kernel behind
- * gs_project, gs_render_fwd, the two halves of gs_render_bwd, the writing pass of gs_densify
- * and gs_adam_q16).  From then on each launch of that kernel is bracketed
- * by two HIP events recorded on the caller's stream; the events are created on first use
- * and kept by the library until the process ends.
- * gs_kernel_timer_stop disarms the timer, waits for the last recorded event and writes the
- * number of timed launches and the sum of their durations in milliseconds.
- * One timer per process; arming it while it is armed is an error.
- * Errors: INVALID_ARG (unknown kernel name, already armed / not armed, NULL outputs),
- * HIP (an event could not be created, recorded or read).
- */
-gs_status gs_kernel_timer_start(const char* kernel);
-gs_status gs_kernel_timer_stop(int64_t* launches, double* total_ms);
 
 #ifdef __cplusplus
 }

@@ -7,12 +7,12 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gs_raster.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("gs_raster.h", "gs_measure.h")]
 LIB = os.path.join(ROOT, "tile_differentiable_rasterizer_amd", "libgsraster.so")
 
 
 def declared():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^\s*(?:gs_status|size_t|const char\*)\s+(gs_\w+)\s*\(", text, re.M)))
 
 

@@ -4,10 +4,12 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
 #include "gs_device.h"
+#include "../../include/gs_measure.h"
 
 namespace gs {
 hipError_t launch_project(int64_t n, const float* means, const float* scales, const float* quats,
@@ -88,6 +90,7 @@ enum TimedKernel { kNone = 0, kProject, kRenderFwd, kRenderBwd, kProjectBwd, kDe
 
 struct KernelTimer {
   std::mutex mu;
+  std::atomic<int> armed_any{0};  // read without the lock on every launch
   TimedKernel armed = kNone;
   std::vector<hipEvent_t> events;  // pairs: start, stop
   size_t used = 0;                 // events recorded since arming
@@ -110,9 +113,11 @@ TimedKernel timed_kernel_id(const char* name) {
   return kNone;
 }
 
-// Records one event of the pair for kernel k when the timer is armed for it.
+// Records one event of the pair for kernel k when the timer is armed for it.  While it is
+// not armed a launch pays one relaxed atomic load and takes no lock.
 void timer_mark(TimedKernel k, hipStream_t s) {
   KernelTimer& t = timer();
+  if (!t.armed_any.load(std::memory_order_acquire)) return;
   std::lock_guard<std::mutex> g(t.mu);
   if (t.armed != k || t.failed) return;
   if (t.used == t.events.size()) {
@@ -243,15 +248,29 @@ gs_status gs_project_qsh(int64_t n, const float* means, const float* scales, con
   }));
 }
 
-// True when p is page-locked host memory (hipHostMalloc, or a pinned torch tensor): a
-// device-to-host copy into it completes without the host draining the whole stream.
-static bool host_pinned(const void* p) {
-  hipPointerAttribute_t a;
-  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
-    (void)hipGetLastError();  // an ordinary host pointer: not an error of this call
-    return false;
+// The event gs_bin_tiles waits on for its pair-count copy: one per host thread and GPU,
+// created on the thread's first binning call on that GPU and kept, so a frame creates
+// nothing.
+hipError_t count_event(hipStream_t s, hipEvent_t* ev) {
+  constexpr int kMaxDevices = 64;
+  thread_local hipEvent_t events[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(s, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  if (!events[dev]) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    hipEvent_t created = nullptr;
+    e = hipEventCreateWithFlags(&created, hipEventDisableTiming);
+    const hipError_t r = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (r != hipSuccess) return r;
+    events[dev] = created;
   }
-  return a.type == hipMemoryTypeHost;
+  *ev = events[dev];
+  return hipSuccess;
 }
 
 gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint64_t* keys, uint32_t* vals,
@@ -269,16 +288,18 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
   if (launch_bin_count(n, proj.n_tiles, workspace, s) != hipSuccess) return GS_ERR_HIP;
   const uint64_t* dP = bin_totals_ptr(n, workspace);
   int64_t P = 0;
-  if (keys && host_pinned(n_pairs)) {
-    // the count lands in the caller's pinned word; the depth phase is queued behind the
-    // copy and runs while the host waits for the copy alone
+  if (keys) {
+    // the count lands in the caller's word and the depth phase, which needs no host value,
+    // is queued behind the copy: with page-locked memory the GPU runs the depth phase while
+    // the host waits for the copy alone; into pageable memory the copy completes before
+    // hipMemcpyAsync returns (HIP performs it synchronously), so the same results follow
+    // without the overlap
     hipEvent_t ev;
-    if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) return GS_ERR_HIP;
-    hipError_t e = hipMemcpyAsync(n_pairs, dP, sizeof(int64_t), hipMemcpyDeviceToHost, s);
+    hipError_t e = count_event(s, &ev);
+    if (e == hipSuccess) e = hipMemcpyAsync(n_pairs, dP, sizeof(int64_t), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipEventRecord(ev, s);
     if (e == hipSuccess) e = launch_bin_depth(n, proj, dc, workspace, s);
     if (e == hipSuccess) e = hipEventSynchronize(ev);
-    (void)hipEventDestroy(ev);
     if (e != hipSuccess) return GS_ERR_HIP;
     P = *n_pairs;
     if (P < 0) return GS_ERR_OVERFLOW;  // a count past INT64_MAX
@@ -287,10 +308,8 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
     if (hipMemcpyAsync(&total, dP, sizeof total, hipMemcpyDeviceToHost, s) != hipSuccess) return GS_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return GS_ERR_HIP;
     if (total > (uint64_t)INT64_MAX) return GS_ERR_OVERFLOW;
-    P = (int64_t)total;
-    *n_pairs = P;
-    if (!keys) return GS_OK;
-    if (launch_bin_depth(n, proj, dc, workspace, s) != hipSuccess) return GS_ERR_HIP;
+    *n_pairs = (int64_t)total;
+    return GS_OK;
   }
   if (P > capacity) return GS_ERR_CAPACITY;
   if (workspace_bytes < bin_workspace_bytes(n, P)) return GS_ERR_WORKSPACE;
@@ -424,6 +443,7 @@ gs_status gs_kernel_timer_start(const char* kernel) {
   t.armed = k;
   t.used = 0;
   t.failed = false;
+  t.armed_any.store(1, std::memory_order_release);
   return GS_OK;
 }
 
@@ -433,6 +453,7 @@ gs_status gs_kernel_timer_stop(int64_t* launches, double* total_ms) {
   std::lock_guard<std::mutex> g(t.mu);
   if (t.armed == kNone) return GS_ERR_INVALID_ARG;
   t.armed = kNone;
+  t.armed_any.store(0, std::memory_order_release);
   *launches = 0;
   *total_ms = 0.0;
   if (t.failed) return GS_ERR_HIP;
