@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration report")
     ap.add_argument("--frames", type=int, default=20, help="timed frames per camera in the per-configuration report")
     ap.add_argument("--oracle-10m", action="store_true",
-                    help="also time the oracle on the 10M-Gaussian configuration (about a minute per thread count)")
+                    help="also time the oracle single-threaded on the 10M-Gaussian configuration (minutes)")
     ap.add_argument("--profile", action="store_true",
                     help="profiler run: no CPU baseline, plus a 1 GiB device copy that calibrates HBM counters")
     return ap.parse_args()
@@ -130,10 +130,10 @@ def main():
             mark(5)
         rec.append((e, with_bwd, P))
 
-    def run(steps, with_bwd, staged=False):
+    def run(steps, with_bwd, staged=False, kern=None):
         recs = []
-        # the library brackets every launch of the compositing kernel with HIP events on its stream
-        kern = "k_render_bwd" if with_bwd else "k_render_fwd"
+        # the library brackets every launch of one kernel with HIP events on its stream
+        kern = kern or ("k_render_bwd" if with_bwd else "k_render_fwd")
         assert raster.kernel_timer_start(kern) == raster.GS_OK
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -172,7 +172,10 @@ def main():
     log("timed: forward only")
     secs_f, times_f, _ = run(args.steps, False)
     fwd_fps = frames / secs_f
-    kernel_ms = {"k_render_bwd": times_t["k_render_bwd"][0], "k_render_fwd": times_f["k_render_fwd"][0]}
+    log("timed: forward only, projection kernel")
+    _, times_p, _ = run(max(1, args.steps // 2), False, kern="k_project")
+    kernel_ms = {"k_render_bwd": times_t["k_render_bwd"][0], "k_render_fwd": times_f["k_render_fwd"][0],
+                 "k_project": times_p["k_project"][0]}
     # per-stage breakdown: a separate pass with events between the stages
     log("stage breakdown")
     _, times, _ = run(max(1, args.steps // 2), True, staged=True)
@@ -206,8 +209,8 @@ def main():
     # stages are whole entry points (several kernels for bin, sort and render_bwd); the
     # roofline object is for the single kernel that takes the most time, k_render_bwd
     stage_report = {s: dict(ms=round(avg[s], 4), **roof(algo[s], avg[s])) for s in algo}
-    kernel_report = {k: dict(ms=round(v, 4), **roof(algo["render_" + k.split("_")[-1]], v))
-                     for k, v in kernel_ms.items()}
+    kernel_stage = {"k_render_bwd": "render_bwd", "k_render_fwd": "render_fwd", "k_project": "project"}
+    kernel_report = {k: dict(ms=round(v, 4), **roof(algo[kernel_stage[k]], v)) for k, v in kernel_ms.items()}
     roof_dom = dict(kernel_report["k_render_bwd"], kernel="k_render_bwd", launches_timed=frames,
                     traffic=traffic_bytes("k_render_bwd"))
 
@@ -292,10 +295,10 @@ def stage_work(N, K, P, tiles, evals, walk, pixels, with_bwd):
         # 16 B per visible + 4 B histogram), the depth-ordered gather (20 B per visible),
         # pairs written (12 B each)
         "bin": (4 * N + 16 * V + (4 * 16 + 4) * V + 20 * V + 12 * P, 0.0),
-        # 24 B/pair per pass, ranges (8 B/pair: the step's read of the sorted keys, counted as
-        # the step's work although the last pass records the ranges without it) + 16 B/tile
-        # (the digit counts come from the binning, so there is no counting read)
-        "sort": ((24 * passes + 8) * P + 16 * tiles, 0.0),
+        # 24 B/pair per pass (keys and ids read and written) and the ranges written
+        # (16 B/tile); the digit counts come from the binning and the last pass records the
+        # ranges, so there is no counting read and no read of the sorted keys
+        "sort": (24 * passes * P + 16 * tiles, 0.0),
         # list entries read once per tile; colour, transmittance and count written per pixel
         "render_fwd": (4 * P + 20 * pixels, OPS_PER_EVAL_FWD * evals),
     }
@@ -497,19 +500,19 @@ def config_report(args, raster, scenes, dev, sc3, cams3):
                  "pairs": int(np.mean([c["pairs"] for c in cams_out])), "peak_alloc_bytes": int(peak)}
         if len(cams_out) > 1:
             entry["cameras"] = cams_out
-        # the oracle on the first camera: every tile for the small scenes, sampled tiles beyond
+        # the oracle on the first camera: every tile for the small scenes, sampled tiles beyond;
+        # at 10M with every host thread by default (about half a minute), single-threaded too
+        # with --oracle-10m
         big = name == "aniso_10m_sh3_1080p"
-        if not args.no_cpu_baseline and (not big or args.oracle_10m):
+        if not args.no_cpu_baseline:
             orc = {}
-            for th in (threads, 1):
+            for th in ((threads, 1) if not big or args.oracle_10m else (threads,)):
                 oracle.set_threads(th)
                 secs, desc = oracle_frame(sc, cam, dLs[0] if with_bwd else None, budget=8.0)
                 orc[f"{th}_threads"] = {"s_per_frame": round(secs, 3), "tiles": desc,
                                         "gpu_speedup": round(secs * 1e3 / mean_ms, 1)}
             oracle.set_threads(threads)
             entry["oracle"] = orc
-        elif big:
-            entry["oracle"] = "not timed by default (--oracle-10m)"
         rep["per_config"][name] = entry
         del sc
     return rep
