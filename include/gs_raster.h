@@ -57,6 +57,8 @@ enum {
 #define GS_REC_FLOATS 12 /* floats per projected render record                            */
 #define GS_GRAD_SCREEN 10 /* floats per Gaussian in the screen-space gradient block        */
 #define GS_TILE_DIGIT_COUNTS 512 /* uint64 words of gs_bin_tiles' tile-digit counts (2 x 256) */
+#define GS_ROW_BLOCK 256     /* Gaussians per region of gs_projected.rows                       */
+#define GS_ROWS_PER_BLOCK 128 /* entries (uint32 pairs) per region of gs_projected.rows          */
 
 /* Pinhole camera, OpenCV frame: x right, y down, z forward.  x_cam = R x_world + t with
  * R row major.  Pixel (i, j) has its centre at (i + 0.5, j + 0.5).  Gaussians with
@@ -87,9 +89,18 @@ typedef struct gs_camera {
  *  runs[n][8]: the tile record gs_bin_tiles expands, 32 bytes per Gaussian: words 0-3
  *              the kept tiles of each tile row of a rectangle of at most 8 tile rows and
  *              255 tile columns, two bytes per row (first kept column - tx0, kept count),
- *              rows in order from ty0; all bytes 0xFF for a larger rectangle, whose kept
- *              tiles gs_bin_tiles recomputes from rec by the same test; word 4 =
- *              tx0 | tx1 << 16; word 5 = ty0 | ty1 << 16; word 6 = n_tiles; word 7 = 0. */
+ *              rows in order from ty0; for a larger rectangle word 0 = 0xFFFFFFFE and word
+ *              1 = the index of its first entry in `rows`, or, when its block's region of
+ *              `rows` is full, all bytes 0xFF (gs_bin_tiles then recomputes its kept tiles
+ *              from rec by the same test); word 4 = tx0 | tx1 << 16; word 5 = ty0 | ty1 << 16;
+ *              word 6 = n_tiles; word 7 = 0.
+ *  rows[ceil(n / GS_ROW_BLOCK) * GS_ROWS_PER_BLOCK][2]: the larger rectangles' kept tiles,
+ *              one entry per tile row from ty0: (first kept column | kept count << 16,
+ *              kept tiles of the rectangle's earlier rows).  Block b of GS_ROW_BLOCK
+ *              Gaussians owns entries [GS_ROWS_PER_BLOCK b, GS_ROWS_PER_BLOCK (b + 1)), a
+ *              quarter of them for each 64 consecutive Gaussians: its first 31 entries
+ *              filled in id order, its last one's first word 1 when one of the 64 has a
+ *              rectangle that did not fit (then left to the float64 path), else 0. */
 typedef struct gs_projected {
   float* rec;
   float* depth;
@@ -97,6 +108,7 @@ typedef struct gs_projected {
   uint32_t* n_tiles;
   uint8_t* clamp;
   uint32_t* runs;
+  uint32_t* rows;
 } gs_projected;
 
 /* Gradients written by gs_render_bwd (all overwritten, N rows each).

@@ -19,10 +19,11 @@ hipError_t launch_project_bwd(int64_t n, const float* means, const float* scales
                               const float* sh, int L, const DevCamera& cam, const gs_projected& proj,
                               const gs_grads& gr, float* accum, int32_t* denom, hipStream_t s);
 size_t bin_workspace_bytes(int64_t n, int64_t n_pairs);
-hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, void* ws, hipStream_t s);
-uint64_t* bin_totals_ptr(int64_t n, void* ws);
+hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, const uint32_t* rows, void* ws, hipStream_t s);
+uint64_t* bin_report_ptr(int64_t n, void* ws);
+bool bin_report(uint64_t report, int64_t* P, bool* large);
 hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, uint64_t* digit_counts, void* ws, hipStream_t s);
-hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int tiles_x, int tile_bits,
+hipError_t launch_bin_emit(int64_t n, int64_t P, bool large, const gs_projected& proj, int tiles_x, int tile_bits,
                            uint64_t* digit_counts, void* ws, uint64_t* keys, uint32_t* vals, hipStream_t s);
 size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_bits);
 int sort_significant_bits(int64_t num_tiles);
@@ -79,7 +80,9 @@ DevCamera dev_camera(const gs_camera* c) {
   return d;
 }
 
-bool projected_ok(const gs_projected& p) { return p.rec && p.depth && p.rect && p.n_tiles && p.clamp && p.runs; }
+bool projected_ok(const gs_projected& p) {
+  return p.rec && p.depth && p.rect && p.n_tiles && p.clamp && p.runs && p.rows;
+}
 
 gs_status hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP; }
 
@@ -285,9 +288,11 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
   const DevCamera d = dev_camera(cam);
   const int tile_bits = sort_significant_bits((int64_t)d.tiles_x * d.tiles_y) - 32;
   uint64_t* dc = keys ? tile_digit_counts : nullptr;
-  if (launch_bin_count(n, proj.n_tiles, workspace, s) != hipSuccess) return GS_ERR_HIP;
-  const uint64_t* dP = bin_totals_ptr(n, workspace);
+  if (launch_bin_count(n, proj.n_tiles, proj.rows, workspace, s) != hipSuccess) return GS_ERR_HIP;
+  // the report word: P, with a flag bit that the call strips (bin_report)
+  const uint64_t* dP = bin_report_ptr(n, workspace);
   int64_t P = 0;
+  bool large = false;
   if (keys) {
     // the count lands in the caller's word and the depth phase, which needs no host value,
     // is queued behind the copy: with page-locked memory the GPU runs the depth phase while
@@ -301,19 +306,19 @@ gs_status gs_bin_tiles(int64_t n, gs_projected proj, const gs_camera* cam, uint6
     if (e == hipSuccess) e = launch_bin_depth(n, proj, dc, workspace, s);
     if (e == hipSuccess) e = hipEventSynchronize(ev);
     if (e != hipSuccess) return GS_ERR_HIP;
-    P = *n_pairs;
-    if (P < 0) return GS_ERR_OVERFLOW;  // a count past INT64_MAX
+    if (!bin_report((uint64_t)*n_pairs, &P, &large)) return GS_ERR_OVERFLOW;  // a count past 2^62
+    *n_pairs = P;
   } else {
-    uint64_t total = 0;
-    if (hipMemcpyAsync(&total, dP, sizeof total, hipMemcpyDeviceToHost, s) != hipSuccess) return GS_ERR_HIP;
+    uint64_t report = 0;
+    if (hipMemcpyAsync(&report, dP, sizeof report, hipMemcpyDeviceToHost, s) != hipSuccess) return GS_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return GS_ERR_HIP;
-    if (total > (uint64_t)INT64_MAX) return GS_ERR_OVERFLOW;
-    *n_pairs = (int64_t)total;
+    if (!bin_report(report, &P, &large)) return GS_ERR_OVERFLOW;
+    *n_pairs = P;
     return GS_OK;
   }
   if (P > capacity) return GS_ERR_CAPACITY;
   if (workspace_bytes < bin_workspace_bytes(n, P)) return GS_ERR_WORKSPACE;
-  return hip_status(launch_bin_emit(n, P, proj, d.tiles_x, tile_bits, dc, workspace, keys, vals, s));
+  return hip_status(launch_bin_emit(n, P, large, proj, d.tiles_x, tile_bits, dc, workspace, keys, vals, s));
 }
 
 gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys, uint32_t* vals,

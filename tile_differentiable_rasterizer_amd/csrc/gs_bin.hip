@@ -57,19 +57,35 @@ constexpr int kEmitPart = kBinBlock * kEmitPer;  // pairs per emission partition
 constexpr int kDigits = 256;                      // values of the tile's low byte
 constexpr int kCountParts = 8;                    // partitions per counting workgroup
 constexpr int kDigitCopies = 16;                  // copies of the tile-digit counts (spreads the atomics)
-// Bit of a depth-ordered pair count (sn) marking a Gaussian whose rectangle has no packed
-// runs.  The emission passes come in two variants: the common one expands packed runs with
-// integer work only; the other also derives rows from the render record (float64), and
-// runs for the partitions (counting chunks) that hold such a Gaussian.  Keeping the
-// float64 path out of the common variant keeps its registers, and so its occupancy, low.
+// Bit of a depth-ordered pair count (sn) marking a Gaussian whose rectangle has neither
+// packed runs nor rows in the projection's row table.  The emission passes come in two
+// variants: the common one expands packed runs and table rows with integer work only; the
+// other also derives rows from the render record (float64), and runs for the partitions
+// (counting chunks) that hold such a Gaussian.  Keeping the float64 path out of the common
+// variant keeps its registers, and so its occupancy, low.
 constexpr uint32_t kLargeRect = 0x80000000u;
-constexpr int kLargeGrid = 512;  // workgroups of the large variants (persistent over their lists)
+constexpr int kLargeGrid = 64;  // workgroups of the large variants (persistent over their lists)
 
 
 __global__ __launch_bounds__(kBinBlock) void k_count_blocks(int64_t n, const uint32_t* __restrict__ n_tiles,
+                                                            const uint2* __restrict__ rows,
                                                             uint64_t* __restrict__ pair_sums,
-                                                            uint64_t* __restrict__ vis_sums) {
+                                                            uint64_t* __restrict__ vis_sums,
+                                                            uint64_t* __restrict__ ovf_sums) {
   __shared__ uint64_t s_p[kBinBlock / kWave], s_v[kBinBlock / kWave];
+  // the projection's overflow flags for this block's Gaussians: one per 64 (the last entry
+  // of each wavefront region of the row table), read by the first kBinChunk / 64 lanes
+  constexpr int kRegions = kBinChunk / kWave;
+  constexpr int kRegionRows = GS_ROWS_PER_BLOCK / (GS_ROW_BLOCK / kWave);
+  uint64_t ovf = 0;
+  {
+    const int64_t r = (int64_t)blockIdx.x * kRegions + threadIdx.x;
+    if (threadIdx.x < kRegions && r * kWave < n) ovf = rows[r * kRegionRows + kRegionRows - 1].x;
+  }
+  if (threadIdx.x < kWave) {
+    ovf = wave_sum(ovf);
+    if (threadIdx.x == 0) ovf_sums[blockIdx.x] = ovf;
+  }
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
   uint64_t acc = 0, vis = 0;
 #pragma unroll
@@ -150,11 +166,21 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(int64_t nb, uint64_t* __re
   scan_sums<1024, 1>(nb, arrays, total);
 }
 
-// The count phase's two scans (pair sums, visible sums) side by side in one launch.
-__global__ __launch_bounds__(1024) void k_scan_blocks2(int64_t nb, uint64_t* __restrict__ a,
-                                                       uint64_t* __restrict__ b, uint64_t* __restrict__ totals) {
-  uint64_t* const arrays[2] = {a, b};
-  scan_sums<1024, 2>(nb, arrays, totals);
+// The count phase's scans (pair sums, visible sums, overflow flags) side by side in one
+// launch: totals[0..2] = P, V, overflowing wavefront regions; then the host's report word
+// totals[3] = P with bit kReportLarge set when a rectangle takes the float64 path
+// (kReportTooLarge when P does not fit below that bit).
+constexpr uint64_t kReportLarge = 1ull << 62;
+constexpr uint64_t kReportTooLarge = ~0ull >> 1;
+__global__ __launch_bounds__(1024) void k_scan_blocks3(int64_t nb, uint64_t* __restrict__ a, uint64_t* __restrict__ b,
+                                                       uint64_t* __restrict__ c, uint64_t* __restrict__ totals) {
+  uint64_t* const arrays[3] = {a, b, c};
+  scan_sums<1024, 3>(nb, arrays, totals);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t P = totals[0];
+    totals[3] = P < kReportLarge ? P | (totals[2] ? kReportLarge : 0ull) : kReportTooLarge;
+  }
 }
 
 // Visible Gaussians' (depth bits, id) in id order.  Round r of a workgroup covers ids
@@ -164,12 +190,10 @@ __global__ __launch_bounds__(kBinBlock) void k_compact(int64_t n, const uint32_t
                                                        const uint64_t* __restrict__ vis_off,
                                                        uint32_t* __restrict__ dkeys, uint32_t* __restrict__ dvals,
                                                        uint64_t* __restrict__ dcopies,
-                                                       uint32_t* __restrict__ sort_ws, int64_t sort_words,
-                                                       uint64_t* __restrict__ lctr) {
+                                                       uint32_t* __restrict__ sort_ws, int64_t sort_words) {
   __shared__ uint32_t s_w[kBinPer][kBinBlock / kWave];
   const int64_t base = (int64_t)blockIdx.x * kBinChunk;
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  if (blockIdx.x == 0 && tid < 2) lctr[tid] = 0;  // large-rectangle list length, table rows used
   // the depth sort's counters and look-back words start cleared (spread over the grid)
   for (int64_t i = (int64_t)blockIdx.x * kBinBlock + tid; i < sort_words; i += (int64_t)gridDim.x * kBinBlock)
     sort_ws[i] = 0;
@@ -210,8 +234,9 @@ __global__ __launch_bounds__(kBinBlock) void k_compact(int64_t n, const uint32_t
 // Per 1024 depth-sorted Gaussians: their pair count; also gathers their tile records
 // into depth order for the emission (the one random-access pass over the Gaussians), with
 // words 6 and 7 (the count, and zero) replaced by the Gaussian's id and depth bits, and
-// the count in sn; the positions of rectangles without packed runs go to llist (lctr[0]
-// of them).  The depth sort leaves its result in (dk0, dv0) or (dk1, dv1), as *in_tmp says.
+// the count in sn, with kLargeRect set for a rectangle whose rows the projection could not
+// keep in its row table.  The depth sort leaves its result in (dk0, dv0) or (dk1, dv1), as
+// *in_tmp says.
 __global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __restrict__ vcount,
                                                             const int32_t* __restrict__ in_tmp,
                                                             const uint32_t* __restrict__ dk0,
@@ -220,8 +245,7 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __re
                                                             const uint32_t* __restrict__ dv1,
                                                             const uint4* __restrict__ runs,
                                                             uint4* __restrict__ sruns, uint32_t* __restrict__ sn,
-                                                            uint64_t* __restrict__ sums, uint64_t* __restrict__ lctr,
-                                                            uint32_t* __restrict__ llist) {
+                                                            uint64_t* __restrict__ sums) {
   __shared__ uint64_t s_p[kBinBlock / kWave];
   const int64_t v = (int64_t)*vcount;  // visible Gaussians (the grid covers all of them)
   const bool tmp = *in_tmp != 0;
@@ -253,9 +277,7 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __re
     if (i < v) {
       sruns[2 * i] = a[j];
       sruns[2 * i + 1] = make_uint4(b[j].x, b[j].y, id[j], db[j]);
-      sn[i] = b[j].z;
-      if (!spans_packed(a[j]))
-        llist[atomicAdd(reinterpret_cast<unsigned long long*>(&lctr[0]), 1ull)] = (uint32_t)i;
+      sn[i] = b[j].z | (a[j].x == kNoSpans ? kLargeRect : 0u);
       acc += b[j].z;
     }
   }
@@ -267,53 +289,6 @@ __global__ __launch_bounds__(kBinBlock) void k_count_sorted(const uint64_t* __re
 #pragma unroll
     for (int w = 0; w < kBinBlock / kWave; ++w) t += s_p[w];
     sums[blockIdx.x] = t;
-  }
-}
-
-// Row table of the large rectangles (those without packed runs), one wavefront per
-// rectangle: its rows' kept columns by the ellipse test of its render record (float64,
-// rows in parallel) and each row's kept tiles before it, so that the emission passes find
-// a pair's row by a binary search and expand the rows with integer work only.  The
-// rectangle's depth-ordered record then points at its first row (kTableSpans).  A
-// rectangle that does not fit in the table keeps its record and gets kLargeRect in sn:
-// the emission's float64 variants expand it.  Runs while the host waits for the pair
-// count.
-constexpr int kRowsBlock = 256;
-__global__ __launch_bounds__(kRowsBlock) void k_large_rows(const uint64_t* __restrict__ lctr_list,
-                                                           uint64_t* __restrict__ lctr_rows,
-                                                           const uint32_t* __restrict__ llist,
-                                                           const float4* __restrict__ rec, uint4* __restrict__ sruns,
-                                                           uint32_t* __restrict__ sn, uint2* __restrict__ table,
-                                                           int64_t table_rows) {
-  const uint64_t nl = *lctr_list;
-  const int lane = __lane_id();
-  const uint64_t waves = (uint64_t)gridDim.x * (kRowsBlock / kWave);
-  for (uint64_t it = (uint64_t)blockIdx.x * (kRowsBlock / kWave) + threadIdx.x / kWave; it < nl; it += waves) {
-    const uint32_t i = llist[it];
-    const uint4 b = sruns[2 * (size_t)i + 1];
-    const int tx0 = (int)(b.x & 0xFFFFu), tx1 = (int)(b.x >> 16);
-    const int ty0 = (int)(b.y & 0xFFFFu), ty1 = (int)(b.y >> 16);
-    const int rows = ty1 - ty0 + 1;
-    // 64-bit row counter: it keeps growing past the table's end without wrapping
-    uint64_t off = 0;
-    if (lane == 0) off = atomicAdd(reinterpret_cast<unsigned long long*>(lctr_rows), (unsigned long long)rows);
-    off = __shfl(off, 0, kWave);
-    if (off + (uint64_t)rows > (uint64_t)table_rows) {  // no room: the float64 variants expand it
-      if (lane == 0) sn[i] |= kLargeRect;
-      continue;
-    }
-    const TileEllipse te = tile_ellipse_rec(rec[3 * (size_t)b.z], rec[3 * (size_t)b.z + 1], rec[3 * (size_t)b.z + 2]);
-    uint32_t carry = 0;  // kept tiles of the rows before this round
-    for (int r0 = 0; r0 < rows; r0 += kWave) {
-      const int r = r0 + lane;
-      int c0 = 0, c1 = -1;
-      if (r < rows) tile_row_span(te, ty0 + r, tx0, tx1, c0, c1);
-      const uint32_t cnt = c1 >= c0 ? (uint32_t)(c1 - c0 + 1) : 0u;
-      const uint32_t inc = wave_inclusive_scan(cnt);
-      if (r < rows) table[off + r] = make_uint2((uint32_t)(cnt ? c0 : 0) | (cnt << 16), carry + inc - cnt);
-      carry += (uint32_t)__shfl((int)inc, kWave - 1, kWave);
-    }
-    if (lane == 0) sruns[2 * (size_t)i] = make_uint4(kTableSpans, (uint32_t)off, 0u, 0u);
   }
 }
 
@@ -359,7 +334,7 @@ __global__ __launch_bounds__(kBinBlock) void k_offsets(const uint64_t* __restric
     goff[i] = pre;
     for (uint64_t pb = (pre + kEmitPart - 1) / kEmitPart; pb * kEmitPart < pre + cnt[j]; ++pb)
       gstart[pb] = (uint32_t)i;
-    if ((large >> j) & 1u) {
+    if (pflag && ((large >> j) & 1u)) {
       for (uint64_t pb = pre / kEmitPart; pb * kEmitPart < pre + cnt[j]; ++pb) {
         if (atomicExch(&pflag[pb], 1u) == 0u) plist[atomicAdd(&lcount[0], 1u)] = (uint32_t)pb;
         const uint64_t cb = pb / kCountParts;
@@ -645,7 +620,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_count(const uint64_t* __rest
                                                           const uint32_t* __restrict__ gstart, int tiles_x,
                                                           uint32_t* __restrict__ cnt_pre, uint64_t* __restrict__ csum,
                                                           int hp, uint64_t* __restrict__ dcopies) {
-  if (cflag[blockIdx.x]) return;
+  if (cflag && cflag[blockIdx.x]) return;  // left to k_emit_count_large
   emit_count_chunk<false>(blockIdx.x, (int64_t)*vcount, P, nparts, sruns, table, nullptr, goff, gstart, tiles_x,
                           cnt_pre, csum, hp, dcopies);
 }
@@ -869,7 +844,7 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter(
     const uint64_t* __restrict__ gpre, const uint64_t* __restrict__ totals, uint64_t* __restrict__ keys,
     uint32_t* __restrict__ vals) {
   const int64_t b = xcd_contiguous(blockIdx.x, nparts);
-  if (pflag[b]) return;
+  if (pflag && pflag[b]) return;  // left to k_emit_scatter_large
   emit_scatter_part<false>(b, (int64_t)*vcount, P, nparts, sruns, table, nullptr, goff, gstart, tiles_x, cnt_pre,
                            cpre, gpre, totals, keys, vals);
 }
@@ -894,17 +869,12 @@ __global__ __launch_bounds__(kBinBlock) void k_emit_scatter_large(
 // Workspace layout (bytes).  The arrays sized by the pair count come last, so the count
 // phase (which runs before P is known) and the emission phase agree on every offset.
 struct BinLayout {
-  size_t pair_sums, vis_sums, sorted_sums, totals, dcopies, dk0, dv0, dk1, dv1, sort, goff, sruns, sn, lctr, llist,
-      ltable, dtotals, gstart, cnt_pre, csum, gsum, flags, plist, clist, total;
+  size_t pair_sums, vis_sums, ovf_sums, sorted_sums, totals, dcopies, dk0, dv0, dk1, dv1, sort, goff, sruns, sn, dtotals, gstart,
+      cnt_pre, csum, gsum, flags, plist, clist, total;
   int64_t nb, nparts, nchunks, ngroups;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Rows of the large-rectangle table: a quarter row per Gaussian, at least 256.  Large
-// rectangles are a small fraction of the visible Gaussians (well under 0.1% in the 1M and
-// 10M workloads, at most 11 tile rows there); those that do not fit take the float64 path.
-static int64_t large_table_rows(int64_t n) { return n / 4 > 256 ? n / 4 : 256; }
 
 static BinLayout bin_layout(int64_t n, int64_t P) {
   BinLayout l;
@@ -915,7 +885,8 @@ static BinLayout bin_layout(int64_t n, int64_t P) {
   const size_t ids = align256(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
   l.pair_sums = 0;
   l.vis_sums = l.pair_sums + sums;
-  l.sorted_sums = l.vis_sums + sums;
+  l.ovf_sums = l.vis_sums + sums;
+  l.sorted_sums = l.ovf_sums + sums;
   l.totals = l.sorted_sums + sums;
   l.dcopies = l.totals + 256;
   l.dk0 = l.dcopies + sizeof(uint64_t) * kDigitCopies * GS_TILE_DIGIT_COUNTS;
@@ -926,12 +897,7 @@ static BinLayout bin_layout(int64_t n, int64_t P) {
   l.goff = l.sort + align256(radix_workspace_bytes(n, 0, 32));
   l.sruns = l.goff + align256(sizeof(uint64_t) * (size_t)(n + 1));
   l.sn = l.sruns + align256(2 * sizeof(uint4) * (size_t)(n > 0 ? n : 1));
-  // large rectangles: counters (list length, table rows used), the list of their
-  // depth-ordered positions, and the row table
-  l.lctr = l.sn + align256(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
-  l.llist = l.lctr + 256;
-  l.ltable = l.llist + align256(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
-  l.dtotals = l.ltable + align256(sizeof(uint2) * (size_t)large_table_rows(n));
+  l.dtotals = l.sn + align256(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
   l.gstart = l.dtotals + sizeof(uint64_t) * kDigits;
   l.cnt_pre = l.gstart + align256(sizeof(uint32_t) * (size_t)(l.nparts + 1));
   l.csum = l.cnt_pre + align256(sizeof(uint32_t) * kDigits * (size_t)l.nparts);
@@ -948,16 +914,28 @@ static BinLayout bin_layout(int64_t n, int64_t P) {
 
 size_t bin_workspace_bytes(int64_t n, int64_t P) { return bin_layout(n, P).total; }
 
-// Phase 1: per-block sums, their scans, P and the visible count V (device, totals[0..1]).
-hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, void* ws, hipStream_t s) {
+// Phase 1: per-block sums, their scans, P and the visible count V (device, totals[0..1]),
+// and the report word for the host (totals[3]: P, and whether the float64 path is needed).
+hipError_t launch_bin_count(int64_t n, const uint32_t* n_tiles, const uint32_t* rows, void* ws, hipStream_t s) {
   const BinLayout l = bin_layout(n, 0);
   char* w = static_cast<char*>(ws);
   uint64_t* ps = reinterpret_cast<uint64_t*>(w + l.pair_sums);
   uint64_t* vs = reinterpret_cast<uint64_t*>(w + l.vis_sums);
+  uint64_t* os = reinterpret_cast<uint64_t*>(w + l.ovf_sums);
   uint64_t* totals = reinterpret_cast<uint64_t*>(w + l.totals);
-  if (l.nb > 0) k_count_blocks<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, n_tiles, ps, vs);
-  k_scan_blocks2<<<1, 1024, 0, s>>>(l.nb, ps, vs, totals);
+  if (l.nb > 0)
+    k_count_blocks<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, n_tiles, reinterpret_cast<const uint2*>(rows), ps, vs, os);
+  k_scan_blocks3<<<1, 1024, 0, s>>>(l.nb, ps, vs, os, totals);
   return hipGetLastError();
+}
+
+// Decodes the report word: the pair count, and whether a rectangle takes the float64 path;
+// false when the count does not fit below the flag bit.
+bool bin_report(uint64_t report, int64_t* P, bool* large) {
+  if (report == kReportTooLarge) return false;
+  *large = (report & kReportLarge) != 0;
+  *P = (int64_t)(report & ~kReportLarge);
+  return true;
 }
 
 // Exclusive scan of nb per-workgroup sums in place by one workgroup; the total to *total.
@@ -966,8 +944,9 @@ hipError_t launch_scan_sums(int64_t nb, uint64_t* sums, uint64_t* total, hipStre
   return hipGetLastError();
 }
 
-uint64_t* bin_totals_ptr(int64_t n, void* ws) {
-  return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + bin_layout(n, 0).totals);
+// The report word the host reads (totals[3]).
+uint64_t* bin_report_ptr(int64_t n, void* ws) {
+  return reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + bin_layout(n, 0).totals) + 3;
 }
 
 // Depth phase, queued right after the count: compact the visible Gaussians, sort them by
@@ -986,30 +965,24 @@ hipError_t launch_bin_depth(int64_t n, const gs_projected& proj, uint64_t* digit
   uint64_t* totals = reinterpret_cast<uint64_t*>(w + l.totals);
   uint4* sruns = reinterpret_cast<uint4*>(w + l.sruns);
   uint32_t* sn = reinterpret_cast<uint32_t*>(w + l.sn);
-  uint64_t* lctr = reinterpret_cast<uint64_t*>(w + l.lctr);
-  uint32_t* llist = reinterpret_cast<uint32_t*>(w + l.llist);
   k_compact<<<(unsigned)l.nb, kBinBlock, 0, s>>>(n, proj.n_tiles, proj.depth,
                                                  reinterpret_cast<const uint64_t*>(w + l.vis_sums), dk0, dv0,
                                                  digit_counts ? reinterpret_cast<uint64_t*>(w + l.dcopies) : nullptr,
                                                  reinterpret_cast<uint32_t*>(w + l.sort),
-                                                 (int64_t)(radix_zero_bytes(n, 0, 32) / 4), lctr);
+                                                 (int64_t)(radix_zero_bytes(n, 0, 32) / 4));
   // the sorted depths stay where the last pass wrote them: k_count_sorted picks the buffer
   hipError_t e = radix_sort_u32(n, totals + 1, dk0, dv0, dk1, dv1, 0, 32, w + l.sort, s, false, true);
   if (e != hipSuccess) return e;
   k_count_sorted<<<(unsigned)l.nb, kBinBlock, 0, s>>>(totals + 1, radix_result_in_tmp(w + l.sort), dk0, dv0, dk1,
-                                                      dv1, reinterpret_cast<const uint4*>(proj.runs), sruns, sn, ss,
-                                                      lctr, llist);
-  k_large_rows<<<kLargeGrid / 4, kRowsBlock, 0, s>>>(lctr, lctr + 1, llist, reinterpret_cast<const float4*>(proj.rec),
-                                                     sruns, sn, reinterpret_cast<uint2*>(w + l.ltable),
-                                                     large_table_rows(n));
-  k_scan_blocks<<<1, 1024, 0, s>>>(l.nb, ss, totals + 2);
+                                                      dv1, reinterpret_cast<const uint4*>(proj.runs), sruns, sn, ss);
+  k_scan_blocks<<<1, 1024, 0, s>>>(l.nb, ss, totals + 4);
   return hipGetLastError();
 }
 
 // Emission phase (the host has read P, and the workspace holds the P-sized arrays): pair
 // offsets and partition starts, then the two emission passes over partitions of
 // kEmitPart pairs.
-hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int tiles_x, int tile_bits,
+hipError_t launch_bin_emit(int64_t n, int64_t P, bool large, const gs_projected& proj, int tiles_x, int tile_bits,
                            uint64_t* digit_counts, void* ws, uint64_t* keys, uint32_t* vals, hipStream_t s) {
   if (n == 0 || P == 0)
     return digit_counts ? launch_fill_u32(digit_counts, 2 * GS_TILE_DIGIT_COUNTS, 0u, s) : hipSuccess;
@@ -1025,13 +998,17 @@ hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int t
   uint32_t* cnt_pre = reinterpret_cast<uint32_t*>(w + l.cnt_pre);
   uint64_t* csum = reinterpret_cast<uint64_t*>(w + l.csum);
   uint64_t* gsum = reinterpret_cast<uint64_t*>(w + l.gsum);
-  uint32_t* pflag = reinterpret_cast<uint32_t*>(w + l.flags);
-  uint32_t* cflag = pflag + l.nparts;
-  uint32_t* lcount = cflag + l.nchunks;
+  // the lists of the float64 variants, only when a rectangle needs them (large): its flags
+  // are cleared first; otherwise the flags stay unread and those variants are not launched
+  uint32_t* pflag = large ? reinterpret_cast<uint32_t*>(w + l.flags) : nullptr;
+  uint32_t* cflag = large ? pflag + l.nparts : nullptr;
+  uint32_t* lcount = large ? cflag + l.nchunks : nullptr;
   uint32_t* plist = reinterpret_cast<uint32_t*>(w + l.plist);
   uint32_t* clist = reinterpret_cast<uint32_t*>(w + l.clist);
-  hipError_t e = launch_fill_u32(pflag, l.nparts + l.nchunks + 2, 0u, s);
-  if (e != hipSuccess) return e;
+  if (large) {
+    const hipError_t e = launch_fill_u32(pflag, l.nparts + l.nchunks + 2, 0u, s);
+    if (e != hipSuccess) return e;
+  }
   k_offsets<<<(unsigned)l.nb, kBinBlock, 0, s>>>(vcount, sn, ss, goff, gstart, pflag, cflag, plist, clist, lcount);
   // digit passes of the pair sort above the low byte (tile ids have at most 24 bits)
   const int hp = digit_counts ? (tile_bits > 8 ? (tile_bits - 1) / 8 : 0) : 0;
@@ -1040,18 +1017,20 @@ hipError_t launch_bin_emit(int64_t n, int64_t P, const gs_projected& proj, int t
   // a chunk / partition holding a Gaussian with a large rectangle runs in the large
   // variant (small persistent grids over the lists k_offsets built), every other one in
   // the common variant
-  const uint2* table = reinterpret_cast<const uint2*>(w + l.ltable);
+  const uint2* table = reinterpret_cast<const uint2*>(proj.rows);
   k_emit_count<<<(unsigned)l.nchunks, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, table, cflag, goff, gstart,
                                                          tiles_x, cnt_pre, csum, hp, dcopies);
-  k_emit_count_large<<<(unsigned)min(l.nchunks, (int64_t)kLargeGrid), kBinBlock, 0, s>>>(
-      vcount, P, l.nparts, sruns, table, rec, clist, lcount, goff, gstart, tiles_x, cnt_pre, csum, hp, dcopies);
+  if (large)
+    k_emit_count_large<<<(unsigned)min(l.nchunks, (int64_t)kLargeGrid), kBinBlock, 0, s>>>(
+        vcount, P, l.nparts, sruns, table, rec, clist, lcount, goff, gstart, tiles_x, cnt_pre, csum, hp, dcopies);
   k_group_scan<<<(unsigned)l.ngroups, kBinBlock, 0, s>>>(l.nchunks, csum, gsum);
   k_digit_scan<<<kDigits, kBinBlock, 0, s>>>(l.ngroups, gsum, dtotals, dcopies, digit_counts);
   k_emit_scatter<<<(unsigned)l.nparts, kBinBlock, 0, s>>>(vcount, P, l.nparts, sruns, table, pflag, goff, gstart,
                                                           tiles_x, cnt_pre, csum, gsum, dtotals, keys, vals);
-  k_emit_scatter_large<<<(unsigned)min(l.nparts, (int64_t)kLargeGrid), kBinBlock, 0, s>>>(
-      vcount, P, l.nparts, sruns, table, rec, plist, lcount, goff, gstart, tiles_x, cnt_pre, csum, gsum, dtotals, keys,
-      vals);
+  if (large)
+    k_emit_scatter_large<<<(unsigned)min(l.nparts, (int64_t)kLargeGrid), kBinBlock, 0, s>>>(
+        vcount, P, l.nparts, sruns, table, rec, plist, lcount, goff, gstart, tiles_x, cnt_pre, csum, gsum, dtotals,
+        keys, vals);
   return hipGetLastError();
 }
 

@@ -23,6 +23,10 @@
 namespace gs {
 
 constexpr int kProjBlock = 256;
+// A wavefront's region of the row table (gs_projected.rows): kWaveRows entries for its
+// large rectangles' rows, then one entry whose first word flags a rectangle that did not fit.
+constexpr uint32_t kRegionRows = GS_ROWS_PER_BLOCK / (kProjBlock / kWave);
+constexpr uint32_t kWaveRows = kRegionRows - 1;
 
 template <int L>
 struct ShLayout {
@@ -206,8 +210,9 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
     const void* __restrict__ shq, const float2* __restrict__ shb,
     const DevCamera cam, float4* __restrict__ rec, float* __restrict__ depth_out,
     ushort4* __restrict__ rect_out, uint32_t* __restrict__ ntiles_out, uint8_t* __restrict__ clamp_out,
-    uint4* __restrict__ runs_out) {
+    uint4* __restrict__ runs_out, uint2* __restrict__ rows_out) {
   using S = ShLayout<L>;
+  static_assert(kProjBlock == GS_ROW_BLOCK, "one row-table region per workgroup");
   const int64_t base = (int64_t)blockIdx.x * kProjBlock;
   const int cnt = (int)min((int64_t)kProjBlock, n - base);
   const int tid = threadIdx.x;
@@ -246,6 +251,7 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
   ushort4 rc = make_ushort4(0, 0, 0, 0);
   uint4 sp = make_uint4(0u, 0u, 0u, 0u);
   uint32_t nt = 0;
+  bool overflow = false;  // a visible rectangle whose rows did not fit in the row table
   if (g.t[2] > cam.near_z) {  // NaN fails
     double t0[3], t1[3], St0[3], St1[3];
     proj_rows(cam, g.t, t0, t1);
@@ -293,13 +299,28 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
             w[k >> 1] |= half << (16 * (k & 1));
           }
           sp = make_uint4(w[0], w[1], w[2], w[3]);
-        } else {  // the same test; the emission recomputes the runs from the record
+        } else {  // the same test, rows kept in this wavefront's region of the row table when they fit
+          // entries in lane order: the rows of the wavefront's lower large rectangles come first
+          // (the loop is uniform over the lanes that take this branch)
+          const uint32_t R = (uint32_t)(ty1 - ty0 + 1);
+          const uint64_t large = __ballot(1);
+          uint32_t off = 0;
+          for (uint64_t m = large; m; m &= m - 1) {
+            const int l = __builtin_ctzll(m);
+            const uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)R, l);
+            off += l < (int)__lane_id() ? r : 0u;
+          }
+          const bool fits = off + R <= kWaveRows;
+          const uint32_t first = (uint32_t)blockIdx.x * GS_ROWS_PER_BLOCK + (uint32_t)(tid / kWave) * kRegionRows + off;
           for (int ty = ty0; ty <= ty1; ++ty) {
             int lo, hi;
             tile_row_span(te, ty, tx0, tx1, lo, hi);
-            nt += hi >= lo ? (uint32_t)(hi - lo + 1) : 0u;
+            const uint32_t c = hi >= lo ? (uint32_t)(hi - lo + 1) : 0u;
+            if (fits) rows_out[first + (uint32_t)(ty - ty0)] = make_uint2((c ? (uint32_t)lo : 0u) | (c << 16), nt);
+            nt += c;
           }
-          sp = make_uint4(kNoSpans, kNoSpans, kNoSpans, kNoSpans);
+          sp = fits ? make_uint4(kTableSpans, first, 0u, 0u) : make_uint4(kNoSpans, kNoSpans, kNoSpans, kNoSpans);
+          overflow = !fits && nt > 0;
         }
       }
     }
@@ -312,6 +333,13 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
   runs_out[2 * i] = sp;
   runs_out[2 * i + 1] = make_uint4((uint32_t)rc.x | ((uint32_t)rc.y << 16), (uint32_t)rc.z | ((uint32_t)rc.w << 16),
                                    nt, 0u);
+  // the last entry of the wavefront's region says whether one of its rectangles overflowed,
+  // so that the binning skips its float64 path when none did (lane 0 of every wavefront
+  // with a Gaussian is active here)
+  const uint64_t ovf = __ballot(overflow);
+  if (__lane_id() == 0)
+    rows_out[(size_t)(blockIdx.x * (kProjBlock / kWave) + tid / kWave) * kRegionRows + kWaveRows] =
+        make_uint2(ovf ? 1u : 0u, 0u);
 }
 
 // Backward of the projection for one Gaussian (float64 geometry), plus the densification
@@ -480,7 +508,7 @@ static hipError_t launch_project_L(int64_t n, const float* means, const float* s
   k_project<L, QB><<<blocks, kProjBlock, 0, s>>>(
       n, means, scales, reinterpret_cast<const float4*>(quats), opac, sh, shq, reinterpret_cast<const float2*>(shb),
       cam, reinterpret_cast<float4*>(out.rec), out.depth, reinterpret_cast<ushort4*>(out.rect), out.n_tiles,
-      out.clamp, reinterpret_cast<uint4*>(out.runs));
+      out.clamp, reinterpret_cast<uint4*>(out.runs), reinterpret_cast<uint2*>(out.rows));
   return hipGetLastError();
 }
 

@@ -20,6 +20,8 @@ TILE = 16
 REC_FLOATS = 12
 GRAD_SCREEN = 10
 TILE_DIGIT_COUNTS = 512  # GS_TILE_DIGIT_COUNTS
+ROW_BLOCK = 256  # GS_ROW_BLOCK
+ROWS_PER_BLOCK = 128  # GS_ROWS_PER_BLOCK
 
 EXPORTS = ("gs_project", "gs_workspace_bytes", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd",
            "gs_render_bwd", "gs_densify", "gs_densify_workspace_bytes", "gs_adam_q16", "gs_quantize_sh",
@@ -40,7 +42,7 @@ class GsCamera(C.Structure):
 
 class GsProjected(C.Structure):
     _fields_ = [("rec", C.c_void_p), ("depth", C.c_void_p), ("rect", C.c_void_p),
-                ("n_tiles", C.c_void_p), ("clamp", C.c_void_p), ("runs", C.c_void_p)]
+                ("n_tiles", C.c_void_p), ("clamp", C.c_void_p), ("runs", C.c_void_p), ("rows", C.c_void_p)]
 
 
 class GsDensifyParams(C.Structure):
@@ -156,12 +158,13 @@ def alloc_projected(n: int, device="cuda") -> dict:
                 rect=torch.empty((n, 4), dtype=torch.int16, device=device),
                 n_tiles=torch.empty(n, dtype=torch.int32, device=device),
                 clamp=torch.empty(n, dtype=torch.uint8, device=device),
-                runs=torch.empty((n, 8), dtype=torch.int32, device=device))
+                runs=torch.empty((n, 8), dtype=torch.int32, device=device),
+                rows=torch.empty((max(1, -(-n // ROW_BLOCK)) * ROWS_PER_BLOCK, 2), dtype=torch.int32, device=device))
 
 
 def projected_struct(p: dict) -> GsProjected:
     return GsProjected(_ptr(p["rec"]), _ptr(p["depth"]), _ptr(p["rect"]), _ptr(p["n_tiles"]), _ptr(p["clamp"]),
-                       _ptr(p["runs"]))
+                       _ptr(p["runs"]), _ptr(p["rows"]))
 
 
 def project(means, scales, quats, opacities, sh, sh_degree: int, cam, out: dict | None = None, stream=None) -> dict:
