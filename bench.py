@@ -118,8 +118,8 @@ def main():
         st, P = raster.bin_tiles(rz.proj, cam, rz.keys, rz.vals, rz.workspace, digit_counts=rz.digit_counts)
         assert st == raster.GS_OK
         mark(2)
-        in_tmp = raster.sort_keys(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, ranges[k], rz.workspace,
-                                  orders[k], leave_in_tmp=True, digit_counts=rz.digit_counts)
+        in_tmp = raster.sort_ids(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, ranges[k], rz.workspace,
+                                 orders[k], digit_counts=rz.digit_counts)
         sv = rz.vals_tmp if in_tmp else rz.vals
         mark(3)
         raster.render_fwd(rz.proj, sv, ranges[k], cam, (0.0, 0.0, 0.0), images[k], finalT[k], ncon[k], orders[k])
@@ -295,10 +295,11 @@ def stage_work(N, K, P, tiles, evals, walk, pixels, with_bwd):
         # 16 B per visible + 4 B histogram), the depth-ordered gather (20 B per visible),
         # pairs written (12 B each)
         "bin": (4 * N + 16 * V + (4 * 16 + 4) * V + 20 * V + 12 * P, 0.0),
-        # 24 B/pair per pass (keys and ids read and written) and the ranges written
-        # (16 B/tile); the digit counts come from the binning and the last pass records the
-        # ranges, so there is no counting read and no read of the sorted keys
-        "sort": (24 * passes * P + 16 * tiles, 0.0),
+        # gs_sort_ids: 24 B/pair per pass (keys and ids read and written) except the last,
+        # which writes the ids only (16 B/pair), and the ranges written (16 B/tile); the
+        # digit counts come from the binning and the last pass records the ranges, so there
+        # is no counting read and no read of the sorted keys
+        "sort": ((24 * passes - 8 if passes else 0) * P + 16 * tiles, 0.0),
         # list entries read once per tile; colour, transmittance and count written per pixel
         "render_fwd": (4 * P + 20 * pixels, OPS_PER_EVAL_FWD * evals),
     }
@@ -370,8 +371,8 @@ def config_frames(raster, scenes, dev, sc, cams, dLs, nframes, warm=3):
             raster.project(means, scales, quats, opac, sh, L, cam, rz.proj)
             st, P = raster.bin_tiles(rz.proj, cam, rz.keys, rz.vals, rz.workspace, digit_counts=rz.digit_counts)
             assert st == raster.GS_OK
-            in_tmp = raster.sort_keys(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, rg, rz.workspace, order,
-                                      leave_in_tmp=True, digit_counts=rz.digit_counts)
+            in_tmp = raster.sort_ids(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, rg, rz.workspace, order,
+                                     digit_counts=rz.digit_counts)
             sv = rz.vals_tmp if in_tmp else rz.vals
             raster.render_fwd(rz.proj, sv, rg, cam, (0.0, 0.0, 0.0), img, fT, nc, order)
             if with_bwd:

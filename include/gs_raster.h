@@ -244,6 +244,21 @@ gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bi
                        int32_t* result_in_tmp, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gs_sort_ids -- gs_sort_keys for the compositing calls, which read only the sorted ids
+ * and the tile ranges ("Better Gaussian Splatting in Julia" s3.2: blend takes each tile's
+ * depth-ordered Gaussians).  Same arguments and results, except that the last digit pass
+ * does not write the sorted keys (8 of the pass's 24 bytes per pair): after the call the
+ * keys of the buffer pair holding the result are unspecified when a digit pass ran, while
+ * the ids, tile_ranges, tile_order and *result_in_tmp are those of gs_sort_keys.
+ * result_in_tmp [host] is required.
+ * Errors: INVALID_ARG (also for result_in_tmp NULL), WORKSPACE, OVERFLOW, HIP.
+ */
+gs_status gs_sort_ids(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys,
+                      uint32_t* vals, uint64_t* keys_tmp, uint32_t* vals_tmp, int64_t* tile_ranges,
+                      int32_t* tile_order, const uint64_t* digit_counts, int32_t* result_in_tmp,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * gs_sort_keys_noalloc -- gs_sort_keys for callers that cannot allocate device memory or
  * hand over a workspace: code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation.  Same arguments, results and errors as gs_sort_keys, without the

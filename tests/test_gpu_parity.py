@@ -9,9 +9,10 @@ import math
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
-from tile_differentiable_rasterizer_amd import scenes
+from tile_differentiable_rasterizer_amd import raster, scenes
 
 pytestmark = pytest.mark.gpu
 
@@ -124,6 +125,66 @@ def test_sort_counts_its_own_digits_the_same(spheres):
     b = gpu_stages(sc, cam, keep_unsorted=False, digit_counts=False)
     for k in ("keys", "vals", "ranges", "image"):
         assert np.array_equal(a[k], b[k]), k
+
+
+def _binned_pairs(sc, cam):
+    dev = torch.device("cuda")
+    means, scales, quats, opac, sh = raster.scene_to_device(sc, dev)
+    proj = raster.project(means, scales, quats, opac, sh, sc.sh_degree, cam)
+    tiles = cam.num_tiles
+    ws = torch.empty(max(raster.workspace_bytes(sc.n, 1, tiles), 8), dtype=torch.uint8, device=dev)
+    st, P = raster.bin_tiles(proj, cam, None, None, ws)
+    keys = torch.empty(max(P, 1), dtype=torch.int64, device=dev)
+    vals = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(raster.workspace_bytes(sc.n, P, tiles), dtype=torch.uint8, device=dev)
+    dc = torch.empty(raster.TILE_DIGIT_COUNTS, dtype=torch.int64, device=dev)
+    st, P = raster.bin_tiles(proj, cam, keys, vals, ws, digit_counts=dc)
+    assert st == raster.GS_OK
+    return P, tiles, keys, vals, dc, ws
+
+
+@pytest.mark.parametrize("case", ["spheres", "aniso1m_cam5", "large_image"])
+def test_sort_ids_matches_sort_keys(case, spheres, aniso1m):
+    """gs_sort_ids (the last digit pass writes the ids only) leaves the ids, ranges and
+    result buffer of gs_sort_keys, bit for bit: one digit pass (800x800, 1080p) and two
+    (a 4200x4150 image, whose first pass must still write the keys)."""
+    if case == "spheres":
+        sc, cam = spheres
+    elif case == "aniso1m_cam5":
+        sc, cam = aniso1m[0], aniso1m[1][5]
+    else:
+        sc, _ = scenes.tiny_scene(11, 2000)
+        cam = scenes.Camera(np.eye(3, dtype=np.float32), np.zeros(3, np.float32), 4400.0, 4400.0, 2100.0, 2075.0,
+                            4200, 4150, 0.2)
+    P, tiles, keys, vals, dc, ws = _binned_pairs(sc, cam)
+    out = []
+    for fn in (raster.sort_keys, raster.sort_ids):
+        k, v = keys.clone(), vals.clone()
+        kt, vt = torch.empty_like(k), torch.empty_like(v)
+        rg = torch.empty((tiles, 2), dtype=torch.int64, device=k.device)
+        order = torch.empty(tiles, dtype=torch.int32, device=k.device)
+        if fn is raster.sort_keys:
+            in_tmp = fn(P, tiles, k, v, kt, vt, rg, ws, order, leave_in_tmp=True, digit_counts=dc)
+        else:
+            in_tmp = fn(P, tiles, k, v, kt, vt, rg, ws, order, digit_counts=dc)
+        torch.cuda.synchronize()
+        rv = (vt if in_tmp else v)[:P].cpu().numpy()
+        out.append((in_tmp, rv, rg.cpu().numpy(), order.cpu().numpy()))
+    (t0, v0, r0, o0), (t1, v1, r1, o1) = out
+    assert t0 == t1 and np.array_equal(v0, v1) and np.array_equal(r0, r1)
+    assert np.array_equal(np.sort(o1), np.arange(tiles))
+    lens = (r1[:, 1] - r1[:, 0])[o1]
+    assert np.all(np.diff(np.floor(np.log2(np.maximum(lens, 1)))) <= 0)
+    say(f"sort_ids {case}: P={P}, result in tmp: {t1}")
+
+
+def test_sort_ids_requires_the_result_word():
+    import ctypes as C
+    L = raster.lib()
+    d = torch.zeros(8, dtype=torch.int64, device="cuda")
+    st = L.gs_sort_ids(0, 16, 40, d.data_ptr(), d.data_ptr(), d.data_ptr(), d.data_ptr(), d.data_ptr(), None, None,
+                       None, d.data_ptr(), 64, None)
+    assert st == raster.GS_ERR_INVALID_ARG
 
 
 def _needles(sc, rng, k, lo, hi, thin=None):

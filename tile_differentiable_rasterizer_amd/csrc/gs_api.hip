@@ -29,7 +29,8 @@ size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_b
 int sort_significant_bits(int64_t num_tiles);
 hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
                        uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits,
-                       const uint64_t* digit_counts, int32_t* result_in_tmp, void* ws, hipStream_t s);
+                       const uint64_t* digit_counts, int32_t* result_in_tmp, void* ws, hipStream_t s,
+                       bool ids_only);
 hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
 size_t densify_workspace_bytes(int64_t n);
 hipError_t launch_quantize_sh(int64_t U, const float* sh, int bits, void* codes, float* bounds, hipStream_t s);
@@ -333,7 +334,22 @@ gs_status gs_sort_keys(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bi
     return GS_ERR_WORKSPACE;
   return hip_status(launch_sort(n_pairs, num_tiles, keys, vals, keys_tmp, vals_tmp, tile_ranges, tile_order,
                                 sorted_low_bits, digit_counts, result_in_tmp, workspace,
-                                static_cast<hipStream_t>(stream)));
+                                static_cast<hipStream_t>(stream), false));
+}
+
+gs_status gs_sort_ids(int64_t n_pairs, int32_t num_tiles, int32_t sorted_low_bits, uint64_t* keys, uint32_t* vals,
+                      uint64_t* keys_tmp, uint32_t* vals_tmp, int64_t* tile_ranges, int32_t* tile_order,
+                      const uint64_t* digit_counts, int32_t* result_in_tmp, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (n_pairs < 0 || num_tiles < 1 || !tile_ranges || sorted_low_bits < 0 || sorted_low_bits > 64 || !result_in_tmp)
+    return GS_ERR_INVALID_ARG;
+  if (n_pairs > 0 && (!keys || !vals || !keys_tmp || !vals_tmp)) return GS_ERR_INVALID_ARG;
+  if (n_pairs >= ((int64_t)1 << 62)) return GS_ERR_OVERFLOW;
+  if (!workspace || workspace_bytes < sort_workspace_bytes(n_pairs, num_tiles, sorted_low_bits))
+    return GS_ERR_WORKSPACE;
+  return hip_status(launch_sort(n_pairs, num_tiles, keys, vals, keys_tmp, vals_tmp, tile_ranges, tile_order,
+                                sorted_low_bits, digit_counts, result_in_tmp, workspace,
+                                static_cast<hipStream_t>(stream), true));
 }
 
 }  // extern "C"
@@ -392,7 +408,7 @@ gs_status gs_sort_keys_noalloc(int64_t n_pairs, int32_t num_tiles, int32_t sorte
   void* ws = nullptr;
   if (sort_scratch(s, &ws) != hipSuccess) return GS_ERR_HIP;
   return hip_status(launch_sort(n_pairs, num_tiles, keys, vals, keys_tmp, vals_tmp, tile_ranges, tile_order,
-                                sorted_low_bits, digit_counts, result_in_tmp, ws, s));
+                                sorted_low_bits, digit_counts, result_in_tmp, ws, s, false));
 }
 
 gs_status gs_render_fwd(int64_t n, gs_projected proj, const uint32_t* sorted_vals, const int64_t* tile_ranges,

@@ -179,9 +179,10 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
     const int32_t* __restrict__ plan, int mode_arg, const uint64_t* __restrict__ dbase,
     const uint64_t* __restrict__ counts, int copies, int32_t* __restrict__ result_word,
     uint64_t* __restrict__ status, uint32_t* __restrict__ tickets, int64_t* __restrict__ tile_ranges,
-    int64_t num_tiles) {
+    int64_t num_tiles, int write_keys) {
   // the buffers this pass reads and writes: given by the host when it knows them (no pass
-  // skipped), else from the plan, which also marks passes to skip
+  // skipped), else from the plan, which also marks passes to skip.  With write_keys = 0
+  // (the last pass of a sort whose caller needs the ids only) the keys are not written.
   const int mode = mode_arg >= 0 ? mode_arg : plan[pass];
   if (mode < 0) return;  // digit constant over all keys: nothing to do
   const K* kin = mode ? k1 : k0;
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
     const uint32_t dd = (uint32_t)(k >> shift) & dmask;
     const uint64_t g = s_gbase[dd] + (uint64_t)(i - (int)s_lbase[dd]);
     if (g < (uint64_t)P) {  // always, given exact digit counts; caller-supplied ones are not trusted
-      kout[g] = k;
+      if (write_keys) kout[g] = k;
       vout[g] = s_vals[i];
       if constexpr (sizeof(K) == 8) {
         // the last pass of a pair sort: the partition is in final order here, so a tile's
@@ -497,7 +498,8 @@ template <typename K>
 static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_t* vals, K* keys_tmp,
                              uint32_t* vals_tmp, int lo, int hi, void* ws, hipStream_t s, bool copy_back = true,
                              bool keep_all = false, const uint64_t* digit_counts = nullptr,
-                             bool ws_zeroed = false, int64_t* tile_ranges = nullptr, int64_t num_tiles = 0) {
+                             bool ws_zeroed = false, int64_t* tile_ranges = nullptr, int64_t num_tiles = 0,
+                             bool ids_only = false) {
   const int passes = radix_passes(lo, hi);
   char* w = static_cast<char*>(ws);
   if (P <= 1 || passes == 0)  // nothing moves: the result is in keys/vals, as the word says
@@ -545,7 +547,7 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
         keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p, pbits[p], plan, planless ? p % 2 : -1,
         dbase + p * kRadix, planless ? digit_counts + p * kRadix : nullptr, 1,
         planless && p == passes - 1 ? plan + kMaxPasses : nullptr, status + poff[p], tickets,
-        p == passes - 1 ? tile_ranges : nullptr, num_tiles);
+        p == passes - 1 ? tile_ranges : nullptr, num_tiles, ids_only && p == passes - 1 ? 0 : 1);
   }
   if (copy_back) {
     const int64_t want = (P + 255) / 256;
@@ -603,7 +605,8 @@ size_t sort_workspace_bytes(int64_t n_pairs, int64_t num_tiles, int sorted_low_b
 // reports where it is; with NULL, k_ranges moves it back to keys/vals.
 hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* vals, uint64_t* keys_tmp,
                        uint32_t* vals_tmp, int64_t* ranges, int32_t* order, int sorted_low_bits,
-                       const uint64_t* digit_counts, int32_t* result_in_tmp, void* ws, hipStream_t s) {
+                       const uint64_t* digit_counts, int32_t* result_in_tmp, void* ws, hipStream_t s,
+                       bool ids_only) {
   const int hi = sort_significant_bits(num_tiles);
   const int passes = P > 1 ? radix_passes(sorted_low_bits, hi) : 0;
   const bool in_tmp = passes % 2 == 1;
@@ -616,7 +619,7 @@ hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* v
     k_zero2<<<blocks, 256, 0, s>>>(reinterpret_cast<uint32_t*>(ranges), 4 * num_tiles,
                                    reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + off), (int64_t)(len / 4));
     e = radix_sort<uint64_t>(P, nullptr, keys, vals, keys_tmp, vals_tmp, sorted_low_bits, hi, ws, s, false, true,
-                             digit_counts, true, ranges, num_tiles);
+                             digit_counts, true, ranges, num_tiles, ids_only);
   } else {
     e = launch_fill_u32(ranges, 4 * num_tiles, 0u, s);
   }

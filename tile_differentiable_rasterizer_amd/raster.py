@@ -23,7 +23,7 @@ TILE_DIGIT_COUNTS = 512  # GS_TILE_DIGIT_COUNTS
 ROW_BLOCK = 256  # GS_ROW_BLOCK
 ROWS_PER_BLOCK = 128  # GS_ROWS_PER_BLOCK
 
-EXPORTS = ("gs_project", "gs_workspace_bytes", "gs_bin_tiles", "gs_sort_keys", "gs_render_fwd",
+EXPORTS = ("gs_project", "gs_workspace_bytes", "gs_bin_tiles", "gs_sort_keys", "gs_sort_ids", "gs_render_fwd",
            "gs_render_bwd", "gs_densify", "gs_densify_workspace_bytes", "gs_adam_q16", "gs_quantize_sh",
            "gs_project_qsh", "gs_status_string")
 
@@ -78,6 +78,7 @@ def lib():
         L.gs_bin_tiles.argtypes = [i64, GsProjected, C.POINTER(GsCamera), vp, vp, i64, C.POINTER(i64), vp, vp, sz, vp]
         L.gs_sort_keys.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, C.POINTER(i32), vp, sz, vp]
         L.gs_sort_keys_noalloc.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, C.POINTER(i32), vp]
+        L.gs_sort_ids.argtypes = [i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, C.POINTER(i32), vp, sz, vp]
         L.gs_render_fwd.argtypes = [i64, GsProjected, vp, vp, vp, C.POINTER(GsCamera), C.POINTER(C.c_float), vp,
                                     vp, vp, vp]
         L.gs_render_bwd.argtypes = [i64, vp, vp, vp, vp, vp, i32, C.POINTER(GsCamera), GsProjected, vp, vp, vp,
@@ -89,7 +90,7 @@ def lib():
         L.gs_adam_q16.argtypes = [i64, vp, vp, vp, vp, C.POINTER(GsAdamParams), vp]
         L.gs_quantize_sh.argtypes = [i64, vp, i32, i32, vp, vp, vp]
         L.gs_project_qsh.argtypes = [i64, vp, vp, vp, vp, vp, vp, i32, i32, C.POINTER(GsCamera), GsProjected, vp]
-        for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_sort_keys_noalloc", "gs_render_fwd",
+        for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_sort_ids", "gs_sort_keys_noalloc", "gs_render_fwd",
                      "gs_render_bwd", "gs_densify",
                      "gs_adam_q16", "gs_quantize_sh", "gs_project_qsh"):
             getattr(L, name).restype = i32
@@ -228,6 +229,18 @@ def sort_keys(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, rang
     return bool(where.value == 1) if leave_in_tmp else False
 
 
+def sort_ids(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, ranges, workspace, order=None,
+             sorted_low_bits: int = 40, stream=None, digit_counts=None) -> bool:
+    """gs_sort_ids: sort_keys that leaves the sorted ids and the ranges but not the sorted keys
+    (the compositing calls read only those).  Returns True when the result is in
+    keys_tmp/vals_tmp."""
+    where = C.c_int32(-1)
+    _check(lib().gs_sort_ids(n_pairs, num_tiles, int(sorted_low_bits), _ptr(keys), _ptr(vals), _ptr(keys_tmp),
+                             _ptr(vals_tmp), _ptr(ranges), _ptr(order), _ptr(digit_counts), C.byref(where),
+                             _ptr(workspace), workspace.numel(), _stream(stream)), "gs_sort_ids")
+    return bool(where.value == 1)
+
+
 def sort_keys_noalloc(n_pairs: int, num_tiles: int, keys, vals, keys_tmp, vals_tmp, ranges, order=None,
                       sorted_low_bits: int = 40, stream=None, leave_in_tmp: bool = False, digit_counts=None):
     """gs_sort_keys_noalloc: sort_keys without a workspace (the library's fixed per-GPU
@@ -304,7 +317,9 @@ class Rasterizer:
         if self.workspace is None or self.workspace.numel() < need:
             self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
 
-    def forward(self, cam, bg=(0.0, 0.0, 0.0), stream=None) -> dict:
+    def forward(self, cam, bg=(0.0, 0.0, 0.0), stream=None, with_keys: bool = True) -> dict:
+        """One frame.  with_keys=False sorts with gs_sort_ids: the output's "keys" are then
+        unspecified (the compositing needs the sorted ids only)."""
         W, H = int(cam.width), int(cam.height)
         tiles = ((W + TILE - 1) // TILE) * ((H + TILE - 1) // TILE)
         self._ensure_pairs(self.capacity, tiles)
@@ -316,8 +331,12 @@ class Rasterizer:
             _check(st, "gs_bin_tiles")
         ranges = torch.empty((tiles, 2), dtype=torch.int64, device=self.device)
         order = torch.empty(tiles, dtype=torch.int32, device=self.device)
-        in_tmp = sort_keys(P, tiles, self.keys, self.vals, self.keys_tmp, self.vals_tmp, ranges, self.workspace,
-                           order, stream=stream, leave_in_tmp=True, digit_counts=self.digit_counts)
+        if with_keys:
+            in_tmp = sort_keys(P, tiles, self.keys, self.vals, self.keys_tmp, self.vals_tmp, ranges, self.workspace,
+                               order, stream=stream, leave_in_tmp=True, digit_counts=self.digit_counts)
+        else:
+            in_tmp = sort_ids(P, tiles, self.keys, self.vals, self.keys_tmp, self.vals_tmp, ranges, self.workspace,
+                              order, stream=stream, digit_counts=self.digit_counts)
         sk, sv = (self.keys_tmp, self.vals_tmp) if in_tmp else (self.keys, self.vals)
         image = torch.empty((3, H, W), dtype=torch.float32, device=self.device)
         final_T = torch.empty((H, W), dtype=torch.float32, device=self.device)
