@@ -29,16 +29,19 @@ HBM_PEAK_GBS = 8000.0
 VALU_PEAK_TOPS = 256 * 2.4e9 * 64 / 1e12   # non-packed fp32 lane-ops/s: 39.3 T
 TMIN = float(np.float32(1e-4))
 
-# Algorithmic VALU lane-operations of the plain per-pixel loops.
+# Algorithmic VALU lane-operations of the plain per-pixel loops, one issue slot per operation.
 # Forward, per (pixel, list entry) evaluation: offset (2), quadratic form (5), exp (counted
 # as 4 issue slots: the transcendental rate is a quarter), opacity product and clamp (2),
 # threshold test (1), weight (1), colour accumulate (3), transmittance update (2), stop
 # test (1).
 OPS_PER_EVAL_FWD = 21
-# Backward, per (pixel, contributor) of the reverse walk: the alpha re-evaluation (14),
-# transmittance recovery (reciprocal as 4 slots + 1), colour weights (4), d alpha (9),
-# colour-behind update (3), clamp test (1), the conic/mean/opacity terms (14) and the norm
-# of the mean gradient (sqrt as 4 slots + 1).
+# Backward, per (pixel, contributor) of the reverse walk with one scalar for the colour
+# behind: the alpha re-evaluation (offset 2, quadratic form 5, exponent scale 1 + exp 4,
+# opacity product and clamp 2 = 14), the skip and walk tests (2), transmittance recovery
+# (1 - alpha, reciprocal as 4 slots, product = 6), weight (1), dL.rgb (3), colour gradients
+# (3), d alpha (2) and its background term (2), colour-behind update (1), the alpha-clamp
+# compare and select (2), opacity gradient (1), dq (3), dq.dx and dq.dy (2), conic terms (3),
+# mean terms (4), norm of the mean gradient (product, fma, sqrt as 4 slots = 6).
 OPS_PER_EVAL_BWD = 55
 
 
@@ -65,8 +68,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the multi-GPU layout is a design "
-              "described in DESIGN.md and is not built.", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); this path is built and "
+              "measured for one GPU only; it does not run across GPUs.", file=sys.stderr)
         sys.exit(2)
     import torch
 

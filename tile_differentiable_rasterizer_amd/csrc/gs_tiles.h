@@ -93,15 +93,13 @@ __device__ __forceinline__ void tile_row_span(const TileEllipse& e, int ty, int 
 // emission): words 0-3 the kept runs of a rectangle of at most kSpanRows tile rows and
 // kSpanCols tile columns, two bytes per row (first kept column - tx0, count); then the
 // rectangle (tx0 | tx1 << 16, ty0 | ty1 << 16) and the tile count.  A larger rectangle
-// stores kNoSpans in words 0-3 and its runs are computed from the render record, row by
-// row with tile_row_span, where the emission needs them: the same test, so the same tiles.
+// stores kTableSpans and the index of its first row in the projection's row table (an
+// entry per row: first kept column | count << 16, kept tiles of the earlier rows), or,
+// when its block's region of the table is full, kNoSpans: the emission then computes its
+// rows from the render record with tile_row_span, the same test, so the same tiles.
 constexpr int kSpanRows = 8;
 constexpr int kSpanCols = 255;
 constexpr uint32_t kNoSpans = 0xFFFFFFFFu;
-// The emission's depth-ordered copy of a larger rectangle's record may instead point into
-// a row table the binning builds once per frame: words 0-1 = kTableSpans, the index of the
-// rectangle's first row.  A row entry is (first kept column | kept count << 16, kept tiles
-// of the rectangle's earlier rows).
 constexpr uint32_t kTableSpans = 0xFFFFFFFEu;
 
 __device__ __forceinline__ bool spans_fit(int tx0, int tx1, int ty0, int ty1) {
