@@ -4,11 +4,18 @@ One step = the whole hot path for the 8 orbit cameras of the 1M-Gaussian anisotr
 workload: per camera project -> bin (incl. the pair-count read-back) -> sort -> composite
 -> backward (compositing and projection, with densification statistics).  The upstream
 gradient is sign(render - target) for a uniform [0, 1] target, computed once before
-timing.  Inputs are resident in HBM before the timed region.  Also reported: the
-forward-only rate, per-stage times (HIP events on the launch stream), the roofline of the
-dominant kernel, and the float64 oracle timed on a bounded sample on the host cores.
+timing.  Inputs are resident in HBM before the timed region.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+The cameras of a step are independent, so they go round-robin over --streams HIP streams
+(default priority), each with its own projection, pair, workspace and gradient buffers:
+the latency-bound binning and sort of one camera run beside the compositing of another.
+The same loop on one stream is reported as well ("single_stream"); the per-kernel times
+and the roofline come from that loop, so they are the kernels' own, without another
+stream's work beside them.  Also reported: the forward-only rate, per-stage times (HIP
+events on the launch stream), and the float64 oracle timed on a bounded sample on the
+host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--streams S] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -54,6 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--streams", type=int, default=4, help="HIP streams the cameras of a step go round-robin over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to aim for")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration report")
@@ -61,7 +69,8 @@ def parse():
     ap.add_argument("--oracle-10m", action="store_true",
                     help="also time the oracle single-threaded on the 10M-Gaussian configuration (minutes)")
     ap.add_argument("--profile", action="store_true",
-                    help="profiler run: no CPU baseline, plus a 1 GiB device copy that calibrates HBM counters")
+                    help="profiler run: single-stream loops only (kernels timed alone), no CPU baseline, plus a "
+                         "1 GiB device copy that calibrates HBM counters")
     return ap.parse_args()
 
 
@@ -81,14 +90,20 @@ def main():
     sc, cams, _ = scenes.workload(WORKLOAD)
     N = sc.n
     means, scales, quats, opac, sh = raster.scene_to_device(sc, dev)
-    rz = raster.Rasterizer(means, scales, quats, opac, sh, sc.sh_degree)
+    NS = max(1, args.streams)
+    # one set of per-camera buffers per stream: projection, pairs, workspace (Rasterizer),
+    # gradients and densification statistics
+    rzs = [raster.Rasterizer(means, scales, quats, opac, sh, sc.sh_degree) for _ in range(NS)]
+    rz = rzs[0]
     stream = torch.cuda.current_stream()
+    streams = [stream] + [torch.cuda.Stream(device=dev) for _ in range(NS - 1)]  # default priority
 
     # warm-up pass per camera sizes the pair buffers and builds the upstream gradients
     log("sizing buffers")
-    dLs, frames0 = [], []
+    dLs = []
     for k, cam in enumerate(cams):
-        out = rz.forward(cam)
+        for r in rzs:
+            out = r.forward(cam)
         target = torch.from_numpy(scenes.target_image(5, cam.width, cam.height)).to(dev)
         dLs.append(torch.sign(out["image"] - target).contiguous())
     tiles = cams[0].num_tiles
@@ -98,22 +113,25 @@ def main():
     images = [torch.empty((3, H, W), dtype=torch.float32, device=dev) for _ in cams]
     finalT = [torch.empty((H, W), dtype=torch.float32, device=dev) for _ in cams]
     ncon = [torch.empty((H, W), dtype=torch.int32, device=dev) for _ in cams]
-    grads = raster.alloc_grads(N, sc.sh_degree, dev)
-    accum = torch.zeros((N, 2), dtype=torch.float32, device=dev)
-    denom = torch.zeros(N, dtype=torch.int32, device=dev)
+    grads = [raster.alloc_grads(N, sc.sh_degree, dev) for _ in range(NS)]
+    accums = [torch.zeros((N, 2), dtype=torch.float32, device=dev) for _ in range(NS)]
+    denoms = [torch.zeros(N, dtype=torch.int32, device=dev) for _ in range(NS)]
+    torch.cuda.synchronize()
     stages = ["project", "bin", "sort", "render_fwd", "render_bwd"]
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    def frame(k, cam, with_bwd, rec, staged):
+    def frame(k, cam, j, with_bwd, rec, staged):
+        # camera k on stream j with stream j's buffers (the caller makes streams[j] current);
         # staged: an event between the stages for the per-stage breakdown (each costs the
         # stream a few microseconds, so the throughput runs go without them)
+        rz = rzs[j]
         e = [ev() for _ in range(6)] if staged else None
 
         def mark(i):
             if staged:
-                e[i].record(stream)
+                e[i].record(streams[j])
 
         mark(0)
         raster.project(means, scales, quats, opac, sh, sc.sh_degree, cam, rz.proj)
@@ -129,24 +147,32 @@ def main():
         mark(4)
         if with_bwd:
             raster.render_bwd(means, scales, quats, opac, sh, sc.sh_degree, cam, rz.proj, sv, ranges[k],
-                              (0.0, 0.0, 0.0), finalT[k], ncon[k], dLs[k], grads, accum, denom, orders[k])
+                              (0.0, 0.0, 0.0), finalT[k], ncon[k], dLs[k], grads[j], accums[j], denoms[j],
+                              orders[k])
             mark(5)
         rec.append((e, with_bwd, P))
 
-    def run(steps, with_bwd, staged=False, kern=None):
+    def run(steps, with_bwd, ns=1, staged=False, kern=None):
+        """Times `steps` steps, camera k of a step on stream k mod ns.  With kern (single
+        stream only) the library brackets every launch of that kernel with HIP events on
+        its stream."""
         recs = []
-        # the library brackets every launch of one kernel with HIP events on its stream
-        kern = kern or ("k_render_bwd" if with_bwd else "k_render_fwd")
-        assert raster.kernel_timer_start(kern) == raster.GS_OK
+        assert kern is None or ns == 1
+        if kern:
+            assert raster.kernel_timer_start(kern) == raster.GS_OK
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(steps):
             for k, cam in enumerate(cams):
-                frame(k, cam, with_bwd, recs, staged)
+                j = k % ns
+                with torch.cuda.stream(streams[j]):
+                    frame(k, cam, j, with_bwd, recs, staged)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        st, launches, kms = raster.kernel_timer_stop()
-        assert st == raster.GS_OK and launches == len(recs), (st, launches)
+        launches, kms = 0, 0.0
+        if kern:
+            st, launches, kms = raster.kernel_timer_stop()
+            assert st == raster.GS_OK and launches == len(recs), (st, launches)
         times = {s: [] for s in stages}
         for e, wb, _ in recs:
             if e is None:
@@ -155,7 +181,8 @@ def main():
                 times[s].append(e[i].elapsed_time(e[i + 1]))
             if wb:
                 times["render_bwd"].append(e[4].elapsed_time(e[5]))
-        times[kern] = [kms / launches] if launches else []
+        if kern:
+            times[kern] = [kms / launches] if launches else []
         return t1 - t0, times, [p for _, _, p in recs]
 
     if args.profile:
@@ -166,14 +193,25 @@ def main():
         torch.cuda.synchronize()
         del a, b
         args.no_cpu_baseline = True
+    frames = args.steps * len(cams)
+    overlap = NS > 1 and not args.profile
     log("warm-up")
     run(args.warmup, True)
-    log(f"timed: {args.steps} steps x {len(cams)} cameras, forward + backward")
-    secs, times_t, pairs = run(args.steps, True)
-    frames = args.steps * len(cams)
+    if overlap:
+        run(args.warmup, True, NS)
+        log(f"timed: {args.steps} steps x {len(cams)} cameras, forward + backward, {NS} streams")
+        secs_o, _, _ = run(args.steps, True, NS)
+        log(f"timed: forward only, {NS} streams")
+        secs_fo, _, _ = run(args.steps, False, NS)
+    log(f"timed: {args.steps} steps x {len(cams)} cameras, forward + backward, one stream")
+    secs, times_t, pairs = run(args.steps, True, kern="k_render_bwd")
+    log("timed: forward only, one stream")
+    secs_f, times_f, _ = run(args.steps, False, kern="k_render_fwd")
+    single = {"frames_per_s": round(frames / secs, 2), "forward_only_frames_per_s": round(frames / secs_f, 2),
+              "ms_per_step": round(1e3 * secs / args.steps, 3)}
+    if overlap:
+        secs, secs_f = secs_o, secs_fo
     value = frames / secs
-    log("timed: forward only")
-    secs_f, times_f, _ = run(args.steps, False)
     fwd_fps = frames / secs_f
     log("timed: forward only, projection kernel")
     _, times_p, _ = run(max(1, args.steps // 2), False, kern="k_project")
@@ -218,6 +256,7 @@ def main():
                     traffic=traffic_bytes("k_render_bwd"))
 
     log("densify")
+    accum, denom = sum(accums), sum(denoms)  # every stream's cameras
     dens = densify_measure(raster, means, scales, quats, opac, sh, sc.sh_degree, accum, denom, stream,
                            with_oracle=not args.no_cpu_baseline)
 
@@ -233,7 +272,7 @@ def main():
 
     configs = None
     if not args.profile and not args.no_configs:
-        del rz, grads, accum, denom, images, finalT, ncon, ranges, orders, dLs
+        del rz, rzs, grads, accums, denoms, accum, denom, images, finalT, ncon, ranges, orders, dLs
         del means, scales, quats, opac, sh
         torch.cuda.empty_cache()
         configs = config_report(args, raster, scenes, dev, sc, cams)
@@ -253,11 +292,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "gaussians": N, "sh_degree": 3, "width": W, "height": H,
                    "cameras_per_step": len(cams), "step": "forward+backward per camera",
-                   "mean_pairs_per_frame": int(P_mean)},
+                   "streams": NS if overlap else 1, "mean_pairs_per_frame": int(P_mean)},
         "mpixels_per_s": round(value * W * H / 1e6, 1),
         "forward_only": {"frames_per_s": round(fwd_fps, 2), "mpixels_per_s": round(fwd_fps * W * H / 1e6, 1)},
+        "single_stream": single,
         "stages": stage_report,
-        "stages_timing": "separate forward+backward pass with an event between stages",
+        "stages_timing": "separate single-stream forward+backward pass with an event between stages",
+        "kernels_timing": "library kernel timer over the single-stream timed loops",
         "kernels": kernel_report,
         "evaluations_per_frame": int(evals),
         "contributor_walk_per_frame": int(walk),
