@@ -95,7 +95,10 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
     const int64_t* __restrict__ ranges,
     const int32_t* __restrict__ order, int W, int H, int tiles_x, float bg0, float bg1, float bg2,
     float* __restrict__ image, float* __restrict__ final_T, uint32_t* __restrict__ n_contrib) {
-  __shared__ float4 s_rec[kRenderWaves][kWave * 3];  // each wavefront's staged chunk
+  // each wavefront's staged chunk: the records that reach its quadrant, compacted, then one
+  // inert record, then room for the walk's read-ahead
+  constexpr int kSlots = kWave + 3;
+  __shared__ float4 s_rec[kRenderWaves][kSlots * 3];
   const int tile = tile_of(order, blockIdx.x);
   const int tx = tile % tiles_x, ty = tile / tiles_x;
   const int lane = __lane_id(), wave = threadIdx.x / kWave;
@@ -110,8 +113,9 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
 
   // Each wavefront walks the whole list on its own, 64 records at a time: lane l gathers
   // record c + l (the next chunk is prefetched into registers while this one is
-  // composited), tests it against the wavefront's quadrant and stages it in the
-  // wavefront's LDS slice.  No workgroup barrier: a wavefront never waits for the others.
+  // composited) and tests it against the wavefront's quadrant; the records that reach it
+  // are staged in list order in consecutive slots of the wavefront's LDS slice, each with
+  // its list position.  No workgroup barrier: a wavefront never waits for the others.
   float4 p0 = make_float4(0.f, 0.f, 0.f, 0.f), p1 = p0, p2 = p0;
   if (start + lane < end) {
     const uint32_t id = min(vals[start + lane], id_max);
@@ -120,67 +124,65 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
   // ids run one chunk ahead of the records, so a chunk's record gathers wait on one
   // memory round trip instead of two
   uint32_t nid = start + kWave + lane < end ? vals[start + kWave + lane] : 0u;  // clamped where used
-  // the alpha a record must reach to be taken: 1/255 while the pixel is live, +inf once it
-  // is done (outside the image, or T < 1e-4), so that a done pixel takes nothing
-  float thr = inside ? kAlphaMin : INFINITY;
   for (int64_t b = start; b < end; b += kWave) {
-    if (!__ballot(thr != INFINITY)) break;  // this wavefront's pixels are all done
+    if (!__ballot(inside && T >= kTMin)) break;  // this wavefront's pixels are all done
     float4 s0, s1;
     stage_transform(p0, p1, s0, s1);
     const bool reach =
         b + lane < end && quadrant_reach(s0, s1, __float_as_uint(p2.y), __float_as_uint(p2.z), qx0, qy0);
+    const uint64_t m = __ballot(reach);
+    const uint32_t cnt = (uint32_t)__popcll(m);
+    const uint32_t slot = (uint32_t)__popcll(m & lanemask_lt());
     // the previous chunk's reads are done before these writes, which are done before the
     // reads below (LDS operations of one wavefront stay in order once issued)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    my[3 * lane] = s0; my[3 * lane + 1] = s1; my[3 * lane + 2] = p2;
+    if (reach) {
+      my[3 * slot] = s0;
+      my[3 * slot + 1] = s1;
+      // colour b, and the list position + 1 of the record (what n_contrib counts)
+      my[3 * slot + 2] = make_float4(p2.x, __uint_as_float((uint32_t)(b - start) + 1u + (uint32_t)lane), 0.f, 0.f);
+    }
+    if (lane == 0) {  // an inert record after the last (opacity 0: alpha 0, never taken)
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      my[3 * cnt] = z; my[3 * cnt + 1] = z; my[3 * cnt + 2] = z;
+    }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    uint64_t m = __ballot(reach);
     if (b + kWave + lane < end) {  // prefetch the next chunk
       const uint32_t id = min(nid, id_max);
       p0 = rec[3 * (size_t)id]; p1 = rec[3 * (size_t)id + 1]; p2 = rec[3 * (size_t)id + 2];
     }
     nid = b + 2 * kWave + lane < end ? vals[b + 2 * kWave + lane] : 0u;
-    if (!m) continue;
-    const uint32_t kb = (uint32_t)(b - start) + 1u;  // list position + 1 of staged record 0
-    // one record's contribution; a record this lane does not take gets alpha 0, which
-    // leaves T and the colour exactly as they were; one compare decides the take and nc
-    auto blend = [&](const float4 a, const float4 e1, float bb, uint32_t pos) {
+    if (!cnt) continue;
+    // one record's contribution: the pixel takes it when it is inside the image, not done
+    // (T >= 1e-4) and alpha >= 1/255; a record it does not take gets alpha 0, which leaves
+    // T and the colour exactly as they were
+    auto blend = [&](const float4 a, const float4 e1, const float2 e2) {
       const float dx = fx - a.x, dy = fy - a.y;
       const float alpha = fminf(kAlphaMax, e1.y * gauss_factor(gauss_exponent(a.z, a.w, e1.x, dx, dy)));
-      const bool take = alpha >= thr;
+      const bool take = alpha >= kAlphaMin && T >= kTMin && inside;
       const float at = take ? alpha : 0.0f;
       const float w = at * T;
       cr = fmaf(e1.z, w, cr);
       cg = fmaf(e1.w, w, cg);
-      cb = fmaf(bb, w, cb);
+      cb = fmaf(e2.x, w, cb);
       T = T * (1.0f - at);
-      nc = take ? pos : nc;
-      thr = T < kTMin ? INFINITY : thr;
+      nc = take ? __float_as_uint(e2.y) : nc;
     };
-    // two records per iteration in alternating registers: each one's LDS reads are
-    // issued while the previous one is evaluated
-    int j = __builtin_ctzll(m);
-    m &= m - 1;
-    float4 a0 = my[3 * j], b0 = my[3 * j + 1];
-    float c0 = my[3 * j + 2].x;
-    while (true) {
-      const bool more1 = m != 0;
-      const int j1 = more1 ? __builtin_ctzll(m) : j;
-      m &= m - 1;
-      const float4 a1 = my[3 * j1], b1 = my[3 * j1 + 1];
-      const float c1 = my[3 * j1 + 2].x;
-      blend(a0, b0, c0, kb + (uint32_t)j);
-      if (!more1) break;
-      const bool more2 = m != 0;
-      j = more2 ? __builtin_ctzll(m) : j1;
-      m &= m - 1;
-      a0 = my[3 * j];
-      b0 = my[3 * j + 1];
-      c0 = my[3 * j + 2].x;
-      blend(a1, b1, c1, kb + (uint32_t)j1);
-      if (!more2) break;
+    // two records per step (an odd count ends on the inert record); the next step's
+    // records are read while this step's are evaluated (the read-ahead past the inert
+    // record stays inside the slice and is never used)
+    auto third = [](const float4* r) { return *reinterpret_cast<const float2*>(r); };  // (b, position)
+    float4 a0 = my[0], b0 = my[1], a1 = my[3], b1 = my[4];
+    float2 c0 = third(my + 2), c1 = third(my + 5);
+    for (uint32_t i = 0; i < cnt; i += 2) {
+      const float4* nx = my + 3 * (i + 2);
+      const float4 na0 = nx[0], nb0 = nx[1], na1 = nx[3], nb1 = nx[4];
+      const float2 nc0 = third(nx + 2), nc1 = third(nx + 5);
+      blend(a0, b0, c0);
+      blend(a1, b1, c1);
+      a0 = na0; b0 = nb0; c0 = nc0; a1 = na1; b1 = nb1; c1 = nc1;
     }
   }
   if (inside) {
