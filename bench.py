@@ -255,6 +255,9 @@ def main():
     roof_dom = dict(kernel_report["k_render_bwd"], kernel="k_render_bwd", launches_timed=frames,
                     traffic=traffic_bytes("k_render_bwd"))
 
+    log("memory ceilings")
+    ceil = ceilings(raster, rzs[0], means, scales, quats, opac, sh, sc.sh_degree, cams[0], tiles, dev)
+
     log("densify")
     accum, denom = sum(accums), sum(denoms)  # every stream's cameras
     dens = densify_measure(raster, means, scales, quats, opac, sh, sc.sh_degree, accum, denom, stream,
@@ -303,6 +306,7 @@ def main():
         "evaluations_per_frame": int(evals),
         "contributor_walk_per_frame": int(walk),
         "roofline": roof_dom,
+        "ceilings": ceil,
         "cpu_baseline": cpu,
         "densify": dens,
         "adam": adam,
@@ -586,6 +590,80 @@ def traffic_bytes(kernel):
     if not t or t["source_digest"] != kernel_source_digest():
         return None
     return t["bytes"]
+
+
+def ceilings(raster, rz, means, scales, quats, opac, sh, L, cam, tiles, dev, reps=20):
+    """The projection kernel and the pair sort's digit pass beside kernels that perform only
+    their loads and stores in their layouts (gs_measure.h), on the first camera."""
+    import torch
+
+    def per_launch_ms(f):
+        f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            f()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    N = means.shape[0]
+    K = (L + 1) ** 2
+    proj_io = raster.alloc_projected(N, dev)
+    t_k1 = per_launch_ms(lambda: raster.project(means, scales, quats, opac, sh, L, cam, rz.proj))
+    t_k1io = per_launch_ms(lambda: raster.measure_project_io(means, scales, quats, opac, sh, L, proj_io))
+    k1_bytes = N * (44 + 12 * K + 97)  # the loads and stores both kernels make (as in stage_work)
+    del proj_io
+
+    # the pairs of the camera as the binning leaves them, and every pair's sorted position
+    raster.project(means, scales, quats, opac, sh, L, cam, rz.proj)
+    st, P = raster.bin_tiles(rz.proj, cam, rz.keys, rz.vals, rz.workspace, digit_counts=rz.digit_counts)
+    assert st == raster.GS_OK
+    keys0, vals0, dc = rz.keys[:P].clone(), rz.vals[:P].clone(), rz.digit_counts.clone()
+    ranges = torch.empty((tiles, 2), dtype=torch.int64, device=dev)
+    k, v = keys0.clone(), torch.arange(P, dtype=torch.int32, device=dev)
+    kt, vt = torch.empty_like(k), torch.empty_like(v)
+    in_tmp = raster.sort_keys(P, tiles, k, v, kt, vt, ranges, rz.workspace, leave_in_tmp=True, digit_counts=dc)
+    perm = (vt if in_tmp else v).long()
+    dest = torch.empty(P, dtype=torch.int32, device=dev)
+    dest[perm] = torch.arange(P, dtype=torch.int32, device=dev)
+    # the order in which a digit pass writes: its partitions of 4096 pairs, each grouped by
+    # the pass's digit (the tile bits above the low byte), stably
+    order = torch.argsort((torch.arange(P, device=dev) // 4096) * 256 + ((keys0 >> 40) & 255), stable=True)
+    kr, vr, dr = keys0[order].contiguous(), vals0[order].contiguous(), dest[order].contiguous()
+    del k, v, kt, vt, perm, order, dest
+    out = torch.empty(P, dtype=torch.int32, device=dev)
+    t_sio = per_launch_ms(lambda: raster.measure_scatter_io(kr, vr, dr, out))
+    # the pass itself, as the frames run it (gs_sort_ids with the binning's digit counts)
+    assert raster.kernel_timer_start("k_onesweep_u64") == raster.GS_OK
+    for _ in range(reps):
+        rz.keys[:P].copy_(keys0)
+        rz.vals[:P].copy_(vals0)
+        raster.sort_ids(P, tiles, rz.keys, rz.vals, rz.keys_tmp, rz.vals_tmp, ranges, rz.workspace, None,
+                        digit_counts=dc)
+    st, launches, ms = raster.kernel_timer_stop()
+    assert st == raster.GS_OK and launches > 0
+    passes = launches / reps
+    t_pass = ms / launches
+    del kr, vr, dr, out, keys0, vals0
+
+    def entry(kernel_ms, io_ms, kernel_bytes, io_bytes):
+        return {"kernel_ms": round(kernel_ms, 4), "io_ms": round(io_ms, 4),
+                "kernel_gbs": round(kernel_bytes / (kernel_ms * 1e-3) / 1e9, 1),
+                "io_gbs": round(io_bytes / (io_ms * 1e-3) / 1e9, 1),
+                "kernel_frac_of_hbm_peak": round(kernel_bytes / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "io_frac_of_hbm_peak": round(io_bytes / (io_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "kernel_time_over_io_time": round(kernel_ms / io_ms, 3)}
+
+    return {
+        "what": "each kernel beside a kernel with only its loads and stores in the same layout "
+                "(gs_measure_project_io / gs_measure_scatter_io), first camera, back-to-back launches",
+        "k_project": dict(entry(t_k1, t_k1io, k1_bytes, k1_bytes), bytes=k1_bytes),
+        "k_onesweep_u64": dict(entry(t_pass, t_sio, 16 * P, 20 * P), pairs=P, passes_per_sort=passes,
+                               note="the ids-only pass reads key and id and writes the id (16 B per pair); "
+                                    "the ceiling kernel also reads the destination (20 B per pair)"),
+    }
 
 
 def densify_measure(raster, means, scales, quats, opac, sh, L, accum, denom, stream, with_oracle, reps=5):

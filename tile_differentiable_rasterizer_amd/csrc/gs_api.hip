@@ -32,6 +32,10 @@ hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* v
                        const uint64_t* digit_counts, int32_t* result_in_tmp, void* ws, hipStream_t s,
                        bool ids_only);
 hipError_t launch_fill_u32(void* p, int64_t count, uint32_t v, hipStream_t s);
+hipError_t launch_project_io(int64_t n, const float* means, const float* scales, const float* quats,
+                             const float* opac, const float* sh, int L, const gs_projected& out, hipStream_t s);
+hipError_t launch_scatter_io(int64_t n, const uint64_t* keys, const uint32_t* vals, const uint32_t* dest,
+                             uint32_t* out, hipStream_t s);
 size_t densify_workspace_bytes(int64_t n);
 hipError_t launch_quantize_sh(int64_t U, const float* sh, int bits, void* codes, float* bounds, hipStream_t s);
 hipError_t launch_project_qsh(int64_t n, const float* means, const float* scales, const float* quats,
@@ -90,7 +94,7 @@ gs_status hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP
 // Kernel timer: while armed for one kernel, every launch of that kernel is bracketed by
 // two HIP events recorded on its launch stream.  The events are created on first use and
 // kept for the life of the process (they are reused by later arming).
-enum TimedKernel { kNone = 0, kProject, kRenderFwd, kRenderBwd, kProjectBwd, kDensifyEmit, kAdamQ16 };
+enum TimedKernel { kNone = 0, kProject, kRenderFwd, kRenderBwd, kProjectBwd, kDensifyEmit, kAdamQ16, kSortPass };
 
 struct KernelTimer {
   std::mutex mu;
@@ -114,6 +118,7 @@ TimedKernel timed_kernel_id(const char* name) {
   if (!strcmp(name, "k_project_bwd")) return kProjectBwd;
   if (!strcmp(name, "k_densify_emit")) return kDensifyEmit;
   if (!strcmp(name, "k_adam_q16")) return kAdamQ16;
+  if (!strcmp(name, "k_onesweep_u64")) return kSortPass;
   return kNone;
 }
 
@@ -143,6 +148,10 @@ hipError_t timed(TimedKernel k, hipStream_t s, F&& f) {
 }
 
 }  // namespace
+
+namespace gs {
+void mark_sort_pass(hipStream_t s) { timer_mark(kSortPass, s); }
+}  // namespace gs
 
 extern "C" {
 
@@ -453,6 +462,26 @@ gs_status gs_render_bwd(int64_t n, const float* means, const float* scales, cons
                                 s);
     });
   return hip_status(e);
+}
+
+gs_status gs_measure_project_io(int64_t n, const float* means, const float* scales, const float* quats,
+                                const float* opacities, const float* sh, int32_t sh_degree, gs_projected out,
+                                void* stream) {
+  if (n < 0 || sh_degree < 0 || sh_degree > 3) return GS_ERR_INVALID_ARG;
+  if (n >= kMaxGaussians) return GS_ERR_OVERFLOW;
+  if (n == 0) return GS_OK;
+  if (!means || !scales || !quats || !opacities || !sh || !projected_ok(out)) return GS_ERR_INVALID_ARG;
+  return hip_status(
+      launch_project_io(n, means, scales, quats, opacities, sh, sh_degree, out, static_cast<hipStream_t>(stream)));
+}
+
+gs_status gs_measure_scatter_io(int64_t n, const uint64_t* keys, const uint32_t* vals, const uint32_t* dest,
+                                uint32_t* out, void* stream) {
+  if (n < 0) return GS_ERR_INVALID_ARG;
+  if (n > (int64_t)UINT32_MAX) return GS_ERR_OVERFLOW;
+  if (n == 0) return GS_OK;
+  if (!keys || !vals || !dest || !out) return GS_ERR_INVALID_ARG;
+  return hip_status(launch_scatter_io(n, keys, vals, dest, out, static_cast<hipStream_t>(stream)));
 }
 
 gs_status gs_kernel_timer_start(const char* kernel) {

@@ -564,3 +564,64 @@ hipError_t launch_project_bwd(int64_t n, const float* means, const float* scales
 }
 
 }  // namespace gs
+
+namespace gs {
+
+// Measurement only (gs_measure_project_io): the projection's loads and stores, with the
+// same widths, strides and grid, and none of its arithmetic.  Its time bounds what any
+// projection with these input and output layouts can take.  The outputs hold no valid
+// projection: each value is a sum or a copy of inputs, so that every load is used.
+template <int L>
+__global__ __launch_bounds__(kProjBlock) void k_project_io(
+    int64_t n, const float* __restrict__ means, const float* __restrict__ scales, const float4* __restrict__ quats,
+    const float* __restrict__ opac, const float* __restrict__ sh, float4* __restrict__ rec,
+    float* __restrict__ depth_out, ushort4* __restrict__ rect_out, uint32_t* __restrict__ ntiles_out,
+    uint8_t* __restrict__ clamp_out, uint4* __restrict__ runs_out, uint2* __restrict__ rows_out) {
+  using S = ShLayout<L>;
+  const int64_t base = (int64_t)blockIdx.x * kProjBlock;
+  const int cnt = (int)min((int64_t)kProjBlock, n - base);
+  const int tid = threadIdx.x;
+  if (tid >= cnt) return;
+  const int64_t i = base + tid;
+  const float mx = means[3 * i], my = means[3 * i + 1], mz = means[3 * i + 2];
+  const float sx = scales[3 * i], sy = scales[3 * i + 1], sz = scales[3 * i + 2];
+  const float4 q = quats[i];
+  const float o = opac[i];
+  float coef[S::ROW];
+  load_row<L>(sh + i * S::ROW, coef);
+  float acc = 0.0f;
+#pragma unroll
+  for (int c = 0; c < S::ROW; ++c) acc += coef[c];
+  depth_out[i] = mz;
+  clamp_out[i] = (uint8_t)(acc > 0.0f);
+  rec[3 * i] = make_float4(mx, my, sx + sy, sz);
+  rec[3 * i + 1] = make_float4(q.x + q.y, o, acc, q.z);
+  rec[3 * i + 2] = make_float4(q.w, mx + mz, my + mz, 0.0f);
+  const uint32_t h = __float_as_uint(acc);
+  rect_out[i] = make_ushort4((uint16_t)h, (uint16_t)(h >> 16), (uint16_t)__float_as_uint(o), (uint16_t)__float_as_uint(mz));
+  ntiles_out[i] = h & 7u;
+  runs_out[2 * i] = make_uint4(h, __float_as_uint(mx), __float_as_uint(my), __float_as_uint(sx));
+  runs_out[2 * i + 1] = make_uint4(__float_as_uint(sy), __float_as_uint(sz), h & 7u, 0u);
+  if (__lane_id() == 0)  // the wavefront region's overflow entry, as the projection writes it
+    rows_out[(size_t)(blockIdx.x * (kProjBlock / kWave) + tid / kWave) * kRegionRows + kWaveRows] = make_uint2(0u, 0u);
+}
+
+hipError_t launch_project_io(int64_t n, const float* means, const float* scales, const float* quats,
+                             const float* opac, const float* sh, int L, const gs_projected& out, hipStream_t s) {
+  const unsigned blocks = (unsigned)((n + kProjBlock - 1) / kProjBlock);
+  auto go = [&](auto kernel) {
+    kernel<<<blocks, kProjBlock, 0, s>>>(n, means, scales, reinterpret_cast<const float4*>(quats), opac, sh,
+                                         reinterpret_cast<float4*>(out.rec), out.depth,
+                                         reinterpret_cast<ushort4*>(out.rect), out.n_tiles, out.clamp,
+                                         reinterpret_cast<uint4*>(out.runs), reinterpret_cast<uint2*>(out.rows));
+    return hipGetLastError();
+  };
+  switch (L) {
+    case 0: return go(k_project_io<0>);
+    case 1: return go(k_project_io<1>);
+    case 2: return go(k_project_io<2>);
+    default: return go(k_project_io<3>);
+  }
+}
+
+}  // namespace gs

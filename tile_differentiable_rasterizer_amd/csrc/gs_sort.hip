@@ -35,6 +35,10 @@
 
 namespace gs {
 
+// Records the kernel timer's event for a digit pass of a 64-bit key sort when the timer is
+// armed for those passes (defined with the timer, in the API).
+void mark_sort_pass(hipStream_t s);
+
 constexpr int kHistThreads = 1024;                  // histogram workgroup: 16 wavefronts
 constexpr int kSortKPT = 4;                         // keys per thread of the histogram
 constexpr int kSortPart = kHistThreads * kSortKPT;  // keys per histogram round
@@ -543,11 +547,13 @@ static hipError_t radix_sort(int64_t P, const uint64_t* dcount, K* keys, uint32_
     k_sort_plan<<<1, kRadix, 0, s>>>(digit_counts ? digit_counts : hist, digit_counts ? 1 : kHistCopies, dbase, plan,
                                      passes, P, dcount, keep_all ? 1 : 0);
   for (int p = 0; p < passes; ++p) {
+    if constexpr (sizeof(K) == 8) mark_sort_pass(s);  // the kernel timer's events, when armed for it
     k_onesweep<K><<<(unsigned)((P + Onesweep<K>::part - 1) / Onesweep<K>::part), Onesweep<K>::threads, 0, s>>>(
         keys, vals, keys_tmp, vals_tmp, P, dcount, p, lo + 8 * p, pbits[p], plan, planless ? p % 2 : -1,
         dbase + p * kRadix, planless ? digit_counts + p * kRadix : nullptr, 1,
         planless && p == passes - 1 ? plan + kMaxPasses : nullptr, status + poff[p], tickets,
         p == passes - 1 ? tile_ranges : nullptr, num_tiles, ids_only && p == passes - 1 ? 0 : 1);
+    if constexpr (sizeof(K) == 8) mark_sort_pass(s);
   }
   if (copy_back) {
     const int64_t want = (P + 255) / 256;
@@ -633,6 +639,40 @@ hipError_t launch_sort(int64_t P, int64_t num_tiles, uint64_t* keys, uint32_t* v
                                                            move ? vals : nullptr, P, num_tiles, ranges);
   if (order || recorded) k_tile_order<<<1, 1024, 0, s>>>(ranges, num_tiles, recorded ? 1 : 0, order);
   if (result_in_tmp) *result_in_tmp = in_tmp ? 1 : 0;
+  return hipGetLastError();
+}
+
+}  // namespace gs
+
+namespace gs {
+
+// Measurement only (gs_measure_scatter_io): lane i reads key i, id i and destination i,
+// four per lane in 1024-element workgroups as a digit pass reads its partition, and
+// writes the id (plus the key's low word, so that the key's load is used) to
+// out[dest[i]].  Given the elements in the order a pass writes them, its time bounds what
+// a pass with that read and write pattern can take.  Destinations outside [0, n) are
+// skipped.
+__global__ __launch_bounds__(256) void k_scatter_io(int64_t n, const uint64_t* __restrict__ keys,
+                                                     const uint32_t* __restrict__ vals,
+                                                     const uint32_t* __restrict__ dest, uint32_t* __restrict__ out) {
+  const int64_t base = (int64_t)blockIdx.x * 1024;
+  uint64_t k[4];
+  uint32_t v[4], d[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t i = base + j * 256 + threadIdx.x;
+    k[j] = i < n ? keys[i] : 0ull;
+    v[j] = i < n ? vals[i] : 0u;
+    d[j] = i < n ? dest[i] : ~0u;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if ((int64_t)d[j] < n) out[d[j]] = v[j] + (uint32_t)k[j];
+}
+
+hipError_t launch_scatter_io(int64_t n, const uint64_t* keys, const uint32_t* vals, const uint32_t* dest,
+                             uint32_t* out, hipStream_t s) {
+  k_scatter_io<<<(unsigned)((n + 1023) / 1024), 256, 0, s>>>(n, keys, vals, dest, out);
   return hipGetLastError();
 }
 

@@ -100,13 +100,18 @@ def lib():
         L.gs_kernel_timer_start.restype = i32
         L.gs_kernel_timer_stop.argtypes = [C.POINTER(i64), C.POINTER(C.c_double)]
         L.gs_kernel_timer_stop.restype = i32
+        L.gs_measure_project_io.argtypes = [i64, vp, vp, vp, vp, vp, i32, GsProjected, vp]
+        L.gs_measure_project_io.restype = i32
+        L.gs_measure_scatter_io.argtypes = [i64, vp, vp, vp, vp, vp]
+        L.gs_measure_scatter_io.restype = i32
         _lib = L
     return _lib
 
 
 def kernel_timer_start(kernel):
     """Arm the library's event timer for one kernel ("k_project", "k_render_fwd",
-    "k_render_bwd", "k_project_bwd"); returns the status code."""
+    "k_render_bwd", "k_project_bwd", "k_densify_emit", "k_adam_q16", "k_onesweep_u64");
+    returns the status code."""
     return lib().gs_kernel_timer_start(kernel.encode())
 
 
@@ -115,6 +120,20 @@ def kernel_timer_stop():
     n, ms = C.c_int64(0), C.c_double(0.0)
     st = lib().gs_kernel_timer_stop(C.byref(n), C.byref(ms))
     return st, n.value, ms.value
+
+
+def measure_project_io(means, scales, quats, opacities, sh, sh_degree: int, out: dict, stream=None):
+    """gs_measure_project_io: the projection's loads and stores only (a memory ceiling);
+    overwrites `out` with unspecified values."""
+    _check(lib().gs_measure_project_io(means.shape[0], _ptr(means), _ptr(scales), _ptr(quats), _ptr(opacities),
+                                       _ptr(sh), int(sh_degree), projected_struct(out), _stream(stream)),
+           "gs_measure_project_io")
+
+
+def measure_scatter_io(keys, vals, dest, out, stream=None):
+    """gs_measure_scatter_io: out[dest[i]] = vals[i] + low word of keys[i] (a memory ceiling)."""
+    _check(lib().gs_measure_scatter_io(keys.shape[0], _ptr(keys), _ptr(vals), _ptr(dest), _ptr(out),
+                                       _stream(stream)), "gs_measure_scatter_io")
 
 
 def _ptr(t):
