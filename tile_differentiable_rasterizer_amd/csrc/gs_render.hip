@@ -349,18 +349,16 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
         ks[r] = has ? bit : INT32_MAX;
         if (has) m &= ~(1ull << bit);
       }
-      float v[32];
+      float v[30];
       uint64_t hm[3];
       uint32_t ids[3];
 #pragma unroll
       for (int r = 0; r < 3; ++r) hm[r] = bwd_record(my, js[r], ks[r], p, v + GS_GRAD_SCREEN * r, ids[r]);
-      v[30] = 0.0f;
-      v[31] = 0.0f;
       const uint64_t h0 = hm[0], h1 = hm[1], h2 = hm[2];
       if (h0 | h1 | h2) {
         // lanes 2i and 2i + 1 now hold the wavefront's sum of v[i]; the even lane of each
         // (record, term) pair of a record some pixel took adds it to the Gaussian's gradient
-        const float sum = wave_transpose_reduce32(v);
+        const float sum = wave_transpose_reduce30(v);
         const uint64_t act = (h0 ? kRedLanes0 : 0ull) | (h1 ? kRedLanes1 : 0ull) | (h2 ? kRedLanes2 : 0ull);
         const uint32_t id = red_r == 0 ? ids[0] : red_r == 1 ? ids[1] : ids[2];
         if ((act >> lane) & 1ull) atomicAdd(gscreen + (size_t)GS_GRAD_SCREEN * id + red_e, sum * red_scale);
