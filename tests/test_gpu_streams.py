@@ -9,7 +9,6 @@ atomic additions (relative to each array's largest magnitude, 1e-4, well above t
 that two single-stream runs differ by and far below any wrong term); visit counts exactly.
 This is how the benchmark overlaps the cameras of a step.
 """
-import numpy as np
 import pytest
 import torch
 
@@ -82,3 +81,43 @@ def test_cameras_on_several_streams_match_one_stream(n_streams):
     rel = ((acc - acc0.double()).abs().max() / acc0.double().abs().max()).item()
     assert rel <= 1e-4, f"statistics differ by {rel:.3g}"
     say(f"streams={n_streams}: {len(cams)} cameras equal the one-stream run (statistics {rel:.2g})")
+
+
+def test_bench_workload_on_four_streams():
+    """The benchmark's own arrangement: cameras of the 1M-Gaussian 1080p workload on the
+    current stream and three new ones, each with its own buffers, against the same cameras
+    on one stream."""
+    sc, cams, _ = scenes.workload("aniso_1m_sh3_1080p_8cam")
+    cams = cams[:4]
+    dev = torch.device("cuda")
+    means, scales, quats, opac, sh = raster.scene_to_device(sc, dev)
+    rz0 = raster.Rasterizer(means, scales, quats, opac, sh, sc.sh_degree)
+    ref, dLs = [], []
+    for k, cam in enumerate(cams):
+        fwd, _ = _frame(rz0, cam, None, None, None)
+        target = torch.from_numpy(scenes.target_image(5, cam.width, cam.height)).to(dev)
+        dL = torch.sign(fwd["image"] - target).contiguous()
+        dLs.append(dL)
+        g = rz0.backward(fwd, dL)
+        ref.append((fwd["image"].clone(), fwd["final_T"].clone(), fwd["n_contrib"].clone(),
+                    {key: g[key].clone() for key in GRAD_KEYS}))
+    torch.cuda.synchronize()
+    del rz0
+    rzs = [raster.Rasterizer(means, scales, quats, opac, sh, sc.sh_degree) for _ in cams]
+    for r, cam in zip(rzs, cams):
+        r.forward(cam, with_keys=False)  # sizes the pair buffers
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream(device=dev) for _ in range(len(cams) - 1)]
+    torch.cuda.synchronize()
+    out = []
+    for k, cam in enumerate(cams):
+        with torch.cuda.stream(streams[k]):
+            out.append(_frame(rzs[k], cam, dLs[k], None, None))
+    torch.cuda.synchronize()
+    for k, ((fwd, g), (img, T, nc, gref)) in enumerate(zip(out, ref)):
+        assert torch.equal(fwd["image"], img) and torch.equal(fwd["final_T"], T), f"camera {k}"
+        assert torch.equal(fwd["n_contrib"], nc), f"camera {k}: n_contrib"
+        for key in GRAD_KEYS:
+            a, b = g[key].double(), gref[key].double()
+            rel = ((a - b).abs().max() / b.abs().max().clamp_min(1e-30)).item()
+            assert rel <= 1e-4, f"camera {k}: {key} differs by {rel:.3g} of its largest magnitude"
+    say(f"bench workload: {len(cams)} cameras on {len(streams)} streams equal the one-stream run")
