@@ -357,11 +357,18 @@ struct EmitPart {
   int ng;        // its Gaussians: g0 .. g0 + ng - 1
 };
 
+// Gaussians of a partition whose tile records the scattering pass stages in LDS (the
+// partitions of the bench workload hold 104 on average, 209 at most); the records of any
+// further ones are read from memory.
+constexpr int kStagedRecs = 224;
+
 // Stages s_rel[i] = goff[g0 + i] - base for i in [0, ng] (the last one is the end of the
-// partition's last Gaussian).  Call from every thread; the caller synchronises.
+// partition's last Gaussian) and, with s_runs, the tile records of its first kStagedRecs
+// Gaussians (two uint4 each).  Call from every thread; the caller synchronises.
 __device__ __forceinline__ EmitPart stage_partition(int64_t b, int64_t nparts, int64_t v, int64_t P,
                                                     const uint64_t* __restrict__ goff,
-                                                    const uint32_t* __restrict__ gstart, int32_t* s_rel) {
+                                                    const uint32_t* __restrict__ gstart, int32_t* s_rel,
+                                                    const uint4* __restrict__ sruns, uint4* s_runs) {
   EmitPart e;
   e.base = b * kEmitPart;
   e.n = (int)min((int64_t)kEmitPart, P - e.base);
@@ -369,6 +376,10 @@ __device__ __forceinline__ EmitPart stage_partition(int64_t b, int64_t nparts, i
   const uint32_t g1 = b + 1 < nparts ? gstart[b + 1] : (uint32_t)(v - 1);
   e.ng = (int)(g1 - e.g0) + 1;
   for (int i = threadIdx.x; i <= e.ng; i += kBinBlock) s_rel[i] = (int32_t)((int64_t)goff[e.g0 + i] - e.base);
+  if (s_runs) {
+    const int staged = min(e.ng, kStagedRecs);
+    for (int i = threadIdx.x; i < 2 * staged; i += kBinBlock) s_runs[i] = sruns[2 * (size_t)e.g0 + i];
+  }
   return e;
 }
 
@@ -392,14 +403,14 @@ __device__ __forceinline__ int table_find(const uint2* __restrict__ t, int rows,
 // Generates this lane's pairs; emit(k, tile, id, dbits) receives the pair's slot in the
 // lane's run (0 .. kEmitPer - 1), its tile, its Gaussian's id and the bit pattern of that
 // Gaussian's depth.  sruns holds the depth-sorted Gaussians' tile records (words 6 and 7:
-// id and depth bits).  A Gaussian's pairs are the tiles its ellipse test keeps, rows outer
-// and columns inner: read from the runs the projection stored, or, for a rectangle too
-// large for the record, computed row by row from its render record (rec, by id).  Every
-// loop stays inside the rectangle.
+// id and depth bits), s_runs the partition's first kStagedRecs of them.  A Gaussian's pairs
+// are the tiles its ellipse test keeps, rows outer and columns inner: read from the runs
+// the projection stored, or, for a rectangle too large for the record, computed row by row
+// from its render record (rec, by id).  Every loop stays inside the rectangle.
 template <bool kLarge, typename F>
 __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_rel, const uint4* __restrict__ sruns,
-                                           const uint2* __restrict__ table, const float4* __restrict__ rec,
-                                           int tiles_x, F&& emit) {
+                                           const uint4* s_runs, const uint2* __restrict__ table,
+                                           const float4* __restrict__ rec, int tiles_x, F&& emit) {
   const int p0 = (int)threadIdx.x * kEmitPer;
   if (p0 >= e.n) return;
   int lo = 0, hi = e.ng;  // invariant: s_rel[lo] <= p0 < s_rel[hi]
@@ -430,9 +441,10 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
       row();
     }
   };
-  auto start = [&](uint32_t g) {  // the Gaussian's first kept tile
-    sp = sruns[2 * (size_t)g];
-    const uint4 b = sruns[2 * (size_t)g + 1];
+  auto start = [&](int li) {  // the first kept tile of the partition's Gaussian li
+    const uint4* src = li < kStagedRecs ? s_runs + 2 * li : sruns + 2 * ((size_t)e.g0 + (uint32_t)li);
+    sp = src[0];
+    const uint4 b = src[1];
     r = make_ushort4((uint16_t)(b.x & 0xFFFFu), (uint16_t)(b.x >> 16), (uint16_t)(b.y & 0xFFFFu), (uint16_t)(b.y >> 16));
     id = b.z;
     dbits = b.w;
@@ -442,7 +454,7 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
     row();
     skip_empty();
   };
-  start(e.g0 + (uint32_t)lo);
+  start(lo);
   int local = p0 - s_rel[lo];  // pairs of this Gaussian before the lane's first
   if (sp.x == kTableSpans) {
     // the row holding pair `local`: the last row whose earlier rows hold at most `local`
@@ -463,7 +475,7 @@ __device__ __forceinline__ void lane_pairs(const EmitPart& e, const int32_t* s_r
   for (int k = 0; k < run; ++k) {
     while (p0 + k >= next) {  // on to the next Gaussian
       ++lo;
-      start(e.g0 + (uint32_t)lo);
+      start(lo);
       col = c0;
       next = s_rel[lo + 1];
     }
@@ -731,29 +743,46 @@ __device__ __forceinline__ void emit_scatter_part(int64_t b, int64_t v, int64_t 
   __shared__ int32_t s_rel[kEmitPart + 2];
   __shared__ uint64_t s_keys[kPad];
   __shared__ uint32_t s_vals[kPad];
-  __shared__ uint32_t s_wh[kBinBlock / kWave][kDigits];  // per-wave digit counters, then offsets
-  __shared__ uint32_t s_lbase[kDigits];                    // partition-local digit starts
-  __shared__ uint64_t s_gbase[kDigits];                    // global digit starts for this partition
+  // the staged tile records serve the generation only, the digit arrays the ranking and
+  // what follows it, so they share their LDS
+  union Digits {
+    uint4 runs[2 * kStagedRecs];
+    struct {
+      uint32_t wh[kBinBlock / kWave][kDigits];  // per-wave digit counters, then offsets
+      uint32_t lbase[kDigits];                   // partition-local digit starts
+      uint64_t gbase[kDigits];                   // global digit starts for this partition
+    } d;
+  };
+  static_assert(sizeof(uint4) * 2 * kStagedRecs <= sizeof(Digits), "staged records fit the digit arrays");
+  __shared__ Digits s_u;
+  uint32_t (*s_wh)[kDigits] = s_u.d.wh;
+  uint32_t* s_lbase = s_u.d.lbase;
+  uint64_t* s_gbase = s_u.d.gbase;
   __shared__ uint64_t s_w[kBinBlock / kWave];
   __shared__ uint64_t s_gw[kBinBlock / kWave];
   const int tid = threadIdx.x, lane = __lane_id(), wave = tid / kWave;
-  for (int i = tid; i < (kBinBlock / kWave) * kDigits; i += kBinBlock) (&s_wh[0][0])[i] = 0;
   // digit tid's total and its count in earlier partitions: loaded now, used once the pairs
   // are ranked (the global start of this partition's run of the digit)
   const uint64_t gtot = totals[tid];
   const int64_t chunk = b / kCountParts;
   const uint64_t gpart = gpre[(chunk / kScanGroup) * kDigits + tid] + cpre[chunk * kDigits + tid] +
                          cnt_pre[b * kDigits + tid];
-  const EmitPart e = stage_partition(b, nparts, v, P, goff, gstart, s_rel);
+  const EmitPart e = stage_partition(b, nparts, v, P, goff, gstart, s_rel, sruns, s_u.runs);
   __syncthreads();
   // generate: lane-consecutive, one pad slot per lane so that a wavefront's 8-byte
   // stores spread over the LDS banks
-  lane_pairs<kLarge>(e, s_rel, sruns, table, rec, tiles_x, [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
-    const int slot = tid * (kEmitPer + 1) + k;
-    s_keys[slot] = ((uint64_t)tile << 32) | (uint64_t)dbits;
-    s_vals[slot] = id;
-  });
+  lane_pairs<kLarge>(e, s_rel, sruns, s_u.runs, table, rec, tiles_x,
+                     [&](int k, uint32_t tile, uint32_t id, uint32_t dbits) {
+                       const int slot = tid * (kEmitPer + 1) + k;
+                       s_keys[slot] = ((uint64_t)tile << 32) | (uint64_t)dbits;
+                       s_vals[slot] = id;
+                     });
   __syncthreads();
+  // the staged records are read: each wavefront clears its own row of digit counters
+  // (its LDS operations stay in order, so the ranking's atomics below come after)
+  for (int i = lane; i < kDigits; i += kWave) s_wh[wave][i] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
   // wavefront-striped: wave w owns pairs [w * kWavePart, (w + 1) * kWavePart) of the partition
   constexpr int kWavePart = kEmitPer * kWave;
   uint64_t key[kEmitPer];

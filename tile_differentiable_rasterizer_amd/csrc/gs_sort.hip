@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kRadix) void k_sort_plan(const uint64_t* __restrict
 
 
 template <typename K>
-__global__ __launch_bounds__(Onesweep<K>::threads) void k_onesweep(
+__global__ __launch_bounds__(Onesweep<K>::threads, 8) void k_onesweep(
     K* __restrict__ k0, uint32_t* __restrict__ v0, K* __restrict__ k1, uint32_t* __restrict__ v1,
     int64_t Pmax, const uint64_t* __restrict__ dcount, int pass, int shift, int bits,
     const int32_t* __restrict__ plan, int mode_arg, const uint64_t* __restrict__ dbase,
