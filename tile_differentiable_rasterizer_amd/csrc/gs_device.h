@@ -98,18 +98,18 @@ __device__ __forceinline__ T wave_inclusive_scan(T x) {
 // Lanes of the calling wavefront (among `active`) whose `bits`-bit digit equals this lane's:
 // one ballot per digit bit gives the lanes with that bit set; flipped where this lane's bit
 // is set, it is the lanes that differ from this one in that bit, and the lanes that differ
-// in no bit match.  Bit b of d as a 0 / all-ones word is one bitfield extract, so a bit
-// costs the extract, the ballot's compare and an exclusive-or and an or per half of the
-// 64-lane mask.
+// in no bit match.  A bit costs four instructions: the bit as a 0 / all-ones word (one
+// bitfield extract, kept opaque so that the ballot compares that word), the ballot's
+// compare, and per half of the 64-lane mask one three-input logic op that ors in the
+// exclusive-or (truth table 0xde over (s, differ, ones)).
 __device__ __forceinline__ uint64_t match_digit(uint32_t d, int bits, uint64_t active) {
   uint32_t differ_lo = 0, differ_hi = 0;
-#pragma nounroll
   for (int b = 0; b < bits; ++b) {
-    uint32_t s;  // 0 or 0xFFFFFFFF; opaque, so that the ballot compares it as it is
+    uint32_t s;  // 0 or 0xFFFFFFFF
     asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(s) : "v"(d), "s"(b));
     const uint64_t ones = __ballot(s != 0u);
-    differ_lo |= (uint32_t)ones ^ s;
-    differ_hi |= (uint32_t)(ones >> 32) ^ s;
+    differ_lo = __builtin_amdgcn_bitop3_b32(s, differ_lo, (uint32_t)ones, 0xde);
+    differ_hi = __builtin_amdgcn_bitop3_b32(s, differ_hi, (uint32_t)(ones >> 32), 0xde);
   }
   return active & ~(((uint64_t)differ_hi << 32) | differ_lo);
 }
