@@ -31,7 +31,7 @@
 //                    records (kept runs, rectangle, count) into depth order
 //   k_offsets        per depth-sorted Gaussian: its first pair; per partition: its first
 //                    Gaussian
-//   k_emit_count     per chunk of 8 partitions: counts of the tile's low byte, per
+//   k_emit_count     per chunk of 2 partitions: counts of the tile's low byte, per
 //                    partition as prefixes inside the chunk, and the chunk's totals
 //   k_group_scan,    exclusive scan of the chunk totals over chunks, per digit, in two
 //   k_digit_scan     levels (groups of chunks, then the groups); the digits' totals
@@ -55,7 +55,7 @@ constexpr int kBinChunk = kBinBlock * kBinPer;  // Gaussians per workgroup
 constexpr int kEmitPer = 4;                       // pairs per lane in the emission passes
 constexpr int kEmitPart = kBinBlock * kEmitPer;  // pairs per emission partition
 constexpr int kDigits = 256;                      // values of the tile's low byte
-constexpr int kCountParts = 8;                    // partitions per counting workgroup
+constexpr int kCountParts = 2;                    // partitions per counting workgroup
 constexpr int kDigitCopies = 16;                  // copies of the tile-digit counts (spreads the atomics)
 // Bit of a depth-ordered pair count (sn) marking a Gaussian whose rectangle has neither
 // packed runs nor rows in the projection's row table.  The emission passes come in two
@@ -375,11 +375,14 @@ __device__ __forceinline__ EmitPart stage_partition(int64_t b, int64_t nparts, i
   e.g0 = gstart[b];
   const uint32_t g1 = b + 1 < nparts ? gstart[b + 1] : (uint32_t)(v - 1);
   e.ng = (int)(g1 - e.g0) + 1;
-  for (int i = threadIdx.x; i <= e.ng; i += kBinBlock) s_rel[i] = (int32_t)((int64_t)goff[e.g0 + i] - e.base);
-  if (s_runs) {
-    const int staged = min(e.ng, kStagedRecs);
-    for (int i = threadIdx.x; i < 2 * staged; i += kBinBlock) s_runs[i] = sruns[2 * (size_t)e.g0 + i];
-  }
+  // the first round of both loops issues its loads together
+  const int t = threadIdx.x, nrel = e.ng + 1, nrun = s_runs ? 2 * min(e.ng, kStagedRecs) : 0;
+  const uint64_t rel = t < nrel ? goff[e.g0 + t] : 0;
+  const uint4 run = t < nrun ? sruns[2 * (size_t)e.g0 + t] : make_uint4(0u, 0u, 0u, 0u);
+  if (t < nrel) s_rel[t] = (int32_t)((int64_t)rel - e.base);
+  if (t < nrun) s_runs[t] = run;
+  for (int i = t + kBinBlock; i < nrel; i += kBinBlock) s_rel[i] = (int32_t)((int64_t)goff[e.g0 + i] - e.base);
+  for (int i = t + kBinBlock; i < nrun; i += kBinBlock) s_runs[i] = sruns[2 * (size_t)e.g0 + i];
   return e;
 }
 
