@@ -358,8 +358,8 @@ struct EmitPart {
 };
 
 // Gaussians of a partition whose tile records the scattering pass stages in LDS (the
-// partitions of the bench workload hold 104 on average, 209 at most); the records of any
-// further ones are read from memory.
+// partitions of the 1M-Gaussian 1080p orbit scenes hold 104 on average, 209 at most); the
+// records of any further ones are read from memory.
 constexpr int kStagedRecs = 224;
 
 // Stages s_rel[i] = goff[g0 + i] - base for i in [0, ng] (the last one is the end of the

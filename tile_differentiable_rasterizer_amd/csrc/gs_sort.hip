@@ -176,6 +176,8 @@ __global__ __launch_bounds__(kRadix) void k_sort_plan(const uint64_t* __restrict
 }
 
 
+// At most 64 VGPRs (8 waves per SIMD), so that two 1024-lane workgroups share a CU (their
+// LDS fits); with more registers only one would run.
 template <typename K>
 __global__ __launch_bounds__(Onesweep<K>::threads, 8) void k_onesweep(
     K* __restrict__ k0, uint32_t* __restrict__ v0, K* __restrict__ k1, uint32_t* __restrict__ v1,
