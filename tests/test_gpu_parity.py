@@ -116,6 +116,28 @@ def test_background_and_ragged_image():
                    g["n_contrib"].reshape(-1).astype(np.int64), e2e["render"], "ragged end-to-end")
 
 
+def test_dense_small_gaussians_fill_the_emission_partitions():
+    """60k Gaussians of a pixel or two (one to four tiles each) at 640x480: an emission
+    partition of 1024 pairs then holds ~730 Gaussians, more than the 224 whose tile records
+    the scattering pass stages in LDS, so the records past them are read from memory, and a
+    counting workgroup walks ~1,460 Gaussians.  Binning, sort and ranges bit-exact against
+    the oracle, every pixel of the chained compositing, and the sorted pairs end to end."""
+    sc, _ = scenes.tiny_scene(23, 60000)
+    sc.scales[...] = sc.scales * np.float32(0.05)
+    cam = scenes.Camera(np.eye(3, dtype=np.float32), np.zeros(3, np.float32), 600.0, 600.0, 320.0, 240.0, 640, 480,
+                        float(np.float32(0.2)))
+    g = gpu_stages(sc, cam)
+    vis = int((g["n_tiles"] > 0).sum())
+    per_part = vis / max(1, -(-g["P"] // 1024))
+    say(f"dense small: P={g['P']}, {vis} visible, {per_part:.0f} Gaussians per emission partition")
+    assert per_part > 224
+    info = check_projection(sc, cam, g, "dense small")
+    check_binning(cam, g, "dense small")
+    r = check_render_chained(cam, g, label="dense small")
+    dropped = check_end_to_end_keys(cam, g, "dense small")
+    say(f"dense small: projection {info}, render {r}, end-to-end pairs dropped for flagged Gaussians {dropped}")
+
+
 def test_sort_counts_its_own_digits_the_same(spheres):
     """gs_sort_keys without the binning's tile-digit counts (its own counting read) sorts to
     the same pairs and ranges as with them (the longest-first schedule may order tiles of
