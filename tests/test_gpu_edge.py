@@ -7,7 +7,8 @@ import torch
 import oracle
 from tile_differentiable_rasterizer_amd import raster, scenes
 
-from gpu_util import check_binning, check_projection, check_render_chained, gpu_stages, say
+from gpu_util import (FLAG_CAP, check_binning, check_end_to_end_keys, check_projection, check_render_chained,
+                      gpu_stages, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,6 +56,40 @@ def test_all_culled_and_nan_inputs():
     check_projection(sc, cam, g, "culled")
     check_binning(cam, g, "culled")
     check_render_chained(cam, g, label="culled")
+
+
+@pytest.mark.parametrize("wide", [True, False], ids=["65535x40", "40x65535"])
+def test_largest_image_extent(wide):
+    """The largest width (or height) the boundary accepts, 65535 pixels, on a strip three
+    tiles across: pixel boxes and tile rectangles at the top of their 16-bit range, 4096
+    tiles along the strip.  3,000 Gaussians of a few pixels along it; projection, binning,
+    every pixel and the sorted pairs end to end against the oracle, and one pixel more is
+    an overflow error.  The 2D means reach 65535 px, where a float32 step is 2^-8 px against
+    2^-13 px below 2048 px (the other workloads' coordinates), so the band of decisions
+    within rounding of their thresholds is up to 32 times wider there: the cap on flagged
+    Gaussians per tile decision is 32 times the usual one."""
+    sc, _ = scenes.tiny_scene(29, 3000)
+    rng = np.random.default_rng(31)
+    n = sc.n
+    a, b, z = rng.uniform(-1.05, 1.05, n), rng.uniform(-0.0005, 0.0005, n), rng.uniform(2.8, 3.2, n)
+    sc.means[...] = (np.stack([a, b, z], 1) if wide else np.stack([b, a, z], 1)).astype(np.float32)
+    sc.scales[...] = np.exp(rng.uniform(-10.0, -8.5, (n, 3))).astype(np.float32)
+    W, H = (65535, 40) if wide else (40, 65535)
+    cam = scenes.Camera(np.eye(3, dtype=np.float32), np.zeros(3, np.float32), 90000.0, 90000.0, W / 2, H / 2, W, H,
+                        float(np.float32(0.2)))
+    g = gpu_stages(sc, cam)
+    say(f"extent {W}x{H}: P={g['P']}, {int((g['n_tiles'] > 0).sum())} visible, {cam.num_tiles} tiles")
+    info = check_projection(sc, cam, g, f"{W}x{H}", flag_cap=32 * FLAG_CAP)
+    check_binning(cam, g, f"{W}x{H}")
+    r = check_render_chained(cam, g, label=f"{W}x{H}")
+    dropped = check_end_to_end_keys(cam, g, f"{W}x{H}")
+    say(f"extent {W}x{H}: projection {info}, render {r}, end-to-end pairs dropped for flagged Gaussians {dropped}")
+    import ctypes as C
+    over = raster.camera_struct(scenes.Camera(cam.R, cam.t, cam.fx, cam.fy, cam.cx, cam.cy, W + wide, H + (not wide),
+                                              cam.near))
+    proj = raster.GsProjected()
+    assert raster.lib().gs_project(1, None, None, None, None, None, 0, C.byref(over), proj, None) == \
+        raster.GS_ERR_OVERFLOW
 
 
 def test_single_gaussian_matches_closed_form_alpha():
