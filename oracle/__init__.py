@@ -99,7 +99,12 @@ def sh_basis(L: int, d) -> tuple[np.ndarray, np.ndarray]:
 
 
 def project(scene, cam) -> dict:
-    """Projection of every Gaussian: 2D mean, depth, 2D covariance, conic, colour, rects."""
+    """Projection of every Gaussian: 2D mean, depth, 2D covariance, conic, colour, rects.
+
+    flags marks decisions that lie within rounding of their thresholds and may go either way:
+    bit 0 a depth whose float32 rounding sits on a tie, bit 1 a pixel-box edge, bit 2 a
+    colour channel near 0 (the clamp), bit 3 a tile test near tau, bit 4 a 2D determinant
+    within rounding of 0 (a covariance of rank one: whether the conic exists)."""
     lib = _load()
     means, scales, quats, opac, sh, L = _scene_arrays(scene)
     n = scene.n

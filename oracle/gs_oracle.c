@@ -199,7 +199,8 @@ typedef struct {
   double raw[3], rgb[3];
   int clamp[3];
   int flags;             /* bit0 depth rounding tie, bit1 rect edge, bit2 colour sign,
-                            bit3 a tile-ellipse decision near its threshold          */
+                            bit3 a tile-ellipse decision near its threshold,
+                            bit4 the line cull near its threshold                   */
 } orc_gauss;
 
 /* Is x within tol of an integer? */
@@ -350,7 +351,16 @@ static void project_one(const orc_camera* cam, const double mu[3], const double 
   g->det = g->a * g->c - g->b * g->b;
   g->u = cam->fx * x / z + cam->cx;
   g->v = cam->fy * y / z + cam->cy;
-  if (!(g->det > 0)) return;
+  /* the conic exists for det > 0; a 2D covariance that is a line to working precision is
+     culled too: det <= 1e-9 (a + c)^2.  det / (a + c)^2 = l1 l2 / (l1 + l2)^2 for the
+     eigenvalues l1 >= l2, so this is a screen-space axis ratio below ~3e-5, whatever the
+     rotation.  A covariance of rank one (a zero scale) has det = 0 in exact arithmetic and
+     rounding noise of either sign in practice, far below the threshold, where the sign of det
+     alone would be decided by rounding.  A decision within 1e-11 (a + c)^2 of the threshold
+     is flagged. */
+  const double tr2 = (g->a + g->c) * (g->a + g->c);
+  if (tr2 > 0 && fabs(g->det - 1e-9 * tr2) <= 1e-11 * tr2) g->flags |= 16;
+  if (!(g->det > 1e-9 * tr2)) return;
   g->A = g->c / g->det; g->B = -g->b / g->det; g->C = g->a / g->det;
 
   /* support: alpha >= AMIN  <=>  q <= tau = 2 ln(o / AMIN) */

@@ -119,9 +119,11 @@ def check_projection(scene, cam, g, label="", flag_cap=FLAG_CAP):
     vis_o = p["n_tiles"] > 0
     vis_g = g["n_tiles"] > 0
     # decisions the oracle flags as within float64 / float32 rounding of their thresholds:
-    # a pixel-box edge (bit 1) and a tile test (bit 3) may go either way
+    # a pixel-box edge (bit 1), a tile test (bit 3) and the sign of a determinant within
+    # rounding of 0 (bit 4: whether a conic exists) may go either way
     edge = (flags & 2) != 0
-    amb = edge | ((flags & 8) != 0)
+    degenerate = (flags & 16) != 0
+    amb = edge | ((flags & 8) != 0) | degenerate
     bad_vis = np.nonzero((vis_o != vis_g) & ~amb)[0]
     assert bad_vis.size == 0, f"{label}: visibility differs for ids {bad_vis[:10]}"
     nvis = int(vis_o.sum())
@@ -146,9 +148,11 @@ def check_projection(scene, cam, g, label="", flag_cap=FLAG_CAP):
     uv = p["uv"][both]
     err_uv = np.abs(r[:, 0:2] - uv)
     assert np.all(err_uv <= uv_tolerance(uv)), f"{label}: 2D mean, worst {np.max(err_uv, initial=0)} px"
-    cn = p["conic"][both]
+    # the conic divides by the determinant: compared where that is not rounding noise
+    cdef = ~degenerate[both]
+    cn = p["conic"][both][cdef]
     scale = np.abs(cn[:, 0]) + np.abs(cn[:, 2])
-    err = np.abs(r[:, 2:5] - cn) / scale[:, None]
+    err = np.abs(r[cdef, 2:5] - cn) / scale[:, None]
     assert np.max(err, initial=0) <= 1e-5, f"{label}: conic rel err {np.max(err, initial=0)}"
     assert np.array_equal(r[:, 5], p["opacity"][both]), f"{label}: opacity"
     cerr = np.abs(r[:, 6:9] - p["rgb"][both]) / np.maximum(1.0, np.abs(p["rgb"][both]))
@@ -218,7 +222,7 @@ def check_end_to_end_keys(cam, g, label=""):
     rounding, pixel-box edge or tile test the oracle flags as within rounding of a threshold
     (check_projection caps how many there are).  Returns the number of pairs dropped."""
     p = g["oracle_proj"]
-    amb = (p["flags"] & (1 | 2 | 8)) != 0
+    amb = (p["flags"] & (1 | 2 | 8 | 16)) != 0
     k, v = oracle.emit_projected(p, cam.tiles_x)
     sk, sv = oracle.sort_pairs(k, v)
     keep_o, keep_g = ~amb[sv], ~amb[g["vals"]]

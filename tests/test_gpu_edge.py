@@ -92,6 +92,29 @@ def test_largest_image_extent(wide):
         raster.GS_ERR_OVERFLOW
 
 
+def test_degenerate_scales():
+    """Zero scales: every axis (a point: zero covariance), two axes (a line: a 2D covariance
+    of rank one, whose determinant is rounding noise of either sign) and one axis (a flat
+    disc, an ordinary 2D Gaussian).  Points and lines are culled on both sides (a line by the
+    rule det <= 1e-9 (a + c)^2, which its noise is far below), discs are not; projection,
+    binning, every pixel and the pairs end to end against the oracle."""
+    sc, _ = scenes.tiny_scene(3, 400)
+    sc.scales[0:100] = 0.0
+    sc.scales[100:200, 1:] = 0.0
+    sc.scales[200:300, 2] = 0.0
+    cam = _cam()
+    g = gpu_stages(sc, cam)
+    assert np.all(g["n_tiles"][0:200] == 0)
+    info = check_projection(sc, cam, g, "degenerate")
+    assert not np.any(g["oracle_proj"]["flags"] & 16)
+    assert np.sum(g["n_tiles"][200:300] > 0) > 50
+    check_binning(cam, g, "degenerate")
+    r = check_render_chained(cam, g, label="degenerate")
+    dropped = check_end_to_end_keys(cam, g, "degenerate")
+    say(f"degenerate: projection {info}, discs visible {int((g['n_tiles'][200:300] > 0).sum())}, render {r}, "
+        f"end-to-end pairs dropped {dropped}")
+
+
 def test_single_gaussian_matches_closed_form_alpha():
     s = np.float32(0.05)
     sc = scenes.Scene(np.array([[0.0, 0.0, 2.0]], np.float32), np.array([[s, s, s]], np.float32),

@@ -175,3 +175,43 @@ def test_look_at_is_orthonormal_and_maps_eye_to_origin():
     R = cam.R.astype(np.float64)
     assert np.allclose(R @ R.T, np.eye(3), atol=1e-6)
     assert np.allclose(R @ np.array([1.0, -2.0, 3.0]) + cam.t, 0, atol=1e-5)
+
+
+def test_lines_are_culled_and_thin_gaussians_are_not(orc):
+    """A Gaussian with two zero scales is a line: Sigma = s^2 r r^T, so its 2D covariance is
+    s^2 (T r)(T r)^T with T = J W, exactly rank one (det = 0 in exact arithmetic).  The
+    oracle's 2D covariance must be that outer product, and the Gaussian is culled as a line
+    (det <= 1e-9 (a + c)^2), far from that threshold, so not flagged.  On the optical axis a
+    needle along x with minor scales r times the major has det / (a + c)^2 = r^2 / (1 + r^2)^2:
+    r = 1e-4 stays visible, r = 1e-5 is culled (its one-pixel row holds a pixel centre, so
+    only the line rule can cull it); a thin Gaussian (r = 1/100, rotated) is neither culled
+    nor flagged; one with every scale zero is culled."""
+    cam = id_camera(f=200.0, W=256, H=192, cx=128.0, cy=96.0)
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        q = rng.normal(size=4)
+        q /= np.linalg.norm(q)
+        mean = (rng.uniform(-0.3, 0.3), rng.uniform(-0.3, 0.3), rng.uniform(2.0, 3.0))
+        s = 0.05
+        p = orc.project(one_gaussian(mean, (s, 0.0, 0.0), tuple(q)), cam)
+        # closed form: r = first column of R(q); T = J (identity view)
+        qf = np.array(q, np.float32).astype(np.float64)
+        w, x, y, z = qf / np.linalg.norm(qf)
+        r = np.array([1 - 2 * (y * y + z * z), 2 * (x * y + w * z), 2 * (x * z - w * y)])
+        m = np.array(mean, np.float32).astype(np.float64)
+        fx = f32(200.0)
+        J = np.array([[fx / m[2], 0.0, -fx * m[0] / m[2] ** 2], [0.0, fx / m[2], -fx * m[1] / m[2] ** 2]])
+        t = J @ r * f32(s)
+        a, b, c = p["cov2d"][0]
+        assert np.allclose([a, b, c], [t[0] * t[0], t[0] * t[1], t[1] * t[1]], rtol=1e-12, atol=0)
+        assert p["n_tiles"][0] == 0 and not (p["flags"][0] & 16)
+        thin = orc.project(one_gaussian(mean, (s, s / 100, s / 100), tuple(q)), cam)
+        assert not (thin["flags"][0] & 16) and thin["n_tiles"][0] > 0
+    axis_cam = id_camera(f=200.0, W=256, H=192, cx=128.0, cy=96.5)  # the mean on a pixel-centre row
+    for ratio, visible in ((1e-4, True), (1e-5, False)):
+        p = orc.project(one_gaussian((0.0, 0.0, 2.0), (0.05, 0.05 * ratio, 0.05 * ratio)), axis_cam)
+        a, b, c = p["cov2d"][0]
+        assert b == 0.0 and np.isclose((a * c - b * b) / (a + c) ** 2, ratio ** 2 / (1 + ratio ** 2) ** 2, rtol=1e-6)
+        assert (p["n_tiles"][0] > 0) == visible and not (p["flags"][0] & 16)
+    zero = orc.project(one_gaussian((0.0, 0.0, 2.0), (0.0, 0.0, 0.0)), cam)
+    assert zero["n_tiles"][0] == 0 and not (zero["flags"][0] & 16)

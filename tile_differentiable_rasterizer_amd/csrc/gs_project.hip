@@ -262,7 +262,10 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
     const double c = t1[0] * St1[0] + t1[1] * St1[1] + t1[2] * St1[2];
     const double det = a * c - b * b;
     const double o = opac[i];
-    if (det > 0.0 && o >= (double)kAlphaMin) {
+    // culled with det <= 1e-9 (a + c)^2 (screen-space axis ratio below ~3e-5, whatever the
+    // rotation): a covariance that is a line to working precision, whose det, zero in exact
+    // arithmetic for a rank-one covariance, would be rounding noise of either sign
+    if (det > 1e-9 * ((a + c) * (a + c)) && o >= (double)kAlphaMin) {
       const double iz = 1.0 / g.t[2];
       const double u = cam.fx * g.t[0] * iz + cam.cx;
       const double v = cam.fy * g.t[1] * iz + cam.cy;
