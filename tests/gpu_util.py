@@ -15,7 +15,7 @@ compare them with the float64 oracle under the acceptance rules:
   decision that float32 rounding could flip, up to three per pixel), and the same
   contributor count; pixels with more than three such decisions are excluded and may be
   at most 1e-5 of those compared;
-* gradients: |g - g_ref| <= max(1e-3 |g_ref|, 1e-5, 8 * 2^-24 * S), where S is the sum of
+* gradients: |g - g_ref| <= max(1e-3 |g_ref|, 1e-5, 16 * 2^-24 * S), where S is the sum of
   the absolute per-pixel terms that make up the element (the oracle reports it).  The
   last term is float32's own floor for a sum whose terms cancel: each per-pixel term
   carries a few float32 roundings and the sum adds a few more, so a correct float32
@@ -265,7 +265,13 @@ def check_render_chained(cam, g, bg=(0.0, 0.0, 0.0), pix=None, label=""):
     return compare_pixels(img, T, n, orc, label)
 
 
-COND_ULPS = 8.0 * 2.0 ** -24
+# float32's conditioning floor for a screen-space gradient sum S = sum_k t_k, in units of
+# sum_k |t_k|: each term carries its own evaluation's rounding (a chain of ~10 operations),
+# the wavefront's tree reduction adds 6 levels and the float32 atomics one rounding per
+# (tile, quadrant) that adds into the Gaussian's total, so the first-order bound is
+# (10 + 6 + visits - 1) u.  16 u covers the terms, the tree and the first accumulations; the
+# elements that need it must be badly conditioned and few (check_conditioning_only)
+COND_ULPS = 16.0 * 2.0 ** -24
 
 
 def grad_mismatch(gpu, ref, absum=None, counts=None):
