@@ -42,9 +42,17 @@ def test_codes_bit_exact(bits, L, n):
 
 
 @pytest.mark.parametrize("bits", [8, 16])
-@pytest.mark.parametrize("name,n", [("spheres_100k_sh3_800", 30000), ("aniso_1m_sh3_1080p_8cam", None)])
-def test_projection_of_codes(bits, name, n):
+@pytest.mark.parametrize("name,n,L", [("spheres_100k_sh3_800", 30000, 0), ("spheres_100k_sh3_800", 30000, 1),
+                                      ("spheres_100k_sh3_800", 30000, 2), ("spheres_100k_sh3_800", 30000, 3),
+                                      ("aniso_1m_sh3_1080p_8cam", None, 3)])
+def test_projection_of_codes(bits, name, n, L):
+    """The projection of codes (compiled per SH degree and code width) equals the float32
+    projection of the decoded coefficients, and the oracle's; degrees below 3 cut the
+    scene's SH."""
     sc, cams, _ = scenes.workload(name, n)
+    if L < sc.sh_degree:
+        sc = scenes.Scene(sc.means, sc.scales, sc.quats, sc.opacities,
+                          np.ascontiguousarray(sc.sh[:, :(L + 1) ** 2, :]), L)
     cam = cams[0]
     dev = torch.device("cuda")
     means, scales, quats, opac, sh = raster.scene_to_device(sc, dev)
