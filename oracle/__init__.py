@@ -264,10 +264,13 @@ def set_threads(n: int) -> None:
     _load().orc_set_threads(C.c_int(int(n)))
 
 
-def render_bwd(W: int, H: int, bg, rec, vals, ranges, n: int, dL_dimg, with_abs: bool = False, pix=None):
+def render_bwd(W: int, H: int, bg, rec, vals, ranges, n: int, dL_dimg, with_abs: bool = False, pix=None,
+               with_err: bool = False):
     """grad_screen (n, 10): dL/d(u, v, A, B, C, opacity, r, g, b), sum_p ||dL_p/d(u, v)||.
 
-    With ``with_abs`` also returns the per-element sum of |per-pixel terms|."""
+    With ``with_abs`` also returns the per-element sum of |per-pixel terms|; with
+    ``with_err`` (and with_abs) also the per-element scale of the rounding a float32 reverse
+    walk carries into its terms (see orc_render_bwd): (grad, abs, err)."""
     lib = _load()
     rec = np.ascontiguousarray(rec, dtype=np.float64)
     vals = np.ascontiguousarray(vals, dtype=np.uint32)
@@ -276,10 +279,13 @@ def render_bwd(W: int, H: int, bg, rec, vals, ranges, n: int, dL_dimg, with_abs:
     dL = np.ascontiguousarray(np.asarray(dL_dimg, dtype=np.float64).reshape(3, H, W))
     gs = np.zeros((n, 10))
     ga = np.zeros((n, 10)) if with_abs else None
+    ge = np.zeros((n, 10)) if with_err else None
     pixa = None if pix is None else np.ascontiguousarray(pix, dtype=np.int64)
     lib.orc_render_bwd(C.c_int64(W), C.c_int64(H), _p(bg), _p(rec), _p(vals), _p(ranges),
-                       C.c_int64(n), _p(dL), _p(gs), _p(ga), C.c_int64(0 if pixa is None else pixa.shape[0]),
-                       _p(pixa))
+                       C.c_int64(n), _p(dL), _p(gs), _p(ga), _p(ge),
+                       C.c_int64(0 if pixa is None else pixa.shape[0]), _p(pixa))
+    if with_err:
+        return gs, ga, ge
     return (gs, ga) if with_abs else gs
 
 

@@ -679,13 +679,21 @@ void orc_render_brute(int64_t W, int64_t H, const double bg[3], const double* re
 void orc_render_bwd(int64_t W, int64_t H, const double bg[3], const double* rec,
                     const uint32_t* vals, const int64_t* ranges, int64_t n,
                     const double* dL_dimg, double* grad_screen, double* grad_abs,
-                    int64_t npix, const int64_t* pix) {
+                    double* grad_err, int64_t npix, const int64_t* pix) {
   /* pix (optional): only these pixels (linear j*W + i) contribute; NULL = all W*H. */
   /* grad_abs (optional): per element, the sum of |per-pixel terms|, so a caller can tell
    * an ill-conditioned sum (|sum| << sum |terms|) from a wrong one. */
+  /* grad_err (optional): per element, a scale of the rounding that a float32 reverse walk
+   * carries into the terms: the walk recovers T by dividing by (1 - alpha) and sums the
+   * colour behind one contributor at a time, so at the contributor with s contributors
+   * behind it both carry about s roundings, and they enter the term through dL/dalpha =
+   * T dC.c - dC.behind / (1 - alpha), whose parts may cancel.  Each term adds
+   * (s + 1) * sum_ch |dC_ch| (c_ch T + behind_ch / (1 - alpha)) * |d term / d dL/dalpha|
+   * (for the colour terms, (s + 1) * |term|). */
   const int64_t tiles_x = (W + ORC_TILE - 1) / ORC_TILE;
   memset(grad_screen, 0, sizeof(double) * 10 * (size_t)n);
   if (grad_abs) memset(grad_abs, 0, sizeof(double) * 10 * (size_t)n);
+  if (grad_err) memset(grad_err, 0, sizeof(double) * 10 * (size_t)n);
 #pragma omp parallel
   {
     int64_t cap = 1024;
@@ -733,11 +741,14 @@ void orc_render_bwd(int64_t W, int64_t H, const double bg[3], const double* rec,
         const double dx = st[6 * k + 3], dy = st[6 * k + 4];
         const int clamped = st[6 * k + 5] != 0.0;
         double g[10] = {0};
-        double dL_dalpha = 0;
+        double dL_dalpha = 0, parts = 0;
         for (int ch = 0; ch < 3; ++ch) {
           g[6 + ch] = dC[ch] * alpha * Tk;
           dL_dalpha += dC[ch] * (r[6 + ch] * Tk - behind[ch] / (1.0 - alpha));
+          parts += fabs(dC[ch]) * (r[6 + ch] * Tk + behind[ch] / (1.0 - alpha));
         }
+        double es[10] = {0};  /* |d term / d dL/dalpha|, the colour terms' own size */
+        const double steps = (double)(m - k);
         for (int ch = 0; ch < 3; ++ch) behind[ch] += r[6 + ch] * alpha * Tk;
         if (!clamped) {
           const double o = r[5];
@@ -750,7 +761,16 @@ void orc_render_bwd(int64_t W, int64_t H, const double bg[3], const double* rec,
           g[0] = dL_dq * (-2.0 * (r[2] * dx + r[3] * dy));
           g[1] = dL_dq * (-2.0 * (r[3] * dx + r[4] * dy));
           g[9] = sqrt(g[0] * g[0] + g[1] * g[1]);
+          const double h = 0.5 * o * G, mu = 2.0 * fabs(r[2] * dx + r[3] * dy), mv = 2.0 * fabs(r[3] * dx + r[4] * dy);
+          es[5] = parts * G;
+          es[2] = parts * h * dx * dx;
+          es[3] = parts * h * 2.0 * fabs(dx * dy);
+          es[4] = parts * h * dy * dy;
+          es[0] = parts * h * mu;
+          es[1] = parts * h * mv;
+          es[9] = parts * h * sqrt(mu * mu + mv * mv);
         }
+        for (int ch = 0; ch < 3; ++ch) es[6 + ch] = fabs(g[6 + ch]);
         double* out = grad_screen + 10 * (size_t)id;
         for (int e = 0; e < 10; ++e) {
 #pragma omp atomic
@@ -758,9 +778,16 @@ void orc_render_bwd(int64_t W, int64_t H, const double bg[3], const double* rec,
         }
         if (grad_abs) {
           double* oa = grad_abs + 10 * (size_t)id;
-          for (int e = 0; e < 10; ++e) {
+          for (int c = 0; c < 10; ++c) {
 #pragma omp atomic
-            oa[e] += fabs(g[e]);
+            oa[c] += fabs(g[c]);
+          }
+        }
+        if (grad_err) {
+          double* oe = grad_err + 10 * (size_t)id;
+          for (int c = 0; c < 10; ++c) {
+#pragma omp atomic
+            oe[c] += steps * es[c];
           }
         }
       }

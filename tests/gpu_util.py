@@ -15,11 +15,13 @@ compare them with the float64 oracle under the acceptance rules:
   decision that float32 rounding could flip, up to three per pixel), and the same
   contributor count; pixels with more than three such decisions are excluded and may be
   at most 1e-5 of those compared;
-* gradients: |g - g_ref| <= max(1e-3 |g_ref|, 1e-5, 16 * 2^-24 * S), where S is the sum of
-  the absolute per-pixel terms that make up the element (the oracle reports it).  The
-  last term is float32's own floor for a sum whose terms cancel: each per-pixel term
-  carries a few float32 roundings and the sum adds a few more, so a correct float32
-  result can be off by a small multiple of 2^-24 * S even when |g_ref| << S.  Elements
+* gradients: |g - g_ref| <= max(1e-3 |g_ref|, 1e-5, 16 * 2^-24 * S + 4 * 2^-24 * E), where S is the sum of
+  the absolute per-pixel terms that make up the element and E the oracle's rounding scale
+  of the float32 reverse walk (both reported by the oracle).  The last term is float32's
+  own floor for a sum whose terms cancel: each per-pixel term carries a few roundings, the
+  walk's transmittance and colour behind carry one or two per contributor into the parts
+  of dL/dalpha (which may cancel too), and the sum adds a few more, so a correct float32
+  result can be off by that much even when |g_ref| << S.  Elements
   that pass only through that term are reported with their conditioning
   kappa = S / |g_ref|; each must have kappa >= 1e2 (a summation limit, not a wrong term),
   and there may be at most max(4, 1e-6 * elements) of them.
@@ -272,13 +274,19 @@ def check_render_chained(cam, g, bg=(0.0, 0.0, 0.0), pix=None, label=""):
 # (10 + 6 + visits - 1) u.  16 u covers the terms, the tree and the first accumulations; the
 # elements that need it must be badly conditioned and few (check_conditioning_only)
 COND_ULPS = 16.0 * 2.0 ** -24
+# the rounding a float32 reverse walk carries into its terms, in units of the oracle's
+# per-element scale (orc_render_bwd grad_err: at each contributor, the contributors behind it
+# times the size of the parts of dL/dalpha): T recovered by a reciprocal and a product, and
+# the colour behind accumulated with one fma, per contributor
+ERR_ULPS = 4.0 * 2.0 ** -24
 
 
-def grad_mismatch(gpu, ref, absum=None, counts=None):
+def grad_mismatch(gpu, ref, absum=None, counts=None, errscale=None):
     """Indices violating the gradient tolerance, and the worst ratio |g - ref| / tol.
 
     With ``absum`` (per-element sum of |terms|) the float32 conditioning floor joins the
-    tolerance; ``counts`` (a dict) then receives how many elements needed it and the
+    tolerance, with ``errscale`` (the oracle's rounding scale of the reverse walk) the walk's
+    rounding too; ``counts`` (a dict) then receives how many elements needed them and the
     conditioning kappa = absum / |ref| of each."""
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
@@ -286,6 +294,8 @@ def grad_mismatch(gpu, ref, absum=None, counts=None):
     if absum is not None:
         absum = np.asarray(absum, np.float64)
         cond = COND_ULPS * absum
+        if errscale is not None:
+            cond = cond + ERR_ULPS * np.asarray(errscale, np.float64)
         if counts is not None:
             err = np.abs(gpu - ref)
             only = (err > tol) & (err <= cond)

@@ -44,9 +44,10 @@ def _run(sc, cam, target, label):
     torch.cuda.synchronize()
     gs = to_np(grads["grad_screen"]).astype(np.float64)
     say(f"{label}: oracle backward")
-    ref, refabs = oracle.render_bwd(W, H, bg, rec, g["vals"], g["ranges"], n, dL, with_abs=True)
+    ref, refabs, referr = oracle.render_bwd(W, H, bg, rec, g["vals"], g["ranges"], n, dL, with_abs=True,
+                                            with_err=True)
     counts = {}
-    bad, worst = grad_mismatch(gs, ref, refabs, counts)
+    bad, worst = grad_mismatch(gs, ref, refabs, counts, referr)
     if bad[0].size:
         kappa = refabs[bad] / np.maximum(np.abs(ref[bad]), 1e-300)
         say(f"{label}: screen grads {bad[0].size} bad, worst ratio {worst:.3g}, kappa of bad: "
@@ -85,19 +86,20 @@ def test_backward_small_sh3():
 @pytest.mark.parametrize("L", [1, 2])
 def test_forward_and_backward_sh_degrees_1_and_2(L):
     """The projection and its backward are compiled per SH degree; degrees 0 and 3 run in the
-    other tests.  The 20k sphere scene with its SH cut to degree L: projection, binning and
-    every pixel against the oracle, then the backward as above."""
+    other tests.  The 20k sphere scene with its SH cut to degree L, on a ragged 333x247 image
+    (partial tiles on the right and bottom edges): projection, binning and every pixel
+    against the oracle, then the backward as above."""
     from gpu_util import check_binning, check_projection, check_render_chained
     full = scenes.sphere_scene(31, 20000, anisotropic=True)
     K = (L + 1) ** 2
     sc = scenes.Scene(full.means, full.scales, full.quats, full.opacities,
                       np.ascontiguousarray(full.sh[:, :K, :]), L)
-    cam = scenes.orbit_camera(1.9, 320, 240, f=300.0)
+    cam = scenes.orbit_camera(1.9, 333, 247, f=300.0)
     g = gpu_stages(sc, cam)
     check_projection(sc, cam, g, f"L={L}")
     check_binning(cam, g, f"L={L}")
     check_render_chained(cam, g, label=f"L={L}")
-    _run(sc, cam, scenes.target_image(33 + L, 320, 240), f"bwd L={L}")
+    _run(sc, cam, scenes.target_image(33 + L, 333, 247), f"bwd L={L}")
 
 
 def test_backward_sh0_tiny():

@@ -170,3 +170,31 @@ def test_absolute_statistic_is_sum_of_per_pixel_l2_norms(orc):
     assert np.allclose(full[:, 9], acc, rtol=1e-12, atol=1e-15)
     assert np.allclose(full[:, :2], acc_uv, rtol=1e-10, atol=1e-13)
     assert np.any(acc > 0)
+
+
+def test_rounding_scale_of_the_reverse_walk_closed_form(orc):
+    """The per-element rounding scale the GPU parity test admits for a float32 reverse walk
+    (orc_render_bwd's grad_err), by hand for one pixel behind which two records lie at its
+    centre (G = 1, so the mean and conic terms vanish): contributor k with s contributors
+    behind it adds (s + 1) sum_ch |dC_ch| (c_ch T_k + behind_ch / (1 - alpha_k)) to the
+    opacity term and (s + 1) |dC_ch alpha_k T_k| to the colour terms."""
+    rec = np.array([[0.5, 0.5, 1.0, 0.0, 1.0, 0.5, 0.2, 0.4, 0.6],
+                    [0.5, 0.5, 1.0, 0.0, 1.0, 0.6, 0.9, 0.1, 0.3]])
+    vals = np.array([0, 1], np.uint32)
+    ranges = np.array([[0, 2]], np.int64)
+    bg = (0.1, 0.1, 0.1)
+    dL = np.zeros((3, 16, 16))
+    dL[:, 0, 0] = (1.0, -2.0, 0.5)
+    g, ga, ge = orc.render_bwd(16, 16, bg, rec, vals, ranges, 2, dL, with_abs=True, pix=[0], with_err=True)
+    # back record: T = 0.5, behind = bg * T_final = 0.02; front: T = 1, behind = 0.02 + c1 * 0.3
+    dC = np.array([1.0, -2.0, 0.5])
+    c0, c1 = rec[0, 6:9], rec[1, 6:9]
+    behind1 = np.full(3, 0.1 * 0.5 * 0.4)
+    parts1 = np.sum(np.abs(dC) * (c1 * 0.5 + behind1 / 0.4))
+    behind0 = behind1 + c1 * 0.6 * 0.5
+    parts0 = np.sum(np.abs(dC) * (c0 * 1.0 + behind0 / 0.5))
+    assert np.isclose(ge[1, 5], 1 * parts1) and np.isclose(ge[0, 5], 2 * parts0)
+    assert np.allclose(ge[1, 6:9], np.abs(dC * 0.6 * 0.5)) and np.allclose(ge[0, 6:9], 2 * np.abs(dC * 0.5))
+    assert np.all(ge[:, [0, 1, 2, 3, 4, 9]] == 0.0)
+    # the scale bounds the terms' own size: every part is at least the term it makes up
+    assert np.all(ge[:, 5] >= np.abs(g[:, 5])) and np.all(ge[:, 6:9] >= ga[:, 6:9])
