@@ -139,9 +139,11 @@ typedef struct gs_grads {
  *                   with d the unit direction from the camera centre to the mean
  *  cam [host]       camera
  * The 2D covariance is J W Sigma W^T J^T (first-order perspective Jacobian J at the
- * camera-space mean, no low-pass dilation).  A Gaussian is kept when z > near_z,
- * det > 0, opacity >= 1/255 and its support {q <= 2 ln(255 opacity)} covers at least
- * one pixel centre; the tile rect is the support's pixel-centre bounding box >> 4.
+ * camera-space mean, no low-pass dilation).  A Gaussian is kept when z > near_z, its 2D
+ * covariance [[a, b], [b, c]] is not a line to working precision (det = a c - b^2 >
+ * 1e-9 (a + c)^2, a screen-space axis ratio above ~3e-5: a zero scale otherwise leaves det
+ * as rounding noise), opacity >= 1/255 and its support {q <= 2 ln(255 opacity)} covers at
+ * least one pixel centre; the tile rect is the support's pixel-centre bounding box >> 4.
  * Errors: INVALID_ARG, OVERFLOW (n >= 2^32), HIP.
  */
 gs_status gs_project(int64_t n, const float* means, const float* scales, const float* quats,
