@@ -83,15 +83,38 @@ __device__ __forceinline__ uint64_t lookback_exclusive(const uint64_t* col, int6
   }
 }
 
-// Inclusive prefix sum across a 64-wide wavefront.
+// One DPP move of a 32-bit word: lanes whose source lies outside their row (or whose row the
+// row mask leaves out) receive 0.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, 0xF, false);
+}
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = dpp_u32<kCtrl, kRowMask>((uint32_t)x), hi = dpp_u32<kCtrl, kRowMask>((uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int kCtrl, int kRowMask, typename T>
+__device__ __forceinline__ T dpp_move(T x) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit words");
+  if constexpr (sizeof(T) == 8)
+    return (T)dpp_u64<kCtrl, kRowMask>((uint64_t)x);
+  else
+    return (T)dpp_u32<kCtrl, kRowMask>((uint32_t)x);
+}
+
+// Inclusive prefix sum across a 64-wide wavefront (every lane active), with DPP moves and no
+// LDS round trips: shifts right by 1, 2, 4 and 8 within each row of 16 lanes scan the rows;
+// the last lane of row 0 (2) is then added into row 1 (3), and the last lane of row 1 into
+// rows 2 and 3.
 template <typename T>
 __device__ __forceinline__ T wave_inclusive_scan(T x) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    T y = __shfl_up(x, d, 64);
-    if (lane >= d) x += y;
-  }
+  x += dpp_move<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_move<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_move<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_move<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_move<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_move<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
   return x;
 }
 
