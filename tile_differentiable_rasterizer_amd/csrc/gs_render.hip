@@ -34,20 +34,22 @@ namespace gs {
 constexpr int kRenderBlock = 256;
 constexpr int kRenderWaves = kRenderBlock / kWave;
 
-// Staged record: (u, v, a2, b2) (c2, opacity, r, g) (b, box x, box y, id) [A, B, C, 0].
-// a2, b2, c2 are the conic scaled to the base-2 exponent: -log2(e)/2 * (A, 2B, C).
+// Staged record: (u, v, a2, b2) (c2, lo, r, g) (b, box x, box y, id) [A, B, C, 1 / opacity].
+// a2, b2, c2 are the conic scaled to the base-2 exponent: -log2(e)/2 * (A, 2B, C); lo is
+// log2(opacity), so that alpha = 2^(exponent + lo) needs no product with the opacity.
 __device__ __forceinline__ void stage_transform(const float4 r0, const float4 r1, float4& s0, float4& s1) {
   s0 = make_float4(r0.x, r0.y, -0.5f * kLog2e * r0.z, -kLog2e * r0.w);
-  s1 = make_float4(-0.5f * kLog2e * r1.x, r1.y, r1.z, r1.w);
+  s1 = make_float4(-0.5f * kLog2e * r1.x, __builtin_amdgcn_logf(r1.y), r1.z, r1.w);
 }
 
-// Base-2 exponent of the Gaussian factor at offset (dx, dy) from the 2D mean.  Every
-// operation is spelled out so that the forward and the backward round identically.
-__device__ __forceinline__ float gauss_exponent(float a2, float b2, float c2, float dx, float dy) {
+// Base-2 exponent of opacity * (Gaussian factor) at offset (dx, dy) from the 2D mean, lo =
+// log2(opacity).  Every operation is spelled out so that the forward and the backward
+// round identically.
+__device__ __forceinline__ float gauss_exponent(float a2, float b2, float c2, float lo, float dx, float dy) {
 #pragma clang fp contract(off)
   const float inner = fmaf(a2, dx, b2 * dy);  // a2 dx + b2 dy
   const float cy = c2 * dy;
-  return fmaf(dx, inner, cy * dy);
+  return fmaf(dx, inner, fmaf(cy, dy, lo));
 }
 
 __device__ __forceinline__ float gauss_factor(float e) { return __builtin_amdgcn_exp2f(e); }
@@ -83,7 +85,7 @@ __device__ __forceinline__ bool quadrant_reach(const float4 s0, const float4 s1,
   const int x0 = (int)(bx & 0xFFFFu), x1 = (int)(bx >> 16);
   const int y0 = (int)(by & 0xFFFFu), y1 = (int)(by >> 16);
   if (!(x0 <= qx0 + 7 && x1 >= qx0 && y0 <= qy0 + 7 && y1 >= qy0)) return false;
-  const float thr = __builtin_amdgcn_logf(kAlphaMin) - __builtin_amdgcn_logf(s1.y) - 0.01f;
+  const float thr = __builtin_amdgcn_logf(kAlphaMin) - s1.y - 0.01f;
   const float X0 = (float)qx0 + 0.5f - s0.x, Y0 = (float)qy0 + 0.5f - s0.y;
   return box_max_exponent(s0.z, s0.w, s1.x, X0, X0 + 7.0f, Y0, Y0 + 7.0f) >= thr;
 }
@@ -143,9 +145,9 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
       // colour b, and the list position + 1 of the record (what n_contrib counts)
       my[3 * slot + 2] = make_float4(p2.x, __uint_as_float((uint32_t)(b - start) + 1u + (uint32_t)lane), 0.f, 0.f);
     }
-    if (lane == 0) {  // an inert record after the last (opacity 0: alpha 0, never taken)
+    if (lane == 0) {  // an inert record after the last (opacity 0, lo = -inf: alpha 0, never taken)
       const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-      my[3 * cnt] = z; my[3 * cnt + 1] = z; my[3 * cnt + 2] = z;
+      my[3 * cnt] = z; my[3 * cnt + 1] = make_float4(0.f, -INFINITY, 0.f, 0.f); my[3 * cnt + 2] = z;
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -160,14 +162,14 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_fwd(
     // T and the colour exactly as they were
     auto blend = [&](const float4 a, const float4 e1, const float2 e2) {
       const float dx = fx - a.x, dy = fy - a.y;
-      const float alpha = fminf(kAlphaMax, e1.y * gauss_factor(gauss_exponent(a.z, a.w, e1.x, dx, dy)));
+      const float alpha = fminf(kAlphaMax, gauss_factor(gauss_exponent(a.z, a.w, e1.x, e1.y, dx, dy)));
       const bool take = alpha >= kAlphaMin && T >= kTMin && inside;
       const float at = take ? alpha : 0.0f;
       const float w = at * T;
       cr = fmaf(e1.z, w, cr);
       cg = fmaf(e1.w, w, cg);
       cb = fmaf(e2.x, w, cb);
-      T = T * (1.0f - at);
+      T = fmaf(-at, T, T);  // T (1 - alpha), rounded once
       nc = take ? __float_as_uint(e2.y) : nc;
     };
     // two records per step (an odd count ends on the inert record); the next step's
@@ -229,8 +231,7 @@ __device__ __forceinline__ uint64_t bwd_record(const float4* __restrict__ s_rec,
   const float4 s0 = s_rec[4 * j], s1 = s_rec[4 * j + 1], s2 = s_rec[4 * j + 2], s3 = s_rec[4 * j + 3];
   id = __float_as_uint(s2.w);  // the Gaussian the record belongs to
   const float dx = p.fx - s0.x, dy = p.fy - s0.y;
-  const float G = gauss_factor(gauss_exponent(s0.z, s0.w, s1.x, dx, dy));
-  const float oG = s1.y * G;
+  const float oG = gauss_factor(gauss_exponent(s0.z, s0.w, s1.x, s1.y, dx, dy));  // opacity * G
   const float alpha = fminf(kAlphaMax, oG);
   const bool contrib = kr < p.ncr && alpha >= kAlphaMin;
   // the same two compares as lane masks (ICmp SLT = 40, FCmp OGE = 3), so the wavefront's
@@ -249,8 +250,8 @@ __device__ __forceinline__ uint64_t bwd_record(const float4* __restrict__ s_rec,
   p.H = fmaf(D, w, p.H);
   p.T = contrib ? Tk : p.T;
   dalpha = contrib && oG <= kAlphaMax ? dalpha : 0.0f;  // the clamp at 0.99 stops the gradient
-  g[5] = dalpha * G;
   const float dq = dalpha * oG;
+  g[5] = dq * s3.w;  // dL/dalpha * G, with G = oG / opacity
   const float dqx = dq * dx, dqy = dq * dy;
   g[2] = dqx * dx;
   g[3] = dqx * dy;
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(kRenderBlock) void k_render_bwd(
       my[4 * lane] = s0;
       my[4 * lane + 1] = s1;
       my[4 * lane + 2] = make_float4(q2.x, q2.y, q2.z, __uint_as_float(pid));
-      my[4 * lane + 3] = make_float4(q0.z, q0.w, q1.x, 0.0f);
+      my[4 * lane + 3] = make_float4(q0.z, q0.w, q1.x, __builtin_amdgcn_rcpf(q1.y));
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
     }
