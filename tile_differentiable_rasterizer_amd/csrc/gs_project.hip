@@ -96,6 +96,50 @@ __device__ __forceinline__ void load_row(const float* __restrict__ row, float* c
   }
 }
 
+// Degree-3 float32 SH rows (192 bytes, twelve 16-byte pieces) reach a lane in two parts.  The
+// first kShLds pieces of the rows of a wavefront's 64 Gaussians are copied into the
+// wavefront's LDS slice by direct global-to-LDS 16-byte loads: consecutive lanes of one copy
+// take consecutive pieces of the (contiguous) rows, so the reads are coalesced, and the data
+// bypasses the registers while the float64 geometry runs.  The last pieces are loaded per lane
+// when the colour is evaluated, which keeps the slice at 32 KB per 256 lanes (four waves per
+// SIMD, as the registers allow).
+constexpr int kShPieces = 12;
+constexpr int kShLds = 8;
+
+// Issues the copies for the wavefront whose first Gaussian is wbase (n Gaussians in all) into
+// dst (kWave * kShLds pieces).  Copy q = k 64 + lane is piece q % kShLds of row q / kShLds.
+// Every lane copies a piece, past the last row the array's last piece again into a slot that
+// no lane reads, so the copies are unconditional: with copies that some lanes skip, the
+// compiler's waits for later loads would also have to wait for every copy.
+__device__ __forceinline__ void copy_rows_to_lds(const float* __restrict__ sh, int64_t n, int64_t wbase,
+                                                 float4* dst) {
+  const int lane = (int)__lane_id();
+  const float4* src = reinterpret_cast<const float4*>(sh) + wbase * kShPieces;
+  const int64_t last = (n - wbase) * kShPieces - 1;
+#pragma unroll
+  for (int k = 0; k < kShLds; ++k) {
+    const int q = k * kWave + lane, r = q / kShLds;
+    const int64_t p = min((int64_t)(r * kShPieces + (q - r * kShLds)), last);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + p),
+                                     (__attribute__((address_space(3))) void*)(dst + k * kWave), 16, 0, 0);
+  }
+}
+
+// Gaussian i's row (48 floats) from its LDS slot (the compiler waits for the copies) and its
+// last pieces from global memory.
+__device__ __forceinline__ void row_from_lds(const float4* my_row, const float* __restrict__ sh, int64_t i,
+                                             float* coef) {
+  float4 tail[kShPieces - kShLds];
+#pragma unroll
+  for (int t = 0; t < kShPieces - kShLds; ++t)
+    tail[t] = reinterpret_cast<const float4*>(sh)[i * kShPieces + kShLds + t];
+#pragma unroll
+  for (int c = 0; c < kShPieces; ++c) {
+    const float4 q = c < kShLds ? my_row[c] : tail[c - kShLds];
+    coef[4 * c] = q.x; coef[4 * c + 1] = q.y; coef[4 * c + 2] = q.z; coef[4 * c + 3] = q.w;
+  }
+}
+
 // This lane's SH row from q8 / q16 codes (QB bits) with (lo, hi) bounds per 256 units ("Training
 // 10M Gaussians in 8 GB: Spirula Studio's VRAM efficiency", quantised training section): unit
 // u = i ROW + c lies in block u / 256, so a row spans one or two blocks.  Decoded in float32,
@@ -213,46 +257,77 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
     uint4* __restrict__ runs_out, uint2* __restrict__ rows_out) {
   using S = ShLayout<L>;
   static_assert(kProjBlock == GS_ROW_BLOCK, "one row-table region per workgroup");
+  // degree-3 float32 rows come through LDS (copy_rows_to_lds)
+  constexpr bool kDma = L == 3 && QB == 0;
+  static_assert(!kDma || S::ROW == 4 * kShPieces, "degree-3 rows");
+  __shared__ float4 s_sh[kDma ? kProjBlock * kShLds : 1];
   const int64_t base = (int64_t)blockIdx.x * kProjBlock;
   const int cnt = (int)min((int64_t)kProjBlock, n - base);
   const int tid = threadIdx.x;
-  if (tid >= cnt) return;
-  const int64_t i = base + tid;
-
-  const double mx = means[3 * i], my = means[3 * i + 1], mz = means[3 * i + 2];
-  const double sc[3] = {scales[3 * i], scales[3 * i + 1], scales[3 * i + 2]};
-  Geom g;
-  geom(cam, mx, my, mz, sc, quats[i], g);
-  depth_out[i] = (float)g.t[2];
-
-  // view-dependent colour: 0.5 + sum_k Y_k(d) sh_k, clamped at 0
-  float coef[S::ROW];
-  if constexpr (QB == 0)
-    load_row<L>(sh + i * S::ROW, coef);
-  else
-    load_row_q<L, QB>(shq, shb, i, coef);
-  const double vx = mx - cam.campos[0], vy = my - cam.campos[1], vz = mz - cam.campos[2];
-  const double il = 1.0 / sqrt(vx * vx + vy * vy + vz * vz);
-  float Y[S::K];
-  sh_basis<L>((float)(vx * il), (float)(vy * il), (float)(vz * il), Y);
-  float col[3];
-  uint32_t cl = 0;
-#pragma unroll
-  for (int ch = 0; ch < 3; ++ch) {
-    float acc = 0.5f;
-#pragma unroll
-    for (int k = 0; k < S::K; ++k) acc = fmaf(Y[k], coef[3 * k + ch], acc);
-    if (acc < 0.0f) { cl |= 1u << ch; acc = 0.0f; }
-    col[ch] = acc;
+  const bool act = tid < cnt;
+  const int64_t i = base + (act ? tid : 0);
+  // the geometry's inputs are requested before the row copies, so that waiting for them
+  // does not wait for the copies (vector memory counters drain in issue order)
+  const float mxf = means[3 * i], myf = means[3 * i + 1], mzf = means[3 * i + 2];
+  const float s0f = scales[3 * i], s1f = scales[3 * i + 1], s2f = scales[3 * i + 2];
+  const float4 qt = quats[i];
+  const float opf = opac[i];
+  if constexpr (kDma) {
+    // the inputs are in registers before the copies are issued: the compiler cannot count
+    // direct-to-LDS loads apart from ordinary ones, so a later wait for the inputs would also
+    // wait for every copy
+    asm volatile("" ::"v"(mxf), "v"(myf), "v"(mzf), "v"(s0f), "v"(s1f), "v"(s2f), "v"(qt.x), "v"(qt.y), "v"(qt.z),
+                 "v"(qt.w), "v"(opf));
+    const int w = tid / kWave;
+    copy_rows_to_lds(sh, n, base + (int64_t)w * kWave, s_sh + w * kWave * kShLds);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  clamp_out[i] = (uint8_t)cl;
+  // lanes past the last Gaussian compute with Gaussian `base` and store nothing (no early
+  // return: the input loads stay ahead of the row copies)
+  const double mx = mxf, my = myf, mz = mzf;
+  const double sc[3] = {s0f, s1f, s2f};
+  Geom g;
+  geom(cam, mx, my, mz, sc, qt, g);
+  if (act) depth_out[i] = (float)g.t[2];
+
+  // view-dependent colour: 0.5 + sum_k Y_k(d) sh_k, clamped at 0.  Evaluated before the
+  // screen-space work, except where the row comes through LDS: there it is evaluated last,
+  // once the copies have had the geometry's time to land
+  float col[3];
+  auto colour = [&]() {
+    float coef[S::ROW];
+    if constexpr (kDma) {
+      __builtin_amdgcn_sched_barrier(0);  // the row is read after the geometry, not hoisted into it
+      row_from_lds(s_sh + tid * kShLds, sh, i, coef);
+    } else if constexpr (QB == 0)
+      load_row<L>(sh + i * S::ROW, coef);
+    else
+      load_row_q<L, QB>(shq, shb, i, coef);
+    const double vx = mx - cam.campos[0], vy = my - cam.campos[1], vz = mz - cam.campos[2];
+    const double il = 1.0 / sqrt(vx * vx + vy * vy + vz * vz);
+    float Y[S::K];
+    sh_basis<L>((float)(vx * il), (float)(vy * il), (float)(vz * il), Y);
+    uint32_t cl = 0;
+#pragma unroll
+    for (int ch = 0; ch < 3; ++ch) {
+      float acc = 0.5f;
+#pragma unroll
+      for (int k = 0; k < S::K; ++k) acc = fmaf(Y[k], coef[3 * k + ch], acc);
+      if (acc < 0.0f) { cl |= 1u << ch; acc = 0.0f; }
+      col[ch] = acc;
+    }
+    if (act) clamp_out[i] = (uint8_t)cl;
+  };
+  if constexpr (!kDma) colour();
+
 
   float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0, r2 = r0;
   ushort4 rc = make_ushort4(0, 0, 0, 0);
   uint4 sp = make_uint4(0u, 0u, 0u, 0u);
   uint32_t nt = 0;
   bool overflow = false;  // a visible rectangle whose rows did not fit in the row table
-  if (g.t[2] > cam.near_z) {  // NaN fails
+  bool vis = false;
+  if (act && g.t[2] > cam.near_z) {  // NaN fails
     double t0[3], t1[3], St0[3], St1[3];
     proj_rows(cam, g.t, t0, t1);
     sym_mul(g.S, t0, St0);
@@ -261,7 +336,7 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
     const double b = t0[0] * St1[0] + t0[1] * St1[1] + t0[2] * St1[2];
     const double c = t1[0] * St1[0] + t1[1] * St1[1] + t1[2] * St1[2];
     const double det = a * c - b * b;
-    const double o = opac[i];
+    const double o = opf;
     // culled with det <= 1e-9 (a + c)^2 (screen-space axis ratio below ~3e-5, whatever the
     // rotation): a covariance that is a line to working precision, whose det, zero in exact
     // arithmetic for a rank-one covariance, would be rounding noise of either sign
@@ -282,8 +357,9 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
         const uint32_t px0 = (uint32_t)lx, px1 = (uint32_t)hx, py0 = (uint32_t)ly, py1 = (uint32_t)hy;
         const double idet = 1.0 / det;
         r0 = make_float4((float)u, (float)v, (float)(c * idet), (float)(-b * idet));
-        r1 = make_float4((float)(a * idet), (float)o, col[0], col[1]);
-        r2 = make_float4(col[2], __uint_as_float(px0 | (px1 << 16)), __uint_as_float(py0 | (py1 << 16)), 0.0f);
+        r1 = make_float4((float)(a * idet), (float)o, 0.0f, 0.0f);  // colour below
+        r2 = make_float4(0.0f, __uint_as_float(px0 | (px1 << 16)), __uint_as_float(py0 | (py1 << 16)), 0.0f);
+        vis = true;
         rc = make_ushort4((uint16_t)(px0 >> 4), (uint16_t)(px1 >> 4), (uint16_t)(py0 >> 4), (uint16_t)(py1 >> 4));
         // tiles of the rectangle that pass the ellipse test of the record as stored, and
         // their runs packed for the emission
@@ -328,19 +404,27 @@ __global__ __launch_bounds__(kProjBlock) void k_project(
       }
     }
   }
-  rec[3 * i] = r0;
-  rec[3 * i + 1] = r1;
-  rec[3 * i + 2] = r2;
-  rect_out[i] = rc;
-  ntiles_out[i] = nt;
-  runs_out[2 * i] = sp;
-  runs_out[2 * i + 1] = make_uint4((uint32_t)rc.x | ((uint32_t)rc.y << 16), (uint32_t)rc.z | ((uint32_t)rc.w << 16),
-                                   nt, 0u);
+  if constexpr (kDma) colour();
+  if (vis) {
+    r1.z = col[0];
+    r1.w = col[1];
+    r2.x = col[2];
+  }
+  if (act) {
+    rec[3 * i] = r0;
+    rec[3 * i + 1] = r1;
+    rec[3 * i + 2] = r2;
+    rect_out[i] = rc;
+    ntiles_out[i] = nt;
+    runs_out[2 * i] = sp;
+    runs_out[2 * i + 1] = make_uint4((uint32_t)rc.x | ((uint32_t)rc.y << 16),
+                                     (uint32_t)rc.z | ((uint32_t)rc.w << 16), nt, 0u);
+  }
   // the last entry of the wavefront's region says whether one of its rectangles overflowed,
-  // so that the binning skips its float64 path when none did (lane 0 of every wavefront
-  // with a Gaussian is active here)
+  // so that the binning skips its float64 path when none did (written by lane 0 of every
+  // wavefront that holds a Gaussian)
   const uint64_t ovf = __ballot(overflow);
-  if (__lane_id() == 0)
+  if (__lane_id() == 0 && act)
     rows_out[(size_t)(blockIdx.x * (kProjBlock / kWave) + tid / kWave) * kRegionRows + kWaveRows] =
         make_uint2(ovf ? 1u : 0u, 0u);
 }
@@ -581,17 +665,29 @@ __global__ __launch_bounds__(kProjBlock) void k_project_io(
     float* __restrict__ depth_out, ushort4* __restrict__ rect_out, uint32_t* __restrict__ ntiles_out,
     uint8_t* __restrict__ clamp_out, uint4* __restrict__ runs_out, uint2* __restrict__ rows_out) {
   using S = ShLayout<L>;
+  constexpr bool kDma = L == 3;  // degree-3 rows through LDS, as k_project reads them
+  __shared__ float4 s_sh[kDma ? kProjBlock * kShLds : 1];
   const int64_t base = (int64_t)blockIdx.x * kProjBlock;
   const int cnt = (int)min((int64_t)kProjBlock, n - base);
   const int tid = threadIdx.x;
-  if (tid >= cnt) return;
-  const int64_t i = base + tid;
+  const bool act = tid < cnt;
+  const int64_t i = base + (act ? tid : 0);
   const float mx = means[3 * i], my = means[3 * i + 1], mz = means[3 * i + 2];
   const float sx = scales[3 * i], sy = scales[3 * i + 1], sz = scales[3 * i + 2];
   const float4 q = quats[i];
   const float o = opac[i];
+  if constexpr (kDma) {
+    asm volatile("" ::"v"(mx), "v"(my), "v"(mz), "v"(sx), "v"(sy), "v"(sz), "v"(q.x), "v"(q.y), "v"(q.z), "v"(q.w),
+                 "v"(o));
+    const int w = tid / kWave;
+    copy_rows_to_lds(sh, n, base + (int64_t)w * kWave, s_sh + w * kWave * kShLds);
+  }
+  if (!act) return;
   float coef[S::ROW];
-  load_row<L>(sh + i * S::ROW, coef);
+  if constexpr (kDma)
+    row_from_lds(s_sh + tid * kShLds, sh, i, coef);
+  else
+    load_row<L>(sh + i * S::ROW, coef);
   float acc = 0.0f;
 #pragma unroll
   for (int c = 0; c < S::ROW; ++c) acc += coef[c];
