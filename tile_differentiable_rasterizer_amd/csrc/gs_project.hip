@@ -96,21 +96,25 @@ __device__ __forceinline__ void load_row(const float* __restrict__ row, float* c
   }
 }
 
-// Degree-3 float32 SH rows (192 bytes, twelve 16-byte pieces) reach a lane in two parts.  The
-// first kShLds pieces of the rows of a wavefront's 64 Gaussians are copied into the
-// wavefront's LDS slice by direct global-to-LDS 16-byte loads: consecutive lanes of one copy
-// take consecutive pieces of the (contiguous) rows, so the reads are coalesced, and the data
-// bypasses the registers while the float64 geometry runs.  The last pieces are loaded per lane
-// when the colour is evaluated, which keeps the slice at 32 KB per 256 lanes (four waves per
-// SIMD, as the registers allow).
+// Degree-3 float32 SH rows (192 bytes, twelve 16-byte pieces) reach a lane in two parts.  Two
+// consecutive rows are three 128-byte lines: the even row's pieces 0-7, then its pieces 8-11
+// with the odd row's pieces 0-3, then the odd row's pieces 4-11.  The first and third lines of
+// every pair in a wavefront's 64 rows are copied into the wavefront's LDS slice (8 pieces a
+// row) by direct global-to-LDS 16-byte loads: consecutive lanes of one copy take consecutive
+// pieces, so the reads are coalesced, and the data bypasses the registers while the float64
+// geometry runs.  The middle lines are loaded per lane (each lane its own half) when the
+// colour is evaluated, so every line is fetched once, and the slice stays at 32 KB per 256
+// lanes (four waves per SIMD, as the registers allow).
 constexpr int kShPieces = 12;
 constexpr int kShLds = 8;
 
 // Issues the copies for the wavefront whose first Gaussian is wbase (n Gaussians in all) into
-// dst (kWave * kShLds pieces).  Copy q = k 64 + lane is piece q % kShLds of row q / kShLds.
-// Every lane copies a piece, past the last row the array's last piece again into a slot that
-// no lane reads, so the copies are unconditional: with copies that some lanes skip, the
-// compiler's waits for later loads would also have to wait for every copy.
+// dst (kWave * kShLds pieces).  Copy q = k 64 + lane is LDS piece q % kShLds of row r = q /
+// kShLds: the row's piece q % kShLds, or q % kShLds + 4 for an odd row.  Every lane copies a
+// piece, past the last row the array's last piece again into a slot that no lane reads, so
+// the copies are unconditional: with copies that some lanes skip, the compiler's waits for
+// later loads would also have to wait for every copy.  (Rows are paired by their index in the
+// array; wbase is a multiple of 64.)
 __device__ __forceinline__ void copy_rows_to_lds(const float* __restrict__ sh, int64_t n, int64_t wbase,
                                                  float4* dst) {
   const int lane = (int)__lane_id();
@@ -119,24 +123,30 @@ __device__ __forceinline__ void copy_rows_to_lds(const float* __restrict__ sh, i
 #pragma unroll
   for (int k = 0; k < kShLds; ++k) {
     const int q = k * kWave + lane, r = q / kShLds;
-    const int64_t p = min((int64_t)(r * kShPieces + (q - r * kShLds)), last);
+    const int64_t p = min((int64_t)(r * kShPieces + (q - r * kShLds) + (r & 1) * (kShPieces - kShLds)), last);
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + p),
                                      (__attribute__((address_space(3))) void*)(dst + k * kWave), 16, 0, 0);
   }
 }
 
 // Gaussian i's row (48 floats) from its LDS slot (the compiler waits for the copies) and its
-// last pieces from global memory.
+// other four pieces from global memory: pieces 8-11 of an even row, 0-3 of an odd one.
 __device__ __forceinline__ void row_from_lds(const float4* my_row, const float* __restrict__ sh, int64_t i,
                                              float* coef) {
-  float4 tail[kShPieces - kShLds];
+  constexpr int kT = kShPieces - kShLds;
+  const bool odd = (i & 1) != 0;
+  float4 tail[kT], lds[kShLds];
 #pragma unroll
-  for (int t = 0; t < kShPieces - kShLds; ++t)
-    tail[t] = reinterpret_cast<const float4*>(sh)[i * kShPieces + kShLds + t];
+  for (int t = 0; t < kT; ++t)
+    tail[t] = reinterpret_cast<const float4*>(sh)[i * kShPieces + (odd ? 0 : kShLds) + t];
+#pragma unroll
+  for (int c = 0; c < kShLds; ++c) lds[c] = my_row[c];
 #pragma unroll
   for (int c = 0; c < kShPieces; ++c) {
-    const float4 q = c < kShLds ? my_row[c] : tail[c - kShLds];
-    coef[4 * c] = q.x; coef[4 * c + 1] = q.y; coef[4 * c + 2] = q.z; coef[4 * c + 3] = q.w;
+    const float4 e = c < kShLds ? lds[c] : tail[c - kShLds];  // even rows: LDS pieces, then the tail
+    const float4 o = c < kT ? tail[c] : lds[c - kT];           // odd rows: the tail, then LDS pieces
+    coef[4 * c] = odd ? o.x : e.x; coef[4 * c + 1] = odd ? o.y : e.y;
+    coef[4 * c + 2] = odd ? o.z : e.z; coef[4 * c + 3] = odd ? o.w : e.w;
   }
 }
 
