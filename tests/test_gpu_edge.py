@@ -115,6 +115,27 @@ def test_degenerate_scales():
         f"end-to-end pairs dropped {dropped}")
 
 
+@pytest.mark.parametrize("n", [1, 2, 63, 64, 65, 130, 257, 1023])
+def test_projection_sh3_ragged_wavefronts(n):
+    """Degree-3 SH rows reach the projection through LDS copies of a whole wavefront's rows,
+    each pair of rows split on 128-byte lines between the copies and per-lane loads (pieces
+    0-7 of an even row, 4-11 of an odd one, copied).  Counts below, at and just past one
+    wavefront and one workgroup: partial wavefronts, wavefronts with no Gaussian, an odd or
+    even last row.  Every row's coefficients differ, so a row taken from the wrong slot or
+    the wrong half of a line changes the colour far beyond the tolerance; compared with the
+    oracle on an orbit view that sees the whole scene."""
+    full = scenes.sphere_scene(41, max(n, 8), anisotropic=True)
+    sc = scenes.Scene(np.ascontiguousarray(full.means[:n]), np.ascontiguousarray(full.scales[:n]),
+                      np.ascontiguousarray(full.quats[:n]), np.ascontiguousarray(full.opacities[:n]),
+                      np.ascontiguousarray(full.sh[:n]), 3)
+    cam = scenes.orbit_camera(0.7, 320, 240, f=200.0, radius=6.0)
+    g = gpu_stages(sc, cam)
+    info = check_projection(sc, cam, g, f"n={n}")
+    assert info["visible"] >= (n + 1) // 2, f"n={n}: only {info['visible']} visible"
+    check_binning(cam, g, f"n={n}")
+    say(f"projection n={n}: {info}")
+
+
 def test_single_gaussian_matches_closed_form_alpha():
     s = np.float32(0.05)
     sc = scenes.Scene(np.array([[0.0, 0.0, 2.0]], np.float32), np.array([[s, s, s]], np.float32),
