@@ -1,5 +1,5 @@
-"""float64 oracle of the fused Adam step with 16-bit packed moments -- TEST INFRASTRUCTURE
-ONLY (see oracle/__init__.py).
+"""float64 oracle of the fused Adam step with 16-bit packed moments (and, in its second form,
+16-bit packed parameters too) -- TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 
 "Training 10M Gaussians in 8 GB: Spirula Studio's VRAM efficiency" (mhpq.cn), quantised
 training section: the Adam moments are kept as 16-bit codes packed next to each other, in a
@@ -83,3 +83,76 @@ def adam_q16(params, grads, state, bounds, *, lr: float, beta1: float, beta2: fl
     if full:
         return new_p, new_w, new_b, dict(m=m, v=v, update=upd)
     return new_p, new_w, new_b
+
+
+# --- parameters packed too ("FPBO") ------------------------------------------------------------
+# The same page packs the parameters into 16-bit words together with both moments.  Readings
+# (the page gives neither the word layout nor the arithmetic):
+#   * a block of 256 units is stored transposed: three planes of 256 uint16 codes, the
+#     parameters' codes, then the first moments', then the second moments'; state has shape
+#     [nb][3][256] and the codes past the last unit of the last block are 0;
+#   * bounds[b] = (p_lo, p_hi, m_lo, m_hi, v_lo, v_hi), float32, with the encoding and decoding
+#     above for all three quantities;
+#   * a step decodes the parameter, takes Adam's update in float64 (no float32 rounding of the
+#     parameter in between: its storage is the 16-bit code) and encodes the new parameter with
+#     its block's new bounds, as the moments are; the float32 parameters a renderer reads are
+#     the decoded new codes, lo + code (hi - lo) / 65535 rounded once to float32.
+
+
+def fpbo_pack(params):
+    """float32 params [U] -> (state uint16 [nb][3][256], bounds float32 [nb][6]): the parameters
+    encoded per block, both moments zero (codes 0, bounds 0)."""
+    p = np.asarray(params, np.float32).astype(np.float64)
+    U = p.shape[0]
+    nb = (U + BLOCK - 1) // BLOCK
+    state = np.zeros((nb, 3, BLOCK), np.uint16)
+    bounds = np.zeros((nb, 6), np.float32)
+    codes, lo, hi = encode_blocks(p)
+    pad = np.zeros(nb * BLOCK, np.uint16)
+    pad[:U] = codes
+    state[:, 0, :] = pad.reshape(nb, BLOCK)
+    bounds[:, 0], bounds[:, 1] = lo, hi
+    return state, bounds
+
+
+def fpbo_decode_params(state, bounds, U: int):
+    """The float32 parameters held by a packed state: lo + code (hi - lo) / 65535, rounded once."""
+    st = np.asarray(state, np.uint16).reshape(-1, 3, BLOCK)
+    bd = np.asarray(bounds, np.float32).reshape(-1, 6)
+    blk = np.arange(U) // BLOCK
+    return decode(st[:, 0, :].reshape(-1)[:U], bd[blk, 0], bd[blk, 1]).astype(np.float32)
+
+
+def adam_fpbo(state, bounds, grads, *, lr: float, beta1: float, beta2: float, eps: float, step: int,
+              full: bool = False):
+    """One Adam step on a packed state (see fpbo_pack).  grads float32 [U].  Returns (state,
+    bounds, params) after the step, params being the decoded float32 parameters; with ``full``
+    also a dict of the float64 parameters, moments and updates (for tolerances)."""
+    g = np.asarray(grads, np.float32).astype(np.float64)
+    U = g.shape[0]
+    st = np.asarray(state, np.uint16).reshape(-1, 3, BLOCK)
+    bd = np.asarray(bounds, np.float32).reshape(-1, 6)
+    nb = st.shape[0]
+    blk = np.arange(U) // BLOCK
+    theta = decode(st[:, 0, :].reshape(-1)[:U], bd[blk, 0], bd[blk, 1])
+    m = decode(st[:, 1, :].reshape(-1)[:U], bd[blk, 2], bd[blk, 3])
+    v = decode(st[:, 2, :].reshape(-1)[:U], bd[blk, 4], bd[blk, 5])
+    b1, b2 = np.float64(np.float32(beta1)), np.float64(np.float32(beta2))
+    m = b1 * m + (1.0 - b1) * g
+    v = b2 * v + (1.0 - b2) * (g * g)
+    m_hat = m / (1.0 - math.pow(float(b1), step))
+    v_hat = v / (1.0 - math.pow(float(b2), step))
+    upd = np.float64(np.float32(lr)) * m_hat / (np.sqrt(v_hat) + np.float64(np.float32(eps)))
+    theta = theta - upd
+    new_st = np.zeros((nb, 3, BLOCK), np.uint16)
+    new_bd = np.zeros((nb, 6), np.float32)
+    for plane, x in enumerate((theta, m, v)):
+        codes, lo, hi = encode_blocks(x)
+        pad = np.zeros(nb * BLOCK, np.uint16)
+        pad[:U] = codes
+        new_st[:, plane, :] = pad.reshape(nb, BLOCK)
+        new_bd[:, 2 * plane], new_bd[:, 2 * plane + 1] = lo, hi
+    params = fpbo_decode_params(new_st, new_bd, U)
+    if full:
+        return new_st, new_bd, params, dict(theta=theta, m=m, v=v, update=upd)
+    return new_st, new_bd, params

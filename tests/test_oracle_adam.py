@@ -77,3 +77,90 @@ def test_empty():
     p, w, b = A.adam_q16(np.zeros(0, np.float32), np.zeros(0, np.float32), np.zeros(0, np.uint32),
                          np.zeros((0, 4), np.float32), step=1, **H)
     assert p.shape == (0,) and w.shape == (0,) and b.shape == (0, 4)
+
+
+# --- parameters packed too (adam_fpbo) ---------------------------------------------------------
+
+
+def test_fpbo_pack_layout_and_round_trip():
+    rng = np.random.default_rng(3)
+    U = 600  # blocks of 256, 256 and 88
+    p = rng.normal(size=U).astype(np.float32)
+    st, bd = A.fpbo_pack(p)
+    assert st.shape == (3, 3, 256) and st.dtype == np.uint16 and bd.shape == (3, 6)
+    # moments start at zero; the padding past the last unit is zero
+    assert not st[:, 1:, :].any() and not bd[:, 2:].any() and not st[2, 0, 88:].any()
+    for b in range(3):
+        seg = p[256 * b:256 * b + 256]
+        assert bd[b, 0] == seg.min() and bd[b, 1] == seg.max()
+        assert st[b, 0, np.argmin(seg)] == 0 and st[b, 0, np.argmax(seg)] == 65535
+    # every parameter decodes within half a code step of its float32 value
+    blk = np.arange(U) // 256
+    half = (bd[blk, 1].astype(np.float64) - bd[blk, 0]) / 65535.0 / 2
+    dec = A.fpbo_decode_params(st, bd, U)
+    assert np.all(np.abs(dec.astype(np.float64) - p) <= half * (1 + 1e-9) + np.spacing(np.abs(p)))
+    # a constant block keeps its value exactly
+    st, bd = A.fpbo_pack(np.full(5, -1.5, np.float32))
+    assert np.all(st[0, 0] == 0) and bd[0, 0] == bd[0, 1] == np.float32(-1.5)
+    assert np.all(A.fpbo_decode_params(st, bd, 5) == np.float32(-1.5))
+
+
+def test_fpbo_first_step_closed_form():
+    rng = np.random.default_rng(4)
+    U = 1000
+    p = rng.normal(size=U).astype(np.float32)
+    g = (rng.uniform(0.5, 2.0, U) * rng.choice([-1, 1], U)).astype(np.float32)
+    st, bd = A.fpbo_pack(p)
+    theta0 = A.fpbo_decode_params(st, bd, U).astype(np.float64)
+    st1, bd1, p1 = A.adam_fpbo(st, bd, g, step=1, **H)
+    # from zero moments: m_hat = g, v_hat = g^2, so the parameter moves by lr g / (|g| + eps);
+    # the stored result is that value to within half a code step of its new block
+    g64 = g.astype(np.float64)
+    want = theta0 - np.float32(H["lr"]) * g64 / (np.abs(g64) + np.float32(H["eps"]))
+    blk = np.arange(U) // 256
+    half = (bd1[blk, 1].astype(np.float64) - bd1[blk, 0]) / 65535.0 / 2
+    assert np.all(np.abs(p1.astype(np.float64) - want) <= half * (1 + 1e-6) + np.spacing(np.abs(want)))
+    # the new bounds are the extremes of the new parameters (rounded to float32)
+    for b in range(bd1.shape[0]):
+        seg = want[256 * b:256 * b + 256]
+        assert abs(bd1[b, 0] - seg.min()) <= abs(np.spacing(np.float32(seg.min()))) + 1e-12
+        assert abs(bd1[b, 1] - seg.max()) <= abs(np.spacing(np.float32(seg.max()))) + 1e-12
+    # first moment after one step is (1 - b1) g: its codes sit at the block's two ends when
+    # the gradients of a block take just two values
+    st2, bd2, _ = A.adam_fpbo(st, bd, np.where(np.arange(U) % 2, 1.0, -1.0).astype(np.float32), step=1, **H)
+    assert set(np.unique(st2[:3, 1, :])) == {0, 65535}
+    assert bd2[0, 2] == np.float32(-0.1 * 1.0) or abs(bd2[0, 2] + 0.1) < 1e-7
+
+
+def test_fpbo_steps_follow_torch_adam():
+    rng = np.random.default_rng(5)
+    U = 2048
+    p0 = rng.normal(size=U).astype(np.float32)
+    st, bd = A.fpbo_pack(p0)
+    p = A.fpbo_decode_params(st, bd, U)
+    theta = torch.tensor(p.astype(np.float64), requires_grad=True)
+    opt = torch.optim.Adam([theta], lr=np.float32(H["lr"]).item(), betas=(np.float32(0.9).item(),
+                           np.float32(0.999).item()), eps=np.float32(H["eps"]).item())
+    drift = 0.0
+    for t in range(1, 6):
+        g = (rng.uniform(0.5, 2.0, U) * rng.choice([-1, 1], U)).astype(np.float32)
+        theta.grad = torch.tensor(g.astype(np.float64))
+        opt.step()
+        st, bd, p = A.adam_fpbo(st, bd, g, step=t, **H)
+        # each step stores the parameter to within half a code step (~5.5 / 65535 / 2 for these
+        # N(0, 1) blocks), and the quantised moments move the update by far less than that here
+        blk = np.arange(U) // 256
+        drift += np.max((bd[blk, 1].astype(np.float64) - bd[blk, 0]) / 65535.0 / 2) + 2e-6
+        assert np.max(np.abs(p.astype(np.float64) - theta.detach().numpy())) <= drift, t
+    # the moments against torch's, as in the moments-only form
+    mm = st[:, 1, :].reshape(-1)[:U]
+    m = A.decode(mm, bd[blk, 2], bd[blk, 3])
+    step_m = (bd[blk, 3].astype(np.float64) - bd[blk, 2]) / 65535.0
+    assert np.max(np.abs(m - opt.state[theta]["exp_avg"].numpy()) / step_m) < 4.0
+
+
+def test_fpbo_empty():
+    st, bd = A.fpbo_pack(np.zeros(0, np.float32))
+    assert st.shape == (0, 3, 256) and bd.shape == (0, 6)
+    st, bd, p = A.adam_fpbo(st, bd, np.zeros(0, np.float32), step=1, **H)
+    assert st.shape == (0, 3, 256) and p.shape == (0,)
