@@ -790,7 +790,29 @@ def adam_measure(raster, dev, with_oracle, gaussians=5_000_000, reps=5):
            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(ach / HBM_PEAK_GBS, 4), "bytes": int(nbytes)},
            "pages_context_ms": {"before": 13.8, "after": 8.5, "note": "5M points, hardware unspecified"}}
-    del params, grads, state, bounds
+    del state, bounds
+    torch.cuda.empty_cache()
+    # the same step with the parameters packed too (gs_adam_fpbo): per unit the three codes
+    # read and written (6 B each way), the gradient read and the decoded float32 parameter
+    # written for the renderer; 24 B of bounds per 256 units read and written
+    pstate, pbounds = raster.fpbo_pack(params)
+    raster.adam_fpbo(U, pstate, pbounds, grads, params, lr=1e-3, step=1)
+    torch.cuda.synchronize()
+    assert raster.kernel_timer_start("k_adam_fpbo") == raster.GS_OK
+    for t in range(2, reps + 2):
+        raster.adam_fpbo(U, pstate, pbounds, grads, params, lr=1e-3, step=t)
+    torch.cuda.synchronize()
+    st, launches, kms = raster.kernel_timer_stop()
+    assert st == raster.GS_OK and launches == reps
+    ms = kms / launches
+    nbytes = U * (6 + 4 + 6 + 4) + ((U + 255) // 256) * 48
+    ach = nbytes / (ms * 1e-3) / 1e9
+    res["packed_params"] = {
+        "call": "gs_adam_fpbo (parameters and both moments as 16-bit codes, decoded parameters written)",
+        "ms": round(ms, 4), "state_bytes_per_unit": 6,
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "bytes": int(nbytes)}}
+    del params, grads, pstate, pbounds
     torch.cuda.empty_cache()
     if with_oracle:
         import time as _t
@@ -806,6 +828,10 @@ def adam_measure(raster, dev, with_oracle, gaussians=5_000_000, reps=5):
                    beta2=0.999, eps=1e-8, step=1)
         res["cpu_oracle_ms"] = round(1e3 * (_t.perf_counter() - t0) * U / n, 1)
         res["cpu_oracle_sample"] = f"one step on {n} units, scaled to {U}"
+        st0, bd0 = A.fpbo_pack(p)
+        t0 = _t.perf_counter()
+        A.adam_fpbo(st0, bd0, g, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, step=1)
+        res["packed_params"]["cpu_oracle_ms"] = round(1e3 * (_t.perf_counter() - t0) * U / n, 1)
     return res
 
 

@@ -396,6 +396,36 @@ typedef struct gs_adam_params {
 gs_status gs_adam_q16(int64_t n, float* params, const float* grads, uint32_t* state, float* bounds,
                       const gs_adam_params* hyper, void* stream);
 
+/*
+ * gs_fpbo_pack / gs_adam_fpbo -- the fused Adam step with the parameters kept as 16-bit codes
+ * too, beside both moments ("Training 10M Gaussians in 8 GB: Spirula Studio's VRAM
+ * efficiency", quantised training section: parameters and moments packed together into
+ * 16-bit words in a transposed layout, bounds per 256 units, float32 gradients).
+ *  state[ceil(n/256)][3][256]  uint16 (device; 8-byte aligned): per block of 256 units three
+ *              planes of codes, the parameters', the first moments', the second moments'; codes
+ *              past unit n - 1 are 0.  Updated in place.
+ *  bounds[ceil(n/256)][6]  float32 (device; 8-byte aligned): (p_lo, p_hi, m_lo, m_hi, v_lo,
+ *              v_hi) of each block.  Updated in place.
+ * gs_fpbo_pack writes the start state from float32 params[n] (device, 16-byte aligned): the
+ * parameters' codes with their blocks' exact minimum and maximum, both moments 0 (codes 0,
+ * bounds 0).
+ * gs_adam_fpbo takes grads[n] (float32, device, 16-byte aligned) and hyper as gs_adam_q16.  Per
+ * unit it decodes the parameter and both moments (lo + code (hi - lo) / 65535), updates the
+ * moments in float64, takes the parameter's step in float32 (about 5e-7 relative) and
+ * subtracts it in float64; each block's new bounds are the float32 roundings of the minimum
+ * and maximum of each quantity, and a code is rint((x - lo) / (hi - lo) * 65535) clamped to
+ * [0, 65535] (0 when hi == lo).  A parameter's update smaller than half its block's code
+ * step leaves its code unchanged.  params_out[n] (float32, device, 16-byte aligned; may be
+ * NULL) receives the new parameters as stored, each new code decoded and rounded once.
+ * Constants enter as reciprocals computed once, so a code decided within a few float64
+ * roundings of a half-integer can differ by one from the definition's.
+ * Errors: INVALID_ARG (null pointer with n > 0, misaligned pointer, step < 1, beta outside
+ * [0, 1)), OVERFLOW (n >= 2^40), HIP.
+ */
+gs_status gs_fpbo_pack(int64_t n, const float* params, uint16_t* state, float* bounds, void* stream);
+gs_status gs_adam_fpbo(int64_t n, uint16_t* state, float* bounds, const float* grads, float* params_out,
+                       const gs_adam_params* hyper, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* gs_status_string(gs_status status);
 

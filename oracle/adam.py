@@ -35,6 +35,17 @@ def decode(codes, lo, hi):
     return lo + np.asarray(codes, np.float64) * (hi - lo) / QMAX
 
 
+def encode(x, lo, hi):
+    """float64 values with the float32 bounds of their blocks (per value) -> uint16 codes:
+    rint((x - lo) / (hi - lo) * 65535) clamped to [0, 65535], 0 where hi == lo."""
+    x = np.asarray(x, np.float64)
+    lo = np.asarray(lo, np.float32).astype(np.float64)
+    hi = np.asarray(hi, np.float32).astype(np.float64)
+    span = hi - lo
+    c = np.where(span != 0.0, np.rint((x - lo) / np.where(span != 0.0, span, 1.0) * QMAX), 0.0)
+    return np.clip(c, 0.0, QMAX).astype(np.uint16)
+
+
 def encode_blocks(x):
     """float64 values [U] -> (codes uint16 [U], lo float32 [nb], hi float32 [nb]) per 256-unit block."""
     x = np.asarray(x, np.float64)
@@ -42,18 +53,12 @@ def encode_blocks(x):
     nb = (U + BLOCK - 1) // BLOCK
     lo = np.empty(nb, np.float32)
     hi = np.empty(nb, np.float32)
-    codes = np.empty(U, np.uint16)
     for b in range(nb):
         seg = x[b * BLOCK:(b + 1) * BLOCK]
         lo[b] = np.float32(seg.min())
         hi[b] = np.float32(seg.max())
-        l, h = np.float64(lo[b]), np.float64(hi[b])
-        if h == l:
-            c = np.zeros(seg.shape[0])
-        else:
-            c = np.rint((seg - l) / (h - l) * QMAX)
-        codes[b * BLOCK:(b + 1) * BLOCK] = np.clip(c, 0.0, QMAX).astype(np.uint16)
-    return codes, lo, hi
+    blk = np.arange(U) // BLOCK
+    return encode(x, lo[blk], hi[blk]), lo, hi
 
 
 def adam_q16(params, grads, state, bounds, *, lr: float, beta1: float, beta2: float, eps: float, step: int,

@@ -48,6 +48,31 @@ def test_host_only_calls():
 
 
 @pytest.mark.skipif(not os.path.exists(LIB), reason="libgsraster.so not built")
+def test_packed_adam_argument_checks():
+    # every case is refused before any HIP call: null or misaligned pointers, bad hyper-parameters
+    from tile_differentiable_rasterizer_amd import raster
+
+    L = raster.lib()
+    ok = raster.GsAdamParams(1e-3, 0.9, 0.999, 1e-8, 1)
+    a16, a8 = 1 << 20, 1 << 20  # aligned stand-ins, never dereferenced
+    bad = raster.GS_ERR_INVALID_ARG
+    assert L.gs_fpbo_pack(-1, a16, a8, a8, None) == bad
+    assert L.gs_fpbo_pack(10, None, a8, a8, None) == bad
+    assert L.gs_fpbo_pack(10, a16 + 4, a8, a8, None) == bad
+    assert L.gs_fpbo_pack(10, a16, a8 + 2, a8, None) == bad
+    assert L.gs_adam_fpbo(10, a8, a8, None, None, C.byref(ok), None) == bad
+    assert L.gs_adam_fpbo(10, a8, a8, a16 + 8, None, C.byref(ok), None) == bad
+    assert L.gs_adam_fpbo(10, a8, a8, a16, a16 + 4, C.byref(ok), None) == bad
+    assert L.gs_adam_fpbo(10, a8, a8 + 4, a16, None, C.byref(ok), None) == bad
+    for h in (raster.GsAdamParams(1e-3, 0.9, 0.999, 1e-8, 0), raster.GsAdamParams(1e-3, 1.0, 0.999, 1e-8, 1)):
+        assert L.gs_adam_fpbo(10, a8, a8, a16, None, C.byref(h), None) == bad
+    assert L.gs_adam_fpbo(1 << 40, a8, a8, a16, None, C.byref(ok), None) == raster.GS_ERR_OVERFLOW
+    # nothing to do: no launch
+    assert L.gs_fpbo_pack(0, None, None, None, None) == raster.GS_OK
+    assert L.gs_adam_fpbo(0, None, None, None, None, C.byref(ok), None) == raster.GS_OK
+
+
+@pytest.mark.skipif(not os.path.exists(LIB), reason="libgsraster.so not built")
 def test_kernel_timer_host_logic():
     # no launch happens between start and stop, so no HIP call is made
     from tile_differentiable_rasterizer_amd import raster

@@ -1,4 +1,4 @@
-"""GPU parity of gs_adam_q16 against the float64 oracle (oracle/adam.py, Adam in its defining
+"""GPU parity of gs_adam_q16 (and of gs_fpbo_pack / gs_adam_fpbo, below) against the float64 oracle (oracle/adam.py, Adam in its defining
 form), through the C ABI.  Each step is chained: the oracle takes the GPU's state after the
 previous step.
 
@@ -150,3 +150,145 @@ def test_empty_and_errors():
     assert L.gs_adam_q16(10, None, p.data_ptr(), s.data_ptr(), b.data_ptr(), C.byref(h), None) == \
         raster.GS_ERR_INVALID_ARG
     torch.cuda.synchronize()
+
+
+# --- parameters packed too: gs_fpbo_pack / gs_adam_fpbo against oracle.adam.fpbo_pack / adam_fpbo
+#
+# The same rule, applied to each of the three planes (parameters, first and second moments).
+# The parameter's float64 value differs from the oracle's by at most
+# DX = 16 * 2^-53 * (|lo| + |hi| + |theta|) + 1e-6 |update|, since its step is taken in
+# float32; with updates of order lr that is far wider than the moments' DX, so blocks whose
+# float32 bounds round differently are expected, not rare.  Hence:
+# * a bound equals the oracle's or lies between the float32 roundings of the oracle's
+#   extreme -/+ DX;
+# * every code is compared, with the GPU's bounds of its block: it equals the oracle's
+#   encoding of the oracle's value with those bounds (oracle.adam.encode), or differs by one
+#   where that value lies within 65535 DX / (hi - lo) + 1e-9 of a rounding boundary;
+# * the counts of differing bounds and codes are capped at three times what DX predicts
+#   (the sum over bounds of 2 DX / float32 spacing, over units of 2 eta) plus a few.
+# The decoded float32 parameters (params_out) are the GPU's own new codes decoded: they must
+# equal the oracle's decoding of those codes to one float32 spacing.
+
+
+def _check_plane(label, name, gc, gb_lo, gb_hi, ob_lo, ob_hi, x, dx, U):
+    """GPU codes gc [U] (int64) and bounds per block against the oracle's bounds and float64
+    values x, with error bound dx [U].  Returns (differing codes, differing bounds)."""
+    nb = ob_lo.shape[0]
+    mn, mx, imn, imx = _block_extremes(x, U)
+    amb_b, exp_b = 0, 0.0
+    for g_b, o_b, ext, idx in ((gb_lo, ob_lo, mn, imn), (gb_hi, ob_hi, mx, imx)):
+        d = dx[np.arange(nb) * 256 + idx]
+        lo32, hi32 = (ext - d).astype(np.float32), (ext + d).astype(np.float32)
+        same = g_b == o_b
+        ok = same | ((g_b >= lo32) & (g_b <= hi32))
+        assert np.all(ok), f"{label}: {name} bounds, blocks {np.nonzero(~ok)[0][:5]}"
+        amb_b += int((~same).sum())
+        sp = np.abs(np.spacing(o_b)).astype(np.float64)
+        exp_b += float(np.minimum(1.0, 2.0 * d / np.where(sp > 0, sp, 1e-45)).sum())
+    assert amb_b <= max(2, 3 * exp_b + 2), f"{label}: {name}: {amb_b} bounds differ, {exp_b:.2f} expected"
+    blk = np.arange(U) // 256
+    lo, hi = gb_lo[blk].astype(np.float64), gb_hi[blk].astype(np.float64)
+    oc = A.encode(x, gb_lo[blk], gb_hi[blk]).astype(np.int64)
+    span = np.where(hi > lo, hi - lo, 1.0)
+    scaled = (x - lo) / span * 65535.0
+    eta = np.where(hi > lo, 65535.0 * dx / span + 1e-9, 0.0)
+    near_half = np.abs(scaled - np.floor(scaled) - 0.5) <= eta
+    diff = np.abs(gc - oc)
+    bad = ~((diff == 0) | ((diff == 1) & near_half))
+    assert not bad.any(), f"{label}: {name} codes differ at {np.nonzero(bad)[0][:5]}"
+    amb_u = int((diff == 1).sum())
+    exp_u = float(np.minimum(1.0, 2.0 * eta).sum())
+    assert amb_u <= max(4, 3 * exp_u + 4), f"{label}: {name}: {amb_u} codes differ by one, {exp_u:.1f} expected"
+    return amb_u, amb_b
+
+
+def check_fpbo(U, gpu, orc, prev_bd, g, label):
+    gst, gbd, gp = gpu
+    ost, obd, op, x = orc
+    nb = obd.shape[0]
+    blk = np.arange(U) // 256
+    g = g.astype(np.float64)
+    pb = prev_bd.astype(np.float64)
+    dx = {
+        0: 16 * EPS64 * (np.abs(pb[blk, 0]) + np.abs(pb[blk, 1]) + np.abs(x["theta"])) + 1e-6 * np.abs(x["update"]),
+        1: 16 * EPS64 * (np.abs(pb[blk, 2]) + np.abs(pb[blk, 3]) + np.abs(x["m"]) + np.abs(g)),
+        2: 16 * EPS64 * (np.abs(pb[blk, 4]) + np.abs(pb[blk, 5]) + np.abs(x["v"]) + g * g),
+    }
+    amb_u = amb_b = 0
+    for plane, name, key in ((0, "param", "theta"), (1, "m", "m"), (2, "v", "v")):
+        gc = gst[:, plane, :].reshape(-1)[:U].astype(np.int64)
+        u, b = _check_plane(label, name, gc, gbd[:, 2 * plane], gbd[:, 2 * plane + 1], obd[:, 2 * plane],
+                            obd[:, 2 * plane + 1], x[key], dx[plane], U)
+        amb_u += u
+        amb_b += b
+    assert not np.any(gst[nb - 1, :, U - 256 * (nb - 1):]), f"{label}: codes past the last unit"
+    want = A.fpbo_decode_params(gst, gbd, U).astype(np.float64)
+    err = np.abs(gp.astype(np.float64) - want)
+    assert np.all(err <= np.abs(np.spacing(want.astype(np.float32))).astype(np.float64)), f"{label}: params_out"
+    return amb_u, amb_b, int((err > 0).sum())
+
+
+def run_fpbo(U, steps, seed, **hyper):
+    rng = np.random.default_rng(seed)
+    dev = torch.device("cuda")
+    p = rng.normal(size=U).astype(np.float32)
+    h = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    h.update(hyper)
+    tst, tbd = raster.fpbo_pack(torch.from_numpy(p).to(dev))
+    ost, obd = A.fpbo_pack(p)
+    torch.cuda.synchronize()
+    gst, gbd = tst.cpu().numpy().view(np.uint16), tbd.cpu().numpy()
+    assert np.array_equal(gbd, obd), f"pack U={U}: bounds"
+    nb = obd.shape[0]
+    blk = np.arange(U) // 256
+    x0 = p.astype(np.float64)
+    pack_dx = 16 * EPS64 * (np.abs(obd[blk, 0].astype(np.float64)) + np.abs(obd[blk, 1]) + np.abs(x0))
+    u, _ = _check_plane(f"pack U={U}", "param", gst[:, 0, :].reshape(-1)[:U].astype(np.int64), gbd[:, 0],
+                        gbd[:, 1], obd[:, 0], obd[:, 1], x0, pack_dx, U)
+    assert not gst[:, 1:, :].any() and (nb == 0 or not gst[nb - 1, 0, U - 256 * (nb - 1):].any())
+    assert u <= max(4, 1e-6 * U)
+    tp = torch.empty(U, dtype=torch.float32, device=dev)
+    for t in range(1, steps + 1):
+        g = grads_for(rng, U, t)
+        raster.adam_fpbo(U, tst, tbd, torch.from_numpy(g).to(dev), tp, step=t, **h)
+        orc = A.adam_fpbo(gst, gbd, g, step=t, full=True, **h)
+        torch.cuda.synchronize()
+        nst, nbd, gp = tst.cpu().numpy().view(np.uint16), tbd.cpu().numpy(), tp.cpu().numpy()
+        info = check_fpbo(U, (nst, nbd, gp), orc, gbd, g, f"fpbo U={U} step {t}")
+        say(f"adam_fpbo U={U} step {t}: ambiguous codes {info[0]}, block bounds {info[1]}, "
+            f"params_out off by one spacing {info[2]}")
+        gst, gbd = nst.copy(), nbd.copy()  # the next step starts from the GPU's state
+
+
+@pytest.mark.parametrize("U", [1, 255, 256, 257, 100_003])
+def test_fpbo_parity_steps(U):
+    run_fpbo(U, 4, 60 + U % 89)
+
+
+def test_fpbo_parity_hyperparameters():
+    run_fpbo(50_000, 3, 17, lr=0.05, beta1=0.5, beta2=0.9, eps=1e-4)
+    run_fpbo(50_000, 3, 18, lr=1e-4, beta1=0.0, beta2=0.0, eps=1e-12)
+
+
+def test_fpbo_parity_ten_million_units():
+    run_fpbo(10_000_000, 2, 19)
+
+
+def test_fpbo_without_params_out_and_empty():
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(21)
+    U = 5000
+    p = torch.from_numpy(rng.normal(size=U).astype(np.float32)).to(dev)
+    g = torch.from_numpy(grads_for(rng, U, 2)).to(dev)
+    s1, b1 = raster.fpbo_pack(p)
+    s2, b2 = s1.clone(), b1.clone()
+    out = torch.empty(U, device=dev)
+    raster.adam_fpbo(U, s1, b1, g, out, lr=1e-3, step=1)
+    raster.adam_fpbo(U, s2, b2, g, None, lr=1e-3, step=1)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(b1, b2)
+    e = torch.zeros(0, device=dev)
+    s0, b0 = raster.fpbo_pack(e)
+    raster.adam_fpbo(0, s0, b0, e, e, lr=1e-3, step=1)
+    torch.cuda.synchronize()
+    assert s0.shape == (0, 3, 256) and b0.shape == (0, 6)

@@ -43,6 +43,9 @@ hipError_t launch_project_qsh(int64_t n, const float* means, const float* scales
                               const DevCamera& cam, const gs_projected& out, hipStream_t s);
 hipError_t launch_adam_q16(int64_t U, float* params, const float* grads, uint32_t* state, float* bounds,
                            const gs_adam_params& p, hipStream_t s);
+hipError_t launch_fpbo_pack(int64_t U, const float* params, uint16_t* state, float* bounds, hipStream_t s);
+hipError_t launch_adam_fpbo(int64_t U, uint16_t* state, float* bounds, const float* grads, float* params_out,
+                            const gs_adam_params& p, hipStream_t s);
 hipError_t launch_densify_count(int64_t n, const float* scales, const float* opac, const float* accum,
                                 const int32_t* denom, const gs_densify_params& q, void* ws, uint64_t** total,
                                 hipStream_t s);
@@ -94,7 +97,7 @@ gs_status hip_status(hipError_t e) { return e == hipSuccess ? GS_OK : GS_ERR_HIP
 // Kernel timer: while armed for one kernel, every launch of that kernel is bracketed by
 // two HIP events recorded on its launch stream.  The events are created on first use and
 // kept for the life of the process (they are reused by later arming).
-enum TimedKernel { kNone = 0, kProject, kRenderFwd, kRenderBwd, kProjectBwd, kDensifyEmit, kAdamQ16, kSortPass };
+enum TimedKernel { kNone = 0, kProject, kRenderFwd, kRenderBwd, kProjectBwd, kDensifyEmit, kAdamQ16, kSortPass, kAdamFpbo };
 
 struct KernelTimer {
   std::mutex mu;
@@ -118,6 +121,7 @@ TimedKernel timed_kernel_id(const char* name) {
   if (!strcmp(name, "k_project_bwd")) return kProjectBwd;
   if (!strcmp(name, "k_densify_emit")) return kDensifyEmit;
   if (!strcmp(name, "k_adam_q16")) return kAdamQ16;
+  if (!strcmp(name, "k_adam_fpbo")) return kAdamFpbo;
   if (!strcmp(name, "k_onesweep_u64")) return kSortPass;
   return kNone;
 }
@@ -199,6 +203,33 @@ gs_status gs_adam_q16(int64_t n, float* params, const float* grads, uint32_t* st
   if (n >= ((int64_t)1 << 40)) return GS_ERR_OVERFLOW;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(timed(kAdamQ16, s, [&] { return launch_adam_q16(n, params, grads, state, bounds, p, s); }));
+}
+
+namespace {
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+}  // namespace
+
+gs_status gs_fpbo_pack(int64_t n, const float* params, uint16_t* state, float* bounds, void* stream) {
+  if (n < 0) return GS_ERR_INVALID_ARG;
+  if (n > 0 && (!params || !state || !bounds)) return GS_ERR_INVALID_ARG;
+  if (!aligned(params, 16) || !aligned(state, 8) || !aligned(bounds, 8)) return GS_ERR_INVALID_ARG;
+  if (n >= ((int64_t)1 << 40)) return GS_ERR_OVERFLOW;
+  return hip_status(launch_fpbo_pack(n, params, state, bounds, static_cast<hipStream_t>(stream)));
+}
+
+gs_status gs_adam_fpbo(int64_t n, uint16_t* state, float* bounds, const float* grads, float* params_out,
+                       const gs_adam_params* hyper, void* stream) {
+  if (n < 0 || !hyper) return GS_ERR_INVALID_ARG;
+  const gs_adam_params p = *hyper;
+  if (p.step < 1 || !(p.beta1 >= 0.0f && p.beta1 < 1.0f) || !(p.beta2 >= 0.0f && p.beta2 < 1.0f))
+    return GS_ERR_INVALID_ARG;
+  if (n > 0 && (!state || !bounds || !grads)) return GS_ERR_INVALID_ARG;
+  if (!aligned(grads, 16) || !aligned(params_out, 16) || !aligned(state, 8) || !aligned(bounds, 8))
+    return GS_ERR_INVALID_ARG;
+  if (n >= ((int64_t)1 << 40)) return GS_ERR_OVERFLOW;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(
+      timed(kAdamFpbo, s, [&] { return launch_adam_fpbo(n, state, bounds, grads, params_out, p, s); }));
 }
 
 const char* gs_status_string(gs_status s) {

@@ -24,7 +24,8 @@ ROW_BLOCK = 256  # GS_ROW_BLOCK
 ROWS_PER_BLOCK = 128  # GS_ROWS_PER_BLOCK
 
 EXPORTS = ("gs_project", "gs_workspace_bytes", "gs_bin_tiles", "gs_sort_keys", "gs_sort_ids", "gs_render_fwd",
-           "gs_render_bwd", "gs_densify", "gs_densify_workspace_bytes", "gs_adam_q16", "gs_quantize_sh",
+           "gs_render_bwd", "gs_densify", "gs_densify_workspace_bytes", "gs_adam_q16", "gs_fpbo_pack",
+           "gs_adam_fpbo", "gs_quantize_sh",
            "gs_project_qsh", "gs_status_string")
 
 
@@ -88,11 +89,13 @@ def lib():
         L.gs_densify.argtypes = [i64, vp, vp, vp, vp, vp, i32, vp, vp, vp, C.POINTER(GsDensifyParams), vp, vp, vp,
                                  vp, vp, vp, i64, C.POINTER(i64), vp, sz, vp]
         L.gs_adam_q16.argtypes = [i64, vp, vp, vp, vp, C.POINTER(GsAdamParams), vp]
+        L.gs_fpbo_pack.argtypes = [i64, vp, vp, vp, vp]
+        L.gs_adam_fpbo.argtypes = [i64, vp, vp, vp, vp, C.POINTER(GsAdamParams), vp]
         L.gs_quantize_sh.argtypes = [i64, vp, i32, i32, vp, vp, vp]
         L.gs_project_qsh.argtypes = [i64, vp, vp, vp, vp, vp, vp, i32, i32, C.POINTER(GsCamera), GsProjected, vp]
         for name in ("gs_project", "gs_bin_tiles", "gs_sort_keys", "gs_sort_ids", "gs_sort_keys_noalloc", "gs_render_fwd",
                      "gs_render_bwd", "gs_densify",
-                     "gs_adam_q16", "gs_quantize_sh", "gs_project_qsh"):
+                     "gs_adam_q16", "gs_fpbo_pack", "gs_adam_fpbo", "gs_quantize_sh", "gs_project_qsh"):
             getattr(L, name).restype = i32
         L.gs_status_string.argtypes = [i32]
         L.gs_status_string.restype = C.c_char_p
@@ -110,7 +113,7 @@ def lib():
 
 def kernel_timer_start(kernel):
     """Arm the library's event timer for one kernel ("k_project", "k_render_fwd",
-    "k_render_bwd", "k_project_bwd", "k_densify_emit", "k_adam_q16", "k_onesweep_u64");
+    "k_render_bwd", "k_project_bwd", "k_densify_emit", "k_adam_q16", "k_adam_fpbo", "k_onesweep_u64");
     returns the status code."""
     return lib().gs_kernel_timer_start(kernel.encode())
 
@@ -430,6 +433,26 @@ def adam_q16(params, grads, state, bounds, lr: float, step: int, beta1: float = 
     h = GsAdamParams(lr, beta1, beta2, eps, int(step))
     _check(lib().gs_adam_q16(params.numel(), _ptr(params), _ptr(grads), _ptr(state), _ptr(bounds), C.byref(h),
                              _stream(stream)), "gs_adam_q16")
+
+
+def fpbo_pack(params, stream=None) -> tuple:
+    """gs_fpbo_pack: packed start state of flat float32 params, (state uint16 as int16
+    [ceil(n/256)][3][256], bounds float32 [ceil(n/256)][6])."""
+    n = params.numel()
+    nb = (n + 255) // 256
+    state = torch.empty((nb, 3, 256), dtype=torch.int16, device=params.device)
+    bounds = torch.empty((nb, 6), dtype=torch.float32, device=params.device)
+    _check(lib().gs_fpbo_pack(n, _ptr(params), _ptr(state), _ptr(bounds), _stream(stream)), "gs_fpbo_pack")
+    return state, bounds
+
+
+def adam_fpbo(n: int, state, bounds, grads, params_out, lr: float, step: int, beta1: float = 0.9,
+              beta2: float = 0.999, eps: float = 1e-8, stream=None):
+    """gs_adam_fpbo on a packed state (updated in place); params_out (flat float32, or None)
+    receives the decoded new parameters."""
+    h = GsAdamParams(lr, beta1, beta2, eps, int(step))
+    _check(lib().gs_adam_fpbo(int(n), _ptr(state), _ptr(bounds), _ptr(grads), _ptr(params_out), C.byref(h),
+                              _stream(stream)), "gs_adam_fpbo")
 
 
 def quantize_sh(sh, sh_degree: int, bits: int, stream=None) -> tuple:
