@@ -9,9 +9,12 @@
 // coefficients whose count depends on the degree.  The formulas (EWA 2D covariance, real
 // SH) are the textbook ones; the pages omit them.
 //
-// Memory: every input is read once per call.  Each lane reads its own SH row (up to 192 B)
-// with 16-byte loads; the cache assembles the rows' lines, which measured faster than
-// staging them through LDS (the LDS would cap occupancy).  The backward writes its dL/dsh
+// Memory: every input is read once per call.  Degree-3 float32 SH rows (192 B each) reach
+// LDS by direct 16-byte global-to-LDS copies, two of every three 128-byte lines, coalesced
+// across the wavefront and overlapped with the float64 geometry; each lane loads the
+// remaining line of its row pair itself (copy_rows_to_lds, row_from_lds).  Rows of the
+// other degrees and quantised rows are read per lane with 16-byte loads, where the cache
+// assembles the lines.  The backward writes its dL/dsh
 // rows through LDS instead (odd float4 row stride, no bank conflicts) so the stores leave
 // as whole lines: per-lane strided stores of them measured far slower.  The
 // binning-critical geometry (camera-space mean, 2D covariance, support, pixel box) is
