@@ -40,13 +40,12 @@ __device__ __forceinline__ double decode_q16(uint32_t code, float lo, double ste
   return (double)lo + (double)code * step;
 }
 
-// scale = 65535 / (hi - lo) of the block; unused when hi == lo
-__device__ __forceinline__ uint32_t encode_q16(double x, float lo, float hi, double scale) {
+// scale = 65535 / (hi - lo) of the block, 0 when hi == lo (every code is then 0); the clamp
+// to [0, 65535] is a float64 max and min
+__device__ __forceinline__ uint32_t encode_q16(double x, float lo, double scale) {
 #pragma clang fp contract(off)
-  const double l = lo, h = hi;
-  if (h == l) return 0u;
-  const double c = rint((x - l) * scale);
-  return c <= 0.0 ? 0u : c >= kQMax ? 65535u : (uint32_t)c;
+  const double c = rint((x - (double)lo) * scale);
+  return (uint32_t)fmin(fmax(c, 0.0), kQMax);
 }
 
 constexpr int kUnitsPerLane = kAdamBlock / kWave;  // 4: one wavefront owns one block
@@ -54,21 +53,19 @@ constexpr int kUnitsPerLane = kAdamBlock / kWave;  // 4: one wavefront owns one 
 // Wavefront w of workgroup g owns block 4 g + w; lane l owns its units 4 l .. 4 l + 3 (16-byte
 // accesses).  The block's extremes are the float32 roundings of its float64 moments (rounding
 // is monotonic, so this rounds the float64 extremes; the values are finite), reduced inside
-// the lane and then across the wavefront: no LDS, no barrier.
-__global__ __launch_bounds__(kAdamBlock) void k_adam_q16(int64_t U, float* __restrict__ params,
-                                                         const float* __restrict__ grads,
-                                                         uint32_t* __restrict__ state, float4* __restrict__ bounds,
-                                                         AdamConsts k) {
+// the lane and then across the wavefront: no LDS, no barrier.  kFull: every unit of the block
+// is below U (all blocks but a ragged last one), so no unit needs a bounds test.
+template <bool kFull>
+__device__ __forceinline__ void adam_q16_block(int64_t U, int64_t blk, float* __restrict__ params,
+                                               const float* __restrict__ grads, uint32_t* __restrict__ state,
+                                               float4* __restrict__ bounds, const AdamConsts& k) {
 #pragma clang fp contract(off)
   constexpr int R = kUnitsPerLane;
-  const int64_t nb = (U + kAdamBlock - 1) / kAdamBlock;
-  const int64_t blk = (int64_t)blockIdx.x * (kAdamBlock / kWave) + threadIdx.x / kWave;
-  if (blk >= nb) return;  // uniform per wavefront
   const int64_t u0 = blk * kAdamBlock + (int64_t)__lane_id() * R;
   const float4 bd = bounds[blk];  // m_lo, m_hi, v_lo, v_hi
   float pv[R], gv[R];
   uint32_t wv[R];
-  const bool full = u0 + R <= U;
+  const bool full = kFull || u0 + R <= U;
   if (full) {
     const float4 p4 = *reinterpret_cast<const float4*>(params + u0);
     const float4 g4 = *reinterpret_cast<const float4*>(grads + u0);
@@ -101,7 +98,7 @@ __global__ __launch_bounds__(kAdamBlock) void k_adam_q16(int64_t U, float* __res
     const float den = __builtin_amdgcn_sqrtf(vh) + k.eps;
     const float upd = k.lr * mh * __builtin_amdgcn_rcpf(den);
     pv[r] = (float)((double)pv[r] - (double)upd);
-    if (u0 + r < U) {
+    if (kFull || u0 + r < U) {
       const int km = order_key((float)m[r]), kv = order_key((float)v[r]);
       mn = min(mn, km); mx = max(mx, km);
       vn = min(vn, kv); vx = max(vx, kv);
@@ -112,7 +109,7 @@ __global__ __launch_bounds__(kAdamBlock) void k_adam_q16(int64_t U, float* __res
   const double sm = mhi == mlo ? 0.0 : kQMax / ((double)mhi - (double)mlo);
   const double sv = vhi == vlo ? 0.0 : kQMax / ((double)vhi - (double)vlo);
 #pragma unroll
-  for (int r = 0; r < R; ++r) wv[r] = encode_q16(m[r], mlo, mhi, sm) | (encode_q16(v[r], vlo, vhi, sv) << 16);
+  for (int r = 0; r < R; ++r) wv[r] = encode_q16(m[r], mlo, sm) | (encode_q16(v[r], vlo, sv) << 16);
   if (full) {
     *reinterpret_cast<float4*>(params + u0) = make_float4(pv[0], pv[1], pv[2], pv[3]);
     *reinterpret_cast<uint4*>(state + u0) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
@@ -125,6 +122,19 @@ __global__ __launch_bounds__(kAdamBlock) void k_adam_q16(int64_t U, float* __res
       }
   }
   if (__lane_id() == 0) bounds[blk] = make_float4(mlo, mhi, vlo, vhi);
+}
+
+__global__ __launch_bounds__(kAdamBlock) void k_adam_q16(int64_t U, float* __restrict__ params,
+                                                         const float* __restrict__ grads,
+                                                         uint32_t* __restrict__ state, float4* __restrict__ bounds,
+                                                         AdamConsts k) {
+  const int64_t nb = (U + kAdamBlock - 1) / kAdamBlock;
+  const int64_t blk = (int64_t)blockIdx.x * (kAdamBlock / kWave) + threadIdx.x / kWave;
+  if (blk >= nb) return;  // uniform per wavefront
+  if ((blk + 1) * kAdamBlock <= U)
+    adam_q16_block<true>(U, blk, params, grads, state, bounds, k);
+  else
+    adam_q16_block<false>(U, blk, params, grads, state, bounds, k);
 }
 
 // Parameters packed too.  The same page keeps the parameters as 16-bit codes beside both
@@ -141,9 +151,11 @@ __device__ __forceinline__ void unpack4(uint2 w, uint32_t c[4]) {
 }
 __device__ __forceinline__ uint2 pack4(const uint32_t c[4]) { return make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16)); }
 
-// The block's float32 gradients (or parameters) of this lane, 0 past the last unit.
+// The block's float32 gradients (or parameters) of this lane, 0 past the last unit.  kFull:
+// every unit of the block is below U (no bounds tests).
+template <bool kFull>
 __device__ __forceinline__ void load4(const float* __restrict__ x, int64_t u0, int64_t U, float v[4]) {
-  if (u0 + kUnitsPerLane <= U) {
+  if (kFull || u0 + kUnitsPerLane <= U) {
     const float4 q = *reinterpret_cast<const float4*>(x + u0);
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
   } else {
@@ -152,8 +164,9 @@ __device__ __forceinline__ void load4(const float* __restrict__ x, int64_t u0, i
   }
 }
 
+template <bool kFull>
 __device__ __forceinline__ void store4(float* __restrict__ x, int64_t u0, int64_t U, const float v[4]) {
-  if (u0 + kUnitsPerLane <= U) {
+  if (kFull || u0 + kUnitsPerLane <= U) {
     *reinterpret_cast<float4*>(x + u0) = make_float4(v[0], v[1], v[2], v[3]);
   } else {
 #pragma unroll
@@ -164,11 +177,12 @@ __device__ __forceinline__ void store4(float* __restrict__ x, int64_t u0, int64_
 
 // Block bounds (lo, hi) of the float32 roundings of x over this lane's units below U, reduced
 // across the wavefront.
+template <bool kFull>
 __device__ __forceinline__ float2 block_bounds(const double x[4], int64_t u0, int64_t U) {
   int lo = INT32_MAX, hi = INT32_MIN;
 #pragma unroll
   for (int r = 0; r < kUnitsPerLane; ++r)
-    if (u0 + r < U) {
+    if (kFull || u0 + r < U) {
       const int kx = order_key((float)x[r]);
       lo = min(lo, kx);
       hi = max(hi, kx);
@@ -177,30 +191,29 @@ __device__ __forceinline__ float2 block_bounds(const double x[4], int64_t u0, in
 }
 
 // Codes of x with the block's bounds b, 0 past the last unit.
+template <bool kFull>
 __device__ __forceinline__ uint2 encode4(const double x[4], float2 b, int64_t u0, int64_t U) {
   const double sc = b.y == b.x ? 0.0 : kQMax / ((double)b.y - (double)b.x);
   uint32_t c[kUnitsPerLane];
 #pragma unroll
-  for (int r = 0; r < kUnitsPerLane; ++r) c[r] = u0 + r < U ? encode_q16(x[r], b.x, b.y, sc) : 0u;
+  for (int r = 0; r < kUnitsPerLane; ++r) c[r] = kFull || u0 + r < U ? encode_q16(x[r], b.x, sc) : 0u;
   return pack4(c);
 }
 
 // Initial packed state: the parameters' codes, both moments zero.
-__global__ __launch_bounds__(kAdamBlock) void k_fpbo_pack(int64_t U, const float* __restrict__ params,
-                                                          uint2* __restrict__ state, float2* __restrict__ bounds) {
-  const int64_t nb = (U + kAdamBlock - 1) / kAdamBlock;
-  const int64_t blk = (int64_t)blockIdx.x * (kAdamBlock / kWave) + threadIdx.x / kWave;
-  if (blk >= nb) return;  // uniform per wavefront
+template <bool kFull>
+__device__ __forceinline__ void fpbo_pack_block(int64_t U, int64_t blk, const float* __restrict__ params,
+                                                uint2* __restrict__ state, float2* __restrict__ bounds) {
   const int lane = (int)__lane_id();
   const int64_t u0 = blk * kAdamBlock + (int64_t)lane * kUnitsPerLane;
   float pv[kUnitsPerLane];
-  load4(params, u0, U, pv);
+  load4<kFull>(params, u0, U, pv);
   double x[kUnitsPerLane];
 #pragma unroll
   for (int r = 0; r < kUnitsPerLane; ++r) x[r] = pv[r];
-  const float2 b = block_bounds(x, u0, U);
+  const float2 b = block_bounds<kFull>(x, u0, U);
   uint2* st = state + blk * 3 * kPlaneWords;
-  st[lane] = encode4(x, b, u0, U);
+  st[lane] = encode4<kFull>(x, b, u0, U);
   st[kPlaneWords + lane] = make_uint2(0u, 0u);
   st[2 * kPlaneWords + lane] = make_uint2(0u, 0u);
   if (lane == 0) {
@@ -210,15 +223,23 @@ __global__ __launch_bounds__(kAdamBlock) void k_fpbo_pack(int64_t U, const float
   }
 }
 
-__global__ __launch_bounds__(kAdamBlock) void k_adam_fpbo(int64_t U, uint2* __restrict__ state,
-                                                          float2* __restrict__ bounds,
-                                                          const float* __restrict__ grads,
-                                                          float* __restrict__ params_out, AdamConsts k) {
-#pragma clang fp contract(off)
-  constexpr int R = kUnitsPerLane;
+__global__ __launch_bounds__(kAdamBlock) void k_fpbo_pack(int64_t U, const float* __restrict__ params,
+                                                          uint2* __restrict__ state, float2* __restrict__ bounds) {
   const int64_t nb = (U + kAdamBlock - 1) / kAdamBlock;
   const int64_t blk = (int64_t)blockIdx.x * (kAdamBlock / kWave) + threadIdx.x / kWave;
   if (blk >= nb) return;  // uniform per wavefront
+  if ((blk + 1) * kAdamBlock <= U)
+    fpbo_pack_block<true>(U, blk, params, state, bounds);
+  else
+    fpbo_pack_block<false>(U, blk, params, state, bounds);
+}
+
+template <bool kFull>
+__device__ __forceinline__ void adam_fpbo_block(int64_t U, int64_t blk, uint2* __restrict__ state,
+                                                float2* __restrict__ bounds, const float* __restrict__ grads,
+                                                float* __restrict__ params_out, const AdamConsts& k) {
+#pragma clang fp contract(off)
+  constexpr int R = kUnitsPerLane;
   const int lane = (int)__lane_id();
   const int64_t u0 = blk * kAdamBlock + (int64_t)lane * R;
   uint2* st = state + blk * 3 * kPlaneWords;
@@ -228,7 +249,7 @@ __global__ __launch_bounds__(kAdamBlock) void k_adam_fpbo(int64_t U, uint2* __re
   unpack4(st[kPlaneWords + lane], cm);
   unpack4(st[2 * kPlaneWords + lane], cv);
   float gv[R];
-  load4(grads, u0, U, gv);
+  load4<kFull>(grads, u0, U, gv);
   const double pstep = ((double)bp.y - (double)bp.x) * kInvQMax;
   const double mstep = ((double)bm.y - (double)bm.x) * kInvQMax;
   const double vstep = ((double)bv.y - (double)bv.x) * kInvQMax;
@@ -246,11 +267,12 @@ __global__ __launch_bounds__(kAdamBlock) void k_adam_fpbo(int64_t U, uint2* __re
     const float upd = k.lr * mh * __builtin_amdgcn_rcpf(den);
     th[r] = th[r] - (double)upd;
   }
-  const float2 np = block_bounds(th, u0, U), nm = block_bounds(m, u0, U), nv = block_bounds(v, u0, U);
-  const uint2 wp = encode4(th, np, u0, U);
+  const float2 np = block_bounds<kFull>(th, u0, U), nm = block_bounds<kFull>(m, u0, U),
+               nv = block_bounds<kFull>(v, u0, U);
+  const uint2 wp = encode4<kFull>(th, np, u0, U);
   st[lane] = wp;
-  st[kPlaneWords + lane] = encode4(m, nm, u0, U);
-  st[2 * kPlaneWords + lane] = encode4(v, nv, u0, U);
+  st[kPlaneWords + lane] = encode4<kFull>(m, nm, u0, U);
+  st[2 * kPlaneWords + lane] = encode4<kFull>(v, nv, u0, U);
   if (lane == 0) {
     bounds[3 * blk] = np;
     bounds[3 * blk + 1] = nm;
@@ -263,7 +285,7 @@ __global__ __launch_bounds__(kAdamBlock) void k_adam_fpbo(int64_t U, uint2* __re
     float pv[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) pv[r] = (float)decode_q16(c[r], np.x, step);
-    store4(params_out, u0, U, pv);
+    store4<kFull>(params_out, u0, U, pv);
   }
 }
 
@@ -283,6 +305,19 @@ hipError_t launch_adam_q16(int64_t U, float* params, const float* grads, uint32_
   const int64_t groups = (nb + kAdamBlock / kWave - 1) / (kAdamBlock / kWave);
   k_adam_q16<<<(unsigned)groups, kAdamBlock, 0, s>>>(U, params, grads, state, reinterpret_cast<float4*>(bounds), k);
   return hipGetLastError();
+}
+
+__global__ __launch_bounds__(kAdamBlock) void k_adam_fpbo(int64_t U, uint2* __restrict__ state,
+                                                          float2* __restrict__ bounds,
+                                                          const float* __restrict__ grads,
+                                                          float* __restrict__ params_out, AdamConsts k) {
+  const int64_t nb = (U + kAdamBlock - 1) / kAdamBlock;
+  const int64_t blk = (int64_t)blockIdx.x * (kAdamBlock / kWave) + threadIdx.x / kWave;
+  if (blk >= nb) return;  // uniform per wavefront
+  if ((blk + 1) * kAdamBlock <= U)
+    adam_fpbo_block<true>(U, blk, state, bounds, grads, params_out, k);
+  else
+    adam_fpbo_block<false>(U, blk, state, bounds, grads, params_out, k);
 }
 
 namespace {
