@@ -268,6 +268,9 @@ def test_fpbo_parity_steps(U):
 def test_fpbo_parity_hyperparameters():
     run_fpbo(50_000, 3, 17, lr=0.05, beta1=0.5, beta2=0.9, eps=1e-4)
     run_fpbo(50_000, 3, 18, lr=1e-4, beta1=0.0, beta2=0.0, eps=1e-12)
+    # updates far below half a parameter code step (~4e-5 here): the stored parameters keep
+    # their codes wherever the block bounds do not move, on both sides
+    run_fpbo(50_000, 3, 22, lr=1e-7)
 
 
 def test_fpbo_parity_ten_million_units():
