@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 WORKLOAD = "aniso_1m_sh3_1080p_8cam"
 HBM_PEAK_GBS = 8000.0
-VALU_PEAK_TOPS = 256 * 2.4e9 * 64 / 1e12   # non-packed fp32 lane-ops/s: 39.3 T
+VALU_PEAK_TOPS = 157.3 / 2   # fp32 lane-ops/s: the published 157.3 TFLOP/s, an FMA as one op: 78.6 T
 TMIN = float(np.float32(1e-4))
 
 # Algorithmic VALU lane-operations of the plain per-pixel loops, one issue slot per operation.
@@ -511,7 +511,7 @@ def config_report(args, raster, scenes, dev, sc3, cams3):
              ("aniso_10m_sh3_1080p", False), ("aniso_1m_sh3_720p_bwd", True)]
     rep = {"copy_gbs": round(copy_gbs, 1), "frames_per_camera": args.frames,
            "timing": "median wall time per frame between device synchronisations, pair-count read-back included",
-           "roofline": "sum over stages of max(HBM bytes / rate, VALU lane-op slots / 39.3 T/s) / measured time",
+           "roofline": "sum over stages of max(HBM bytes / rate, VALU lane-op slots / 78.6 T/s) / measured time",
            "oracle_threads": threads, "host_cpus": usable, "host_cpu_model": model, "per_config": {}}
     for name, with_bwd in specs:
         log(f"configuration {name}")
