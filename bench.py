@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 
 WORKLOAD = "aniso_1m_sh3_1080p_8cam"
 HBM_PEAK_GBS = 8000.0
-VALU_PEAK_TOPS = 157.3 / 2   # fp32 lane-ops/s: the published 157.3 TFLOP/s, an FMA as one op: 78.6 T
+VALU_PEAK_TOPS = 78.6   # fp32 lane-ops/s: the published 157.3 TFLOP/s with an FMA as one op (157.3 / 2)
 TMIN = float(np.float32(1e-4))
 
 # Algorithmic VALU lane-operations of the plain per-pixel loops, one issue slot per operation.
